@@ -191,8 +191,9 @@ def dispatch(ids: np.ndarray, E: int, m_tile: int = 1, rows_cap: Optional[int] =
 
 
 def expert_ffn(x_rows: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray, w_down: np.ndarray,
-               mirror_h: bool = False) -> np.ndarray:
-    """y [n][H] (fp64) of one SwiGLU expert on n rows."""
+               h_bf16: bool = False) -> np.ndarray:
+    """y [n][H] (fp64) of one SwiGLU expert on n rows; h_bf16 stores the
+    intermediate activation in bf16 (the activation format of a bf16 layer)."""
     x_rows, w_gate, w_up, w_down = _c(x_rows), _c(w_gate), _c(w_up), _c(w_down)
     n, H = x_rows.shape
     I = w_gate.shape[0]
@@ -200,7 +201,7 @@ def expert_ffn(x_rows: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray, w_down:
     assert w_gate.dtype == w_up.dtype == w_down.dtype
     y = np.empty((n, H), dtype=np.float64)
     lib().orc_expert_ffn(n, H, I, _dtype_code(x_rows), _p(x_rows), _dtype_code(w_gate),
-                         _p(w_gate), _p(w_up), _p(w_down), int(mirror_h), _p(y))
+                         _p(w_gate), _p(w_up), _p(w_down), int(h_bf16), _p(y))
     return y
 
 
@@ -235,7 +236,7 @@ def combine(y_rows: np.ndarray, tok_row: np.ndarray, topk_w: np.ndarray,
 
 def layer(x, w_router, w_gate, w_up, w_down, k: int, score: int = SOFTMAX, n_groups: int = 1,
           topk_groups: int = 1, group_score: int = TOP2_SUM, renormalize: bool = True,
-          routed_scale: float = 1.0, bias=None, shared=None, mirror_h: bool = False):
+          routed_scale: float = 1.0, bias=None, shared=None, h_bf16: bool = False):
     """The whole layer.  w_gate/w_up [E][I][H], w_down [E][H][I]; shared is
     None or (sh_gate [Is][H], sh_up [Is][H], sh_down [H][Is]).
     Returns dict(out fp64 [T][H], logits, topk_ids, topk_w)."""
@@ -259,7 +260,7 @@ def layer(x, w_router, w_gate, w_up, w_down, k: int, score: int = SOFTMAX, n_gro
     rc = lib().orc_layer(T, H, E, k, I, score, n_groups, topk_groups, group_score,
                          int(renormalize), float(routed_scale), _dtype_code(x), _p(x),
                          _p(w_router), _p(bias), _dtype_code(w_gate), _p(w_gate), _p(w_up),
-                         _p(w_down), Is, _p(sg), _p(su), _p(sd), int(mirror_h), _p(out),
+                         _p(w_down), Is, _p(sg), _p(su), _p(sd), int(h_bf16), _p(out),
                          _p(logits), _p(ids), _p(w))
     if rc != 0:
         raise ValueError("orc_layer: invalid arguments")

@@ -102,8 +102,8 @@ uint8_t orc_e4m3_rne_sat(double v) {
 }
 
 /* Round a double to bf16, nearest-even.  The value is first rounded to fp32
- * (nearest-even, the C default), then fp32 to bf16.  Used only by the
- * mirrored mode, which rounds the fp32 value the GPU holds. */
+ * (nearest-even, the C default), then fp32 to bf16: the rounding decision is
+ * taken on the fp32 value, the precision in which the kernels hold it. */
 uint16_t orc_bf16_rne(double v) {
     float f = (float)v;
     uint32_t u;
@@ -417,12 +417,14 @@ static double silu(double z) { return z / (1.0 + exp(-z)); }
  *   g_i = sum_h x[r][h] * w_gate[i][h],   u_i = sum_h x[r][h] * w_up[i][h]
  *   a_i = silu(g_i) * u_i,                silu(z) = z / (1 + e^-z)
  *   y[r][h] = sum_i a_i * w_down[h][i]
- * mirror_h = 1 rounds a_i to bf16 (nearest-even) before the down projection,
- * the rounding the GPU path applies where it stores the intermediate; 0 keeps
- * the exact definition. */
+ * h_bf16 = 1 stores the intermediate activation a in bf16 (nearest-even, the
+ * decision taken on its fp32 value) before the down projection: in a layer
+ * whose activations are bf16, a is one of them.  h_bf16 = 0 keeps a exact,
+ * which is the definition for fp32 layers and the reference for measuring
+ * what the bf16 storage itself costs. */
 void orc_expert_ffn(int64_t n, int64_t H, int64_t I, int x_dtype, const void *x_rows,
                     int w_dtype, const void *w_gate, const void *w_up, const void *w_down,
-                    int mirror_h, double *y) {
+                    int h_bf16, double *y) {
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t r = 0; r < n; ++r) {
         double *xr = (double *)malloc(sizeof(double) * (size_t)H);
@@ -436,7 +438,7 @@ void orc_expert_ffn(int64_t n, int64_t H, int64_t I, int x_dtype, const void *x_
                     u += xr[h] * ld(w_dtype, w_up, (size_t)(i * H + h));
                 }
                 a[i] = silu(g) * u;
-                if (mirror_h) a[i] = orc_bf16_to_f64(orc_bf16_rne(a[i]));
+                if (h_bf16) a[i] = orc_bf16_to_f64(orc_bf16_rne(a[i]));
             }
             for (int64_t h = 0; h < H; ++h) {
                 double acc = 0.0;
@@ -456,7 +458,7 @@ void orc_expert_ffn(int64_t n, int64_t H, int64_t I, int x_dtype, const void *x_
  *   g, u, a as in orc_expert_ffn, in double.
  * The intermediate a is carried to the down projection as fp8 with one scale
  * per row and 128-column block (this step is part of the definition of the
- * fp8 layer, not a mirror):
+ * fp8 layer):
  *   a32_i   = fp32(a_i)
  *   amax    = max_i |a32_i| over the block
  *   s       = amax / 448 as an fp32 division  (s = 1 when amax == 0)
@@ -539,7 +541,7 @@ int orc_layer(int64_t T, int64_t H, int E, int k, int64_t I, int score_fn, int n
               int x_dtype, const void *x, const void *w_router, const float *bias,
               int w_dtype, const void *w_gate, const void *w_up, const void *w_down,
               int64_t I_shared, const void *sh_gate, const void *sh_up, const void *sh_down,
-              int mirror_h, double *out, float *logits_out, int32_t *ids_out, float *w_out) {
+              int h_bf16, double *out, float *logits_out, int32_t *ids_out, float *w_out) {
     int rc = -1;
     size_t xs = x_dtype == ORC_F32 ? 4 : (x_dtype == ORC_BF16 ? 2 : 1);
     size_t ws = w_dtype == ORC_F32 ? 4 : (w_dtype == ORC_BF16 ? 2 : 1);
@@ -575,13 +577,13 @@ int orc_layer(int64_t T, int64_t H, int E, int k, int64_t I, int score_fn, int n
                    xs * (size_t)H);
         }
         if (n > 0)
-            orc_expert_ffn(n, H, I, x_dtype, x_rows, w_dtype, wg, wu, wd, mirror_h,
+            orc_expert_ffn(n, H, I, x_dtype, x_rows, w_dtype, wg, wu, wd, h_bf16,
                            y_rows + (size_t)offs[e] * (size_t)H);
     }
     if (sh_gate) {
         y_sh = (double *)malloc(sizeof(double) * (size_t)(T * H + 1));
         if (!y_sh) goto done;
-        orc_expert_ffn(T, H, I_shared, x_dtype, x, w_dtype, sh_gate, sh_up, sh_down, mirror_h,
+        orc_expert_ffn(T, H, I_shared, x_dtype, x, w_dtype, sh_gate, sh_up, sh_down, h_bf16,
                        y_sh);
     }
     orc_combine(T, k, H, y_rows, tok_row, w, y_sh, out);

@@ -311,7 +311,7 @@ def test_expert_ffn_matches_numpy_chain():
     X, G, U, D = (oracle.bf16_to_f64(a) for a in (x, wg, wu, wd))
     np.testing.assert_allclose(got, _np_ffn(X, G, U, D), rtol=1e-12, atol=1e-12)
     rb = lambda a: f64(torch.tensor(a).to(torch.float32).to(torch.bfloat16))
-    got = oracle.expert_ffn(x, wg, wu, wd, mirror_h=True)
+    got = oracle.expert_ffn(x, wg, wu, wd, h_bf16=True)
     np.testing.assert_allclose(got, _np_ffn(X, G, U, D, rb), rtol=1e-12, atol=1e-12)
     xf = rng.normal(0, 1, (3, 16)).astype(np.float32)
     wgf, wuf = (rng.normal(0, 0.25, (8, 16)).astype(np.float32) for _ in range(2))
