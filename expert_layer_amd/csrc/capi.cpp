@@ -1,0 +1,397 @@
+// capi.cpp -- the C ABI of the MoE layer (include/moe.h): argument checks,
+// workspace layout and the enqueue order of the kernels.  Host code only.
+// Every entry point checks all arguments before the first launch, so an
+// invalid call enqueues nothing; no entry point allocates, frees or
+// synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "common.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+moe_status hip_fail(hipError_t e, const char* where) {
+    return fail(MOE_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
+
+int dtype_bytes(int d) { return d == MOE_F32 ? 4 : (d == MOE_BF16 ? 2 : 1); }
+
+int m_tile_of(const moe_cfg& c) { return c.m_tile > 0 ? c.m_tile : 1; }
+
+constexpr int64_t kMaxRows = INT32_MAX / 2;
+
+int64_t max_rows_of(const moe_cfg& c) {
+    return (int64_t)c.T * c.k + (int64_t)c.E * (m_tile_of(c) - 1);
+}
+
+moe_status check_cfg(const moe_cfg* cp) {
+    if (!cp) return fail(MOE_ERR_INVALID_ARG, "cfg is NULL");
+    const moe_cfg& c = *cp;
+    if (c.T < 0) return fail(MOE_ERR_INVALID_ARG, "T=%d must be >= 0", c.T);
+    if (c.H <= 0 || c.H % 8) return fail(MOE_ERR_INVALID_ARG, "H=%d must be a positive multiple of 8", c.H);
+    if (c.E < 1 || c.E > 1024) return fail(MOE_ERR_INVALID_ARG, "E=%d must be in [1, 1024]", c.E);
+    if (c.k < 1 || c.k > c.E || c.k > 32)
+        return fail(MOE_ERR_INVALID_ARG, "k=%d must be in [1, min(E, 32)]", c.k);
+    if (c.I <= 0 || c.I % 8) return fail(MOE_ERR_INVALID_ARG, "I=%d must be a positive multiple of 8", c.I);
+    if (c.n_groups < 1 || c.n_groups > 64 || c.E % c.n_groups)
+        return fail(MOE_ERR_INVALID_ARG, "n_groups=%d must divide E=%d and be in [1, 64]", c.n_groups, c.E);
+    if (c.topk_groups < 1 || c.topk_groups > c.n_groups)
+        return fail(MOE_ERR_INVALID_ARG, "topk_groups=%d must be in [1, n_groups]", c.topk_groups);
+    if ((int64_t)c.k > (int64_t)c.topk_groups * (c.E / c.n_groups))
+        return fail(MOE_ERR_INVALID_ARG, "k=%d exceeds the experts of the kept groups", c.k);
+    if (c.score_fn != MOE_SCORE_SOFTMAX && c.score_fn != MOE_SCORE_SIGMOID)
+        return fail(MOE_ERR_INVALID_ARG, "score_fn=%d", c.score_fn);
+    if (c.group_score != MOE_GROUP_TOP2_SUM && c.group_score != MOE_GROUP_MAX)
+        return fail(MOE_ERR_INVALID_ARG, "group_score=%d", c.group_score);
+    if (c.renormalize != 0 && c.renormalize != 1) return fail(MOE_ERR_INVALID_ARG, "renormalize=%d", c.renormalize);
+    if (!std::isfinite(c.routed_scale)) return fail(MOE_ERR_INVALID_ARG, "routed_scale is not finite");
+    if (c.has_shared != 0 && c.has_shared != 1) return fail(MOE_ERR_INVALID_ARG, "has_shared=%d", c.has_shared);
+    if (c.has_shared && (c.I_shared <= 0 || c.I_shared % 8))
+        return fail(MOE_ERR_INVALID_ARG, "I_shared=%d must be a positive multiple of 8", c.I_shared);
+    if (c.act_dtype < MOE_F32 || c.act_dtype > MOE_FP8_E4M3)
+        return fail(MOE_ERR_INVALID_ARG, "act_dtype=%d", c.act_dtype);
+    if (c.w_dtype != c.act_dtype)
+        return fail(MOE_ERR_UNSUPPORTED, "w_dtype=%d differs from act_dtype=%d", c.w_dtype, c.act_dtype);
+    if (c.y_dtype != MOE_F32 && c.y_dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "y_dtype=%d", c.y_dtype);
+    if (c.out_dtype != MOE_F32 && c.out_dtype != MOE_BF16)
+        return fail(MOE_ERR_INVALID_ARG, "out_dtype=%d", c.out_dtype);
+    if (c.act_dtype == MOE_FP8_E4M3) {
+        if (c.H % 128 || c.I % 128)
+            return fail(MOE_ERR_INVALID_ARG, "fp8 needs H and I multiples of 128 (H=%d, I=%d)", c.H, c.I);
+        if (c.has_shared) return fail(MOE_ERR_UNSUPPORTED, "fp8 with a shared expert");
+    }
+    if (c.m_tile < 0 || c.m_tile > 4096) return fail(MOE_ERR_INVALID_ARG, "m_tile=%d must be in [0, 4096]", c.m_tile);
+    if (max_rows_of(c) > kMaxRows) return fail(MOE_ERR_INVALID_ARG, "T*k + E*(m_tile-1) is too large");
+    if ((int64_t)c.T * c.H > (int64_t)INT32_MAX * 8) return fail(MOE_ERR_INVALID_ARG, "T*H is too large");
+    return MOE_OK;
+}
+
+// ---------------------------------------------------------------- workspace
+
+struct Carve {
+    char* base;
+    size_t off = 0;
+    explicit Carve(void* p) : base(static_cast<char*>(p)) {}
+    template <typename T>
+    T* take(size_t n) {
+        T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+        off = align_up(off + n * sizeof(T));
+        return p;
+    }
+};
+
+int ffn_bm(const moe_cfg& c) { return c.act_dtype == MOE_F32 ? moe::kFfnBmF32 : moe::kFfnBmBf16; }
+
+int64_t ffn_max_tiles(const moe_cfg& c, int64_t n_rows_cap) {
+    const int bm = ffn_bm(c);
+    return (n_rows_cap + bm - 1) / bm + c.E + (c.has_shared ? (c.T + bm - 1) / bm : 0) + 1;
+}
+
+size_t route_ws(const moe_cfg& c) { return align_up((size_t)c.T * c.E * sizeof(float)); }
+
+struct PermuteCarve {
+    moe::PermuteWs ws;
+    size_t bytes;
+};
+PermuteCarve permute_carve(const moe_cfg& c, void* p) {
+    Carve cv(p);
+    const size_t n = (size_t)moe::permute_blocks(c.T) * c.E;
+    moe::PermuteWs w;
+    w.hist = cv.take<int32_t>(n);
+    w.base = cv.take<int32_t>(n);
+    return {w, cv.off};
+}
+
+struct FfnCarve {
+    int32_t* tiles;
+    int32_t* n_tiles;
+    void* h;
+    float* h_scale;
+    void* h_sh;
+    int64_t max_tiles;
+    size_t bytes;
+};
+FfnCarve ffn_carve(const moe_cfg& c, int64_t n_rows_cap, void* p) {
+    Carve cv(p);
+    FfnCarve f{};
+    f.max_tiles = ffn_max_tiles(c, n_rows_cap);
+    f.tiles = cv.take<int32_t>((size_t)f.max_tiles * 4);
+    f.n_tiles = cv.take<int32_t>(1);
+    const int hb = c.act_dtype == MOE_F32 ? 4 : (c.act_dtype == MOE_BF16 ? 2 : 1);
+    f.h = cv.take<char>((size_t)n_rows_cap * c.I * hb);
+    f.h_scale = c.act_dtype == MOE_FP8_E4M3 ? cv.take<float>((size_t)n_rows_cap * (c.I / 128)) : nullptr;
+    f.h_sh = c.has_shared ? cv.take<char>((size_t)c.T * c.I_shared * hb) : nullptr;
+    f.bytes = cv.off;
+    return f;
+}
+
+struct LayerCarve {
+    int32_t *ids, *counts, *offsets, *row_src, *tok_row;
+    float* topk_w;
+    void *x_perm, *y_rows, *y_shared, *scratch;
+    size_t bytes;
+};
+LayerCarve layer_carve(const moe_cfg& c, void* p) {
+    Carve cv(p);
+    LayerCarve l{};
+    const int64_t rows = max_rows_of(c);
+    const size_t tk = (size_t)c.T * c.k;
+    l.ids = cv.take<int32_t>(tk);
+    l.topk_w = cv.take<float>(tk);
+    l.counts = cv.take<int32_t>(c.E);
+    l.offsets = cv.take<int32_t>(c.E + 1);
+    l.row_src = cv.take<int32_t>((size_t)rows);
+    l.tok_row = cv.take<int32_t>(tk);
+    l.x_perm = cv.take<char>((size_t)rows * c.H * dtype_bytes(c.act_dtype));
+    l.y_rows = cv.take<char>((size_t)rows * c.H * dtype_bytes(c.y_dtype));
+    l.y_shared = c.has_shared ? cv.take<char>((size_t)c.T * c.H * dtype_bytes(c.y_dtype)) : nullptr;
+    size_t scratch = route_ws(c);
+    size_t pb = permute_carve(c, nullptr).bytes;
+    size_t fb = ffn_carve(c, rows, nullptr).bytes;
+    if (pb > scratch) scratch = pb;
+    if (fb > scratch) scratch = fb;
+    l.scratch = cv.take<char>(scratch);
+    l.bytes = cv.off;
+    return l;
+}
+
+moe_status check_ws(void* ws, size_t have, size_t need) {
+    if (need == 0) return MOE_OK;
+    if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+    if (reinterpret_cast<uintptr_t>(ws) % kAlign) return fail(MOE_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+    if (have < need) return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", have, need);
+    return MOE_OK;
+}
+
+#define REQUIRE(p, name) \
+    if (!(p)) return fail(MOE_ERR_INVALID_ARG, "%s is NULL", name)
+
+moe_status ffn_enqueue(const moe_cfg& c, int64_t n_rows_cap, const void* x_rows, const float* x_scale,
+                       const int32_t* offsets, const moe_weights& w, const void* x_tokens, void* y_rows,
+                       void* y_shared, void* ws, hipStream_t s) {
+    (void)x_scale;
+    FfnCarve f = ffn_carve(c, n_rows_cap, ws);
+    hipError_t e;
+    if (c.act_dtype == MOE_BF16)
+        e = moe::launch_gemm_bf16(c, f.max_tiles, n_rows_cap, x_rows, offsets, w, x_tokens, y_rows, y_shared, f.tiles,
+                                  f.n_tiles, f.h, f.h_sh, s);
+    else if (c.act_dtype == MOE_F32)
+        e = moe::launch_gemm_f32(c, f.max_tiles, n_rows_cap, x_rows, offsets, w, x_tokens, y_rows, y_shared, f.tiles,
+                                 f.n_tiles, f.h, f.h_sh, s);
+    else
+        return fail(MOE_ERR_UNSUPPORTED, "fp8 grouped FFN is not built");
+    if (e != hipSuccess) return hip_fail(e, "moe_grouped_ffn");
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_validate(const moe_cfg* cfg) { return check_cfg(cfg); }
+
+int64_t moe_max_rows(const moe_cfg* cfg) {
+    if (check_cfg(cfg) != MOE_OK) return -1;
+    return max_rows_of(*cfg);
+}
+
+size_t moe_workspace_bytes(const moe_cfg* cfg, int32_t stage) {
+    if (check_cfg(cfg) != MOE_OK) return (size_t)-1;
+    const moe_cfg& c = *cfg;
+    switch (stage) {
+    case MOE_STAGE_ROUTE: return route_ws(c);
+    case MOE_STAGE_PERMUTE: return permute_carve(c, nullptr).bytes;
+    case MOE_STAGE_FFN: return ffn_carve(c, max_rows_of(c), nullptr).bytes;
+    case MOE_STAGE_LAYER: return layer_carve(c, nullptr).bytes;
+    default: fail(MOE_ERR_INVALID_ARG, "stage=%d", stage); return (size_t)-1;
+    }
+}
+
+size_t moe_ffn_workspace_bytes(const moe_cfg* cfg, int64_t n_rows_cap) {
+    if (check_cfg(cfg) != MOE_OK) return (size_t)-1;
+    if (n_rows_cap < 0 || n_rows_cap > kMaxRows) {
+        fail(MOE_ERR_INVALID_ARG, "n_rows_cap=%lld must be in [0, 2^30)", (long long)n_rows_cap);
+        return (size_t)-1;
+    }
+    return ffn_carve(*cfg, n_rows_cap, nullptr).bytes;
+}
+
+moe_status moe_route(const moe_cfg* cfg, const void* x, const void* w_router, const float* bias,
+                     const float* logits_in, float* logits_out, int32_t* topk_ids, float* topk_w, void* ws,
+                     size_t ws_bytes, void* stream) {
+    moe_status st = check_cfg(cfg);
+    if (st != MOE_OK) return st;
+    const moe_cfg& c = *cfg;
+    if (c.act_dtype == MOE_FP8_E4M3) return fail(MOE_ERR_UNSUPPORTED, "router on fp8 activations");
+    if (!logits_in) {
+        REQUIRE(x, "x");
+        REQUIRE(w_router, "w_router");
+    }
+    REQUIRE(topk_ids, "topk_ids");
+    REQUIRE(topk_w, "topk_w");
+    const bool need_ws = !logits_in && !logits_out;
+    if (need_ws && (st = check_ws(ws, ws_bytes, route_ws(c))) != MOE_OK) return st;
+    if (c.T == 0) return MOE_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const float* l = logits_in;
+    float* copy = nullptr;
+    if (!logits_in) {
+        float* dst = logits_out ? logits_out : static_cast<float*>(ws);
+        hipError_t e = moe::launch_router_logits(c, x, w_router, dst, s);
+        if (e != hipSuccess) return hip_fail(e, "moe_route (logits)");
+        l = dst;
+    } else if (logits_out) {
+        copy = logits_out;
+    }
+    hipError_t e = moe::launch_route_select(c, l, bias, copy, topk_ids, topk_w, s);
+    if (e != hipSuccess) return hip_fail(e, "moe_route (select)");
+    return MOE_OK;
+}
+
+moe_status moe_permute(const moe_cfg* cfg, const void* x, const float* x_scale, const int32_t* topk_ids,
+                       int32_t* expert_counts, int32_t* expert_offsets, int32_t* row_src, int32_t* tok_row,
+                       void* x_perm, float* x_perm_scale, void* ws, size_t ws_bytes, void* stream) {
+    moe_status st = check_cfg(cfg);
+    if (st != MOE_OK) return st;
+    const moe_cfg& c = *cfg;
+    REQUIRE(x, "x");
+    REQUIRE(topk_ids, "topk_ids");
+    REQUIRE(expert_counts, "expert_counts");
+    REQUIRE(expert_offsets, "expert_offsets");
+    REQUIRE(row_src, "row_src");
+    REQUIRE(tok_row, "tok_row");
+    REQUIRE(x_perm, "x_perm");
+    if (c.act_dtype == MOE_FP8_E4M3) {
+        REQUIRE(x_scale, "x_scale");
+        REQUIRE(x_perm_scale, "x_perm_scale");
+    }
+    PermuteCarve pc = permute_carve(c, ws);
+    if ((st = check_ws(ws, ws_bytes, pc.bytes)) != MOE_OK) return st;
+    if (c.T == 0) return MOE_OK;
+    hipError_t e = moe::launch_permute(c, x, x_scale, topk_ids, expert_counts, expert_offsets, row_src, tok_row,
+                                       x_perm, x_perm_scale, max_rows_of(c), pc.ws, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "moe_permute");
+    return MOE_OK;
+}
+
+moe_status moe_grouped_ffn(const moe_cfg* cfg, int64_t n_rows_cap, const void* x_rows, const float* x_scale,
+                           const int32_t* expert_offsets, const moe_weights* w, const void* x_tokens, void* y_rows,
+                           void* y_shared, void* ws, size_t ws_bytes, void* stream) {
+    moe_status st = check_cfg(cfg);
+    if (st != MOE_OK) return st;
+    const moe_cfg& c = *cfg;
+    if (n_rows_cap < 0 || n_rows_cap > kMaxRows)
+        return fail(MOE_ERR_INVALID_ARG, "n_rows_cap=%lld must be in [0, 2^30)", (long long)n_rows_cap);
+    REQUIRE(w, "w");
+    REQUIRE(expert_offsets, "expert_offsets");
+    REQUIRE(w->w_gate, "w->w_gate");
+    REQUIRE(w->w_up, "w->w_up");
+    REQUIRE(w->w_down, "w->w_down");
+    if (n_rows_cap > 0) {
+        REQUIRE(x_rows, "x_rows");
+        REQUIRE(y_rows, "y_rows");
+    }
+    if (c.act_dtype == MOE_FP8_E4M3) {
+        REQUIRE(x_scale, "x_scale");
+        REQUIRE(w->s_gate, "w->s_gate");
+        REQUIRE(w->s_up, "w->s_up");
+        REQUIRE(w->s_down, "w->s_down");
+    }
+    if (c.has_shared) {
+        REQUIRE(x_tokens, "x_tokens");
+        REQUIRE(y_shared, "y_shared");
+        REQUIRE(w->sh_gate, "w->sh_gate");
+        REQUIRE(w->sh_up, "w->sh_up");
+        REQUIRE(w->sh_down, "w->sh_down");
+    }
+    if (c.act_dtype == MOE_FP8_E4M3) return fail(MOE_ERR_UNSUPPORTED, "fp8 grouped FFN is not built");
+    const size_t need = ffn_carve(c, n_rows_cap, nullptr).bytes;
+    if ((st = check_ws(ws, ws_bytes, need)) != MOE_OK) return st;
+    if (n_rows_cap == 0 && !(c.has_shared && c.T > 0)) return MOE_OK;
+    return ffn_enqueue(c, n_rows_cap, x_rows, x_scale, expert_offsets, *w, x_tokens, y_rows, y_shared, ws,
+                       static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_combine(const moe_cfg* cfg, const void* y_rows, const int32_t* tok_row, const float* topk_w,
+                       const void* y_shared, void* out, void* stream) {
+    moe_status st = check_cfg(cfg);
+    if (st != MOE_OK) return st;
+    const moe_cfg& c = *cfg;
+    REQUIRE(y_rows, "y_rows");
+    REQUIRE(tok_row, "tok_row");
+    REQUIRE(topk_w, "topk_w");
+    REQUIRE(out, "out");
+    if (c.T == 0) return MOE_OK;
+    hipError_t e = moe::launch_combine(c, y_rows, tok_row, topk_w, y_shared, out, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "moe_combine");
+    return MOE_OK;
+}
+
+moe_status moe_layer(const moe_cfg* cfg, const void* w_router, const float* bias, const moe_weights* w,
+                     const void* x, void* out, void* ws, size_t ws_bytes, void* stream) {
+    moe_status st = check_cfg(cfg);
+    if (st != MOE_OK) return st;
+    const moe_cfg& c = *cfg;
+    if (c.act_dtype == MOE_FP8_E4M3) return fail(MOE_ERR_UNSUPPORTED, "moe_layer on fp8 activations");
+    REQUIRE(w_router, "w_router");
+    REQUIRE(w, "w");
+    REQUIRE(w->w_gate, "w->w_gate");
+    REQUIRE(w->w_up, "w->w_up");
+    REQUIRE(w->w_down, "w->w_down");
+    if (c.has_shared) {
+        REQUIRE(w->sh_gate, "w->sh_gate");
+        REQUIRE(w->sh_up, "w->sh_up");
+        REQUIRE(w->sh_down, "w->sh_down");
+    }
+    REQUIRE(x, "x");
+    REQUIRE(out, "out");
+    LayerCarve l = layer_carve(c, ws);
+    if ((st = check_ws(ws, ws_bytes, l.bytes)) != MOE_OK) return st;
+    if (c.T == 0) return MOE_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = moe::launch_router_logits(c, x, w_router, static_cast<float*>(l.scratch), s);
+    if (e != hipSuccess) return hip_fail(e, "moe_layer (router)");
+    e = moe::launch_route_select(c, static_cast<float*>(l.scratch), bias, nullptr, l.ids, l.topk_w, s);
+    if (e != hipSuccess) return hip_fail(e, "moe_layer (select)");
+    PermuteCarve pc = permute_carve(c, l.scratch);
+    e = moe::launch_permute(c, x, nullptr, l.ids, l.counts, l.offsets, l.row_src, l.tok_row, l.x_perm, nullptr,
+                            max_rows_of(c), pc.ws, s);
+    if (e != hipSuccess) return hip_fail(e, "moe_layer (permute)");
+    st = ffn_enqueue(c, max_rows_of(c), l.x_perm, nullptr, l.offsets, *w, x, l.y_rows, l.y_shared, l.scratch, s);
+    if (st != MOE_OK) return st;
+    e = moe::launch_combine(c, l.y_rows, l.tok_row, l.topk_w, l.y_shared, out, s);
+    if (e != hipSuccess) return hip_fail(e, "moe_layer (combine)");
+    return MOE_OK;
+}
+
+const char* moe_status_string(moe_status status) {
+    switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    }
+    return "MOE_ERR_UNKNOWN";
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+}  // extern "C"

@@ -1,0 +1,105 @@
+// combine.hip -- weighted gather-reduce of the expert results back to token
+// order ("ASAP", section 3.2.2: the expert results of every token and choice
+// return to the token's owner and are combined), plus the shared expert.
+//
+//   out[t][h] = sum_{j<k} w[t][j] * y_rows[tok_row[t][j]][h]  (+ y_shared[t][h])
+//
+// One workgroup per token; every thread owns 8 consecutive columns and reads
+// them from the k expert rows with 16-byte loads.  Pure HBM streaming: the
+// expert rows are read once, the output written once.
+#include "common.hpp"
+
+namespace moe {
+namespace {
+
+template <typename YT>
+__device__ __forceinline__ void load8(const YT* p, float (&v)[8]);
+
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float (&v)[8]) {
+    f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p) + 1);
+    v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+    v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
+}
+
+template <>
+__device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float (&v)[8]) {
+    i32x4 a = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(p));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint32_t u = (uint32_t)a[i];
+        v[2 * i] = __uint_as_float(u << 16);
+        v[2 * i + 1] = __uint_as_float(u & 0xFFFF0000u);
+    }
+}
+
+template <typename YT, typename OT>
+__global__ void __launch_bounds__(256)
+combine_kernel(const YT* __restrict__ y, const int32_t* __restrict__ tok_row, const float* __restrict__ tw,
+               const YT* __restrict__ ysh, OT* __restrict__ out, int k, int H) {
+    const int t = blockIdx.x;
+    __shared__ int32_t rows[32];
+    __shared__ float wts[32];
+    if (threadIdx.x < k) {
+        rows[threadIdx.x] = tok_row[(size_t)t * k + threadIdx.x];
+        wts[threadIdx.x] = tw[(size_t)t * k + threadIdx.x];
+    }
+    __syncthreads();
+    for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
+        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (int j = 0; j < k; ++j) {
+            float v[8];
+            load8<YT>(y + (size_t)rows[j] * H + c, v);
+            const float wj = wts[j];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj, v[i], acc[i]);
+        }
+        if (ysh) {
+            float v[8];
+            load8<YT>(ysh + (size_t)t * H + c, v);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] += v[i];
+        }
+        if constexpr (sizeof(OT) == 4) {
+            f32x4* o = reinterpret_cast<f32x4*>(out + (size_t)t * H + c);
+            o[0] = f32x4{acc[0], acc[1], acc[2], acc[3]};
+            o[1] = f32x4{acc[4], acc[5], acc[6], acc[7]};
+        } else {
+            i32x4 p;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                p[i] = (int)((uint32_t)f32_to_bf16(acc[2 * i]) | ((uint32_t)f32_to_bf16(acc[2 * i + 1]) << 16));
+            *reinterpret_cast<i32x4*>(out + (size_t)t * H + c) = p;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const moe_cfg& c, const void* y_rows, const int32_t* tok_row, const float* topk_w,
+                          const void* y_shared, void* out, hipStream_t s) {
+    dim3 grid(c.T), block(256);
+    if (c.y_dtype == MOE_F32) {
+        auto y = static_cast<const float*>(y_rows);
+        auto ys = static_cast<const float*>(y_shared);
+        if (c.out_dtype == MOE_F32)
+            hipLaunchKernelGGL((combine_kernel<float, float>), grid, block, 0, s, y, tok_row, topk_w, ys,
+                               static_cast<float*>(out), c.k, c.H);
+        else
+            hipLaunchKernelGGL((combine_kernel<float, uint16_t>), grid, block, 0, s, y, tok_row, topk_w, ys,
+                               static_cast<uint16_t*>(out), c.k, c.H);
+    } else {
+        auto y = static_cast<const uint16_t*>(y_rows);
+        auto ys = static_cast<const uint16_t*>(y_shared);
+        if (c.out_dtype == MOE_F32)
+            hipLaunchKernelGGL((combine_kernel<uint16_t, float>), grid, block, 0, s, y, tok_row, topk_w, ys,
+                               static_cast<float*>(out), c.k, c.H);
+        else
+            hipLaunchKernelGGL((combine_kernel<uint16_t, uint16_t>), grid, block, 0, s, y, tok_row, topk_w, ys,
+                               static_cast<uint16_t*>(out), c.k, c.H);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,138 @@
+// common.hpp -- device types, MFMA fragments and launch helpers shared by the
+// HIP kernels of the MoE layer (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+typedef __bf16 bf16_t;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 bit pattern (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return 0x7FC0;
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// OCP e4m3 code -> fp32 (exact).
+__device__ __forceinline__ float e4m3_to_f32(uint8_t c) {
+    uint32_t s = (uint32_t)(c & 0x80) << 24;
+    uint32_t e = (c >> 3) & 0xF;
+    uint32_t m = c & 0x7;
+    if (e == 0xF && m == 0x7) return __uint_as_float(0x7FC00000u | s);
+    if (e == 0) return __uint_as_float(s) + (s ? -1.0f : 1.0f) * (float)m * 0.001953125f;  // m * 2^-9
+    return __uint_as_float(s | ((e + 120u) << 23) | (m << 20));
+}
+
+// fp32 -> OCP e4m3, nearest-even, saturating at +-448.  The value v is first
+// clamped; the result is the nearest representable value.  Works on the bit
+// pattern: e4m3 normal numbers keep 3 fraction bits of an fp32 whose exponent
+// lies in [-6, 8]; below 2^-6 the spacing is the fixed 2^-9.
+__device__ __forceinline__ uint8_t f32_to_e4m3(float v) {
+    uint32_t u = __float_as_uint(v);
+    uint8_t sign = (uint8_t)((u >> 24) & 0x80);
+    float a = fabsf(v);
+    if (a != a) return 0x7F;
+    if (a >= 448.0f) return sign | 0x7E;
+    uint8_t code;
+    if (a < 0.015625f) {                   // subnormal range: multiples of 2^-9
+        float q = a * 512.0f;              // exact (power-of-two scaling)
+        float r = rintf(q);                // ties to even
+        code = (uint8_t)r;                 // 0..8 (8 == smallest normal)
+    } else {
+        uint32_t ua = __float_as_uint(a);
+        uint32_t lsb = (ua >> 20) & 1u;
+        ua += 0x7FFFFu + lsb;              // round to 3 fraction bits, ties to even
+        uint32_t e = (ua >> 23) - 120u;    // e4m3 biased exponent
+        uint32_t m = (ua >> 20) & 7u;
+        if (e > 15u || (e == 15u && m == 7u)) return sign | 0x7E;
+        code = (uint8_t)((e << 3) | m);
+    }
+    return code ? (uint8_t)(sign | code) : (uint8_t)0;
+}
+
+__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+
+// ---------------------------------------------------------------- MFMA
+// v_mfma_f32_32x32x16_bf16: A fragment = 8 bf16 of one row (lane % 32) at
+// k-half (lane / 32); B fragment = 8 bf16 of one column; C/D 16 fp32 per lane:
+// column = lane % 32, row = (i / 4) * 8 + (lane / 32) * 4 + (i % 4).
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// v_mfma_f32_32x32x64_f8f6f4 with both operands e4m3 (format code 0): A/B
+// fragment = 32 e4m3 bytes of one row/column at k-half (lane / 32).
+__device__ __forceinline__ f32x16 mfma32x32x64_fp8(i32x8 a, i32x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ int c_row(int i, int lane) { return (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3); }
+
+// Remaps a linear block id so that consecutive logical tiles run on the same
+// XCD: the dispatcher hands block b to XCD b % 8, so logical tile
+// L = (b % 8) * per_xcd + b / 8 keeps a contiguous run of tiles (sharing an A
+// panel or a weight panel) inside one XCD's L2.  Returns -1 for idle blocks.
+__device__ __forceinline__ int xcd_remap(int b, int n_valid) {
+    constexpr int kXcd = 8;
+    int per = (n_valid + kXcd - 1) / kXcd;
+    int x = b % kXcd, i = b / kXcd;
+    if (i >= per) return -1;
+    int L = x * per + i;
+    return L < n_valid ? L : -1;
+}
+
+}  // namespace moe
+
+// ---------------------------------------------------------------- launchers
+// Implemented in the .hip files; called by the C ABI layer (capi.cpp) after
+// argument checks.  Each returns hipSuccess or the launch error.
+namespace moe {
+
+hipError_t launch_router_logits(const moe_cfg& c, const void* x, const void* w_router,
+                                float* logits, hipStream_t s);
+hipError_t launch_route_select(const moe_cfg& c, const float* logits, const float* bias,
+                               float* logits_copy, int32_t* ids, float* w, hipStream_t s);
+
+struct PermuteWs {
+    int32_t* hist;   // [nblk][E] per-block expert counts
+    int32_t* base;   // [nblk][E] first row of block b's segment of expert e
+};
+int permute_blocks(int T);
+hipError_t launch_permute(const moe_cfg& c, const void* x, const float* x_scale, const int32_t* ids,
+                          int32_t* counts, int32_t* offsets, int32_t* row_src, int32_t* tok_row,
+                          void* x_perm, float* x_perm_scale, int64_t max_rows, PermuteWs ws,
+                          hipStream_t s);
+
+// Grouped FFN building blocks (gemm_bf16.hip, gemm_f32.hip).
+constexpr int kFfnBmBf16 = 256;
+constexpr int kFfnBmF32 = 64;
+hipError_t launch_build_tiles(const moe_cfg& c, const int32_t* offsets, int bm, int64_t rows_cap,
+                              int32_t* tiles, int32_t* n_tiles, hipStream_t s);
+hipError_t launch_gemm_bf16(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_cap, const void* x_rows, const int32_t* offsets,
+                            const moe_weights& w, const void* x_tokens, void* y_rows, void* y_shared,
+                            int32_t* tiles, int32_t* n_tiles, void* h, void* h_sh, hipStream_t s);
+hipError_t launch_gemm_f32(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_cap, const void* x_rows, const int32_t* offsets,
+                           const moe_weights& w, const void* x_tokens, void* y_rows, void* y_shared,
+                           int32_t* tiles, int32_t* n_tiles, void* h, void* h_sh, hipStream_t s);
+
+hipError_t launch_combine(const moe_cfg& c, const void* y_rows, const int32_t* tok_row,
+                          const float* topk_w, const void* y_shared, void* out, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,231 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) Mixture-of-Experts layer of a prefill
+ * step: router + top-k gating, dispatch (permute) by expert, per-expert SwiGLU
+ * FFN as a grouped GEMM, and the weighted combine back to token order.
+ *
+ * Where the operation is defined:
+ *  - "ASAP: A DiSaggregated and Asynchronous Inference System for MoE
+ *    Prefill", section 3.4.2: the MoE kernel is a grouped matrix
+ *    multiplication (GMM) whose left operand is the hidden states and whose
+ *    right operand is the expert weights of the layer.
+ *  - same page, Table 1 (K experts per token out of E_total, hidden size H) and
+ *    Table 2 with section 3.2 (the dispatch carries expert IDs, token counts
+ *    per expert and the hidden states; the combine returns the expert results
+ *    per token and choice).
+ *  - "Memory-Compute Disaggregation ... AFD Architecture Analysis", section 3:
+ *    the FFN side receives hidden states plus batch metadata, performs gated
+ *    routing and expert computation, and returns the layer output.
+ *  - same page, section 5 (MegaMoE operator fusion): routing/movement and the
+ *    expert GEMM are separable stages; this library exposes each stage and
+ *    the composed layer.
+ * The pages do not write the formulas; the exact arithmetic (scores, group
+ * limit, renormalisation, SwiGLU, fp8 block scales) is stated at each entry
+ * point below.
+ *
+ * Conventions (all entry points):
+ *  - Every array argument is a DEVICE pointer owned by the caller.  The
+ *    library never allocates, frees or keeps memory; scratch space is the
+ *    caller's workspace `ws` of at least moe_workspace_bytes() bytes, 256-byte
+ *    aligned.
+ *  - Every call is asynchronous on `stream` (a hipStream_t, NULL = the null
+ *    stream).  Nothing is read back to the host and no call synchronises.
+ *    Buffers must stay alive until the stream has executed the work.
+ *  - Arguments are checked on the host before anything is enqueued; an error
+ *    enqueues nothing.  A HIP launch error returns MOE_ERR_HIP; a device fault
+ *    shows up at the caller's next synchronisation.  moe_last_error() gives
+ *    the message of the last failure on the calling thread.
+ *  - Inputs are never written.  Outputs are written in full (padding included).
+ *  - T == 0 is valid: the call returns MOE_OK and enqueues nothing.
+ *  - Matrices are [out][in] row-major (the reduction index is contiguous):
+ *    w_router [E][H]; w_gate, w_up [E][I][H]; w_down [E][H][I]; the shared
+ *    expert sh_gate, sh_up [I_shared][H], sh_down [H][I_shared].
+ *  - Pointers are 16-byte aligned; H and I are multiples of 8 (bf16/fp32) or
+ *    of 128 (fp8).
+ *  - The library is stateless: concurrent calls on different streams need
+ *    different workspaces and outputs.
+ */
+#ifndef EXPERT_LAYER_AMD_MOE_H
+#define EXPERT_LAYER_AMD_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1, /* a size, pointer or option is out of range */
+    MOE_ERR_UNSUPPORTED = 2, /* a valid combination this library does not implement */
+    MOE_ERR_WORKSPACE = 3,   /* ws is NULL, misaligned or smaller than required */
+    MOE_ERR_HIP = 4          /* the HIP runtime reported an error at enqueue */
+} moe_status;
+
+typedef enum moe_dtype {
+    MOE_F32 = 0,
+    MOE_BF16 = 1,
+    MOE_FP8_E4M3 = 2 /* OCP e4m3: bias 7, max 448, S.1111.111 = NaN, no inf */
+} moe_dtype;
+
+typedef enum moe_score_fn { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score_fn;
+typedef enum moe_group_score { MOE_GROUP_TOP2_SUM = 0, MOE_GROUP_MAX = 1 } moe_group_score;
+
+typedef enum moe_stage {
+    MOE_STAGE_ROUTE = 0,
+    MOE_STAGE_PERMUTE = 1,
+    MOE_STAGE_FFN = 2,
+    MOE_STAGE_LAYER = 3
+} moe_stage;
+
+/* Problem statement of one MoE layer call.
+ *   T            tokens in the batch (rows of x)
+ *   H            hidden size
+ *   E            routed experts (ASAP's E_total; not its EP degree)
+ *   k            experts chosen per token (ASAP's K), 1 <= k <= min(E, 32)
+ *   I            intermediate size of a routed expert
+ *   n_groups     expert groups for group-limited routing (1 = none); E % n_groups == 0
+ *   topk_groups  groups kept per token (1 <= topk_groups <= n_groups)
+ *   score_fn     MOE_SCORE_SOFTMAX or MOE_SCORE_SIGMOID
+ *   group_score  MOE_GROUP_TOP2_SUM or MOE_GROUP_MAX
+ *   renormalize  1: the k weights are divided by their sum
+ *   routed_scale factor applied to the k weights after renormalisation
+ *   has_shared   1: a shared expert (weight 1) is added to every token
+ *   I_shared     intermediate size of the shared expert
+ *   act_dtype    x dtype (MOE_F32, MOE_BF16, or MOE_FP8_E4M3 for the grouped FFN)
+ *   w_dtype      expert weight dtype (equal to act_dtype)
+ *   y_dtype      dtype of the per-row expert outputs (y_rows, y_shared):
+ *                MOE_F32 or MOE_BF16
+ *   out_dtype    dtype of the layer output: MOE_F32 or MOE_BF16
+ *   m_tile       row padding of each expert segment produced by moe_permute
+ *                (1 = no padding; 0 = library default, 1)
+ * E <= 1024. */
+typedef struct moe_cfg {
+    int32_t T, H, E, k, I;
+    int32_t n_groups, topk_groups;
+    int32_t score_fn, group_score, renormalize;
+    float routed_scale;
+    int32_t has_shared, I_shared;
+    int32_t act_dtype, w_dtype, y_dtype, out_dtype;
+    int32_t m_tile;
+} moe_cfg;
+
+/* Expert weights.  For fp8 weights the s_* arrays hold one fp32 scale per
+ * 128 x 128 block: s_gate, s_up [E][I/128][H/128]; s_down [E][H/128][I/128]
+ * (dequantised weight = e4m3 value * block scale); NULL otherwise.  sh_* are
+ * the shared expert's matrices (NULL when has_shared == 0; bf16/fp32 only). */
+typedef struct moe_weights {
+    const void *w_gate, *w_up, *w_down;
+    const float *s_gate, *s_up, *s_down;
+    const void *sh_gate, *sh_up, *sh_down;
+} moe_weights;
+
+/* Checks a configuration on the host (no HIP call).  MOE_OK if every entry
+ * point accepts it. */
+moe_status moe_validate(const moe_cfg *cfg);
+
+/* Upper bound of the dispatched rows: T*k + E*(m_tile - 1).  Sizes row_src,
+ * x_perm and y_rows.  Returns -1 for an invalid cfg. */
+int64_t moe_max_rows(const moe_cfg *cfg);
+
+/* Workspace bytes the given stage needs (0 if none); (size_t)-1 for an
+ * invalid cfg or stage. */
+size_t moe_workspace_bytes(const moe_cfg *cfg, int32_t stage);
+
+/* Workspace bytes of moe_grouped_ffn for n_rows_cap rows (the FFN stage of
+ * moe_workspace_bytes is this with n_rows_cap = moe_max_rows(cfg)).
+ * (size_t)-1 for an invalid cfg or a negative / too large n_rows_cap. */
+size_t moe_ffn_workspace_bytes(const moe_cfg *cfg, int64_t n_rows_cap);
+
+/* Router GEMM and top-k gating (the "gated routing" of the AFD page, section
+ * 3; ASAP's expert IDs of Table 2).
+ *   logits[t][e] = sum_h x[t][h] * w_router[e][h]   (fp32 accumulation)
+ * or, when logits_in != NULL, logits = logits_in (x and w_router are then
+ * ignored and may be NULL).
+ *   softmax: z_e = logits[t][e] + bias[e] (bias may be NULL), p = softmax(z);
+ *            the selection key of expert e is z_e, its raw score p_e.
+ *   sigmoid: s_e = 1 / (1 + exp(-logits[t][e])); key s_e + bias[e]; raw s_e.
+ *   group limit (n_groups > 1): group g = experts [g*E/G, (g+1)*E/G); group
+ *            score = sum of its two largest keys (TOP2_SUM) or its largest
+ *            (MAX); the topk_groups best groups are kept (ties: lower group).
+ *   top-k:   the k best keys among kept experts, slot j = j-th best, ties to the
+ *            lower expert index; keys are fp32 values.
+ *   weight:  w_j = raw_j / sum(raw over the k) if renormalize else raw_j,
+ *            times routed_scale.
+ * x [T][H] act_dtype (F32 or BF16), w_router [E][H] same dtype, bias [E] fp32
+ * or NULL, logits_in [T][E] fp32 or NULL, logits_out [T][E] fp32 or NULL
+ * (written when non-NULL), topk_ids [T][k] int32, topk_w [T][k] fp32.
+ * ws: moe_workspace_bytes(cfg, MOE_STAGE_ROUTE). */
+moe_status moe_route(const moe_cfg *cfg, const void *x, const void *w_router, const float *bias,
+                     const float *logits_in, float *logits_out, int32_t *topk_ids,
+                     float *topk_w, void *ws, size_t ws_bytes, void *stream);
+
+/* Dispatch: a deterministic counting sort of the (token, choice) pairs by
+ * expert (ASAP section 3.2.1: token counts per expert plus the token payload).
+ *   expert_counts[e]  = #{(t, j) : topk_ids[t][j] == e}
+ *   expert_offsets[e] = sum_{e' < e} ceil(count[e'] / m_tile) * m_tile   (E + 1 entries)
+ *   inside an expert the rows follow ascending token index:
+ *   row(t, j)         = expert_offsets[e] + #{t' < t : e in topk_ids[t']}
+ *   row_src[row]      = t * k + j, or -1 for a padding row (moe_max_rows entries)
+ *   tok_row[t*k + j]  = row(t, j)
+ *   x_perm[row]       = x[t] (bit copy), zero rows where row_src == -1
+ *   x_perm_scale[row] = x_scale[t] (fp8 activations only; [rows][H/128])
+ * topk_ids must hold distinct ids in [0, E) per token.
+ * ws: moe_workspace_bytes(cfg, MOE_STAGE_PERMUTE). */
+moe_status moe_permute(const moe_cfg *cfg, const void *x, const float *x_scale,
+                       const int32_t *topk_ids, int32_t *expert_counts,
+                       int32_t *expert_offsets, int32_t *row_src, int32_t *tok_row,
+                       void *x_perm, float *x_perm_scale, void *ws, size_t ws_bytes,
+                       void *stream);
+
+/* Grouped SwiGLU FFN over expert-contiguous rows (ASAP section 3.4.2's GMM).
+ * For every expert e and every row r in [expert_offsets[e], expert_offsets[e+1]):
+ *   g_i = sum_h x_rows[r][h] * w_gate[e][i][h],  u_i = sum_h x_rows[r][h] * w_up[e][i][h]
+ *   a_i = silu(g_i) * u_i,  silu(z) = z / (1 + exp(-z))
+ *   y_rows[r][h] = sum_i a_i * w_down[e][h][i]
+ * with fp32 accumulation.  The intermediate a is stored as bf16 (bf16
+ * operands), fp32 (fp32 operands) or, for fp8 operands, as e4m3 with one fp32
+ * scale per row and 128 columns: s = max|a| / 448 (1 if the block is zero),
+ * q = e4m3_rne_sat(a / s).  fp8 operands are dequantised as code * scale with
+ * x_scale [n_rows_cap][H/128] (1 x 128 per-row blocks) and the 128 x 128
+ * weight block scales.  Offsets may be unpadded (any alignment) and rows of
+ * x_rows outside [0, expert_offsets[E]) are neither read nor written.
+ * When cfg->has_shared, the shared expert is applied to every token of
+ * x_tokens [T][H] into y_shared [T][H] (weight 1).
+ * y_rows [n_rows_cap][H] and y_shared in cfg->y_dtype.  n_rows_cap is the
+ * row count of x_rows and y_rows, independent of T (rows may arrive already
+ * dispatched); expert_offsets[E] <= n_rows_cap.
+ * ws: moe_ffn_workspace_bytes(cfg, n_rows_cap). */
+moe_status moe_grouped_ffn(const moe_cfg *cfg, int64_t n_rows_cap, const void *x_rows,
+                           const float *x_scale, const int32_t *expert_offsets,
+                           const moe_weights *w, const void *x_tokens, void *y_rows,
+                           void *y_shared, void *ws, size_t ws_bytes, void *stream);
+
+/* Combine: the weighted gather-reduce back to token order (ASAP section
+ * 3.2.2's expert results per token and choice).
+ *   out[t][h] = sum_{j=0..k-1} topk_w[t][j] * y_rows[tok_row[t*k+j]][h]  (+ y_shared[t][h])
+ * accumulated in fp32 in slot order, the shared term last.
+ * y_rows, y_shared in cfg->y_dtype; y_shared may be NULL; out [T][H] in
+ * cfg->out_dtype. */
+moe_status moe_combine(const moe_cfg *cfg, const void *y_rows, const int32_t *tok_row,
+                       const float *topk_w, const void *y_shared, void *out, void *stream);
+
+/* The whole layer: moe_route -> moe_permute -> moe_grouped_ffn -> moe_combine,
+ * enqueued on `stream` with no host synchronisation.  x [T][H] in act_dtype
+ * (F32 or BF16); out [T][H] in out_dtype.  All intermediates live in ws.
+ * ws: moe_workspace_bytes(cfg, MOE_STAGE_LAYER). */
+moe_status moe_layer(const moe_cfg *cfg, const void *w_router, const float *bias,
+                     const moe_weights *w, const void *x, void *out, void *ws,
+                     size_t ws_bytes, void *stream);
+
+/* Static text of a status code. */
+const char *moe_status_string(moe_status status);
+
+/* Message of the last failed call on the calling thread ("" if none). */
+const char *moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXPERT_LAYER_AMD_MOE_H */

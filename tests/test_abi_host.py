@@ -1,0 +1,166 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every
+symbol include/moe.h declares, validates configurations, sizes workspaces and
+rejects bad arguments before touching the HIP runtime."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import expert_layer_amd as m
+from expert_layer_amd import _ffi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = set()
+    inc = os.path.join(ROOT, "include")
+    for f in os.listdir(inc):
+        if f.endswith(".h"):
+            src = open(os.path.join(inc, f)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    decl = _declared()
+    assert decl >= set(_ffi.EXPORTS) and decl == set(_ffi.EXPORTS)
+    L = ctypes.CDLL(_ffi.LIB_PATH)
+    for n in sorted(decl):
+        assert hasattr(L, n), n
+
+
+def _dsv3(**kw):
+    base = dict(T=8192, H=7168, E=256, k=8, I=2048, n_groups=8, topk_groups=4, score_fn=m.MOE_SCORE_SIGMOID,
+                routed_scale=2.5, has_shared=True, I_shared=2048)
+    base.update(kw)
+    return m.make_cfg(**base)
+
+
+def test_validate_accepts_workload_shapes():
+    assert m.moe_validate(_dsv3()) == m.MOE_OK
+    assert m.moe_validate(m.make_cfg(T=256, H=512, E=8, k=2, I=1024, act_dtype=m.MOE_F32)) == m.MOE_OK
+    assert m.moe_validate(m.make_cfg(T=16384, H=4096, E=128, k=8, I=1536)) == m.MOE_OK
+    assert m.moe_validate(m.make_cfg(T=0, H=64, E=4, k=1, I=64)) == m.MOE_OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=9, E=8), m.MOE_ERR_INVALID_ARG),
+    (dict(k=0), m.MOE_ERR_INVALID_ARG),
+    (dict(k=33, E=64), m.MOE_ERR_INVALID_ARG),
+    (dict(E=1025, k=8, n_groups=5), m.MOE_ERR_INVALID_ARG),
+    (dict(n_groups=3), m.MOE_ERR_INVALID_ARG),
+    (dict(topk_groups=9), m.MOE_ERR_INVALID_ARG),
+    (dict(topk_groups=0), m.MOE_ERR_INVALID_ARG),
+    (dict(k=8, topk_groups=1, n_groups=64), m.MOE_ERR_INVALID_ARG),
+    (dict(H=7170), m.MOE_ERR_INVALID_ARG),
+    (dict(I=0), m.MOE_ERR_INVALID_ARG),
+    (dict(T=-1), m.MOE_ERR_INVALID_ARG),
+    (dict(score_fn=2), m.MOE_ERR_INVALID_ARG),
+    (dict(group_score=5), m.MOE_ERR_INVALID_ARG),
+    (dict(I_shared=0), m.MOE_ERR_INVALID_ARG),
+    (dict(y_dtype=m.MOE_FP8_E4M3), m.MOE_ERR_INVALID_ARG),
+    (dict(out_dtype=7), m.MOE_ERR_INVALID_ARG),
+    (dict(act_dtype=m.MOE_BF16, w_dtype=m.MOE_F32), m.MOE_ERR_UNSUPPORTED),
+    (dict(act_dtype=m.MOE_FP8_E4M3), m.MOE_ERR_UNSUPPORTED),  # fp8 + shared expert
+    (dict(m_tile=-1), m.MOE_ERR_INVALID_ARG),
+    (dict(routed_scale=float("inf")), m.MOE_ERR_INVALID_ARG),
+])
+def test_validate_rejects(kw, code):
+    c = _dsv3(**kw)
+    assert m.moe_validate(c) == code
+    assert m.moe_last_error() != ""
+    assert m.moe_max_rows(c) == -1
+    assert m.moe_workspace_bytes(c, m.MOE_STAGE_LAYER) == ctypes.c_size_t(-1).value
+
+
+def test_fp8_needs_128_multiples():
+    c = m.make_cfg(T=64, H=7168, E=8, k=1, I=2048, act_dtype=m.MOE_FP8_E4M3, y_dtype=m.MOE_BF16)
+    assert m.moe_validate(c) == m.MOE_OK
+    c = m.make_cfg(T=64, H=7168 + 64, E=8, k=1, I=2048, act_dtype=m.MOE_FP8_E4M3)
+    assert m.moe_validate(c) == m.MOE_ERR_INVALID_ARG
+
+
+def test_status_strings():
+    names = ["MOE_OK", "MOE_ERR_INVALID_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE", "MOE_ERR_HIP"]
+    for i, n in enumerate(names):
+        assert m.moe_status_string(i) == n
+    assert m.moe_status_string(99) == "MOE_ERR_UNKNOWN"
+
+
+def test_max_rows_and_workspace_sizes():
+    for mt in (0, 1, 16, 128):
+        c = _dsv3(m_tile=mt)
+        assert m.moe_max_rows(c) == 8192 * 8 + 256 * (max(mt, 1) - 1)
+    c = _dsv3()
+    ws = [m.moe_workspace_bytes(c, s) for s in range(4)]
+    assert ws[m.MOE_STAGE_ROUTE] == 8192 * 256 * 4
+    assert all(w % 256 == 0 for w in ws)
+    # the layer workspace holds x_perm (bf16), y_rows (fp32) and y_shared at least
+    rows = 8192 * 8
+    assert ws[m.MOE_STAGE_LAYER] >= rows * 7168 * 2 + rows * 7168 * 4 + 8192 * 7168 * 4
+    assert ws[m.MOE_STAGE_FFN] >= rows * 2048 * 2  # h in bf16
+    assert m.moe_workspace_bytes(c, 7) == ctypes.c_size_t(-1).value
+    assert m.moe_ffn_workspace_bytes(c, rows) == ws[m.MOE_STAGE_FFN]
+    assert m.moe_ffn_workspace_bytes(c, 10) < ws[m.MOE_STAGE_FFN]
+    assert m.moe_ffn_workspace_bytes(c, -1) == ctypes.c_size_t(-1).value
+
+
+def test_entry_points_reject_bad_arguments_before_any_launch():
+    c = m.make_cfg(T=16, H=64, E=8, k=2, I=64)
+    lib = _ffi.lib()
+    fake = ctypes.c_void_p(0x100000)  # never dereferenced: every call below fails its checks
+    st = lib.moe_route(ctypes.byref(c), fake, fake, None, None, None, None, fake, fake, 1 << 20, None)
+    assert st == m.MOE_ERR_INVALID_ARG and "topk_ids" in m.moe_last_error()
+    st = lib.moe_route(ctypes.byref(c), fake, fake, None, None, None, fake, fake, None, 0, None)
+    assert st == m.MOE_ERR_WORKSPACE
+    st = lib.moe_route(ctypes.byref(c), fake, fake, None, None, None, fake, fake, ctypes.c_void_p(0x100010),
+                       1 << 20, None)
+    assert st == m.MOE_ERR_WORKSPACE and "aligned" in m.moe_last_error()
+    st = lib.moe_route(ctypes.byref(c), fake, fake, None, None, None, fake, fake, fake, 16, None)
+    assert st == m.MOE_ERR_WORKSPACE
+    w = m.moe_weights(w_gate=0x100000, w_up=0x100000, w_down=None)
+    st = lib.moe_grouped_ffn(ctypes.byref(c), 32, fake, None, fake, ctypes.byref(w), None, fake, None, fake,
+                             1 << 30, None)
+    assert st == m.MOE_ERR_INVALID_ARG and "w_down" in m.moe_last_error()
+    w = m.moe_weights(w_gate=0x100000, w_up=0x100000, w_down=0x100000)
+    st = lib.moe_grouped_ffn(ctypes.byref(c), 1 << 31, fake, None, fake, ctypes.byref(w), None, fake, None, fake,
+                             1 << 30, None)
+    assert st == m.MOE_ERR_INVALID_ARG and "n_rows_cap" in m.moe_last_error()
+    st = lib.moe_grouped_ffn(ctypes.byref(c), 10**6, fake, None, fake, ctypes.byref(w), None, fake, None, fake,
+                             1 << 20, None)
+    assert st == m.MOE_ERR_WORKSPACE
+    st = lib.moe_combine(ctypes.byref(c), fake, None, fake, None, fake, None)
+    assert st == m.MOE_ERR_INVALID_ARG
+    st = lib.moe_layer(ctypes.byref(c), fake, None, ctypes.byref(w), fake, None, fake, 1 << 40, None)
+    assert st == m.MOE_ERR_INVALID_ARG and "out" in m.moe_last_error()
+    cs = m.make_cfg(T=16, H=64, E=8, k=2, I=64, has_shared=True, I_shared=64)
+    st = lib.moe_layer(ctypes.byref(cs), fake, None, ctypes.byref(w), fake, fake, fake, 1 << 40, None)
+    assert st == m.MOE_ERR_INVALID_ARG and "sh_gate" in m.moe_last_error()
+    fp8 = m.make_cfg(T=16, H=128, E=8, k=2, I=128, act_dtype=m.MOE_FP8_E4M3, y_dtype=m.MOE_BF16)
+    st = lib.moe_route(ctypes.byref(fp8), fake, fake, None, None, fake, fake, fake, fake, 1 << 20, None)
+    assert st == m.MOE_ERR_UNSUPPORTED
+
+
+def test_zero_tokens_enqueue_nothing():
+    """T == 0 returns MOE_OK without a launch (fake pointers, no GPU here)."""
+    c = m.make_cfg(T=0, H=64, E=8, k=2, I=64)
+    lib = _ffi.lib()
+    fake = ctypes.c_void_p(0x100000)
+    w = m.moe_weights(w_gate=0x100000, w_up=0x100000, w_down=0x100000)
+    ws = ctypes.c_void_p(0x100000)
+    assert lib.moe_route(ctypes.byref(c), fake, fake, None, None, fake, fake, fake, None, 0, None) == m.MOE_OK
+    assert lib.moe_permute(ctypes.byref(c), fake, None, fake, fake, fake, fake, fake, fake, None, ws, 1 << 20,
+                           None) == m.MOE_OK
+    assert lib.moe_combine(ctypes.byref(c), fake, fake, fake, None, fake, None) == m.MOE_OK
+    assert lib.moe_layer(ctypes.byref(c), fake, None, ctypes.byref(w), fake, fake, ws, 1 << 20, None) == m.MOE_OK
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    c = m.make_cfg(T=4, H=64, E=8, k=2, I=64)
+    with pytest.raises(ValueError):
+        m.moe_combine(c, torch.zeros(8, 64), torch.zeros(4, 2, dtype=torch.int32), torch.zeros(4, 2), None,
+                      torch.zeros(4, 64))
