@@ -1,0 +1,265 @@
+"""Benchmark of the MoE layer of a prefill step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3_dsv3_bf16]
+
+One step is one moe_layer call -- router GEMM + group-limited top-k, dispatch,
+grouped SwiGLU FFN (bf16 MFMA, shared expert included), combine -- over one
+batch of synthetic inputs already resident in HBM.  The default workload is the
+DeepSeek-V3-shaped prefill layer: T=8192 tokens, H=7168, 256 routed experts
+(top-8, sigmoid, 8 groups keep 4, renormalised x2.5) + 1 shared expert, SwiGLU
+intermediate 2048, bf16 weights and activations, fp32 accumulation, bf16
+output.  Inputs follow the workload's distributions (activations N(0,1),
+weights N(0, 1/fan_in)) from the seeded counter-based generator.
+
+Prints one JSON line: value = layer TFLOP/s (algorithmic: 6*H*I per routed
+(token, expert) pair and per token for the shared expert, plus 2*T*H*E for the
+router), tokens/s, the fraction of the bf16 dense MFMA peak, a per-stage
+breakdown timed with HIP events on the launch stream, the roofline of the
+dominant stage (the grouped FFN), and the oracle's CPU throughput on a bounded
+sample of the same arithmetic.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+METRIC = "MoE-layer TFLOP/s + tokens/s (1 GPU, DSV3 prefill shape); % of MFMA peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_grouped_ffn_c3_dsv3_bf16.json")
+FFN_SOURCES = [os.path.join(ROOT, "expert_layer_amd", "csrc", f) for f in ("gemm_bf16.hip", "common.hpp")]
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="c3_dsv3_bf16")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    return p.parse_args()
+
+
+def ffn_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in FFN_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def main():
+    a = parse()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import expert_layer_amd as moe
+    import synth
+
+    dev = torch.device("cuda:0")
+    s = synth.config(a.workload)
+    if s.dtype != "bf16":
+        raise SystemExit("bench.py times the bf16 layers (c2/c3/c4)")
+    T, H, E, k, I = s.T, s.H, s.E, s.k, s.I
+    c = moe.make_cfg(T=T, H=H, E=E, k=k, I=I, n_groups=s.n_groups, topk_groups=s.topk_groups,
+                     score_fn=moe.MOE_SCORE_SIGMOID if s.score == "sigmoid" else moe.MOE_SCORE_SOFTMAX,
+                     renormalize=s.renormalize, routed_scale=s.routed_scale, has_shared=s.shared,
+                     I_shared=s.I_shared, act_dtype=moe.MOE_BF16, y_dtype=moe.MOE_F32, out_dtype=moe.MOE_BF16)
+
+    # ---- inputs, resident in HBM before timing
+    t_gen = time.time()
+    x, w_r, bias = synth.router_inputs(s, dev)
+    wg = torch.empty((E, I, H), dtype=torch.bfloat16, device=dev)
+    wu = torch.empty_like(wg)
+    wd = torch.empty((E, H, I), dtype=torch.bfloat16, device=dev)
+    for e in range(E):
+        wg[e], wu[e], wd[e] = synth.expert_weights(s, e, dev)
+    sh = synth.shared_weights(s, dev) if s.shared else (None, None, None)
+    w = moe.weights(wg, wu, wd, sh_gate=sh[0], sh_up=sh[1], sh_down=sh[2])
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    ws = moe.workspace(c, moe.MOE_STAGE_LAYER, dev)
+    torch.cuda.synchronize()
+    print(f"[bench] inputs ready in {time.time() - t_gen:.1f}s; workspace {ws.numel() / 2**30:.2f} GiB",
+          file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+
+    def step():
+        moe.moe_layer(c, w_r, bias, w, x, out, ws, stream)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: K whole-layer steps
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(a.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = ev0.elapsed_time(ev1) / a.steps
+
+    # ---- per-stage breakdown: the same kernels through the stage entry points,
+    # with events between stages on the launch stream
+    R = T * k
+    rows = moe.moe_max_rows(c)
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    tw = torch.empty((T, k), dtype=torch.float32, device=dev)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offs = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    row_src = torch.empty(rows, dtype=torch.int32, device=dev)
+    tok_row = torch.empty((T, k), dtype=torch.int32, device=dev)
+    x_perm = torch.empty((rows, H), dtype=torch.bfloat16, device=dev)
+    y_rows = torch.empty((rows, H), dtype=torch.float32, device=dev)
+    y_sh = torch.empty((T, H), dtype=torch.float32, device=dev) if s.shared else None
+    ws_r = moe.workspace(c, moe.MOE_STAGE_ROUTE, dev)
+    ws_p = moe.workspace(c, moe.MOE_STAGE_PERMUTE, dev)
+    ws_f = moe.workspace(c, moe.MOE_STAGE_FFN, dev)
+    names = ["route", "permute", "grouped_ffn", "combine"]
+
+    def stage_step(evs):
+        evs[0].record(stream)
+        moe.moe_route(c, x, w_r, bias, None, None, ids, tw, ws_r, stream)
+        evs[1].record(stream)
+        moe.moe_permute(c, x, None, ids, counts, offs, row_src, tok_row, x_perm, None, ws_p, stream)
+        evs[2].record(stream)
+        moe.moe_grouped_ffn(c, rows, x_perm, None, offs, w, x, y_rows, y_sh, ws_f, stream)
+        evs[3].record(stream)
+        moe.moe_combine(c, y_rows, tok_row, tw, y_sh, out, stream)
+        evs[4].record(stream)
+
+    for _ in range(2):
+        stage_step([torch.cuda.Event(enable_timing=True) for _ in range(5)])
+    torch.cuda.synchronize()
+    stage_ms = np.zeros(4)
+    all_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(a.steps)]
+    for evs in all_evs:
+        stage_step(evs)
+    torch.cuda.synchronize()
+    for evs in all_evs:
+        stage_ms += np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(4)])
+    stage_ms /= a.steps
+
+    # ---- algorithmic work
+    I_sh = s.I_shared if s.shared else 0
+    ffn_flop = 6.0 * H * I * R + 6.0 * H * I_sh * T
+    router_flop = 2.0 * T * H * E
+    layer_flop = ffn_flop + router_flop
+    w_bytes = 3.0 * E * H * I * 2 + 3.0 * H * I_sh * 2
+    bytes_ = {
+        "route": T * H * 2 + E * H * 2 + T * k * 8,
+        "permute": T * H * 2 + R * H * 2 + T * k * 4 + 2 * R * 4,
+        "grouped_ffn": w_bytes + R * H * 2 + T * H * 2 * bool(s.shared) + (R + T * bool(s.shared)) * H * 4,
+        "combine": R * H * 4 + T * H * 4 * bool(s.shared) + T * H * 2 + T * k * 8,
+    }
+    tflops = layer_flop / (ms_step * 1e-3) / 1e12
+    stages = {}
+    for i, n in enumerate(names):
+        ms = float(stage_ms[i])
+        st = {"ms": round(ms, 4), "GB/s": round(bytes_[n] / (ms * 1e-3) / 1e9, 1),
+              "hbm_frac": round(bytes_[n] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        if n == "grouped_ffn":
+            st["TFLOP/s"] = round(ffn_flop / (ms * 1e-3) / 1e12, 1)
+            st["mfma_frac"] = round(ffn_flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+        if n == "route":
+            st["TFLOP/s"] = round(router_flop / (ms * 1e-3) / 1e12, 1)
+        stages[n] = st
+
+    ffn_achieved = ffn_flop / (stage_ms[2] * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        tf = json.load(open(TRAFFIC_FILE))
+        if tf.get("source_hash") == ffn_source_hash() and tf.get("workload") == a.workload:
+            traffic = tf.get("hbm_bytes_per_launch")
+    roofline = {"bound": "mfma", "achieved": round(ffn_achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ffn_achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "kernel": "moe_grouped_ffn (ffn_gemm_bf16<0> gate/up+SwiGLU, ffn_gemm_bf16<1> down, tile list)",
+                "flop_per_launch": ffn_flop}
+
+    cpu = None if a.no_cpu_baseline else cpu_baseline(s, x, w_r, wg, wu, wd, a.cpu_seconds)
+
+    sclk = None
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
+        for line in r.stdout.splitlines():
+            if "sclk" in line and "Mhz" in line:
+                sclk = line.split("(")[-1].split(")")[0]
+                break
+    except Exception:
+        pass
+
+    res = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": a.workload, "T": T, "H": H, "E": E, "k": k, "I": I, "shared_experts": int(s.shared),
+                   "I_shared": I_sh, "router": s.score, "n_groups": s.n_groups, "topk_groups": s.topk_groups,
+                   "routed_scale": s.routed_scale, "out_dtype": "bf16", "expert_out_dtype": "fp32"},
+        "tokens_per_s": round(T / (ms_step * 1e-3), 1),
+        "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "layer_flop": layer_flop,
+        "wall_s_timed": round(wall, 3),
+        "stages": stages,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "sclk": sclk,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(s, x, w_r, wg, wu, wd, target_s):
+    """The oracle as it stands on the host cores: router logits + gating and one
+    routed expert's SwiGLU FFN for a sample of token rows (the per-row
+    arithmetic of the layer), sized to about target_s seconds; reported in
+    TFLOP/s of that sample."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    def bits(t):
+        return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+    wh = bits(w_r)
+    g, u, d = bits(wg[0]), bits(wu[0]), bits(wd[0])
+    per_row = 2.0 * s.H * s.E + 6.0 * s.H * s.I
+
+    def run(n):
+        xr = bits(x[:n])
+        t0 = time.perf_counter()
+        lg = oracle.router_logits(xr, wh)
+        oracle.route_select(lg, s.k, score=1 if s.score == "sigmoid" else 0, n_groups=s.n_groups,
+                            topk_groups=s.topk_groups, renormalize=s.renormalize, routed_scale=s.routed_scale)
+        oracle.expert_ffn(xr, g, u, d, h_bf16=True)
+        return time.perf_counter() - t0
+
+    n = 32
+    dt = run(n)
+    n = int(min(4096, max(32, n * target_s / max(dt, 1e-3))))
+    dt = run(n)
+    threads = min(oracle.threads(), n)
+    return {"value": round(n * per_row / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} token rows: router logits + group-limited top-k over {s.E} experts and one routed "
+                      f"SwiGLU expert (H={s.H}, I={s.I}), fp64, {dt:.1f} s",
+            "seconds": round(dt, 2)}
+
+
+if __name__ == "__main__":
+    main()

@@ -120,8 +120,7 @@ PermuteCarve permute_carve(const moe_cfg& c, void* p) {
 }
 
 struct FfnCarve {
-    int32_t* tiles;
-    int32_t* n_tiles;
+    moe::FfnWork wk;
     void* h;
     float* h_scale;
     void* h_sh;
@@ -132,8 +131,15 @@ FfnCarve ffn_carve(const moe_cfg& c, int64_t n_rows_cap, void* p) {
     Carve cv(p);
     FfnCarve f{};
     f.max_tiles = ffn_max_tiles(c, n_rows_cap);
-    f.tiles = cv.take<int32_t>((size_t)f.max_tiles * 4);
-    f.n_tiles = cv.take<int32_t>(1);
+    const bool f32 = c.act_dtype == MOE_F32;
+    const int n1 = f32 ? moe::kFfnN1F32 : moe::kFfnN1Bf16, n2 = f32 ? moe::kFfnN2F32 : moe::kFfnN2Bf16;
+    const int imax = c.has_shared && c.I_shared > c.I ? c.I_shared : c.I;
+    f.wk.nt1 = (imax + n1 - 1) / n1;
+    f.wk.nt2 = (c.H + n2 - 1) / n2;
+    f.wk.tiles = cv.take<int32_t>((size_t)f.max_tiles * 4);
+    f.wk.n_tiles = cv.take<int32_t>(1);
+    f.wk.work1 = cv.take<int32_t>((size_t)f.max_tiles * f.wk.nt1 * 2);
+    f.wk.work2 = cv.take<int32_t>((size_t)f.max_tiles * f.wk.nt2 * 2);
     const int hb = c.act_dtype == MOE_F32 ? 4 : (c.act_dtype == MOE_BF16 ? 2 : 1);
     f.h = cv.take<char>((size_t)n_rows_cap * c.I * hb);
     f.h_scale = c.act_dtype == MOE_FP8_E4M3 ? cv.take<float>((size_t)n_rows_cap * (c.I / 128)) : nullptr;
@@ -190,11 +196,11 @@ moe_status ffn_enqueue(const moe_cfg& c, int64_t n_rows_cap, const void* x_rows,
     FfnCarve f = ffn_carve(c, n_rows_cap, ws);
     hipError_t e;
     if (c.act_dtype == MOE_BF16)
-        e = moe::launch_gemm_bf16(c, f.max_tiles, n_rows_cap, x_rows, offsets, w, x_tokens, y_rows, y_shared, f.tiles,
-                                  f.n_tiles, f.h, f.h_sh, s);
+        e = moe::launch_gemm_bf16(c, f.max_tiles, n_rows_cap, x_rows, offsets, w, x_tokens, y_rows, y_shared, f.wk,
+                                  f.h, f.h_sh, s);
     else if (c.act_dtype == MOE_F32)
-        e = moe::launch_gemm_f32(c, f.max_tiles, n_rows_cap, x_rows, offsets, w, x_tokens, y_rows, y_shared, f.tiles,
-                                 f.n_tiles, f.h, f.h_sh, s);
+        e = moe::launch_gemm_f32(c, f.max_tiles, n_rows_cap, x_rows, offsets, w, x_tokens, y_rows, y_shared, f.wk,
+                                 f.h, f.h_sh, s);
     else
         return fail(MOE_ERR_UNSUPPORTED, "fp8 grouped FFN is not built");
     if (e != hipSuccess) return hip_fail(e, "moe_grouped_ffn");

@@ -120,17 +120,27 @@ hipError_t launch_permute(const moe_cfg& c, const void* x, const float* x_scale,
                           void* x_perm, float* x_perm_scale, int64_t max_rows, PermuteWs ws,
                           hipStream_t s);
 
-// Grouped FFN building blocks (gemm_bf16.hip, gemm_f32.hip).
-constexpr int kFfnBmBf16 = 256;
-constexpr int kFfnBmF32 = 64;
+// Grouped FFN building blocks (gemm_bf16.hip, gemm_f32.hip).  Tile heights
+// (rows) and the h / output columns one tile covers in GEMM1 / GEMM2.
+constexpr int kFfnBmBf16 = 256, kFfnN1Bf16 = 128, kFfnN2Bf16 = 256;
+constexpr int kFfnBmF32 = 64, kFfnN1F32 = 64, kFfnN2F32 = 64;
+
+// Device work lists of the grouped FFN, carved from the workspace.
+struct FfnWork {
+    int32_t* tiles;    // [max_tiles] x int4 {group, row_begin, row_end, 0}
+    int32_t* n_tiles;  // [1] M tiles written
+    int32_t* work1;    // [max_tiles * nt1] x int2 {M tile, N tile} of GEMM1
+    int32_t* work2;    // [max_tiles * nt2] x int2 {M tile, N tile} of GEMM2
+    int nt1, nt2;      // N tiles per M tile of GEMM1 / GEMM2
+};
 hipError_t launch_build_tiles(const moe_cfg& c, const int32_t* offsets, int bm, int64_t rows_cap,
-                              int32_t* tiles, int32_t* n_tiles, hipStream_t s);
-hipError_t launch_gemm_bf16(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_cap, const void* x_rows, const int32_t* offsets,
-                            const moe_weights& w, const void* x_tokens, void* y_rows, void* y_shared,
-                            int32_t* tiles, int32_t* n_tiles, void* h, void* h_sh, hipStream_t s);
-hipError_t launch_gemm_f32(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_cap, const void* x_rows, const int32_t* offsets,
-                           const moe_weights& w, const void* x_tokens, void* y_rows, void* y_shared,
-                           int32_t* tiles, int32_t* n_tiles, void* h, void* h_sh, hipStream_t s);
+                              const FfnWork& wk, hipStream_t s);
+hipError_t launch_gemm_bf16(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_cap, const void* x_rows,
+                            const int32_t* offsets, const moe_weights& w, const void* x_tokens, void* y_rows,
+                            void* y_shared, const FfnWork& wk, void* h, void* h_sh, hipStream_t s);
+hipError_t launch_gemm_f32(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_cap, const void* x_rows,
+                           const int32_t* offsets, const moe_weights& w, const void* x_tokens, void* y_rows,
+                           void* y_shared, const FfnWork& wk, void* h, void* h_sh, hipStream_t s);
 
 hipError_t launch_combine(const moe_cfg& c, const void* y_rows, const int32_t* tok_row,
                           const float* topk_w, const void* y_shared, void* out, hipStream_t s);

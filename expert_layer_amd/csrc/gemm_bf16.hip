@@ -10,27 +10,77 @@
 // host: the grid is sized from the host-known bound and blocks past the
 // device-side count exit at once.
 //
-// Tile.  256 rows x 256 weight rows x 64-wide K slices, 4 waves.  Each wave
-// owns all 256 rows and 64 weight rows (two 32-column MFMA blocks), so a short
-// tile skips whole 32-row blocks and all four SIMDs stay equally busy.
+// Tile.  256 rows x 256 weight rows, 4 waves.  Each wave owns all rows of the
+// tile and 64 weight rows (two 32-column MFMA blocks, v_mfma_f32_32x32x16_bf16),
+// so a short tile drops whole 32-row blocks and the four SIMDs stay equally
+// loaded; the tile body is specialised on the number of 32-row blocks.
 //   GEMM1: the 64 weight rows of wave w are 32 gate rows and the 32 up rows of
-//          the same h columns, so SwiGLU h = silu(g) * u is formed in
-//          registers and stored once as bf16.
+//          the same h columns: h = silu(g) * u is formed in registers.
 //   GEMM2: 256 output columns of y = h . w_down^T, fp32 or bf16.
-// Operands stream through LDS in 16-byte chunks, double-buffered, with the
-// chunk index XOR-swizzled by row; each global load instruction reads whole
-// 128-byte row segments.  Tiles are ordered (M tile, N tile) with N fastest
-// and remapped so that a contiguous run lives on one XCD: the 16 (or 28) N
-// tiles of one M tile share the A panel in that XCD's L2.
+// Pipeline.  K advances in 32-wide stages through a ring of four 32 KiB LDS
+// buffers.  Operands move HBM -> LDS by buffer_load ... lds (no staging
+// registers), issued three stages ahead; a chunk outside the tile (rows past
+// the expert's end, columns past N, the K tail, stages past the end) carries an
+// offset beyond its buffer descriptor and loads as zero with no memory traffic.
+// Each stage has two 16-wide k steps with a register set each: the fragments of
+// the next k step are read while the MFMAs of this one run.  Between a stage's
+// two k steps: wait for the next stage's loads, one s_barrier, and issue the
+// loads three stages ahead into the buffer just drained -- so LDS latency and
+// HBM latency both hide behind the MFMA pipe.
+// LDS chunks of 16 B are XOR-swizzled by row, physical chunk = logical ^
+// ((row >> 1) & 3) ^ ((row >> 3) & 1): a fragment read of 16 consecutive rows
+// (one pass of ds_read_b128 through the 64 banks of gfx950's LDS) touches 16
+// distinct 16-byte bank groups, and so does any 8 consecutive rows.  Tiles are ordered (M tile,
+// N tile) with N fastest and remapped so that a contiguous run lives on one
+// XCD: the N tiles of one M tile share its A panel in that XCD's L2.
 #include "common.hpp"
 
 namespace moe {
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 64, NTH = 256;
-constexpr int kLdsBytes = 2 * (BM + BN) * BK * 2;  // 128 KiB
+constexpr int BM = 256, BN = 256, BK = 32, NST = 4, NTH = 256;
+constexpr int kSlots = BM * 4;           // 16-byte slots of one operand in one stage
+constexpr uint32_t kOOB = 0x40000000u;   // past every tile descriptor: the load returns zero
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
+typedef __attribute__((address_space(3))) void* lds_t;
+
+// The four stage buffers, [A: 256 rows x 64 B][B: 256 rows x 64 B] each.  They
+// are distinct objects so that the compiler can tell which buffer an in-flight
+// LDS DMA writes and never waits for a load into another buffer.
+__shared__ i32x4 ring0[2 * kSlots];
+__shared__ i32x4 ring1[2 * kSlots];
+__shared__ i32x4 ring2[2 * kSlots];
+__shared__ i32x4 ring3[2 * kSlots];
+
+template <int BUF>
+__device__ __forceinline__ i32x4* ring() {
+    if constexpr (BUF == 0) return ring0;
+    else if constexpr (BUF == 1) return ring1;
+    else if constexpr (BUF == 2) return ring2;
+    else return ring3;
+}
+
+// Workgroup barrier without a memory fence (a fence would wait for every
+// in-flight LDS DMA); the clobber keeps LDS accesses on their side of it.
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_barrier" ::: "memory"); }
+
+// s_waitcnt on the vector-memory counter alone (gfx9 encoding: vmcnt[3:0] in
+// bits 3:0, vmcnt[5:4] in bits 15:14, expcnt 7 and lgkmcnt 15 mean no wait).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+// lgkmcnt(0): every LDS read of this wave has returned.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// XOR pattern of the 16-byte chunks of an LDS row (only bits 1..3 of the row
+// matter, so rows 32 apart share it).
+__device__ __forceinline__ int swz_of_row(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
 
 struct GemmArgs {
     const uint16_t* a_routed;  // GEMM1: x_rows [rows][H]; GEMM2: h [rows][I]
@@ -43,6 +93,7 @@ struct GemmArgs {
     void* out_shared;          // GEMM1: h_sh; GEMM2: y_shared
     const int4* tiles;
     const int32_t* n_tiles;
+    const int2* work;          // {M tile, N tile} in launch order
     int E;
     int NT;                    // N tiles per M tile in the launch grid
     int K_routed, K_shared;    // reduction length
@@ -50,74 +101,113 @@ struct GemmArgs {
     int out_f32;               // GEMM2 output dtype
 };
 
-template <int MODE>
-__global__ void __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1)))
-ffn_gemm_bf16(GemmArgs p) {
-    extern __shared__ i32x4 lds[];
-    i32x4* sA = lds;                   // [2][BM * 8]
-    i32x4* sB = lds + 2 * BM * 8;      // [2][BN * 8]
+// Per-tile DMA state: buffer descriptors and the byte offsets of this lane's
+// 16-byte chunks (four A and four B load instructions per stage).
+struct Dma {
+    __amdgpu_buffer_rsrc_t ra, rb0, rb1;
+    uint32_t va[4], vb[4];
+    uint32_t kvalid_last;   // valid K columns in the last stage (multiple of 8)
+    int nsteps;             // real stages
+};
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31;
-    const int n_valid = p.n_tiles[0] * p.NT;
-    const int L = xcd_remap(blockIdx.x, n_valid);
-    if (L < 0) return;
-    const int mt = L / p.NT, nt = L % p.NT;
-    const int4 td = p.tiles[mt];
-    const int g = td.x, row0 = td.y, M = td.z - td.y;
-    const bool shared = g == p.E;
-    const int K = shared ? p.K_shared : p.K_routed;
-    const int N = shared ? p.N_shared : p.N_routed;
-    const int n0 = MODE == 0 ? nt * (BN / 2) : nt * BN;
-    if (n0 >= N) return;
-    const int nrb = (M + 31) >> 5;
-
-    const uint16_t* A = shared ? p.a_shared : p.a_routed;
-    const size_t wmat = (size_t)K * (size_t)N;
-    const uint16_t* W0 = shared ? p.w0_shared : p.w0_routed + (size_t)g * wmat;
-    const uint16_t* W1 = MODE == 0 ? (shared ? p.w1_shared : p.w1_routed + (size_t)g * wmat) : nullptr;
-
-    // Global source of the 8 A chunks and 8 B chunks this thread stages.
-    const uint16_t* a_src[8];
-    const uint16_t* b_src[8];
-    bool a_ok[8], b_ok[8];
+template <int MODE, int BUF>
+__device__ __forceinline__ void dma_stage(const Dma& d, int t, int wave, int lane) {
+    i32x4* buf = ring<BUF>();
+    const bool real = t < d.nsteps;
+    const bool last = t == d.nsteps - 1;
+    const uint32_t kb = (uint32_t)t * (BK * 2);
+    const uint32_t logical8 = (uint32_t)(((lane & 3) ^ swz_of_row(lane >> 2)) * 8);
+    const bool tail_ok = !last || logical8 < d.kvalid_last;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int q = tid + NTH * i, r = q >> 3, c = q & 7;
-        a_ok[i] = r < M;
-        a_src[i] = A + (size_t)(row0 + (a_ok[i] ? r : 0)) * K + c * 8;
-        int col;
-        const uint16_t* Wm;
-        if (MODE == 0) {
-            const int wj = r >> 6, jj = r & 63;
-            col = n0 + wj * 32 + (jj & 31);
-            Wm = jj < 32 ? W0 : W1;
-        } else {
-            col = n0 + r;
-            Wm = W0;
-        }
-        b_ok[i] = col < N;
-        b_src[i] = Wm + (size_t)(b_ok[i] ? col : 0) * K + c * 8;
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t off = (real && tail_ok) ? d.va[i] + kb : kOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ra, (lds_t)(buf + (wave * 4 + i) * 64), 16, off, 0, 0, 0);
     }
-    const int ccol = (tid & 7) * 8;  // K offset of this thread's chunks inside a slice
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t off = (real && tail_ok) ? d.vb[i] + kb : kOOB;
+        const __amdgpu_buffer_rsrc_t r = (MODE == 0 && i >= 2) ? d.rb1 : d.rb0;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_t)(buf + kSlots + (wave * 4 + i) * 64), 16, off, 0, 0, 0);
+    }
+}
 
-    i32x4 ra[8], rb[8];
-    auto load = [&](int ks) {
-        const int kc = ks * BK;
-        const bool kin = kc + ccol < K;
+// MFMA fragments of one 16-wide k step (kk) of a stage: A rows r*32 + lane%32
+// and B rows wave*64 + {0, 32} + lane%32, at logical chunk 2*kk + lane/32.
+template <int NRB, int BUF, int KK>
+__device__ __forceinline__ void read_frags(int wave, int lane, i32x4 (&a)[NRB], i32x4 (&b)[2]) {
+    const i32x4* buf = ring<BUF>();
+    const int l32 = lane & 31, half = lane >> 5;
+    const int phys = (KK * 2 + half) ^ swz_of_row(l32);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            ra[i] = (a_ok[i] && kin) ? *reinterpret_cast<const i32x4*>(a_src[i] + kc) : i32x4{0, 0, 0, 0};
-            rb[i] = (b_ok[i] && kin) ? *reinterpret_cast<const i32x4*>(b_src[i] + kc) : i32x4{0, 0, 0, 0};
-        }
-    };
-    auto store = [&](int buf) {
+    for (int r = 0; r < NRB; ++r) a[r] = buf[(r * 32 + l32) * 4 + phys];
+    b[0] = buf[kSlots + (wave * 64 + l32) * 4 + phys];
+    b[1] = buf[kSlots + (wave * 64 + 32 + l32) * 4 + phys];
+}
+
+template <int NRB>
+__device__ __forceinline__ void mma(const i32x4 (&a)[NRB], const i32x4 (&b)[2], f32x16 (&acc0)[8],
+                                    f32x16 (&acc1)[8]) {
+    const bf16x8 b0 = __builtin_bit_cast(bf16x8, b[0]);
+    const bf16x8 b1 = __builtin_bit_cast(bf16x8, b[1]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int q = tid + NTH * i, r = q >> 3, c = q & 7;
-            sA[buf * BM * 8 + swz(r, c)] = ra[i];
-            sB[buf * BN * 8 + swz(r, c)] = rb[i];
-        }
-    };
+    for (int r = 0; r < NRB; ++r) {
+        const bf16x8 av = __builtin_bit_cast(bf16x8, a[r]);
+        acc0[r] = mfma32x32x16(av, b0, acc0[r]);
+        acc1[r] = mfma32x32x16(av, b1, acc1[r]);
+    }
+}
+
+// One pipeline stage (two 16-wide k steps) on stage s, held in buffer BUF.
+// Fragment set kk holds k step kk; entering, set 0 holds stage s, k step 0.
+template <int MODE, int NRB, int BUF>
+__device__ __forceinline__ void stage(const Dma& d, int s, int wave, int lane, i32x4 (&fa)[2][NRB],
+                                      i32x4 (&fb)[2][2], f32x16 (&acc0)[8], f32x16 (&acc1)[8]) {
+    // k step 0: read k step 1 of this stage while the MFMAs of k step 0 run
+    wait_lgkm0();
+    read_frags<NRB, BUF, 1>(wave, lane, fa[1], fb[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    mma<NRB>(fa[0], fb[0], acc0, acc1);
+    __builtin_amdgcn_sched_barrier(0);
+    // k step 1: hand buffer BUF back to the DMA and start on stage s+1
+    wait_lgkm0();     // every read of buffer BUF by this wave has returned
+    wait_vm<16>();    // this wave's loads of stage s+1 have landed (s+2, s+3 may be in flight)
+    barrier_lds();    // ... everybody's have, and everybody is done with buffer BUF
+    dma_stage<MODE, BUF>(d, s + NST, wave, lane);
+    read_frags<NRB, (BUF + 1) % NST, 0>(wave, lane, fa[0], fb[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    mma<NRB>(fa[1], fb[1], acc0, acc1);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int MODE, int NRB>
+__device__ __forceinline__ void run_tile(const GemmArgs& p, int g, int row0, int M, int n0, int K, int N,
+                                         bool shared) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l32 = lane & 31;
+
+    const uint16_t* A = (shared ? p.a_shared : p.a_routed) + (size_t)row0 * K;
+    const size_t wmat = (size_t)K * (size_t)N;
+    const uint16_t* W0 = (shared ? p.w0_shared : p.w0_routed + (size_t)g * wmat) + (size_t)n0 * K;
+    const uint16_t* W1 =
+        MODE == 0 ? (shared ? p.w1_shared : p.w1_routed + (size_t)g * wmat) + (size_t)n0 * K : nullptr;
+
+    Dma d;
+    d.nsteps = (K + BK - 1) / BK;
+    d.kvalid_last = (uint32_t)(K - (d.nsteps - 1) * BK);
+    d.ra = make_rsrc(A, (uint32_t)M * (uint32_t)K * 2u);
+    const int ncols = MODE == 0 ? min(BN / 2, N - n0) : min(BN, N - n0);
+    d.rb0 = make_rsrc(W0, (uint32_t)ncols * (uint32_t)K * 2u);
+    d.rb1 = MODE == 0 ? make_rsrc(W1, (uint32_t)ncols * (uint32_t)K * 2u) : d.rb0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = (wave * 4 + i) * 16 + (lane >> 2);
+        const uint32_t logical8 = (uint32_t)(((lane & 3) ^ swz_of_row(row)) * 8);
+        d.va[i] = row < M ? ((uint32_t)row * (uint32_t)K + logical8) * 2u : kOOB;
+        // B row of this chunk, relative to the tile's first weight row n0
+        const int bc = MODE == 0 ? wave * 32 + (i & 1) * 16 + (lane >> 2) : wave * 64 + i * 16 + (lane >> 2);
+        d.vb[i] = bc < ncols ? ((uint32_t)bc * (uint32_t)K + logical8) * 2u : kOOB;
+    }
 
     f32x16 acc0[8], acc1[8];
 #pragma unroll
@@ -125,32 +215,25 @@ ffn_gemm_bf16(GemmArgs p) {
         acc0[i] = f32x16{};
         acc1[i] = f32x16{};
     }
-    const int nsteps = (K + BK - 1) / BK;
-    load(0);
-    store(0);
-    __syncthreads();
-    for (int ks = 0; ks < nsteps; ++ks) {
-        const int buf = ks & 1;
-        if (ks + 1 < nsteps) load(ks + 1);
-        const i32x4* A_l = sA + buf * BM * 8;
-        const i32x4* B_l = sB + buf * BN * 8;
-#pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-            const int chunk = kk * 2 + (lane >> 5);
-            const bf16x8 b0 = __builtin_bit_cast(bf16x8, B_l[swz(wave * 64 + l32, chunk)]);
-            const bf16x8 b1 = __builtin_bit_cast(bf16x8, B_l[swz(wave * 64 + 32 + l32, chunk)]);
-#pragma unroll
-            for (int rbk = 0; rbk < 8; ++rbk) {
-                if (rbk < nrb) {
-                    const bf16x8 a = __builtin_bit_cast(bf16x8, A_l[swz(rbk * 32 + l32, chunk)]);
-                    acc0[rbk] = mfma32x32x16(a, b0, acc0[rbk]);
-                    acc1[rbk] = mfma32x32x16(a, b1, acc1[rbk]);
-                }
-            }
-        }
-        if (ks + 1 < nsteps) store(buf ^ 1);
-        __syncthreads();
+    i32x4 fa[2][NRB], fb[2][2];
+
+    dma_stage<MODE, 0>(d, 0, wave, lane);
+    dma_stage<MODE, 1>(d, 1, wave, lane);
+    dma_stage<MODE, 2>(d, 2, wave, lane);
+    dma_stage<MODE, 3>(d, 3, wave, lane);
+    wait_vm<24>();
+    barrier_lds();
+    read_frags<NRB, 0, 0>(wave, lane, fa[0], fb[0]);
+    // stages past the end load zeros, so the loop runs in whole turns of the ring
+    const int nsteps4 = (d.nsteps + NST - 1) & ~(NST - 1);
+    for (int s = 0; s < nsteps4; s += NST) {
+        stage<MODE, NRB, 0>(d, s, wave, lane, fa, fb, acc0, acc1);
+        stage<MODE, NRB, 1>(d, s + 1, wave, lane, fa, fb, acc0, acc1);
+        stage<MODE, NRB, 2>(d, s + 2, wave, lane, fa, fb, acc0, acc1);
+        stage<MODE, NRB, 3>(d, s + 3, wave, lane, fa, fb, acc0, acc1);
     }
+    wait_vm<0>();  // no LDS DMA may outlive the workgroup
+    wait_lgkm0();
 
     void* out = shared ? p.out_shared : p.out_routed;
     if (MODE == 0) {
@@ -158,42 +241,61 @@ ffn_gemm_bf16(GemmArgs p) {
         if (col < N) {
             uint16_t* h = static_cast<uint16_t*>(out);
 #pragma unroll
-            for (int rbk = 0; rbk < 8; ++rbk) {
-                if (rbk < nrb) {
+            for (int r = 0; r < NRB; ++r) {
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int r = rbk * 32 + c_row(i, lane);
-                        if (r < M) {
-                            const float gv = acc0[rbk][i], uv = acc1[rbk][i];
-                            h[(size_t)(row0 + r) * N + col] = f32_to_bf16(silu_f(gv) * uv);
-                        }
-                    }
+                for (int i = 0; i < 16; ++i) {
+                    const int row = r * 32 + c_row(i, lane);
+                    if (row < M) h[(size_t)(row0 + row) * N + col] = f32_to_bf16(silu_f(acc0[r][i]) * acc1[r][i]);
                 }
             }
         }
     } else {
         const int c0 = n0 + wave * 64 + l32, c1 = c0 + 32;
 #pragma unroll
-        for (int rbk = 0; rbk < 8; ++rbk) {
-            if (rbk < nrb) {
+        for (int r = 0; r < NRB; ++r) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int r = rbk * 32 + c_row(i, lane);
-                    if (r < M) {
-                        const size_t o = (size_t)(row0 + r) * N;
-                        if (p.out_f32) {
-                            float* y = static_cast<float*>(out);
-                            if (c0 < N) y[o + c0] = acc0[rbk][i];
-                            if (c1 < N) y[o + c1] = acc1[rbk][i];
-                        } else {
-                            uint16_t* y = static_cast<uint16_t*>(out);
-                            if (c0 < N) y[o + c0] = f32_to_bf16(acc0[rbk][i]);
-                            if (c1 < N) y[o + c1] = f32_to_bf16(acc1[rbk][i]);
-                        }
+            for (int i = 0; i < 16; ++i) {
+                const int row = r * 32 + c_row(i, lane);
+                if (row < M) {
+                    const size_t o = (size_t)(row0 + row) * N;
+                    if (p.out_f32) {
+                        float* y = static_cast<float*>(out);
+                        if (c0 < N) y[o + c0] = acc0[r][i];
+                        if (c1 < N) y[o + c1] = acc1[r][i];
+                    } else {
+                        uint16_t* y = static_cast<uint16_t*>(out);
+                        if (c0 < N) y[o + c0] = f32_to_bf16(acc0[r][i]);
+                        if (c1 < N) y[o + c1] = f32_to_bf16(acc1[r][i]);
                     }
                 }
             }
         }
+    }
+}
+
+template <int MODE>
+__global__ void __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1)))
+ffn_gemm_bf16(GemmArgs p) {
+    const int L = xcd_remap(blockIdx.x, p.n_tiles[0] * p.NT);
+    if (L < 0) return;
+    const int2 wl = p.work[L];
+    const int mt = wl.x, nt = wl.y;
+    const int4 td = p.tiles[mt];
+    const int g = td.x, row0 = td.y, M = td.z - td.y;
+    const bool shared = g == p.E;
+    const int K = shared ? p.K_shared : p.K_routed;
+    const int N = shared ? p.N_shared : p.N_routed;
+    const int n0 = MODE == 0 ? nt * (BN / 2) : nt * BN;
+    if (n0 >= N || M <= 0) return;
+    switch ((M + 31) >> 5) {
+    case 1: run_tile<MODE, 1>(p, g, row0, M, n0, K, N, shared); break;
+    case 2: run_tile<MODE, 2>(p, g, row0, M, n0, K, N, shared); break;
+    case 3: run_tile<MODE, 3>(p, g, row0, M, n0, K, N, shared); break;
+    case 4: run_tile<MODE, 4>(p, g, row0, M, n0, K, N, shared); break;
+    case 5: run_tile<MODE, 5>(p, g, row0, M, n0, K, N, shared); break;
+    case 6: run_tile<MODE, 6>(p, g, row0, M, n0, K, N, shared); break;
+    case 7: run_tile<MODE, 7>(p, g, row0, M, n0, K, N, shared); break;
+    default: run_tile<MODE, 8>(p, g, row0, M, n0, K, N, shared); break;
     }
 }
 
@@ -203,10 +305,14 @@ ffn_gemm_bf16(GemmArgs p) {
 // One workgroup of 1024 threads.  Group g < E covers rows [offsets[g],
 // offsets[g+1]); group E (the shared expert, when present) covers tokens
 // [0, T).  A group of n rows gets nmt = ceil(n / bm) tiles of height
-// ceil(ceil(n / nmt) / 32) * 32 (the last one shorter).
+// ceil(ceil(n / nmt) / 32) * 32 (the last one shorter).  The work lists put,
+// for each group, N tile by N tile, all its M tiles next to each other: the M
+// tiles of one expert that share a weight panel run side by side on one XCD,
+// so the panel streams from HBM once and the second reader hits L2.
 __global__ void __launch_bounds__(1024)
 ffn_build_tiles(const int32_t* __restrict__ offsets, int E, int has_shared, int T, int bm, int rows_cap,
-                int4* __restrict__ tiles, int32_t* __restrict__ n_tiles) {
+                int4* __restrict__ tiles, int32_t* __restrict__ n_tiles, int2* __restrict__ work1, int nt1,
+                int2* __restrict__ work2, int nt2) {
     __shared__ int32_t wsum[16];
     const int G = E + has_shared;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -250,6 +356,10 @@ ffn_build_tiles(const int32_t* __restrict__ offsets, int E, int has_shared, int 
             const int re = min(e, rb + hgt);
             tiles[st + m] = int4{g, rb, re, 0};
         }
+        for (int nt = 0; nt < nt1; ++nt)
+            for (int m = 0; m < nmt; ++m) work1[st * nt1 + nt * nmt + m] = int2{st + m, nt};
+        for (int nt = 0; nt < nt2; ++nt)
+            for (int m = 0; m < nmt; ++m) work2[st * nt2 + nt * nmt + m] = int2{st + m, nt};
     };
     if (tid < G) emit(tid, b0, e0, n0, start);
     if (tid == 0 && G > 1024) {
@@ -263,31 +373,23 @@ ffn_build_tiles(const int32_t* __restrict__ offsets, int E, int has_shared, int 
 }
 
 hipError_t launch_build_tiles(const moe_cfg& c, const int32_t* offsets, int bm, int64_t rows_cap,
-                              int32_t* tiles, int32_t* n_tiles, hipStream_t s) {
+                              const FfnWork& wk, hipStream_t s) {
     hipLaunchKernelGGL(ffn_build_tiles, dim3(1), dim3(1024), 0, s, offsets, c.E, c.has_shared ? 1 : 0, c.T,
-                       bm, (int)rows_cap, reinterpret_cast<int4*>(tiles), n_tiles);
+                       bm, (int)rows_cap, reinterpret_cast<int4*>(wk.tiles), wk.n_tiles,
+                       reinterpret_cast<int2*>(wk.work1), wk.nt1, reinterpret_cast<int2*>(wk.work2), wk.nt2);
     return hipGetLastError();
 }
 
-hipError_t launch_gemm_bf16(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_cap, const void* x_rows, const int32_t* offsets,
-                            const moe_weights& w, const void* x_tokens, void* y_rows, void* y_shared,
-                            int32_t* tiles, int32_t* n_tiles, void* h, void* h_sh, hipStream_t s) {
-    static bool attr_done = false;
-    if (!attr_done) {
-        hipError_t e1 = hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_gemm_bf16<0>),
-                                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-        hipError_t e2 = hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_gemm_bf16<1>),
-                                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-        if (e1 != hipSuccess) return e1;
-        if (e2 != hipSuccess) return e2;
-        attr_done = true;
-    }
+hipError_t launch_gemm_bf16(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_cap, const void* x_rows,
+                            const int32_t* offsets, const moe_weights& w, const void* x_tokens, void* y_rows,
+                            void* y_shared, const FfnWork& wk, void* h, void* h_sh, hipStream_t s) {
     const int has_sh = c.has_shared ? 1 : 0;
-    hipError_t e0 = launch_build_tiles(c, offsets, BM, n_rows_cap, tiles, n_tiles, s);
+    hipError_t e0 = launch_build_tiles(c, offsets, BM, n_rows_cap, wk, s);
     if (e0 != hipSuccess) return e0;
     GemmArgs a{};
-    a.tiles = reinterpret_cast<const int4*>(tiles);
-    a.n_tiles = n_tiles;
+    a.tiles = reinterpret_cast<const int4*>(wk.tiles);
+    a.n_tiles = wk.n_tiles;
+    a.work = reinterpret_cast<const int2*>(wk.work1);
     a.E = c.E;
     // GEMM1: gate/up + SwiGLU -> h
     a.a_routed = static_cast<const uint16_t*>(x_rows);
@@ -302,10 +404,9 @@ hipError_t launch_gemm_bf16(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_
     a.K_shared = c.H;
     a.N_routed = c.I;
     a.N_shared = has_sh ? c.I_shared : c.I;
-    const int nmax1 = has_sh ? (c.I > c.I_shared ? c.I : c.I_shared) : c.I;
-    a.NT = (nmax1 + BN / 2 - 1) / (BN / 2);
+    a.NT = wk.nt1;
     a.out_f32 = 0;
-    hipLaunchKernelGGL(ffn_gemm_bf16<0>, dim3((unsigned)(max_tiles * a.NT)), dim3(NTH), kLdsBytes, s, a);
+    hipLaunchKernelGGL(ffn_gemm_bf16<0>, dim3((unsigned)(max_tiles * a.NT)), dim3(NTH), 0, s, a);
     // GEMM2: down -> y
     a.a_routed = static_cast<const uint16_t*>(h);
     a.a_shared = static_cast<const uint16_t*>(h_sh);
@@ -319,9 +420,10 @@ hipError_t launch_gemm_bf16(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_
     a.K_shared = has_sh ? c.I_shared : c.I;
     a.N_routed = c.H;
     a.N_shared = c.H;
-    a.NT = (c.H + BN - 1) / BN;
+    a.NT = wk.nt2;
+    a.work = reinterpret_cast<const int2*>(wk.work2);
     a.out_f32 = c.y_dtype == MOE_F32;
-    hipLaunchKernelGGL(ffn_gemm_bf16<1>, dim3((unsigned)(max_tiles * a.NT)), dim3(NTH), kLdsBytes, s, a);
+    hipLaunchKernelGGL(ffn_gemm_bf16<1>, dim3((unsigned)(max_tiles * a.NT)), dim3(NTH), 0, s, a);
     return hipGetLastError();
 }
 

@@ -22,6 +22,7 @@ struct F32Args {
     void* out_shared;
     const int4* tiles;
     const int32_t* n_tiles;
+    const int2* work;
     int E, NT, K_routed, K_shared, N_routed, N_shared, out_f32;
 };
 
@@ -33,7 +34,8 @@ __global__ void __launch_bounds__(256) ffn_gemm_f32(F32Args p) {
     const int n_valid = p.n_tiles[0] * p.NT;
     const int L = blockIdx.x;
     if (L >= n_valid) return;
-    const int mt = L / p.NT, nt = L % p.NT;
+    const int2 wl = p.work[L];
+    const int mt = wl.x, nt = wl.y;
     const int4 td = p.tiles[mt];
     const int g = td.x, row0 = td.y, M = td.z - td.y;
     const bool shared = g == p.E;
@@ -94,15 +96,16 @@ __global__ void __launch_bounds__(256) ffn_gemm_f32(F32Args p) {
 
 }  // namespace
 
-hipError_t launch_gemm_f32(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_cap, const void* x_rows, const int32_t* offsets,
-                           const moe_weights& w, const void* x_tokens, void* y_rows, void* y_shared,
-                           int32_t* tiles, int32_t* n_tiles, void* h, void* h_sh, hipStream_t s) {
+hipError_t launch_gemm_f32(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_cap, const void* x_rows,
+                           const int32_t* offsets, const moe_weights& w, const void* x_tokens, void* y_rows,
+                           void* y_shared, const FfnWork& wk, void* h, void* h_sh, hipStream_t s) {
     const int has_sh = c.has_shared ? 1 : 0;
-    hipError_t e0 = launch_build_tiles(c, offsets, TB, n_rows_cap, tiles, n_tiles, s);
+    hipError_t e0 = launch_build_tiles(c, offsets, TB, n_rows_cap, wk, s);
     if (e0 != hipSuccess) return e0;
     F32Args a{};
-    a.tiles = reinterpret_cast<const int4*>(tiles);
-    a.n_tiles = n_tiles;
+    a.tiles = reinterpret_cast<const int4*>(wk.tiles);
+    a.n_tiles = wk.n_tiles;
+    a.work = reinterpret_cast<const int2*>(wk.work1);
     a.E = c.E;
     a.a_routed = static_cast<const float*>(x_rows);
     a.a_shared = static_cast<const float*>(x_tokens);
@@ -116,8 +119,7 @@ hipError_t launch_gemm_f32(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_c
     a.K_shared = c.H;
     a.N_routed = c.I;
     a.N_shared = has_sh ? c.I_shared : c.I;
-    const int nmax1 = has_sh ? (c.I > c.I_shared ? c.I : c.I_shared) : c.I;
-    a.NT = (nmax1 + TB - 1) / TB;
+    a.NT = wk.nt1;
     a.out_f32 = 1;
     hipLaunchKernelGGL(ffn_gemm_f32<0>, dim3((unsigned)(max_tiles * a.NT)), dim3(256), 0, s, a);
     a.a_routed = static_cast<const float*>(h);
@@ -132,7 +134,8 @@ hipError_t launch_gemm_f32(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_c
     a.K_shared = has_sh ? c.I_shared : c.I;
     a.N_routed = c.H;
     a.N_shared = c.H;
-    a.NT = (c.H + TB - 1) / TB;
+    a.NT = wk.nt2;
+    a.work = reinterpret_cast<const int2*>(wk.work2);
     a.out_f32 = c.y_dtype == MOE_F32;
     hipLaunchKernelGGL(ffn_gemm_f32<1>, dim3((unsigned)(max_tiles * a.NT)), dim3(256), 0, s, a);
     return hipGetLastError();

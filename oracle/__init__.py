@@ -51,6 +51,8 @@ def lib():
         L = ctypes.CDLL(_SO)
         P = ctypes.c_void_p
         i64, i32, dbl = ctypes.c_int64, ctypes.c_int, ctypes.c_double
+        L.orc_threads.argtypes = []
+        L.orc_threads.restype = i32
         L.orc_bf16_to_f64.argtypes = [ctypes.c_uint16]
         L.orc_bf16_to_f64.restype = dbl
         L.orc_e4m3_to_f64.argtypes = [ctypes.c_uint8]
@@ -96,6 +98,11 @@ def _dtype_code(a: np.ndarray) -> int:
 
 def _c(a):
     return None if a is None else np.ascontiguousarray(a)
+
+
+def threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(lib().orc_threads())
 
 
 # ---------------------------------------------------------------- formats

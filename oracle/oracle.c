@@ -40,6 +40,7 @@
  *    kernels use.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -47,6 +48,9 @@
 #define ORC_F32 0
 #define ORC_BF16 1
 #define ORC_E4M3 2
+
+/* Threads an OpenMP loop of the oracle runs on (for reporting). */
+int orc_threads(void) { return omp_get_max_threads(); }
 
 /* ---------------------------------------------------------------- formats */
 
