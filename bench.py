@@ -46,6 +46,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="c3_dsv3_bf16")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--rowmajor-weights", action="store_true",
+                   help="time the row-major weight layout instead of the tiled one")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     return p.parse_args()
 
@@ -89,6 +91,13 @@ def main():
         wg[e], wu[e], wd[e] = synth.expert_weights(s, e, dev)
     sh = synth.shared_weights(s, dev) if s.shared else (None, None, None)
     w = moe.weights(wg, wu, wd, sh_gate=sh[0], sh_up=sh[1], sh_down=sh[2])
+    tiled_buf = None
+    if not a.rowmajor_weights:
+        # weights are static: tiled once at load time, outside the timed region
+        w, tiled_buf = moe.tile_weights(c, w, dev)
+        del wg, wu, wd, sh
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     ws = moe.workspace(c, moe.MOE_STAGE_LAYER, dev)
     torch.cuda.synchronize()
@@ -193,7 +202,7 @@ def main():
                 "kernel": "moe_grouped_ffn (ffn_gemm_bf16<0> gate/up+SwiGLU, ffn_gemm_bf16<1> down, tile list)",
                 "flop_per_launch": ffn_flop}
 
-    cpu = None if a.no_cpu_baseline else cpu_baseline(s, x, w_r, wg, wu, wd, a.cpu_seconds)
+    cpu = None if a.no_cpu_baseline else cpu_baseline(s, x, w_r, a.cpu_seconds)
 
     sclk = None
     try:
@@ -211,7 +220,8 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": a.workload, "T": T, "H": H, "E": E, "k": k, "I": I, "shared_experts": int(s.shared),
                    "I_shared": I_sh, "router": s.score, "n_groups": s.n_groups, "topk_groups": s.topk_groups,
-                   "routed_scale": s.routed_scale, "out_dtype": "bf16", "expert_out_dtype": "fp32"},
+                   "routed_scale": s.routed_scale, "out_dtype": "bf16", "expert_out_dtype": "fp32",
+                   "weight_layout": "row-major" if a.rowmajor_weights else "tiled"},
         "tokens_per_s": round(T / (ms_step * 1e-3), 1),
         "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
         "layer_flop": layer_flop,
@@ -224,7 +234,7 @@ def main():
     print(json.dumps(res), flush=True)
 
 
-def cpu_baseline(s, x, w_r, wg, wu, wd, target_s):
+def cpu_baseline(s, x, w_r, target_s):
     """The oracle as it stands on the host cores: router logits + gating and one
     routed expert's SwiGLU FFN for a sample of token rows (the per-row
     arithmetic of the layer), sized to about target_s seconds; reported in
@@ -237,8 +247,10 @@ def cpu_baseline(s, x, w_r, wg, wu, wd, target_s):
     def bits(t):
         return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
 
+    import synth
+
     wh = bits(w_r)
-    g, u, d = bits(wg[0]), bits(wu[0]), bits(wd[0])
+    g, u, d = (bits(t) for t in synth.expert_weights(s, 0, "cpu"))
     per_row = 2.0 * s.H * s.E + 6.0 * s.H * s.I
 
     def run(n):

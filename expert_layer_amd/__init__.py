@@ -21,7 +21,7 @@ from . import _ffi
 from ._ffi import (MOE_BF16, MOE_ERR_HIP, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE,
                    MOE_F32, MOE_FP8_E4M3, MOE_GROUP_MAX, MOE_GROUP_TOP2_SUM, MOE_OK, MOE_SCORE_SIGMOID,
                    MOE_SCORE_SOFTMAX, MOE_STAGE_FFN, MOE_STAGE_LAYER, MOE_STAGE_PERMUTE, MOE_STAGE_ROUTE,
-                   moe_cfg, moe_weights)
+                   MOE_LAYOUT_ROWMAJOR, MOE_LAYOUT_TILED, moe_cfg, moe_weights)
 
 __all__ = [
     "MoeError", "make_cfg", "weights", "workspace", "moe_validate", "moe_max_rows", "moe_workspace_bytes", "moe_ffn_workspace_bytes",
@@ -30,7 +30,8 @@ __all__ = [
     "MOE_OK", "MOE_ERR_INVALID_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE", "MOE_ERR_HIP",
     "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3", "MOE_SCORE_SOFTMAX", "MOE_SCORE_SIGMOID",
     "MOE_GROUP_TOP2_SUM", "MOE_GROUP_MAX", "MOE_STAGE_ROUTE", "MOE_STAGE_PERMUTE", "MOE_STAGE_FFN",
-    "MOE_STAGE_LAYER",
+    "MOE_STAGE_LAYER", "MOE_LAYOUT_ROWMAJOR", "MOE_LAYOUT_TILED", "moe_tiled_weights_bytes",
+    "moe_tile_weights", "tile_weights",
 ]
 
 lib_path = _ffi.LIB_PATH
@@ -88,9 +89,29 @@ def _check(status: int):
 
 
 def weights(w_gate, w_up, w_down, s_gate=None, s_up=None, s_down=None, sh_gate=None, sh_up=None,
-            sh_down=None) -> moe_weights:
+            sh_down=None, layout: int = MOE_LAYOUT_ROWMAJOR) -> moe_weights:
     return moe_weights(*(_ptr(t) for t in (w_gate, w_up, w_down, s_gate, s_up, s_down, sh_gate,
-                                             sh_up, sh_down)))
+                                             sh_up, sh_down)), layout)
+
+
+def moe_tiled_weights_bytes(cfg: moe_cfg) -> int:
+    return _ffi.lib().moe_tiled_weights_bytes(ctypes.byref(cfg))
+
+
+def moe_tile_weights(cfg: moe_cfg, src: moe_weights, dst, stream=None) -> moe_weights:
+    """Writes the tiled copy of row-major bf16 weights into the device buffer dst
+    and returns the moe_weights that point into it (keep dst alive)."""
+    out = moe_weights()
+    _check(_ffi.lib().moe_tile_weights(ctypes.byref(cfg), ctypes.byref(src), _ptr(dst),
+                                       dst.numel() * dst.element_size(), ctypes.byref(out), _stream(stream)))
+    return out
+
+
+def tile_weights(cfg: moe_cfg, src: moe_weights, device):
+    """(tiled moe_weights, owning byte buffer): allocates the buffer (torch) and
+    calls moe_tile_weights on the current stream."""
+    buf = torch.empty(max(moe_tiled_weights_bytes(cfg), 1), dtype=torch.uint8, device=device)
+    return moe_tile_weights(cfg, src, buf), buf
 
 
 def moe_validate(cfg: moe_cfg) -> int:

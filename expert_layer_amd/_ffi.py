@@ -16,9 +16,11 @@ MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_GROUP_TOP2_SUM, MOE_GROUP_MAX = 0, 1
 MOE_STAGE_ROUTE, MOE_STAGE_PERMUTE, MOE_STAGE_FFN, MOE_STAGE_LAYER = 0, 1, 2, 3
+MOE_LAYOUT_ROWMAJOR, MOE_LAYOUT_TILED = 0, 1
 
-EXPORTS = ("moe_validate", "moe_max_rows", "moe_workspace_bytes", "moe_ffn_workspace_bytes", "moe_route", "moe_permute",
-           "moe_grouped_ffn", "moe_combine", "moe_layer", "moe_status_string", "moe_last_error")
+EXPORTS = ("moe_validate", "moe_max_rows", "moe_workspace_bytes", "moe_ffn_workspace_bytes",
+           "moe_tiled_weights_bytes", "moe_tile_weights", "moe_route", "moe_permute", "moe_grouped_ffn",
+           "moe_combine", "moe_layer", "moe_status_string", "moe_last_error")
 
 
 class moe_cfg(ctypes.Structure):
@@ -31,7 +33,7 @@ class moe_cfg(ctypes.Structure):
 
 class moe_weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down",
-                                               "sh_gate", "sh_up", "sh_down")]
+                                               "sh_gate", "sh_up", "sh_down")] + [("layout", ctypes.c_int32)]
 
 
 _lib = None
@@ -55,6 +57,10 @@ def lib() -> ctypes.CDLL:
         L.moe_workspace_bytes.restype = sz
         L.moe_ffn_workspace_bytes.argtypes = [C, i64]
         L.moe_ffn_workspace_bytes.restype = sz
+        L.moe_tiled_weights_bytes.argtypes = [C]
+        L.moe_tiled_weights_bytes.restype = sz
+        L.moe_tile_weights.argtypes = [C, W, P, sz, W, P]
+        L.moe_tile_weights.restype = i32
         L.moe_route.argtypes = [C, P, P, P, P, P, P, P, P, sz, P]
         L.moe_route.restype = i32
         L.moe_permute.argtypes = [C, P, P, P, P, P, P, P, P, P, P, sz, P]

@@ -121,9 +121,9 @@ PermuteCarve permute_carve(const moe_cfg& c, void* p) {
 
 struct FfnCarve {
     moe::FfnWork wk;
-    void* h;
-    float* h_scale;
-    void* h_sh;
+    void* h;         // bf16: the h tile slots (max_tiles x 256 rows, tiled); fp32: [n_rows_cap][I]
+    float* h_scale;  // fp8: [n_rows_cap][I / 128]
+    void* h_sh;      // fp32: [T][I_shared]
     int64_t max_tiles;
     size_t bytes;
 };
@@ -140,12 +140,41 @@ FfnCarve ffn_carve(const moe_cfg& c, int64_t n_rows_cap, void* p) {
     f.wk.n_tiles = cv.take<int32_t>(1);
     f.wk.work1 = cv.take<int32_t>((size_t)f.max_tiles * f.wk.nt1 * 2);
     f.wk.work2 = cv.take<int32_t>((size_t)f.max_tiles * f.wk.nt2 * 2);
-    const int hb = c.act_dtype == MOE_F32 ? 4 : (c.act_dtype == MOE_BF16 ? 2 : 1);
-    f.h = cv.take<char>((size_t)n_rows_cap * c.I * hb);
-    f.h_scale = c.act_dtype == MOE_FP8_E4M3 ? cv.take<float>((size_t)n_rows_cap * (c.I / 128)) : nullptr;
-    f.h_sh = c.has_shared ? cv.take<char>((size_t)c.T * c.I_shared * hb) : nullptr;
+    if (c.act_dtype == MOE_BF16) {
+        f.h = cv.take<char>((size_t)f.max_tiles * moe::h_slot_bytes(c));
+    } else {
+        const int hb = f32 ? 4 : 1;
+        f.h = cv.take<char>((size_t)n_rows_cap * c.I * hb);
+        f.h_scale = c.act_dtype == MOE_FP8_E4M3 ? cv.take<float>((size_t)n_rows_cap * (c.I / 128)) : nullptr;
+        f.h_sh = c.has_shared ? cv.take<char>((size_t)c.T * c.I_shared * hb) : nullptr;
+    }
     f.bytes = cv.off;
     return f;
+}
+
+// The layer path pads expert segments to 16 rows; for bf16 the permuted rows
+// are tiled and the shared expert's copy of the tokens follows the routed rows.
+struct LayerGeom {
+    moe_cfg c16;        // cfg with m_tile = 16
+    int64_t rows;       // routed rows (max_rows of c16)
+    int64_t rows_pad;   // rounded up to 16: first row of the shared-expert copy
+    bool tiled;
+    size_t x_perm_bytes;
+};
+LayerGeom layer_geom(const moe_cfg& c) {
+    LayerGeom g{};
+    g.c16 = c;
+    g.c16.m_tile = 16;
+    g.rows = max_rows_of(g.c16);
+    g.rows_pad = (g.rows + 15) / 16 * 16;
+    g.tiled = c.act_dtype == MOE_BF16;
+    if (g.tiled) {
+        const int64_t all = g.rows_pad + (c.has_shared ? (c.T + 15) / 16 * 16 : 0);
+        g.x_perm_bytes = (size_t)(all / 16) * ((c.H + 31) / 32) * 1024;
+    } else {
+        g.x_perm_bytes = (size_t)g.rows * c.H * dtype_bytes(c.act_dtype);
+    }
+    return g;
 }
 
 struct LayerCarve {
@@ -157,20 +186,20 @@ struct LayerCarve {
 LayerCarve layer_carve(const moe_cfg& c, void* p) {
     Carve cv(p);
     LayerCarve l{};
-    const int64_t rows = max_rows_of(c);
+    const LayerGeom g = layer_geom(c);
     const size_t tk = (size_t)c.T * c.k;
     l.ids = cv.take<int32_t>(tk);
     l.topk_w = cv.take<float>(tk);
     l.counts = cv.take<int32_t>(c.E);
     l.offsets = cv.take<int32_t>(c.E + 1);
-    l.row_src = cv.take<int32_t>((size_t)rows);
+    l.row_src = cv.take<int32_t>((size_t)g.rows);
     l.tok_row = cv.take<int32_t>(tk);
-    l.x_perm = cv.take<char>((size_t)rows * c.H * dtype_bytes(c.act_dtype));
-    l.y_rows = cv.take<char>((size_t)rows * c.H * dtype_bytes(c.y_dtype));
+    l.x_perm = cv.take<char>(g.x_perm_bytes);
+    l.y_rows = cv.take<char>((size_t)g.rows * c.H * dtype_bytes(c.y_dtype));
     l.y_shared = c.has_shared ? cv.take<char>((size_t)c.T * c.H * dtype_bytes(c.y_dtype)) : nullptr;
     size_t scratch = route_ws(c);
     size_t pb = permute_carve(c, nullptr).bytes;
-    size_t fb = ffn_carve(c, rows, nullptr).bytes;
+    size_t fb = ffn_carve(g.c16, g.rows, nullptr).bytes;
     if (pb > scratch) scratch = pb;
     if (fb > scratch) scratch = fb;
     l.scratch = cv.take<char>(scratch);
@@ -189,18 +218,39 @@ moe_status check_ws(void* ws, size_t have, size_t need) {
 #define REQUIRE(p, name) \
     if (!(p)) return fail(MOE_ERR_INVALID_ARG, "%s is NULL", name)
 
-moe_status ffn_enqueue(const moe_cfg& c, int64_t n_rows_cap, const void* x_rows, const float* x_scale,
-                       const int32_t* offsets, const moe_weights& w, const void* x_tokens, void* y_rows,
-                       void* y_shared, void* ws, hipStream_t s) {
+// Checks the weight pointers a call reads (before anything is enqueued).
+moe_status check_weights(const moe_cfg& c, const moe_weights* w) {
+    if (!w) return fail(MOE_ERR_INVALID_ARG, "w is NULL");
+    if (w->layout != MOE_LAYOUT_ROWMAJOR && w->layout != MOE_LAYOUT_TILED)
+        return fail(MOE_ERR_INVALID_ARG, "w->layout=%d", w->layout);
+    const bool tiled = w->layout == MOE_LAYOUT_TILED;
+    if (tiled && c.act_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "tiled weights are bf16 only");
+    REQUIRE(w->w_gate, "w->w_gate");
+    if (!tiled) REQUIRE(w->w_up, "w->w_up");
+    REQUIRE(w->w_down, "w->w_down");
+    if (c.act_dtype == MOE_FP8_E4M3) {
+        REQUIRE(w->s_gate, "w->s_gate");
+        REQUIRE(w->s_up, "w->s_up");
+        REQUIRE(w->s_down, "w->s_down");
+    }
+    if (c.has_shared) {
+        REQUIRE(w->sh_gate, "w->sh_gate");
+        if (!tiled) REQUIRE(w->sh_up, "w->sh_up");
+        REQUIRE(w->sh_down, "w->sh_down");
+    }
+    return MOE_OK;
+}
+
+moe_status ffn_enqueue(const moe_cfg& c, int64_t n_rows_cap, const moe::FfnOperands& op, const float* x_scale,
+                       const int32_t* offsets, const moe_weights& w, void* ws, hipStream_t s) {
     (void)x_scale;
     FfnCarve f = ffn_carve(c, n_rows_cap, ws);
     hipError_t e;
     if (c.act_dtype == MOE_BF16)
-        e = moe::launch_gemm_bf16(c, f.max_tiles, n_rows_cap, x_rows, offsets, w, x_tokens, y_rows, y_shared, f.wk,
-                                  f.h, f.h_sh, s);
+        e = moe::launch_gemm_bf16(c, f.max_tiles, n_rows_cap, op, offsets, w, f.wk, f.h, s);
     else if (c.act_dtype == MOE_F32)
-        e = moe::launch_gemm_f32(c, f.max_tiles, n_rows_cap, x_rows, offsets, w, x_tokens, y_rows, y_shared, f.wk,
-                                 f.h, f.h_sh, s);
+        e = moe::launch_gemm_f32(c, f.max_tiles, n_rows_cap, op.x_rows, offsets, w, op.x_tokens, op.y_rows,
+                                 op.y_shared, f.wk, f.h, f.h_sh, s);
     else
         return fail(MOE_ERR_UNSUPPORTED, "fp8 grouped FFN is not built");
     if (e != hipSuccess) return hip_fail(e, "moe_grouped_ffn");
@@ -292,7 +342,8 @@ moe_status moe_permute(const moe_cfg* cfg, const void* x, const float* x_scale, 
     if ((st = check_ws(ws, ws_bytes, pc.bytes)) != MOE_OK) return st;
     if (c.T == 0) return MOE_OK;
     hipError_t e = moe::launch_permute(c, x, x_scale, topk_ids, expert_counts, expert_offsets, row_src, tok_row,
-                                       x_perm, x_perm_scale, max_rows_of(c), pc.ws, static_cast<hipStream_t>(stream));
+                                       x_perm, x_perm_scale, max_rows_of(c), pc.ws, moe::PermuteLayout{0, -1},
+                                       static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "moe_permute");
     return MOE_OK;
 }
@@ -305,34 +356,58 @@ moe_status moe_grouped_ffn(const moe_cfg* cfg, int64_t n_rows_cap, const void* x
     const moe_cfg& c = *cfg;
     if (n_rows_cap < 0 || n_rows_cap > kMaxRows)
         return fail(MOE_ERR_INVALID_ARG, "n_rows_cap=%lld must be in [0, 2^30)", (long long)n_rows_cap);
-    REQUIRE(w, "w");
     REQUIRE(expert_offsets, "expert_offsets");
-    REQUIRE(w->w_gate, "w->w_gate");
-    REQUIRE(w->w_up, "w->w_up");
-    REQUIRE(w->w_down, "w->w_down");
+    if ((st = check_weights(c, w)) != MOE_OK) return st;
     if (n_rows_cap > 0) {
         REQUIRE(x_rows, "x_rows");
         REQUIRE(y_rows, "y_rows");
     }
-    if (c.act_dtype == MOE_FP8_E4M3) {
-        REQUIRE(x_scale, "x_scale");
-        REQUIRE(w->s_gate, "w->s_gate");
-        REQUIRE(w->s_up, "w->s_up");
-        REQUIRE(w->s_down, "w->s_down");
-    }
+    if (c.act_dtype == MOE_FP8_E4M3) REQUIRE(x_scale, "x_scale");
     if (c.has_shared) {
         REQUIRE(x_tokens, "x_tokens");
         REQUIRE(y_shared, "y_shared");
-        REQUIRE(w->sh_gate, "w->sh_gate");
-        REQUIRE(w->sh_up, "w->sh_up");
-        REQUIRE(w->sh_down, "w->sh_down");
     }
     if (c.act_dtype == MOE_FP8_E4M3) return fail(MOE_ERR_UNSUPPORTED, "fp8 grouped FFN is not built");
     const size_t need = ffn_carve(c, n_rows_cap, nullptr).bytes;
     if ((st = check_ws(ws, ws_bytes, need)) != MOE_OK) return st;
     if (n_rows_cap == 0 && !(c.has_shared && c.T > 0)) return MOE_OK;
-    return ffn_enqueue(c, n_rows_cap, x_rows, x_scale, expert_offsets, *w, x_tokens, y_rows, y_shared, ws,
-                       static_cast<hipStream_t>(stream));
+    moe::FfnOperands op{x_rows, x_tokens, 0, 0, y_rows, y_shared};
+    return ffn_enqueue(c, n_rows_cap, op, x_scale, expert_offsets, *w, ws, static_cast<hipStream_t>(stream));
+}
+
+size_t moe_tiled_weights_bytes(const moe_cfg* cfg) {
+    if (check_cfg(cfg) != MOE_OK) return (size_t)-1;
+    const moe::TiledSizes t = moe::tiled_sizes(*cfg);
+    return align_up(t.w13) + align_up(t.w2) + align_up(t.sh13) + align_up(t.sh2);
+}
+
+moe_status moe_tile_weights(const moe_cfg* cfg, const moe_weights* src, void* dst, size_t dst_bytes,
+                            moe_weights* tiled, void* stream) {
+    moe_status st = check_cfg(cfg);
+    if (st != MOE_OK) return st;
+    const moe_cfg& c = *cfg;
+    if (c.act_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "tiled weights are bf16 only");
+    if ((st = check_weights(c, src)) != MOE_OK) return st;
+    if (src->layout != MOE_LAYOUT_ROWMAJOR) return fail(MOE_ERR_INVALID_ARG, "src must be row-major");
+    REQUIRE(tiled, "tiled");
+    const moe::TiledSizes t = moe::tiled_sizes(c);
+    const size_t need = align_up(t.w13) + align_up(t.w2) + align_up(t.sh13) + align_up(t.sh2);
+    if ((st = check_ws(dst, dst_bytes, need)) != MOE_OK) return st;
+    char* base = static_cast<char*>(dst);
+    void* w13 = base;
+    void* w2 = base + align_up(t.w13);
+    void* sh13 = c.has_shared ? base + align_up(t.w13) + align_up(t.w2) : nullptr;
+    void* sh2 = c.has_shared ? base + align_up(t.w13) + align_up(t.w2) + align_up(t.sh13) : nullptr;
+    hipError_t e = moe::launch_tile_weights(c, *src, w13, w2, sh13, sh2, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "moe_tile_weights");
+    moe_weights o{};
+    o.w_gate = w13;
+    o.w_down = w2;
+    o.sh_gate = sh13;
+    o.sh_down = sh2;
+    o.layout = MOE_LAYOUT_TILED;
+    *tiled = o;
+    return MOE_OK;
 }
 
 moe_status moe_combine(const moe_cfg* cfg, const void* y_rows, const int32_t* tok_row, const float* topk_w,
@@ -357,30 +432,35 @@ moe_status moe_layer(const moe_cfg* cfg, const void* w_router, const float* bias
     const moe_cfg& c = *cfg;
     if (c.act_dtype == MOE_FP8_E4M3) return fail(MOE_ERR_UNSUPPORTED, "moe_layer on fp8 activations");
     REQUIRE(w_router, "w_router");
-    REQUIRE(w, "w");
-    REQUIRE(w->w_gate, "w->w_gate");
-    REQUIRE(w->w_up, "w->w_up");
-    REQUIRE(w->w_down, "w->w_down");
-    if (c.has_shared) {
-        REQUIRE(w->sh_gate, "w->sh_gate");
-        REQUIRE(w->sh_up, "w->sh_up");
-        REQUIRE(w->sh_down, "w->sh_down");
-    }
+    if ((st = check_weights(c, w)) != MOE_OK) return st;
     REQUIRE(x, "x");
     REQUIRE(out, "out");
     LayerCarve l = layer_carve(c, ws);
     if ((st = check_ws(ws, ws_bytes, l.bytes)) != MOE_OK) return st;
     if (c.T == 0) return MOE_OK;
+    const LayerGeom g = layer_geom(c);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = moe::launch_router_logits(c, x, w_router, static_cast<float*>(l.scratch), s);
     if (e != hipSuccess) return hip_fail(e, "moe_layer (router)");
     e = moe::launch_route_select(c, static_cast<float*>(l.scratch), bias, nullptr, l.ids, l.topk_w, s);
     if (e != hipSuccess) return hip_fail(e, "moe_layer (select)");
-    PermuteCarve pc = permute_carve(c, l.scratch);
-    e = moe::launch_permute(c, x, nullptr, l.ids, l.counts, l.offsets, l.row_src, l.tok_row, l.x_perm, nullptr,
-                            max_rows_of(c), pc.ws, s);
+    PermuteCarve pc = permute_carve(g.c16, l.scratch);
+    moe::PermuteLayout lay{g.tiled ? 1 : 0, (g.tiled && c.has_shared) ? g.rows_pad : -1};
+    e = moe::launch_permute(g.c16, x, nullptr, l.ids, l.counts, l.offsets, l.row_src, l.tok_row, l.x_perm, nullptr,
+                            g.rows, pc.ws, lay, s);
     if (e != hipSuccess) return hip_fail(e, "moe_layer (permute)");
-    st = ffn_enqueue(c, max_rows_of(c), l.x_perm, nullptr, l.offsets, *w, x, l.y_rows, l.y_shared, l.scratch, s);
+    moe::FfnOperands op{};
+    op.x_rows = l.x_perm;
+    op.x_rows_tiled = g.tiled ? 1 : 0;
+    if (g.tiled && c.has_shared) {
+        op.x_tokens = static_cast<const char*>(l.x_perm) + (size_t)(g.rows_pad / 16) * ((c.H + 31) / 32) * 1024;
+        op.x_tokens_tiled = 1;
+    } else {
+        op.x_tokens = x;
+    }
+    op.y_rows = l.y_rows;
+    op.y_shared = l.y_shared;
+    st = ffn_enqueue(g.c16, g.rows, op, nullptr, l.offsets, *w, l.scratch, s);
     if (st != MOE_OK) return st;
     e = moe::launch_combine(c, l.y_rows, l.tok_row, l.topk_w, l.y_shared, out, s);
     if (e != hipSuccess) return hip_fail(e, "moe_layer (combine)");

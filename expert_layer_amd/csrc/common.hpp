@@ -67,6 +67,17 @@ __device__ __forceinline__ uint8_t f32_to_e4m3(float v) {
     return code ? (uint8_t)(sign | code) : (uint8_t)0;
 }
 
+// The tiled bf16 layout of the grouped FFN's operands: 1 KiB blocks of 16 rows
+// x 32 k, block (row / 16, k / 32) at 16-byte chunk (row / 16 * KS + k / 32) * 64,
+// and inside a block chunk c (8 k values) of row r at r * 4 + (c ^ tile_swz(r)).
+// The XOR makes any 16 consecutive rows of one chunk column land on 16
+// distinct LDS bank groups once the block is copied to LDS verbatim.
+__device__ __forceinline__ int tile_swz(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
+__device__ __forceinline__ size_t tiled_chunk(int64_t row, int chunk, int KS) {
+    const int r = (int)(row & 15);
+    return ((size_t)(row >> 4) * (size_t)KS + (size_t)(chunk >> 2)) * 64 + (size_t)(r * 4 + ((chunk & 3) ^ tile_swz(r)));
+}
+
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
 
 // ---------------------------------------------------------------- MFMA
@@ -115,10 +126,17 @@ struct PermuteWs {
     int32_t* base;   // [nblk][E] first row of block b's segment of expert e
 };
 int permute_blocks(int T);
+// Layout of the permuted rows: row-major [max_rows][H], or (bf16 only) tiled
+// with KS = ceil(H / 32); with shared_row0 >= 0 the tiled output also holds
+// token t at row shared_row0 + t (the shared expert's operand).
+struct PermuteLayout {
+    int tiled;
+    int64_t shared_row0;
+};
 hipError_t launch_permute(const moe_cfg& c, const void* x, const float* x_scale, const int32_t* ids,
                           int32_t* counts, int32_t* offsets, int32_t* row_src, int32_t* tok_row,
                           void* x_perm, float* x_perm_scale, int64_t max_rows, PermuteWs ws,
-                          hipStream_t s);
+                          PermuteLayout lay, hipStream_t s);
 
 // Grouped FFN building blocks (gemm_bf16.hip, gemm_f32.hip).  Tile heights
 // (rows) and the h / output columns one tile covers in GEMM1 / GEMM2.
@@ -135,9 +153,29 @@ struct FfnWork {
 };
 hipError_t launch_build_tiles(const moe_cfg& c, const int32_t* offsets, int bm, int64_t rows_cap,
                               const FfnWork& wk, hipStream_t s);
-hipError_t launch_gemm_bf16(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_cap, const void* x_rows,
-                            const int32_t* offsets, const moe_weights& w, const void* x_tokens, void* y_rows,
-                            void* y_shared, const FfnWork& wk, void* h, void* h_sh, hipStream_t s);
+// Row operands of the grouped FFN: GEMM1 inputs (routed rows, shared-expert
+// tokens; row-major or tiled) and GEMM2 outputs.
+struct FfnOperands {
+    const void* x_rows;
+    const void* x_tokens;
+    int x_rows_tiled, x_tokens_tiled;
+    void* y_rows;
+    void* y_shared;
+};
+hipError_t launch_gemm_bf16(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_cap, const FfnOperands& op,
+                            const int32_t* offsets, const moe_weights& w, const FfnWork& wk, void* h_tiles,
+                            hipStream_t s);
+// Bytes of one h tile slot (256 rows) of the bf16 path.
+inline size_t h_slot_bytes(const moe_cfg& c) {
+    const int imax = c.has_shared && c.I_shared > c.I ? c.I_shared : c.I;
+    return (size_t)256 * ((imax + 31) / 32) * 32 * 2;
+}
+struct TiledSizes {
+    size_t w13, w2, sh13, sh2;  // bytes of the tiled routed and shared matrices
+};
+TiledSizes tiled_sizes(const moe_cfg& c);
+hipError_t launch_tile_weights(const moe_cfg& c, const moe_weights& src, void* w13, void* w2, void* sh13, void* sh2,
+                               hipStream_t s);
 hipError_t launch_gemm_f32(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_cap, const void* x_rows,
                            const int32_t* offsets, const moe_weights& w, const void* x_tokens, void* y_rows,
                            void* y_shared, const FfnWork& wk, void* h, void* h_sh, hipStream_t s);

@@ -75,22 +75,27 @@ __device__ __forceinline__ void wait_vm() {
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // XOR pattern of the 16-byte chunks of an LDS row (only bits 1..3 of the row
-// matter, so rows 32 apart share it).
-__device__ __forceinline__ int swz_of_row(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
+// matter, so rows 16 apart share it): the tiled layout's pattern.
+__device__ __forceinline__ int swz_of_row(int row) { return tile_swz(row); }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// Operand layouts.  Row-major: [rows][K], K contiguous.  Tiled: 1 KiB blocks
+// of 16 rows x 32 k, block (rb, ks) at byte (rb * KS + ks) * 1024 with
+// KS = ceil(K / 32), the 16-byte chunks inside a block already in the LDS
+// order (chunk c of row r at slot r * 4 + (c ^ swz_of_row(r))), zero padded.
+// A tiled stage of 16 rows is one contiguous 1 KiB read.
 struct GemmArgs {
-    const uint16_t* a_routed;  // GEMM1: x_rows [rows][H]; GEMM2: h [rows][I]
-    const uint16_t* a_shared;  // GEMM1: x_tokens [T][H]; GEMM2: h_sh [T][I_sh]
-    const uint16_t* w0_routed; // GEMM1: w_gate [E][I][H]; GEMM2: w_down [E][H][I]
-    const uint16_t* w1_routed; // GEMM1: w_up
+    const uint16_t* a_routed;  // GEMM1: x rows (row-major or tiled); GEMM2: h tile slots (tiled)
+    const uint16_t* a_shared;  // GEMM1: shared-expert tokens (row-major or tiled); GEMM2: h tile slots
+    const uint16_t* w0_routed; // GEMM1: w_gate [E][I][H] or tiled w13; GEMM2: w_down [E][H][I] or tiled
+    const uint16_t* w1_routed; // GEMM1: w_up (row-major only)
     const uint16_t* w0_shared;
     const uint16_t* w1_shared;
-    void* out_routed;          // GEMM1: h; GEMM2: y_rows
-    void* out_shared;          // GEMM1: h_sh; GEMM2: y_shared
+    void* out_routed;          // GEMM1: h tile slots; GEMM2: y_rows
+    void* out_shared;          // GEMM1: h tile slots; GEMM2: y_shared
     const int4* tiles;
     const int32_t* n_tiles;
     const int2* work;          // {M tile, N tile} in launch order
@@ -99,15 +104,21 @@ struct GemmArgs {
     int K_routed, K_shared;    // reduction length
     int N_routed, N_shared;    // GEMM1: h columns (I, I_sh); GEMM2: H
     int out_f32;               // GEMM2 output dtype
+    int a_tiled_routed, a_tiled_shared;  // A operand layout of the two groups
+    int w_tiled;               // weights tiled (w13 / w2 layout)
+    int h_slot_ks;             // k blocks of one h tile slot (ceil(max(I, I_sh) / 32))
 };
 
-// Per-tile DMA state: buffer descriptors and the byte offsets of this lane's
-// 16-byte chunks (four A and four B load instructions per stage).
+// Per-tile DMA state: buffer descriptors, the byte offsets of this lane's
+// 16-byte chunks in stage 0 (four A and four B load instructions per stage),
+// and how far a stage moves them (64 B row-major, 1 KiB tiled).
 struct Dma {
     __amdgpu_buffer_rsrc_t ra, rb0, rb1;
     uint32_t va[4], vb[4];
+    uint32_t sa, sb;        // bytes per stage
     uint32_t kvalid_last;   // valid K columns in the last stage (multiple of 8)
     int nsteps;             // real stages
+    bool a_rm, b_rm;        // row-major operand: the K tail must be masked
 };
 
 template <int MODE, int BUF>
@@ -115,17 +126,19 @@ __device__ __forceinline__ void dma_stage(const Dma& d, int t, int wave, int lan
     i32x4* buf = ring<BUF>();
     const bool real = t < d.nsteps;
     const bool last = t == d.nsteps - 1;
-    const uint32_t kb = (uint32_t)t * (BK * 2);
+    // row-major chunks of the K tail load zero (tiled operands are zero padded)
     const uint32_t logical8 = (uint32_t)(((lane & 3) ^ swz_of_row(lane >> 2)) * 8);
     const bool tail_ok = !last || logical8 < d.kvalid_last;
+    const bool a_ok = real && (!d.a_rm || tail_ok), b_ok = real && (!d.b_rm || tail_ok);
+    const uint32_t ka = (uint32_t)t * d.sa, kb = (uint32_t)t * d.sb;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const uint32_t off = (real && tail_ok) ? d.va[i] + kb : kOOB;
+        const uint32_t off = a_ok ? d.va[i] + ka : kOOB;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ra, (lds_t)(buf + (wave * 4 + i) * 64), 16, off, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const uint32_t off = (real && tail_ok) ? d.vb[i] + kb : kOOB;
+        const uint32_t off = b_ok ? d.vb[i] + kb : kOOB;
         const __amdgpu_buffer_rsrc_t r = (MODE == 0 && i >= 2) ? d.rb1 : d.rb0;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_t)(buf + kSlots + (wave * 4 + i) * 64), 16, off, 0, 0, 0);
     }
@@ -180,33 +193,72 @@ __device__ __forceinline__ void stage(const Dma& d, int s, int wave, int lane, i
 }
 
 template <int MODE, int NRB>
-__device__ __forceinline__ void run_tile(const GemmArgs& p, int g, int row0, int M, int n0, int K, int N,
+__device__ __forceinline__ void run_tile(const GemmArgs& p, int mt, int g, int row0, int M, int n0, int K, int N,
                                          bool shared) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l32 = lane & 31;
-
-    const uint16_t* A = (shared ? p.a_shared : p.a_routed) + (size_t)row0 * K;
-    const size_t wmat = (size_t)K * (size_t)N;
-    const uint16_t* W0 = (shared ? p.w0_shared : p.w0_routed + (size_t)g * wmat) + (size_t)n0 * K;
-    const uint16_t* W1 =
-        MODE == 0 ? (shared ? p.w1_shared : p.w1_routed + (size_t)g * wmat) + (size_t)n0 * K : nullptr;
+    const int KS = (K + BK - 1) / BK;
 
     Dma d;
-    d.nsteps = (K + BK - 1) / BK;
-    d.kvalid_last = (uint32_t)(K - (d.nsteps - 1) * BK);
-    d.ra = make_rsrc(A, (uint32_t)M * (uint32_t)K * 2u);
+    d.nsteps = KS;
+    d.kvalid_last = (uint32_t)(K - (KS - 1) * BK);
+    // ---- A: rows row0 .. row0+M of this group
+    const bool a_tiled = MODE == 1 || (shared ? p.a_tiled_shared : p.a_tiled_routed);
+    d.a_rm = !a_tiled;
+    if (MODE == 1) {
+        // GEMM2 reads the h tile slot of this M tile, written tiled by GEMM1
+        const uint16_t* A = (shared ? p.a_shared : p.a_routed) + (size_t)mt * 16 * p.h_slot_ks * 512;
+        d.ra = make_rsrc(A, (uint32_t)((NRB * 2) * KS * 1024));
+    } else if (a_tiled) {
+        // row0 is a multiple of 16 here (the caller aligns expert segments)
+        const uint16_t* A = (shared ? p.a_shared : p.a_routed) + (size_t)(row0 / 16) * KS * 512;
+        d.ra = make_rsrc(A, (uint32_t)(((M + 15) / 16) * KS * 1024));
+    } else {
+        const uint16_t* A = (shared ? p.a_shared : p.a_routed) + (size_t)row0 * K;
+        d.ra = make_rsrc(A, (uint32_t)M * (uint32_t)K * 2u);
+    }
+    d.sa = a_tiled ? 1024u : (uint32_t)(BK * 2);
+    // ---- B: the weight rows of this N tile
     const int ncols = MODE == 0 ? min(BN / 2, N - n0) : min(BN, N - n0);
-    d.rb0 = make_rsrc(W0, (uint32_t)ncols * (uint32_t)K * 2u);
-    d.rb1 = MODE == 0 ? make_rsrc(W1, (uint32_t)ncols * (uint32_t)K * 2u) : d.rb0;
+    d.b_rm = !p.w_tiled;
+    if (p.w_tiled) {
+        // GEMM1: w13 tiled, 2 * roundup(I, 128) rows with gate and up interleaved per
+        // wave (32 gate rows, then the 32 up rows of the same h columns);
+        // GEMM2: w2 tiled, H rows.  The tile starts at row-block 16 * nt.
+        const int rows = MODE == 0 ? 2 * (((N + 127) / 128) * 128) : N;
+        const int rbs = (rows + 15) / 16;
+        const size_t mat = (size_t)rbs * KS * 512;
+        const uint16_t* W = (shared ? p.w0_shared : p.w0_routed + (size_t)g * mat);
+        const int rb0 = MODE == 0 ? (n0 / 128) * 16 : (n0 / 256) * 16;
+        d.rb0 = make_rsrc(W + (size_t)rb0 * KS * 512, (uint32_t)((rbs - rb0) * KS * 1024));
+        d.rb1 = d.rb0;
+        d.sb = 1024u;
+    } else {
+        const size_t wmat = (size_t)K * (size_t)N;
+        const uint16_t* W0 = (shared ? p.w0_shared : p.w0_routed + (size_t)g * wmat) + (size_t)n0 * K;
+        const uint16_t* W1 =
+            MODE == 0 ? (shared ? p.w1_shared : p.w1_routed + (size_t)g * wmat) + (size_t)n0 * K : nullptr;
+        d.rb0 = make_rsrc(W0, (uint32_t)ncols * (uint32_t)K * 2u);
+        d.rb1 = MODE == 0 ? make_rsrc(W1, (uint32_t)ncols * (uint32_t)K * 2u) : d.rb0;
+        d.sb = (uint32_t)(BK * 2);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int row = (wave * 4 + i) * 16 + (lane >> 2);
+        const int blk = wave * 4 + i;           // 16-row block of the tile this instruction fills
+        const int row = blk * 16 + (lane >> 2);
         const uint32_t logical8 = (uint32_t)(((lane & 3) ^ swz_of_row(row)) * 8);
-        d.va[i] = row < M ? ((uint32_t)row * (uint32_t)K + logical8) * 2u : kOOB;
-        // B row of this chunk, relative to the tile's first weight row n0
-        const int bc = MODE == 0 ? wave * 32 + (i & 1) * 16 + (lane >> 2) : wave * 64 + i * 16 + (lane >> 2);
-        d.vb[i] = bc < ncols ? ((uint32_t)bc * (uint32_t)K + logical8) * 2u : kOOB;
+        if (a_tiled)
+            d.va[i] = blk * 16 < NRB * 32 ? ((uint32_t)blk * (uint32_t)KS * 1024u + (uint32_t)lane * 16u) : kOOB;
+        else
+            d.va[i] = row < M ? ((uint32_t)row * (uint32_t)K + logical8) * 2u : kOOB;
+        if (p.w_tiled) {
+            d.vb[i] = (uint32_t)blk * (uint32_t)KS * 1024u + (uint32_t)lane * 16u;
+        } else {
+            // B row of this chunk, relative to the tile's first weight row n0
+            const int bc = MODE == 0 ? wave * 32 + (i & 1) * 16 + (lane >> 2) : wave * 64 + i * 16 + (lane >> 2);
+            d.vb[i] = bc < ncols ? ((uint32_t)bc * (uint32_t)K + logical8) * 2u : kOOB;
+        }
     }
 
     f32x16 acc0[8], acc1[8];
@@ -237,15 +289,25 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, int g, int row0, int
 
     void* out = shared ? p.out_shared : p.out_routed;
     if (MODE == 0) {
+        // h = silu(g) * u into this M tile's slot, tiled with the slot's own KS
+        // (the K of GEMM2), so GEMM2 streams it with contiguous 1 KiB reads
+        // Columns in [N, roundup(N, 32)) are GEMM2's K padding: they get zeros.
         const int col = n0 + wave * 32 + l32;
-        if (col < N) {
-            uint16_t* h = static_cast<uint16_t*>(out);
+        const int ksh = (N + BK - 1) / BK;
+        if (col < ksh * BK) {
+            const bool live = col < N;
+            uint16_t* h = static_cast<uint16_t*>(out) + (size_t)mt * 16 * p.h_slot_ks * 512;
+            const int kb = col >> 5, c8 = (col & 31) >> 3, e8 = col & 7;
 #pragma unroll
             for (int r = 0; r < NRB; ++r) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int row = r * 32 + c_row(i, lane);
-                    if (row < M) h[(size_t)(row0 + row) * N + col] = f32_to_bf16(silu_f(acc0[r][i]) * acc1[r][i]);
+                    if (row < M) {
+                        const size_t o = ((size_t)(row >> 4) * ksh + kb) * 512 +
+                                         (size_t)(((row & 15) * 4 + (c8 ^ swz_of_row(row))) * 8 + e8);
+                        h[o] = live ? f32_to_bf16(silu_f(acc0[r][i]) * acc1[r][i]) : (uint16_t)0;
+                    }
                 }
             }
         }
@@ -288,14 +350,14 @@ ffn_gemm_bf16(GemmArgs p) {
     const int n0 = MODE == 0 ? nt * (BN / 2) : nt * BN;
     if (n0 >= N || M <= 0) return;
     switch ((M + 31) >> 5) {
-    case 1: run_tile<MODE, 1>(p, g, row0, M, n0, K, N, shared); break;
-    case 2: run_tile<MODE, 2>(p, g, row0, M, n0, K, N, shared); break;
-    case 3: run_tile<MODE, 3>(p, g, row0, M, n0, K, N, shared); break;
-    case 4: run_tile<MODE, 4>(p, g, row0, M, n0, K, N, shared); break;
-    case 5: run_tile<MODE, 5>(p, g, row0, M, n0, K, N, shared); break;
-    case 6: run_tile<MODE, 6>(p, g, row0, M, n0, K, N, shared); break;
-    case 7: run_tile<MODE, 7>(p, g, row0, M, n0, K, N, shared); break;
-    default: run_tile<MODE, 8>(p, g, row0, M, n0, K, N, shared); break;
+    case 1: run_tile<MODE, 1>(p, mt, g, row0, M, n0, K, N, shared); break;
+    case 2: run_tile<MODE, 2>(p, mt, g, row0, M, n0, K, N, shared); break;
+    case 3: run_tile<MODE, 3>(p, mt, g, row0, M, n0, K, N, shared); break;
+    case 4: run_tile<MODE, 4>(p, mt, g, row0, M, n0, K, N, shared); break;
+    case 5: run_tile<MODE, 5>(p, mt, g, row0, M, n0, K, N, shared); break;
+    case 6: run_tile<MODE, 6>(p, mt, g, row0, M, n0, K, N, shared); break;
+    case 7: run_tile<MODE, 7>(p, mt, g, row0, M, n0, K, N, shared); break;
+    default: run_tile<MODE, 8>(p, mt, g, row0, M, n0, K, N, shared); break;
     }
 }
 
@@ -380,26 +442,32 @@ hipError_t launch_build_tiles(const moe_cfg& c, const int32_t* offsets, int bm, 
     return hipGetLastError();
 }
 
-hipError_t launch_gemm_bf16(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_cap, const void* x_rows,
-                            const int32_t* offsets, const moe_weights& w, const void* x_tokens, void* y_rows,
-                            void* y_shared, const FfnWork& wk, void* h, void* h_sh, hipStream_t s) {
+hipError_t launch_gemm_bf16(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_cap, const FfnOperands& op,
+                            const int32_t* offsets, const moe_weights& w, const FfnWork& wk, void* h_tiles,
+                            hipStream_t s) {
     const int has_sh = c.has_shared ? 1 : 0;
     hipError_t e0 = launch_build_tiles(c, offsets, BM, n_rows_cap, wk, s);
     if (e0 != hipSuccess) return e0;
+    const bool tiled = w.layout == MOE_LAYOUT_TILED;
+    const int imax = has_sh && c.I_shared > c.I ? c.I_shared : c.I;
     GemmArgs a{};
     a.tiles = reinterpret_cast<const int4*>(wk.tiles);
     a.n_tiles = wk.n_tiles;
-    a.work = reinterpret_cast<const int2*>(wk.work1);
     a.E = c.E;
-    // GEMM1: gate/up + SwiGLU -> h
-    a.a_routed = static_cast<const uint16_t*>(x_rows);
-    a.a_shared = static_cast<const uint16_t*>(x_tokens);
+    a.w_tiled = tiled;
+    a.h_slot_ks = (imax + BK - 1) / BK;
+    // GEMM1: gate/up + SwiGLU -> h tile slots
+    a.work = reinterpret_cast<const int2*>(wk.work1);
+    a.a_routed = static_cast<const uint16_t*>(op.x_rows);
+    a.a_shared = static_cast<const uint16_t*>(op.x_tokens);
+    a.a_tiled_routed = op.x_rows_tiled;
+    a.a_tiled_shared = op.x_tokens_tiled;
     a.w0_routed = static_cast<const uint16_t*>(w.w_gate);
     a.w1_routed = static_cast<const uint16_t*>(w.w_up);
     a.w0_shared = static_cast<const uint16_t*>(w.sh_gate);
     a.w1_shared = static_cast<const uint16_t*>(w.sh_up);
-    a.out_routed = h;
-    a.out_shared = h_sh;
+    a.out_routed = h_tiles;
+    a.out_shared = h_tiles;
     a.K_routed = c.H;
     a.K_shared = c.H;
     a.N_routed = c.I;
@@ -408,22 +476,86 @@ hipError_t launch_gemm_bf16(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_
     a.out_f32 = 0;
     hipLaunchKernelGGL(ffn_gemm_bf16<0>, dim3((unsigned)(max_tiles * a.NT)), dim3(NTH), 0, s, a);
     // GEMM2: down -> y
-    a.a_routed = static_cast<const uint16_t*>(h);
-    a.a_shared = static_cast<const uint16_t*>(h_sh);
+    a.work = reinterpret_cast<const int2*>(wk.work2);
+    a.a_routed = static_cast<const uint16_t*>(h_tiles);
+    a.a_shared = static_cast<const uint16_t*>(h_tiles);
+    a.a_tiled_routed = 1;
+    a.a_tiled_shared = 1;
     a.w0_routed = static_cast<const uint16_t*>(w.w_down);
     a.w1_routed = nullptr;
     a.w0_shared = static_cast<const uint16_t*>(w.sh_down);
     a.w1_shared = nullptr;
-    a.out_routed = y_rows;
-    a.out_shared = y_shared;
+    a.out_routed = op.y_rows;
+    a.out_shared = op.y_shared;
     a.K_routed = c.I;
     a.K_shared = has_sh ? c.I_shared : c.I;
     a.N_routed = c.H;
     a.N_shared = c.H;
     a.NT = wk.nt2;
-    a.work = reinterpret_cast<const int2*>(wk.work2);
     a.out_f32 = c.y_dtype == MOE_F32;
     hipLaunchKernelGGL(ffn_gemm_bf16<1>, dim3((unsigned)(max_tiles * a.NT)), dim3(NTH), 0, s, a);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------- weight tiling
+// Rewrites E row-major bf16 matrices [rows][K] into the tiled layout, one
+// thread per destination 16-byte chunk.  With `pair` set, the destination row
+// d of two source matrices (gate, up) is interleaved the way GEMM1 consumes
+// it: in every 256-row group j, wave w owns rows 64w .. 64w+63 = the 32 gate
+// rows then the 32 up rows of h columns 128j + 32w .. +31.  Rows and columns
+// past the source are zero.
+__global__ void __launch_bounds__(256)
+tile_matrices(const uint16_t* __restrict__ src0, const uint16_t* __restrict__ src1, int E, int rows, int K,
+              int pair, uint16_t* __restrict__ dst, int rbs, int KS) {
+    const size_t per = (size_t)rbs * KS * 64;
+    const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= per * E) return;
+    const int e = (int)(idx / per);
+    const size_t rem = idx % per;
+    const int slot = (int)(rem & 63);
+    const size_t blk = rem >> 6;
+    const int ks = (int)(blk % KS), rb = (int)(blk / KS);
+    const int r = slot >> 2, chunk = (slot & 3) ^ swz_of_row(r);
+    const int drow = rb * 16 + r, k0 = ks * BK + chunk * 8;
+    const uint16_t* src = src0;
+    int srow = drow;
+    if (pair) {
+        const int j = drow >> 8, w = (drow & 255) >> 6, q = drow & 63;
+        src = q < 32 ? src0 : src1;
+        srow = j * 128 + w * 32 + (q & 31);
+    }
+    i32x4 v = {0, 0, 0, 0};
+    if (srow < rows && k0 < K) v = *reinterpret_cast<const i32x4*>(src + ((size_t)e * rows + srow) * K + k0);
+    reinterpret_cast<i32x4*>(dst)[(size_t)e * per + blk * 64 + slot] = v;
+}
+
+TiledSizes tiled_sizes(const moe_cfg& c) {
+    TiledSizes t{};
+    auto w13 = [&](int I) { return (size_t)(2 * ((I + 127) / 128) * 128 / 16) * ((c.H + BK - 1) / BK) * 1024; };
+    auto w2 = [&](int I) { return (size_t)((c.H + 15) / 16) * ((I + BK - 1) / BK) * 1024; };
+    t.w13 = w13(c.I) * c.E;
+    t.w2 = w2(c.I) * c.E;
+    t.sh13 = c.has_shared ? w13(c.I_shared) : 0;
+    t.sh2 = c.has_shared ? w2(c.I_shared) : 0;
+    return t;
+}
+
+hipError_t launch_tile_weights(const moe_cfg& c, const moe_weights& src, void* w13, void* w2, void* sh13, void* sh2,
+                               hipStream_t s) {
+    auto go = [&](const void* a, const void* b, int E, int rows, int K, int pair, void* dst) {
+        const int rows_t = pair ? 2 * ((rows + 127) / 128) * 128 : rows;
+        const int rbs = (rows_t + 15) / 16, KS = (K + BK - 1) / BK;
+        const size_t n = (size_t)E * rbs * KS * 64;
+        hipLaunchKernelGGL(tile_matrices, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                           static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b), E, rows, K, pair,
+                           static_cast<uint16_t*>(dst), rbs, KS);
+    };
+    go(src.w_gate, src.w_up, c.E, c.I, c.H, 1, w13);
+    go(src.w_down, nullptr, c.E, c.H, c.I, 0, w2);
+    if (c.has_shared) {
+        go(src.sh_gate, src.sh_up, 1, c.I_shared, c.H, 1, sh13);
+        go(src.sh_down, nullptr, 1, c.H, c.I_shared, 0, sh2);
+    }
     return hipGetLastError();
 }
 

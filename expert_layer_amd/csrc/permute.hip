@@ -119,6 +119,38 @@ perm_gather(const uint8_t* __restrict__ x, const float* __restrict__ x_scale, co
         }
 }
 
+// Tiled bf16 output: one workgroup per token; x[t] is read once and its
+// 16-byte chunks are stored to the tiled blocks of its k rows (and of row
+// shared_row0 + t when the shared expert needs the token too).
+__global__ void __launch_bounds__(256)
+perm_gather_tiled(const uint16_t* __restrict__ x, const int32_t* __restrict__ tok_row, uint16_t* __restrict__ x_perm,
+                  int k, int H, int KS, int64_t shared_row0) {
+    const int t = blockIdx.x;
+    __shared__ int64_t rows[33];
+    if (threadIdx.x < k) rows[threadIdx.x] = tok_row[(size_t)t * k + threadIdx.x];
+    if (threadIdx.x == 32) rows[32] = shared_row0 >= 0 ? shared_row0 + t : -1;
+    __syncthreads();
+    // chunks past H up to the last 32-column block are K padding: zeros
+    const int nchunk = H / 8, nchunk_pad = KS * 4;
+    const i32x4* src = reinterpret_cast<const i32x4*>(x + (size_t)t * H);
+    i32x4* dst = reinterpret_cast<i32x4*>(x_perm);
+    const int64_t srow = rows[32];
+    for (int c = threadIdx.x; c < nchunk_pad; c += 256) {
+        const i32x4 v = c < nchunk ? __builtin_nontemporal_load(src + c) : i32x4{0, 0, 0, 0};
+        for (int j = 0; j < k; ++j) dst[tiled_chunk(rows[j], c, KS)] = v;
+        if (srow >= 0) dst[tiled_chunk(srow, c, KS)] = v;
+    }
+}
+
+__global__ void __launch_bounds__(256)
+perm_zero_tiled(const int32_t* __restrict__ row_src, uint16_t* __restrict__ x_perm, int64_t max_rows, int KS) {
+    const int sub = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t r = (int64_t)blockIdx.x * 4 + sub;
+    if (r >= max_rows || row_src[r] != -1) return;
+    i32x4* dst = reinterpret_cast<i32x4*>(x_perm);
+    for (int c = lane; c < KS * 4; c += 64) dst[tiled_chunk(r, c, KS)] = i32x4{0, 0, 0, 0};
+}
+
 // Zero the payload of padding rows (row_src == -1); 4 rows per workgroup.
 __global__ void __launch_bounds__(256)
 perm_zero(const int32_t* __restrict__ row_src, uint8_t* __restrict__ x_perm, float* __restrict__ x_perm_scale,
@@ -141,7 +173,7 @@ static int dtype_bytes(int d) { return d == MOE_F32 ? 4 : (d == MOE_BF16 ? 2 : 1
 hipError_t launch_permute(const moe_cfg& c, const void* x, const float* x_scale, const int32_t* ids,
                           int32_t* counts, int32_t* offsets, int32_t* row_src, int32_t* tok_row,
                           void* x_perm, float* x_perm_scale, int64_t max_rows, PermuteWs ws,
-                          hipStream_t s) {
+                          PermuteLayout lay, hipStream_t s) {
     const int nblk = permute_blocks(c.T);
     const int m_tile = c.m_tile > 0 ? c.m_tile : 1;
     hipLaunchKernelGGL(perm_hist, dim3(nblk), dim3(PB), c.E * sizeof(int32_t), s, ids, ws.hist, c.T, c.k,
@@ -153,6 +185,15 @@ hipError_t launch_permute(const moe_cfg& c, const void* x, const float* x_scale,
                            max_rows, -1);
     hipLaunchKernelGGL(perm_scatter, dim3(nblk), dim3(PB), (size_t)c.E * (PB / 32) * sizeof(uint32_t), s,
                        ids, ws.base, row_src, tok_row, c.T, c.k, c.E);
+    if (lay.tiled) {
+        const int KS = (c.H + 31) / 32;
+        hipLaunchKernelGGL(perm_gather_tiled, dim3(c.T), dim3(256), 0, s, static_cast<const uint16_t*>(x), tok_row,
+                           static_cast<uint16_t*>(x_perm), c.k, c.H, KS, lay.shared_row0);
+        if (m_tile > 1)
+            hipLaunchKernelGGL(perm_zero_tiled, dim3((unsigned)((max_rows + 3) / 4)), dim3(256), 0, s, row_src,
+                               static_cast<uint16_t*>(x_perm), max_rows, KS);
+        return hipGetLastError();
+    }
     const int row_bytes = c.H * dtype_bytes(c.act_dtype);
     const int n_scale = c.act_dtype == MOE_FP8_E4M3 ? c.H / 128 : 0;
     const float* xs = c.act_dtype == MOE_FP8_E4M3 ? x_scale : nullptr;

@@ -71,6 +71,11 @@ typedef enum moe_dtype {
 typedef enum moe_score_fn { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score_fn;
 typedef enum moe_group_score { MOE_GROUP_TOP2_SUM = 0, MOE_GROUP_MAX = 1 } moe_group_score;
 
+typedef enum moe_layout {
+    MOE_LAYOUT_ROWMAJOR = 0, /* [out][in] row-major, the reduction index contiguous */
+    MOE_LAYOUT_TILED = 1     /* bf16 tiled layout written by moe_tile_weights */
+} moe_layout;
+
 typedef enum moe_stage {
     MOE_STAGE_ROUTE = 0,
     MOE_STAGE_PERMUTE = 1,
@@ -113,11 +118,16 @@ typedef struct moe_cfg {
 /* Expert weights.  For fp8 weights the s_* arrays hold one fp32 scale per
  * 128 x 128 block: s_gate, s_up [E][I/128][H/128]; s_down [E][H/128][I/128]
  * (dequantised weight = e4m3 value * block scale); NULL otherwise.  sh_* are
- * the shared expert's matrices (NULL when has_shared == 0; bf16/fp32 only). */
+ * the shared expert's matrices (NULL when has_shared == 0; bf16/fp32 only).
+ * layout MOE_LAYOUT_ROWMAJOR: the matrices as above.  layout MOE_LAYOUT_TILED
+ * (bf16 only): w_gate and sh_gate point to the tiled gate+up matrices and
+ * w_down and sh_down to the tiled down matrices written by moe_tile_weights;
+ * w_up and sh_up are unused (NULL). */
 typedef struct moe_weights {
     const void *w_gate, *w_up, *w_down;
     const float *s_gate, *s_up, *s_down;
     const void *sh_gate, *sh_up, *sh_down;
+    int32_t layout;
 } moe_weights;
 
 /* Checks a configuration on the host (no HIP call).  MOE_OK if every entry
@@ -136,6 +146,29 @@ size_t moe_workspace_bytes(const moe_cfg *cfg, int32_t stage);
  * moe_workspace_bytes is this with n_rows_cap = moe_max_rows(cfg)).
  * (size_t)-1 for an invalid cfg or a negative / too large n_rows_cap. */
 size_t moe_ffn_workspace_bytes(const moe_cfg *cfg, int64_t n_rows_cap);
+
+/* Bytes of the tiled copy of the expert weights (routed and shared) that
+ * moe_tile_weights writes; (size_t)-1 for an invalid cfg. */
+size_t moe_tiled_weights_bytes(const moe_cfg *cfg);
+
+/* Rewrites row-major bf16 expert weights into the tiled layout the grouped
+ * GEMM streams with contiguous 1 KiB loads (weights are static: done once, at
+ * load time).  The tiled layout: a matrix of R rows and K columns becomes 1 KiB
+ * blocks of 16 rows x 32 columns, block (r / 16, k / 32) at byte offset
+ * ((r / 16) * ceil(K / 32) + k / 32) * 1024; inside a block the 16-byte chunk c
+ * (8 columns) of row r sits at chunk index r % 16 * 4 + (c ^ s(r % 16)),
+ * s(r) = ((r >> 1) & 3) ^ ((r >> 3) & 1); rows and columns past the matrix are
+ * zero.  Gate and up are merged into one matrix of 2 * roundup(I, 128) rows:
+ * rows 256 j + 64 w + q hold gate row 128 j + 32 w + q (q < 32) and up row
+ * 128 j + 32 w + q - 32 (q >= 32).  Down keeps its H rows.  Per expert the
+ * gate+up matrix spans 2 * roundup(I, 128) / 16 * ceil(H / 32) KiB and the down
+ * matrix ceil(H / 16) * ceil(I / 32) KiB; the routed experts follow each other,
+ * then the shared expert's two matrices.
+ * src: row-major bf16 weights (w_gate, w_up, w_down, and sh_* when has_shared);
+ * dst: device buffer of moe_tiled_weights_bytes(cfg) bytes, 256-byte aligned;
+ * tiled: filled with the pointers into dst and layout MOE_LAYOUT_TILED. */
+moe_status moe_tile_weights(const moe_cfg *cfg, const moe_weights *src, void *dst, size_t dst_bytes,
+                            moe_weights *tiled, void *stream);
 
 /* Router GEMM and top-k gating (the "gated routing" of the AFD page, section
  * 3; ASAP's expert IDs of Table 2).
@@ -213,6 +246,9 @@ moe_status moe_combine(const moe_cfg *cfg, const void *y_rows, const int32_t *to
 /* The whole layer: moe_route -> moe_permute -> moe_grouped_ffn -> moe_combine,
  * enqueued on `stream` with no host synchronisation.  x [T][H] in act_dtype
  * (F32 or BF16); out [T][H] in out_dtype.  All intermediates live in ws.
+ * Internally the expert segments are padded to 16 rows and, for bf16, the
+ * permuted rows are stored in the tiled layout (cfg->m_tile only shapes the
+ * output of the standalone moe_permute).  w may be row-major or tiled.
  * ws: moe_workspace_bytes(cfg, MOE_STAGE_LAYER). */
 moe_status moe_layer(const moe_cfg *cfg, const void *w_router, const float *bias,
                      const moe_weights *w, const void *x, void *out, void *ws,

@@ -123,3 +123,51 @@ def test_combine_matches_oracle(ydt, odt, shared):
         assert rel_err(got, ref) <= 1e-6
     else:
         assert rel_err_bf16_out(got, ref) <= 1e-6
+
+
+@pytest.mark.parametrize("H,I,counts,shared_T,I_sh", [
+    (7168, 2048, [300, 0, 17, 256], 100, 2048),
+    (520, 264, [31, 33, 2], 9, 136),        # I not a multiple of 128, H not of 256
+    (256, 384, [0, 0, 0], 70, 512),         # only the shared expert, I_sh > I
+    (4096, 1536, [513, 1, 33, 0], 0, 0),
+])
+def test_tiled_weights_give_identical_results(H, I, counts, shared_T, I_sh):
+    """The tiled layout is the LDS image of the row-major operands, so the
+    grouped FFN must produce bit-identical outputs from either layout."""
+    d = dev()
+    E = len(counts)
+    s, wg, wu, wd = _weights(E, H, I, "bf16", seed=H + 3 * I, device=d)
+    cap = int(sum(counts)) + 5
+    x_rows = synth.normal(synth.stream_key(11, "rows"), (cap, H), 1.0, d, torch.bfloat16)
+    offs = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32, device=d)
+    has_sh = shared_T > 0
+    T = max(shared_T, 1)
+    sh = (None, None, None)
+    x_tok = y_sh = None
+    if has_sh:
+        ss = synth.MoeShape("t", T=T, H=H, E=1, k=1, I=I_sh, dtype="bf16", seed=78)
+        sh = synth.expert_weights(ss, 0, d)
+        x_tok = synth.normal(synth.stream_key(11, "tok"), (T, H), 1.0, d, torch.bfloat16)
+    c = moe.make_cfg(T=T, H=H, E=E, k=1, I=I, has_shared=has_sh, I_shared=I_sh if has_sh else 0)
+    rm = moe.weights(wg, wu, wd, sh_gate=sh[0], sh_up=sh[1], sh_down=sh[2])
+    tiled, buf = moe.tile_weights(c, rm, d)
+    outs = []
+    for w in (rm, tiled):
+        y = torch.full((cap, H), -3.0, device=d)
+        ysh = torch.full((T, H), -3.0, device=d) if has_sh else None
+        moe.moe_grouped_ffn(c, cap, x_rows, None, offs, w, x_tok, y, ysh,
+                            moe.workspace(c, moe.MOE_STAGE_FFN, d, n_rows_cap=cap))
+        torch.cuda.synchronize()
+        outs.append((y, ysh))
+    assert torch.equal(outs[0][0], outs[1][0])
+    if has_sh:
+        assert torch.equal(outs[0][1], outs[1][1])
+    n = int(sum(counts))
+    assert torch.all(outs[1][0][n:] == -3.0)
+    # and the tiled result is right on its own (first non-empty expert)
+    e = next(i for i, v in enumerate(counts) if v > 0) if n else None
+    if e is not None:
+        o = int(np.sum(counts[:e]))
+        ref = oracle.expert_ffn(to_np(x_rows[o:o + counts[e]]), to_np(wg[e]), to_np(wu[e]), to_np(wd[e]),
+                                h_bf16=True)
+        assert rel_err(f64(outs[1][0][o:o + counts[e]]), ref) <= 1e-2

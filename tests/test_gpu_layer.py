@@ -33,7 +33,10 @@ def _weights(s):
     return _W[key]
 
 
-def _run_layer(s, rc, T, ydt, odt, m_tile=0):
+_TILED = {}
+
+
+def _run_layer(s, rc, T, ydt, odt, m_tile=0, tiled=False):
     (wg, wu, wd), sh = _weights(s)
     c = lib_cfg(s, T=T, y_dtype=ydt, out_dtype=odt, m_tile=m_tile)
     out = torch.full((T, s.H), float("nan"), dtype=torch.float32 if odt == moe.MOE_F32 else torch.bfloat16,
@@ -41,6 +44,12 @@ def _run_layer(s, rc, T, ydt, odt, m_tile=0):
     ws = moe.workspace(c, moe.MOE_STAGE_LAYER, dev())
     shg, shu, shd = sh if sh else (None, None, None)
     w = moe.weights(wg, wu, wd, sh_gate=shg, sh_up=shu, sh_down=shd)
+    if tiled:
+        key = (s.name, s.E, s.I, s.H, s.seed)
+        if key not in _TILED:
+            _TILED.clear()
+            _TILED[key] = moe.tile_weights(c, w, dev())
+        w = _TILED[key][0]
     moe.moe_layer(c, rc["w_r"], rc["bias"], w, rc["x"], out, ws)
     torch.cuda.synchronize()
     return out
@@ -91,18 +100,21 @@ def test_layer_small_matches_oracle(name, T):
         assert rel_err(out.cpu().numpy(), _oracle_tokens(s, rc, np.arange(T), exact=True)) <= 3e-2
     out = _run_layer(s, rc, T, moe.MOE_F32, moe.MOE_BF16, m_tile=16)
     assert rel_err_bf16_out(out.float().cpu().numpy(), ref) <= _tol(s)
+    if s.dtype == "bf16":  # tiled weights: the same kernels on the same LDS image, bit for bit
+        out_t = _run_layer(s, rc, T, moe.MOE_F32, moe.MOE_BF16, m_tile=16, tiled=True)
+        assert torch.equal(out.view(torch.int16), out_t.view(torch.int16))
 
 
-@pytest.mark.parametrize("name,odt", [
-    ("c3_dsv3_bf16", moe.MOE_BF16),   # the benchmarked configuration
-    ("c3_dsv3_bf16", moe.MOE_F32),
-    ("c2_mixtral_bf16", moe.MOE_F32),
-    ("c4_qwen3_skew_bf16", moe.MOE_F32),
+@pytest.mark.parametrize("name,odt,tiled", [
+    ("c3_dsv3_bf16", moe.MOE_BF16, True),   # the benchmarked configuration
+    ("c3_dsv3_bf16", moe.MOE_F32, False),
+    ("c2_mixtral_bf16", moe.MOE_F32, True),
+    ("c4_qwen3_skew_bf16", moe.MOE_F32, True),
 ])
-def test_layer_full_size_sampled(name, odt):
+def test_layer_full_size_sampled(name, odt, tiled):
     s = synth.config(name)
     rc = router_case(s)
-    out = _run_layer(s, rc, s.T, moe.MOE_F32, odt)
+    out = _run_layer(s, rc, s.T, moe.MOE_F32, odt, tiled=tiled)
     # routing of every token through the standalone router
     c = lib_cfg(s)
     ids = torch.empty((s.T, s.k), dtype=torch.int32, device=dev())
