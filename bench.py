@@ -49,7 +49,79 @@ def parse():
     p.add_argument("--rowmajor-weights", action="store_true",
                    help="time the row-major weight layout instead of the tiled one")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    p.add_argument("--traffic-run", action="store_true",
+                   help="the program to run under rocprofv3 --pmc: CAL_RUNS plain streaming kernels (torch.neg "
+                        "over CAL_BYTES of fp32, as many bytes written) to scale the counters, then warmup + steps "
+                        "passes of the stage calls on the workload's routing, with the expert weights drawn by "
+                        "torch.randn (their values do not change which bytes the kernels move; a few hundred "
+                        "dispatches in all); prints no JSON line")
+    p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                   help="no GPU: read two rocprofv3 --pmc result databases of a --traffic-run (FETCH_SIZE, then "
+                        "WRITE_SIZE), write the grouped FFN's HBM bytes per launch to the traffic file, exit")
     return p.parse_args()
+
+
+CAL_BYTES = 1 << 30
+CAL_RUNS = 3
+FFN_KERNELS = ("ffn_build_tiles", "ffn_gemm_bf16<0>", "ffn_gemm_bf16<1>")
+
+
+def calibrate_copy(dev):
+    import torch
+    a = torch.ones(CAL_BYTES // 4, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(CAL_RUNS):
+        torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    del a, b
+    torch.cuda.empty_cache()
+
+
+def _pmc_per_dispatch(db, counter):
+    """{dispatch_id: (kernel_name, value)} of one counter in a rocprofv3 results database."""
+    import sqlite3
+    con = sqlite3.connect(db)
+    out = {}
+    for name, cname, val, disp in con.execute(
+            "select kernel_name, counter_name, value, dispatch_id from counters_collection"):
+        if cname != counter:
+            continue
+        n, v = out.get(disp, (name, 0.0))
+        out[disp] = (n, v + float(val))
+    con.close()
+    return out
+
+
+def traffic_from(fetch_db, write_db, workload):
+    """HBM bytes per moe_grouped_ffn launch: FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch) summed over the launch's three kernels, each scaled so that the
+    calibration kernel reads and writes exactly CAL_BYTES."""
+    res = {"workload": workload, "source_hash": ffn_source_hash()}
+    total = 0.0
+    for key, db, counter in (("fetch", fetch_db, "FETCH_SIZE"), ("write", write_db, "WRITE_SIZE")):
+        d = _pmc_per_dispatch(db, counter)
+        cal = [v for n, v in d.values() if "neg_kernel" in n]
+        if len(cal) < 1:
+            raise SystemExit(f"{db}: no calibration dispatch (profile bench.py --traffic-run)")
+        cal_kib = sum(cal) / len(cal)
+        scale = CAL_BYTES / (cal_kib * 1024.0)
+        per = {k: [v for n, v in d.values() if k in n] for k in FFN_KERNELS}
+        launches = len(per["ffn_build_tiles"])
+        if launches == 0 or any(len(v) != launches for v in per.values()):
+            raise SystemExit(f"{db}: FFN dispatch counts differ: { {k: len(v) for k, v in per.items()} }")
+        b = {k: sum(v) / launches * 1024.0 * scale for k, v in per.items()}
+        res[f"{key}_calibration_kib"] = cal_kib
+        res[f"{key}_scale"] = scale
+        res[f"{key}_bytes_per_launch"] = sum(b.values())
+        res[f"{key}_bytes_per_kernel"] = b
+        res[f"{key}_launches"] = launches
+        total += sum(b.values())
+    res["hbm_bytes_per_launch"] = total
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(res, f, indent=1)
+    print(json.dumps(res))
 
 
 def ffn_source_hash() -> str:
@@ -61,6 +133,9 @@ def ffn_source_hash() -> str:
 
 def main():
     a = parse()
+    if a.traffic_from:
+        traffic_from(*a.traffic_from, a.workload)
+        return
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
@@ -72,6 +147,8 @@ def main():
     import synth
 
     dev = torch.device("cuda:0")
+    if a.traffic_run:
+        calibrate_copy(dev)
     s = synth.config(a.workload)
     if s.dtype != "bf16":
         raise SystemExit("bench.py times the bf16 layers (c2/c3/c4)")
@@ -84,12 +161,18 @@ def main():
     # ---- inputs, resident in HBM before timing
     t_gen = time.time()
     x, w_r, bias = synth.router_inputs(s, dev)
-    wg = torch.empty((E, I, H), dtype=torch.bfloat16, device=dev)
-    wu = torch.empty_like(wg)
-    wd = torch.empty((E, H, I), dtype=torch.bfloat16, device=dev)
-    for e in range(E):
-        wg[e], wu[e], wd[e] = synth.expert_weights(s, e, dev)
-    sh = synth.shared_weights(s, dev) if s.shared else (None, None, None)
+    if a.traffic_run:
+        def rnd(*shape):
+            return (torch.randn(*shape, device=dev) / math.sqrt(shape[-1])).to(torch.bfloat16)
+        wg, wu, wd = rnd(E, I, H), rnd(E, I, H), rnd(E, H, I)
+        sh = (rnd(s.I_shared, H), rnd(s.I_shared, H), rnd(H, s.I_shared)) if s.shared else (None, None, None)
+    else:
+        wg = torch.empty((E, I, H), dtype=torch.bfloat16, device=dev)
+        wu = torch.empty_like(wg)
+        wd = torch.empty((E, H, I), dtype=torch.bfloat16, device=dev)
+        for e in range(E):
+            wg[e], wu[e], wd[e] = synth.expert_weights(s, e, dev)
+        sh = synth.shared_weights(s, dev) if s.shared else (None, None, None)
     w = moe.weights(wg, wu, wd, sh_gate=sh[0], sh_up=sh[1], sh_down=sh[2])
     tiled_buf = None
     if not a.rowmajor_weights:
@@ -109,25 +192,32 @@ def main():
     def step():
         moe.moe_layer(c, w_r, bias, w, x, out, ws, stream)
 
-    for _ in range(a.warmup):
-        step()
-    torch.cuda.synchronize()
+    ms_step = wall = None
+    if not a.traffic_run:
+        for _ in range(a.warmup):
+            step()
+        torch.cuda.synchronize()
 
-    # ---- timed region: K whole-layer steps
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(a.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = ev0.elapsed_time(ev1) / a.steps
+        # ---- timed region: K whole-layer steps
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for _ in range(a.steps):
+            step()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms_step = ev0.elapsed_time(ev1) / a.steps
 
-    # ---- per-stage breakdown: the same kernels through the stage entry points,
-    # with events between stages on the launch stream
+    # ---- per-stage breakdown: moe_layer is these four stage calls with m_tile 16
+    # and the tiled x_perm (bit-identical results); events between the stages on
+    # the launch stream
     R = T * k
+    c = moe.make_cfg(T=T, H=H, E=E, k=k, I=I, n_groups=s.n_groups, topk_groups=s.topk_groups,
+                     score_fn=c.score_fn, renormalize=s.renormalize, routed_scale=s.routed_scale,
+                     has_shared=s.shared, I_shared=s.I_shared, act_dtype=moe.MOE_BF16, y_dtype=moe.MOE_F32,
+                     out_dtype=moe.MOE_BF16, m_tile=16, x_layout=moe.MOE_LAYOUT_TILED)
     rows = moe.moe_max_rows(c)
     ids = torch.empty((T, k), dtype=torch.int32, device=dev)
     tw = torch.empty((T, k), dtype=torch.float32, device=dev)
@@ -135,7 +225,7 @@ def main():
     offs = torch.empty(E + 1, dtype=torch.int32, device=dev)
     row_src = torch.empty(rows, dtype=torch.int32, device=dev)
     tok_row = torch.empty((T, k), dtype=torch.int32, device=dev)
-    x_perm = torch.empty((rows, H), dtype=torch.bfloat16, device=dev)
+    x_perm = moe.x_perm_buffer(c, dev)
     y_rows = torch.empty((rows, H), dtype=torch.float32, device=dev)
     y_sh = torch.empty((T, H), dtype=torch.float32, device=dev) if s.shared else None
     ws_r = moe.workspace(c, moe.MOE_STAGE_ROUTE, dev)
@@ -149,12 +239,12 @@ def main():
         evs[1].record(stream)
         moe.moe_permute(c, x, None, ids, counts, offs, row_src, tok_row, x_perm, None, ws_p, stream)
         evs[2].record(stream)
-        moe.moe_grouped_ffn(c, rows, x_perm, None, offs, w, x, y_rows, y_sh, ws_f, stream)
+        moe.moe_grouped_ffn(c, rows, x_perm, None, offs, w, None, y_rows, y_sh, ws_f, stream)
         evs[3].record(stream)
         moe.moe_combine(c, y_rows, tok_row, tw, y_sh, out, stream)
         evs[4].record(stream)
 
-    for _ in range(2):
+    for _ in range(a.warmup if a.traffic_run else 2):
         stage_step([torch.cuda.Event(enable_timing=True) for _ in range(5)])
     torch.cuda.synchronize()
     stage_ms = np.zeros(4)
@@ -165,6 +255,10 @@ def main():
     for evs in all_evs:
         stage_ms += np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(4)])
     stage_ms /= a.steps
+    if a.traffic_run:
+        print(f"[bench] traffic run done: {a.warmup + a.steps} stage passes, grouped FFN "
+              f"{stage_ms[2]:.3f} ms", flush=True)
+        return
 
     # ---- algorithmic work
     I_sh = s.I_shared if s.shared else 0
@@ -174,7 +268,7 @@ def main():
     w_bytes = 3.0 * E * H * I * 2 + 3.0 * H * I_sh * 2
     bytes_ = {
         "route": T * H * 2 + E * H * 2 + T * k * 8,
-        "permute": T * H * 2 + R * H * 2 + T * k * 4 + 2 * R * 4,
+        "permute": T * H * 2 + (R + T * bool(s.shared)) * H * 2 + T * k * 4 + 2 * R * 4,
         "grouped_ffn": w_bytes + R * H * 2 + T * H * 2 * bool(s.shared) + (R + T * bool(s.shared)) * H * 4,
         "combine": R * H * 4 + T * H * 4 * bool(s.shared) + T * H * 2 + T * k * 8,
     }

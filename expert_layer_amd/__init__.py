@@ -31,7 +31,7 @@ __all__ = [
     "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3", "MOE_SCORE_SOFTMAX", "MOE_SCORE_SIGMOID",
     "MOE_GROUP_TOP2_SUM", "MOE_GROUP_MAX", "MOE_STAGE_ROUTE", "MOE_STAGE_PERMUTE", "MOE_STAGE_FFN",
     "MOE_STAGE_LAYER", "MOE_LAYOUT_ROWMAJOR", "MOE_LAYOUT_TILED", "moe_tiled_weights_bytes",
-    "moe_tile_weights", "tile_weights",
+    "moe_tile_weights", "tile_weights", "moe_x_perm_bytes", "x_perm_buffer",
 ]
 
 lib_path = _ffi.LIB_PATH
@@ -47,12 +47,13 @@ def make_cfg(T: int, H: int, E: int, k: int, I: int, n_groups: int = 1, topk_gro
              score_fn: int = MOE_SCORE_SOFTMAX, group_score: int = MOE_GROUP_TOP2_SUM,
              renormalize: bool = True, routed_scale: float = 1.0, has_shared: bool = False,
              I_shared: int = 0, act_dtype: int = MOE_BF16, w_dtype: Optional[int] = None,
-             y_dtype: int = MOE_F32, out_dtype: int = MOE_BF16, m_tile: int = 0) -> moe_cfg:
+             y_dtype: int = MOE_F32, out_dtype: int = MOE_BF16, m_tile: int = 0,
+             x_layout: int = MOE_LAYOUT_ROWMAJOR) -> moe_cfg:
     return moe_cfg(T=T, H=H, E=E, k=k, I=I, n_groups=n_groups, topk_groups=topk_groups,
                    score_fn=score_fn, group_score=group_score, renormalize=int(bool(renormalize)),
                    routed_scale=routed_scale, has_shared=int(bool(has_shared)), I_shared=I_shared,
                    act_dtype=act_dtype, w_dtype=act_dtype if w_dtype is None else w_dtype,
-                   y_dtype=y_dtype, out_dtype=out_dtype, m_tile=m_tile)
+                   y_dtype=y_dtype, out_dtype=out_dtype, m_tile=m_tile, x_layout=x_layout)
 
 
 def _ptr(t) -> Optional[int]:
@@ -92,6 +93,19 @@ def weights(w_gate, w_up, w_down, s_gate=None, s_up=None, s_down=None, sh_gate=N
             sh_down=None, layout: int = MOE_LAYOUT_ROWMAJOR) -> moe_weights:
     return moe_weights(*(_ptr(t) for t in (w_gate, w_up, w_down, s_gate, s_up, s_down, sh_gate,
                                              sh_up, sh_down)), layout)
+
+
+def moe_x_perm_bytes(cfg: moe_cfg) -> int:
+    return _ffi.lib().moe_x_perm_bytes(ctypes.byref(cfg))
+
+
+def x_perm_buffer(cfg: moe_cfg, device) -> torch.Tensor:
+    """An x_perm buffer for cfg.x_layout: [moe_max_rows, H] in the activation
+    dtype when row-major, a flat byte buffer when tiled."""
+    if cfg.x_layout == MOE_LAYOUT_TILED:
+        return torch.empty(max(moe_x_perm_bytes(cfg), 1), dtype=torch.uint8, device=device)
+    dt = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16, MOE_FP8_E4M3: torch.uint8}[cfg.act_dtype]
+    return torch.empty((moe_max_rows(cfg), cfg.H), dtype=dt, device=device)
 
 
 def moe_tiled_weights_bytes(cfg: moe_cfg) -> int:

@@ -19,7 +19,7 @@ MOE_STAGE_ROUTE, MOE_STAGE_PERMUTE, MOE_STAGE_FFN, MOE_STAGE_LAYER = 0, 1, 2, 3
 MOE_LAYOUT_ROWMAJOR, MOE_LAYOUT_TILED = 0, 1
 
 EXPORTS = ("moe_validate", "moe_max_rows", "moe_workspace_bytes", "moe_ffn_workspace_bytes",
-           "moe_tiled_weights_bytes", "moe_tile_weights", "moe_route", "moe_permute", "moe_grouped_ffn",
+           "moe_x_perm_bytes", "moe_tiled_weights_bytes", "moe_tile_weights", "moe_route", "moe_permute", "moe_grouped_ffn",
            "moe_combine", "moe_layer", "moe_status_string", "moe_last_error")
 
 
@@ -28,7 +28,7 @@ class moe_cfg(ctypes.Structure):
                                               "score_fn", "group_score", "renormalize")] + \
                [("routed_scale", ctypes.c_float)] + \
                [(n, ctypes.c_int32) for n in ("has_shared", "I_shared", "act_dtype", "w_dtype",
-                                              "y_dtype", "out_dtype", "m_tile")]
+                                              "y_dtype", "out_dtype", "m_tile", "x_layout")]
 
 
 class moe_weights(ctypes.Structure):
@@ -57,6 +57,8 @@ def lib() -> ctypes.CDLL:
         L.moe_workspace_bytes.restype = sz
         L.moe_ffn_workspace_bytes.argtypes = [C, i64]
         L.moe_ffn_workspace_bytes.restype = sz
+        L.moe_x_perm_bytes.argtypes = [C]
+        L.moe_x_perm_bytes.restype = sz
         L.moe_tiled_weights_bytes.argtypes = [C]
         L.moe_tiled_weights_bytes.restype = sz
         L.moe_tile_weights.argtypes = [C, W, P, sz, W, P]

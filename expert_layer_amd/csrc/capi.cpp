@@ -78,6 +78,13 @@ moe_status check_cfg(const moe_cfg* cp) {
         if (c.has_shared) return fail(MOE_ERR_UNSUPPORTED, "fp8 with a shared expert");
     }
     if (c.m_tile < 0 || c.m_tile > 4096) return fail(MOE_ERR_INVALID_ARG, "m_tile=%d must be in [0, 4096]", c.m_tile);
+    if (c.x_layout != MOE_LAYOUT_ROWMAJOR && c.x_layout != MOE_LAYOUT_TILED)
+        return fail(MOE_ERR_INVALID_ARG, "x_layout=%d", c.x_layout);
+    if (c.x_layout == MOE_LAYOUT_TILED) {
+        if (c.act_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "tiled x_perm is bf16 only");
+        if (c.m_tile % 16 || c.m_tile == 0)
+            return fail(MOE_ERR_INVALID_ARG, "tiled x_perm needs m_tile a multiple of 16 (m_tile=%d)", c.m_tile);
+    }
     if (max_rows_of(c) > kMaxRows) return fail(MOE_ERR_INVALID_ARG, "T*k + E*(m_tile-1) is too large");
     if ((int64_t)c.T * c.H > (int64_t)INT32_MAX * 8) return fail(MOE_ERR_INVALID_ARG, "T*H is too large");
     return MOE_OK;
@@ -152,29 +159,37 @@ FfnCarve ffn_carve(const moe_cfg& c, int64_t n_rows_cap, void* p) {
     return f;
 }
 
-// The layer path pads expert segments to 16 rows; for bf16 the permuted rows
-// are tiled and the shared expert's copy of the tokens follows the routed rows.
-struct LayerGeom {
-    moe_cfg c16;        // cfg with m_tile = 16
-    int64_t rows;       // routed rows (max_rows of c16)
-    int64_t rows_pad;   // rounded up to 16: first row of the shared-expert copy
+// x_perm geometry.  Tiled: the routed rows occupy R16 = roundup(max_rows, 16)
+// rows and the shared expert's copy of the tokens follows them.
+struct XPermGeom {
     bool tiled;
-    size_t x_perm_bytes;
+    int64_t rows_pad;       // first row of the shared-expert copy (tiled)
+    size_t shared_off;      // its byte offset in x_perm (tiled)
+    size_t bytes;
 };
-LayerGeom layer_geom(const moe_cfg& c) {
-    LayerGeom g{};
-    g.c16 = c;
-    g.c16.m_tile = 16;
-    g.rows = max_rows_of(g.c16);
-    g.rows_pad = (g.rows + 15) / 16 * 16;
-    g.tiled = c.act_dtype == MOE_BF16;
+XPermGeom x_perm_geom(const moe_cfg& c) {
+    XPermGeom g{};
+    const int64_t rows = max_rows_of(c);
+    g.tiled = c.x_layout == MOE_LAYOUT_TILED;
     if (g.tiled) {
-        const int64_t all = g.rows_pad + (c.has_shared ? (c.T + 15) / 16 * 16 : 0);
-        g.x_perm_bytes = (size_t)(all / 16) * ((c.H + 31) / 32) * 1024;
+        const size_t blk = (size_t)((c.H + 31) / 32) * 1024;  // one 16-row band
+        g.rows_pad = (rows + 15) / 16 * 16;
+        g.shared_off = (size_t)(g.rows_pad / 16) * blk;
+        g.bytes = g.shared_off + (c.has_shared ? (size_t)((c.T + 15) / 16) * blk : 0);
     } else {
-        g.x_perm_bytes = (size_t)g.rows * c.H * dtype_bytes(c.act_dtype);
+        g.rows_pad = rows;
+        g.bytes = (size_t)rows * c.H * dtype_bytes(c.act_dtype);
     }
     return g;
+}
+
+// The configuration moe_layer runs its stages with: expert segments padded to
+// 16 rows, and x_perm tiled for bf16.
+moe_cfg layer_stage_cfg(const moe_cfg& c) {
+    moe_cfg s = c;
+    s.m_tile = 16;
+    s.x_layout = c.act_dtype == MOE_BF16 ? MOE_LAYOUT_TILED : MOE_LAYOUT_ROWMAJOR;
+    return s;
 }
 
 struct LayerCarve {
@@ -186,20 +201,21 @@ struct LayerCarve {
 LayerCarve layer_carve(const moe_cfg& c, void* p) {
     Carve cv(p);
     LayerCarve l{};
-    const LayerGeom g = layer_geom(c);
+    const moe_cfg cs = layer_stage_cfg(c);
+    const int64_t rows = max_rows_of(cs);
     const size_t tk = (size_t)c.T * c.k;
     l.ids = cv.take<int32_t>(tk);
     l.topk_w = cv.take<float>(tk);
     l.counts = cv.take<int32_t>(c.E);
     l.offsets = cv.take<int32_t>(c.E + 1);
-    l.row_src = cv.take<int32_t>((size_t)g.rows);
+    l.row_src = cv.take<int32_t>((size_t)rows);
     l.tok_row = cv.take<int32_t>(tk);
-    l.x_perm = cv.take<char>(g.x_perm_bytes);
-    l.y_rows = cv.take<char>((size_t)g.rows * c.H * dtype_bytes(c.y_dtype));
+    l.x_perm = cv.take<char>(x_perm_geom(cs).bytes);
+    l.y_rows = cv.take<char>((size_t)rows * c.H * dtype_bytes(c.y_dtype));
     l.y_shared = c.has_shared ? cv.take<char>((size_t)c.T * c.H * dtype_bytes(c.y_dtype)) : nullptr;
     size_t scratch = route_ws(c);
-    size_t pb = permute_carve(c, nullptr).bytes;
-    size_t fb = ffn_carve(g.c16, g.rows, nullptr).bytes;
+    size_t pb = permute_carve(cs, nullptr).bytes;
+    size_t fb = ffn_carve(cs, rows, nullptr).bytes;
     if (pb > scratch) scratch = pb;
     if (fb > scratch) scratch = fb;
     l.scratch = cv.take<char>(scratch);
@@ -241,9 +257,33 @@ moe_status check_weights(const moe_cfg& c, const moe_weights* w) {
     return MOE_OK;
 }
 
-moe_status ffn_enqueue(const moe_cfg& c, int64_t n_rows_cap, const moe::FfnOperands& op, const float* x_scale,
-                       const int32_t* offsets, const moe_weights& w, void* ws, hipStream_t s) {
+// Enqueue halves of the stage entry points (arguments already checked); the
+// layer calls the same functions, so its kernels are the stage kernels.
+moe_status permute_enqueue(const moe_cfg& c, const void* x, const float* x_scale, const int32_t* ids,
+                           int32_t* counts, int32_t* offsets, int32_t* row_src, int32_t* tok_row, void* x_perm,
+                           float* x_perm_scale, void* ws, hipStream_t s) {
+    const PermuteCarve pc = permute_carve(c, ws);
+    const XPermGeom g = x_perm_geom(c);
+    const moe::PermuteLayout lay{g.tiled ? 1 : 0, (g.tiled && c.has_shared) ? g.rows_pad : -1};
+    hipError_t e = moe::launch_permute(c, x, x_scale, ids, counts, offsets, row_src, tok_row, x_perm, x_perm_scale,
+                                       max_rows_of(c), pc.ws, lay, s);
+    if (e != hipSuccess) return hip_fail(e, "moe_permute");
+    return MOE_OK;
+}
+
+moe_status ffn_enqueue(const moe_cfg& c, int64_t n_rows_cap, const void* x_rows, const float* x_scale,
+                       const int32_t* offsets, const moe_weights& w, const void* x_tokens, void* y_rows,
+                       void* y_shared, void* ws, hipStream_t s) {
     (void)x_scale;
+    moe::FfnOperands op{x_rows, x_tokens, 0, 0, y_rows, y_shared};
+    const XPermGeom g = x_perm_geom(c);
+    if (g.tiled) {
+        op.x_rows_tiled = 1;
+        if (c.has_shared) {
+            op.x_tokens = static_cast<const char*>(x_rows) + g.shared_off;
+            op.x_tokens_tiled = 1;
+        }
+    }
     FfnCarve f = ffn_carve(c, n_rows_cap, ws);
     hipError_t e;
     if (c.act_dtype == MOE_BF16)
@@ -341,11 +381,8 @@ moe_status moe_permute(const moe_cfg* cfg, const void* x, const float* x_scale, 
     PermuteCarve pc = permute_carve(c, ws);
     if ((st = check_ws(ws, ws_bytes, pc.bytes)) != MOE_OK) return st;
     if (c.T == 0) return MOE_OK;
-    hipError_t e = moe::launch_permute(c, x, x_scale, topk_ids, expert_counts, expert_offsets, row_src, tok_row,
-                                       x_perm, x_perm_scale, max_rows_of(c), pc.ws, moe::PermuteLayout{0, -1},
-                                       static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "moe_permute");
-    return MOE_OK;
+    return permute_enqueue(c, x, x_scale, topk_ids, expert_counts, expert_offsets, row_src, tok_row, x_perm,
+                           x_perm_scale, ws, static_cast<hipStream_t>(stream));
 }
 
 moe_status moe_grouped_ffn(const moe_cfg* cfg, int64_t n_rows_cap, const void* x_rows, const float* x_scale,
@@ -363,16 +400,28 @@ moe_status moe_grouped_ffn(const moe_cfg* cfg, int64_t n_rows_cap, const void* x
         REQUIRE(y_rows, "y_rows");
     }
     if (c.act_dtype == MOE_FP8_E4M3) REQUIRE(x_scale, "x_scale");
+    const bool tiled = c.x_layout == MOE_LAYOUT_TILED;
+    if (tiled) {
+        if (n_rows_cap != max_rows_of(c))
+            return fail(MOE_ERR_INVALID_ARG, "tiled x_rows: n_rows_cap=%lld must equal moe_max_rows (%lld)",
+                        (long long)n_rows_cap, (long long)max_rows_of(c));
+        if (c.has_shared) REQUIRE(x_rows, "x_rows");
+    }
     if (c.has_shared) {
-        REQUIRE(x_tokens, "x_tokens");
+        if (!tiled) REQUIRE(x_tokens, "x_tokens");
         REQUIRE(y_shared, "y_shared");
     }
     if (c.act_dtype == MOE_FP8_E4M3) return fail(MOE_ERR_UNSUPPORTED, "fp8 grouped FFN is not built");
     const size_t need = ffn_carve(c, n_rows_cap, nullptr).bytes;
     if ((st = check_ws(ws, ws_bytes, need)) != MOE_OK) return st;
     if (n_rows_cap == 0 && !(c.has_shared && c.T > 0)) return MOE_OK;
-    moe::FfnOperands op{x_rows, x_tokens, 0, 0, y_rows, y_shared};
-    return ffn_enqueue(c, n_rows_cap, op, x_scale, expert_offsets, *w, ws, static_cast<hipStream_t>(stream));
+    return ffn_enqueue(c, n_rows_cap, x_rows, x_scale, expert_offsets, *w, x_tokens, y_rows, y_shared, ws,
+                       static_cast<hipStream_t>(stream));
+}
+
+size_t moe_x_perm_bytes(const moe_cfg* cfg) {
+    if (check_cfg(cfg) != MOE_OK) return (size_t)-1;
+    return x_perm_geom(*cfg).bytes;
 }
 
 size_t moe_tiled_weights_bytes(const moe_cfg* cfg) {
@@ -438,29 +487,16 @@ moe_status moe_layer(const moe_cfg* cfg, const void* w_router, const float* bias
     LayerCarve l = layer_carve(c, ws);
     if ((st = check_ws(ws, ws_bytes, l.bytes)) != MOE_OK) return st;
     if (c.T == 0) return MOE_OK;
-    const LayerGeom g = layer_geom(c);
+    const moe_cfg cs = layer_stage_cfg(c);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = moe::launch_router_logits(c, x, w_router, static_cast<float*>(l.scratch), s);
     if (e != hipSuccess) return hip_fail(e, "moe_layer (router)");
     e = moe::launch_route_select(c, static_cast<float*>(l.scratch), bias, nullptr, l.ids, l.topk_w, s);
     if (e != hipSuccess) return hip_fail(e, "moe_layer (select)");
-    PermuteCarve pc = permute_carve(g.c16, l.scratch);
-    moe::PermuteLayout lay{g.tiled ? 1 : 0, (g.tiled && c.has_shared) ? g.rows_pad : -1};
-    e = moe::launch_permute(g.c16, x, nullptr, l.ids, l.counts, l.offsets, l.row_src, l.tok_row, l.x_perm, nullptr,
-                            g.rows, pc.ws, lay, s);
-    if (e != hipSuccess) return hip_fail(e, "moe_layer (permute)");
-    moe::FfnOperands op{};
-    op.x_rows = l.x_perm;
-    op.x_rows_tiled = g.tiled ? 1 : 0;
-    if (g.tiled && c.has_shared) {
-        op.x_tokens = static_cast<const char*>(l.x_perm) + (size_t)(g.rows_pad / 16) * ((c.H + 31) / 32) * 1024;
-        op.x_tokens_tiled = 1;
-    } else {
-        op.x_tokens = x;
-    }
-    op.y_rows = l.y_rows;
-    op.y_shared = l.y_shared;
-    st = ffn_enqueue(g.c16, g.rows, op, nullptr, l.offsets, *w, l.scratch, s);
+    st = permute_enqueue(cs, x, nullptr, l.ids, l.counts, l.offsets, l.row_src, l.tok_row, l.x_perm, nullptr,
+                         l.scratch, s);
+    if (st != MOE_OK) return st;
+    st = ffn_enqueue(cs, max_rows_of(cs), l.x_perm, nullptr, l.offsets, *w, x, l.y_rows, l.y_shared, l.scratch, s);
     if (st != MOE_OK) return st;
     e = moe::launch_combine(c, l.y_rows, l.tok_row, l.topk_w, l.y_shared, out, s);
     if (e != hipSuccess) return hip_fail(e, "moe_layer (combine)");

@@ -104,6 +104,13 @@ typedef enum moe_stage {
  *   out_dtype    dtype of the layer output: MOE_F32 or MOE_BF16
  *   m_tile       row padding of each expert segment produced by moe_permute
  *                (1 = no padding; 0 = library default, 1)
+ *   x_layout     layout of x_perm between moe_permute and moe_grouped_ffn:
+ *                MOE_LAYOUT_ROWMAJOR: [moe_max_rows][H] in act_dtype;
+ *                MOE_LAYOUT_TILED (bf16, m_tile a multiple of 16): the tiled
+ *                layout of moe_tile_weights over R16 = roundup(moe_max_rows, 16)
+ *                rows of H columns, followed, when has_shared, by a tiled copy
+ *                of x's T rows (padded to 16) that the shared expert reads;
+ *                moe_x_perm_bytes gives the size.
  * E <= 1024. */
 typedef struct moe_cfg {
     int32_t T, H, E, k, I;
@@ -113,6 +120,7 @@ typedef struct moe_cfg {
     int32_t has_shared, I_shared;
     int32_t act_dtype, w_dtype, y_dtype, out_dtype;
     int32_t m_tile;
+    int32_t x_layout;
 } moe_cfg;
 
 /* Expert weights.  For fp8 weights the s_* arrays hold one fp32 scale per
@@ -146,6 +154,10 @@ size_t moe_workspace_bytes(const moe_cfg *cfg, int32_t stage);
  * moe_workspace_bytes is this with n_rows_cap = moe_max_rows(cfg)).
  * (size_t)-1 for an invalid cfg or a negative / too large n_rows_cap. */
 size_t moe_ffn_workspace_bytes(const moe_cfg *cfg, int64_t n_rows_cap);
+
+/* Bytes of x_perm for cfg->x_layout (moe_max_rows * H * sizeof(act_dtype)
+ * when row-major); (size_t)-1 for an invalid cfg. */
+size_t moe_x_perm_bytes(const moe_cfg *cfg);
 
 /* Bytes of the tiled copy of the expert weights (routed and shared) that
  * moe_tile_weights writes; (size_t)-1 for an invalid cfg. */
@@ -203,6 +215,9 @@ moe_status moe_route(const moe_cfg *cfg, const void *x, const void *w_router, co
  *   tok_row[t*k + j]  = row(t, j)
  *   x_perm[row]       = x[t] (bit copy), zero rows where row_src == -1
  *   x_perm_scale[row] = x_scale[t] (fp8 activations only; [rows][H/128])
+ * x_perm is laid out as cfg->x_layout says (moe_x_perm_bytes bytes); the tiled
+ * layout also receives the shared expert's copy of x when has_shared, and its
+ * column padding up to a multiple of 32 is zero.
  * topk_ids must hold distinct ids in [0, E) per token.
  * ws: moe_workspace_bytes(cfg, MOE_STAGE_PERMUTE). */
 moe_status moe_permute(const moe_cfg *cfg, const void *x, const float *x_scale,
@@ -225,6 +240,11 @@ moe_status moe_permute(const moe_cfg *cfg, const void *x, const float *x_scale,
  * x_rows outside [0, expert_offsets[E]) are neither read nor written.
  * When cfg->has_shared, the shared expert is applied to every token of
  * x_tokens [T][H] into y_shared [T][H] (weight 1).
+ * cfg->x_layout MOE_LAYOUT_TILED: x_rows is the tiled x_perm of moe_permute
+ * with the same cfg, n_rows_cap must equal moe_max_rows(cfg), the expert
+ * offsets must be multiples of 16 (results are undefined otherwise, accesses
+ * stay inside x_rows), and the shared expert reads its copy of the tokens
+ * inside x_rows (x_tokens is ignored and may be NULL).
  * y_rows [n_rows_cap][H] and y_shared in cfg->y_dtype.  n_rows_cap is the
  * row count of x_rows and y_rows, independent of T (rows may arrive already
  * dispatched); expert_offsets[E] <= n_rows_cap.
@@ -246,9 +266,10 @@ moe_status moe_combine(const moe_cfg *cfg, const void *y_rows, const int32_t *to
 /* The whole layer: moe_route -> moe_permute -> moe_grouped_ffn -> moe_combine,
  * enqueued on `stream` with no host synchronisation.  x [T][H] in act_dtype
  * (F32 or BF16); out [T][H] in out_dtype.  All intermediates live in ws.
- * Internally the expert segments are padded to 16 rows and, for bf16, the
- * permuted rows are stored in the tiled layout (cfg->m_tile only shapes the
- * output of the standalone moe_permute).  w may be row-major or tiled.
+ * The stages run with m_tile = 16 and, for bf16, x_layout =
+ * MOE_LAYOUT_TILED, whatever cfg->m_tile and cfg->x_layout say (those shape
+ * the standalone stage calls only); the result equals that of the four stage
+ * calls made with those two fields.  w may be row-major or tiled.
  * ws: moe_workspace_bytes(cfg, MOE_STAGE_LAYER). */
 moe_status moe_layer(const moe_cfg *cfg, const void *w_router, const float *bias,
                      const moe_weights *w, const void *x, void *out, void *ws,

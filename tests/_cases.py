@@ -25,12 +25,13 @@ def dev():
 
 
 def lib_cfg(s: synth.MoeShape, T: Optional[int] = None, y_dtype=moe.MOE_F32, out_dtype=moe.MOE_F32,
-            m_tile: int = 0):
+            m_tile: int = 0, x_layout: int = moe.MOE_LAYOUT_ROWMAJOR):
     return moe.make_cfg(T=s.T if T is None else T, H=s.H, E=s.E, k=s.k, I=s.I, n_groups=s.n_groups,
                         topk_groups=s.topk_groups, score_fn=SCORE[s.score] if s.score in SCORE else 0,
                         group_score=GSCORE[s.group_score], renormalize=s.renormalize,
                         routed_scale=s.routed_scale, has_shared=s.shared, I_shared=s.I_shared,
-                        act_dtype=LIB_DT[s.dtype], y_dtype=y_dtype, out_dtype=out_dtype, m_tile=m_tile)
+                        act_dtype=LIB_DT[s.dtype], y_dtype=y_dtype, out_dtype=out_dtype, m_tile=m_tile,
+                        x_layout=x_layout)
 
 
 def route_kw(s: synth.MoeShape):

@@ -67,6 +67,10 @@ def test_validate_accepts_workload_shapes():
     (dict(act_dtype=m.MOE_FP8_E4M3), m.MOE_ERR_UNSUPPORTED),  # fp8 + shared expert
     (dict(m_tile=-1), m.MOE_ERR_INVALID_ARG),
     (dict(routed_scale=float("inf")), m.MOE_ERR_INVALID_ARG),
+    (dict(x_layout=2), m.MOE_ERR_INVALID_ARG),
+    (dict(x_layout=m.MOE_LAYOUT_TILED, m_tile=8), m.MOE_ERR_INVALID_ARG),
+    (dict(x_layout=m.MOE_LAYOUT_TILED, m_tile=0), m.MOE_ERR_INVALID_ARG),
+    (dict(x_layout=m.MOE_LAYOUT_TILED, m_tile=16, act_dtype=m.MOE_F32), m.MOE_ERR_UNSUPPORTED),
 ])
 def test_validate_rejects(kw, code):
     c = _dsv3(**kw)
@@ -108,6 +112,19 @@ def test_max_rows_and_workspace_sizes():
     assert m.moe_ffn_workspace_bytes(c, -1) == ctypes.c_size_t(-1).value
 
 
+def test_x_perm_sizes():
+    c = _dsv3(m_tile=16)
+    assert m.moe_x_perm_bytes(c) == m.moe_max_rows(c) * 7168 * 2
+    t = _dsv3(m_tile=16, x_layout=m.MOE_LAYOUT_TILED)
+    r16 = (m.moe_max_rows(t) + 15) // 16 * 16
+    assert m.moe_x_perm_bytes(t) == (r16 // 16 + 8192 // 16) * (7168 // 32) * 1024
+    # H not a multiple of 32: every 16-row band spans ceil(H / 32) KiB
+    t = m.make_cfg(T=77, H=520, E=6, k=2, I=264, m_tile=32, x_layout=m.MOE_LAYOUT_TILED)
+    r16 = (m.moe_max_rows(t) + 15) // 16 * 16
+    assert m.moe_x_perm_bytes(t) == r16 // 16 * 17 * 1024
+    assert m.moe_x_perm_bytes(_dsv3(x_layout=3)) == ctypes.c_size_t(-1).value
+
+
 def test_entry_points_reject_bad_arguments_before_any_launch():
     c = m.make_cfg(T=16, H=64, E=8, k=2, I=64)
     lib = _ffi.lib()
@@ -132,6 +149,10 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
     st = lib.moe_grouped_ffn(ctypes.byref(c), 10**6, fake, None, fake, ctypes.byref(w), None, fake, None, fake,
                              1 << 20, None)
     assert st == m.MOE_ERR_WORKSPACE
+    ct = m.make_cfg(T=16, H=64, E=8, k=2, I=64, m_tile=16, x_layout=m.MOE_LAYOUT_TILED)
+    st = lib.moe_grouped_ffn(ctypes.byref(ct), 32, fake, None, fake, ctypes.byref(w), None, fake, None, fake,
+                             1 << 30, None)
+    assert st == m.MOE_ERR_INVALID_ARG and "n_rows_cap" in m.moe_last_error()
     st = lib.moe_combine(ctypes.byref(c), fake, None, fake, None, fake, None)
     assert st == m.MOE_ERR_INVALID_ARG
     st = lib.moe_layer(ctypes.byref(c), fake, None, ctypes.byref(w), fake, None, fake, 1 << 40, None)

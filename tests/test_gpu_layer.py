@@ -138,6 +138,48 @@ def test_layer_full_size_sampled(name, odt, tiled):
     assert err <= _tol(s), err
 
 
+@pytest.mark.parametrize("shape", [
+    synth.config("c3_dsv3_bf16").with_(T=300),
+    synth.config("c2_mixtral_bf16").with_(T=200),
+    # H and I not multiples of 32: the tiled rows carry zero column padding
+    synth.MoeShape("ragged_shared", T=77, H=520, E=6, k=2, I=264, shared=True, I_shared=136, seed=9),
+])
+def test_layer_equals_its_stage_calls(shape):
+    """moe_layer is route -> permute -> grouped_ffn -> combine run with m_tile
+    16 and the tiled x_perm: the four stage calls with that cfg give the same
+    bits, and they match the oracle."""
+    s = shape
+    rc = router_case(s, s.T)
+    T = rc["x"].shape[0]
+    (wg, wu, wd), sh = _weights(s)
+    shg, shu, shd = sh if sh else (None, None, None)
+    w = moe.weights(wg, wu, wd, sh_gate=shg, sh_up=shu, sh_down=shd)
+    w, _buf = moe.tile_weights(lib_cfg(s, T=T), w, dev())
+    layer = _run_layer(s, rc, T, moe.MOE_F32, moe.MOE_BF16, tiled=True)
+    c = lib_cfg(s, T=T, y_dtype=moe.MOE_F32, out_dtype=moe.MOE_BF16, m_tile=16, x_layout=moe.MOE_LAYOUT_TILED)
+    rows = moe.moe_max_rows(c)
+    i32 = dict(dtype=torch.int32, device=dev())
+    ids, tw = torch.empty((T, s.k), **i32), torch.empty((T, s.k), dtype=torch.float32, device=dev())
+    counts, offs = torch.empty(s.E, **i32), torch.empty(s.E + 1, **i32)
+    row_src, tok_row = torch.empty(rows, **i32), torch.empty((T, s.k), **i32)
+    x_perm = moe.x_perm_buffer(c, dev())
+    assert x_perm.numel() == moe.moe_x_perm_bytes(c)
+    x_perm.fill_(0xFF)  # NaN bf16 pattern: everything the FFN reads must be written by permute
+    y_rows = torch.empty((rows, s.H), dtype=torch.float32, device=dev())
+    y_sh = torch.empty((T, s.H), dtype=torch.float32, device=dev()) if s.shared else None
+    out = torch.empty((T, s.H), dtype=torch.bfloat16, device=dev())
+    moe.moe_route(c, rc["x"], rc["w_r"], rc["bias"], None, None, ids, tw,
+                  moe.workspace(c, moe.MOE_STAGE_ROUTE, dev()))
+    moe.moe_permute(c, rc["x"], None, ids, counts, offs, row_src, tok_row, x_perm, None,
+                    moe.workspace(c, moe.MOE_STAGE_PERMUTE, dev()))
+    moe.moe_grouped_ffn(c, rows, x_perm, None, offs, w, None, y_rows, y_sh,
+                        moe.workspace(c, moe.MOE_STAGE_FFN, dev()))
+    moe.moe_combine(c, y_rows, tok_row, tw, y_sh, out)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), layer.view(torch.int16))
+    assert rel_err_bf16_out(out.float().cpu().numpy(), _oracle_tokens(s, rc, np.arange(T))) <= 1e-2
+
+
 def test_layer_is_deterministic():
     s = synth.config("c4_qwen3_skew_bf16")
     rc = router_case(s, 3000)
