@@ -18,7 +18,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libexpert_layer_amd.so")
-SOURCES = ["capi.cpp", "route.hip", "permute.hip", "gemm_bf16.hip", "gemm_f32.hip", "combine.hip"]
+SOURCES = ["capi.cpp", "route.hip", "permute.hip", "gemm_bf16.hip", "gemm_fp8.hip", "gemm_f32.hip", "combine.hip"]
+VGPR_FORM = {"gemm_fp8.hip"}
 ARCH = "gfx950"
 
 
@@ -35,6 +36,9 @@ def _flags(src: str):
         f += [f"--offload-arch={ARCH}", "-x", "hip",
               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
               "-munsafe-fp-atomics"]
+        if src in VGPR_FORM:
+            # MFMA results in VGPRs: the fp8 path promotes every MFMA result on the VALU
+            f += ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]
     else:
         f += ["-D__HIP_PLATFORM_AMD__"]
     return f

@@ -76,6 +76,8 @@ moe_status check_cfg(const moe_cfg* cp) {
         if (c.H % 128 || c.I % 128)
             return fail(MOE_ERR_INVALID_ARG, "fp8 needs H and I multiples of 128 (H=%d, I=%d)", c.H, c.I);
         if (c.has_shared) return fail(MOE_ERR_UNSUPPORTED, "fp8 with a shared expert");
+        if (c.H > 16384 || c.I > 16384)
+            return fail(MOE_ERR_UNSUPPORTED, "fp8 supports H and I up to 16384 (H=%d, I=%d)", c.H, c.I);
     }
     if (c.m_tile < 0 || c.m_tile > 4096) return fail(MOE_ERR_INVALID_ARG, "m_tile=%d must be in [0, 4096]", c.m_tile);
     if (c.x_layout != MOE_LAYOUT_ROWMAJOR && c.x_layout != MOE_LAYOUT_TILED)
@@ -274,7 +276,6 @@ moe_status permute_enqueue(const moe_cfg& c, const void* x, const float* x_scale
 moe_status ffn_enqueue(const moe_cfg& c, int64_t n_rows_cap, const void* x_rows, const float* x_scale,
                        const int32_t* offsets, const moe_weights& w, const void* x_tokens, void* y_rows,
                        void* y_shared, void* ws, hipStream_t s) {
-    (void)x_scale;
     moe::FfnOperands op{x_rows, x_tokens, 0, 0, y_rows, y_shared};
     const XPermGeom g = x_perm_geom(c);
     if (g.tiled) {
@@ -292,7 +293,8 @@ moe_status ffn_enqueue(const moe_cfg& c, int64_t n_rows_cap, const void* x_rows,
         e = moe::launch_gemm_f32(c, f.max_tiles, n_rows_cap, op.x_rows, offsets, w, op.x_tokens, op.y_rows,
                                  op.y_shared, f.wk, f.h, f.h_sh, s);
     else
-        return fail(MOE_ERR_UNSUPPORTED, "fp8 grouped FFN is not built");
+        e = moe::launch_gemm_fp8(c, f.max_tiles, n_rows_cap, x_rows, x_scale, offsets, w, y_rows, f.wk, f.h,
+                                 f.h_scale, s);
     if (e != hipSuccess) return hip_fail(e, "moe_grouped_ffn");
     return MOE_OK;
 }
@@ -411,7 +413,6 @@ moe_status moe_grouped_ffn(const moe_cfg* cfg, int64_t n_rows_cap, const void* x
         if (!tiled) REQUIRE(x_tokens, "x_tokens");
         REQUIRE(y_shared, "y_shared");
     }
-    if (c.act_dtype == MOE_FP8_E4M3) return fail(MOE_ERR_UNSUPPORTED, "fp8 grouped FFN is not built");
     const size_t need = ffn_carve(c, n_rows_cap, nullptr).bytes;
     if ((st = check_ws(ws, ws_bytes, need)) != MOE_OK) return st;
     if (n_rows_cap == 0 && !(c.has_shared && c.T > 0)) return MOE_OK;

@@ -71,7 +71,7 @@ def lib():
         L.orc_dispatch.restype = i32
         L.orc_expert_ffn.argtypes = [i64, i64, i64, i32, P, i32, P, P, P, i32, P]
         L.orc_expert_ffn.restype = None
-        L.orc_expert_ffn_fp8.argtypes = [i64, i64, i64, P, P, P, P, P, P, P, P, P]
+        L.orc_expert_ffn_fp8.argtypes = [i64, i64, i64, P, P, P, P, P, P, P, P, P, P]
         L.orc_expert_ffn_fp8.restype = None
         L.orc_combine.argtypes = [i64, i32, i64, P, P, P, P, P]
         L.orc_combine.restype = None
@@ -212,8 +212,9 @@ def expert_ffn(x_rows: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray, w_down:
     return y
 
 
-def expert_ffn_fp8(xq, xs, wg, sg, wu, su, wd, sd) -> np.ndarray:
-    """y [n][H] (fp64) of one fp8 block-scaled SwiGLU expert; see orc_expert_ffn_fp8."""
+def expert_ffn_fp8(xq, xs, wg, sg, wu, su, wd, sd, return_h: bool = False):
+    """y [n][H] (fp64) of one fp8 block-scaled SwiGLU expert; see orc_expert_ffn_fp8.
+    With return_h, also the SwiGLU intermediate a [n][I] before its requantisation."""
     xq, xs, wg, sg, wu, su, wd, sd = (_c(a) for a in (xq, xs, wg, sg, wu, su, wd, sd))
     n, H = xq.shape
     I = wg.shape[0]
@@ -221,9 +222,42 @@ def expert_ffn_fp8(xq, xs, wg, sg, wu, su, wd, sd) -> np.ndarray:
     assert xs.shape == (n, H // 128) and sg.shape == (I // 128, H // 128)
     assert sd.shape == (H // 128, I // 128) and wd.shape == (H, I)
     y = np.empty((n, H), dtype=np.float64)
+    a = np.empty((n, I), dtype=np.float64) if return_h else None
     lib().orc_expert_ffn_fp8(n, H, I, _p(xq), _p(xs), _p(wg), _p(sg), _p(wu), _p(su),
-                             _p(wd), _p(sd), _p(y))
-    return y
+                             _p(wd), _p(sd), _p(y), _p(a))
+    return (y, a) if return_h else y
+
+
+def fp8_h_alternatives(a: np.ndarray, eta: float):
+    """The requantisation decisions of the fp8 intermediate that a computation
+    in fp32 may take the other way.  For each row and 128-column block of a
+    (fp64, [n][I]) the decision is the one orc_expert_ffn_fp8 takes:
+    s = fp32(max|fp32(a)|) / 448, v = fp32(fp32(a) / s), code = e4m3_rne_sat(v).
+    A decision is ambiguous when v lies within eta * max(|v|, 2^-6) of the
+    midpoint between its two neighbouring e4m3 values: a value of a computed
+    with fp32 rounding (accumulation, exponential, division) can then land on
+    either side.  Returns, per row, a list of (column i, dh): dh is the change
+    of the dequantised intermediate a'_i when the other neighbour is taken."""
+    a32 = np.asarray(a, dtype=np.float64).astype(np.float32)
+    n, I = a32.shape
+    assert I % 128 == 0
+    vals = e4m3_to_f64(np.arange(0, 0x7F, dtype=np.uint8))  # the finite non-negative values, ascending
+    blk = a32.reshape(n, I // 128, 128)
+    amax = np.abs(blk).max(axis=2)
+    s = np.where(amax > 0, (amax / np.float32(448.0)).astype(np.float32), np.float32(1.0))
+    v = (blk / s[:, :, None]).astype(np.float32).astype(np.float64)
+    av = np.minimum(np.abs(v), 448.0)
+    hi_i = np.clip(np.searchsorted(vals, av, side="left"), 1, len(vals) - 1)
+    lo, hi = vals[hi_i - 1], vals[hi_i]
+    mid = 0.5 * (lo + hi)
+    amb = np.abs(av - mid) <= eta * np.maximum(av, 2.0 ** -6)
+    chosen = e4m3_to_f64(e4m3_rne_sat(v.reshape(-1))).reshape(v.shape)
+    other = np.where(np.abs(chosen) == lo, hi, lo) * np.sign(v)
+    dh = (other - chosen) * s[:, :, None].astype(np.float64)
+    out = [[] for _ in range(n)]
+    for r, b, j in zip(*np.nonzero(amb)):
+        out[r].append((int(b * 128 + j), float(dh[r, b, j])))
+    return out
 
 
 def combine(y_rows: np.ndarray, tok_row: np.ndarray, topk_w: np.ndarray,

@@ -468,10 +468,11 @@ void orc_expert_ffn(int64_t n, int64_t H, int64_t I, int x_dtype, const void *x_
  *   s       = amax / 448 as an fp32 division  (s = 1 when amax == 0)
  *   q_i     = e4m3_rne_sat( fp32(a32_i / s) )               (fp32 division)
  *   a'_i    = e4m3(q_i) * s
- *   y[r][h] = sum_i a'_i * Wd[h][i]. */
+ *   y[r][h] = sum_i a'_i * Wd[h][i].
+ * a_out (NULL allowed) receives a [n][I] before the requantisation. */
 void orc_expert_ffn_fp8(int64_t n, int64_t H, int64_t I, const uint8_t *xq, const float *xs,
                         const uint8_t *wg, const float *sg, const uint8_t *wu, const float *su,
-                        const uint8_t *wd, const float *sd, double *y) {
+                        const uint8_t *wd, const float *sd, double *y, double *a_out) {
     int64_t HB = H / 128, IB = I / 128;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t r = 0; r < n; ++r) {
@@ -489,6 +490,7 @@ void orc_expert_ffn_fp8(int64_t n, int64_t H, int64_t I, const uint8_t *xq, cons
                     u += xr[h] * wuv;
                 }
                 a[i] = silu(g) * u;
+                if (a_out) a_out[r * I + i] = a[i];
             }
             for (int64_t b = 0; b < IB; ++b) {
                 float amax = 0.0f;

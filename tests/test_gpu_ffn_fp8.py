@@ -1,0 +1,160 @@
+"""GPU parity of the fp8 (OCP e4m3) grouped SwiGLU FFN against the oracle.
+
+The operands are e4m3 codes with fp32 block scales (1 x 128 per row for the
+dispatched rows, 128 x 128 for the weights); the oracle dequantises them
+exactly in fp64 and requantises the SwiGLU intermediate per row and 128
+columns, as the layer does.
+
+That requantisation turns floating point into integer codes.  Both sides take
+each decision in fp32, but from values of the intermediate that differ by
+fp32 rounding (accumulation order, exponential), so where a value sits within
+that rounding of an e4m3 midpoint either neighbour is a correct code.  The
+oracle lists those ambiguous decisions (fp8_h_alternatives, within 2^-12 of a
+midpoint, relative: five times the largest distance observed for a flipped
+code), and a row matches when its output equals the oracle's for some choice
+of at most two of them.  One flip moves a whole output row by up to ~7% of
+rms(ref), which is what the plain comparison of a large layer would otherwise
+report.  Bounds on the resolved difference: max|err| / rms(ref) <= 4e-2 and
+rms(err) / rms(ref) <= 1e-3 (a regression detector: a wrong scale or a dropped
+K block moves every row), 2.5e-3 for bf16 outputs, whose round-to-nearest
+storage alone contributes 2^-9 / sqrt(3) ~ 1.1e-3."""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import expert_layer_amd as moe
+import oracle
+import synth
+from tests._cases import dev
+
+pytestmark = pytest.mark.gpu
+
+TOL = 4e-2
+TOL_RMS = 1e-3
+TOL_RMS_BF16 = 2.5e-3
+ETA = 2.0 ** -12
+
+
+def _u8(t):
+    return t.detach().contiguous().cpu().numpy().astype(np.uint8)
+
+
+def _f32(t):
+    return t.detach().contiguous().cpu().numpy().astype(np.float32)
+
+
+def _inputs(E, H, I, n_rows, seed, device):
+    s = synth.MoeShape("fp8t", T=max(n_rows, 1), H=H, E=E, k=1, I=I, dtype="fp8", seed=seed)
+    wq = [synth.fp8_expert_weights(s, e, device) for e in range(E)]
+    stack = [torch.stack([w[i] for w in wq]) for i in range(6)]  # wg, sg, wu, su, wd, sd
+    xq, xs = synth.fp8_rows(s, max(n_rows, 1), device)
+    return s, wq, stack, xq, xs
+
+
+def _run(E, H, I, counts, ydt, extra_rows, seed):
+    d = dev()
+    n = int(sum(counts))
+    cap = n + extra_rows
+    s, wq, (wg, sg, wu, su, wd, sd), xq, xs = _inputs(E, H, I, cap, seed, d)
+    offs = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32, device=d)
+    c = moe.make_cfg(T=max(cap, 1), H=H, E=E, k=1, I=I, act_dtype=moe.MOE_FP8_E4M3, y_dtype=ydt)
+    assert moe.moe_validate(c) == moe.MOE_OK, moe.moe_last_error()
+    ytd = torch.float32 if ydt == moe.MOE_F32 else torch.bfloat16
+    sentinel = -12345.0
+    y = torch.full((max(cap, 1), H), sentinel, dtype=ytd, device=d)
+    ws = moe.workspace(c, moe.MOE_STAGE_FFN, d, n_rows_cap=cap)
+    w = moe.weights(wg, wu, wd, s_gate=sg, s_up=su, s_down=sd)
+    moe.moe_grouped_ffn(c, cap, xq, xs, offs, w, None, y, None, ws)
+    torch.cuda.synchronize()
+    return wq, xq, xs, y, sentinel
+
+
+def _resolve(resid, alts, WD):
+    """The smallest max|resid - sum of flips| over the row's ambiguous
+    decisions, choosing none, one or two of them."""
+    best = resid
+    cands = alts[:64]
+    cols = [dh * WD[:, i] for i, dh in cands]
+    for k in (1, 2):
+        for sub in itertools.combinations(range(len(cands)), k):
+            r = resid - sum(cols[j] for j in sub)
+            if np.abs(r).max() < np.abs(best).max():
+                best = r
+    return best
+
+
+def _check_rows(wq, xq, xs, y, rows_by_expert):
+    """Oracle on the listed rows of each expert, flips of ambiguous h codes
+    resolved; returns (max err, rms err) / rms(ref) and the number of rows
+    that needed a flip."""
+    refs, res = [], []
+    flipped = 0
+    for e, rows in rows_by_expert.items():
+        if len(rows) == 0:
+            continue
+        rows = np.asarray(rows)
+        wg, sg, wu, su, wd, sd = (_u8(t) if i % 2 == 0 else _f32(t) for i, t in enumerate(wq[e]))
+        ref, a = oracle.expert_ffn_fp8(_u8(xq[rows]), _f32(xs[rows]), wg, sg, wu, su, wd, sd, return_h=True)
+        alts = oracle.fp8_h_alternatives(a, ETA)
+        WD = oracle.e4m3_to_f64(wd) * np.repeat(np.repeat(sd.astype(np.float64), 128, 0), 128, 1)
+        got = y[torch.as_tensor(rows, device=y.device)].float().cpu().numpy().astype(np.float64)
+        for r in range(len(rows)):
+            resid = got[r] - ref[r]
+            if alts[r]:
+                rr = _resolve(resid, alts[r], WD)
+                flipped += int(np.abs(rr).max() < np.abs(resid).max())
+                resid = rr
+            res.append(resid)
+        refs.append(ref)
+    ref = np.concatenate(refs)
+    res = np.stack(res)
+    scale = np.sqrt(np.mean(ref ** 2))
+    return float(np.abs(res).max() / scale), float(np.sqrt(np.mean(res ** 2)) / scale), flipped
+
+
+@pytest.mark.parametrize("H,I,counts,ydt,extra", [
+    (512, 256, [37, 0, 5, 300, 64, 1, 0, 257], moe.MOE_F32, 0),   # unaligned offsets, empty experts, 2 tiles
+    (384, 384, [129, 3, 260], moe.MOE_BF16, 11),                  # odd K blocks, a partial GEMM2 N tile
+    (1024, 512, [600], moe.MOE_BF16, 0),                          # one expert over 3 M tiles
+    (256, 128, [1, 1, 1, 1], moe.MOE_F32, 5),                     # single rows
+])
+def test_grouped_ffn_fp8_matches_oracle(H, I, counts, ydt, extra):
+    E = len(counts)
+    wq, xq, xs, y, sentinel = _run(E, H, I, counts, ydt, extra, seed=H + 7 * I)
+    oc = np.concatenate([[0], np.cumsum(counts)]).astype(int)
+    rows = {e: list(range(oc[e], oc[e + 1])) for e in range(E)}
+    err, rms, flipped = _check_rows(wq, xq, xs, y, rows)
+    assert err <= TOL and rms <= (TOL_RMS if ydt == moe.MOE_F32 else TOL_RMS_BF16), (err, rms, flipped)
+    # rows past expert_offsets[E] are not written
+    if extra:
+        assert torch.all(y[oc[-1]:] == torch.tensor(sentinel, dtype=y.dtype, device=y.device))
+
+
+def test_grouped_ffn_fp8_full_size_sampled():
+    """The c5 workload: 65536 dispatched rows over 8 experts (Zipf(1.0) counts),
+    H = 7168, I = 2048, bf16 output; the oracle checks a seeded sample of rows
+    of every expert, including each expert's first and last row."""
+    s = synth.config("c5_dsv3_ep_fp8")
+    counts = synth.fp8_counts(s)
+    assert sum(counts) == s.T
+    d = dev()
+    wq = [synth.fp8_expert_weights(s, e, d) for e in range(s.E)]
+    wg, sg, wu, su, wd, sd = (torch.stack([w[i] for w in wq]) for i in range(6))
+    xq, xs = synth.fp8_rows(s, s.T, d)
+    offs = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32, device=d)
+    c = moe.make_cfg(T=s.T, H=s.H, E=s.E, k=1, I=s.I, act_dtype=moe.MOE_FP8_E4M3, y_dtype=moe.MOE_BF16)
+    y = torch.empty((s.T, s.H), dtype=torch.bfloat16, device=d)
+    ws = moe.workspace(c, moe.MOE_STAGE_FFN, d, n_rows_cap=s.T)
+    w = moe.weights(wg, wu, wd, s_gate=sg, s_up=su, s_down=sd)
+    moe.moe_grouped_ffn(c, s.T, xq, xs, offs, w, None, y, None, ws)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(s.seed)
+    oc = np.concatenate([[0], np.cumsum(counts)]).astype(int)
+    rows = {}
+    for e in range(s.E):
+        pick = rng.choice(np.arange(oc[e], oc[e + 1]), size=min(3, counts[e]), replace=False)
+        rows[e] = sorted(set(pick.tolist()) | {oc[e], oc[e + 1] - 1})
+    err, rms, flipped = _check_rows(wq, xq, xs, y, rows)
+    assert err <= TOL and rms <= TOL_RMS_BF16, (err, rms, flipped)

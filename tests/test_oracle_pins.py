@@ -342,6 +342,41 @@ def test_expert_ffn_fp8_matches_numpy_and_torch():
     a2 = (q * s.astype(np.float64)).reshape(5, 384)
     ref = a2 @ D.T
     np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-10 * np.abs(ref).max())
+    # the intermediate before requantisation
+    got2, a_or = oracle.expert_ffn_fp8(*(to_np(t) for t in (xq, xs, wg, sg, wu, su, wd, sd)), return_h=True)
+    np.testing.assert_array_equal(got2, got)
+    a64 = g / (1 + np.exp(-g)) * u
+    np.testing.assert_allclose(a_or, a64, rtol=1e-12, atol=1e-12 * np.abs(a64).max())
+
+
+def test_fp8_h_alternatives_flags_midpoints():
+    """Rows of 128 values with amax = 448, so the block scale is exactly 1 and
+    v = a: e4m3 neighbours around 1 are 1 and 1.125 (midpoint 1.0625), around
+    300 are 288 and 320 (midpoint 304), and 2^-9, 2^-8 below 2^-6 (midpoint
+    1.5 * 2^-9).  The helper flags exactly the values near a midpoint and gives
+    the step to the other neighbour (ties go to the even code)."""
+    a = np.full((1, 128), 1.03, dtype=np.float64)
+    a[0, 0] = 448.0
+    a[0, 1] = 1.0625                     # exact tie -> 1.0 (even); other = 1.125
+    a[0, 2] = 1.0625 * (1 + 2.0 ** -20)  # just above -> 1.125; other = 1.0
+    a[0, 3] = -1.0625                    # tie -> -1.0; other = -1.125
+    a[0, 4] = 304.0 * (1 - 2.0 ** -16)   # just below 304 -> 288; other = 320
+    a[0, 5] = 1.5 * 2.0 ** -9            # subnormal tie -> 2^-8 (even); other = 2^-9
+    a[0, 6] = 0.0
+    a[0, 7] = 1.0625 * (1 + 2.0 ** -8)   # far from the midpoint
+    alt = dict(oracle.fp8_h_alternatives(a, 2.0 ** -12)[0])
+    assert set(alt) == {1, 2, 3, 4, 5}
+    assert alt[1] == 0.125 and alt[2] == -0.125 and alt[3] == -0.125
+    assert alt[4] == 32.0 and alt[5] == -(2.0 ** -9)
+    # a tighter eta drops the values that are not exact ties
+    tight = dict(oracle.fp8_h_alternatives(a, 2.0 ** -22)[0])
+    assert set(tight) == {1, 3, 5}
+    # scale != 1: amax 224 gives s = 0.5, v = 2 a, dh in units of a
+    b = np.full((1, 128), 1.03, dtype=np.float64)
+    b[0, 0] = 224.0
+    b[0, 1] = 1.0625 / 2
+    alt_b = dict(oracle.fp8_h_alternatives(b, 2.0 ** -12)[0])
+    assert alt_b[1] == 0.125 * 0.5
 
 
 def test_fp8_power_of_two_scales_are_exact():
