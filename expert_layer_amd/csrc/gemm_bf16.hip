@@ -30,34 +30,38 @@
 // LDS chunks of 16 B are XOR-swizzled by row, physical chunk = logical ^
 // ((row >> 1) & 3) ^ ((row >> 3) & 1): a fragment read of 16 consecutive rows
 // (one pass of ds_read_b128 through the 64 banks of gfx950's LDS) touches 16
-// distinct 16-byte bank groups, and so does any 8 consecutive rows.  Tiles are ordered (M tile,
-// N tile) with N fastest and remapped so that a contiguous run lives on one
-// XCD: the N tiles of one M tile share its A panel in that XCD's L2.
+// distinct 16-byte bank groups, and so does any 8 consecutive rows.
+// Launch order: the work list (see ffn_build_tiles) remapped so that a
+// contiguous run of items lives on one XCD and shares its L2.
 #include "common.hpp"
 
 namespace moe {
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 32, NST = 4, NTH = 256;
+constexpr int BM = 256, BN = 256, BK = 32, NTH = 256;
+constexpr int NST = 4;                   // LDS stages in the ring (4 x 32 KiB; 5 measured no faster)
 constexpr int kSlots = BM * 4;           // 16-byte slots of one operand in one stage
 constexpr uint32_t kOOB = 0x40000000u;   // past every tile descriptor: the load returns zero
 
 typedef __attribute__((address_space(3))) void* lds_t;
 
-// The four stage buffers, [A: 256 rows x 64 B][B: 256 rows x 64 B] each.  They
-// are distinct objects so that the compiler can tell which buffer an in-flight
-// LDS DMA writes and never waits for a load into another buffer.
+// The stage buffers, [A: 256 rows x 64 B][B: 256 rows x 64 B] each.  They are
+// distinct objects so that the compiler can tell which buffer an in-flight LDS
+// DMA writes and never waits for a load into another buffer.
 __shared__ i32x4 ring0[2 * kSlots];
 __shared__ i32x4 ring1[2 * kSlots];
 __shared__ i32x4 ring2[2 * kSlots];
 __shared__ i32x4 ring3[2 * kSlots];
+__shared__ i32x4 ring4[2 * kSlots];
 
 template <int BUF>
 __device__ __forceinline__ i32x4* ring() {
+    static_assert(BUF < NST, "ring buffer index");
     if constexpr (BUF == 0) return ring0;
     else if constexpr (BUF == 1) return ring1;
     else if constexpr (BUF == 2) return ring2;
-    else return ring3;
+    else if constexpr (BUF == 3) return ring3;
+    else return ring4;
 }
 
 // Workgroup barrier without a memory fence (a fence would wait for every
@@ -183,7 +187,7 @@ __device__ __forceinline__ void stage(const Dma& d, int s, int wave, int lane, i
     __builtin_amdgcn_sched_barrier(0);
     // k step 1: hand buffer BUF back to the DMA and start on stage s+1
     wait_lgkm0();     // every read of buffer BUF by this wave has returned
-    wait_vm<16>();    // this wave's loads of stage s+1 have landed (s+2, s+3 may be in flight)
+    wait_vm<(NST - 2) * 8>();  // this wave's loads of stage s+1 have landed (s+2 .. s+NST-1 may be in flight)
     barrier_lds();    // ... everybody's have, and everybody is done with buffer BUF
     dma_stage<MODE, BUF>(d, s + NST, wave, lane);
     read_frags<NRB, (BUF + 1) % NST, 0>(wave, lane, fa[0], fb[0]);
@@ -269,20 +273,23 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, int mt, int g, int r
     }
     i32x4 fa[2][NRB], fb[2][2];
 
+    static_assert(NST == 4 || NST == 5, "the prologue and the loop body are written for 4 or 5 stages");
     dma_stage<MODE, 0>(d, 0, wave, lane);
     dma_stage<MODE, 1>(d, 1, wave, lane);
     dma_stage<MODE, 2>(d, 2, wave, lane);
     dma_stage<MODE, 3>(d, 3, wave, lane);
-    wait_vm<24>();
+    if constexpr (NST == 5) dma_stage<MODE, NST - 1>(d, 4, wave, lane);
+    wait_vm<(NST - 1) * 8>();
     barrier_lds();
     read_frags<NRB, 0, 0>(wave, lane, fa[0], fb[0]);
     // stages past the end load zeros, so the loop runs in whole turns of the ring
-    const int nsteps4 = (d.nsteps + NST - 1) & ~(NST - 1);
-    for (int s = 0; s < nsteps4; s += NST) {
+    const int nturns = (d.nsteps + NST - 1) / NST;
+    for (int s = 0; s < nturns * NST; s += NST) {
         stage<MODE, NRB, 0>(d, s, wave, lane, fa, fb, acc0, acc1);
         stage<MODE, NRB, 1>(d, s + 1, wave, lane, fa, fb, acc0, acc1);
         stage<MODE, NRB, 2>(d, s + 2, wave, lane, fa, fb, acc0, acc1);
         stage<MODE, NRB, 3>(d, s + 3, wave, lane, fa, fb, acc0, acc1);
+        if constexpr (NST == 5) stage<MODE, NRB, NST - 1>(d, s + 4, wave, lane, fa, fb, acc0, acc1);
     }
     wait_vm<0>();  // no LDS DMA may outlive the workgroup
     wait_lgkm0();
@@ -364,13 +371,15 @@ ffn_gemm_bf16(GemmArgs p) {
 }  // namespace
 
 // ------------------------------------------------------------- tile list
+constexpr int kMBlock = 4;  // M tiles of one expert whose work items are interleaved
 // One workgroup of 1024 threads.  Group g < E covers rows [offsets[g],
 // offsets[g+1]); group E (the shared expert, when present) covers tokens
 // [0, T).  A group of n rows gets nmt = ceil(n / bm) tiles of height
-// ceil(ceil(n / nmt) / 32) * 32 (the last one shorter).  The work lists put,
-// for each group, N tile by N tile, all its M tiles next to each other: the M
-// tiles of one expert that share a weight panel run side by side on one XCD,
-// so the panel streams from HBM once and the second reader hits L2.
+// ceil(ceil(n / nmt) / 32) * 32 (the last one shorter).  The work lists take a
+// group's M tiles in blocks of four and, inside a block, N tile by N tile with
+// the block's M tiles next to each other: the items that run side by side on
+// one XCD share a few row panels and weight panels in its L2, so a panel
+// streams from HBM about once per block instead of once per N tile.
 __global__ void __launch_bounds__(1024)
 ffn_build_tiles(const int32_t* __restrict__ offsets, int E, int has_shared, int T, int bm, int rows_cap,
                 int4* __restrict__ tiles, int32_t* __restrict__ n_tiles, int2* __restrict__ work1, int nt1,
@@ -418,10 +427,16 @@ ffn_build_tiles(const int32_t* __restrict__ offsets, int E, int has_shared, int 
             const int re = min(e, rb + hgt);
             tiles[st + m] = int4{g, rb, re, 0};
         }
-        for (int nt = 0; nt < nt1; ++nt)
-            for (int m = 0; m < nmt; ++m) work1[st * nt1 + nt * nmt + m] = int2{st + m, nt};
-        for (int nt = 0; nt < nt2; ++nt)
-            for (int m = 0; m < nmt; ++m) work2[st * nt2 + nt * nmt + m] = int2{st + m, nt};
+        // blocks of kMBlock M tiles, N tile by N tile: 32 consecutive items (one
+        // XCD's CUs) share kMBlock row panels and 32 / kMBlock weight panels
+        int i1 = st * nt1, i2 = st * nt2;
+        for (int mb = 0; mb < nmt; mb += kMBlock) {
+            const int mc = min(kMBlock, nmt - mb);
+            for (int nt = 0; nt < nt1; ++nt)
+                for (int m = mb; m < mb + mc; ++m) work1[i1++] = int2{st + m, nt};
+            for (int nt = 0; nt < nt2; ++nt)
+                for (int m = mb; m < mb + mc; ++m) work2[i2++] = int2{st + m, nt};
+        }
     };
     if (tid < G) emit(tid, b0, e0, n0, start);
     if (tid == 0 && G > 1024) {
