@@ -156,7 +156,7 @@ def main():
     c = moe.make_cfg(T=T, H=H, E=E, k=k, I=I, n_groups=s.n_groups, topk_groups=s.topk_groups,
                      score_fn=moe.MOE_SCORE_SIGMOID if s.score == "sigmoid" else moe.MOE_SCORE_SOFTMAX,
                      renormalize=s.renormalize, routed_scale=s.routed_scale, has_shared=s.shared,
-                     I_shared=s.I_shared, act_dtype=moe.MOE_BF16, y_dtype=moe.MOE_F32, out_dtype=moe.MOE_BF16)
+                     I_shared=s.I_shared, act_dtype=moe.MOE_BF16, y_dtype=moe.MOE_BF16, out_dtype=moe.MOE_BF16)
 
     # ---- inputs, resident in HBM before timing
     t_gen = time.time()
@@ -211,13 +211,14 @@ def main():
         ms_step = ev0.elapsed_time(ev1) / a.steps
 
     # ---- per-stage breakdown: moe_layer is these four stage calls with m_tile 16
-    # and the tiled x_perm (bit-identical results); events between the stages on
-    # the launch stream
+    # and the indexed x_perm (the permute writes the maps, GEMM1 reads x through
+    # row_src; bit-identical results); events between the stages on the launch
+    # stream
     R = T * k
     c = moe.make_cfg(T=T, H=H, E=E, k=k, I=I, n_groups=s.n_groups, topk_groups=s.topk_groups,
                      score_fn=c.score_fn, renormalize=s.renormalize, routed_scale=s.routed_scale,
-                     has_shared=s.shared, I_shared=s.I_shared, act_dtype=moe.MOE_BF16, y_dtype=moe.MOE_F32,
-                     out_dtype=moe.MOE_BF16, m_tile=16, x_layout=moe.MOE_LAYOUT_TILED)
+                     has_shared=s.shared, I_shared=s.I_shared, act_dtype=moe.MOE_BF16, y_dtype=moe.MOE_BF16,
+                     out_dtype=moe.MOE_BF16, m_tile=16, x_layout=moe.MOE_LAYOUT_INDEXED)
     rows = moe.moe_max_rows(c)
     ids = torch.empty((T, k), dtype=torch.int32, device=dev)
     tw = torch.empty((T, k), dtype=torch.float32, device=dev)
@@ -226,8 +227,8 @@ def main():
     row_src = torch.empty(rows, dtype=torch.int32, device=dev)
     tok_row = torch.empty((T, k), dtype=torch.int32, device=dev)
     x_perm = moe.x_perm_buffer(c, dev)
-    y_rows = torch.empty((rows, H), dtype=torch.float32, device=dev)
-    y_sh = torch.empty((T, H), dtype=torch.float32, device=dev) if s.shared else None
+    y_rows = torch.empty((rows, H), dtype=torch.bfloat16, device=dev)
+    y_sh = torch.empty((T, H), dtype=torch.bfloat16, device=dev) if s.shared else None
     ws_r = moe.workspace(c, moe.MOE_STAGE_ROUTE, dev)
     ws_p = moe.workspace(c, moe.MOE_STAGE_PERMUTE, dev)
     ws_f = moe.workspace(c, moe.MOE_STAGE_FFN, dev)
@@ -239,7 +240,7 @@ def main():
         evs[1].record(stream)
         moe.moe_permute(c, x, None, ids, counts, offs, row_src, tok_row, x_perm, None, ws_p, stream)
         evs[2].record(stream)
-        moe.moe_grouped_ffn(c, rows, x_perm, None, offs, w, None, y_rows, y_sh, ws_f, stream)
+        moe.moe_grouped_ffn(c, rows, x, None, offs, w, None, y_rows, y_sh, ws_f, stream, row_src=row_src)
         evs[3].record(stream)
         moe.moe_combine(c, y_rows, tok_row, tw, y_sh, out, stream)
         evs[4].record(stream)
@@ -268,9 +269,11 @@ def main():
     w_bytes = 3.0 * E * H * I * 2 + 3.0 * H * I_sh * 2
     bytes_ = {
         "route": T * H * 2 + E * H * 2 + T * k * 8,
-        "permute": T * H * 2 + (R + T * bool(s.shared)) * H * 2 + T * k * 4 + 2 * R * 4,
-        "grouped_ffn": w_bytes + R * H * 2 + T * H * 2 * bool(s.shared) + (R + T * bool(s.shared)) * H * 4,
-        "combine": R * H * 4 + T * H * 4 * bool(s.shared) + T * H * 2 + T * k * 8,
+        # the maps only: ids read, counts/offsets/row_src/tok_row written (the
+        # payload gather is GEMM1's A load)
+        "permute": T * k * 4 + E * 8 + rows * 4 + T * k * 4,
+        "grouped_ffn": w_bytes + R * H * 2 + T * H * 2 * bool(s.shared) + (R + T * bool(s.shared)) * H * 2,
+        "combine": R * H * 2 + T * H * 2 * bool(s.shared) + T * H * 2 + T * k * 8,
     }
     tflops = layer_flop / (ms_step * 1e-3) / 1e12
     stages = {}
@@ -314,7 +317,7 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": a.workload, "T": T, "H": H, "E": E, "k": k, "I": I, "shared_experts": int(s.shared),
                    "I_shared": I_sh, "router": s.score, "n_groups": s.n_groups, "topk_groups": s.topk_groups,
-                   "routed_scale": s.routed_scale, "out_dtype": "bf16", "expert_out_dtype": "fp32",
+                   "routed_scale": s.routed_scale, "out_dtype": "bf16", "expert_out_dtype": "bf16",
                    "weight_layout": "row-major" if a.rowmajor_weights else "tiled"},
         "tokens_per_s": round(T / (ms_step * 1e-3), 1),
         "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),

@@ -21,7 +21,7 @@ from . import _ffi
 from ._ffi import (MOE_BF16, MOE_ERR_HIP, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE,
                    MOE_F32, MOE_FP8_E4M3, MOE_GROUP_MAX, MOE_GROUP_TOP2_SUM, MOE_OK, MOE_SCORE_SIGMOID,
                    MOE_SCORE_SOFTMAX, MOE_STAGE_FFN, MOE_STAGE_LAYER, MOE_STAGE_PERMUTE, MOE_STAGE_ROUTE,
-                   MOE_LAYOUT_ROWMAJOR, MOE_LAYOUT_TILED, moe_cfg, moe_weights)
+                   MOE_LAYOUT_ROWMAJOR, MOE_LAYOUT_TILED, MOE_LAYOUT_INDEXED, moe_cfg, moe_weights)
 
 __all__ = [
     "MoeError", "make_cfg", "weights", "workspace", "moe_validate", "moe_max_rows", "moe_workspace_bytes", "moe_ffn_workspace_bytes",
@@ -30,7 +30,7 @@ __all__ = [
     "MOE_OK", "MOE_ERR_INVALID_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE", "MOE_ERR_HIP",
     "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3", "MOE_SCORE_SOFTMAX", "MOE_SCORE_SIGMOID",
     "MOE_GROUP_TOP2_SUM", "MOE_GROUP_MAX", "MOE_STAGE_ROUTE", "MOE_STAGE_PERMUTE", "MOE_STAGE_FFN",
-    "MOE_STAGE_LAYER", "MOE_LAYOUT_ROWMAJOR", "MOE_LAYOUT_TILED", "moe_tiled_weights_bytes",
+    "MOE_STAGE_LAYER", "MOE_LAYOUT_ROWMAJOR", "MOE_LAYOUT_TILED", "MOE_LAYOUT_INDEXED", "moe_tiled_weights_bytes",
     "moe_tile_weights", "tile_weights", "moe_x_perm_bytes", "x_perm_buffer",
 ]
 
@@ -101,8 +101,9 @@ def moe_x_perm_bytes(cfg: moe_cfg) -> int:
 
 def x_perm_buffer(cfg: moe_cfg, device) -> torch.Tensor:
     """An x_perm buffer for cfg.x_layout: [moe_max_rows, H] in the activation
-    dtype when row-major, a flat byte buffer when tiled."""
-    if cfg.x_layout == MOE_LAYOUT_TILED:
+    dtype when row-major, a flat byte buffer when tiled (one byte, unused, when
+    indexed)."""
+    if cfg.x_layout in (MOE_LAYOUT_TILED, MOE_LAYOUT_INDEXED):
         return torch.empty(max(moe_x_perm_bytes(cfg), 1), dtype=torch.uint8, device=device)
     dt = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16, MOE_FP8_E4M3: torch.uint8}[cfg.act_dtype]
     return torch.empty((moe_max_rows(cfg), cfg.H), dtype=dt, device=device)
@@ -169,11 +170,13 @@ def moe_permute(cfg, x, x_scale, topk_ids, expert_counts, expert_offsets, row_sr
 
 
 def moe_grouped_ffn(cfg, n_rows_cap, x_rows, x_scale, expert_offsets, w: moe_weights, x_tokens, y_rows,
-                    y_shared, ws, stream=None):
+                    y_shared, ws, stream=None, row_src=None):
+    """row_src: the dispatch map of moe_permute, read with cfg.x_layout ==
+    MOE_LAYOUT_INDEXED (x_rows is then x itself)."""
     p, n = _ws(ws)
     _check(_ffi.lib().moe_grouped_ffn(ctypes.byref(cfg), int(n_rows_cap), _ptr(x_rows), _ptr(x_scale),
-                                      _ptr(expert_offsets), ctypes.byref(w), _ptr(x_tokens), _ptr(y_rows),
-                                      _ptr(y_shared), p, n, _stream(stream)))
+                                      _ptr(expert_offsets), _ptr(row_src), ctypes.byref(w), _ptr(x_tokens),
+                                      _ptr(y_rows), _ptr(y_shared), p, n, _stream(stream)))
 
 
 def moe_combine(cfg, y_rows, tok_row, topk_w, y_shared, out, stream=None):

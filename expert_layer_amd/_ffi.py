@@ -16,7 +16,7 @@ MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_GROUP_TOP2_SUM, MOE_GROUP_MAX = 0, 1
 MOE_STAGE_ROUTE, MOE_STAGE_PERMUTE, MOE_STAGE_FFN, MOE_STAGE_LAYER = 0, 1, 2, 3
-MOE_LAYOUT_ROWMAJOR, MOE_LAYOUT_TILED = 0, 1
+MOE_LAYOUT_ROWMAJOR, MOE_LAYOUT_TILED, MOE_LAYOUT_INDEXED = 0, 1, 2
 
 EXPORTS = ("moe_validate", "moe_max_rows", "moe_workspace_bytes", "moe_ffn_workspace_bytes",
            "moe_x_perm_bytes", "moe_tiled_weights_bytes", "moe_tile_weights", "moe_route", "moe_permute", "moe_grouped_ffn",
@@ -67,7 +67,7 @@ def lib() -> ctypes.CDLL:
         L.moe_route.restype = i32
         L.moe_permute.argtypes = [C, P, P, P, P, P, P, P, P, P, P, sz, P]
         L.moe_permute.restype = i32
-        L.moe_grouped_ffn.argtypes = [C, i64, P, P, P, W, P, P, P, P, sz, P]
+        L.moe_grouped_ffn.argtypes = [C, i64, P, P, P, P, W, P, P, P, P, sz, P]
         L.moe_grouped_ffn.restype = i32
         L.moe_combine.argtypes = [C, P, P, P, P, P, P]
         L.moe_combine.restype = i32

@@ -80,8 +80,13 @@ moe_status check_cfg(const moe_cfg* cp) {
             return fail(MOE_ERR_UNSUPPORTED, "fp8 supports H and I up to 16384 (H=%d, I=%d)", c.H, c.I);
     }
     if (c.m_tile < 0 || c.m_tile > 4096) return fail(MOE_ERR_INVALID_ARG, "m_tile=%d must be in [0, 4096]", c.m_tile);
-    if (c.x_layout != MOE_LAYOUT_ROWMAJOR && c.x_layout != MOE_LAYOUT_TILED)
+    if (c.x_layout != MOE_LAYOUT_ROWMAJOR && c.x_layout != MOE_LAYOUT_TILED && c.x_layout != MOE_LAYOUT_INDEXED)
         return fail(MOE_ERR_INVALID_ARG, "x_layout=%d", c.x_layout);
+    if (c.x_layout == MOE_LAYOUT_INDEXED) {
+        if (c.act_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "indexed x_perm is bf16 only");
+        if ((int64_t)c.T * c.H * 2 >= ((int64_t)1 << 32))
+            return fail(MOE_ERR_UNSUPPORTED, "indexed x_perm needs T*H*2 < 2^32");
+    }
     if (c.x_layout == MOE_LAYOUT_TILED) {
         if (c.act_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "tiled x_perm is bf16 only");
         if (c.m_tile % 16 || c.m_tile == 0)
@@ -113,7 +118,10 @@ int64_t ffn_max_tiles(const moe_cfg& c, int64_t n_rows_cap) {
     return (n_rows_cap + bm - 1) / bm + c.E + (c.has_shared ? (c.T + bm - 1) / bm : 0) + 1;
 }
 
-size_t route_ws(const moe_cfg& c) { return align_up((size_t)c.T * c.E * sizeof(float)); }
+// K-split partial logits of the router
+size_t route_ws(const moe_cfg& c) {
+    return align_up((size_t)moe::router_splits(c) * c.T * c.E * sizeof(float));
+}
 
 struct PermuteCarve {
     moe::PermuteWs ws;
@@ -173,7 +181,10 @@ XPermGeom x_perm_geom(const moe_cfg& c) {
     XPermGeom g{};
     const int64_t rows = max_rows_of(c);
     g.tiled = c.x_layout == MOE_LAYOUT_TILED;
-    if (g.tiled) {
+    if (c.x_layout == MOE_LAYOUT_INDEXED) {
+        g.rows_pad = rows;
+        g.bytes = 0;
+    } else if (g.tiled) {
         const size_t blk = (size_t)((c.H + 31) / 32) * 1024;  // one 16-row band
         g.rows_pad = (rows + 15) / 16 * 16;
         g.shared_off = (size_t)(g.rows_pad / 16) * blk;
@@ -186,11 +197,11 @@ XPermGeom x_perm_geom(const moe_cfg& c) {
 }
 
 // The configuration moe_layer runs its stages with: expert segments padded to
-// 16 rows, and x_perm tiled for bf16.
+// 16 rows, and for bf16 no x_perm (GEMM1 reads x through row_src).
 moe_cfg layer_stage_cfg(const moe_cfg& c) {
     moe_cfg s = c;
     s.m_tile = 16;
-    s.x_layout = c.act_dtype == MOE_BF16 ? MOE_LAYOUT_TILED : MOE_LAYOUT_ROWMAJOR;
+    s.x_layout = c.act_dtype == MOE_BF16 ? MOE_LAYOUT_INDEXED : MOE_LAYOUT_ROWMAJOR;
     return s;
 }
 
@@ -266,7 +277,8 @@ moe_status permute_enqueue(const moe_cfg& c, const void* x, const float* x_scale
                            float* x_perm_scale, void* ws, hipStream_t s) {
     const PermuteCarve pc = permute_carve(c, ws);
     const XPermGeom g = x_perm_geom(c);
-    const moe::PermuteLayout lay{g.tiled ? 1 : 0, (g.tiled && c.has_shared) ? g.rows_pad : -1};
+    const moe::PermuteLayout lay{g.tiled ? 1 : 0, (g.tiled && c.has_shared) ? g.rows_pad : -1,
+                                 c.x_layout == MOE_LAYOUT_INDEXED ? 0 : 1};
     hipError_t e = moe::launch_permute(c, x, x_scale, ids, counts, offsets, row_src, tok_row, x_perm, x_perm_scale,
                                        max_rows_of(c), pc.ws, lay, s);
     if (e != hipSuccess) return hip_fail(e, "moe_permute");
@@ -274,11 +286,14 @@ moe_status permute_enqueue(const moe_cfg& c, const void* x, const float* x_scale
 }
 
 moe_status ffn_enqueue(const moe_cfg& c, int64_t n_rows_cap, const void* x_rows, const float* x_scale,
-                       const int32_t* offsets, const moe_weights& w, const void* x_tokens, void* y_rows,
-                       void* y_shared, void* ws, hipStream_t s) {
-    moe::FfnOperands op{x_rows, x_tokens, 0, 0, y_rows, y_shared};
+                       const int32_t* offsets, const int32_t* row_src, const moe_weights& w, const void* x_tokens,
+                       void* y_rows, void* y_shared, void* ws, hipStream_t s) {
+    moe::FfnOperands op{x_rows, x_tokens, 0, 0, y_rows, y_shared, nullptr};
     const XPermGeom g = x_perm_geom(c);
-    if (g.tiled) {
+    if (c.x_layout == MOE_LAYOUT_INDEXED) {
+        op.row_src = row_src;
+        op.x_tokens = x_rows;  // x itself: the shared expert's operand too
+    } else if (g.tiled) {
         op.x_rows_tiled = 1;
         if (c.has_shared) {
             op.x_tokens = static_cast<const char*>(x_rows) + g.shared_off;
@@ -344,21 +359,19 @@ moe_status moe_route(const moe_cfg* cfg, const void* x, const void* w_router, co
     }
     REQUIRE(topk_ids, "topk_ids");
     REQUIRE(topk_w, "topk_w");
-    const bool need_ws = !logits_in && !logits_out;
+    const bool need_ws = !logits_in;
     if (need_ws && (st = check_ws(ws, ws_bytes, route_ws(c))) != MOE_OK) return st;
     if (c.T == 0) return MOE_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const float* l = logits_in;
-    float* copy = nullptr;
+    int nsplit = 1;
     if (!logits_in) {
-        float* dst = logits_out ? logits_out : static_cast<float*>(ws);
-        hipError_t e = moe::launch_router_logits(c, x, w_router, dst, s);
+        hipError_t e = moe::launch_router_logits(c, x, w_router, static_cast<float*>(ws), s);
         if (e != hipSuccess) return hip_fail(e, "moe_route (logits)");
-        l = dst;
-    } else if (logits_out) {
-        copy = logits_out;
+        l = static_cast<const float*>(ws);
+        nsplit = moe::router_splits(c);
     }
-    hipError_t e = moe::launch_route_select(c, l, bias, copy, topk_ids, topk_w, s);
+    hipError_t e = moe::launch_route_select(c, l, nsplit, bias, logits_out, topk_ids, topk_w, s);
     if (e != hipSuccess) return hip_fail(e, "moe_route (select)");
     return MOE_OK;
 }
@@ -375,7 +388,7 @@ moe_status moe_permute(const moe_cfg* cfg, const void* x, const float* x_scale, 
     REQUIRE(expert_offsets, "expert_offsets");
     REQUIRE(row_src, "row_src");
     REQUIRE(tok_row, "tok_row");
-    REQUIRE(x_perm, "x_perm");
+    if (c.x_layout != MOE_LAYOUT_INDEXED) REQUIRE(x_perm, "x_perm");
     if (c.act_dtype == MOE_FP8_E4M3) {
         REQUIRE(x_scale, "x_scale");
         REQUIRE(x_perm_scale, "x_perm_scale");
@@ -388,8 +401,9 @@ moe_status moe_permute(const moe_cfg* cfg, const void* x, const float* x_scale, 
 }
 
 moe_status moe_grouped_ffn(const moe_cfg* cfg, int64_t n_rows_cap, const void* x_rows, const float* x_scale,
-                           const int32_t* expert_offsets, const moe_weights* w, const void* x_tokens, void* y_rows,
-                           void* y_shared, void* ws, size_t ws_bytes, void* stream) {
+                           const int32_t* expert_offsets, const int32_t* row_src, const moe_weights* w,
+                           const void* x_tokens, void* y_rows, void* y_shared, void* ws, size_t ws_bytes,
+                           void* stream) {
     moe_status st = check_cfg(cfg);
     if (st != MOE_OK) return st;
     const moe_cfg& c = *cfg;
@@ -402,21 +416,25 @@ moe_status moe_grouped_ffn(const moe_cfg* cfg, int64_t n_rows_cap, const void* x
         REQUIRE(y_rows, "y_rows");
     }
     if (c.act_dtype == MOE_FP8_E4M3) REQUIRE(x_scale, "x_scale");
-    const bool tiled = c.x_layout == MOE_LAYOUT_TILED;
+    const bool tiled = c.x_layout == MOE_LAYOUT_TILED, indexed = c.x_layout == MOE_LAYOUT_INDEXED;
     if (tiled) {
         if (n_rows_cap != max_rows_of(c))
             return fail(MOE_ERR_INVALID_ARG, "tiled x_rows: n_rows_cap=%lld must equal moe_max_rows (%lld)",
                         (long long)n_rows_cap, (long long)max_rows_of(c));
         if (c.has_shared) REQUIRE(x_rows, "x_rows");
     }
+    if (indexed) {
+        if (n_rows_cap > 0) REQUIRE(row_src, "row_src");
+        if (c.has_shared) REQUIRE(x_rows, "x_rows");
+    }
     if (c.has_shared) {
-        if (!tiled) REQUIRE(x_tokens, "x_tokens");
+        if (!tiled && !indexed) REQUIRE(x_tokens, "x_tokens");
         REQUIRE(y_shared, "y_shared");
     }
     const size_t need = ffn_carve(c, n_rows_cap, nullptr).bytes;
     if ((st = check_ws(ws, ws_bytes, need)) != MOE_OK) return st;
     if (n_rows_cap == 0 && !(c.has_shared && c.T > 0)) return MOE_OK;
-    return ffn_enqueue(c, n_rows_cap, x_rows, x_scale, expert_offsets, *w, x_tokens, y_rows, y_shared, ws,
+    return ffn_enqueue(c, n_rows_cap, x_rows, x_scale, expert_offsets, row_src, *w, x_tokens, y_rows, y_shared, ws,
                        static_cast<hipStream_t>(stream));
 }
 
@@ -492,12 +510,15 @@ moe_status moe_layer(const moe_cfg* cfg, const void* w_router, const float* bias
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = moe::launch_router_logits(c, x, w_router, static_cast<float*>(l.scratch), s);
     if (e != hipSuccess) return hip_fail(e, "moe_layer (router)");
-    e = moe::launch_route_select(c, static_cast<float*>(l.scratch), bias, nullptr, l.ids, l.topk_w, s);
+    e = moe::launch_route_select(c, static_cast<float*>(l.scratch), moe::router_splits(c), bias, nullptr, l.ids,
+                                 l.topk_w, s);
     if (e != hipSuccess) return hip_fail(e, "moe_layer (select)");
     st = permute_enqueue(cs, x, nullptr, l.ids, l.counts, l.offsets, l.row_src, l.tok_row, l.x_perm, nullptr,
                          l.scratch, s);
     if (st != MOE_OK) return st;
-    st = ffn_enqueue(cs, max_rows_of(cs), l.x_perm, nullptr, l.offsets, *w, x, l.y_rows, l.y_shared, l.scratch, s);
+    const void* x_rows = cs.x_layout == MOE_LAYOUT_INDEXED ? x : l.x_perm;
+    st = ffn_enqueue(cs, max_rows_of(cs), x_rows, nullptr, l.offsets, l.row_src, *w, x, l.y_rows, l.y_shared,
+                     l.scratch, s);
     if (st != MOE_OK) return st;
     e = moe::launch_combine(c, l.y_rows, l.tok_row, l.topk_w, l.y_shared, out, s);
     if (e != hipSuccess) return hip_fail(e, "moe_layer (combine)");

@@ -4,9 +4,9 @@
 //
 //   out[t][h] = sum_{j<k} w[t][j] * y_rows[tok_row[t][j]][h]  (+ y_shared[t][h])
 //
-// One workgroup per token; every thread owns 8 consecutive columns and reads
-// them from the k expert rows with 16-byte loads.  Pure HBM streaming: the
-// expert rows are read once, the output written once.
+// One workgroup per token; threads own 8-column chunks and read them from
+// the k expert rows with 16-byte loads.  Pure HBM streaming: the expert rows
+// are read once, the output written once.
 #include "common.hpp"
 
 namespace moe {
@@ -34,6 +34,24 @@ __device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float (&v)[8]
     }
 }
 
+template <typename OT>
+__device__ __forceinline__ void store8(OT* o, const float (&acc)[8]) {
+    if constexpr (sizeof(OT) == 4) {
+        f32x4* p = reinterpret_cast<f32x4*>(o);
+        p[0] = f32x4{acc[0], acc[1], acc[2], acc[3]};
+        p[1] = f32x4{acc[4], acc[5], acc[6], acc[7]};
+    } else {
+        i32x4 p;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            p[i] = (int)((uint32_t)f32_to_bf16(acc[2 * i]) | ((uint32_t)f32_to_bf16(acc[2 * i + 1]) << 16));
+        *reinterpret_cast<i32x4*>(o) = p;
+    }
+}
+
+// One workgroup per token; thread i owns the 8-column chunks i and i + 256 of
+// each pass of 512 chunks, so the loads of both chunks' k rows are in flight
+// together.
 template <typename YT, typename OT>
 __global__ void __launch_bounds__(256)
 combine_kernel(const YT* __restrict__ y, const int32_t* __restrict__ tok_row, const float* __restrict__ tw,
@@ -46,32 +64,35 @@ combine_kernel(const YT* __restrict__ y, const int32_t* __restrict__ tok_row, co
         wts[threadIdx.x] = tw[(size_t)t * k + threadIdx.x];
     }
     __syncthreads();
-    for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
-        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    const int nchunk = H / 8;
+    for (int c0 = threadIdx.x; c0 < nchunk; c0 += 512) {
+        const int c1 = c0 + 256;
+        const bool two = c1 < nchunk;
+        float a0[8] = {0, 0, 0, 0, 0, 0, 0, 0}, a1[8] = {0, 0, 0, 0, 0, 0, 0, 0};
         for (int j = 0; j < k; ++j) {
-            float v[8];
-            load8<YT>(y + (size_t)rows[j] * H + c, v);
+            const YT* row = y + (size_t)rows[j] * H;
             const float wj = wts[j];
+            float v0[8], v1[8];
+            load8<YT>(row + c0 * 8, v0);
+            if (two) load8<YT>(row + c1 * 8, v1);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj, v[i], acc[i]);
+            for (int i = 0; i < 8; ++i) a0[i] = fmaf(wj, v0[i], a0[i]);
+            if (two)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) a1[i] = fmaf(wj, v1[i], a1[i]);
         }
         if (ysh) {
-            float v[8];
-            load8<YT>(ysh + (size_t)t * H + c, v);
+            float v0[8], v1[8];
+            load8<YT>(ysh + (size_t)t * H + c0 * 8, v0);
+            if (two) load8<YT>(ysh + (size_t)t * H + c1 * 8, v1);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] += v[i];
-        }
-        if constexpr (sizeof(OT) == 4) {
-            f32x4* o = reinterpret_cast<f32x4*>(out + (size_t)t * H + c);
-            o[0] = f32x4{acc[0], acc[1], acc[2], acc[3]};
-            o[1] = f32x4{acc[4], acc[5], acc[6], acc[7]};
-        } else {
-            i32x4 p;
+            for (int i = 0; i < 8; ++i) a0[i] += v0[i];
+            if (two)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                p[i] = (int)((uint32_t)f32_to_bf16(acc[2 * i]) | ((uint32_t)f32_to_bf16(acc[2 * i + 1]) << 16));
-            *reinterpret_cast<i32x4*>(out + (size_t)t * H + c) = p;
+                for (int i = 0; i < 8; ++i) a1[i] += v1[i];
         }
+        store8<OT>(out + (size_t)t * H + c0 * 8, a0);
+        if (two) store8<OT>(out + (size_t)t * H + c1 * 8, a1);
     }
 }
 

@@ -116,9 +116,12 @@ __device__ __forceinline__ int xcd_remap(int b, int n_valid) {
 // argument checks.  Each returns hipSuccess or the launch error.
 namespace moe {
 
+// The router writes router_splits(c) K-split partial logits [split][T][E]
+// (one for fp32); route_select sums them in split order.
+int router_splits(const moe_cfg& c);
 hipError_t launch_router_logits(const moe_cfg& c, const void* x, const void* w_router,
-                                float* logits, hipStream_t s);
-hipError_t launch_route_select(const moe_cfg& c, const float* logits, const float* bias,
+                                float* partial_logits, hipStream_t s);
+hipError_t launch_route_select(const moe_cfg& c, const float* logits, int nsplit, const float* bias,
                                float* logits_copy, int32_t* ids, float* w, hipStream_t s);
 
 struct PermuteWs {
@@ -132,6 +135,7 @@ int permute_blocks(int T);
 struct PermuteLayout {
     int tiled;
     int64_t shared_row0;
+    int payload;  // 0: the maps only (indexed layout), no x_perm
 };
 hipError_t launch_permute(const moe_cfg& c, const void* x, const float* x_scale, const int32_t* ids,
                           int32_t* counts, int32_t* offsets, int32_t* row_src, int32_t* tok_row,
@@ -161,6 +165,7 @@ struct FfnOperands {
     int x_rows_tiled, x_tokens_tiled;
     void* y_rows;
     void* y_shared;
+    const int32_t* row_src;  // non-NULL: x_rows is x [T][H], row r is token row_src[r] / k
 };
 hipError_t launch_gemm_bf16(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_cap, const FfnOperands& op,
                             const int32_t* offsets, const moe_weights& w, const FfnWork& wk, void* h_tiles,

@@ -109,6 +109,9 @@ struct GemmArgs {
     int N_routed, N_shared;    // GEMM1: h columns (I, I_sh); GEMM2: H
     int out_f32;               // GEMM2 output dtype
     int a_tiled_routed, a_tiled_shared;  // A operand layout of the two groups
+    const int32_t* a_row_src;  // GEMM1, routed groups: non-NULL -> A row r is x row a_row_src[r] / a_row_k
+    int a_row_k;
+    int a_rows;                // rows of x (the indexed A operand)
     int w_tiled;               // weights tiled (w13 / w2 layout)
     int h_slot_ks;             // k blocks of one h tile slot (ceil(max(I, I_sh) / 32))
 };
@@ -218,10 +221,14 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, int mt, int g, int r
         // row0 is a multiple of 16 here (the caller aligns expert segments)
         const uint16_t* A = (shared ? p.a_shared : p.a_routed) + (size_t)(row0 / 16) * KS * 512;
         d.ra = make_rsrc(A, (uint32_t)(((M + 15) / 16) * KS * 1024));
+    } else if (!shared && p.a_row_src) {
+        // indexed: the rows of x named by row_src (the descriptor spans all of x)
+        d.ra = make_rsrc(p.a_routed, (uint32_t)p.a_rows * (uint32_t)K * 2u);
     } else {
         const uint16_t* A = (shared ? p.a_shared : p.a_routed) + (size_t)row0 * K;
         d.ra = make_rsrc(A, (uint32_t)M * (uint32_t)K * 2u);
     }
+    const bool a_indexed = MODE == 0 && !shared && p.a_row_src != nullptr;
     d.sa = a_tiled ? 1024u : (uint32_t)(BK * 2);
     // ---- B: the weight rows of this N tile
     const int ncols = MODE == 0 ? min(BN / 2, N - n0) : min(BN, N - n0);
@@ -252,10 +259,14 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, int mt, int g, int r
         const int blk = wave * 4 + i;           // 16-row block of the tile this instruction fills
         const int row = blk * 16 + (lane >> 2);
         const uint32_t logical8 = (uint32_t)(((lane & 3) ^ swz_of_row(row)) * 8);
-        if (a_tiled)
+        if (a_tiled) {
             d.va[i] = blk * 16 < NRB * 32 ? ((uint32_t)blk * (uint32_t)KS * 1024u + (uint32_t)lane * 16u) : kOOB;
-        else
+        } else if (a_indexed) {
+            const int src = row < M ? p.a_row_src[row0 + row] : -1;
+            d.va[i] = src >= 0 ? ((uint32_t)(src / p.a_row_k) * (uint32_t)K + logical8) * 2u : kOOB;
+        } else {
             d.va[i] = row < M ? ((uint32_t)row * (uint32_t)K + logical8) * 2u : kOOB;
+        }
         if (p.w_tiled) {
             d.vb[i] = (uint32_t)blk * (uint32_t)KS * 1024u + (uint32_t)lane * 16u;
         } else {
@@ -477,6 +488,9 @@ hipError_t launch_gemm_bf16(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_
     a.a_shared = static_cast<const uint16_t*>(op.x_tokens);
     a.a_tiled_routed = op.x_rows_tiled;
     a.a_tiled_shared = op.x_tokens_tiled;
+    a.a_row_src = op.row_src;
+    a.a_row_k = c.k;
+    a.a_rows = c.T;
     a.w0_routed = static_cast<const uint16_t*>(w.w_gate);
     a.w1_routed = static_cast<const uint16_t*>(w.w_up);
     a.w0_shared = static_cast<const uint16_t*>(w.sh_gate);
@@ -496,6 +510,7 @@ hipError_t launch_gemm_bf16(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_
     a.a_shared = static_cast<const uint16_t*>(h_tiles);
     a.a_tiled_routed = 1;
     a.a_tiled_shared = 1;
+    a.a_row_src = nullptr;
     a.w0_routed = static_cast<const uint16_t*>(w.w_down);
     a.w1_routed = nullptr;
     a.w0_shared = static_cast<const uint16_t*>(w.sh_down);

@@ -12,8 +12,10 @@
 //                  count of the mask below its token, so rows follow ascending
 //                  token order whatever the scheduling;
 //  4. perm_gather  token-major copy: each token row of x is read once from HBM
-//                  and written to its k destination rows with 16-byte stores;
-//  5. perm_zero    padding rows (m_tile > 1) are zero-filled.
+//                  and written to its k destination rows with 16-byte stores
+//                  (row-major x_perm); perm_band_tiled instead writes the tiled
+//                  x_perm band by band, gathering each row from its token;
+//  5. perm_zero    padding rows (m_tile > 1) of the row-major x_perm are zeroed.
 #include "common.hpp"
 
 namespace moe {
@@ -119,36 +121,40 @@ perm_gather(const uint8_t* __restrict__ x, const float* __restrict__ x_scale, co
         }
 }
 
-// Tiled bf16 output: one workgroup per token; x[t] is read once and its
-// 16-byte chunks are stored to the tiled blocks of its k rows (and of row
-// shared_row0 + t when the shared expert needs the token too).
+// Tiled bf16 output, gathered by destination: one workgroup per band of 16
+// rows writes the band's ceil(H / 32) blocks of 1 KiB as one contiguous run;
+// each 16-byte chunk is read from the row's token in x (zeros for padding rows,
+// for rows past max_rows and for the column padding).  Bands at and after
+// rows_pad hold token rows_pad + t (the shared expert's copy of x).
 __global__ void __launch_bounds__(256)
-perm_gather_tiled(const uint16_t* __restrict__ x, const int32_t* __restrict__ tok_row, uint16_t* __restrict__ x_perm,
-                  int k, int H, int KS, int64_t shared_row0) {
-    const int t = blockIdx.x;
-    __shared__ int64_t rows[33];
-    if (threadIdx.x < k) rows[threadIdx.x] = tok_row[(size_t)t * k + threadIdx.x];
-    if (threadIdx.x == 32) rows[32] = shared_row0 >= 0 ? shared_row0 + t : -1;
-    __syncthreads();
-    // chunks past H up to the last 32-column block are K padding: zeros
-    const int nchunk = H / 8, nchunk_pad = KS * 4;
-    const i32x4* src = reinterpret_cast<const i32x4*>(x + (size_t)t * H);
-    i32x4* dst = reinterpret_cast<i32x4*>(x_perm);
-    const int64_t srow = rows[32];
-    for (int c = threadIdx.x; c < nchunk_pad; c += 256) {
-        const i32x4 v = c < nchunk ? __builtin_nontemporal_load(src + c) : i32x4{0, 0, 0, 0};
-        for (int j = 0; j < k; ++j) dst[tiled_chunk(rows[j], c, KS)] = v;
-        if (srow >= 0) dst[tiled_chunk(srow, c, KS)] = v;
+perm_band_tiled(const uint16_t* __restrict__ x, const int32_t* __restrict__ row_src, uint16_t* __restrict__ x_perm,
+                int64_t max_rows, int64_t rows_pad, int T, int k, int H, int KS) {
+    const int64_t band = blockIdx.x;
+    __shared__ int32_t tok[16];  // token of each row of the band, -1 for a zero row
+    if (threadIdx.x < 16) {
+        const int64_t r = band * 16 + threadIdx.x;
+        int32_t t = -1;
+        if (r < rows_pad) {
+            if (r < max_rows) {
+                const int32_t v = row_src[r];
+                t = v >= 0 ? v / k : -1;
+            }
+        } else if (r - rows_pad < T) {
+            t = (int32_t)(r - rows_pad);
+        }
+        tok[threadIdx.x] = t;
     }
-}
-
-__global__ void __launch_bounds__(256)
-perm_zero_tiled(const int32_t* __restrict__ row_src, uint16_t* __restrict__ x_perm, int64_t max_rows, int KS) {
-    const int sub = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t r = (int64_t)blockIdx.x * 4 + sub;
-    if (r >= max_rows || row_src[r] != -1) return;
-    i32x4* dst = reinterpret_cast<i32x4*>(x_perm);
-    for (int c = lane; c < KS * 4; c += 64) dst[tiled_chunk(r, c, KS)] = i32x4{0, 0, 0, 0};
+    __syncthreads();
+    const int nq = KS * 64, nch = H / 8;
+    i32x4* dst = reinterpret_cast<i32x4*>(x_perm) + band * (int64_t)nq;
+    for (int q = threadIdx.x; q < nq; q += 256) {
+        const int r = (q >> 2) & 15;
+        const int c = (q >> 6) * 4 + ((q & 3) ^ tile_swz(r));
+        const int32_t t = tok[r];
+        i32x4 v = {0, 0, 0, 0};
+        if (t >= 0 && c < nch) v = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(x + (size_t)t * H) + c);
+        dst[q] = v;
+    }
 }
 
 // Zero the payload of padding rows (row_src == -1); 4 rows per workgroup.
@@ -180,18 +186,18 @@ hipError_t launch_permute(const moe_cfg& c, const void* x, const float* x_scale,
                        c.E);
     hipLaunchKernelGGL(perm_scan, dim3(1), dim3(1024), 0, s, ws.hist, ws.base, counts, offsets, nblk, c.E,
                        m_tile);
-    if (m_tile > 1)
+    if (m_tile > 1 || lay.tiled || !lay.payload)
         hipLaunchKernelGGL(fill_i32, dim3((unsigned)((max_rows + 255) / 256)), dim3(256), 0, s, row_src,
                            max_rows, -1);
     hipLaunchKernelGGL(perm_scatter, dim3(nblk), dim3(PB), (size_t)c.E * (PB / 32) * sizeof(uint32_t), s,
                        ids, ws.base, row_src, tok_row, c.T, c.k, c.E);
+    if (!lay.payload) return hipGetLastError();
     if (lay.tiled) {
         const int KS = (c.H + 31) / 32;
-        hipLaunchKernelGGL(perm_gather_tiled, dim3(c.T), dim3(256), 0, s, static_cast<const uint16_t*>(x), tok_row,
-                           static_cast<uint16_t*>(x_perm), c.k, c.H, KS, lay.shared_row0);
-        if (m_tile > 1)
-            hipLaunchKernelGGL(perm_zero_tiled, dim3((unsigned)((max_rows + 3) / 4)), dim3(256), 0, s, row_src,
-                               static_cast<uint16_t*>(x_perm), max_rows, KS);
+        const int64_t rows_pad = (max_rows + 15) / 16 * 16;
+        const int64_t bands = rows_pad / 16 + (lay.shared_row0 >= 0 ? (c.T + 15) / 16 : 0);
+        hipLaunchKernelGGL(perm_band_tiled, dim3((unsigned)bands), dim3(256), 0, s, static_cast<const uint16_t*>(x),
+                           row_src, static_cast<uint16_t*>(x_perm), max_rows, rows_pad, c.T, c.k, c.H, KS);
         return hipGetLastError();
     }
     const int row_bytes = c.H * dtype_bytes(c.act_dtype);

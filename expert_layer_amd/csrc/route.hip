@@ -18,81 +18,160 @@
 namespace moe {
 namespace {
 
-constexpr int RT_M = 32;    // tokens per workgroup
-constexpr int RT_N = 128;   // experts per workgroup
-constexpr int RT_K = 64;    // K slice per stage
-constexpr int RT_THREADS = 256;
+constexpr int RB_M = 128, RB_N = 256, RB_K = 32, RB_NST = 4, RB_THREADS = 256;
+constexpr int kRA = RB_M * 4;                // 16-byte chunks of A (128 rows x 64 B) in one stage
+constexpr int kRB = RB_N * 4;                // of B (256 expert rows x 64 B)
+constexpr uint32_t kROOB = 0x40000000u;      // past every descriptor: the load returns zero
 
-// LDS tile [rows][64 bf16]: 8 chunks of 16 B per row, chunk c stored at
-// c ^ (row & 7) so that 8 consecutive rows reading the same logical chunk
-// touch 8 different bank groups.
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
+typedef __attribute__((address_space(3))) void* rlds_t;
 
-__global__ void __launch_bounds__(RT_THREADS)
-router_logits_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, float* __restrict__ logits,
-                   int T, int H, int E) {
-    __shared__ i32x4 sA[2][RT_M * 8];
-    __shared__ i32x4 sB[2][RT_N * 8];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int t0 = blockIdx.x * RT_M, e0 = blockIdx.y * RT_N;
-    const int nk = H / RT_K;  // H % 64 handled by the tail below
+// The four stage buffers [A | B], distinct objects (see gemm_bf16.hip).
+__shared__ i32x4 rring0[kRA + kRB];
+__shared__ i32x4 rring1[kRA + kRB];
+__shared__ i32x4 rring2[kRA + kRB];
+__shared__ i32x4 rring3[kRA + kRB];
 
-    // global -> register staging: A 256 chunks (1 per thread), B 1024 (4 per thread)
-    auto load = [&](int ks, i32x4& ra, i32x4 (&rb)[4]) {
-        {
-            int r = tid >> 3, c = tid & 7;
-            int t = t0 + r;
-            int kcol = ks * RT_K + c * 8;
-            if (t < T && kcol + 8 <= H) ra = *reinterpret_cast<const i32x4*>(x + (size_t)t * H + kcol);
-            else ra = i32x4{0, 0, 0, 0};
-        }
+template <int BUF>
+__device__ __forceinline__ i32x4* rring() {
+    if constexpr (BUF == 0) return rring0;
+    else if constexpr (BUF == 1) return rring1;
+    else if constexpr (BUF == 2) return rring2;
+    else return rring3;
+}
+
+__device__ __forceinline__ void rbarrier() { asm volatile("s_barrier" ::: "memory"); }
+
+struct RDma {
+    __amdgpu_buffer_rsrc_t ra, rb;
+    uint32_t va[2], vb[4];   // byte offset of this lane's chunk at k = k0 (kROOB: outside the tile)
+    uint32_t lc[2], lcb[4];  // the chunk's column offset (elements) inside a stage
+    int k0, k_end, nsteps;
+};
+
+// Loads of stage t into buffer BUF: 2 A and 4 B chunk loads per lane, zero
+// past the tile's rows and past the split's K range.
+template <int BUF>
+__device__ __forceinline__ void rdma(const RDma& d, int t, int wave) {
+    i32x4* buf = rring<BUF>();
+    const int kst = d.k0 + t * RB_K;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            int q = tid + i * RT_THREADS;
-            int r = q >> 3, c = q & 7;
-            int e = e0 + r;
-            int kcol = ks * RT_K + c * 8;
-            if (e < E && kcol + 8 <= H) rb[i] = *reinterpret_cast<const i32x4*>(w + (size_t)e * H + kcol);
-            else rb[i] = i32x4{0, 0, 0, 0};
-        }
-    };
-    auto store = [&](int buf, const i32x4& ra, const i32x4 (&rb)[4]) {
-        sA[buf][swz(tid >> 3, tid & 7)] = ra;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            int q = tid + i * RT_THREADS;
-            sB[buf][swz(q >> 3, q & 7)] = rb[i];
-        }
-    };
-
-    f32x16 acc = {};
-    i32x4 ra, rb[4];
-    const int nsteps = (H + RT_K - 1) / RT_K;
-    load(0, ra, rb);
-    store(0, ra, rb);
-    __syncthreads();
-    for (int ks = 0; ks < nsteps; ++ks) {
-        const int buf = ks & 1;
-        if (ks + 1 < nsteps) load(ks + 1, ra, rb);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            int chunk = kk * 2 + (lane >> 5);
-            i32x4 a = sA[buf][swz(lane & 31, chunk)];
-            i32x4 b = sB[buf][swz(wave * 32 + (lane & 31), chunk)];
-            acc = mfma32x32x16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc);
-        }
-        if (ks + 1 < nsteps) store(buf ^ 1, ra, rb);
-        __syncthreads();
+    for (int i = 0; i < 2; ++i) {
+        const bool ok = d.va[i] != kROOB && kst + (int)d.lc[i] < d.k_end;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ra, (rlds_t)(buf + (wave * 2 + i) * 64), 16,
+                                                 ok ? d.va[i] + (uint32_t)t * (RB_K * 2) : kROOB, 0, 0, 0);
     }
-    (void)nk;
-    // H not a multiple of 8 never reaches here (validated); a tail of H % 64
-    // in multiples of 8 is covered by the zero-filled chunks above.
-    const int e = e0 + wave * 32 + (lane & 31);
-    if (e < E) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            int t = t0 + c_row(i, lane);
-            if (t < T) logits[(size_t)t * E + e] = acc[i];
+    for (int i = 0; i < 4; ++i) {
+        const bool ok = d.vb[i] != kROOB && kst + (int)d.lcb[i] < d.k_end;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rb, (rlds_t)(buf + kRA + (wave * 4 + i) * 64), 16,
+                                                 ok ? d.vb[i] + (uint32_t)t * (RB_K * 2) : kROOB, 0, 0, 0);
+    }
+}
+
+// One stage: two 16-wide k steps of the wave's 4 x 2 blocks of 32 x 32.
+template <int BUF>
+__device__ __forceinline__ void rstage(int wave, int lane, f32x16 (&acc)[4][2]) {
+    const i32x4* buf = rring<BUF>();
+    const int l32 = lane & 31;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        const int chunk = kk * 2 + (lane >> 5);
+        i32x4 a[4], b[2];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = r * 32 + l32;
+            a[r] = buf[row * 4 + (chunk ^ tile_swz(row))];
+        }
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int row = wave * 64 + c * 32 + l32;
+            b[c] = buf[kRA + row * 4 + (chunk ^ tile_swz(row))];
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+                acc[r][c] = mfma32x32x16(__builtin_bit_cast(bf16x8, a[r]), __builtin_bit_cast(bf16x8, b[c]),
+                                         acc[r][c]);
+    }
+}
+
+// partial[split][t][e] = sum over the split's K range of x[t][h] * w[e][h].
+// Workgroup: 128 tokens x 256 experts x one K range; wave w owns experts
+// 64 w + [0, 64).  Operands move HBM -> LDS by buffer_load ... lds through a
+// ring of four stages (64-byte row segments, the chunks XOR-swizzled by row so
+// that fragment reads are free of bank conflicts).  Splitting K lets T / 128
+// token blocks fill the chip; the router weights are then read from L2 about
+// T / 128 times instead of once per 32 tokens.
+__global__ void __launch_bounds__(RB_THREADS)
+router_logits_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, float* __restrict__ partial,
+                   int T, int H, int E, int ksplit) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int t0 = blockIdx.x * RB_M, e0 = blockIdx.y * RB_N, split = blockIdx.z;
+    RDma d;
+    d.k0 = split * ksplit;
+    d.k_end = min(H, d.k0 + ksplit);
+    d.nsteps = (d.k_end - d.k0 + RB_K - 1) / RB_K;
+    const int mt = min(RB_M, T - t0), ne = min(RB_N, E - e0);
+    d.ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x + (size_t)t0 * H), (short)0,
+                                              (int)((uint32_t)mt * (uint32_t)H * 2u), 0x00020000);
+    d.rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(w + (size_t)e0 * H), (short)0,
+                                              (int)((uint32_t)ne * (uint32_t)H * 2u), 0x00020000);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int row = (wave * 2 + i) * 16 + (lane >> 2);
+        const int logical = (lane & 3) ^ tile_swz(row);
+        d.lc[i] = (uint32_t)(logical * 8);
+        d.va[i] = row < mt ? ((uint32_t)row * (uint32_t)H + (uint32_t)(d.k0 + logical * 8)) * 2u : kROOB;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = (wave * 4 + i) * 16 + (lane >> 2);
+        const int logical = (lane & 3) ^ tile_swz(row);
+        d.lcb[i] = (uint32_t)(logical * 8);
+        d.vb[i] = row < ne ? ((uint32_t)row * (uint32_t)H + (uint32_t)(d.k0 + logical * 8)) * 2u : kROOB;
+    }
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) acc[r][c] = f32x16{};
+
+    rdma<0>(d, 0, wave);
+    rdma<1>(d, 1, wave);
+    rdma<2>(d, 2, wave);
+    rdma<3>(d, 3, wave);
+    const int nturns = (d.nsteps + RB_NST - 1) / RB_NST;
+    for (int s = 0; s < nturns * RB_NST; s += RB_NST) {
+        // stage s + j landed (the next three may be in flight: 18 loads), then
+        // compute on it and hand the buffer back to stage s + j + 4
+#define ROUTER_STAGE(J)                                              \
+        __builtin_amdgcn_s_waitcnt((18 & 15) | ((18 >> 4) << 14) | 0x0F70); \
+        rbarrier();                                                  \
+        rstage<J>(wave, lane, acc);                                  \
+        __builtin_amdgcn_s_waitcnt(0xC07F);                          \
+        rbarrier();                                                  \
+        rdma<J>(d, s + J + RB_NST, wave);
+        ROUTER_STAGE(0)
+        ROUTER_STAGE(1)
+        ROUTER_STAGE(2)
+        ROUTER_STAGE(3)
+#undef ROUTER_STAGE
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // no LDS DMA may outlive the workgroup
+    float* out = partial + (size_t)split * T * E;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const int e = e0 + wave * 64 + c * 32 + (lane & 31);
+        if (e < E) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int t = t0 + r * 32 + c_row(i, lane);
+                    if (t < T) out[(size_t)t * E + e] = acc[r][c][i];
+                }
         }
     }
 }
@@ -132,9 +211,9 @@ __device__ __forceinline__ void wave_argmax(float& key, int& idx) {
 
 template <int PL>
 __global__ void __launch_bounds__(256)
-route_select(const float* __restrict__ logits, const float* __restrict__ bias, float* __restrict__ logits_copy,
-             int32_t* __restrict__ ids, float* __restrict__ wout, int T, int E, int k, int score_fn,
-             int n_groups, int topk_groups, int group_score, int renorm, float scale) {
+route_select(const float* __restrict__ logits, int nsplit, const float* __restrict__ bias,
+             float* __restrict__ logits_copy, int32_t* __restrict__ ids, float* __restrict__ wout, int T, int E,
+             int k, int score_fn, int n_groups, int topk_groups, int group_score, int renorm, float scale) {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int t = blockIdx.x * 4 + wv;
     if (t >= T) return;
@@ -147,7 +226,12 @@ route_select(const float* __restrict__ logits, const float* __restrict__ bias, f
     for (int i = 0; i < PL; ++i) {
         int e = lane + 64 * i;
         ok[i] = e < E;
-        float v = ok[i] ? l[e] : 0.0f;
+        // the logit is the sum of the K-split partials, in split order
+        float v = 0.0f;
+        if (ok[i]) {
+            v = l[e];
+            for (int p = 1; p < nsplit; ++p) v += l[(size_t)p * T * E + e];
+        }
         if (logits_copy && ok[i]) logits_copy[(size_t)t * E + e] = v;
         float b = (bias && ok[i]) ? bias[e] : 0.0f;
         if (score_fn == MOE_SCORE_SOFTMAX) {
@@ -265,13 +349,25 @@ route_select(const float* __restrict__ logits, const float* __restrict__ bias, f
 
 }  // namespace
 
+int router_splits(const moe_cfg& c) {
+    if (c.act_dtype != MOE_BF16) return 1;
+    const int blocks = ((c.T + RB_M - 1) / RB_M) * ((c.E + RB_N - 1) / RB_N);
+    if (blocks == 0) return 1;                      // T == 0
+    int sp = (256 + blocks - 1) / blocks;          // about one workgroup per CU
+    sp = sp < 1 ? 1 : (sp > 8 ? 8 : sp);
+    const int kmax = (c.H + 255) / 256;             // at least 256 columns per split
+    return sp < kmax ? sp : kmax;
+}
+
 hipError_t launch_router_logits(const moe_cfg& c, const void* x, const void* w_router, float* logits,
                                 hipStream_t s) {
     if (c.act_dtype == MOE_BF16) {
-        dim3 grid((c.T + RT_M - 1) / RT_M, (c.E + RT_N - 1) / RT_N);
-        hipLaunchKernelGGL(router_logits_bf16, grid, dim3(RT_THREADS), 0, s,
+        const int sp = router_splits(c);
+        const int ksplit = ((c.H + sp - 1) / sp + RB_K - 1) / RB_K * RB_K;
+        dim3 grid((c.T + RB_M - 1) / RB_M, (c.E + RB_N - 1) / RB_N, sp);
+        hipLaunchKernelGGL(router_logits_bf16, grid, dim3(RB_THREADS), 0, s,
                            static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_router),
-                           logits, c.T, c.H, c.E);
+                           logits, c.T, c.H, c.E, ksplit);
     } else {
         int64_t n = (int64_t)c.T * c.E;
         hipLaunchKernelGGL(router_logits_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
@@ -281,12 +377,12 @@ hipError_t launch_router_logits(const moe_cfg& c, const void* x, const void* w_r
     return hipGetLastError();
 }
 
-hipError_t launch_route_select(const moe_cfg& c, const float* logits, const float* bias,
+hipError_t launch_route_select(const moe_cfg& c, const float* logits, int nsplit, const float* bias,
                                float* logits_copy, int32_t* ids, float* w, hipStream_t s) {
     dim3 grid((c.T + 3) / 4), block(256);
     int pl = (c.E + 63) / 64;
 #define SEL(P)                                                                                      \
-    hipLaunchKernelGGL(route_select<P>, grid, block, 0, s, logits, bias, logits_copy, ids, w, c.T, \
+    hipLaunchKernelGGL(route_select<P>, grid, block, 0, s, logits, nsplit, bias, logits_copy, ids, w, c.T, \
                        c.E, c.k, c.score_fn, c.n_groups, c.topk_groups, c.group_score,            \
                        c.renormalize, c.routed_scale)
     if (pl <= 1) SEL(1);

@@ -73,7 +73,8 @@ typedef enum moe_group_score { MOE_GROUP_TOP2_SUM = 0, MOE_GROUP_MAX = 1 } moe_g
 
 typedef enum moe_layout {
     MOE_LAYOUT_ROWMAJOR = 0, /* [out][in] row-major, the reduction index contiguous */
-    MOE_LAYOUT_TILED = 1     /* bf16 tiled layout written by moe_tile_weights */
+    MOE_LAYOUT_TILED = 1,    /* bf16 tiled layout written by moe_tile_weights */
+    MOE_LAYOUT_INDEXED = 2   /* x_layout only: no x_perm; the FFN reads x through row_src */
 } moe_layout;
 
 typedef enum moe_stage {
@@ -110,7 +111,10 @@ typedef enum moe_stage {
  *                layout of moe_tile_weights over R16 = roundup(moe_max_rows, 16)
  *                rows of H columns, followed, when has_shared, by a tiled copy
  *                of x's T rows (padded to 16) that the shared expert reads;
- *                moe_x_perm_bytes gives the size.
+ *                MOE_LAYOUT_INDEXED (bf16): x_perm is not materialised --
+ *                moe_permute writes the maps only and moe_grouped_ffn reads
+ *                dispatched row r from x itself, at token row_src[r] / k;
+ *                moe_x_perm_bytes gives the size (0 when indexed).
  * E <= 1024. */
 typedef struct moe_cfg {
     int32_t T, H, E, k, I;
@@ -200,7 +204,8 @@ moe_status moe_tile_weights(const moe_cfg *cfg, const moe_weights *src, void *ds
  * x [T][H] act_dtype (F32 or BF16), w_router [E][H] same dtype, bias [E] fp32
  * or NULL, logits_in [T][E] fp32 or NULL, logits_out [T][E] fp32 or NULL
  * (written when non-NULL), topk_ids [T][k] int32, topk_w [T][k] fp32.
- * ws: moe_workspace_bytes(cfg, MOE_STAGE_ROUTE). */
+ * ws: moe_workspace_bytes(cfg, MOE_STAGE_ROUTE) (it holds the K-split partial
+ * logits; unused, and may be NULL, when logits_in != NULL). */
 moe_status moe_route(const moe_cfg *cfg, const void *x, const void *w_router, const float *bias,
                      const float *logits_in, float *logits_out, int32_t *topk_ids,
                      float *topk_w, void *ws, size_t ws_bytes, void *stream);
@@ -217,7 +222,8 @@ moe_status moe_route(const moe_cfg *cfg, const void *x, const void *w_router, co
  *   x_perm_scale[row] = x_scale[t] (fp8 activations only; [rows][H/128])
  * x_perm is laid out as cfg->x_layout says (moe_x_perm_bytes bytes); the tiled
  * layout also receives the shared expert's copy of x when has_shared, and its
- * column padding up to a multiple of 32 is zero.
+ * column padding up to a multiple of 32 is zero.  With MOE_LAYOUT_INDEXED
+ * x_perm is not written and may be NULL.
  * topk_ids must hold distinct ids in [0, E) per token.
  * ws: moe_workspace_bytes(cfg, MOE_STAGE_PERMUTE). */
 moe_status moe_permute(const moe_cfg *cfg, const void *x, const float *x_scale,
@@ -245,14 +251,20 @@ moe_status moe_permute(const moe_cfg *cfg, const void *x, const float *x_scale,
  * offsets must be multiples of 16 (results are undefined otherwise, accesses
  * stay inside x_rows), and the shared expert reads its copy of the tokens
  * inside x_rows (x_tokens is ignored and may be NULL).
+ * cfg->x_layout MOE_LAYOUT_INDEXED: x_rows is x [T][H] itself and row_src
+ * [n_rows_cap] (int32, as written by moe_permute) maps row r to token
+ * row_src[r] / k, a zero row where row_src[r] < 0; the shared expert reads
+ * x_rows too (x_tokens is ignored and may be NULL).  row_src is unused (may
+ * be NULL) for the other layouts.
  * y_rows [n_rows_cap][H] and y_shared in cfg->y_dtype.  n_rows_cap is the
  * row count of x_rows and y_rows, independent of T (rows may arrive already
  * dispatched); expert_offsets[E] <= n_rows_cap.
  * ws: moe_ffn_workspace_bytes(cfg, n_rows_cap). */
 moe_status moe_grouped_ffn(const moe_cfg *cfg, int64_t n_rows_cap, const void *x_rows,
                            const float *x_scale, const int32_t *expert_offsets,
-                           const moe_weights *w, const void *x_tokens, void *y_rows,
-                           void *y_shared, void *ws, size_t ws_bytes, void *stream);
+                           const int32_t *row_src, const moe_weights *w, const void *x_tokens,
+                           void *y_rows, void *y_shared, void *ws, size_t ws_bytes,
+                           void *stream);
 
 /* Combine: the weighted gather-reduce back to token order (ASAP section
  * 3.2.2's expert results per token and choice).
@@ -267,7 +279,7 @@ moe_status moe_combine(const moe_cfg *cfg, const void *y_rows, const int32_t *to
  * enqueued on `stream` with no host synchronisation.  x [T][H] in act_dtype
  * (F32 or BF16); out [T][H] in out_dtype.  All intermediates live in ws.
  * The stages run with m_tile = 16 and, for bf16, x_layout =
- * MOE_LAYOUT_TILED, whatever cfg->m_tile and cfg->x_layout say (those shape
+ * MOE_LAYOUT_INDEXED, whatever cfg->m_tile and cfg->x_layout say (those shape
  * the standalone stage calls only); the result equals that of the four stage
  * calls made with those two fields.  w may be row-major or tiled.
  * ws: moe_workspace_bytes(cfg, MOE_STAGE_LAYER). */

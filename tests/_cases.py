@@ -101,6 +101,15 @@ def rel_err_bf16_out(got: np.ndarray, ref: np.ndarray) -> float:
     return float(np.max(e)) / max(rms, 1e-300)
 
 
+def rel_err_allow(got: np.ndarray, ref: np.ndarray, allow: np.ndarray) -> float:
+    """max(|got - ref| - allow, 0) / rms(ref): the error beyond a per-element
+    allowance for roundings that the definition leaves to storage (bf16
+    stores of an output or of the expert outputs)."""
+    rms = math.sqrt(float(np.mean(ref.astype(np.float64) ** 2)))
+    e = np.maximum(np.abs(got.astype(np.float64) - ref) - allow, 0.0)
+    return float(np.max(e)) / max(rms, 1e-300)
+
+
 def host(t: torch.Tensor) -> np.ndarray:
     return to_np(t)
 

@@ -67,7 +67,8 @@ def test_validate_accepts_workload_shapes():
     (dict(act_dtype=m.MOE_FP8_E4M3), m.MOE_ERR_UNSUPPORTED),  # fp8 + shared expert
     (dict(m_tile=-1), m.MOE_ERR_INVALID_ARG),
     (dict(routed_scale=float("inf")), m.MOE_ERR_INVALID_ARG),
-    (dict(x_layout=2), m.MOE_ERR_INVALID_ARG),
+    (dict(x_layout=3), m.MOE_ERR_INVALID_ARG),
+    (dict(x_layout=m.MOE_LAYOUT_INDEXED, act_dtype=m.MOE_F32), m.MOE_ERR_UNSUPPORTED),
     (dict(x_layout=m.MOE_LAYOUT_TILED, m_tile=8), m.MOE_ERR_INVALID_ARG),
     (dict(x_layout=m.MOE_LAYOUT_TILED, m_tile=0), m.MOE_ERR_INVALID_ARG),
     (dict(x_layout=m.MOE_LAYOUT_TILED, m_tile=16, act_dtype=m.MOE_F32), m.MOE_ERR_UNSUPPORTED),
@@ -100,11 +101,13 @@ def test_max_rows_and_workspace_sizes():
         assert m.moe_max_rows(c) == 8192 * 8 + 256 * (max(mt, 1) - 1)
     c = _dsv3()
     ws = [m.moe_workspace_bytes(c, s) for s in range(4)]
-    assert ws[m.MOE_STAGE_ROUTE] == 8192 * 256 * 4
+    # the router's K-split partial logits: whole [T][E] fp32 copies
+    assert ws[m.MOE_STAGE_ROUTE] % (8192 * 256 * 4) == 0 and 8192 * 256 * 4 <= ws[m.MOE_STAGE_ROUTE] <= 8 * 8192 * 256 * 4
     assert all(w % 256 == 0 for w in ws)
-    # the layer workspace holds x_perm (bf16), y_rows (fp32) and y_shared at least
+    # the layer workspace holds y_rows (fp32) and y_shared at least; a bf16 layer
+    # materialises no x_perm (its GEMM reads x through row_src)
     rows = 8192 * 8
-    assert ws[m.MOE_STAGE_LAYER] >= rows * 7168 * 2 + rows * 7168 * 4 + 8192 * 7168 * 4
+    assert rows * 7168 * 4 + 8192 * 7168 * 4 <= ws[m.MOE_STAGE_LAYER] < rows * 7168 * 6
     assert ws[m.MOE_STAGE_FFN] >= rows * 2048 * 2  # h in bf16
     assert m.moe_workspace_bytes(c, 7) == ctypes.c_size_t(-1).value
     assert m.moe_ffn_workspace_bytes(c, rows) == ws[m.MOE_STAGE_FFN]
@@ -122,6 +125,7 @@ def test_x_perm_sizes():
     t = m.make_cfg(T=77, H=520, E=6, k=2, I=264, m_tile=32, x_layout=m.MOE_LAYOUT_TILED)
     r16 = (m.moe_max_rows(t) + 15) // 16 * 16
     assert m.moe_x_perm_bytes(t) == r16 // 16 * 17 * 1024
+    assert m.moe_x_perm_bytes(_dsv3(x_layout=m.MOE_LAYOUT_INDEXED)) == 0
     assert m.moe_x_perm_bytes(_dsv3(x_layout=3)) == ctypes.c_size_t(-1).value
 
 
@@ -139,20 +143,24 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
     st = lib.moe_route(ctypes.byref(c), fake, fake, None, None, None, fake, fake, fake, 16, None)
     assert st == m.MOE_ERR_WORKSPACE
     w = m.moe_weights(w_gate=0x100000, w_up=0x100000, w_down=None)
-    st = lib.moe_grouped_ffn(ctypes.byref(c), 32, fake, None, fake, ctypes.byref(w), None, fake, None, fake,
+    st = lib.moe_grouped_ffn(ctypes.byref(c), 32, fake, None, fake, None, ctypes.byref(w), None, fake, None, fake,
                              1 << 30, None)
     assert st == m.MOE_ERR_INVALID_ARG and "w_down" in m.moe_last_error()
     w = m.moe_weights(w_gate=0x100000, w_up=0x100000, w_down=0x100000)
-    st = lib.moe_grouped_ffn(ctypes.byref(c), 1 << 31, fake, None, fake, ctypes.byref(w), None, fake, None, fake,
+    st = lib.moe_grouped_ffn(ctypes.byref(c), 1 << 31, fake, None, fake, None, ctypes.byref(w), None, fake, None, fake,
                              1 << 30, None)
     assert st == m.MOE_ERR_INVALID_ARG and "n_rows_cap" in m.moe_last_error()
-    st = lib.moe_grouped_ffn(ctypes.byref(c), 10**6, fake, None, fake, ctypes.byref(w), None, fake, None, fake,
+    st = lib.moe_grouped_ffn(ctypes.byref(c), 10**6, fake, None, fake, None, ctypes.byref(w), None, fake, None, fake,
                              1 << 20, None)
     assert st == m.MOE_ERR_WORKSPACE
     ct = m.make_cfg(T=16, H=64, E=8, k=2, I=64, m_tile=16, x_layout=m.MOE_LAYOUT_TILED)
-    st = lib.moe_grouped_ffn(ctypes.byref(ct), 32, fake, None, fake, ctypes.byref(w), None, fake, None, fake,
+    st = lib.moe_grouped_ffn(ctypes.byref(ct), 32, fake, None, fake, None, ctypes.byref(w), None, fake, None, fake,
                              1 << 30, None)
     assert st == m.MOE_ERR_INVALID_ARG and "n_rows_cap" in m.moe_last_error()
+    ci = m.make_cfg(T=16, H=64, E=8, k=2, I=64, m_tile=16, x_layout=m.MOE_LAYOUT_INDEXED)
+    st = lib.moe_grouped_ffn(ctypes.byref(ci), 32, fake, None, fake, None, ctypes.byref(w), None, fake, None, fake,
+                             1 << 30, None)
+    assert st == m.MOE_ERR_INVALID_ARG and "row_src" in m.moe_last_error()
     st = lib.moe_combine(ctypes.byref(c), fake, None, fake, None, fake, None)
     assert st == m.MOE_ERR_INVALID_ARG
     st = lib.moe_layer(ctypes.byref(c), fake, None, ctypes.byref(w), fake, None, fake, 1 << 40, None)

@@ -171,3 +171,39 @@ def test_tiled_weights_give_identical_results(H, I, counts, shared_T, I_sh):
         ref = oracle.expert_ffn(to_np(x_rows[o:o + counts[e]]), to_np(wg[e]), to_np(wu[e]), to_np(wd[e]),
                                 h_bf16=True)
         assert rel_err(f64(outs[1][0][o:o + counts[e]]), ref) <= 1e-2
+
+
+@pytest.mark.parametrize("H,I,counts,extra", [
+    (512, 1024, [37, 0, 5, 300, 64, 1, 0, 257], 9),
+    (520, 264, [31, 33, 2], 0),
+])
+def test_indexed_rows_equal_materialised_rows(H, I, counts, extra):
+    """MOE_LAYOUT_INDEXED: GEMM1 reads row r from x at token row_src[r] / k
+    (zero where row_src[r] < 0); the result equals, bit for bit, the FFN over
+    the materialised rows x_perm[r] = x[row_src[r] / k]."""
+    d = dev()
+    E, k, T = len(counts), 3, 50
+    s, wg, wu, wd = _weights(E, H, I, "bf16", seed=H + I + 1, device=d)
+    n = int(sum(counts))
+    cap = n + extra
+    x = synth.normal(synth.stream_key(11, "x"), (T, H), 1.0, d, torch.bfloat16)
+    g = torch.Generator().manual_seed(H)
+    src = torch.randint(0, T * k, (cap,), generator=g, dtype=torch.int32)
+    src[torch.randint(0, cap, (max(cap // 7, 1),), generator=g)] = -1   # padding rows
+    row_src = src.to(d)
+    xp = torch.zeros((cap, H), dtype=torch.bfloat16, device=d)
+    ok = src >= 0
+    xp[ok.to(d)] = x[(src[ok] // k).long().to(d)]
+    offs = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32, device=d)
+    w = moe.weights(wg, wu, wd)
+    outs = []
+    for lay in (moe.MOE_LAYOUT_ROWMAJOR, moe.MOE_LAYOUT_INDEXED):
+        c = moe.make_cfg(T=T, H=H, E=E, k=k, I=I, act_dtype=moe.MOE_BF16, y_dtype=moe.MOE_F32, m_tile=1,
+                         x_layout=lay)
+        y = torch.full((cap, H), -7.0, dtype=torch.float32, device=d)
+        ws = moe.workspace(c, moe.MOE_STAGE_FFN, d, n_rows_cap=cap)
+        moe.moe_grouped_ffn(c, cap, xp if lay == moe.MOE_LAYOUT_ROWMAJOR else x, None, offs, w, None, y, None, ws,
+                            row_src=row_src if lay == moe.MOE_LAYOUT_INDEXED else None)
+        torch.cuda.synchronize()
+        outs.append(y)
+    assert torch.equal(outs[0], outs[1])

@@ -15,8 +15,8 @@ import torch
 import expert_layer_amd as moe
 import oracle
 import synth
-from tests._cases import (dev, expert_stack, lib_cfg, rel_err, rel_err_bf16_out, route_kw, router_case,
-                          shared_stack)
+from tests._cases import (dev, expert_stack, lib_cfg, rel_err, rel_err_allow, rel_err_bf16_out, route_kw,
+                          router_case, shared_stack)
 from tests._np import to_np
 
 pytestmark = pytest.mark.gpu
@@ -55,10 +55,12 @@ def _run_layer(s, rc, T, ydt, odt, m_tile=0, tiled=False):
     return out
 
 
-def _oracle_tokens(s, rc, toks, exact=False):
+def _oracle_tokens(s, rc, toks, exact=False, absum=False):
     """Oracle output (fp64) of the listed tokens: their logits rows -> gating ->
     each chosen expert on the token row -> combine (+ shared expert).  The
-    intermediate is stored in bf16 for bf16 layers unless `exact`."""
+    intermediate is stored in bf16 for bf16 layers unless `exact`.  With
+    absum, also sum_j |w_j y_j| + |y_shared| per output (the scale of what
+    bf16 stores of the expert outputs may move)."""
     hb = s.dtype == "bf16" and not exact
     (wg, wu, wd), sh = _weights(s)
     toks = np.asarray(toks)
@@ -75,7 +77,11 @@ def _oracle_tokens(s, rc, toks, exact=False):
     if sh:
         y_sh = oracle.expert_ffn(xh, *(to_np(t) for t in sh), h_bf16=hb)
     tok_row = np.arange(n * k, dtype=np.int32).reshape(n, k)
-    return oracle.combine(y_rows, tok_row, w, y_sh)
+    out = oracle.combine(y_rows, tok_row, w, y_sh)
+    if not absum:
+        return out
+    mag = oracle.combine(np.abs(y_rows), tok_row, np.abs(w), None if y_sh is None else np.abs(y_sh))
+    return out, mag
 
 
 def _tol(s):
@@ -103,18 +109,36 @@ def test_layer_small_matches_oracle(name, T):
     if s.dtype == "bf16":  # tiled weights: the same kernels on the same LDS image, bit for bit
         out_t = _run_layer(s, rc, T, moe.MOE_F32, moe.MOE_BF16, m_tile=16, tiled=True)
         assert torch.equal(out.view(torch.int16), out_t.view(torch.int16))
+        # bf16 expert outputs, fp32 layer output
+        out_y = _run_layer(s, rc, T, moe.MOE_BF16, moe.MOE_F32, tiled=True)
+        ref2, mag = _oracle_tokens(s, rc, np.arange(T), absum=True)
+        assert _err(out_y.cpu().numpy(), ref2, mag, moe.MOE_BF16, moe.MOE_F32) <= _tol(s)
 
 
-@pytest.mark.parametrize("name,odt,tiled", [
-    ("c3_dsv3_bf16", moe.MOE_BF16, True),   # the benchmarked configuration
-    ("c3_dsv3_bf16", moe.MOE_F32, False),
-    ("c2_mixtral_bf16", moe.MOE_F32, True),
-    ("c4_qwen3_skew_bf16", moe.MOE_F32, True),
+def _err(got, ref, mag, ydt, odt):
+    """Error beyond the storage roundings of this configuration: a bf16 store
+    moves a value by at most 2^-8 of its magnitude (half an ulp), so a bf16
+    output may differ by 2^-8 |ref| and bf16 expert outputs by 2^-8 times
+    sum_j |w_j y_j| + |y_shared|."""
+    allow = np.zeros_like(ref)
+    if odt == moe.MOE_BF16:
+        allow += 2.0 ** -8 * np.abs(ref)
+    if ydt == moe.MOE_BF16:
+        allow += 2.0 ** -8 * mag
+    return rel_err_allow(got, ref, allow)
+
+
+@pytest.mark.parametrize("name,odt,tiled,ydt", [
+    ("c3_dsv3_bf16", moe.MOE_BF16, True, moe.MOE_BF16),   # the benchmarked configuration
+    ("c3_dsv3_bf16", moe.MOE_BF16, True, moe.MOE_F32),
+    ("c3_dsv3_bf16", moe.MOE_F32, False, moe.MOE_F32),
+    ("c2_mixtral_bf16", moe.MOE_F32, True, moe.MOE_F32),
+    ("c4_qwen3_skew_bf16", moe.MOE_F32, True, moe.MOE_BF16),
 ])
-def test_layer_full_size_sampled(name, odt, tiled):
+def test_layer_full_size_sampled(name, odt, tiled, ydt):
     s = synth.config(name)
     rc = router_case(s)
-    out = _run_layer(s, rc, s.T, moe.MOE_F32, odt, tiled=tiled)
+    out = _run_layer(s, rc, s.T, ydt, odt, tiled=tiled)
     # routing of every token through the standalone router
     c = lib_cfg(s)
     ids = torch.empty((s.T, s.k), dtype=torch.int32, device=dev())
@@ -132,22 +156,24 @@ def test_layer_full_size_sampled(name, odt, tiled):
     extra = [int(np.nonzero((ref_ids == hot).any(1))[0][0]), int(np.nonzero((ref_ids == cold).any(1))[0][-1]),
              0, s.T - 1]
     toks = np.unique(np.concatenate([toks, extra]))
-    ref = _oracle_tokens(s, rc, toks)
+    ref, mag = _oracle_tokens(s, rc, toks, absum=True)
     got = out[torch.as_tensor(toks, device=dev())].float().cpu().numpy()
-    err = rel_err(got, ref) if odt == moe.MOE_F32 else rel_err_bf16_out(got, ref)
+    err = _err(got, ref, mag, ydt, odt)
     assert err <= _tol(s), err
 
 
+@pytest.mark.parametrize("layout", [moe.MOE_LAYOUT_TILED, moe.MOE_LAYOUT_INDEXED])
 @pytest.mark.parametrize("shape", [
     synth.config("c3_dsv3_bf16").with_(T=300),
     synth.config("c2_mixtral_bf16").with_(T=200),
     # H and I not multiples of 32: the tiled rows carry zero column padding
     synth.MoeShape("ragged_shared", T=77, H=520, E=6, k=2, I=264, shared=True, I_shared=136, seed=9),
 ])
-def test_layer_equals_its_stage_calls(shape):
+def test_layer_equals_its_stage_calls(shape, layout):
     """moe_layer is route -> permute -> grouped_ffn -> combine run with m_tile
-    16 and the tiled x_perm: the four stage calls with that cfg give the same
-    bits, and they match the oracle."""
+    16 and the indexed x_perm: the four stage calls with that cfg give the same
+    bits; so do they with the tiled x_perm (the GEMM's arithmetic does not
+    depend on where its operands come from), and they match the oracle."""
     s = shape
     rc = router_case(s, s.T)
     T = rc["x"].shape[0]
@@ -156,14 +182,14 @@ def test_layer_equals_its_stage_calls(shape):
     w = moe.weights(wg, wu, wd, sh_gate=shg, sh_up=shu, sh_down=shd)
     w, _buf = moe.tile_weights(lib_cfg(s, T=T), w, dev())
     layer = _run_layer(s, rc, T, moe.MOE_F32, moe.MOE_BF16, tiled=True)
-    c = lib_cfg(s, T=T, y_dtype=moe.MOE_F32, out_dtype=moe.MOE_BF16, m_tile=16, x_layout=moe.MOE_LAYOUT_TILED)
+    c = lib_cfg(s, T=T, y_dtype=moe.MOE_F32, out_dtype=moe.MOE_BF16, m_tile=16, x_layout=layout)
     rows = moe.moe_max_rows(c)
     i32 = dict(dtype=torch.int32, device=dev())
     ids, tw = torch.empty((T, s.k), **i32), torch.empty((T, s.k), dtype=torch.float32, device=dev())
     counts, offs = torch.empty(s.E, **i32), torch.empty(s.E + 1, **i32)
     row_src, tok_row = torch.empty(rows, **i32), torch.empty((T, s.k), **i32)
     x_perm = moe.x_perm_buffer(c, dev())
-    assert x_perm.numel() == moe.moe_x_perm_bytes(c)
+    assert x_perm.numel() == max(moe.moe_x_perm_bytes(c), 1)
     x_perm.fill_(0xFF)  # NaN bf16 pattern: everything the FFN reads must be written by permute
     y_rows = torch.empty((rows, s.H), dtype=torch.float32, device=dev())
     y_sh = torch.empty((T, s.H), dtype=torch.float32, device=dev()) if s.shared else None
@@ -172,8 +198,9 @@ def test_layer_equals_its_stage_calls(shape):
                   moe.workspace(c, moe.MOE_STAGE_ROUTE, dev()))
     moe.moe_permute(c, rc["x"], None, ids, counts, offs, row_src, tok_row, x_perm, None,
                     moe.workspace(c, moe.MOE_STAGE_PERMUTE, dev()))
-    moe.moe_grouped_ffn(c, rows, x_perm, None, offs, w, None, y_rows, y_sh,
-                        moe.workspace(c, moe.MOE_STAGE_FFN, dev()))
+    indexed = layout == moe.MOE_LAYOUT_INDEXED
+    moe.moe_grouped_ffn(c, rows, rc["x"] if indexed else x_perm, None, offs, w, None, y_rows, y_sh,
+                        moe.workspace(c, moe.MOE_STAGE_FFN, dev()), row_src=row_src if indexed else None)
     moe.moe_combine(c, y_rows, tok_row, tw, y_sh, out)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), layer.view(torch.int16))

@@ -22,7 +22,8 @@ def _route(c, x, w_r, bias, logits_in=None):
     ids = torch.full((T, k), -7, dtype=torch.int32, device=dev())
     w = torch.full((T, k), float("nan"), dtype=torch.float32, device=dev())
     lg = torch.full((T, E), float("nan"), dtype=torch.float32, device=dev())
-    moe.moe_route(c, x, w_r, bias, logits_in, lg, ids, w, None)
+    ws = None if logits_in is not None else moe.workspace(c, moe.MOE_STAGE_ROUTE, dev())
+    moe.moe_route(c, x, w_r, bias, logits_in, lg, ids, w, ws)
     torch.cuda.synchronize()
     return ids.cpu().numpy(), w.cpu().numpy(), lg.cpu().numpy()
 
