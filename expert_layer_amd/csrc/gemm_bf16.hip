@@ -396,6 +396,7 @@ ffn_build_tiles(const int32_t* __restrict__ offsets, int E, int has_shared, int 
                 int4* __restrict__ tiles, int32_t* __restrict__ n_tiles, int2* __restrict__ work1, int nt1,
                 int2* __restrict__ work2, int nt2) {
     __shared__ int32_t wsum[16];
+    __shared__ int32_t gend[1025];  // inclusive prefix of the groups' tile counts
     const int G = E + has_shared;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     // Row ranges are clamped to [0, rows_cap] and never negative, so malformed
@@ -409,11 +410,13 @@ ffn_build_tiles(const int32_t* __restrict__ offsets, int E, int has_shared, int 
             e = T;
         }
     };
-    // thread tid owns group tid; thread 0 also owns group 1024 (E == 1024 + shared)
-    int b0 = 0, e0 = 0, n0 = 0;
+    // 1. tile counts and their prefix: thread tid owns group tid; thread 0
+    //    also owns group 1024 (E == 1024 with a shared expert)
+    int n0 = 0;
     if (tid < G) {
-        group_rows(tid, b0, e0);
-        n0 = (e0 - b0 + bm - 1) / bm;
+        int b, e;
+        group_rows(tid, b, e);
+        n0 = (e - b + bm - 1) / bm;
     }
     int incl = n0;
 #pragma unroll
@@ -425,38 +428,52 @@ ffn_build_tiles(const int32_t* __restrict__ offsets, int E, int has_shared, int 
     __syncthreads();
     int before = 0;
     for (int w = 0; w < wv; ++w) before += wsum[w];
-    int total = 0;
-    for (int w = 0; w < 16; ++w) total += wsum[w];
-    const int start = before + incl - n0;
-    auto emit = [&](int g, int b, int e, int nmt, int st) {
-        if (nmt == 0) return;
-        const int n = e - b;
-        int hgt = (n + nmt - 1) / nmt;
-        hgt = ((hgt + 31) / 32) * 32;
-        for (int m = 0; m < nmt; ++m) {
-            const int rb = b + m * hgt;
-            const int re = min(e, rb + hgt);
-            tiles[st + m] = int4{g, rb, re, 0};
-        }
-        // blocks of kMBlock M tiles, N tile by N tile: 32 consecutive items (one
-        // XCD's CUs) share kMBlock row panels and 32 / kMBlock weight panels
-        int i1 = st * nt1, i2 = st * nt2;
-        for (int mb = 0; mb < nmt; mb += kMBlock) {
-            const int mc = min(kMBlock, nmt - mb);
-            for (int nt = 0; nt < nt1; ++nt)
-                for (int m = mb; m < mb + mc; ++m) work1[i1++] = int2{st + m, nt};
-            for (int nt = 0; nt < nt2; ++nt)
-                for (int m = mb; m < mb + mc; ++m) work2[i2++] = int2{st + m, nt};
-        }
-    };
-    if (tid < G) emit(tid, b0, e0, n0, start);
+    if (tid < G) gend[tid] = before + incl;
     if (tid == 0 && G > 1024) {
+        int total = 0;
+        for (int w = 0; w < 16; ++w) total += wsum[w];
         int b, e;
         group_rows(1024, b, e);
-        const int n = (e - b + bm - 1) / bm;
-        emit(1024, b, e, n, total);
-        total += n;
+        gend[1024] = total + (e - b + bm - 1) / bm;
     }
+    __syncthreads();
+    const int total = G > 0 ? gend[G - 1] : 0;
+    // the group holding tile ti: the first whose prefix end exceeds ti
+    auto group_of = [&](int ti) {
+        int lo = 0, hi = G - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (gend[mid] > ti) hi = mid;
+            else lo = mid + 1;
+        }
+        return lo;
+    };
+    // 2. tiles: a group of n rows gets nmt equal tiles of height rounded up to 32
+    for (int ti = tid; ti < total; ti += 1024) {
+        const int g = group_of(ti);
+        const int st = g ? gend[g - 1] : 0, nmt = gend[g] - st;
+        int b, e;
+        group_rows(g, b, e);
+        int hgt = (e - b + nmt - 1) / nmt;
+        hgt = ((hgt + 31) / 32) * 32;
+        const int rb = b + (ti - st) * hgt;
+        tiles[ti] = int4{g, rb, min(e, rb + hgt), 0};
+    }
+    // 3. work lists: per group, blocks of kMBlock M tiles, N tile by N tile, the
+    //    block's M tiles next to each other (32 consecutive items -- one XCD's
+    //    CUs -- share kMBlock row panels and 32 / kMBlock weight panels)
+    auto emit = [&](int2* __restrict__ work, int nt) {
+        for (int i = tid; i < total * nt; i += 1024) {
+            const int g = group_of(i / nt);
+            const int st = g ? gend[g - 1] : 0, nmt = gend[g] - st;
+            const int j = i - st * nt;
+            const int mb = (j / (kMBlock * nt)) * kMBlock;
+            const int r = j - mb * nt, mc = min(kMBlock, nmt - mb);
+            work[i] = int2{st + mb + r % mc, r / mc};
+        }
+    };
+    emit(work1, nt1);
+    emit(work2, nt2);
     if (tid == 0) n_tiles[0] = total;
 }
 

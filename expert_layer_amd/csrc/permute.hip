@@ -35,7 +35,8 @@ perm_hist(const int32_t* __restrict__ ids, int32_t* __restrict__ hist, int T, in
     for (int e = threadIdx.x; e < E; e += PB) hist[(size_t)blockIdx.x * E + e] = cnt[e];
 }
 
-// One workgroup of 1024 threads; thread e owns expert e (E <= 1024).
+// One workgroup of 1024 threads; thread e owns expert e (E <= 1024).  The
+// block counts are read in groups of 8 independent loads.
 __global__ void __launch_bounds__(1024)
 perm_scan(const int32_t* __restrict__ hist, int32_t* __restrict__ base, int32_t* __restrict__ counts,
           int32_t* __restrict__ offsets, int nblk, int E, int m_tile) {
@@ -43,10 +44,12 @@ perm_scan(const int32_t* __restrict__ hist, int32_t* __restrict__ base, int32_t*
     const int e = threadIdx.x, lane = e & 63, wv = e >> 6;
     int total = 0;
     if (e < E)
-        for (int b = 0; b < nblk; ++b) {
-            int v = hist[(size_t)b * E + e];
-            base[(size_t)b * E + e] = total;  // relative; made absolute below
-            total += v;
+        for (int b0 = 0; b0 < nblk; b0 += 8) {
+            int v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = b0 + i < nblk ? hist[(size_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) total += v[i];
         }
     int padded = e < E ? ((total + m_tile - 1) / m_tile) * m_tile : 0;
     // inclusive wave scan
@@ -60,11 +63,21 @@ perm_scan(const int32_t* __restrict__ hist, int32_t* __restrict__ base, int32_t*
     __syncthreads();
     int before = 0;
     for (int w = 0; w < wv; ++w) before += wsum[w];
-    int excl = before + incl - padded;
+    const int excl = before + incl - padded;
     if (e < E) {
         counts[e] = total;
         offsets[e] = excl;
-        for (int b = 0; b < nblk; ++b) base[(size_t)b * E + e] += excl;
+        int run = excl;
+        for (int b0 = 0; b0 < nblk; b0 += 8) {
+            int v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = b0 + i < nblk ? hist[(size_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if (b0 + i < nblk) base[(size_t)(b0 + i) * E + e] = run;
+                run += v[i];
+            }
+        }
     }
     if (e == E - 1) offsets[E] = excl + padded;
 }
