@@ -79,13 +79,21 @@ moe_status check_cfg(const moe_cfg* cp) {
         if (c.H > 16384 || c.I > 16384)
             return fail(MOE_ERR_UNSUPPORTED, "fp8 supports H and I up to 16384 (H=%d, I=%d)", c.H, c.I);
     }
+    if (c.act_dtype == MOE_BF16) {
+        // the bf16 GEMMs address one expert's matrices (and, indexed, all of x)
+        // through buffer descriptors below 2 GiB
+        auto mat = [&](int I) { return (int64_t)((I + 127) / 128) * 128 * 2 * ((c.H + 31) / 32) * 32 * 2; };
+        if (c.H > 65536 || c.I > 65536 || mat(c.I) >= ((int64_t)1 << 31) ||
+            (c.has_shared && (c.I_shared > 65536 || mat(c.I_shared) >= ((int64_t)1 << 31))))
+            return fail(MOE_ERR_UNSUPPORTED, "bf16 supports H, I <= 65536 and one expert's gate+up under 2 GiB");
+    }
     if (c.m_tile < 0 || c.m_tile > 4096) return fail(MOE_ERR_INVALID_ARG, "m_tile=%d must be in [0, 4096]", c.m_tile);
     if (c.x_layout != MOE_LAYOUT_ROWMAJOR && c.x_layout != MOE_LAYOUT_TILED && c.x_layout != MOE_LAYOUT_INDEXED)
         return fail(MOE_ERR_INVALID_ARG, "x_layout=%d", c.x_layout);
     if (c.x_layout == MOE_LAYOUT_INDEXED) {
         if (c.act_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "indexed x_perm is bf16 only");
-        if ((int64_t)c.T * c.H * 2 >= ((int64_t)1 << 32))
-            return fail(MOE_ERR_UNSUPPORTED, "indexed x_perm needs T*H*2 < 2^32");
+        if ((int64_t)c.T * c.H * 2 >= ((int64_t)1 << 31))
+            return fail(MOE_ERR_UNSUPPORTED, "indexed x_perm needs T*H*2 < 2^31");
     }
     if (c.x_layout == MOE_LAYOUT_TILED) {
         if (c.act_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "tiled x_perm is bf16 only");

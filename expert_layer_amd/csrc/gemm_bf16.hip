@@ -17,51 +17,78 @@
 //   GEMM1: the 64 weight rows of wave w are 32 gate rows and the 32 up rows of
 //          the same h columns: h = silu(g) * u is formed in registers.
 //   GEMM2: 256 output columns of y = h . w_down^T, fp32 or bf16.
-// Pipeline.  K advances in 32-wide stages through a ring of four 32 KiB LDS
-// buffers.  Operands move HBM -> LDS by buffer_load ... lds (no staging
-// registers), issued three stages ahead; a chunk outside the tile (rows past
-// the expert's end, columns past N, the K tail, stages past the end) carries an
-// offset beyond its buffer descriptor and loads as zero with no memory traffic.
-// Each stage has two 16-wide k steps with a register set each: the fragments of
+// Operand paths.  The rows (A) are shared by the four waves and go through
+// LDS; the weight rows of a wave are read by that wave alone, so they skip LDS
+// and stream from HBM straight into a ring of register sets, one per stage, in
+// MFMA fragment order (the tiled weight layout below makes each wave's stage
+// one contiguous 4 KiB read).  LDS then carries 80 KiB per stage (16 KiB of DMA
+// writes, 64 KiB of fragment reads) instead of 112 KiB.
+// Pipeline.  K advances in 32-wide stages; NS stages are in flight: NS LDS
+// buffers of 16 KiB for A, filled by buffer_load ... lds (no staging
+// registers), and NS register sets of 16 VGPRs for B.  A stage's loads are
+// issued NS - 1 stages ahead; a chunk outside the tile (rows past the expert's
+// end, columns past N, the K tail, stages past the end) carries an offset
+// beyond its buffer descriptor and loads as zero with no memory traffic.  Each
+// stage has two 16-wide k steps with an A register set each: the fragments of
 // the next k step are read while the MFMAs of this one run.  Between a stage's
-// two k steps: wait for the next stage's loads, one s_barrier, and issue the
-// loads three stages ahead into the buffer just drained -- so LDS latency and
-// HBM latency both hide behind the MFMA pipe.
+// two k steps: wait for the next stage's A, one s_barrier, and reissue the
+// drained A buffer; after a stage's last MFMA its B register set is reloaded.
 // LDS chunks of 16 B are XOR-swizzled by row, physical chunk = logical ^
 // ((row >> 1) & 3) ^ ((row >> 3) & 1): a fragment read of 16 consecutive rows
 // (one pass of ds_read_b128 through the 64 banks of gfx950's LDS) touches 16
 // distinct 16-byte bank groups, and so does any 8 consecutive rows.
 // Launch order: the work list (see ffn_build_tiles) remapped so that a
 // contiguous run of items lives on one XCD and shares its L2.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace moe {
 namespace {
 
 constexpr int BM = 256, BN = 256, BK = 32, NTH = 256;
-constexpr int NST = 4;                   // LDS stages in the ring (4 x 32 KiB; 5 measured no faster)
-constexpr int kSlots = BM * 4;           // 16-byte slots of one operand in one stage
-constexpr uint32_t kOOB = 0x40000000u;   // past every tile descriptor: the load returns zero
+#ifndef MOE_GEMM_STAGES
+#define MOE_GEMM_STAGES 6
+#endif
+constexpr int NS = MOE_GEMM_STAGES;      // stages in flight (A: LDS buffers, B: register sets)
+static_assert(NS >= 3 && NS <= 8, "the vmcnt arithmetic below holds for 3 to 8 stages");
+constexpr int kSlots = BM * 4;           // 16-byte slots of the A operand in one stage
+constexpr int kLoadsA = 4, kLoadsB = 4;  // vector-memory instructions per wave per stage
+constexpr uint32_t kOOB = 0x80000000u;   // past every descriptor (all are < 2 GiB): the load returns zero
 
 typedef __attribute__((address_space(3))) void* lds_t;
 
-// The stage buffers, [A: 256 rows x 64 B][B: 256 rows x 64 B] each.  They are
-// distinct objects so that the compiler can tell which buffer an in-flight LDS
-// DMA writes and never waits for a load into another buffer.
-__shared__ i32x4 ring0[2 * kSlots];
-__shared__ i32x4 ring1[2 * kSlots];
-__shared__ i32x4 ring2[2 * kSlots];
-__shared__ i32x4 ring3[2 * kSlots];
-__shared__ i32x4 ring4[2 * kSlots];
+// The A stage buffers, 256 rows x 64 B each.  They are distinct objects so
+// that the compiler can tell which buffer an in-flight LDS DMA writes and
+// never waits for a load into another buffer.
+__shared__ i32x4 ring0[kSlots];
+__shared__ i32x4 ring1[kSlots];
+__shared__ i32x4 ring2[kSlots];
+__shared__ i32x4 ring3[kSlots];
+__shared__ i32x4 ring4[kSlots];
+__shared__ i32x4 ring5[kSlots];
+__shared__ i32x4 ring6[kSlots];
+__shared__ i32x4 ring7[kSlots];
 
 template <int BUF>
 __device__ __forceinline__ i32x4* ring() {
-    static_assert(BUF < NST, "ring buffer index");
+    static_assert(BUF < NS, "ring buffer index");
     if constexpr (BUF == 0) return ring0;
     else if constexpr (BUF == 1) return ring1;
     else if constexpr (BUF == 2) return ring2;
     else if constexpr (BUF == 3) return ring3;
-    else return ring4;
+    else if constexpr (BUF == 4) return ring4;
+    else if constexpr (BUF == 5) return ring5;
+    else if constexpr (BUF == 6) return ring6;
+    else return ring7;
+}
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
 }
 
 // Workgroup barrier without a memory fence (a fence would wait for every
@@ -79,18 +106,26 @@ __device__ __forceinline__ void wait_vm() {
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // XOR pattern of the 16-byte chunks of an LDS row (only bits 1..3 of the row
-// matter, so rows 16 apart share it): the tiled layout's pattern.
+// matter, so rows 16 apart share it): the tiled row layout's pattern.
 __device__ __forceinline__ int swz_of_row(int row) { return tile_swz(row); }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// Operand layouts.  Row-major: [rows][K], K contiguous.  Tiled: 1 KiB blocks
-// of 16 rows x 32 k, block (rb, ks) at byte (rb * KS + ks) * 1024 with
-// KS = ceil(K / 32), the 16-byte chunks inside a block already in the LDS
-// order (chunk c of row r at slot r * 4 + (c ^ swz_of_row(r))), zero padded.
-// A tiled stage of 16 rows is one contiguous 1 KiB read.
+// Operand layouts.
+//  Row-major: [rows][K], K contiguous.
+//  Tiled rows (x_perm, the shared expert's tokens, the h tile slots): 1 KiB
+//    blocks of 16 rows x 32 k, block (rb, ks) at byte (rb * KS + ks) * 1024
+//    with KS = ceil(K / 32), the 16-byte chunks inside a block already in the
+//    LDS order (chunk c of row r at slot r * 4 + (c ^ swz_of_row(r))), zero
+//    padded.  A tiled stage of 16 rows is one contiguous 1 KiB read.
+//  Tiled weights (fragment order): the rows in groups of 64 (GEMM1: the 32
+//    gate rows and the 32 up rows of 32 h columns; GEMM2: 64 rows of w_down),
+//    group q, stage ks at byte (q * KS + ks) * 4096; inside, four 1 KiB MFMA
+//    B fragments j = 2 * c + kk (c: 32-row half, kk: 16-wide k step), lane l's
+//    16 bytes at l * 16 = row 32 c + l % 32, k = 32 ks + 16 kk + 8 (l / 32)
+//    .. + 7.  Zero padded in rows and k.
 struct GemmArgs {
     const uint16_t* a_routed;  // GEMM1: x rows (row-major or tiled); GEMM2: h tile slots (tiled)
     const uint16_t* a_shared;  // GEMM1: shared-expert tokens (row-major or tiled); GEMM2: h tile slots
@@ -112,63 +147,75 @@ struct GemmArgs {
     const int32_t* a_row_src;  // GEMM1, routed groups: non-NULL -> A row r is x row a_row_src[r] / a_row_k
     int a_row_k;
     int a_rows;                // rows of x (the indexed A operand)
-    int w_tiled;               // weights tiled (w13 / w2 layout)
+    int w_tiled;               // weights tiled (fragment order)
     int h_slot_ks;             // k blocks of one h tile slot (ceil(max(I, I_sh) / 32))
 };
 
-// Per-tile DMA state: buffer descriptors, the byte offsets of this lane's
-// 16-byte chunks in stage 0 (four A and four B load instructions per stage),
-// and how far a stage moves them (64 B row-major, 1 KiB tiled).
+// Per-tile load state.  A: the buffer descriptor, the byte offsets of this
+// lane's four 16-byte chunks in stage 0 and how far a stage moves them (64 B
+// row-major, 1 KiB tiled).  B: a descriptor per 32-row half of the wave's
+// weight rows, this lane's offset in stage 0, and the per-stage and per-k-step
+// moves (tiled: 4 KiB and 1 KiB; row-major: 64 B and 32 B).
 struct Dma {
-    __amdgpu_buffer_rsrc_t ra, rb0, rb1;
-    uint32_t va[4], vb[4];
-    uint32_t sa, sb;        // bytes per stage
+    __amdgpu_buffer_rsrc_t ra, rb[2];
+    uint32_t va[4];
+    uint32_t vb[2];
+    uint32_t sa, sb, kb;    // bytes per stage (A, B), bytes per k step (B)
     uint32_t kvalid_last;   // valid K columns in the last stage (multiple of 8)
     int nsteps;             // real stages
-    bool a_rm, b_rm;        // row-major operand: the K tail must be masked
+    int klim;               // B: this lane's loads of k step kk in stage t are real while 32 t + 16 kk < klim
+    bool a_rm;              // row-major A: the K tail must be masked
 };
 
-template <int MODE, int BUF>
-__device__ __forceinline__ void dma_stage(const Dma& d, int t, int wave, int lane) {
+template <int BUF>
+__device__ __forceinline__ void dma_a(const Dma& d, int t, int lane) {
     i32x4* buf = ring<BUF>();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const bool real = t < d.nsteps;
     const bool last = t == d.nsteps - 1;
     // row-major chunks of the K tail load zero (tiled operands are zero padded)
     const uint32_t logical8 = (uint32_t)(((lane & 3) ^ swz_of_row(lane >> 2)) * 8);
-    const bool tail_ok = !last || logical8 < d.kvalid_last;
-    const bool a_ok = real && (!d.a_rm || tail_ok), b_ok = real && (!d.b_rm || tail_ok);
-    const uint32_t ka = (uint32_t)t * d.sa, kb = (uint32_t)t * d.sb;
+    const bool a_ok = real && (!d.a_rm || !last || logical8 < d.kvalid_last);
+    const uint32_t ka = (uint32_t)t * d.sa;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kLoadsA; ++i) {
         const uint32_t off = a_ok ? d.va[i] + ka : kOOB;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ra, (lds_t)(buf + (wave * 4 + i) * 64), 16, off, 0, 0, 0);
     }
+}
+
+// B fragments of stage t: q[2 c + kk] = 32-row half c, k step kk.  A load is
+// real while kk * 16 is below the lane's limit for the stage (no limit for
+// the zero-padded tiled weights, the K tail for row-major ones, none at all
+// past the last stage); the rest carry kOOB.  Selects only: a branch here
+// would cost the wait counters their precision.
+__device__ __forceinline__ void load_b(const Dma& d, int t, i32x4 (&q)[4]) {
+    const int lim = t < d.nsteps ? d.klim - t * BK : -1;
+    const uint32_t base = (uint32_t)t * d.sb;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t off = b_ok ? d.vb[i] + kb : kOOB;
-        const __amdgpu_buffer_rsrc_t r = (MODE == 0 && i >= 2) ? d.rb1 : d.rb0;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_t)(buf + kSlots + (wave * 4 + i) * 64), 16, off, 0, 0, 0);
+    for (int j = 0; j < 4; ++j) {
+        const int c = j >> 1, kk = j & 1;
+        const uint32_t off = kk * 16 < lim ? d.vb[c] + base + (uint32_t)kk * d.kb : kOOB;
+        q[j] = __builtin_amdgcn_raw_buffer_load_b128(d.rb[c], off, 0, 0);
     }
 }
 
-// MFMA fragments of one 16-wide k step (kk) of a stage: A rows r*32 + lane%32
-// and B rows wave*64 + {0, 32} + lane%32, at logical chunk 2*kk + lane/32.
+// A fragments of one 16-wide k step (KK) of a stage: rows r*32 + lane%32 at
+// logical chunk 2*KK + lane/32.
 template <int NRB, int BUF, int KK>
-__device__ __forceinline__ void read_frags(int wave, int lane, i32x4 (&a)[NRB], i32x4 (&b)[2]) {
+__device__ __forceinline__ void read_a(int lane, i32x4 (&a)[NRB]) {
     const i32x4* buf = ring<BUF>();
     const int l32 = lane & 31, half = lane >> 5;
     const int phys = (KK * 2 + half) ^ swz_of_row(l32);
 #pragma unroll
     for (int r = 0; r < NRB; ++r) a[r] = buf[(r * 32 + l32) * 4 + phys];
-    b[0] = buf[kSlots + (wave * 64 + l32) * 4 + phys];
-    b[1] = buf[kSlots + (wave * 64 + 32 + l32) * 4 + phys];
 }
 
 template <int NRB>
-__device__ __forceinline__ void mma(const i32x4 (&a)[NRB], const i32x4 (&b)[2], f32x16 (&acc0)[8],
+__device__ __forceinline__ void mma(const i32x4 (&a)[NRB], const i32x4& b0i, const i32x4& b1i, f32x16 (&acc0)[8],
                                     f32x16 (&acc1)[8]) {
-    const bf16x8 b0 = __builtin_bit_cast(bf16x8, b[0]);
-    const bf16x8 b1 = __builtin_bit_cast(bf16x8, b[1]);
+    const bf16x8 b0 = __builtin_bit_cast(bf16x8, b0i);
+    const bf16x8 b1 = __builtin_bit_cast(bf16x8, b1i);
 #pragma unroll
     for (int r = 0; r < NRB; ++r) {
         const bf16x8 av = __builtin_bit_cast(bf16x8, a[r]);
@@ -177,31 +224,42 @@ __device__ __forceinline__ void mma(const i32x4 (&a)[NRB], const i32x4 (&b)[2], 
     }
 }
 
-// One pipeline stage (two 16-wide k steps) on stage s, held in buffer BUF.
-// Fragment set kk holds k step kk; entering, set 0 holds stage s, k step 0.
+// vmcnt after which this wave's A loads of the next stage have landed: the
+// loads issued after them are that stage's B loads and the A and B loads of
+// the NS - 2 stages after it.
+constexpr int kWaitNextA = kLoadsB + (kLoadsA + kLoadsB) * (NS - 2);
+// ... and, in the prologue, stage 0's A loads: every later load of NS stages.
+constexpr int kWaitFirstA = kLoadsB + (kLoadsA + kLoadsB) * (NS - 1);
+static_assert(kWaitFirstA < 64, "vmcnt is 6 bits");
+
+// One pipeline stage (two 16-wide k steps) on stage s, A in buffer BUF, B in
+// register set BUF.  A set kk holds k step kk; entering, set 0 holds stage s,
+// k step 0.
 template <int MODE, int NRB, int BUF>
-__device__ __forceinline__ void stage(const Dma& d, int s, int wave, int lane, i32x4 (&fa)[2][NRB],
-                                      i32x4 (&fb)[2][2], f32x16 (&acc0)[8], f32x16 (&acc1)[8]) {
+__device__ __forceinline__ void stage(const Dma& d, int s, int lane, i32x4 (&fa)[2][NRB], i32x4 (&bq)[NS][4],
+                                      f32x16 (&acc0)[8], f32x16 (&acc1)[8]) {
     // k step 0: read k step 1 of this stage while the MFMAs of k step 0 run
     wait_lgkm0();
-    read_frags<NRB, BUF, 1>(wave, lane, fa[1], fb[1]);
+    read_a<NRB, BUF, 1>(lane, fa[1]);
     __builtin_amdgcn_sched_barrier(0);
-    mma<NRB>(fa[0], fb[0], acc0, acc1);
+    mma<NRB>(fa[0], bq[BUF][0], bq[BUF][2], acc0, acc1);
     __builtin_amdgcn_sched_barrier(0);
-    // k step 1: hand buffer BUF back to the DMA and start on stage s+1
-    wait_lgkm0();     // every read of buffer BUF by this wave has returned
-    wait_vm<(NST - 2) * 8>();  // this wave's loads of stage s+1 have landed (s+2 .. s+NST-1 may be in flight)
-    barrier_lds();    // ... everybody's have, and everybody is done with buffer BUF
-    dma_stage<MODE, BUF>(d, s + NST, wave, lane);
-    read_frags<NRB, (BUF + 1) % NST, 0>(wave, lane, fa[0], fb[0]);
+    // k step 1: hand A buffer BUF back to the DMA and start on stage s+1
+    wait_lgkm0();             // every read of buffer BUF by this wave has returned
+    wait_vm<kWaitNextA>();    // this wave's A loads of stage s+1 have landed
+    barrier_lds();            // ... everybody's have, and everybody is done with buffer BUF
+    dma_a<BUF>(d, s + NS, lane);
+    read_a<NRB, (BUF + 1) % NS, 0>(lane, fa[0]);
     __builtin_amdgcn_sched_barrier(0);
-    mma<NRB>(fa[1], fb[1], acc0, acc1);
+    mma<NRB>(fa[1], bq[BUF][1], bq[BUF][3], acc0, acc1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_b(d, s + NS, bq[BUF]);  // register set BUF is free once its MFMAs have issued
     __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int MODE, int NRB>
 __device__ __forceinline__ void run_tile(const GemmArgs& p, int mt, int g, int row0, int M, int n0, int K, int N,
-                                         bool shared) {
+                                         bool shared, int nt) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l32 = lane & 31;
@@ -230,32 +288,8 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, int mt, int g, int r
     }
     const bool a_indexed = MODE == 0 && !shared && p.a_row_src != nullptr;
     d.sa = a_tiled ? 1024u : (uint32_t)(BK * 2);
-    // ---- B: the weight rows of this N tile
-    const int ncols = MODE == 0 ? min(BN / 2, N - n0) : min(BN, N - n0);
-    d.b_rm = !p.w_tiled;
-    if (p.w_tiled) {
-        // GEMM1: w13 tiled, 2 * roundup(I, 128) rows with gate and up interleaved per
-        // wave (32 gate rows, then the 32 up rows of the same h columns);
-        // GEMM2: w2 tiled, H rows.  The tile starts at row-block 16 * nt.
-        const int rows = MODE == 0 ? 2 * (((N + 127) / 128) * 128) : N;
-        const int rbs = (rows + 15) / 16;
-        const size_t mat = (size_t)rbs * KS * 512;
-        const uint16_t* W = (shared ? p.w0_shared : p.w0_routed + (size_t)g * mat);
-        const int rb0 = MODE == 0 ? (n0 / 128) * 16 : (n0 / 256) * 16;
-        d.rb0 = make_rsrc(W + (size_t)rb0 * KS * 512, (uint32_t)((rbs - rb0) * KS * 1024));
-        d.rb1 = d.rb0;
-        d.sb = 1024u;
-    } else {
-        const size_t wmat = (size_t)K * (size_t)N;
-        const uint16_t* W0 = (shared ? p.w0_shared : p.w0_routed + (size_t)g * wmat) + (size_t)n0 * K;
-        const uint16_t* W1 =
-            MODE == 0 ? (shared ? p.w1_shared : p.w1_routed + (size_t)g * wmat) + (size_t)n0 * K : nullptr;
-        d.rb0 = make_rsrc(W0, (uint32_t)ncols * (uint32_t)K * 2u);
-        d.rb1 = MODE == 0 ? make_rsrc(W1, (uint32_t)ncols * (uint32_t)K * 2u) : d.rb0;
-        d.sb = (uint32_t)(BK * 2);
-    }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kLoadsA; ++i) {
         const int blk = wave * 4 + i;           // 16-row block of the tile this instruction fills
         const int row = blk * 16 + (lane >> 2);
         const uint32_t logical8 = (uint32_t)(((lane & 3) ^ swz_of_row(row)) * 8);
@@ -267,13 +301,40 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, int mt, int g, int r
         } else {
             d.va[i] = row < M ? ((uint32_t)row * (uint32_t)K + logical8) * 2u : kOOB;
         }
-        if (p.w_tiled) {
-            d.vb[i] = (uint32_t)blk * (uint32_t)KS * 1024u + (uint32_t)lane * 16u;
-        } else {
-            // B row of this chunk, relative to the tile's first weight row n0
-            const int bc = MODE == 0 ? wave * 32 + (i & 1) * 16 + (lane >> 2) : wave * 64 + i * 16 + (lane >> 2);
-            d.vb[i] = bc < ncols ? ((uint32_t)bc * (uint32_t)K + logical8) * 2u : kOOB;
+    }
+    // ---- B: the 64 weight rows of this wave (GEMM1: 32 gate and 32 up rows of
+    // h columns n0 + 32 w .. +31; GEMM2: rows n0 + 64 w .. +63)
+    if (p.w_tiled) {
+        d.klim = 1 << 30;  // zero padded
+        // fragment-order groups of 64 rows: GEMM1 2 * roundup(N, 128) rows, GEMM2 N rows
+        const int groups = MODE == 0 ? ((N + 127) / 128) * 4 : (N + 63) / 64;
+        const size_t mat = (size_t)groups * KS * 2048;  // elements of one expert's matrix
+        const uint16_t* W = shared ? p.w0_shared : p.w0_routed + (size_t)g * mat;
+        const int q0 = nt * 4;                          // first group of the N tile
+        d.rb[0] = make_rsrc(W + (size_t)q0 * KS * 2048, (uint32_t)((groups - q0) * KS * 4096));
+        d.rb[1] = d.rb[0];
+        const uint32_t base = (uint32_t)wave * (uint32_t)KS * 4096u + (uint32_t)lane * 16u;
+        d.vb[0] = base;
+        d.vb[1] = base + 2048u;
+        d.sb = 4096u;
+        d.kb = 1024u;
+    } else {
+        const int ncols = MODE == 0 ? min(BN / 2, N - n0) : min(BN, N - n0);
+        const size_t wmat = (size_t)K * (size_t)N;
+        const uint16_t* W0 = (shared ? p.w0_shared : p.w0_routed + (size_t)g * wmat) + (size_t)n0 * K;
+        const uint16_t* W1 =
+            MODE == 0 ? (shared ? p.w1_shared : p.w1_routed + (size_t)g * wmat) + (size_t)n0 * K : W0;
+        d.rb[0] = make_rsrc(W0, (uint32_t)ncols * (uint32_t)K * 2u);
+        d.rb[1] = make_rsrc(W1, (uint32_t)ncols * (uint32_t)K * 2u);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            // the B row of half c relative to n0 (GEMM1: gate for c = 0, up for c = 1, same row)
+            const int br = MODE == 0 ? wave * 32 + l32 : wave * 64 + c * 32 + l32;
+            d.vb[c] = br < ncols ? ((uint32_t)br * (uint32_t)K + (uint32_t)(lane >> 5) * 8u) * 2u : kOOB;
         }
+        d.sb = (uint32_t)(BK * 2);
+        d.kb = 32u;
+        d.klim = K - (lane >> 5) * 8;  // the lane's chunk starts 8 (lane / 32) into the k step
     }
 
     f32x16 acc0[8], acc1[8];
@@ -282,29 +343,27 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, int mt, int g, int r
         acc0[i] = f32x16{};
         acc1[i] = f32x16{};
     }
-    i32x4 fa[2][NRB], fb[2][2];
+    i32x4 fa[2][NRB];
+    i32x4 bq[NS][4];
 
-    static_assert(NST == 4 || NST == 5, "the prologue and the loop body are written for 4 or 5 stages");
-    dma_stage<MODE, 0>(d, 0, wave, lane);
-    dma_stage<MODE, 1>(d, 1, wave, lane);
-    dma_stage<MODE, 2>(d, 2, wave, lane);
-    dma_stage<MODE, 3>(d, 3, wave, lane);
-    if constexpr (NST == 5) dma_stage<MODE, NST - 1>(d, 4, wave, lane);
-    wait_vm<(NST - 1) * 8>();
+    static_for<0, NS>([&](auto c) {
+        constexpr int t = decltype(c)::value;
+        dma_a<t>(d, t, lane);
+        load_b(d, t, bq[t]);
+    });
+    wait_vm<kWaitFirstA>();
     barrier_lds();
-    read_frags<NRB, 0, 0>(wave, lane, fa[0], fb[0]);
+    read_a<NRB, 0, 0>(lane, fa[0]);
     // stages past the end load zeros, so the loop runs in whole turns of the ring
-    const int nturns = (d.nsteps + NST - 1) / NST;
-    for (int s = 0; s < nturns * NST; s += NST) {
-        stage<MODE, NRB, 0>(d, s, wave, lane, fa, fb, acc0, acc1);
-        stage<MODE, NRB, 1>(d, s + 1, wave, lane, fa, fb, acc0, acc1);
-        stage<MODE, NRB, 2>(d, s + 2, wave, lane, fa, fb, acc0, acc1);
-        stage<MODE, NRB, 3>(d, s + 3, wave, lane, fa, fb, acc0, acc1);
-        if constexpr (NST == 5) stage<MODE, NRB, NST - 1>(d, s + 4, wave, lane, fa, fb, acc0, acc1);
+    const int nturns = (d.nsteps + NS - 1) / NS;
+    for (int s = 0; s < nturns * NS; s += NS) {
+        static_for<0, NS>([&](auto c) {
+            constexpr int b = decltype(c)::value;
+            stage<MODE, NRB, b>(d, s + b, lane, fa, bq, acc0, acc1);
+        });
     }
     wait_vm<0>();  // no LDS DMA may outlive the workgroup
     wait_lgkm0();
-
     void* out = shared ? p.out_shared : p.out_routed;
     if (MODE == 0) {
         // h = silu(g) * u into this M tile's slot, tiled with the slot's own KS
@@ -368,14 +427,14 @@ ffn_gemm_bf16(GemmArgs p) {
     const int n0 = MODE == 0 ? nt * (BN / 2) : nt * BN;
     if (n0 >= N || M <= 0) return;
     switch ((M + 31) >> 5) {
-    case 1: run_tile<MODE, 1>(p, mt, g, row0, M, n0, K, N, shared); break;
-    case 2: run_tile<MODE, 2>(p, mt, g, row0, M, n0, K, N, shared); break;
-    case 3: run_tile<MODE, 3>(p, mt, g, row0, M, n0, K, N, shared); break;
-    case 4: run_tile<MODE, 4>(p, mt, g, row0, M, n0, K, N, shared); break;
-    case 5: run_tile<MODE, 5>(p, mt, g, row0, M, n0, K, N, shared); break;
-    case 6: run_tile<MODE, 6>(p, mt, g, row0, M, n0, K, N, shared); break;
-    case 7: run_tile<MODE, 7>(p, mt, g, row0, M, n0, K, N, shared); break;
-    default: run_tile<MODE, 8>(p, mt, g, row0, M, n0, K, N, shared); break;
+    case 1: run_tile<MODE, 1>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
+    case 2: run_tile<MODE, 2>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
+    case 3: run_tile<MODE, 3>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
+    case 4: run_tile<MODE, 4>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
+    case 5: run_tile<MODE, 5>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
+    case 6: run_tile<MODE, 6>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
+    case 7: run_tile<MODE, 7>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
+    default: run_tile<MODE, 8>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
     }
 }
 
@@ -545,41 +604,45 @@ hipError_t launch_gemm_bf16(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_
 }
 
 // ------------------------------------------------------------- weight tiling
-// Rewrites E row-major bf16 matrices [rows][K] into the tiled layout, one
-// thread per destination 16-byte chunk.  With `pair` set, the destination row
-// d of two source matrices (gate, up) is interleaved the way GEMM1 consumes
-// it: in every 256-row group j, wave w owns rows 64w .. 64w+63 = the 32 gate
-// rows then the 32 up rows of h columns 128j + 32w .. +31.  Rows and columns
-// past the source are zero.
+// Rewrites E row-major bf16 matrices [rows][K] into the fragment-order layout
+// (see the operand layouts above), one thread per destination 16-byte chunk.
+// With `pair` set, the 64 rows of group q are the 32 gate rows (src0) and then
+// the 32 up rows (src1) of h columns 32 q .. 32 q + 31, the way a GEMM1 wave
+// consumes them.  Rows and columns past the source are zero.
 __global__ void __launch_bounds__(256)
 tile_matrices(const uint16_t* __restrict__ src0, const uint16_t* __restrict__ src1, int E, int rows, int K,
-              int pair, uint16_t* __restrict__ dst, int rbs, int KS) {
-    const size_t per = (size_t)rbs * KS * 64;
+              int pair, uint16_t* __restrict__ dst, int groups, int KS) {
+    const size_t per = (size_t)groups * KS * 256;  // 16-byte chunks of one matrix
     const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= per * E) return;
     const int e = (int)(idx / per);
     const size_t rem = idx % per;
-    const int slot = (int)(rem & 63);
-    const size_t blk = rem >> 6;
-    const int ks = (int)(blk % KS), rb = (int)(blk / KS);
-    const int r = slot >> 2, chunk = (slot & 3) ^ swz_of_row(r);
-    const int drow = rb * 16 + r, k0 = ks * BK + chunk * 8;
+    const int lane = (int)(rem & 63), j = (int)((rem >> 6) & 3);
+    const size_t qs = rem >> 8;
+    const int ks = (int)(qs % KS), q = (int)(qs / KS);
+    const int c = j >> 1, kk = j & 1;
+    const int k0 = ks * BK + kk * 16 + (lane >> 5) * 8;
     const uint16_t* src = src0;
-    int srow = drow;
+    int srow = q * 64 + c * 32 + (lane & 31);
     if (pair) {
-        const int j = drow >> 8, w = (drow & 255) >> 6, q = drow & 63;
-        src = q < 32 ? src0 : src1;
-        srow = j * 128 + w * 32 + (q & 31);
+        src = c ? src1 : src0;
+        srow = q * 32 + (lane & 31);
     }
     i32x4 v = {0, 0, 0, 0};
     if (srow < rows && k0 < K) v = *reinterpret_cast<const i32x4*>(src + ((size_t)e * rows + srow) * K + k0);
-    reinterpret_cast<i32x4*>(dst)[(size_t)e * per + blk * 64 + slot] = v;
+    reinterpret_cast<i32x4*>(dst)[idx] = v;
 }
+
+// Groups of 64 rows of the fragment-order matrices: gate+up of I h columns
+// (I padded to 128: whole GEMM1 N tiles), down of H rows.
+static int groups13(int I) { return ((I + 127) / 128) * 4; }
+static int groups2(int H) { return (H + 63) / 64; }
 
 TiledSizes tiled_sizes(const moe_cfg& c) {
     TiledSizes t{};
-    auto w13 = [&](int I) { return (size_t)(2 * ((I + 127) / 128) * 128 / 16) * ((c.H + BK - 1) / BK) * 1024; };
-    auto w2 = [&](int I) { return (size_t)((c.H + 15) / 16) * ((I + BK - 1) / BK) * 1024; };
+    const size_t ksh = (size_t)((c.H + BK - 1) / BK);
+    auto w13 = [&](int I) { return (size_t)groups13(I) * ksh * 4096; };
+    auto w2 = [&](int I) { return (size_t)groups2(c.H) * (size_t)((I + BK - 1) / BK) * 4096; };
     t.w13 = w13(c.I) * c.E;
     t.w2 = w2(c.I) * c.E;
     t.sh13 = c.has_shared ? w13(c.I_shared) : 0;
@@ -590,12 +653,11 @@ TiledSizes tiled_sizes(const moe_cfg& c) {
 hipError_t launch_tile_weights(const moe_cfg& c, const moe_weights& src, void* w13, void* w2, void* sh13, void* sh2,
                                hipStream_t s) {
     auto go = [&](const void* a, const void* b, int E, int rows, int K, int pair, void* dst) {
-        const int rows_t = pair ? 2 * ((rows + 127) / 128) * 128 : rows;
-        const int rbs = (rows_t + 15) / 16, KS = (K + BK - 1) / BK;
-        const size_t n = (size_t)E * rbs * KS * 64;
+        const int groups = pair ? groups13(rows) : groups2(rows), KS = (K + BK - 1) / BK;
+        const size_t n = (size_t)E * groups * KS * 256;
         hipLaunchKernelGGL(tile_matrices, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                            static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b), E, rows, K, pair,
-                           static_cast<uint16_t*>(dst), rbs, KS);
+                           static_cast<uint16_t*>(dst), groups, KS);
     };
     go(src.w_gate, src.w_up, c.E, c.I, c.H, 1, w13);
     go(src.w_down, nullptr, c.E, c.H, c.I, 0, w2);

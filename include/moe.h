@@ -107,11 +107,16 @@ typedef enum moe_stage {
  *                (1 = no padding; 0 = library default, 1)
  *   x_layout     layout of x_perm between moe_permute and moe_grouped_ffn:
  *                MOE_LAYOUT_ROWMAJOR: [moe_max_rows][H] in act_dtype;
- *                MOE_LAYOUT_TILED (bf16, m_tile a multiple of 16): the tiled
- *                layout of moe_tile_weights over R16 = roundup(moe_max_rows, 16)
- *                rows of H columns, followed, when has_shared, by a tiled copy
- *                of x's T rows (padded to 16) that the shared expert reads;
- *                MOE_LAYOUT_INDEXED (bf16): x_perm is not materialised --
+ *                MOE_LAYOUT_TILED (bf16, m_tile a multiple of 16): the rows
+ *                in 1 KiB blocks of 16 rows x 32 columns, block (rb, ks) at
+ *                byte (rb * KS + ks) * 1024 with KS = ceil(H / 32), the 16-byte
+ *                chunk c (columns 8c .. 8c+7) of block row r at byte
+ *                (r * 4 + (c ^ s(r))) * 16, s(r) = ((r >> 1) & 3) ^ ((r >> 3) & 1),
+ *                zero padded; R16 = roundup(moe_max_rows, 16) rows, followed,
+ *                when has_shared, by the same layout of x's T rows (padded to
+ *                16) that the shared expert reads;
+ *                MOE_LAYOUT_INDEXED (bf16, T * H * 2 < 2^31): x_perm is not
+ *                materialised --
  *                moe_permute writes the maps only and moe_grouped_ffn reads
  *                dispatched row r from x itself, at token row_src[r] / k;
  *                moe_x_perm_bytes gives the size (0 when indexed).
@@ -132,9 +137,12 @@ typedef struct moe_cfg {
  * (dequantised weight = e4m3 value * block scale); NULL otherwise.  sh_* are
  * the shared expert's matrices (NULL when has_shared == 0; bf16/fp32 only).
  * layout MOE_LAYOUT_ROWMAJOR: the matrices as above.  layout MOE_LAYOUT_TILED
- * (bf16 only): w_gate and sh_gate point to the tiled gate+up matrices and
- * w_down and sh_down to the tiled down matrices written by moe_tile_weights;
- * w_up and sh_up are unused (NULL). */
+ * (bf16 only): w_gate and sh_gate point to the gate+up matrices and w_down and
+ * sh_down to the down matrices that moe_tile_weights writes, rearranged into
+ * the order in which the GEMMs load MFMA operands (an internal layout: write
+ * it with moe_tile_weights only); w_up and sh_up are unused (NULL).
+ * bf16 needs H, I, I_shared <= 65536 and one expert's gate+up matrices
+ * (padded: 2 * roundup(I, 128) x roundup(H, 32) bf16) under 2 GiB. */
 typedef struct moe_weights {
     const void *w_gate, *w_up, *w_down;
     const float *s_gate, *s_up, *s_down;
