@@ -254,6 +254,8 @@ moe_status check_ws(void* ws, size_t have, size_t need) {
 
 #define REQUIRE(p, name) \
     if (!(p)) return fail(MOE_ERR_INVALID_ARG, "%s is NULL", name)
+#define REQUIRE_A16(p, name) \
+    if (reinterpret_cast<uintptr_t>(p) % 16) return fail(MOE_ERR_INVALID_ARG, "%s is not 16-byte aligned", name)
 
 // Checks the weight pointers a call reads (before anything is enqueued).
 moe_status check_weights(const moe_cfg& c, const moe_weights* w) {
@@ -439,6 +441,10 @@ moe_status moe_grouped_ffn(const moe_cfg* cfg, int64_t n_rows_cap, const void* x
         if (!tiled && !indexed) REQUIRE(x_tokens, "x_tokens");
         REQUIRE(y_shared, "y_shared");
     }
+    REQUIRE_A16(x_rows, "x_rows");
+    REQUIRE_A16(x_tokens, "x_tokens");
+    REQUIRE_A16(y_rows, "y_rows");
+    REQUIRE_A16(y_shared, "y_shared");
     const size_t need = ffn_carve(c, n_rows_cap, nullptr).bytes;
     if ((st = check_ws(ws, ws_bytes, need)) != MOE_OK) return st;
     if (n_rows_cap == 0 && !(c.has_shared && c.T > 0)) return MOE_OK;

@@ -389,22 +389,40 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, int mt, int g, int r
             }
         }
     } else {
-        const int c0 = n0 + wave * 64 + l32, c1 = c0 + 32;
+        // y through LDS, one 32-row block at a time: each wave stages its 32 x 64
+        // block in a private 8 KiB slice of the A ring (free once every wave has
+        // left the main loop), fp32, row r at r * 256 B with the two 128-byte
+        // halves swapped when bit 2 of r is set -- the accumulator writes (rows
+        // r and r + 4 in the two half-waves) and the 16-byte reads (16 lanes per
+        // row) both touch 64 distinct banks -- then stores 4 columns per lane:
+        // 16 lanes cover a row's 64 columns.  LDS operations of one wave are
+        // processed in order, so a block's reads finish before the next block's
+        // writes land.
+        barrier_lds();
+        float* st = reinterpret_cast<float*>((wave < 2 ? ring<0>() : ring<1>()) + (wave & 1) * 512);
+        const int cw = n0 + wave * 64;  // first output column of this wave
 #pragma unroll
         for (int r = 0; r < NRB; ++r) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int row = r * 32 + c_row(i, lane);
-                if (row < M) {
-                    const size_t o = (size_t)(row0 + row) * N;
+                const int row = c_row(i, lane);  // bit 2 of row is lane / 32
+                st[row * 64 + lane] = acc0[r][i];
+                st[row * 64 + (lane ^ 32)] = acc1[r][i];
+            }
+#pragma unroll
+            for (int it = 0; it < 8; ++it) {
+                const int q = it * 64 + lane;  // chunk q: row q / 16, columns 4 (q % 16) .. + 3
+                const int row = q >> 4, c4 = (q & 15) * 4;
+                const f32x4 v = *reinterpret_cast<const f32x4*>(st + row * 64 + (c4 ^ (((row >> 2) & 1) << 5)));
+                const int grow = r * 32 + row, col = cw + c4;
+                if (grow < M && col < N) {
+                    const size_t o = (size_t)(row0 + grow) * N + col;
                     if (p.out_f32) {
-                        float* y = static_cast<float*>(out);
-                        if (c0 < N) y[o + c0] = acc0[r][i];
-                        if (c1 < N) y[o + c1] = acc1[r][i];
+                        *reinterpret_cast<f32x4*>(static_cast<float*>(out) + o) = v;
                     } else {
-                        uint16_t* y = static_cast<uint16_t*>(out);
-                        if (c0 < N) y[o + c0] = f32_to_bf16(acc0[r][i]);
-                        if (c1 < N) y[o + c1] = f32_to_bf16(acc1[r][i]);
+                        const uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+                        const uint32_t hi = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+                        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + o) = make_uint2(lo, hi);
                     }
                 }
             }

@@ -153,6 +153,9 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
     st = lib.moe_grouped_ffn(ctypes.byref(c), 10**6, fake, None, fake, None, ctypes.byref(w), None, fake, None, fake,
                              1 << 20, None)
     assert st == m.MOE_ERR_WORKSPACE
+    st = lib.moe_grouped_ffn(ctypes.byref(c), 32, fake, None, fake, None, ctypes.byref(w), None,
+                             ctypes.c_void_p(0x100008), None, fake, 1 << 30, None)
+    assert st == m.MOE_ERR_INVALID_ARG and "y_rows" in m.moe_last_error() and "aligned" in m.moe_last_error()
     ct = m.make_cfg(T=16, H=64, E=8, k=2, I=64, m_tile=16, x_layout=m.MOE_LAYOUT_TILED)
     st = lib.moe_grouped_ffn(ctypes.byref(ct), 32, fake, None, fake, None, ctypes.byref(w), None, fake, None, fake,
                              1 << 30, None)
