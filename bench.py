@@ -17,6 +17,10 @@ router), tokens/s, the fraction of the bf16 dense MFMA peak, a per-stage
 breakdown timed with HIP events on the launch stream, the roofline of the
 dominant stage (the grouped FFN), and the oracle's CPU throughput on a bounded
 sample of the same arithmetic.
+
+--workload c5_dsv3_ep_fp8 times the fp8 grouped FFN alone on one GPU's
+expert-parallel share (65536 dispatched rows over 8 local experts, e4m3 with
+block scales): a step is one moe_grouped_ffn call, against the fp8 peak.
 """
 from __future__ import annotations
 
@@ -32,6 +36,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 (e4m3) MFMA
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 METRIC = "MoE-layer TFLOP/s + tokens/s (1 GPU, DSV3 prefill shape); % of MFMA peak"
@@ -150,8 +155,10 @@ def main():
     if a.traffic_run:
         calibrate_copy(dev)
     s = synth.config(a.workload)
+    if s.dtype == "fp8":
+        return bench_fp8_ffn(a, s, dev)
     if s.dtype != "bf16":
-        raise SystemExit("bench.py times the bf16 layers (c2/c3/c4)")
+        raise SystemExit("bench.py times the bf16 layers (c2/c3/c4) and the fp8 grouped FFN (c5)")
     T, H, E, k, I = s.T, s.H, s.E, s.k, s.I
     c = moe.make_cfg(T=T, H=H, E=E, k=k, I=I, n_groups=s.n_groups, topk_groups=s.topk_groups,
                      score_fn=moe.MOE_SCORE_SIGMOID if s.score == "sigmoid" else moe.MOE_SCORE_SOFTMAX,
@@ -327,6 +334,70 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "sclk": sclk,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def bench_fp8_ffn(a, s, dev):
+    """c5: one GPU's expert-parallel share of a prefill layer -- the rows
+    arrive dispatched (per-expert counts of the workload), so a step is one
+    fp8 moe_grouped_ffn over them: e4m3 rows with 1x128 scales, e4m3 weights
+    with 128x128 block scales, bf16 y."""
+    import numpy as np
+    import torch
+
+    import expert_layer_amd as moe
+    import synth
+
+    if a.traffic_run:
+        raise SystemExit("--traffic-run profiles the bf16 layer")
+    t_gen = time.time()
+    counts = synth.fp8_counts(s)
+    wq = [synth.fp8_expert_weights(s, e, dev) for e in range(s.E)]
+    wg, sg, wu, su, wd, sd = (torch.stack([w[i] for w in wq]) for i in range(6))
+    del wq
+    xq, xs = synth.fp8_rows(s, s.T, dev)
+    offs = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32, device=dev)
+    c = moe.make_cfg(T=s.T, H=s.H, E=s.E, k=1, I=s.I, act_dtype=moe.MOE_FP8_E4M3, y_dtype=moe.MOE_BF16)
+    y = torch.empty((s.T, s.H), dtype=torch.bfloat16, device=dev)
+    ws = moe.workspace(c, moe.MOE_STAGE_FFN, dev, n_rows_cap=s.T)
+    w = moe.weights(wg, wu, wd, s_gate=sg, s_up=su, s_down=sd)
+    torch.cuda.synchronize()
+    print(f"[bench] inputs ready in {time.time() - t_gen:.1f}s", file=sys.stderr, flush=True)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        moe.moe_grouped_ffn(c, s.T, xq, xs, offs, w, None, y, None, ws, stream)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(a.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / a.steps
+    flop = 6.0 * s.H * s.I * s.T
+    tflops = flop / (ms * 1e-3) / 1e12
+    res = {
+        "metric": "grouped FFN TFLOP/s (1 GPU, fp8 expert-parallel share of a DeepSeek-V3 prefill layer)",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8_e4m3", "data": "synthetic",
+        "config": {"workload": a.workload, "rows": s.T, "H": s.H, "E_local": s.E, "I": s.I,
+                   "counts": [int(v) for v in counts], "scales": "1x128 rows, 128x128 weights",
+                   "out_dtype": "bf16"},
+        "tokens_per_s": round(s.T / (ms * 1e-3), 1),
+        "wall_s_timed": round(wall, 3),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_FP8_TFLOPS, 4), "traffic": None,
+                     "kernel": "moe_grouped_ffn (ffn_gemm_fp8 GEMM1+SwiGLU+requantise, GEMM2, tile list)",
+                     "flop_per_launch": flop},
+        "cpu_baseline": None,
     }
     print(json.dumps(res), flush=True)
 
