@@ -16,6 +16,9 @@
 //                  (row-major x_perm); perm_band_tiled instead writes the tiled
 //                  x_perm band by band, gathering each row from its token;
 //  5. perm_zero    padding rows (m_tile > 1) of the row-major x_perm are zeroed.
+// With the indexed layout (moe_layer's) steps 4 and 5 do not run: only the
+// maps are written, and the grouped FFN reads each dispatched row from x
+// through row_src, so the payload crosses HBM once, inside GEMM1.
 #include "common.hpp"
 
 namespace moe {

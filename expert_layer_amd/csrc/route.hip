@@ -6,13 +6,17 @@
 // Table 2, section 3.2.1).
 //
 // Kernel 1 (router_logits_bf16): logits[T][E] = x[T][H] . w_router[E][H]^T on
-// bf16 MFMA with fp32 accumulation.  One workgroup (4 waves) owns 32 tokens x
-// 128 experts; each wave one 32 x 32 block.  The K loop stages 64-wide slices
-// of x and w_router through LDS (double-buffered, XOR-swizzled 16-byte
-// chunks), so x streams from HBM once per expert slab and every global load is
-// a coalesced 128-byte row segment.  The kernel is bound by the HBM read of x.
-// Kernel 2 (route_select): one wave per token -- scores, group limit, top-k
-// with ties to the lower index, renormalisation and scaling.
+// bf16 MFMA with fp32 accumulation.  One workgroup (4 waves) owns 128 tokens x
+// 256 experts over one slice of K; each wave 128 tokens x 64 experts (4 x 2
+// blocks of 32 x 32).  Operands move HBM -> LDS by buffer_load ... lds through
+// a ring of four 32-wide stages (XOR-swizzled 16-byte chunks), so x streams
+// from HBM once per 256 experts.  K is split so that T / 128 token blocks
+// still fill the chip; the splits write fp32 partial logits that route_select
+// adds in split order (a fixed order, so the result does not depend on
+// scheduling).  The kernel is bound by the HBM read of x.
+// Kernel 2 (route_select): one wave per token -- the partial logits summed,
+// scores, group limit, top-k with ties to the lower index, renormalisation and
+// scaling.
 #include "common.hpp"
 
 namespace moe {
