@@ -232,12 +232,96 @@ constexpr int kWaitNextA = kLoadsB + (kLoadsA + kLoadsB) * (NS - 2);
 constexpr int kWaitFirstA = kLoadsB + (kLoadsA + kLoadsB) * (NS - 1);
 static_assert(kWaitFirstA < 64, "vmcnt is 6 bits");
 
+#ifndef MOE_GEMM_INTERLEAVE
+#define MOE_GEMM_INTERLEAVE 1
+#endif
+// MFMA row blocks of k step 1 issued before the stage's barrier (they read
+// registers only), so the MFMA pipe stays busy while the waves meet.
+constexpr int kPreBarrierRows = 2;
+
+// One fragment read of A: row block r of k step KK in buffer BUF.
+template <int BUF, int KK>
+__device__ __forceinline__ i32x4 read_a1(int lane, int r) {
+    const i32x4* buf = ring<BUF>();
+    const int l32 = lane & 31, half = lane >> 5;
+    return buf[(r * 32 + l32) * 4 + ((KK * 2 + half) ^ swz_of_row(l32))];
+}
+
+__device__ __forceinline__ void mma1(const i32x4& a, const i32x4& b0i, const i32x4& b1i, f32x16& c0, f32x16& c1) {
+    const bf16x8 av = __builtin_bit_cast(bf16x8, a);
+    c0 = mfma32x32x16(av, __builtin_bit_cast(bf16x8, b0i), c0);
+    c1 = mfma32x32x16(av, __builtin_bit_cast(bf16x8, b1i), c1);
+}
+
+// A load of stage t into buffer BUF, one instruction (i of kLoadsA).
+template <int BUF>
+__device__ __forceinline__ void dma_a1(const Dma& d, int t, int lane, int i) {
+    i32x4* buf = ring<BUF>();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const bool real = t < d.nsteps;
+    const bool last = t == d.nsteps - 1;
+    const uint32_t logical8 = (uint32_t)(((lane & 3) ^ swz_of_row(lane >> 2)) * 8);
+    const bool a_ok = real & (!d.a_rm | !last | (logical8 < d.kvalid_last));  // no short-circuit branch
+    const uint32_t off = a_ok ? d.va[i] + (uint32_t)t * d.sa : kOOB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ra, (lds_t)(buf + (wave * 4 + i) * 64), 16, off, 0, 0, 0);
+}
+
 // One pipeline stage (two 16-wide k steps) on stage s, A in buffer BUF, B in
 // register set BUF.  A set kk holds k step kk; entering, set 0 holds stage s,
-// k step 0.
+// k step 0.  Memory instructions are spread between the MFMAs (one pair of
+// MFMAs, then a fragment read or an A load), and the first row blocks of k
+// step 1 go ahead of the barrier, so the MFMA pipe is never left without
+// work behind a cluster of issues.
 template <int MODE, int NRB, int BUF>
 __device__ __forceinline__ void stage(const Dma& d, int s, int lane, i32x4 (&fa)[2][NRB], i32x4 (&bq)[NS][4],
                                       f32x16 (&acc0)[8], f32x16 (&acc1)[8]) {
+#if MOE_GEMM_INTERLEAVE
+    constexpr int PRE = NRB < kPreBarrierRows ? NRB : kPreBarrierRows;
+    // k step 0 on set 0, reading k step 1 of this stage into set 1
+#pragma unroll
+    for (int r = 0; r < NRB; ++r) {
+        mma1(fa[0][r], bq[BUF][0], bq[BUF][2], acc0[r], acc1[r]);
+        __builtin_amdgcn_sched_barrier(0);
+        fa[1][r] = read_a1<BUF, 1>(lane, r);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // k step 1, first row blocks: registers only
+#pragma unroll
+    for (int r = 0; r < PRE; ++r) {
+        mma1(fa[1][r], bq[BUF][1], bq[BUF][3], acc0[r], acc1[r]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_lgkm0();             // every read of buffer BUF by this wave has returned
+    wait_vm<kWaitNextA>();    // this wave's A loads of stage s+1 have landed
+    barrier_lds();            // ... everybody's have, and everybody is done with buffer BUF
+    // the rest of k step 1, with the A loads NS ahead into buffer BUF and the
+    // reads of stage s+1's k step 0 in between
+    int issued_dma = 0, issued_rd = 0;
+#pragma unroll
+    for (int r = PRE; r < NRB; ++r) {
+        mma1(fa[1][r], bq[BUF][1], bq[BUF][3], acc0[r], acc1[r]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (issued_dma < kLoadsA) {
+            dma_a1<BUF>(d, s + NS, lane, issued_dma);
+            ++issued_dma;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (issued_rd < NRB) {
+            fa[0][issued_rd] = read_a1<(BUF + 1) % NS, 0>(lane, issued_rd);
+            ++issued_rd;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kLoadsA; ++i)
+        if (i >= issued_dma) dma_a1<BUF>(d, s + NS, lane, i);
+#pragma unroll
+    for (int r = 0; r < NRB; ++r)
+        if (r >= issued_rd) fa[0][r] = read_a1<(BUF + 1) % NS, 0>(lane, r);
+    __builtin_amdgcn_sched_barrier(0);
+    load_b(d, s + NS, bq[BUF]);  // register set BUF is free once its MFMAs have issued
+    __builtin_amdgcn_sched_barrier(0);
+#else
     // k step 0: read k step 1 of this stage while the MFMAs of k step 0 run
     wait_lgkm0();
     read_a<NRB, BUF, 1>(lane, fa[1]);
@@ -255,6 +339,7 @@ __device__ __forceinline__ void stage(const Dma& d, int s, int lane, i32x4 (&fa)
     __builtin_amdgcn_sched_barrier(0);
     load_b(d, s + NS, bq[BUF]);  // register set BUF is free once its MFMAs have issued
     __builtin_amdgcn_sched_barrier(0);
+#endif
 }
 
 template <int MODE, int NRB>
