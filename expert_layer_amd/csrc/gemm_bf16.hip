@@ -47,11 +47,19 @@ namespace moe {
 namespace {
 
 constexpr int BM = 256, BN = 256, BK = 32, NTH = 256;
-#ifndef MOE_GEMM_STAGES
-#define MOE_GEMM_STAGES 6
+#ifndef MOE_GEMM1_STAGES
+#define MOE_GEMM1_STAGES 8
 #endif
-constexpr int NS = MOE_GEMM_STAGES;      // stages in flight (A: LDS buffers, B: register sets)
-static_assert(NS >= 3 && NS <= 8, "the vmcnt arithmetic below holds for 3 to 8 stages");
+#ifndef MOE_GEMM2_STAGES
+#define MOE_GEMM2_STAGES 4
+#endif
+// Stages in flight (A: LDS buffers, B: register sets), per GEMM: the longer K
+// of GEMM1 takes a deeper ring, GEMM2's 64 stages per tile a shorter fill
+// (both measured at c3).
+template <int MODE>
+constexpr int kStages = MODE == 0 ? MOE_GEMM1_STAGES : MOE_GEMM2_STAGES;
+static_assert(kStages<0> >= 3 && kStages<0> <= 8 && kStages<1> >= 3 && kStages<1> <= 8,
+              "the vmcnt arithmetic below holds for 3 to 8 stages");
 constexpr int kSlots = BM * 4;           // 16-byte slots of the A operand in one stage
 constexpr int kLoadsA = 4, kLoadsB = 4;  // vector-memory instructions per wave per stage
 constexpr uint32_t kOOB = 0x80000000u;   // past every descriptor (all are < 2 GiB): the load returns zero
@@ -72,7 +80,7 @@ __shared__ i32x4 ring7[kSlots];
 
 template <int BUF>
 __device__ __forceinline__ i32x4* ring() {
-    static_assert(BUF < NS, "ring buffer index");
+    static_assert(BUF < 8, "ring buffer index");
     if constexpr (BUF == 0) return ring0;
     else if constexpr (BUF == 1) return ring1;
     else if constexpr (BUF == 2) return ring2;
@@ -227,17 +235,26 @@ __device__ __forceinline__ void mma(const i32x4 (&a)[NRB], const i32x4& b0i, con
 // vmcnt after which this wave's A loads of the next stage have landed: the
 // loads issued after them are that stage's B loads and the A and B loads of
 // the NS - 2 stages after it.
+template <int NS>
 constexpr int kWaitNextA = kLoadsB + (kLoadsA + kLoadsB) * (NS - 2);
 // ... and, in the prologue, stage 0's A loads: every later load of NS stages.
+template <int NS>
 constexpr int kWaitFirstA = kLoadsB + (kLoadsA + kLoadsB) * (NS - 1);
-static_assert(kWaitFirstA < 64, "vmcnt is 6 bits");
+static_assert(kWaitFirstA<8> < 64, "vmcnt is 6 bits");
 
 #ifndef MOE_GEMM_INTERLEAVE
 #define MOE_GEMM_INTERLEAVE 1
 #endif
 // MFMA row blocks of k step 1 issued before the stage's barrier (they read
 // registers only), so the MFMA pipe stays busy while the waves meet.
-constexpr int kPreBarrierRows = 2;
+#ifndef MOE_GEMM1_PRE_ROWS
+#define MOE_GEMM1_PRE_ROWS 1
+#endif
+#ifndef MOE_GEMM2_PRE_ROWS
+#define MOE_GEMM2_PRE_ROWS 2
+#endif
+template <int MODE>
+constexpr int kPreBarrierRows = MODE == 0 ? MOE_GEMM1_PRE_ROWS : MOE_GEMM2_PRE_ROWS;
 
 // One fragment read of A: row block r of k step KK in buffer BUF.
 template <int BUF, int KK>
@@ -273,10 +290,11 @@ __device__ __forceinline__ void dma_a1(const Dma& d, int t, int lane, int i) {
 // step 1 go ahead of the barrier, so the MFMA pipe is never left without
 // work behind a cluster of issues.
 template <int MODE, int NRB, int BUF>
-__device__ __forceinline__ void stage(const Dma& d, int s, int lane, i32x4 (&fa)[2][NRB], i32x4 (&bq)[NS][4],
-                                      f32x16 (&acc0)[8], f32x16 (&acc1)[8]) {
+__device__ __forceinline__ void stage(const Dma& d, int s, int lane, i32x4 (&fa)[2][NRB],
+                                      i32x4 (&bq)[kStages<MODE>][4], f32x16 (&acc0)[8], f32x16 (&acc1)[8]) {
+    constexpr int NS = kStages<MODE>;
 #if MOE_GEMM_INTERLEAVE
-    constexpr int PRE = NRB < kPreBarrierRows ? NRB : kPreBarrierRows;
+    constexpr int PRE = NRB < kPreBarrierRows<MODE> ? NRB : kPreBarrierRows<MODE>;
     // k step 0 on set 0, reading k step 1 of this stage into set 1
 #pragma unroll
     for (int r = 0; r < NRB; ++r) {
@@ -292,7 +310,7 @@ __device__ __forceinline__ void stage(const Dma& d, int s, int lane, i32x4 (&fa)
         __builtin_amdgcn_sched_barrier(0);
     }
     wait_lgkm0();             // every read of buffer BUF by this wave has returned
-    wait_vm<kWaitNextA>();    // this wave's A loads of stage s+1 have landed
+    wait_vm<kWaitNextA<NS>>();    // this wave's A loads of stage s+1 have landed
     barrier_lds();            // ... everybody's have, and everybody is done with buffer BUF
     // the rest of k step 1, with the A loads NS ahead into buffer BUF and the
     // reads of stage s+1's k step 0 in between
@@ -330,7 +348,7 @@ __device__ __forceinline__ void stage(const Dma& d, int s, int lane, i32x4 (&fa)
     __builtin_amdgcn_sched_barrier(0);
     // k step 1: hand A buffer BUF back to the DMA and start on stage s+1
     wait_lgkm0();             // every read of buffer BUF by this wave has returned
-    wait_vm<kWaitNextA>();    // this wave's A loads of stage s+1 have landed
+    wait_vm<kWaitNextA<NS>>();    // this wave's A loads of stage s+1 have landed
     barrier_lds();            // ... everybody's have, and everybody is done with buffer BUF
     dma_a<BUF>(d, s + NS, lane);
     read_a<NRB, (BUF + 1) % NS, 0>(lane, fa[0]);
@@ -429,6 +447,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, int mt, int g, int r
         acc1[i] = f32x16{};
     }
     i32x4 fa[2][NRB];
+    constexpr int NS = kStages<MODE>;
     i32x4 bq[NS][4];
 
     static_for<0, NS>([&](auto c) {
@@ -436,7 +455,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, int mt, int g, int r
         dma_a<t>(d, t, lane);
         load_b(d, t, bq[t]);
     });
-    wait_vm<kWaitFirstA>();
+    wait_vm<kWaitFirstA<NS>>();
     barrier_lds();
     read_a<NRB, 0, 0>(lane, fa[0]);
     // stages past the end load zeros, so the loop runs in whole turns of the ring
