@@ -175,21 +175,25 @@ struct Dma {
     bool a_rm;              // row-major A: the K tail must be masked
 };
 
+// A load of stage t into buffer BUF, one instruction (i of kLoadsA): row-major
+// chunks of the K tail load zero (tiled operands are zero padded).
 template <int BUF>
-__device__ __forceinline__ void dma_a(const Dma& d, int t, int lane) {
+__device__ __forceinline__ void dma_a1(const Dma& d, int t, int lane, int i) {
     i32x4* buf = ring<BUF>();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const bool real = t < d.nsteps;
     const bool last = t == d.nsteps - 1;
-    // row-major chunks of the K tail load zero (tiled operands are zero padded)
     const uint32_t logical8 = (uint32_t)(((lane & 3) ^ swz_of_row(lane >> 2)) * 8);
-    const bool a_ok = real && (!d.a_rm || !last || logical8 < d.kvalid_last);
-    const uint32_t ka = (uint32_t)t * d.sa;
+    const bool a_ok = real & (!d.a_rm | !last | (logical8 < d.kvalid_last));  // no short-circuit branch
+    const uint32_t off = a_ok ? d.va[i] + (uint32_t)t * d.sa : kOOB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ra, (lds_t)(buf + (wave * 4 + i) * 64), 16, off, 0, 0, 0);
+}
+
+// All A loads of stage t into buffer BUF.
+template <int BUF>
+__device__ __forceinline__ void dma_a(const Dma& d, int t, int lane) {
 #pragma unroll
-    for (int i = 0; i < kLoadsA; ++i) {
-        const uint32_t off = a_ok ? d.va[i] + ka : kOOB;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ra, (lds_t)(buf + (wave * 4 + i) * 64), 16, off, 0, 0, 0);
-    }
+    for (int i = 0; i < kLoadsA; ++i) dma_a1<BUF>(d, t, lane, i);
 }
 
 // B fragments of stage t: q[2 c + kk] = 32-row half c, k step kk.  A load is
@@ -219,19 +223,6 @@ __device__ __forceinline__ void read_a(int lane, i32x4 (&a)[NRB]) {
     for (int r = 0; r < NRB; ++r) a[r] = buf[(r * 32 + l32) * 4 + phys];
 }
 
-template <int NRB>
-__device__ __forceinline__ void mma(const i32x4 (&a)[NRB], const i32x4& b0i, const i32x4& b1i, f32x16 (&acc0)[8],
-                                    f32x16 (&acc1)[8]) {
-    const bf16x8 b0 = __builtin_bit_cast(bf16x8, b0i);
-    const bf16x8 b1 = __builtin_bit_cast(bf16x8, b1i);
-#pragma unroll
-    for (int r = 0; r < NRB; ++r) {
-        const bf16x8 av = __builtin_bit_cast(bf16x8, a[r]);
-        acc0[r] = mfma32x32x16(av, b0, acc0[r]);
-        acc1[r] = mfma32x32x16(av, b1, acc1[r]);
-    }
-}
-
 // vmcnt after which this wave's A loads of the next stage have landed: the
 // loads issued after them are that stage's B loads and the A and B loads of
 // the NS - 2 stages after it.
@@ -242,9 +233,6 @@ template <int NS>
 constexpr int kWaitFirstA = kLoadsB + (kLoadsA + kLoadsB) * (NS - 1);
 static_assert(kWaitFirstA<8> < 64, "vmcnt is 6 bits");
 
-#ifndef MOE_GEMM_INTERLEAVE
-#define MOE_GEMM_INTERLEAVE 1
-#endif
 // MFMA row blocks of k step 1 issued before the stage's barrier (they read
 // registers only), so the MFMA pipe stays busy while the waves meet.
 #ifndef MOE_GEMM1_PRE_ROWS
@@ -270,19 +258,6 @@ __device__ __forceinline__ void mma1(const i32x4& a, const i32x4& b0i, const i32
     c1 = mfma32x32x16(av, __builtin_bit_cast(bf16x8, b1i), c1);
 }
 
-// A load of stage t into buffer BUF, one instruction (i of kLoadsA).
-template <int BUF>
-__device__ __forceinline__ void dma_a1(const Dma& d, int t, int lane, int i) {
-    i32x4* buf = ring<BUF>();
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const bool real = t < d.nsteps;
-    const bool last = t == d.nsteps - 1;
-    const uint32_t logical8 = (uint32_t)(((lane & 3) ^ swz_of_row(lane >> 2)) * 8);
-    const bool a_ok = real & (!d.a_rm | !last | (logical8 < d.kvalid_last));  // no short-circuit branch
-    const uint32_t off = a_ok ? d.va[i] + (uint32_t)t * d.sa : kOOB;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ra, (lds_t)(buf + (wave * 4 + i) * 64), 16, off, 0, 0, 0);
-}
-
 // One pipeline stage (two 16-wide k steps) on stage s, A in buffer BUF, B in
 // register set BUF.  A set kk holds k step kk; entering, set 0 holds stage s,
 // k step 0.  Memory instructions are spread between the MFMAs (one pair of
@@ -293,7 +268,6 @@ template <int MODE, int NRB, int BUF>
 __device__ __forceinline__ void stage(const Dma& d, int s, int lane, i32x4 (&fa)[2][NRB],
                                       i32x4 (&bq)[kStages<MODE>][4], f32x16 (&acc0)[8], f32x16 (&acc1)[8]) {
     constexpr int NS = kStages<MODE>;
-#if MOE_GEMM_INTERLEAVE
     constexpr int PRE = NRB < kPreBarrierRows<MODE> ? NRB : kPreBarrierRows<MODE>;
     // k step 0 on set 0, reading k step 1 of this stage into set 1
 #pragma unroll
@@ -339,25 +313,6 @@ __device__ __forceinline__ void stage(const Dma& d, int s, int lane, i32x4 (&fa)
     __builtin_amdgcn_sched_barrier(0);
     load_b(d, s + NS, bq[BUF]);  // register set BUF is free once its MFMAs have issued
     __builtin_amdgcn_sched_barrier(0);
-#else
-    // k step 0: read k step 1 of this stage while the MFMAs of k step 0 run
-    wait_lgkm0();
-    read_a<NRB, BUF, 1>(lane, fa[1]);
-    __builtin_amdgcn_sched_barrier(0);
-    mma<NRB>(fa[0], bq[BUF][0], bq[BUF][2], acc0, acc1);
-    __builtin_amdgcn_sched_barrier(0);
-    // k step 1: hand A buffer BUF back to the DMA and start on stage s+1
-    wait_lgkm0();             // every read of buffer BUF by this wave has returned
-    wait_vm<kWaitNextA<NS>>();    // this wave's A loads of stage s+1 have landed
-    barrier_lds();            // ... everybody's have, and everybody is done with buffer BUF
-    dma_a<BUF>(d, s + NS, lane);
-    read_a<NRB, (BUF + 1) % NS, 0>(lane, fa[0]);
-    __builtin_amdgcn_sched_barrier(0);
-    mma<NRB>(fa[1], bq[BUF][1], bq[BUF][3], acc0, acc1);
-    __builtin_amdgcn_sched_barrier(0);
-    load_b(d, s + NS, bq[BUF]);  // register set BUF is free once its MFMAs have issued
-    __builtin_amdgcn_sched_barrier(0);
-#endif
 }
 
 template <int MODE, int NRB>
