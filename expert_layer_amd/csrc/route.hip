@@ -88,7 +88,7 @@ __device__ __forceinline__ void rstage(int wave, int lane, f32x16 (&acc)[4][2]) 
         }
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            const int row = wave * 64 + c * 32 + l32;
+            const int row = (wave & 3) * 64 + c * 32 + l32;  // provably inside the buffer
             b[c] = buf[kRA + row * 4 + (chunk ^ tile_swz(row))];
         }
 #pragma unroll
@@ -142,21 +142,23 @@ router_logits_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
 #pragma unroll
         for (int c = 0; c < 2; ++c) acc[r][c] = f32x16{};
 
+    // Stages 0..2 in flight; at stage s (buffer s % 4): wait until its loads
+    // have landed (the 12 loads of stages s+1, s+2 may still fly), one barrier
+    // -- everyone's stage s has landed and everyone is done with stage s-1 --
+    // refill stage s-1's buffer with stage s+3, then compute on stage s.
     rdma<0>(d, 0, wave);
     rdma<1>(d, 1, wave);
     rdma<2>(d, 2, wave);
-    rdma<3>(d, 3, wave);
     const int nturns = (d.nsteps + RB_NST - 1) / RB_NST;
     for (int s = 0; s < nturns * RB_NST; s += RB_NST) {
-        // stage s + j landed (the next three may be in flight: 18 loads), then
-        // compute on it and hand the buffer back to stage s + j + 4
 #define ROUTER_STAGE(J)                                              \
-        __builtin_amdgcn_s_waitcnt((18 & 15) | ((18 >> 4) << 14) | 0x0F70); \
+        __builtin_amdgcn_s_waitcnt((12 & 15) | ((12 >> 4) << 14) | 0x0070); \
         rbarrier();                                                  \
+        __builtin_amdgcn_sched_barrier(0);                           \
+        rdma<(J + 3) % RB_NST>(d, s + J + 3, wave);                  \
+        __builtin_amdgcn_sched_barrier(0);                           \
         rstage<J>(wave, lane, acc);                                  \
-        __builtin_amdgcn_s_waitcnt(0xC07F);                          \
-        rbarrier();                                                  \
-        rdma<J>(d, s + J + RB_NST, wave);
+        __builtin_amdgcn_sched_barrier(0);
         ROUTER_STAGE(0)
         ROUTER_STAGE(1)
         ROUTER_STAGE(2)
