@@ -468,6 +468,9 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, int mt, int g, int r
                 st[row * 64 + lane] = acc0[r][i];
                 st[row * 64 + (lane ^ 32)] = acc1[r][i];
             }
+            // the staged values are read by other lanes of this wave: keep the
+            // compiler from moving the reads above the writes (no wait is needed)
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 #pragma unroll
             for (int it = 0; it < 8; ++it) {
                 const int q = it * 64 + lane;  // chunk q: row q / 16, columns 4 (q % 16) .. + 3
@@ -485,6 +488,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, int mt, int g, int r
                     }
                 }
             }
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");  // reads before the next block's writes
         }
     }
 }

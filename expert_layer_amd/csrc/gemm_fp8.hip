@@ -15,9 +15,11 @@
 // them in VALU registers, so a wave cannot hold more).  GEMM1: the 64 weight
 // rows of a wave are 32 gate rows then the 32 up rows of the same h columns, so
 // h = silu(g) * u forms in registers; GEMM2: 64 output columns.
-// Pipeline.  K advances in stages of 128 through two LDS buffers of [A 256 x
-// 128 B | B 256 x 128 B | 256 row scales]; operands move HBM -> LDS by
-// buffer_load ... lds, one stage ahead.  Chunks outside the tile (rows past the
+// Pipeline.  K advances in stages of 128 through two A buffers [256 x 128 B |
+// 256 row scales] and two B buffers [256 x 128 B]; operands move HBM -> LDS by
+// buffer_load ... lds.  A wave reads all its B fragments of a stage first, so
+// B of stage s+2 is issued as soon as every wave has them (almost two stages
+// ahead of use) and A of stage s+1 at the start of stage s (one stage ahead).  Chunks outside the tile (rows past the
 // group's end, weight rows past N) carry an offset beyond their buffer
 // descriptor and load as zero.  LDS chunks of 16 B are XOR-swizzled by
 // (row >> 1) & 7, so a fragment read of 16 rows at one logical chunk touches
@@ -32,18 +34,25 @@ namespace {
 
 constexpr int BM = 256, BN = 256, BK = 128, NTH = 512;
 constexpr int kChunks = 256 * 8;               // 16-byte chunks of one operand in one stage
-constexpr int kStage = 2 * kChunks + 128;      // A, B, 256 fp32 row scales, a 1 KiB sink
+constexpr int kStageA = kChunks + 128;         // A, 256 fp32 row scales, a 1 KiB sink
 constexpr uint32_t kOOB = 0x40000000u;         // past every descriptor: the load returns zero
 
 typedef __attribute__((address_space(3))) void* lds_t;
 
-__shared__ i32x4 stg0[kStage];
-__shared__ i32x4 stg1[kStage];
+__shared__ i32x4 stgA0[kStageA];
+__shared__ i32x4 stgA1[kStageA];
+__shared__ i32x4 stgB0[kChunks];
+__shared__ i32x4 stgB1[kChunks];
 
 template <int BUF>
-__device__ __forceinline__ i32x4* stg() {
-    if constexpr (BUF == 0) return stg0;
-    else return stg1;
+__device__ __forceinline__ i32x4* stgA() {
+    if constexpr (BUF == 0) return stgA0;
+    else return stgA1;
+}
+template <int BUF>
+__device__ __forceinline__ i32x4* stgB() {
+    if constexpr (BUF == 0) return stgB0;
+    else return stgB1;
 }
 
 __device__ __forceinline__ void barrier_lds() { asm volatile("s_barrier" ::: "memory"); }
@@ -83,13 +92,13 @@ struct Dma {
     int nsteps;  // K blocks
 };
 
-// Issue the loads of stage t into buffer BUF: 4 A and 4 B chunk loads per
-// lane (8 LDS rows each) and one row-scale load: waves 0..3 load the scales of
-// 64 rows each, waves 4..7 an out-of-range (zero) load into the sink, so every
-// wave has the same 9 loads in flight per stage and one vmcnt covers all.
-template <int MODE, int BUF>
-__device__ __forceinline__ void dma_stage(const Dma& d, int t, int wave) {
-    i32x4* buf = stg<BUF>();
+// A loads of stage t into A buffer BUF: 4 chunk loads per lane (8 LDS rows
+// each) and one row-scale load -- waves 0..3 load the scales of 64 rows each,
+// waves 4..7 an out-of-range (zero) load into the sink, so every wave has the
+// same 5 A loads per stage.
+template <int BUF>
+__device__ __forceinline__ void dma_a(const Dma& d, int t, int wave) {
+    i32x4* buf = stgA<BUF>();
     const uint32_t k = (uint32_t)t * BK;
     const bool real = t < d.nsteps;  // stages past the end load zeros
 #pragma unroll
@@ -97,22 +106,30 @@ __device__ __forceinline__ void dma_stage(const Dma& d, int t, int wave) {
         const uint32_t off = (!real || d.va[i] == kOOB) ? kOOB : d.va[i] + k;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ra, (lds_t)(buf + (wave * 4 + i) * 64), 16, off, 0, 0, 0);
     }
+    const uint32_t so = (!real || d.vs == kOOB) ? kOOB : d.vs + (uint32_t)t * 4u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rs, (lds_t)(buf + kChunks + wave * 16), 4, so, 0, 0, 0);
+}
+
+// B loads of stage t into B buffer BUF: 4 chunk loads per lane.
+template <int MODE, int BUF>
+__device__ __forceinline__ void dma_b(const Dma& d, int t, int wave) {
+    i32x4* buf = stgB<BUF>();
+    const uint32_t k = (uint32_t)t * BK;
+    const bool real = t < d.nsteps;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const uint32_t off = (!real || d.vb[i] == kOOB) ? kOOB : d.vb[i] + k;
         // GEMM1: wave w fills LDS rows 32 w + [0, 32): gate rows of quarter w / 2
         // on even waves, up rows on odd waves
         const __amdgpu_buffer_rsrc_t r = (MODE == 0 && (wave & 1)) ? d.rb1 : d.rb0;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_t)(buf + kChunks + (wave * 4 + i) * 64), 16, off, 0, 0,
-                                                 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_t)(buf + (wave * 4 + i) * 64), 16, off, 0, 0, 0);
     }
-    const uint32_t so = (!real || d.vs == kOOB) ? kOOB : d.vs + (uint32_t)t * 4u;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rs, (lds_t)(buf + 2 * kChunks + wave * 16), 4, so, 0, 0, 0);
 }
 
-// vmcnt(9) with the other counters left alone: the 9 loads of the newest stage
-// may still be in flight.
-__device__ __forceinline__ void wait_prev_stage() { __builtin_amdgcn_s_waitcnt(9 | 0x0F70); }
+// vmcnt(4) with the other counters at zero: a stage's A loads and everything
+// before them have landed (the 4 B loads issued after them may be in flight),
+// and every LDS read of this wave has returned.
+__device__ __forceinline__ void wait_stage() { __builtin_amdgcn_s_waitcnt(4 | 0x0070); }
 
 __device__ __forceinline__ i32x8 cat(i32x4 lo, i32x4 hi) {
     return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -130,29 +147,38 @@ __device__ __forceinline__ void promote(const f32x4 (&t)[4], const f32x4& sa, fl
     }
 }
 
+// The B fragments of this wave (column blocks of 16 rows of weight rows
+// q * 64 ..) in stage buffer BUF.  A lane reads row (16 i + lane % 16) at
+// logical chunks 2 (lane / 16) and 2 (lane / 16) + 1; the swizzle of a row
+// depends on row % 16 only, so every fragment address is one of two per-lane
+// bases plus a constant.
+template <int BUF>
+__device__ __forceinline__ void read_b(int q, int lane, i32x8 (&b)[4]) {
+    const i32x4* buf = stgB<BUF>();
+    const int l16 = lane & 15;
+    const int plo = (2 * (lane >> 4)) ^ swz8(l16), phi = plo ^ 1;
+    const int ib = ((q & 3) * 64 + l16) * 8;  // column block cb: + cb * 128
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) b[cb] = cat(buf[ib + cb * 128 + plo], buf[ib + cb * 128 + phi]);
+}
+
 // One K stage for the 8 row blocks of 16 starting at tile row r0: every (row
 // block, column block) MFMA of this wave, promoted with the stage's row scales
 // and the wave's weight-block scales p0 (gate or down columns) and p1 (up
 // columns).  Software-pipelined over row blocks: while the four MFMAs of row
 // block rb run, the fragments of rb + 1 are read and rb - 1 is promoted.
-// A lane reads row (16 i + lane % 16) at logical chunks 2 (lane / 16) and
-// 2 (lane / 16) + 1; the swizzle of a row depends on row % 16 only, so every
-// fragment address is one of two per-lane bases plus a constant.
 template <int BUF>
-__device__ __forceinline__ void kstep(int r0, int q, int lane, float p0, float p1, f32x4 (&acc)[8][4]) {
+__device__ __forceinline__ void kstep(int r0, int lane, const i32x8 (&b)[4], float p0, float p1,
+                                      f32x4 (&acc)[8][4]) {
     constexpr int RB = 8;
     // Every access indexes the stage buffer itself (an integer base plus a
     // constant), so the compiler can tell it from the DMA in flight into the
-    // other buffer and adds no wait for it.
-    const i32x4* buf = stg<BUF>();
+    // other buffers and adds no wait for it.
+    const i32x4* buf = stgA<BUF>();
     const int l16 = lane & 15;
     const int plo = (2 * (lane >> 4)) ^ swz8(l16), phi = plo ^ 1;
-    const int ia = (r0 + l16) * 8;                 // row block rb: + rb * 128
-    const int ib = kChunks + (q * 64 + l16) * 8;   // column block cb: + cb * 128
-    const int is = 2 * kChunks + r0 / 4 + (lane >> 4);  // row block rb: + rb * 4
-    i32x8 b[4];
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) b[cb] = cat(buf[ib + cb * 128 + plo], buf[ib + cb * 128 + phi]);
+    const int ia = ((r0 & 128) + l16) * 8;              // row block rb: + rb * 128
+    const int is = kChunks + (r0 & 128) / 4 + (lane >> 4);  // row block rb: + rb * 4
     i32x8 a[2];
     f32x4 sa[3];
     f32x4 t[2][4];
@@ -248,25 +274,33 @@ __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int 
 
     // The loop runs whole pairs of stages and always issues the next loads
     // (zeros past the end; an odd last stage computes on zeros with zero
-    // scales), so the wait before a stage is always vmcnt(9).
-    dma_stage<MODE, 0>(d, 0, wave);
-    dma_stage<MODE, 1>(d, 1, wave);
+    // scales).  Per stage, in issue order: A of stage s+1 (5 loads), then B of
+    // stage s+2 (4 loads), so at the start of a stage vmcnt(4) covers its A and
+    // B.  Prologue: B0, A0, B1.
+    dma_b<MODE, 0>(d, 0, wave);
+    dma_a<0>(d, 0, wave);
+    dma_b<MODE, 1>(d, 1, wave);
+    i32x8 b[4];
     for (int s = 0; s < KB; s += 2) {
         float p0, p1;
         wscale(s, p0, p1);
-        wait_prev_stage();  // stage s (buffer 0) has landed; s + 1 may be in flight
-        barrier_lds();
-        if (r0 < M) kstep<0>(r0, q, lane, p0, p1, acc);
+        wait_stage();       // stage s (buffers 0) has landed; this wave's reads of stage s-1 are done
+        barrier_lds();      // ... everybody's: the buffers 1 are free
+        dma_a<1>(d, s + 1, wave);
+        read_b<0>(q, lane, b);
         wait_lgkm0();
-        barrier_lds();      // every wave is done with buffer 0
-        dma_stage<MODE, 0>(d, s + 2, wave);
+        barrier_lds();      // every wave holds its B fragments of stage s
+        dma_b<MODE, 0>(d, s + 2, wave);
+        if (r0 < M) kstep<0>(r0, lane, b, p0, p1, acc);
         wscale(s + 1, p0, p1);
-        wait_prev_stage();
+        wait_stage();
         barrier_lds();
-        if (r0 < M) kstep<1>(r0, q, lane, p0, p1, acc);
+        dma_a<0>(d, s + 2, wave);
+        read_b<1>(q, lane, b);
         wait_lgkm0();
         barrier_lds();
-        dma_stage<MODE, 1>(d, s + 3, wave);
+        dma_b<MODE, 1>(d, s + 3, wave);
+        if (r0 < M) kstep<1>(r0, lane, b, p0, p1, acc);
     }
     wait_vm0();  // no LDS DMA may outlive the workgroup
     barrier_lds();
@@ -289,14 +323,14 @@ __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int 
                 rmax[rb][j] = m;
             }
         // per-row maxima of the four quarters' 32 columns -> LDS [4][256]
-        float* red = reinterpret_cast<float*>(stg0);
+        float* red = reinterpret_cast<float*>(stgA0);
         if (l16 == 0)
 #pragma unroll
             for (int rb = 0; rb < 8; ++rb)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) red[q * 256 + r0 + rb * 16 + rq + j] = rmax[rb][j];
         __syncthreads();
-        uint8_t* qs = reinterpret_cast<uint8_t*>(stg1);  // [256 rows][128 columns] e4m3
+        uint8_t* qs = reinterpret_cast<uint8_t*>(stgB0);  // [256 rows][128 columns] e4m3
         const int qc = q * 32 + l16;
 #pragma unroll
         for (int rb = 0; rb < 8; ++rb)
@@ -318,25 +352,45 @@ __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int 
             *reinterpret_cast<i32x4*>(h + (size_t)(row0 + row) * N + n0 + ch * 16) = qv[c];
         }
     } else {
-        const int col = n0 + q * 64 + l16;
+        // y through LDS, 16 rows at a time: each wave stages its 16 x 64 block
+        // (fp32, 4 KiB of B buffer 0) with the 16-column groups of a row
+        // XOR-ed by bits 2..3 of the row, so the four row groups of a store
+        // instruction and the 16 lanes of a row's read touch distinct banks;
+        // then every lane stores 4 columns (8 B bf16 / 16 B fp32).  LDS
+        // operations of one wave are processed in order.
+        float* st = reinterpret_cast<float*>(stgB0 + wave * 256);
+        const int cw = n0 + q * 64;  // first output column of this wave
 #pragma unroll
-        for (int rb = 0; rb < 8; ++rb)
+        for (int rb = 0; rb < 8; ++rb) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int row = r0 + rb * 16 + rq + j;
-                if (row < M) {
-                    const size_t o = (size_t)(row0 + row) * N + col;
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
-                    for (int cb = 0; cb < 4; ++cb) {
-                        if (col + cb * 16 < N) {
-                            if (p.out_f32)
-                                static_cast<float*>(p.out)[o + cb * 16] = acc[rb][cb][j];
-                            else
-                                static_cast<uint16_t*>(p.out)[o + cb * 16] = f32_to_bf16(acc[rb][cb][j]);
-                        }
+                for (int cb = 0; cb < 4; ++cb) {
+                    const int row = rq + j;  // bits 2..3 of row are lane / 16
+                    st[row * 64 + ((cb * 16 + l16) ^ (((row >> 2) & 3) << 4))] = acc[rb][cb][j];
+                }
+            // the staged values are read by other lanes of this wave: keep the
+            // compiler from moving the reads above the writes (no wait is needed)
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                const int qq = it * 64 + lane;  // chunk qq: row qq / 16, columns 4 (qq % 16) .. + 3
+                const int row = qq >> 4, c4 = (qq & 15) * 4;
+                const f32x4 v = *reinterpret_cast<const f32x4*>(st + row * 64 + (c4 ^ (((row >> 2) & 3) << 4)));
+                const int grow = r0 + rb * 16 + row, col = cw + c4;
+                if (grow < M && col < N) {
+                    const size_t o = (size_t)(row0 + grow) * N + col;
+                    if (p.out_f32) {
+                        *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + o) = v;
+                    } else {
+                        const uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+                        const uint32_t hi = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+                        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + o) = make_uint2(lo, hi);
                     }
                 }
             }
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");  // reads before the next block's writes
+        }
     }
 }
 
