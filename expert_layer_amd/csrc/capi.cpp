@@ -119,7 +119,10 @@ struct Carve {
     }
 };
 
-int ffn_bm(const moe_cfg& c) { return c.act_dtype == MOE_F32 ? moe::kFfnBmF32 : moe::kFfnBmBf16; }
+int ffn_bm(const moe_cfg& c) {
+    if (c.act_dtype == MOE_F32) return moe::kFfnBmF32;
+    return c.act_dtype == MOE_FP8_E4M3 ? moe::kFfnBmFp8 : moe::kFfnBmBf16;
+}
 
 int64_t ffn_max_tiles(const moe_cfg& c, int64_t n_rows_cap) {
     const int bm = ffn_bm(c);

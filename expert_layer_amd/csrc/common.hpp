@@ -142,9 +142,11 @@ hipError_t launch_permute(const moe_cfg& c, const void* x, const float* x_scale,
                           void* x_perm, float* x_perm_scale, int64_t max_rows, PermuteWs ws,
                           PermuteLayout lay, hipStream_t s);
 
-// Grouped FFN building blocks (gemm_bf16.hip, gemm_f32.hip).  Tile heights
-// (rows) and the h / output columns one tile covers in GEMM1 / GEMM2.
+// Grouped FFN building blocks (gemm_bf16.hip, gemm_fp8.hip, gemm_f32.hip).
+// Tile heights (rows) and the h / output columns one tile covers in GEMM1 /
+// GEMM2; fp8 tiles cover the bf16 tiles' columns.
 constexpr int kFfnBmBf16 = 256, kFfnN1Bf16 = 128, kFfnN2Bf16 = 256;
+constexpr int kFfnBmFp8 = 224;
 constexpr int kFfnBmF32 = 64, kFfnN1F32 = 64, kFfnN2F32 = 64;
 
 // Device work lists of the grouped FFN, carved from the workspace.

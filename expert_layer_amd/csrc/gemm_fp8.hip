@@ -9,21 +9,23 @@
 // folded in as acc += t * (s_row * s_weight) on the VALU.  The MFMAs write VGPRs
 // (this file is compiled in the VGPR form), so the promotion reads t directly.
 //
-// Tile.  256 rows x 256 weight rows, 8 waves (two per SIMD); wave w owns rows
-// 128 (w / 4) + [0, 128) and weight rows 64 (w % 4) + [0, 64): 8 x 4 MFMA blocks
-// of 16 x 16 and their fp32 accumulators (128 VGPRs -- the promotion FMAs need
-// them in VALU registers, so a wave cannot hold more).  GEMM1: the 64 weight
+// Tile.  224 rows x 256 weight rows, 8 waves (two per SIMD); wave w owns rows
+// 112 (w / 4) + [0, 112) and weight rows 64 (w % 4) + [0, 64): 7 x 4 MFMA blocks
+// of 16 x 16 and their fp32 accumulators (112 VGPRs -- the promotion FMAs need
+// them in VALU registers).  224 rather than 256 rows is what lets three A
+// stages and two B stages fit in the 160 KiB of LDS.  GEMM1: the 64 weight
 // rows of a wave are 32 gate rows then the 32 up rows of the same h columns, so
 // h = silu(g) * u forms in registers; GEMM2: 64 output columns.
-// Pipeline.  K advances in stages of 128 through two A buffers [256 x 128 B |
+// Pipeline.  K advances in stages of 128 through three A buffers [224 x 128 B |
 // 256 row scales] and two B buffers [256 x 128 B]; operands move HBM -> LDS by
-// buffer_load ... lds.  A wave reads all its B fragments of a stage first, so
-// B of stage s+2 is issued as soon as every wave has them (almost two stages
-// ahead of use) and A of stage s+1 at the start of stage s (one stage ahead).  Chunks outside the tile (rows past the
+// buffer_load ... lds, both two stages ahead: A of stage s+2 at the start of
+// stage s (its buffer held stage s-1), B of stage s+2 as soon as every wave
+// has read its B fragments of stage s into registers.  Chunks outside the tile (rows past the
 // group's end, weight rows past N) carry an offset beyond their buffer
 // descriptor and load as zero.  LDS chunks of 16 B are XOR-swizzled by
-// (row >> 1) & 7, so a fragment read of 16 rows at one logical chunk touches
-// 16 distinct 16-byte bank groups of the 64 banks.
+// (row & 7) ^ ((row >> 3) & 1): a 16-byte read is served eight lanes (128 B)
+// at a time, and the eight rows of such a group, at one logical chunk, land on
+// eight distinct 16-byte bank groups (so do the two row parities of 16 lanes).
 // GEMM1 epilogue: h is requantised per row and 128 columns -- the tile's 128 h
 // columns are one scale block: s = max|h| / 448 (1 for an all-zero block),
 // q = e4m3_rne_sat(h / s) -- staged through LDS and stored as 16-byte chunks.
@@ -32,22 +34,27 @@
 namespace moe {
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 128, NTH = 512;
-constexpr int kChunks = 256 * 8;               // 16-byte chunks of one operand in one stage
-constexpr int kStageA = kChunks + 128;         // A, 256 fp32 row scales, a 1 KiB sink
+constexpr int BM = kFfnBmFp8, BN = 256, BK = 128, NTH = 512;
+constexpr int RB = BM / 32;                    // 16-row blocks per wave (a wave owns half the rows)
+constexpr int kChunksA = BM * 8;               // 16-byte chunks of A in one stage
+constexpr int kChunksB = BN * 8;               // ... of B
+constexpr int kStageA = kChunksA + 72;         // A, then 288 fp32 row scales (rows >= BM zero)
+static_assert(BM % 32 == 0 && BM <= 224, "three A stages and two B stages must fit in 160 KiB of LDS");
 constexpr uint32_t kOOB = 0x40000000u;         // past every descriptor: the load returns zero
 
 typedef __attribute__((address_space(3))) void* lds_t;
 
 __shared__ i32x4 stgA0[kStageA];
 __shared__ i32x4 stgA1[kStageA];
-__shared__ i32x4 stgB0[kChunks];
-__shared__ i32x4 stgB1[kChunks];
+__shared__ i32x4 stgA2[kStageA];
+__shared__ i32x4 stgB0[kChunksB];
+__shared__ i32x4 stgB1[kChunksB];
 
 template <int BUF>
 __device__ __forceinline__ i32x4* stgA() {
     if constexpr (BUF == 0) return stgA0;
-    else return stgA1;
+    else if constexpr (BUF == 1) return stgA1;
+    else return stgA2;
 }
 template <int BUF>
 __device__ __forceinline__ i32x4* stgB() {
@@ -59,7 +66,7 @@ __device__ __forceinline__ void barrier_lds() { asm volatile("s_barrier" ::: "me
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-__device__ __forceinline__ int swz8(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int swz8(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
@@ -93,43 +100,61 @@ struct Dma {
 };
 
 // A loads of stage t into A buffer BUF: 4 chunk loads per lane (8 LDS rows
-// each) and one row-scale load -- waves 0..3 load the scales of 64 rows each,
-// waves 4..7 an out-of-range (zero) load into the sink, so every wave has the
-// same 5 A loads per stage.
-template <int BUF>
-__device__ __forceinline__ void dma_a(const Dma& d, int t, int wave) {
-    i32x4* buf = stgA<BUF>();
-    const uint32_t k = (uint32_t)t * BK;
-    const bool real = t < d.nsteps;  // stages past the end load zeros
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t off = (!real || d.va[i] == kOOB) ? kOOB : d.va[i] + k;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ra, (lds_t)(buf + (wave * 4 + i) * 64), 16, off, 0, 0, 0);
-    }
-    const uint32_t so = (!real || d.vs == kOOB) ? kOOB : d.vs + (uint32_t)t * 4u;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rs, (lds_t)(buf + kChunks + wave * 16), 4, so, 0, 0, 0);
-}
-
-// B loads of stage t into B buffer BUF: 4 chunk loads per lane.
-template <int MODE, int BUF>
-__device__ __forceinline__ void dma_b(const Dma& d, int t, int wave) {
-    i32x4* buf = stgB<BUF>();
+// each) and one row-scale load, the same 5 for every wave.  The tile's BM rows
+// take 28 chunk loads; wave 7 repeats wave 0's, writing the same bytes to the
+// same place.  Wave w loads the scales of rows 32 w + [0, 64): each row's
+// scale is written by two waves, again the same value, and rows past the tile
+// load zeros.  Every destination is an offset into the buffer itself, so the
+// compiler can tell the buffers apart while the loads are in flight.
+//
+// Load J (0..8) of the 9 a wave issues per stage t: J < 4 the A chunk loads,
+// J = 4 the row-scale load (both into A buffer ABUF), J >= 5 the B chunk loads
+// into B buffer BBUF.  A load that is not real (a stage past the end, rows
+// past the tile) carries an offset past its descriptor and loads zeros.
+template <int MODE, int ABUF, int BBUF, int J>
+__device__ __forceinline__ void dma1(const Dma& d, int t, int wave) {
     const uint32_t k = (uint32_t)t * BK;
     const bool real = t < d.nsteps;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    if constexpr (J < 4) {
+        const uint32_t off = (!real || d.va[J] == kOOB) ? kOOB : d.va[J] + k;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ra, (lds_t)(stgA<ABUF>() + ((wave * 4 + J) % (BM / 8)) * 64), 16,
+                                                 off, 0, 0, 0);
+    } else if constexpr (J == 4) {
+        const uint32_t so = (!real || d.vs == kOOB) ? kOOB : d.vs + (uint32_t)t * 4u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rs, (lds_t)(stgA<ABUF>() + kChunksA + wave * 8), 4, so, 0, 0, 0);
+    } else {
+        constexpr int i = J - 5;
         const uint32_t off = (!real || d.vb[i] == kOOB) ? kOOB : d.vb[i] + k;
         // GEMM1: wave w fills LDS rows 32 w + [0, 32): gate rows of quarter w / 2
         // on even waves, up rows on odd waves
         const __amdgpu_buffer_rsrc_t r = (MODE == 0 && (wave & 1)) ? d.rb1 : d.rb0;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_t)(buf + (wave * 4 + i) * 64), 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_t)(stgB<BBUF>() + (wave * 4 + i) * 64), 16, off, 0, 0, 0);
     }
 }
 
-// vmcnt(4) with the other counters at zero: a stage's A loads and everything
-// before them have landed (the 4 B loads issued after them may be in flight),
-// and every LDS read of this wave has returned.
-__device__ __forceinline__ void wait_stage() { __builtin_amdgcn_s_waitcnt(4 | 0x0070); }
+// The A loads (J = 0..4) of stage t into A buffer BUF.
+template <int MODE, int BUF>
+__device__ __forceinline__ void dma_a(const Dma& d, int t, int wave) {
+    dma1<MODE, BUF, 0, 0>(d, t, wave);
+    dma1<MODE, BUF, 0, 1>(d, t, wave);
+    dma1<MODE, BUF, 0, 2>(d, t, wave);
+    dma1<MODE, BUF, 0, 3>(d, t, wave);
+    dma1<MODE, BUF, 0, 4>(d, t, wave);
+}
+
+// The B loads (J = 5..8) of stage t into B buffer BUF.
+template <int MODE, int BUF>
+__device__ __forceinline__ void dma_b(const Dma& d, int t, int wave) {
+    dma1<MODE, 0, BUF, 5>(d, t, wave);
+    dma1<MODE, 0, BUF, 6>(d, t, wave);
+    dma1<MODE, 0, BUF, 7>(d, t, wave);
+    dma1<MODE, 0, BUF, 8>(d, t, wave);
+}
+
+// vmcnt(9) with the other counters at zero: a stage's A and B loads and
+// everything before them have landed (the 9 loads of the next stage may be in
+// flight), and every LDS read of this wave has returned.
+__device__ __forceinline__ void wait_stage() { __builtin_amdgcn_s_waitcnt(9 | 0x0070); }
 
 __device__ __forceinline__ i32x8 cat(i32x4 lo, i32x4 hi) {
     return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -162,33 +187,57 @@ __device__ __forceinline__ void read_b(int q, int lane, i32x8 (&b)[4]) {
     for (int cb = 0; cb < 4; ++cb) b[cb] = cat(buf[ib + cb * 128 + plo], buf[ib + cb * 128 + phi]);
 }
 
-// One K stage for the 8 row blocks of 16 starting at tile row r0: every (row
+// The loads of stage t spread over the row blocks of a K stage, J after the
+// MFMAs of row block rb: two after each of the first three, one after each of
+// the next three.  A wave that issues all 9 at once stalls until the texture
+// unit has taken them, and the other waves' loads are queued there too.
+template <int MODE, int NA, int NB, int RBI>
+__device__ __forceinline__ void dma_slot(const Dma& d, int t, int wave) {
+    if constexpr (RBI < 3) {
+        dma1<MODE, NA, NB, 2 * RBI>(d, t, wave);
+        dma1<MODE, NA, NB, 2 * RBI + 1>(d, t, wave);
+    } else if constexpr (RBI < 6) {
+        dma1<MODE, NA, NB, RBI + 3>(d, t, wave);
+    }
+}
+
+// One K stage for the RB row blocks of 16 starting at tile row r0: every (row
 // block, column block) MFMA of this wave, promoted with the stage's row scales
 // and the wave's weight-block scales p0 (gate or down columns) and p1 (up
-// columns).  Software-pipelined over row blocks: while the four MFMAs of row
-// block rb run, the fragments of rb + 1 are read and rb - 1 is promoted.
-template <int BUF>
-__device__ __forceinline__ void kstep(int r0, int lane, const i32x8 (&b)[4], float p0, float p1,
-                                      f32x4 (&acc)[8][4]) {
-    constexpr int RB = 8;
+// columns), with the loads of stage t into A buffer NA and B buffer NB issued
+// between them.  Software-pipelined over row blocks: while the four MFMAs of
+// row block rb run, the fragments of rb + 1 are read and rb - 1 is promoted.
+template <int MODE, int BUF, int NA, int NB>
+__device__ __forceinline__ void kstep(const Dma& d, int t_stage, int wave, int r0, int lane, const i32x8 (&b)[4],
+                                      float p0, float p1, f32x4 (&acc)[RB][4]) {
     // Every access indexes the stage buffer itself (an integer base plus a
     // constant), so the compiler can tell it from the DMA in flight into the
     // other buffers and adds no wait for it.
     const i32x4* buf = stgA<BUF>();
     const int l16 = lane & 15;
     const int plo = (2 * (lane >> 4)) ^ swz8(l16), phi = plo ^ 1;
-    const int ia = ((r0 & 128) + l16) * 8;              // row block rb: + rb * 128
-    const int is = kChunks + (r0 & 128) / 4 + (lane >> 4);  // row block rb: + rb * 4
+    const int ia = (r0 + l16) * 8;                      // row block rb: + rb * 128
+    const int is = kChunksA + r0 / 4 + (lane >> 4);     // row block rb: + rb * 4
     i32x8 a[2];
     f32x4 sa[3];
     f32x4 t[2][4];
     a[0] = cat(buf[ia + plo], buf[ia + phi]);
     sa[0] = __builtin_bit_cast(f32x4, buf[is]);
     __builtin_amdgcn_sched_barrier(0);
+    static_assert(RB >= 6 && RB <= 8, "the loads of a stage are spread over six row blocks");
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) t[rb & 1][cb] = mfma16x16x128_fp8(a[rb & 1], b[cb]);
+        switch (rb) {  // rb is a constant here: the loop is unrolled
+            case 0: dma_slot<MODE, NA, NB, 0>(d, t_stage, wave); break;
+            case 1: dma_slot<MODE, NA, NB, 1>(d, t_stage, wave); break;
+            case 2: dma_slot<MODE, NA, NB, 2>(d, t_stage, wave); break;
+            case 3: dma_slot<MODE, NA, NB, 3>(d, t_stage, wave); break;
+            case 4: dma_slot<MODE, NA, NB, 4>(d, t_stage, wave); break;
+            case 5: dma_slot<MODE, NA, NB, 5>(d, t_stage, wave); break;
+            default: break;
+        }
         if (rb + 1 < RB) {
             a[(rb + 1) & 1] = cat(buf[ia + (rb + 1) * 128 + plo], buf[ia + (rb + 1) * 128 + phi]);
             sa[(rb + 1) % 3] = __builtin_bit_cast(f32x4, buf[is + (rb + 1) * 4]);
@@ -200,12 +249,14 @@ __device__ __forceinline__ void kstep(int r0, int lane, const i32x8 (&b)[4], flo
 }
 
 // Rows of a tile past the group's end load as zero and are computed like the
-// others; a wave whose half of the tile holds no row skips the MFMAs.
+// others (also by a wave whose half of the tile holds no row: its MFMAs carry
+// the stage's loads, and one load schedule for every wave keeps the compiler's
+// count of loads in flight exact).
 template <int MODE>
 __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int M, int n0) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int mh = wave >> 2, q = wave & 3, r0 = mh * 128;
+    const int mh = wave >> 2, q = wave & 3, r0 = mh * (BM / 2);
     const int K = p.K, N = p.N;
     const int KB = K / BK;  // K and N are multiples of 128
     const int NB = N / BK;
@@ -215,8 +266,8 @@ __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int 
     d.ra = make_rsrc(p.a + (size_t)row0 * K, (uint32_t)M * (uint32_t)K);
     d.rs = make_rsrc(p.a_scale + (size_t)row0 * KB, (uint32_t)M * (uint32_t)KB * 4u);
     {
-        const int r = wave * 64 + lane;
-        d.vs = (wave < 4 && r < M) ? (uint32_t)r * (uint32_t)KB * 4u : kOOB;
+        const int r = wave * 32 + lane;  // < 288: the scale area of a stage
+        d.vs = r < M ? (uint32_t)r * (uint32_t)KB * 4u : kOOB;
     }
     // ---- B: GEMM1 the gate and up rows n0 + [0, 128) (LDS quarter j holds gate
     // rows 32 j + [0, 32) then the up rows of the same h columns); GEMM2 the
@@ -232,9 +283,10 @@ __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int 
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int row = wave * 32 + i * 8 + (lane >> 3);  // LDS row this lane fills (A and B)
+        const int row = wave * 32 + i * 8 + (lane >> 3);  // LDS row this lane fills (B; A modulo BM)
+        const int arow = row % BM;
         const uint32_t logical = (uint32_t)(((lane & 7) ^ swz8(row)) * 16);
-        d.va[i] = row < M ? (uint32_t)row * (uint32_t)K + logical : kOOB;
+        d.va[i] = arow < M ? (uint32_t)arow * (uint32_t)K + (uint32_t)(((lane & 7) ^ swz8(arow)) * 16) : kOOB;
         const int wrow = MODE == 0 ? (wave >> 1) * 32 + i * 8 + (lane >> 3) : row;  // relative to n0
         d.vb[i] = wrow < nlim ? (uint32_t)wrow * (uint32_t)K + logical : kOOB;
     }
@@ -266,41 +318,49 @@ __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int 
         p1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(h ? ws1[1] : ws1[0]), l));
     };
 
-    f32x4 acc[8][4];
+    f32x4 acc[RB][4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < RB; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // The loop runs whole pairs of stages and always issues the next loads
-    // (zeros past the end; an odd last stage computes on zeros with zero
-    // scales).  Per stage, in issue order: A of stage s+1 (5 loads), then B of
-    // stage s+2 (4 loads), so at the start of a stage vmcnt(4) covers its A and
-    // B.  Prologue: B0, A0, B1.
+    // Stage s uses A buffer s % 3 and B buffer s % 2; the loop body is the six
+    // stages of one period of both rings and leaves after stage KB - 1.  Loads
+    // of stages past the end carry zeros.  Issue order: A0, B0, A1, B1, then per
+    // stage s, during its MFMAs: A(s+2) (5 loads), B(s+2) (4).
+    dma_a<MODE, 0>(d, 0, wave);
     dma_b<MODE, 0>(d, 0, wave);
-    dma_a<0>(d, 0, wave);
+    dma_a<MODE, 1>(d, 1, wave);
     dma_b<MODE, 1>(d, 1, wave);
     i32x8 b[4];
-    for (int s = 0; s < KB; s += 2) {
+    int s = 0;
+    auto stage = [&](auto ab, auto bb) {
+        constexpr int AB = decltype(ab)::value, BB = decltype(bb)::value;
         float p0, p1;
         wscale(s, p0, p1);
-        wait_stage();       // stage s (buffers 0) has landed; this wave's reads of stage s-1 are done
-        barrier_lds();      // ... everybody's: the buffers 1 are free
-        dma_a<1>(d, s + 1, wave);
-        read_b<0>(q, lane, b);
+        wait_stage();   // stage s has landed (this wave's loads); this wave's reads of stage s-1 are done
+        barrier_lds();  // ... every wave's: A buffer (s+2) % 3 is free
+        read_b<BB>(q, lane, b);
         wait_lgkm0();
-        barrier_lds();      // every wave holds its B fragments of stage s
-        dma_b<MODE, 0>(d, s + 2, wave);
-        if (r0 < M) kstep<0>(r0, lane, b, p0, p1, acc);
-        wscale(s + 1, p0, p1);
-        wait_stage();
-        barrier_lds();
-        dma_a<0>(d, s + 2, wave);
-        read_b<1>(q, lane, b);
-        wait_lgkm0();
-        barrier_lds();
-        dma_b<MODE, 1>(d, s + 3, wave);
-        if (r0 < M) kstep<1>(r0, lane, b, p0, p1, acc);
+        barrier_lds();  // every wave holds its B fragments of stage s: B buffer s % 2 is free
+        kstep<MODE, AB, (AB + 2) % 3, BB>(d, s + 2, wave, r0, lane, b, p0, p1, acc);
+    };
+    using C0 = std::integral_constant<int, 0>;
+    using C1 = std::integral_constant<int, 1>;
+    using C2 = std::integral_constant<int, 2>;
+    stage(C0{}, C0{});
+    while (++s < KB) {
+        stage(C1{}, C1{});
+        if (++s >= KB) break;
+        stage(C2{}, C0{});
+        if (++s >= KB) break;
+        stage(C0{}, C1{});
+        if (++s >= KB) break;
+        stage(C1{}, C0{});
+        if (++s >= KB) break;
+        stage(C2{}, C1{});
+        if (++s >= KB) break;
+        stage(C0{}, C0{});
     }
     wait_vm0();  // no LDS DMA may outlive the workgroup
     barrier_lds();
@@ -310,7 +370,7 @@ __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int 
         // h = silu(g) * u for h columns n0 + 32 q + 16 c + l16, c = 0, 1
         float rmax[8][4];
 #pragma unroll
-        for (int rb = 0; rb < 8; ++rb)
+        for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 acc[rb][0][j] = silu_f(acc[rb][0][j]) * acc[rb][2][j];
@@ -326,14 +386,14 @@ __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int 
         float* red = reinterpret_cast<float*>(stgA0);
         if (l16 == 0)
 #pragma unroll
-            for (int rb = 0; rb < 8; ++rb)
+            for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) red[q * 256 + r0 + rb * 16 + rq + j] = rmax[rb][j];
         __syncthreads();
-        uint8_t* qs = reinterpret_cast<uint8_t*>(stgB0);  // [256 rows][128 columns] e4m3
+        uint8_t* qs = reinterpret_cast<uint8_t*>(stgB0);  // [BM rows][128 columns] e4m3
         const int qc = q * 32 + l16;
 #pragma unroll
-        for (int rb = 0; rb < 8; ++rb)
+        for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int row = r0 + rb * 16 + rq + j;
@@ -361,7 +421,7 @@ __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int 
         float* st = reinterpret_cast<float*>(stgB0 + wave * 256);
         const int cw = n0 + q * 64;  // first output column of this wave
 #pragma unroll
-        for (int rb = 0; rb < 8; ++rb) {
+        for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
