@@ -15,8 +15,9 @@ Prints one JSON line: value = layer TFLOP/s (algorithmic: 6*H*I per routed
 (token, expert) pair and per token for the shared expert, plus 2*T*H*E for the
 router), tokens/s, the fraction of the bf16 dense MFMA peak, a per-stage
 breakdown timed with HIP events on the launch stream, the roofline of the
-dominant stage (the grouped FFN), and the oracle's CPU throughput on a bounded
-sample of the same arithmetic.
+dominant stage (the grouped FFN: bound by whichever of flop / MFMA peak and
+algorithmic bytes / HBM peak takes longer, both fractions reported), and the
+oracle's CPU throughput on a bounded sample of the same arithmetic.
 
 --workload c5_dsv3_ep_fp8 times the fp8 grouped FFN alone on one GPU's
 expert-parallel share (65536 dispatched rows over 8 local experts, e4m3 with
@@ -301,10 +302,25 @@ def main():
         tf = json.load(open(TRAFFIC_FILE))
         if tf.get("source_hash") == ffn_source_hash() and tf.get("workload") == a.workload:
             traffic = tf.get("hbm_bytes_per_launch")
-    roofline = {"bound": "mfma", "achieved": round(ffn_achieved, 1), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ffn_achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                "kernel": "moe_grouped_ffn (ffn_gemm_bf16<0> gate/up+SwiGLU, ffn_gemm_bf16<1> down, tile list)",
-                "flop_per_launch": ffn_flop}
+    # The bound is the larger of the two roofline times, flop / MFMA peak and
+    # algorithmic bytes / HBM peak; the other fraction is reported beside it.
+    ffn_bytes = bytes_["grouped_ffn"]
+    t_mfma = ffn_flop / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = ffn_bytes / (PEAK_HBM_GBS * 1e9)
+    ffn_gbs = ffn_bytes / (stage_ms[2] * 1e-3) / 1e9
+    if t_hbm > t_mfma:
+        roofline = {"bound": "hbm", "achieved": round(ffn_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(ffn_gbs / PEAK_HBM_GBS, 4)}
+    else:
+        roofline = {"bound": "mfma", "achieved": round(ffn_achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(ffn_achieved / PEAK_BF16_TFLOPS, 4)}
+    roofline.update({
+        "traffic": traffic,
+        "kernel": "moe_grouped_ffn (ffn_gemm_bf16<0> gate/up+SwiGLU, ffn_gemm_bf16<1> down, tile list)",
+        "flop_per_launch": ffn_flop, "bytes_per_launch": ffn_bytes,
+        "roofline_ms": round(max(t_mfma, t_hbm) * 1e3, 4),
+        "mfma_frac": round(ffn_achieved / PEAK_BF16_TFLOPS, 4),
+        "hbm_frac": round(ffn_gbs / PEAK_HBM_GBS, 4)})
 
     cpu = None if a.no_cpu_baseline else cpu_baseline(s, x, w_r, a.cpu_seconds)
 
@@ -383,6 +399,13 @@ def bench_fp8_ffn(a, s, dev):
     ms = ev0.elapsed_time(ev1) / a.steps
     flop = 6.0 * s.H * s.I * s.T
     tflops = flop / (ms * 1e-3) / 1e12
+    # algorithmic bytes: e4m3 weights and their block scales, the rows and their
+    # scales read once, bf16 y written once
+    KB1, KB2 = s.H // 128, s.I // 128
+    nbytes = (3.0 * s.E * s.H * s.I + 3.0 * s.E * KB1 * KB2 * 4 + s.T * s.H + s.T * KB1 * 4 + s.T * s.H * 2)
+    t_mfma = flop / (PEAK_FP8_TFLOPS * 1e12)
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+    assert t_mfma >= t_hbm, "the fp8 FFN workload is expected to be compute-bound"
     res = {
         "metric": "grouped FFN TFLOP/s (1 GPU, fp8 expert-parallel share of a DeepSeek-V3 prefill layer)",
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
@@ -396,7 +419,9 @@ def bench_fp8_ffn(a, s, dev):
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_FP8_TFLOPS, 4), "traffic": None,
                      "kernel": "moe_grouped_ffn (ffn_gemm_fp8 GEMM1+SwiGLU+requantise, GEMM2, tile list)",
-                     "flop_per_launch": flop},
+                     "flop_per_launch": flop, "bytes_per_launch": nbytes,
+                     "roofline_ms": round(max(t_mfma, t_hbm) * 1e3, 4),
+                     "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
         "cpu_baseline": None,
     }
     print(json.dumps(res), flush=True)
