@@ -426,25 +426,51 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, int mt, int g, int r
     void* out = shared ? p.out_shared : p.out_routed;
     if (MODE == 0) {
         // h = silu(g) * u into this M tile's slot, tiled with the slot's own KS
-        // (the K of GEMM2), so GEMM2 streams it with contiguous 1 KiB reads
+        // (the K of GEMM2), so GEMM2 streams it with contiguous 1 KiB reads.
         // Columns in [N, roundup(N, 32)) are GEMM2's K padding: they get zeros.
-        const int col = n0 + wave * 32 + l32;
+        // A wave's 32 columns are one k block of the slot.  Each 32-row block
+        // goes through a private 4 KiB LDS slice of the A ring (free once every
+        // wave has left the main loop), fp32, row r at r * 128 B with rows r and
+        // r ^ 1 exchanged when bit 2 of r is set, so the accumulator writes (rows
+        // r and r + 4 in the two half-waves) touch 64 distinct banks.  It is read
+        // back in the tiled block's own order -- lane q takes slot q, 8 columns
+        // of one row, two 16-byte reads on distinct banks -- and every 16-row
+        // block is one contiguous 1 KiB store.  Rows of the slot past M hold
+        // zeros (their A rows loaded as zeros).  LDS operations of one wave are
+        // processed in order.
+        barrier_lds();
         const int ksh = (N + BK - 1) / BK;
-        if (col < ksh * BK) {
-            const bool live = col < N;
+        const int kb = (n0 >> 5) + wave;  // n0 is a multiple of 32
+        if (kb < ksh) {
+            const bool live = kb * 32 + l32 < N;
             uint16_t* h = static_cast<uint16_t*>(out) + (size_t)mt * 16 * p.h_slot_ks * 512;
-            const int kb = col >> 5, c8 = (col & 31) >> 3, e8 = col & 7;
+            float* st = reinterpret_cast<float*>(ring<0>() + wave * 256);
+            const int rr = lane >> 2, c8 = (lane & 3) ^ swz_of_row(rr);  // the slot this lane stores
 #pragma unroll
             for (int r = 0; r < NRB; ++r) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const int row = r * 32 + c_row(i, lane);
-                    if (row < M) {
-                        const size_t o = ((size_t)(row >> 4) * ksh + kb) * 512 +
-                                         (size_t)(((row & 15) * 4 + (c8 ^ swz_of_row(row))) * 8 + e8);
-                        h[o] = live ? f32_to_bf16(silu_f(acc0[r][i]) * acc1[r][i]) : (uint16_t)0;
-                    }
+                    const int row = c_row(i, lane);  // bit 2 of row is lane / 32
+                    st[(row ^ ((row >> 2) & 1)) * 32 + l32] = live ? silu_f(acc0[r][i]) * acc1[r][i] : 0.0f;
                 }
+                // the staged values are read by other lanes of this wave: keep the
+                // compiler from moving the reads above the writes (no wait is needed)
+                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+                for (int hb = 0; hb < 2; ++hb) {
+                    const int row = hb * 16 + rr;
+                    const float* src = st + (row ^ ((row >> 2) & 1)) * 32 + c8 * 8;
+                    const f32x4 v0 = *reinterpret_cast<const f32x4*>(src);
+                    const f32x4 v1 = *reinterpret_cast<const f32x4*>(src + 4);
+                    uint4 q;
+                    q.x = (uint32_t)f32_to_bf16(v0[0]) | ((uint32_t)f32_to_bf16(v0[1]) << 16);
+                    q.y = (uint32_t)f32_to_bf16(v0[2]) | ((uint32_t)f32_to_bf16(v0[3]) << 16);
+                    q.z = (uint32_t)f32_to_bf16(v1[0]) | ((uint32_t)f32_to_bf16(v1[1]) << 16);
+                    q.w = (uint32_t)f32_to_bf16(v1[2]) | ((uint32_t)f32_to_bf16(v1[3]) << 16);
+                    if (r * 32 + hb * 16 < M)
+                        *reinterpret_cast<uint4*>(h + ((size_t)(r * 2 + hb) * ksh + kb) * 512 + lane * 8) = q;
+                }
+                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");  // reads before the next block's writes
             }
         }
     } else {
