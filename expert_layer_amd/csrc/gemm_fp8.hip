@@ -8,6 +8,10 @@
 // so every MFMA result t is the unscaled partial sum of one scale block and is
 // folded in as acc += t * (s_row * s_weight) on the VALU.  The MFMAs write VGPRs
 // (this file is compiled in the VGPR form), so the promotion reads t directly.
+// The weight fragment is the MFMA's first operand and the row fragment its
+// second, so a 16 x 16 result comes out transposed: lane l holds row l % 16 and
+// the four columns 4 (l / 16) + [0, 4), and one product s_row * s_weight serves
+// all four.
 //
 // Tile.  224 rows x 256 weight rows, 8 waves (two per SIMD); wave w owns rows
 // 112 (w / 4) + [0, 112) and weight rows 64 (w % 4) + [0, 64): 7 x 4 MFMA blocks
@@ -17,7 +21,7 @@
 // rows of a wave are 32 gate rows then the 32 up rows of the same h columns, so
 // h = silu(g) * u forms in registers; GEMM2: 64 output columns.
 // Pipeline.  K advances in stages of 128 through three A buffers [224 x 128 B |
-// 256 row scales] and two B buffers [256 x 128 B]; operands move HBM -> LDS by
+// 288 row scales] and two B buffers [256 x 128 B]; operands move HBM -> LDS by
 // buffer_load ... lds, both two stages ahead: A of stage s+2 at the start of
 // stage s (its buffer held stage s-1), B of stage s+2 as soon as every wave
 // has read its B fragments of stage s into registers.  Chunks outside the tile (rows past the
@@ -38,7 +42,7 @@ constexpr int BM = kFfnBmFp8, BN = 256, BK = 128, NTH = 512;
 constexpr int RB = BM / 32;                    // 16-row blocks per wave (a wave owns half the rows)
 constexpr int kChunksA = BM * 8;               // 16-byte chunks of A in one stage
 constexpr int kChunksB = BN * 8;               // ... of B
-constexpr int kStageA = kChunksA + 72;         // A, then 288 fp32 row scales (rows >= BM zero)
+constexpr int kStageA = kChunksA + 72;         // A, then 288 fp32 row scales (see scale_row)
 static_assert(BM % 32 == 0 && BM <= 224, "three A stages and two B stages must fit in 160 KiB of LDS");
 constexpr uint32_t kOOB = 0x40000000u;         // past every descriptor: the load returns zero
 
@@ -92,6 +96,17 @@ struct Fp8Args {
     int K, N;               // GEMM1: K = H, N = I; GEMM2: K = I, N = H
     int out_f32;            // GEMM2 output dtype
 };
+
+// Row scales of a stage in LDS: position P = 128 h + 64 (rb / 4) + 4 l + rb % 4
+// holds the scale of tile row scale_row(P) = 112 h + 16 rb + l, so the scales a
+// lane needs (rows 16 rb + lane % 16 of its half h, rb = 0..6) are two 16-byte
+// chunks, and the 16 lanes of a row group read 16 consecutive chunks.
+// Positions whose row lies past the tile (rb = 7 in the second half, P >= 256)
+// hold zeros; in the first half rb = 7 repeats a row of the second.
+__device__ __forceinline__ int scale_row(int pos) {
+    const int rb = ((pos >> 6) & 1) * 4 + (pos & 3), l = (pos >> 2) & 15;
+    return (BM / 2) * (pos >> 7) + 16 * rb + l;
+}
 
 struct Dma {
     __amdgpu_buffer_rsrc_t ra, rs, rb0, rb1;
@@ -160,11 +175,12 @@ __device__ __forceinline__ i32x8 cat(i32x4 lo, i32x4 hi) {
     return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-__device__ __forceinline__ void promote(const f32x4 (&t)[4], const f32x4& sa, float p0, float p1,
-                                        f32x4 (&acc)[4]) {
+// acc += t * s_row * s_weight for one row block: sa is this lane's row scale,
+// p0 the weight scale of column blocks 0, 1 (gate or down) and p1 of 2, 3 (up).
+__device__ __forceinline__ void promote(const f32x4 (&t)[4], float sa, float p0, float p1, f32x4 (&acc)[4]) {
+    const float q0 = sa * p0, q1 = sa * p1;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const float q0 = sa[j] * p0, q1 = sa[j] * p1;
         acc[0][j] = __builtin_fmaf(t[0][j], q0, acc[0][j]);
         acc[1][j] = __builtin_fmaf(t[1][j], q0, acc[1][j]);
         acc[2][j] = __builtin_fmaf(t[2][j], q1, acc[2][j]);
@@ -217,18 +233,19 @@ __device__ __forceinline__ void kstep(const Dma& d, int t_stage, int wave, int r
     const int l16 = lane & 15;
     const int plo = (2 * (lane >> 4)) ^ swz8(l16), phi = plo ^ 1;
     const int ia = (r0 + l16) * 8;                      // row block rb: + rb * 128
-    const int is = kChunksA + r0 / 4 + (lane >> 4);     // row block rb: + rb * 4
+    // this lane's row scales: row blocks 0..3 in chunk 32 h + l16, 4..7 in 32 h + 16 + l16
+    const int is = kChunksA + (r0 / (BM / 2)) * 32 + l16;
+    const f32x4 sa_lo = __builtin_bit_cast(f32x4, buf[is]), sa_hi = __builtin_bit_cast(f32x4, buf[is + 16]);
+    auto sa = [&](int rb) { return rb < 4 ? sa_lo[rb & 3] : sa_hi[rb & 3]; };
     i32x8 a[2];
-    f32x4 sa[3];
     f32x4 t[2][4];
     a[0] = cat(buf[ia + plo], buf[ia + phi]);
-    sa[0] = __builtin_bit_cast(f32x4, buf[is]);
     __builtin_amdgcn_sched_barrier(0);
     static_assert(RB >= 6 && RB <= 8, "the loads of a stage are spread over six row blocks");
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) t[rb & 1][cb] = mfma16x16x128_fp8(a[rb & 1], b[cb]);
+        for (int cb = 0; cb < 4; ++cb) t[rb & 1][cb] = mfma16x16x128_fp8(b[cb], a[rb & 1]);
         switch (rb) {  // rb is a constant here: the loop is unrolled
             case 0: dma_slot<MODE, NA, NB, 0>(d, t_stage, wave); break;
             case 1: dma_slot<MODE, NA, NB, 1>(d, t_stage, wave); break;
@@ -238,14 +255,11 @@ __device__ __forceinline__ void kstep(const Dma& d, int t_stage, int wave, int r
             case 5: dma_slot<MODE, NA, NB, 5>(d, t_stage, wave); break;
             default: break;
         }
-        if (rb + 1 < RB) {
-            a[(rb + 1) & 1] = cat(buf[ia + (rb + 1) * 128 + plo], buf[ia + (rb + 1) * 128 + phi]);
-            sa[(rb + 1) % 3] = __builtin_bit_cast(f32x4, buf[is + (rb + 1) * 4]);
-        }
-        if (rb > 0) promote(t[(rb - 1) & 1], sa[(rb - 1) % 3], p0, p1, acc[rb - 1]);
+        if (rb + 1 < RB) a[(rb + 1) & 1] = cat(buf[ia + (rb + 1) * 128 + plo], buf[ia + (rb + 1) * 128 + phi]);
+        if (rb > 0) promote(t[(rb - 1) & 1], sa(rb - 1), p0, p1, acc[rb - 1]);
         __builtin_amdgcn_sched_barrier(0);
     }
-    promote(t[(RB - 1) & 1], sa[(RB - 1) % 3], p0, p1, acc[RB - 1]);
+    promote(t[(RB - 1) & 1], sa(RB - 1), p0, p1, acc[RB - 1]);
 }
 
 // Rows of a tile past the group's end load as zero and are computed like the
@@ -266,7 +280,8 @@ __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int 
     d.ra = make_rsrc(p.a + (size_t)row0 * K, (uint32_t)M * (uint32_t)K);
     d.rs = make_rsrc(p.a_scale + (size_t)row0 * KB, (uint32_t)M * (uint32_t)KB * 4u);
     {
-        const int r = wave * 32 + lane;  // < 288: the scale area of a stage
+        const int pos = wave * 32 + lane;  // < 288: the scale area of a stage
+        const int r = pos < 256 ? scale_row(pos) : BM;
         d.vs = r < M ? (uint32_t)r * (uint32_t)KB * 4u : kOOB;
     }
     // ---- B: GEMM1 the gate and up rows n0 + [0, 128) (LDS quarter j holds gate
@@ -365,79 +380,82 @@ __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int 
     wait_vm0();  // no LDS DMA may outlive the workgroup
     barrier_lds();
 
-    const int l16 = lane & 15, rq = 4 * (lane >> 4);
+    // A lane holds row r0 + 16 rb + l16 of its row blocks and, in column block
+    // cb, the four columns 16 cb + g4 + [0, 4) of its 64 weight rows.
+    const int l16 = lane & 15, g4 = 4 * (lane >> 4);
     if (MODE == 0) {
-        // h = silu(g) * u for h columns n0 + 32 q + 16 c + l16, c = 0, 1
-        float rmax[8][4];
+        // h = silu(g) * u for h columns n0 + 32 q + 16 c + g4 + j, c = 0, 1
+        float rmax[RB];
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
+        for (int rb = 0; rb < RB; ++rb) {
+            float m = 0.0f;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 acc[rb][0][j] = silu_f(acc[rb][0][j]) * acc[rb][2][j];
                 acc[rb][1][j] = silu_f(acc[rb][1][j]) * acc[rb][3][j];
-                float m = fmaxf(fabsf(acc[rb][0][j]), fabsf(acc[rb][1][j]));
-                m = fmaxf(m, __shfl_xor(m, 1, 16));
-                m = fmaxf(m, __shfl_xor(m, 2, 16));
-                m = fmaxf(m, __shfl_xor(m, 4, 16));
-                m = fmaxf(m, __shfl_xor(m, 8, 16));
-                rmax[rb][j] = m;
+                m = fmaxf(m, fmaxf(fabsf(acc[rb][0][j]), fabsf(acc[rb][1][j])));
             }
+            m = fmaxf(m, __shfl_xor(m, 16));
+            m = fmaxf(m, __shfl_xor(m, 32));
+            rmax[rb] = m;
+        }
         // per-row maxima of the four quarters' 32 columns -> LDS [4][256]
         float* red = reinterpret_cast<float*>(stgA0);
-        if (l16 == 0)
+        if (lane < 16)
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) red[q * 256 + r0 + rb * 16 + rq + j] = rmax[rb][j];
+            for (int rb = 0; rb < RB; ++rb) red[q * 256 + r0 + rb * 16 + l16] = rmax[rb];
         __syncthreads();
-        uint8_t* qs = reinterpret_cast<uint8_t*>(stgB0);  // [BM rows][128 columns] e4m3
-        const int qc = q * 32 + l16;
+        // [BM rows][128 columns] e4m3, 32 words a row, the 16-byte chunk c of row r
+        // at chunk c ^ ((r >> 1) & 7): a 4-byte store of 16 rows x 4 words then
+        // touches 64 distinct banks
+        uint32_t* qs = reinterpret_cast<uint32_t*>(stgB0);
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
+        for (int rb = 0; rb < RB; ++rb) {
+            const int row = r0 + rb * 16 + l16;
+            const float amax = fmaxf(fmaxf(red[row], red[256 + row]), fmaxf(red[512 + row], red[768 + row]));
+            const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int row = r0 + rb * 16 + rq + j;
-                const float amax = fmaxf(fmaxf(red[row], red[256 + row]), fmaxf(red[512 + row], red[768 + row]));
-                const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
-                qs[row * 128 + qc] = f32_to_e4m3(acc[rb][0][j] / sc);
-                qs[row * 128 + qc + 16] = f32_to_e4m3(acc[rb][1][j] / sc);
-                if (q == 0 && l16 == 0 && row < M) p.out_scale[(size_t)(row0 + row) * NB + n0 / BK] = sc;
+            for (int c = 0; c < 2; ++c) {
+                uint32_t w = 0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) w |= (uint32_t)f32_to_e4m3(acc[rb][c][j] / sc) << (8 * j);
+                qs[row * 32 + (((q * 2 + c) ^ ((row >> 1) & 7)) << 2) + (lane >> 4)] = w;
             }
+            if (q == 0 && lane < 16 && row < M) p.out_scale[(size_t)(row0 + row) * NB + n0 / BK] = sc;
+        }
         __syncthreads();
         // coalesced 16-byte stores of the tile's M rows x 128 h columns
         uint8_t* h = static_cast<uint8_t*>(p.out);
         const i32x4* qv = reinterpret_cast<const i32x4*>(qs);
         for (int c = threadIdx.x; c < M * 8; c += NTH) {
             const int row = c >> 3, ch = c & 7;
-            *reinterpret_cast<i32x4*>(h + (size_t)(row0 + row) * N + n0 + ch * 16) = qv[c];
+            *reinterpret_cast<i32x4*>(h + (size_t)(row0 + row) * N + n0 + ch * 16) = qv[row * 8 + (ch ^ ((row >> 1) & 7))];
         }
     } else {
         // y through LDS, 16 rows at a time: each wave stages its 16 x 64 block
-        // (fp32, 4 KiB of B buffer 0) with the 16-column groups of a row
-        // XOR-ed by bits 2..3 of the row, so the four row groups of a store
-        // instruction and the 16 lanes of a row's read touch distinct banks;
-        // then every lane stores 4 columns (8 B bf16 / 16 B fp32).  LDS
-        // operations of one wave are processed in order.
+        // (fp32, 4 KiB of B buffer 0), row r's 16-byte chunk c at chunk c ^ r,
+        // so the eight rows of a store group and the eight chunks of a row's
+        // read group touch distinct banks; then every lane stores 4 columns
+        // (8 B bf16 / 16 B fp32).  LDS operations of one wave are processed in
+        // order.
         float* st = reinterpret_cast<float*>(stgB0 + wave * 256);
         const int cw = n0 + q * 64;  // first output column of this wave
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-                for (int cb = 0; cb < 4; ++cb) {
-                    const int row = rq + j;  // bits 2..3 of row are lane / 16
-                    st[row * 64 + ((cb * 16 + l16) ^ (((row >> 2) & 3) << 4))] = acc[rb][cb][j];
-                }
+                for (int j = 0; j < 4; ++j)  // element stores: a whole-vector store here makes the compiler spill acc
+                    st[l16 * 64 + ((4 * cb + (lane >> 4)) ^ l16) * 4 + j] = acc[rb][cb][j];
             // the staged values are read by other lanes of this wave: keep the
             // compiler from moving the reads above the writes (no wait is needed)
             __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 #pragma unroll
             for (int it = 0; it < 4; ++it) {
                 const int qq = it * 64 + lane;  // chunk qq: row qq / 16, columns 4 (qq % 16) .. + 3
-                const int row = qq >> 4, c4 = (qq & 15) * 4;
-                const f32x4 v = *reinterpret_cast<const f32x4*>(st + row * 64 + (c4 ^ (((row >> 2) & 3) << 4)));
-                const int grow = r0 + rb * 16 + row, col = cw + c4;
+                const int row = qq >> 4, c = qq & 15;
+                const f32x4 v = *reinterpret_cast<const f32x4*>(st + row * 64 + (c ^ row) * 4);
+                const int grow = r0 + rb * 16 + row, col = cw + c * 4;
                 if (grow < M && col < N) {
                     const size_t o = (size_t)(row0 + grow) * N + col;
                     if (p.out_f32) {
