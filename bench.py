@@ -51,6 +51,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="c3_dsv3_bf16")
+    p.add_argument("--tokens", type=int, default=0,
+                   help="override the workload's token count T (the small-T, weight-streaming regime)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--rowmajor-weights", action="store_true",
                    help="time the row-major weight layout instead of the tiled one")
@@ -155,7 +157,7 @@ def main():
     dev = torch.device("cuda:0")
     if a.traffic_run:
         calibrate_copy(dev)
-    s = synth.config(a.workload)
+    s = synth.config(a.workload, **({"T": a.tokens} if a.tokens else {}))
     if s.dtype == "fp8":
         return bench_fp8_ffn(a, s, dev)
     if s.dtype != "bf16":
@@ -300,7 +302,7 @@ def main():
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         tf = json.load(open(TRAFFIC_FILE))
-        if tf.get("source_hash") == ffn_source_hash() and tf.get("workload") == a.workload:
+        if tf.get("source_hash") == ffn_source_hash() and tf.get("workload") == a.workload and not a.tokens:
             traffic = tf.get("hbm_bytes_per_launch")
     # The bound is the larger of the two roofline times, flop / MFMA peak and
     # algorithmic bytes / HBM peak; the other fraction is reported beside it.
