@@ -51,6 +51,9 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="c3_dsv3_bf16")
+    p.add_argument("--fp8-experts", action="store_true",
+                   help="a bf16 layer workload with e4m3 experts (128x128 block scales): moe_layer quantises the "
+                        "activations per token and runs the experts in fp8")
     p.add_argument("--tokens", type=int, default=0,
                    help="override the workload's token count T (the small-T, weight-streaming regime)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -160,6 +163,8 @@ def main():
     s = synth.config(a.workload, **({"T": a.tokens} if a.tokens else {}))
     if s.dtype == "fp8":
         return bench_fp8_ffn(a, s, dev)
+    if a.fp8_experts:
+        return bench_fp8_layer(a, s, dev)
     if s.dtype != "bf16":
         raise SystemExit("bench.py times the bf16 layers (c2/c3/c4) and the fp8 grouped FFN (c5)")
     T, H, E, k, I = s.T, s.H, s.E, s.k, s.I
@@ -424,6 +429,159 @@ def bench_fp8_ffn(a, s, dev):
                      "flop_per_launch": flop, "bytes_per_launch": nbytes,
                      "roofline_ms": round(max(t_mfma, t_hbm) * 1e3, 4),
                      "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def bench_fp8_layer(a, s, dev):
+    """The layer with e4m3 experts and bf16 activations: a step is one moe_layer
+    call (route, per-token quantisation, dispatch of the e4m3 rows, the routed
+    and shared fp8 grouped FFNs, combine); the stage breakdown makes the same
+    calls one by one."""
+    import numpy as np
+    import torch
+
+    import expert_layer_amd as moe
+    import synth
+
+    T, H, E, k, I = s.T, s.H, s.E, s.k, s.I
+    I_sh = s.I_shared if s.shared else 0
+    kw = dict(T=T, H=H, E=E, k=k, I=I, n_groups=s.n_groups, topk_groups=s.topk_groups,
+              score_fn=moe.MOE_SCORE_SIGMOID if s.score == "sigmoid" else moe.MOE_SCORE_SOFTMAX,
+              renormalize=s.renormalize, routed_scale=s.routed_scale, has_shared=s.shared, I_shared=I_sh,
+              y_dtype=moe.MOE_BF16, out_dtype=moe.MOE_BF16)
+    c = moe.make_cfg(**kw, act_dtype=moe.MOE_BF16, w_dtype=moe.MOE_FP8_E4M3)
+    t_gen = time.time()
+    x, w_r, bias = synth.router_inputs(s, dev)
+    wg = torch.empty((E, I, H), dtype=torch.uint8, device=dev)
+    wu, wd = torch.empty_like(wg), torch.empty((E, H, I), dtype=torch.uint8, device=dev)
+    sg = torch.empty((E, I // 128, H // 128), device=dev)
+    su, sd = torch.empty_like(sg), torch.empty((E, H // 128, I // 128), device=dev)
+    for e in range(E):
+        wg[e], sg[e], wu[e], su[e], wd[e], sd[e] = synth.fp8_expert_weights(s, e, dev)
+    sh = synth.fp8_expert_weights(s.with_(I=I_sh), E, dev) if s.shared else (None,) * 6
+    w = moe.weights(wg, wu, wd, s_gate=sg, s_up=su, s_down=sd, sh_gate=sh[0], sh_up=sh[2], sh_down=sh[4],
+                    sh_s_gate=sh[1], sh_s_up=sh[3], sh_s_down=sh[5])
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    ws = moe.workspace(c, moe.MOE_STAGE_LAYER, dev)
+    torch.cuda.synchronize()
+    print(f"[bench] fp8 experts ready in {time.time() - t_gen:.1f}s", file=sys.stderr, flush=True)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        moe.moe_layer(c, w_r, bias, w, x, out, ws, stream)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(a.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = ev0.elapsed_time(ev1) / a.steps
+
+    # ---- the same work as stage calls: route, quantise, permute (e4m3 rows,
+    # m_tile 16), the routed grouped FFN, the shared one (one group of T rows),
+    # combine
+    cq = moe.make_cfg(**dict(kw, has_shared=False, I_shared=0), act_dtype=moe.MOE_FP8_E4M3, m_tile=16)
+    c1 = moe.make_cfg(**dict(kw, E=1, k=1, n_groups=1, topk_groups=1, I=max(I_sh, 128), has_shared=False,
+                             I_shared=0), act_dtype=moe.MOE_FP8_E4M3)
+    rows = moe.moe_max_rows(cq)
+    i32 = dict(dtype=torch.int32, device=dev)
+    ids, tw = torch.empty((T, k), **i32), torch.empty((T, k), dtype=torch.float32, device=dev)
+    counts, offs, row_src, tok_row = (torch.empty(E, **i32), torch.empty(E + 1, **i32), torch.empty(rows, **i32),
+                                      torch.empty((T, k), **i32))
+    xq = torch.empty((T, H), dtype=torch.uint8, device=dev)
+    xs = torch.empty((T, H // 128), device=dev)
+    x_perm = torch.empty((rows, H), dtype=torch.uint8, device=dev)
+    xps = torch.empty((rows, H // 128), device=dev)
+    y_rows = torch.empty((rows, H), dtype=torch.bfloat16, device=dev)
+    y_sh = torch.empty((T, H), dtype=torch.bfloat16, device=dev) if s.shared else None
+    offs1 = torch.tensor([0, T], **i32)
+    w1 = moe.weights(sh[0], sh[2], sh[4], s_gate=sh[1], s_up=sh[3], s_down=sh[5]) if s.shared else None
+    ws_r = moe.workspace(c, moe.MOE_STAGE_ROUTE, dev)
+    ws_p = moe.workspace(cq, moe.MOE_STAGE_PERMUTE, dev)
+    ws_f = moe.workspace(cq, moe.MOE_STAGE_FFN, dev, n_rows_cap=rows)
+    ws_1 = moe.workspace(c1, moe.MOE_STAGE_FFN, dev, n_rows_cap=T) if s.shared else None
+    names = ["route", "quantise", "permute", "grouped_ffn", "combine"]
+
+    def stage_step(evs):
+        evs[0].record(stream)
+        moe.moe_route(c, x, w_r, bias, None, None, ids, tw, ws_r, stream)
+        evs[1].record(stream)
+        moe.moe_quantize_fp8(c, x, xq, xs, stream)
+        evs[2].record(stream)
+        moe.moe_permute(cq, xq, xs, ids, counts, offs, row_src, tok_row, x_perm, xps, ws_p, stream)
+        evs[3].record(stream)
+        moe.moe_grouped_ffn(cq, rows, x_perm, xps, offs, w, None, y_rows, None, ws_f, stream)
+        if s.shared:
+            moe.moe_grouped_ffn(c1, T, xq, xs, offs1, w1, None, y_sh, None, ws_1, stream)
+        evs[4].record(stream)
+        moe.moe_combine(c, y_rows, tok_row, tw, y_sh, out, stream)
+        evs[5].record(stream)
+
+    for _ in range(2):
+        stage_step([torch.cuda.Event(enable_timing=True) for _ in range(6)])
+    torch.cuda.synchronize()
+    all_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(a.steps)]
+    for evs in all_evs:
+        stage_step(evs)
+    torch.cuda.synchronize()
+    stage_ms = np.mean([[evs[i].elapsed_time(evs[i + 1]) for i in range(5)] for evs in all_evs], axis=0)
+
+    R = T * k
+    KB1, KB2 = H // 128, I // 128
+    ffn_flop = 6.0 * H * I * R + 6.0 * H * I_sh * T
+    layer_flop = ffn_flop + 2.0 * T * H * E
+    w_bytes = 3.0 * E * H * I + 3.0 * E * KB1 * KB2 * 4 + 3.0 * H * I_sh + 3.0 * KB1 * (I_sh // 128) * 4
+    bytes_ = {
+        "route": T * H * 2 + E * H * 2 + T * k * 8,
+        "quantise": T * H * 2 + T * H + T * KB1 * 4,
+        "permute": T * k * 4 + E * 8 + rows * 4 + T * k * 4 + 2 * (R * H + R * KB1 * 4),
+        "grouped_ffn": w_bytes + (R + T * bool(s.shared)) * (H + KB1 * 4) + (R + T * bool(s.shared)) * H * 2,
+        "combine": R * H * 2 + T * H * 2 * bool(s.shared) + T * H * 2 + T * k * 8,
+    }
+    stages = {}
+    for i, n in enumerate(names):
+        ms = float(stage_ms[i])
+        st = {"ms": round(ms, 4), "GB/s": round(bytes_[n] / (ms * 1e-3) / 1e9, 1),
+              "hbm_frac": round(bytes_[n] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        if n == "grouped_ffn":
+            st["TFLOP/s"] = round(ffn_flop / (ms * 1e-3) / 1e12, 1)
+            st["mfma_frac"] = round(ffn_flop / (ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4)
+        stages[n] = st
+    ffn_ms = float(stage_ms[3])
+    t_mfma = ffn_flop / (PEAK_FP8_TFLOPS * 1e12)
+    t_hbm = bytes_["grouped_ffn"] / (PEAK_HBM_GBS * 1e9)
+    tf = ffn_flop / (ffn_ms * 1e-3) / 1e12
+    gbs = bytes_["grouped_ffn"] / (ffn_ms * 1e-3) / 1e9
+    if t_hbm > t_mfma:
+        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    else:
+        roofline = {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tf / PEAK_FP8_TFLOPS, 4)}
+    roofline.update({"traffic": None, "kernel": "grouped FFN (ffn_gemm_fp8 routed + shared, tile lists)",
+                     "flop_per_launch": ffn_flop, "bytes_per_launch": bytes_["grouped_ffn"],
+                     "roofline_ms": round(max(t_mfma, t_hbm) * 1e3, 4),
+                     "mfma_frac": round(tf / PEAK_FP8_TFLOPS, 4), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)})
+    tflops = layer_flop / (ms_step * 1e-3) / 1e12
+    res = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8_e4m3 experts, bf16 activations", "data": "synthetic",
+        "config": {"workload": a.workload, "T": T, "H": H, "E": E, "k": k, "I": I, "shared_experts": int(s.shared),
+                   "I_shared": I_sh, "experts": "e4m3, 128x128 block scales",
+                   "activations": "bf16, quantised per token (1x128)", "out_dtype": "bf16"},
+        "tokens_per_s": round(T / (ms_step * 1e-3), 1),
+        "wall_s_timed": round(wall, 3),
+        "stages": stages,
+        "roofline": roofline,
         "cpu_baseline": None,
     }
     print(json.dumps(res), flush=True)

@@ -25,7 +25,7 @@ from ._ffi import (MOE_BF16, MOE_ERR_HIP, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORT
 
 __all__ = [
     "MoeError", "make_cfg", "weights", "workspace", "moe_validate", "moe_max_rows", "moe_workspace_bytes", "moe_ffn_workspace_bytes",
-    "moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer", "moe_status_string",
+    "moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_quantize_fp8", "moe_layer", "moe_status_string",
     "moe_last_error", "moe_cfg", "moe_weights", "lib_path",
     "MOE_OK", "MOE_ERR_INVALID_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE", "MOE_ERR_HIP",
     "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3", "MOE_SCORE_SOFTMAX", "MOE_SCORE_SIGMOID",
@@ -90,9 +90,11 @@ def _check(status: int):
 
 
 def weights(w_gate, w_up, w_down, s_gate=None, s_up=None, s_down=None, sh_gate=None, sh_up=None,
-            sh_down=None, layout: int = MOE_LAYOUT_ROWMAJOR) -> moe_weights:
+            sh_down=None, layout: int = MOE_LAYOUT_ROWMAJOR, sh_s_gate=None, sh_s_up=None,
+            sh_s_down=None) -> moe_weights:
     return moe_weights(*(_ptr(t) for t in (w_gate, w_up, w_down, s_gate, s_up, s_down, sh_gate,
-                                             sh_up, sh_down)), layout)
+                                             sh_up, sh_down)), layout,
+                       *(_ptr(t) for t in (sh_s_gate, sh_s_up, sh_s_down)))
 
 
 def moe_x_perm_bytes(cfg: moe_cfg) -> int:
@@ -182,6 +184,11 @@ def moe_grouped_ffn(cfg, n_rows_cap, x_rows, x_scale, expert_offsets, w: moe_wei
 def moe_combine(cfg, y_rows, tok_row, topk_w, y_shared, out, stream=None):
     _check(_ffi.lib().moe_combine(ctypes.byref(cfg), _ptr(y_rows), _ptr(tok_row), _ptr(topk_w),
                                   _ptr(y_shared), _ptr(out), _stream(stream)))
+
+
+def moe_quantize_fp8(cfg, x, x_q, x_scale, stream=None):
+    """x [T][H] bf16 -> x_q [T][H] e4m3 codes (uint8) and x_scale [T][H/128] fp32."""
+    _check(_ffi.lib().moe_quantize_fp8(ctypes.byref(cfg), _ptr(x), _ptr(x_q), _ptr(x_scale), _stream(stream)))
 
 
 def moe_layer(cfg, w_router, bias, w: moe_weights, x, out, ws, stream=None):

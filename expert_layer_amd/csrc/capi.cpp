@@ -67,19 +67,23 @@ moe_status check_cfg(const moe_cfg* cp) {
         return fail(MOE_ERR_INVALID_ARG, "I_shared=%d must be a positive multiple of 8", c.I_shared);
     if (c.act_dtype < MOE_F32 || c.act_dtype > MOE_FP8_E4M3)
         return fail(MOE_ERR_INVALID_ARG, "act_dtype=%d", c.act_dtype);
-    if (c.w_dtype != c.act_dtype)
-        return fail(MOE_ERR_UNSUPPORTED, "w_dtype=%d differs from act_dtype=%d", c.w_dtype, c.act_dtype);
+    const bool fp8x = c.act_dtype == MOE_BF16 && c.w_dtype == MOE_FP8_E4M3;  // fp8 experts, bf16 activations
+    if (c.w_dtype != c.act_dtype && !fp8x)
+        return fail(MOE_ERR_UNSUPPORTED, "w_dtype=%d with act_dtype=%d", c.w_dtype, c.act_dtype);
     if (c.y_dtype != MOE_F32 && c.y_dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "y_dtype=%d", c.y_dtype);
     if (c.out_dtype != MOE_F32 && c.out_dtype != MOE_BF16)
         return fail(MOE_ERR_INVALID_ARG, "out_dtype=%d", c.out_dtype);
-    if (c.act_dtype == MOE_FP8_E4M3) {
+    if (c.w_dtype == MOE_FP8_E4M3) {
         if (c.H % 128 || c.I % 128)
             return fail(MOE_ERR_INVALID_ARG, "fp8 needs H and I multiples of 128 (H=%d, I=%d)", c.H, c.I);
-        if (c.has_shared) return fail(MOE_ERR_UNSUPPORTED, "fp8 with a shared expert");
         if (c.H > 16384 || c.I > 16384)
             return fail(MOE_ERR_UNSUPPORTED, "fp8 supports H and I up to 16384 (H=%d, I=%d)", c.H, c.I);
+        if (c.has_shared && !fp8x) return fail(MOE_ERR_UNSUPPORTED, "fp8 activations with a shared expert");
+        if (c.has_shared && (c.I_shared % 128 || c.I_shared > 16384))
+            return fail(MOE_ERR_UNSUPPORTED, "fp8 needs I_shared a multiple of 128 up to 16384 (I_shared=%d)",
+                        c.I_shared);
     }
-    if (c.act_dtype == MOE_BF16) {
+    if (c.act_dtype == MOE_BF16 && !fp8x) {
         // the bf16 GEMMs address one expert's matrices (and, indexed, all of x)
         // through buffer descriptors below 2 GiB
         auto mat = [&](int I) { return (int64_t)((I + 127) / 128) * 128 * 2 * ((c.H + 31) / 32) * 32 * 2; };
@@ -216,16 +220,42 @@ moe_cfg layer_stage_cfg(const moe_cfg& c) {
     return s;
 }
 
+// Fp8 experts (bf16 activations, e4m3 weights): the layer quantises x per
+// token, then runs the stages on the fp8 cfg of the quantised rows -- the
+// routed experts as one grouped FFN, the shared expert as a second one over
+// the T quantised tokens (one group).
+bool fp8_experts(const moe_cfg& c) { return c.act_dtype == MOE_BF16 && c.w_dtype == MOE_FP8_E4M3; }
+moe_cfg fp8_routed_cfg(const moe_cfg& c) {
+    moe_cfg q = c;
+    q.act_dtype = q.w_dtype = MOE_FP8_E4M3;
+    q.has_shared = 0;
+    q.I_shared = 0;
+    q.m_tile = 16;
+    q.x_layout = MOE_LAYOUT_ROWMAJOR;
+    return q;
+}
+moe_cfg fp8_shared_cfg(const moe_cfg& c) {
+    moe_cfg q = fp8_routed_cfg(c);
+    q.E = q.k = q.n_groups = q.topk_groups = 1;
+    q.I = c.I_shared;
+    q.m_tile = 1;
+    return q;
+}
+
 struct LayerCarve {
     int32_t *ids, *counts, *offsets, *row_src, *tok_row;
     float* topk_w;
     void *x_perm, *y_rows, *y_shared, *scratch;
+    uint8_t* x_q;                // fp8 experts: x quantised [T][H]
+    float *x_s, *x_perm_scale;   // ... its scales [T][H / 128] and those of x_perm
+    int32_t* offsets_sh;         // ... {0, T}
     size_t bytes;
 };
 LayerCarve layer_carve(const moe_cfg& c, void* p) {
     Carve cv(p);
     LayerCarve l{};
-    const moe_cfg cs = layer_stage_cfg(c);
+    const bool f8 = fp8_experts(c);
+    const moe_cfg cs = f8 ? fp8_routed_cfg(c) : layer_stage_cfg(c);
     const int64_t rows = max_rows_of(cs);
     const size_t tk = (size_t)c.T * c.k;
     l.ids = cv.take<int32_t>(tk);
@@ -240,6 +270,16 @@ LayerCarve layer_carve(const moe_cfg& c, void* p) {
     size_t scratch = route_ws(c);
     size_t pb = permute_carve(cs, nullptr).bytes;
     size_t fb = ffn_carve(cs, rows, nullptr).bytes;
+    if (f8) {
+        l.x_q = cv.take<uint8_t>((size_t)c.T * c.H);
+        l.x_s = cv.take<float>((size_t)c.T * (c.H / 128));
+        l.x_perm_scale = cv.take<float>((size_t)rows * (c.H / 128));
+        l.offsets_sh = cv.take<int32_t>(2);
+        if (c.has_shared) {
+            const size_t fs = ffn_carve(fp8_shared_cfg(c), c.T, nullptr).bytes;
+            if (fs > fb) fb = fs;
+        }
+    }
     if (pb > scratch) scratch = pb;
     if (fb > scratch) scratch = fb;
     l.scratch = cv.take<char>(scratch);
@@ -266,11 +306,12 @@ moe_status check_weights(const moe_cfg& c, const moe_weights* w) {
     if (w->layout != MOE_LAYOUT_ROWMAJOR && w->layout != MOE_LAYOUT_TILED)
         return fail(MOE_ERR_INVALID_ARG, "w->layout=%d", w->layout);
     const bool tiled = w->layout == MOE_LAYOUT_TILED;
-    if (tiled && c.act_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "tiled weights are bf16 only");
+    if (tiled && (c.act_dtype != MOE_BF16 || c.w_dtype != MOE_BF16))
+        return fail(MOE_ERR_UNSUPPORTED, "tiled weights are bf16 only");
     REQUIRE(w->w_gate, "w->w_gate");
     if (!tiled) REQUIRE(w->w_up, "w->w_up");
     REQUIRE(w->w_down, "w->w_down");
-    if (c.act_dtype == MOE_FP8_E4M3) {
+    if (c.w_dtype == MOE_FP8_E4M3) {
         REQUIRE(w->s_gate, "w->s_gate");
         REQUIRE(w->s_up, "w->s_up");
         REQUIRE(w->s_down, "w->s_down");
@@ -279,6 +320,11 @@ moe_status check_weights(const moe_cfg& c, const moe_weights* w) {
         REQUIRE(w->sh_gate, "w->sh_gate");
         if (!tiled) REQUIRE(w->sh_up, "w->sh_up");
         REQUIRE(w->sh_down, "w->sh_down");
+        if (c.w_dtype == MOE_FP8_E4M3) {
+            REQUIRE(w->sh_s_gate, "w->sh_s_gate");
+            REQUIRE(w->sh_s_up, "w->sh_s_up");
+            REQUIRE(w->sh_s_down, "w->sh_s_down");
+        }
     }
     return MOE_OK;
 }
@@ -324,6 +370,34 @@ moe_status ffn_enqueue(const moe_cfg& c, int64_t n_rows_cap, const void* x_rows,
         e = moe::launch_gemm_fp8(c, f.max_tiles, n_rows_cap, x_rows, x_scale, offsets, w, y_rows, f.wk, f.h,
                                  f.h_scale, s);
     if (e != hipSuccess) return hip_fail(e, "moe_grouped_ffn");
+    return MOE_OK;
+}
+
+// The rest of moe_layer for fp8 experts (routing done): quantise x, dispatch
+// the fp8 rows, the routed and the shared grouped FFN, combine.
+moe_status layer_fp8_experts(const moe_cfg& c, const moe_weights& w, const void* x, void* out,
+                             const LayerCarve& l, hipStream_t s) {
+    const moe_cfg cq = fp8_routed_cfg(c);
+    hipError_t e = moe::launch_quant_rows_e4m3(x, c.T, c.H, l.x_q, l.x_s, s);
+    if (e != hipSuccess) return hip_fail(e, "moe_layer (quantise)");
+    moe_status st = permute_enqueue(cq, l.x_q, l.x_s, l.ids, l.counts, l.offsets, l.row_src, l.tok_row, l.x_perm,
+                                    l.x_perm_scale, l.scratch, s);
+    if (st != MOE_OK) return st;
+    st = ffn_enqueue(cq, max_rows_of(cq), l.x_perm, l.x_perm_scale, l.offsets, nullptr, w, nullptr, l.y_rows,
+                     nullptr, l.scratch, s);
+    if (st != MOE_OK) return st;
+    if (c.has_shared) {
+        const moe_cfg c1 = fp8_shared_cfg(c);
+        const moe_weights ws1{w.sh_gate, w.sh_up, w.sh_down, w.sh_s_gate, w.sh_s_up, w.sh_s_down,
+                              nullptr, nullptr, nullptr, MOE_LAYOUT_ROWMAJOR, nullptr, nullptr, nullptr};
+        e = moe::launch_offsets_one_group(l.offsets_sh, c.T, s);
+        if (e != hipSuccess) return hip_fail(e, "moe_layer (shared offsets)");
+        st = ffn_enqueue(c1, c.T, l.x_q, l.x_s, l.offsets_sh, nullptr, ws1, nullptr, l.y_shared, nullptr,
+                         l.scratch, s);
+        if (st != MOE_OK) return st;
+    }
+    e = moe::launch_combine(c, l.y_rows, l.tok_row, l.topk_w, l.y_shared, out, s);
+    if (e != hipSuccess) return hip_fail(e, "moe_layer (combine)");
     return MOE_OK;
 }
 
@@ -422,6 +496,9 @@ moe_status moe_grouped_ffn(const moe_cfg* cfg, int64_t n_rows_cap, const void* x
     const moe_cfg& c = *cfg;
     if (n_rows_cap < 0 || n_rows_cap > kMaxRows)
         return fail(MOE_ERR_INVALID_ARG, "n_rows_cap=%lld must be in [0, 2^30)", (long long)n_rows_cap);
+    if (fp8_experts(c))
+        return fail(MOE_ERR_UNSUPPORTED, "fp8 experts take fp8 rows: quantise with moe_quantize_fp8 and call "
+                                         "moe_grouped_ffn with act_dtype = MOE_FP8_E4M3");
     REQUIRE(expert_offsets, "expert_offsets");
     if ((st = check_weights(c, w)) != MOE_OK) return st;
     if (n_rows_cap > 0) {
@@ -510,6 +587,23 @@ moe_status moe_combine(const moe_cfg* cfg, const void* y_rows, const int32_t* to
     return MOE_OK;
 }
 
+moe_status moe_quantize_fp8(const moe_cfg* cfg, const void* x, uint8_t* x_q, float* x_scale, void* stream) {
+    moe_status st = check_cfg(cfg);
+    if (st != MOE_OK) return st;
+    const moe_cfg& c = *cfg;
+    if (c.act_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "moe_quantize_fp8 takes bf16 rows");
+    if (c.H % 128) return fail(MOE_ERR_INVALID_ARG, "moe_quantize_fp8 needs H a multiple of 128 (H=%d)", c.H);
+    if (c.T == 0) return MOE_OK;
+    REQUIRE(x, "x");
+    REQUIRE(x_q, "x_q");
+    REQUIRE(x_scale, "x_scale");
+    REQUIRE_A16(x, "x");
+    if (reinterpret_cast<uintptr_t>(x_q) % 8) return fail(MOE_ERR_INVALID_ARG, "x_q is not 8-byte aligned");
+    hipError_t e = moe::launch_quant_rows_e4m3(x, c.T, c.H, x_q, x_scale, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "moe_quantize_fp8");
+    return MOE_OK;
+}
+
 moe_status moe_layer(const moe_cfg* cfg, const void* w_router, const float* bias, const moe_weights* w,
                      const void* x, void* out, void* ws, size_t ws_bytes, void* stream) {
     moe_status st = check_cfg(cfg);
@@ -520,16 +614,21 @@ moe_status moe_layer(const moe_cfg* cfg, const void* w_router, const float* bias
     if ((st = check_weights(c, w)) != MOE_OK) return st;
     REQUIRE(x, "x");
     REQUIRE(out, "out");
+    if (fp8_experts(c)) {
+        REQUIRE_A16(x, "x");
+        if (w->layout != MOE_LAYOUT_ROWMAJOR) return fail(MOE_ERR_UNSUPPORTED, "fp8 experts take row-major weights");
+    }
     LayerCarve l = layer_carve(c, ws);
     if ((st = check_ws(ws, ws_bytes, l.bytes)) != MOE_OK) return st;
     if (c.T == 0) return MOE_OK;
-    const moe_cfg cs = layer_stage_cfg(c);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = moe::launch_router_logits(c, x, w_router, static_cast<float*>(l.scratch), s);
     if (e != hipSuccess) return hip_fail(e, "moe_layer (router)");
     e = moe::launch_route_select(c, static_cast<float*>(l.scratch), moe::router_splits(c), bias, nullptr, l.ids,
                                  l.topk_w, s);
     if (e != hipSuccess) return hip_fail(e, "moe_layer (select)");
+    if (fp8_experts(c)) return layer_fp8_experts(c, *w, x, out, l, s);
+    const moe_cfg cs = layer_stage_cfg(c);
     st = permute_enqueue(cs, x, nullptr, l.ids, l.counts, l.offsets, l.row_src, l.tok_row, l.x_perm, nullptr,
                          l.scratch, s);
     if (st != MOE_OK) return st;

@@ -142,6 +142,13 @@ hipError_t launch_permute(const moe_cfg& c, const void* x, const float* x_scale,
                           void* x_perm, float* x_perm_scale, int64_t max_rows, PermuteWs ws,
                           PermuteLayout lay, hipStream_t s);
 
+// bf16 rows [T][H] -> e4m3 codes [T][H] and fp32 scales [T][H / 128], one
+// scale per 1 x 128 block (H a multiple of 128; x, q 16- and 8-byte aligned).
+hipError_t launch_quant_rows_e4m3(const void* x, int T, int H, uint8_t* q, float* sc, hipStream_t s);
+// offsets = {0, n}: one expert group covering rows [0, n) (two fill kernels,
+// no memset, so the sequence can be captured in a graph).
+hipError_t launch_offsets_one_group(int32_t* offsets, int n, hipStream_t s);
+
 // Grouped FFN building blocks (gemm_bf16.hip, gemm_fp8.hip, gemm_f32.hip).
 // Tile heights (rows) and the h / output columns one tile covers in GEMM1 /
 // GEMM2; fp8 tiles cover the bf16 tiles' columns.

@@ -186,6 +186,48 @@ perm_zero(const int32_t* __restrict__ row_src, uint8_t* __restrict__ x_perm, flo
         for (int c = lane; c < n_scale; c += 64) x_perm_scale[(size_t)r * n_scale + c] = 0.0f;
 }
 
+// Per-token quantisation of bf16 activations to OCP e4m3 with one fp32 scale
+// per 1 x 128 block: s = max|x| / 448 over the block (1 for an all-zero
+// block), q = e4m3_rne_sat(x / s), both divisions in fp32 (the rule the fp8
+// grouped GEMM applies to h, read for the activations of a layer whose experts
+// are fp8).  16 lanes own a block, 8 values each (16-byte loads, 8-byte
+// stores); a workgroup of 256 threads covers 16 blocks of the [T][H / 128]
+// grid, in row order.
+__global__ void __launch_bounds__(256)
+quant_rows_e4m3(const uint16_t* __restrict__ x, int64_t n_blocks, int nb, int H, uint8_t* __restrict__ q,
+                float* __restrict__ sc) {
+    const int64_t b = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);  // block id: row b / nb, column block b % nb
+    const int l = threadIdx.x & 15;
+    if (b >= n_blocks) return;  // whole 16-lane groups leave together
+    const int64_t row = b / nb;
+    const int cb = (int)(b - row * nb);
+    const size_t off = (size_t)row * H + (size_t)cb * 128 + (size_t)l * 8;
+    const uint4 raw = *reinterpret_cast<const uint4*>(x + off);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = bf16_to_f32((uint16_t)(w[i] & 0xFFFFu));
+        v[2 * i + 1] = bf16_to_f32((uint16_t)(w[i] >> 16));
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+    m = fmaxf(m, __shfl_xor(m, 1, 16));
+    m = fmaxf(m, __shfl_xor(m, 2, 16));
+    m = fmaxf(m, __shfl_xor(m, 4, 16));
+    m = fmaxf(m, __shfl_xor(m, 8, 16));
+    const float s = m > 0.0f ? m / 448.0f : 1.0f;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        lo |= (uint32_t)f32_to_e4m3(v[i] / s) << (8 * i);
+        hi |= (uint32_t)f32_to_e4m3(v[4 + i] / s) << (8 * i);
+    }
+    *reinterpret_cast<uint2*>(q + off) = make_uint2(lo, hi);
+    if (l == 0) sc[b] = s;
+}
+
 }  // namespace
 
 int permute_blocks(int T) { return (T + PB - 1) / PB; }
@@ -225,6 +267,22 @@ hipError_t launch_permute(const moe_cfg& c, const void* x, const float* x_scale,
     if (m_tile > 1)
         hipLaunchKernelGGL(perm_zero, dim3((unsigned)((max_rows + 3) / 4)), dim3(256), 0, s, row_src,
                            static_cast<uint8_t*>(x_perm), xps, max_rows, row_bytes, n_scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_offsets_one_group(int32_t* offsets, int n, hipStream_t s) {
+    hipLaunchKernelGGL(fill_i32, dim3(1), dim3(256), 0, s, offsets, (int64_t)1, 0);
+    hipLaunchKernelGGL(fill_i32, dim3(1), dim3(256), 0, s, offsets + 1, (int64_t)1, (int32_t)n);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_rows_e4m3(const void* x, int T, int H, uint8_t* q, float* sc, hipStream_t s) {
+    const int nb = H / 128;
+    const int64_t n_blocks = (int64_t)T * nb;
+    if (n_blocks == 0) return hipSuccess;
+    const int64_t grid = (n_blocks + 15) / 16;
+    hipLaunchKernelGGL(quant_rows_e4m3, dim3((unsigned)grid), dim3(256), 0, s, static_cast<const uint16_t*>(x),
+                       n_blocks, nb, H, q, sc);
     return hipGetLastError();
 }
 

@@ -99,7 +99,13 @@ typedef enum moe_stage {
  *   has_shared   1: a shared expert (weight 1) is added to every token
  *   I_shared     intermediate size of the shared expert
  *   act_dtype    x dtype (MOE_F32, MOE_BF16, or MOE_FP8_E4M3 for the grouped FFN)
- *   w_dtype      expert weight dtype (equal to act_dtype)
+ *   w_dtype      expert weight dtype: equal to act_dtype, or MOE_FP8_E4M3
+ *                with act_dtype MOE_BF16 ("fp8 experts": moe_layer
+ *                quantises x per token with moe_quantize_fp8's rule and runs
+ *                the experts in fp8; moe_grouped_ffn refuses this pair -- call
+ *                it on the quantised rows with act_dtype = w_dtype =
+ *                MOE_FP8_E4M3).  fp8 weights need H, I (and I_shared) to be
+ *                multiples of 128 up to 16384.
  *   y_dtype      dtype of the per-row expert outputs (y_rows, y_shared):
  *                MOE_F32 or MOE_BF16
  *   out_dtype    dtype of the layer output: MOE_F32 or MOE_BF16
@@ -135,7 +141,9 @@ typedef struct moe_cfg {
 /* Expert weights.  For fp8 weights the s_* arrays hold one fp32 scale per
  * 128 x 128 block: s_gate, s_up [E][I/128][H/128]; s_down [E][H/128][I/128]
  * (dequantised weight = e4m3 value * block scale); NULL otherwise.  sh_* are
- * the shared expert's matrices (NULL when has_shared == 0; bf16/fp32 only).
+ * the shared expert's matrices (NULL when has_shared == 0), sh_s_* their
+ * block scales (fp8 experts only: [I_shared/128][H/128] for gate and up,
+ * [H/128][I_shared/128] for down).
  * layout MOE_LAYOUT_ROWMAJOR: the matrices as above.  layout MOE_LAYOUT_TILED
  * (bf16 only): w_gate and sh_gate point to the gate+up matrices and w_down and
  * sh_down to the down matrices that moe_tile_weights writes, rearranged into
@@ -148,6 +156,7 @@ typedef struct moe_weights {
     const float *s_gate, *s_up, *s_down;
     const void *sh_gate, *sh_up, *sh_down;
     int32_t layout;
+    const float *sh_s_gate, *sh_s_up, *sh_s_down;
 } moe_weights;
 
 /* Checks a configuration on the host (no HIP call).  MOE_OK if every entry
@@ -283,6 +292,15 @@ moe_status moe_grouped_ffn(const moe_cfg *cfg, int64_t n_rows_cap, const void *x
 moe_status moe_combine(const moe_cfg *cfg, const void *y_rows, const int32_t *tok_row,
                        const float *topk_w, const void *y_shared, void *out, void *stream);
 
+/* Per-token quantisation of activations for fp8 experts (the DeepSeek-V3
+ * page's fp8 MoE GEMMs, "fp8 DeepGEMM"; the per-token 1 x 128 activation
+ * scales of its fp8 recipe).  For each row t and 128-column block b of
+ * x [T][H] bf16: s = max|x| / 448 over the block (1 when the block is all
+ * zero), q = e4m3_rne_sat(x / s), the divisions in fp32; x_q [T][H] OCP e4m3
+ * codes, x_scale [T][H/128] fp32 (x, x_q 16- and 8-byte aligned, device).
+ * Takes act_dtype MOE_BF16 and H a multiple of 128. */
+moe_status moe_quantize_fp8(const moe_cfg *cfg, const void *x, uint8_t *x_q, float *x_scale, void *stream);
+
 /* The whole layer: moe_route -> moe_permute -> moe_grouped_ffn -> moe_combine,
  * enqueued on `stream` with no host synchronisation.  x [T][H] in act_dtype
  * (F32 or BF16); out [T][H] in out_dtype.  All intermediates live in ws.
@@ -290,6 +308,12 @@ moe_status moe_combine(const moe_cfg *cfg, const void *y_rows, const int32_t *to
  * MOE_LAYOUT_INDEXED, whatever cfg->m_tile and cfg->x_layout say (those shape
  * the standalone stage calls only); the result equals that of the four stage
  * calls made with those two fields.  w may be row-major or tiled.
+ * Fp8 experts (act_dtype MOE_BF16, w_dtype MOE_FP8_E4M3, row-major e4m3
+ * weights with block scales, x 16-byte aligned): the route on bf16 x, then
+ * moe_quantize_fp8 of x, moe_permute of the e4m3 rows and their scales
+ * (m_tile 16, row-major), the fp8 grouped FFN over the routed rows and,
+ * with a shared expert, a second one over the T quantised tokens, then
+ * moe_combine.
  * ws: moe_workspace_bytes(cfg, MOE_STAGE_LAYER). */
 moe_status moe_layer(const moe_cfg *cfg, const void *w_router, const float *bias,
                      const moe_weights *w, const void *x, void *out, void *ws,

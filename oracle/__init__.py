@@ -126,6 +126,28 @@ def e4m3_rne_sat(values) -> np.ndarray:
                     dtype=np.uint8).reshape(v.shape)
 
 
+def quantize_rows_e4m3(x):
+    """Per-token 1 x 128 quantisation of activations for fp8 experts.  For each
+    row and block of 128 columns: s = fp32(max|x|) / 448 in fp32 (1 for an
+    all-zero block), code = e4m3_rne_sat(fp32(x / s)) -- the rule the fp8
+    recipe of the DeepSeek-V3 page applies to activations (per-token 1 x 128
+    scales) and the one this oracle applies to the SwiGLU intermediate (S9).
+    x: bf16 bit patterns (uint16) or fp32, [n][H] with H a multiple of 128.
+    Returns (codes uint8 [n][H], scales float32 [n][H/128])."""
+    x = np.asarray(x)
+    if x.dtype == np.uint16:  # bf16: the top half of an fp32
+        x = (x.astype(np.uint32) << 16).view(np.float32)
+    x = x.astype(np.float32)
+    n, H = x.shape
+    assert H % 128 == 0
+    blk = x.reshape(n, H // 128, 128)
+    amax = np.abs(blk).max(axis=2)
+    s = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    v = (blk / s[:, :, None]).astype(np.float32)
+    q = e4m3_rne_sat(v.reshape(-1)).reshape(n, H)
+    return q, s
+
+
 def bf16_rne(values) -> np.ndarray:
     L = lib()
     v = np.asarray(values, dtype=np.float64)

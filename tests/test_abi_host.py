@@ -20,7 +20,7 @@ def _declared():
         if f.endswith(".h"):
             src = open(os.path.join(inc, f)).read()
             src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-            names |= set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src))
+            names |= set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src))
     return names
 
 
@@ -86,6 +86,50 @@ def test_fp8_needs_128_multiples():
     assert m.moe_validate(c) == m.MOE_OK
     c = m.make_cfg(T=64, H=7168 + 64, E=8, k=1, I=2048, act_dtype=m.MOE_FP8_E4M3)
     assert m.moe_validate(c) == m.MOE_ERR_INVALID_ARG
+
+
+def test_fp8_experts_cfg():
+    """bf16 activations with e4m3 experts: accepted by moe_validate and sized
+    for the layer; needs 128-multiples (I_shared too); moe_grouped_ffn refuses
+    the pair (it takes the quantised rows); moe_quantize_fp8 checks its
+    arguments before any launch."""
+    kw = dict(T=64, H=7168, E=256, k=8, I=2048, n_groups=8, topk_groups=4, has_shared=True, I_shared=2048,
+              act_dtype=m.MOE_BF16, w_dtype=m.MOE_FP8_E4M3, y_dtype=m.MOE_BF16)
+    c = m.make_cfg(**kw)
+    assert m.moe_validate(c) == m.MOE_OK
+    bf = m.make_cfg(**dict(kw, w_dtype=m.MOE_BF16))
+    # the layer holds the quantised tokens and their scales besides the bf16 layer's buffers
+    assert m.moe_workspace_bytes(c, m.MOE_STAGE_LAYER) > 64 * 7168
+    assert m.moe_validate(m.make_cfg(**dict(kw, I_shared=2048 + 64))) == m.MOE_ERR_UNSUPPORTED
+    assert m.moe_validate(m.make_cfg(**dict(kw, I=2048 + 64))) == m.MOE_ERR_INVALID_ARG
+    assert m.moe_validate(m.make_cfg(**dict(kw, act_dtype=m.MOE_F32))) == m.MOE_ERR_UNSUPPORTED
+    assert m.moe_validate(bf) == m.MOE_OK
+    lib = m._ffi.lib()
+    fake = ctypes.c_void_p(0x100000)
+    w = m.moe_weights(w_gate=0x100000, w_up=0x100000, w_down=0x100000, s_gate=0x100000, s_up=0x100000,
+                      s_down=0x100000)
+    st = lib.moe_grouped_ffn(ctypes.byref(c), 64, fake, fake, fake, None, ctypes.byref(w), fake, fake, fake,
+                             fake, 1 << 40, None)
+    assert st == m.MOE_ERR_UNSUPPORTED and "moe_quantize_fp8" in m.moe_last_error()
+    # the shared expert's block scales are required
+    st = lib.moe_layer(ctypes.byref(c), fake, None, ctypes.byref(w), fake, fake, fake, 1 << 40, None)
+    assert st == m.MOE_ERR_INVALID_ARG and "sh_gate" in m.moe_last_error()
+    w.sh_gate = w.sh_up = w.sh_down = 0x100000
+    st = lib.moe_layer(ctypes.byref(c), fake, None, ctypes.byref(w), fake, fake, fake, 1 << 40, None)
+    assert st == m.MOE_ERR_INVALID_ARG and "sh_s_gate" in m.moe_last_error()
+    w.sh_s_gate = w.sh_s_up = w.sh_s_down = 0x100000
+    st = lib.moe_layer(ctypes.byref(c), fake, None, ctypes.byref(w), ctypes.c_void_p(0x100008), fake, fake,
+                       1 << 40, None)
+    assert st == m.MOE_ERR_INVALID_ARG and "aligned" in m.moe_last_error()
+    # moe_quantize_fp8
+    st = lib.moe_quantize_fp8(ctypes.byref(c), ctypes.c_void_p(0x100008), fake, fake, None)
+    assert st == m.MOE_ERR_INVALID_ARG and "aligned" in m.moe_last_error()
+    st = lib.moe_quantize_fp8(ctypes.byref(c), fake, None, fake, None)
+    assert st == m.MOE_ERR_INVALID_ARG and "x_q" in m.moe_last_error()
+    f8 = m.make_cfg(T=64, H=128, E=8, k=1, I=128, act_dtype=m.MOE_FP8_E4M3, y_dtype=m.MOE_BF16)
+    assert lib.moe_quantize_fp8(ctypes.byref(f8), fake, fake, fake, None) == m.MOE_ERR_UNSUPPORTED
+    z = m.make_cfg(**dict(kw, T=0))
+    assert lib.moe_quantize_fp8(ctypes.byref(z), None, None, None, None) == m.MOE_OK
 
 
 def test_status_strings():

@@ -1,0 +1,122 @@
+"""GPU parity of fp8 experts: moe_quantize_fp8 and moe_layer with bf16
+activations and e4m3 expert weights, against the oracle.
+
+The per-token quantisation is decided in fp32 on both sides from the same bf16
+values, so its codes and scales are compared bit for bit.  The layer is
+compared with the oracle composed step by step: routing on the same margin
+cases as the bf16 layer tests (ids bit-exact), the oracle's quantisation of x,
+each chosen expert's fp8 block-scaled SwiGLU FFN on its token rows (the shared
+expert on every token), then the weighted combine.  Bound: max|err| / rms(ref)
+<= 4e-2, the fp8 tolerance; the rms of the error is also held under 1e-2."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import expert_layer_amd as moe
+import oracle
+import synth
+from tests._cases import dev, lib_cfg, rel_err, route_kw, router_case
+from tests._np import e4m3_f64, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def test_quantize_fp8_is_bit_exact():
+    T, H = 131, 7168
+    g = torch.Generator(device="cpu").manual_seed(11)
+    x = torch.randn((T, H), generator=g) * torch.exp(2.0 * torch.randn((T, H // 128, 1), generator=g)).repeat(
+        1, 1, 128).view(T, H)
+    x[3, :128] = 0.0                       # an all-zero block: scale 1, zero codes
+    x[5, 128:256] *= 1e-30                 # a block of tiny (normal fp32) values: a tiny scale
+    # exact round-to-nearest-even ties: e4m3 midpoints times 2^3, with 448 * 2^3 the block maximum
+    mids = np.array([(a + b) / 2 for a, b in zip(e4m3_f64(np.arange(0, 0x7E)), e4m3_f64(np.arange(1, 0x7F)))])
+    blk = np.resize(mids, 128) * 8.0
+    blk[0] = 448.0 * 8.0
+    x[9, 512:640] = torch.from_numpy(blk)
+    x[9, 640:768] = -torch.from_numpy(blk)
+    x[11, 768:896] = 1e30                  # a constant block of large values: every code 448
+    xb = x.to(torch.bfloat16).to(dev())
+    c = moe.make_cfg(T=T, H=H, E=8, k=1, I=128)
+    xq = torch.full((T, H), 0xFF, dtype=torch.uint8, device=dev())
+    xs = torch.full((T, H // 128), float("nan"), device=dev())
+    moe.moe_quantize_fp8(c, xb, xq, xs)
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quantize_rows_e4m3(to_np(xb))
+    assert np.array_equal(xs.cpu().numpy(), s_ref)
+    assert np.array_equal(xq.cpu().numpy(), q_ref)
+
+
+_W8 = {}
+
+
+def _fp8_weights(s):
+    """Routed fp8 experts stacked on the device ([E][I][H] codes, [E][I/128][H/128]
+    scales, ...) and the shared expert's, drawn by synth (block scales with the
+    survey's jitter)."""
+    key = (s.name, s.E, s.I, s.H, s.I_shared, s.seed)
+    if key not in _W8:
+        _W8.clear()
+        torch.cuda.empty_cache()
+        d = dev()
+        wg = torch.empty((s.E, s.I, s.H), dtype=torch.uint8, device=d)
+        wu, wd = torch.empty_like(wg), torch.empty((s.E, s.H, s.I), dtype=torch.uint8, device=d)
+        sg = torch.empty((s.E, s.I // 128, s.H // 128), device=d)
+        su, sd = torch.empty_like(sg), torch.empty((s.E, s.H // 128, s.I // 128), device=d)
+        for e in range(s.E):
+            g, gs, u, us, dn, ds = synth.fp8_expert_weights(s, e, d)
+            wg[e], sg[e], wu[e], su[e], wd[e], sd[e] = g, gs, u, us, dn, ds
+        sh = None
+        if s.shared:
+            sh = synth.fp8_expert_weights(s.with_(I=s.I_shared), s.E, d)
+        _W8[key] = ((wg, sg, wu, su, wd, sd), sh)
+    return _W8[key]
+
+
+def _oracle_fp8_layer(s, rc, w8):
+    (wg, sg, wu, su, wd, sd), sh = w8
+    T, k = rc["xh"].shape[0], s.k
+    ids, w = oracle.route_select(rc["logits"], k, renormalize=s.renormalize, routed_scale=s.routed_scale,
+                                 bias=rc["bh"], **route_kw(s))
+    xq, xs = oracle.quantize_rows_e4m3(rc["xh"])
+    y_rows = np.zeros((T * k, s.H))
+    for e in np.unique(ids):
+        ti, j = np.nonzero(ids == e)
+        y_rows[ti * k + j] = oracle.expert_ffn_fp8(xq[ti], xs[ti], to_np(wg[e]), to_np(sg[e]), to_np(wu[e]),
+                                                   to_np(su[e]), to_np(wd[e]), to_np(sd[e]))
+    y_sh = None
+    if sh is not None:
+        y_sh = oracle.expert_ffn_fp8(xq, xs, *(to_np(t) for t in sh))
+    tok_row = np.arange(T * k, dtype=np.int32).reshape(T, k)
+    return oracle.combine(y_rows, tok_row, w, y_sh)
+
+
+def _small_shape():
+    return synth.config("c3_dsv3_bf16").with_(H=512, I=256, E=16, k=4, n_groups=4, topk_groups=2, I_shared=384)
+
+
+@pytest.mark.parametrize("shape,T,ydt", [
+    ("small", 77, moe.MOE_F32),
+    ("small", 77, moe.MOE_BF16),
+    ("c3", 24, moe.MOE_BF16),          # DeepSeek-V3 dimensions: 256 fp8 experts and the shared one
+])
+def test_layer_fp8_experts_matches_oracle(shape, T, ydt):
+    s = _small_shape() if shape == "small" else synth.config("c3_dsv3_bf16")
+    rc = router_case(s, T)
+    w8 = _fp8_weights(s)
+    ref = _oracle_fp8_layer(s, rc, w8)
+    (wg, sg, wu, su, wd, sd), sh = w8
+    c = lib_cfg(s, T=T, y_dtype=ydt, out_dtype=moe.MOE_F32)
+    c.w_dtype = moe.MOE_FP8_E4M3
+    w = moe.weights(wg, wu, wd, s_gate=sg, s_up=su, s_down=sd,
+                    sh_gate=sh[0], sh_up=sh[2], sh_down=sh[4], sh_s_gate=sh[1], sh_s_up=sh[3], sh_s_down=sh[5])
+    out = torch.full((T, s.H), float("nan"), device=dev())
+    ws = moe.workspace(c, moe.MOE_STAGE_LAYER, dev())
+    moe.moe_layer(c, rc["w_r"], rc["bias"], w, rc["x"], out, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    assert rel_err(got, ref) <= 4e-2
+    rms = math.sqrt(float(np.mean(ref ** 2)))
+    assert math.sqrt(float(np.mean((got - ref) ** 2))) / rms <= 1e-2

@@ -379,6 +379,41 @@ def test_fp8_h_alternatives_flags_midpoints():
     assert alt_b[1] == 0.125 * 0.5
 
 
+def test_quantize_rows_e4m3_closed_forms():
+    """Blocks built from e4m3 values times 2^k with a +-448 * 2^k element come
+    back as exactly those codes with s = 2^k; an all-zero block has s = 1 and
+    zero codes; negating x flips the sign bit of every nonzero code; random
+    rows dequantise within half an e4m3 step."""
+    rng = np.random.default_rng(31)
+    for k in (-7, 0, 5):
+        mag = rng.integers(1, 0x7F, size=(3, 384)).astype(np.uint8)   # finite nonzero magnitudes
+        mag[:, ::128] = 0x7E                                           # 448 in every block
+        codes = mag | (rng.integers(0, 2, size=mag.shape).astype(np.uint8) << 7)
+        x = (e4m3_f64(codes) * 2.0 ** k).astype(np.float32)
+        q, sc = oracle.quantize_rows_e4m3(x)
+        assert np.array_equal(q, codes)
+        assert np.array_equal(sc, np.full((3, 3), 2.0 ** k, dtype=np.float32))
+        qn, scn = oracle.quantize_rows_e4m3(-x)
+        assert np.array_equal(qn, codes ^ 0x80) and np.array_equal(scn, sc)
+    z = np.zeros((2, 256), dtype=np.float32)
+    z[1, 128:] = rng.standard_normal(128).astype(np.float32)
+    q, sc = oracle.quantize_rows_e4m3(z)
+    assert sc[0, 0] == 1.0 and sc[0, 1] == 1.0 and sc[1, 0] == 1.0 and not (q[:, :128] & 0x7F).any()
+    x = rng.standard_normal((8, 512)).astype(np.float32)
+    bits = (x.view(np.uint32) >> 16).astype(np.uint16)   # bf16 input (truncated): same rule on its values
+    xb = (bits.astype(np.uint32) << 16).view(np.float32)
+    q, sc = oracle.quantize_rows_e4m3(bits)
+    deq = e4m3_f64(q).reshape(8, 4, 128) * sc[:, :, None].astype(np.float64)
+    err = np.abs(deq.reshape(8, 512) - xb.astype(np.float64))
+    # normal e4m3 values carry 3 fraction bits: half a step is 2^-4 of the value; below 2^-6 the step is 2^-9
+    bound = np.maximum(2.0 ** -4 * np.abs(xb.astype(np.float64)), 2.0 ** -10 * np.repeat(sc, 128, axis=1))
+    assert (err <= bound * (1 + 1e-12)).all()
+    # the block maximum maps to 448: it comes back as 448 s, within the rounding of s = fp32(max / 448)
+    dmax = np.abs(deq).reshape(8, 4, 128).max(axis=2)
+    amax = np.abs(xb.astype(np.float64)).reshape(8, 4, 128).max(axis=2)
+    assert (np.abs(dmax - amax) <= 2.0 ** -23 * amax).all()
+
+
 def test_fp8_power_of_two_scales_are_exact():
     """With power-of-two scales the dequantised operands are exact, so the
     fp8 expert equals the bf16/fp64 expert on the decoded values up to the
