@@ -125,7 +125,8 @@ struct Carve {
 
 int ffn_bm(const moe_cfg& c) {
     if (c.act_dtype == MOE_F32) return moe::kFfnBmF32;
-    return c.act_dtype == MOE_FP8_E4M3 ? moe::kFfnBmFp8 : moe::kFfnBmBf16;
+    // fp8 launches run 224- or 128-row tiles: size the tile list for the shorter
+    return c.act_dtype == MOE_FP8_E4M3 ? moe::kFfnBmFp8Small : moe::kFfnBmBf16;
 }
 
 int64_t ffn_max_tiles(const moe_cfg& c, int64_t n_rows_cap) {

@@ -153,7 +153,7 @@ hipError_t launch_offsets_one_group(int32_t* offsets, int n, hipStream_t s);
 // Tile heights (rows) and the h / output columns one tile covers in GEMM1 /
 // GEMM2; fp8 tiles cover the bf16 tiles' columns.
 constexpr int kFfnBmBf16 = 256, kFfnN1Bf16 = 128, kFfnN2Bf16 = 256;
-constexpr int kFfnBmFp8 = 224;
+constexpr int kFfnBmFp8 = 224, kFfnBmFp8Small = 128;
 constexpr int kFfnBmF32 = 64, kFfnN1F32 = 64, kFfnN2F32 = 64;
 
 // Device work lists of the grouped FFN, carved from the workspace.

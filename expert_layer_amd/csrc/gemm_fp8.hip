@@ -38,12 +38,15 @@
 namespace moe {
 namespace {
 
+// BM: the tallest tile (it sizes the LDS); a launch runs tiles of TB = BM or
+// kFfnBmFp8Small rows (the template parameter TB below), a wave owning TB / 32
+// row blocks of 16.
 constexpr int BM = kFfnBmFp8, BN = 256, BK = 128, NTH = 512;
-constexpr int RB = BM / 32;                    // 16-row blocks per wave (a wave owns half the rows)
-constexpr int kChunksA = BM * 8;               // 16-byte chunks of A in one stage
+constexpr int kChunksA = BM * 8;               // 16-byte chunks of A in one stage (the tallest tile)
 constexpr int kChunksB = BN * 8;               // ... of B
 constexpr int kStageA = kChunksA + 72;         // A, then 288 fp32 row scales (see scale_row)
 static_assert(BM % 32 == 0 && BM <= 224, "three A stages and two B stages must fit in 160 KiB of LDS");
+static_assert(kFfnBmFp8Small == 128, "the load slots below are laid out for 4 and 7 row blocks");
 constexpr uint32_t kOOB = 0x40000000u;         // past every descriptor: the load returns zero
 
 typedef __attribute__((address_space(3))) void* lds_t;
@@ -98,14 +101,16 @@ struct Fp8Args {
 };
 
 // Row scales of a stage in LDS: position P = 128 h + 64 (rb / 4) + 4 l + rb % 4
-// holds the scale of tile row scale_row(P) = 112 h + 16 rb + l, so the scales a
-// lane needs (rows 16 rb + lane % 16 of its half h, rb = 0..6) are two 16-byte
-// chunks, and the 16 lanes of a row group read 16 consecutive chunks.
-// Positions whose row lies past the tile (rb = 7 in the second half, P >= 256)
-// hold zeros; in the first half rb = 7 repeats a row of the second.
+// holds the scale of tile row scale_row(P) = (TB / 2) h + 16 rb + l, so the
+// scales a lane needs (rows 16 rb + lane % 16 of its half h) are at most two
+// 16-byte chunks, and the 16 lanes of a row group read 16 consecutive chunks.
+// Positions whose row lies past the tile (the second half's rb >= TB / 32,
+// P >= 256) hold zeros; in the first half such positions repeat rows of the
+// second.
+template <int TB>
 __device__ __forceinline__ int scale_row(int pos) {
     const int rb = ((pos >> 6) & 1) * 4 + (pos & 3), l = (pos >> 2) & 15;
-    return (BM / 2) * (pos >> 7) + 16 * rb + l;
+    return (TB / 2) * (pos >> 7) + 16 * rb + l;
 }
 
 struct Dma {
@@ -115,9 +120,9 @@ struct Dma {
 };
 
 // A loads of stage t into A buffer BUF: 4 chunk loads per lane (8 LDS rows
-// each) and one row-scale load, the same 5 for every wave.  The tile's BM rows
-// take 28 chunk loads; wave 7 repeats wave 0's, writing the same bytes to the
-// same place.  Wave w loads the scales of rows 32 w + [0, 64): each row's
+// each) and one row-scale load, the same 5 for every wave.  The tile's TB rows
+// take TB / 8 chunk loads (28 or 16); the remaining waves repeat the first
+// waves' loads, writing the same bytes to the same place.  Wave w loads the scales of rows 32 w + [0, 64): each row's
 // scale is written by two waves, again the same value, and rows past the tile
 // load zeros.  Every destination is an offset into the buffer itself, so the
 // compiler can tell the buffers apart while the loads are in flight.
@@ -126,13 +131,13 @@ struct Dma {
 // J = 4 the row-scale load (both into A buffer ABUF), J >= 5 the B chunk loads
 // into B buffer BBUF.  A load that is not real (a stage past the end, rows
 // past the tile) carries an offset past its descriptor and loads zeros.
-template <int MODE, int ABUF, int BBUF, int J>
+template <int MODE, int ABUF, int BBUF, int J, int TB>
 __device__ __forceinline__ void dma1(const Dma& d, int t, int wave) {
     const uint32_t k = (uint32_t)t * BK;
     const bool real = t < d.nsteps;
     if constexpr (J < 4) {
         const uint32_t off = (!real || d.va[J] == kOOB) ? kOOB : d.va[J] + k;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ra, (lds_t)(stgA<ABUF>() + ((wave * 4 + J) % (BM / 8)) * 64), 16,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ra, (lds_t)(stgA<ABUF>() + ((wave * 4 + J) % (TB / 8)) * 64), 16,
                                                  off, 0, 0, 0);
     } else if constexpr (J == 4) {
         const uint32_t so = (!real || d.vs == kOOB) ? kOOB : d.vs + (uint32_t)t * 4u;
@@ -148,22 +153,22 @@ __device__ __forceinline__ void dma1(const Dma& d, int t, int wave) {
 }
 
 // The A loads (J = 0..4) of stage t into A buffer BUF.
-template <int MODE, int BUF>
+template <int MODE, int BUF, int TB>
 __device__ __forceinline__ void dma_a(const Dma& d, int t, int wave) {
-    dma1<MODE, BUF, 0, 0>(d, t, wave);
-    dma1<MODE, BUF, 0, 1>(d, t, wave);
-    dma1<MODE, BUF, 0, 2>(d, t, wave);
-    dma1<MODE, BUF, 0, 3>(d, t, wave);
-    dma1<MODE, BUF, 0, 4>(d, t, wave);
+    dma1<MODE, BUF, 0, 0, TB>(d, t, wave);
+    dma1<MODE, BUF, 0, 1, TB>(d, t, wave);
+    dma1<MODE, BUF, 0, 2, TB>(d, t, wave);
+    dma1<MODE, BUF, 0, 3, TB>(d, t, wave);
+    dma1<MODE, BUF, 0, 4, TB>(d, t, wave);
 }
 
 // The B loads (J = 5..8) of stage t into B buffer BUF.
-template <int MODE, int BUF>
+template <int MODE, int BUF, int TB>
 __device__ __forceinline__ void dma_b(const Dma& d, int t, int wave) {
-    dma1<MODE, 0, BUF, 5>(d, t, wave);
-    dma1<MODE, 0, BUF, 6>(d, t, wave);
-    dma1<MODE, 0, BUF, 7>(d, t, wave);
-    dma1<MODE, 0, BUF, 8>(d, t, wave);
+    dma1<MODE, 0, BUF, 5, TB>(d, t, wave);
+    dma1<MODE, 0, BUF, 6, TB>(d, t, wave);
+    dma1<MODE, 0, BUF, 7, TB>(d, t, wave);
+    dma1<MODE, 0, BUF, 8, TB>(d, t, wave);
 }
 
 // vmcnt(9) with the other counters at zero: a stage's A and B loads and
@@ -204,17 +209,20 @@ __device__ __forceinline__ void read_b(int q, int lane, i32x8 (&b)[4]) {
 }
 
 // The loads of stage t spread over the row blocks of a K stage, J after the
-// MFMAs of row block rb: two after each of the first three, one after each of
-// the next three.  A wave that issues all 9 at once stalls until the texture
-// unit has taken them, and the other waves' loads are queued there too.
-template <int MODE, int NA, int NB, int RBI>
+// MFMAs of row block rb -- 7 row blocks: two after each of the first three,
+// one after each of the next three; 4 row blocks: three, then two after each
+// of the rest.  A wave that issues all 9 at once stalls until the texture unit
+// has taken them, and the other waves' loads are queued there too.
+template <int RBN>
+constexpr int slot_start(int r) {
+    return RBN >= 6 ? (r < 3 ? 2 * r : (r + 3 < 9 ? r + 3 : 9)) : (r == 0 ? 0 : (1 + 2 * r < 9 ? 1 + 2 * r : 9));
+}
+template <int MODE, int NA, int NB, int RBI, int TB>
 __device__ __forceinline__ void dma_slot(const Dma& d, int t, int wave) {
-    if constexpr (RBI < 3) {
-        dma1<MODE, NA, NB, 2 * RBI>(d, t, wave);
-        dma1<MODE, NA, NB, 2 * RBI + 1>(d, t, wave);
-    } else if constexpr (RBI < 6) {
-        dma1<MODE, NA, NB, RBI + 3>(d, t, wave);
-    }
+    constexpr int j0 = slot_start<TB / 32>(RBI), j1 = slot_start<TB / 32>(RBI + 1);
+    if constexpr (j0 < j1) dma1<MODE, NA, NB, j0, TB>(d, t, wave);
+    if constexpr (j0 + 1 < j1) dma1<MODE, NA, NB, j0 + 1, TB>(d, t, wave);
+    if constexpr (j0 + 2 < j1) dma1<MODE, NA, NB, j0 + 2, TB>(d, t, wave);
 }
 
 // One K stage for the RB row blocks of 16 starting at tile row r0: every (row
@@ -223,9 +231,10 @@ __device__ __forceinline__ void dma_slot(const Dma& d, int t, int wave) {
 // columns), with the loads of stage t into A buffer NA and B buffer NB issued
 // between them.  Software-pipelined over row blocks: while the four MFMAs of
 // row block rb run, the fragments of rb + 1 are read and rb - 1 is promoted.
-template <int MODE, int BUF, int NA, int NB>
+template <int MODE, int BUF, int NA, int NB, int TB>
 __device__ __forceinline__ void kstep(const Dma& d, int t_stage, int wave, int r0, int lane, const i32x8 (&b)[4],
-                                      float p0, float p1, f32x4 (&acc)[RB][4]) {
+                                      float p0, float p1, f32x4 (&acc)[TB / 32][4]) {
+    constexpr int RB = TB / 32;
     // Every access indexes the stage buffer itself (an integer base plus a
     // constant), so the compiler can tell it from the DMA in flight into the
     // other buffers and adds no wait for it.
@@ -234,25 +243,25 @@ __device__ __forceinline__ void kstep(const Dma& d, int t_stage, int wave, int r
     const int plo = (2 * (lane >> 4)) ^ swz8(l16), phi = plo ^ 1;
     const int ia = (r0 + l16) * 8;                      // row block rb: + rb * 128
     // this lane's row scales: row blocks 0..3 in chunk 32 h + l16, 4..7 in 32 h + 16 + l16
-    const int is = kChunksA + (r0 / (BM / 2)) * 32 + l16;
+    const int is = kChunksA + (r0 / (TB / 2)) * 32 + l16;
     const f32x4 sa_lo = __builtin_bit_cast(f32x4, buf[is]), sa_hi = __builtin_bit_cast(f32x4, buf[is + 16]);
     auto sa = [&](int rb) { return rb < 4 ? sa_lo[rb & 3] : sa_hi[rb & 3]; };
     i32x8 a[2];
     f32x4 t[2][4];
     a[0] = cat(buf[ia + plo], buf[ia + phi]);
     __builtin_amdgcn_sched_barrier(0);
-    static_assert(RB >= 6 && RB <= 8, "the loads of a stage are spread over six row blocks");
+    static_assert(RB == 4 || RB == 7, "the load slots are laid out for 4 and 7 row blocks");
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) t[rb & 1][cb] = mfma16x16x128_fp8(b[cb], a[rb & 1]);
         switch (rb) {  // rb is a constant here: the loop is unrolled
-            case 0: dma_slot<MODE, NA, NB, 0>(d, t_stage, wave); break;
-            case 1: dma_slot<MODE, NA, NB, 1>(d, t_stage, wave); break;
-            case 2: dma_slot<MODE, NA, NB, 2>(d, t_stage, wave); break;
-            case 3: dma_slot<MODE, NA, NB, 3>(d, t_stage, wave); break;
-            case 4: dma_slot<MODE, NA, NB, 4>(d, t_stage, wave); break;
-            case 5: dma_slot<MODE, NA, NB, 5>(d, t_stage, wave); break;
+            case 0: dma_slot<MODE, NA, NB, 0, TB>(d, t_stage, wave); break;
+            case 1: dma_slot<MODE, NA, NB, 1, TB>(d, t_stage, wave); break;
+            case 2: dma_slot<MODE, NA, NB, 2, TB>(d, t_stage, wave); break;
+            case 3: dma_slot<MODE, NA, NB, 3, TB>(d, t_stage, wave); break;
+            case 4: dma_slot<MODE, NA, NB, 4, TB>(d, t_stage, wave); break;
+            case 5: dma_slot<MODE, NA, NB, 5, TB>(d, t_stage, wave); break;
             default: break;
         }
         if (rb + 1 < RB) a[(rb + 1) & 1] = cat(buf[ia + (rb + 1) * 128 + plo], buf[ia + (rb + 1) * 128 + phi]);
@@ -266,11 +275,12 @@ __device__ __forceinline__ void kstep(const Dma& d, int t_stage, int wave, int r
 // others (also by a wave whose half of the tile holds no row: its MFMAs carry
 // the stage's loads, and one load schedule for every wave keeps the compiler's
 // count of loads in flight exact).
-template <int MODE>
+template <int MODE, int TB>
 __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int M, int n0) {
+    constexpr int RB = TB / 32;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int mh = wave >> 2, q = wave & 3, r0 = mh * (BM / 2);
+    const int mh = wave >> 2, q = wave & 3, r0 = mh * (TB / 2);
     const int K = p.K, N = p.N;
     const int KB = K / BK;  // K and N are multiples of 128
     const int NB = N / BK;
@@ -281,7 +291,7 @@ __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int 
     d.rs = make_rsrc(p.a_scale + (size_t)row0 * KB, (uint32_t)M * (uint32_t)KB * 4u);
     {
         const int pos = wave * 32 + lane;  // < 288: the scale area of a stage
-        const int r = pos < 256 ? scale_row(pos) : BM;
+        const int r = pos < 256 ? scale_row<TB>(pos) : TB;
         d.vs = r < M ? (uint32_t)r * (uint32_t)KB * 4u : kOOB;
     }
     // ---- B: GEMM1 the gate and up rows n0 + [0, 128) (LDS quarter j holds gate
@@ -298,8 +308,8 @@ __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int 
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int row = wave * 32 + i * 8 + (lane >> 3);  // LDS row this lane fills (B; A modulo BM)
-        const int arow = row % BM;
+        const int row = wave * 32 + i * 8 + (lane >> 3);  // LDS row this lane fills (B; A modulo TB)
+        const int arow = row % TB;
         const uint32_t logical = (uint32_t)(((lane & 7) ^ swz8(row)) * 16);
         d.va[i] = arow < M ? (uint32_t)arow * (uint32_t)K + (uint32_t)(((lane & 7) ^ swz8(arow)) * 16) : kOOB;
         const int wrow = MODE == 0 ? (wave >> 1) * 32 + i * 8 + (lane >> 3) : row;  // relative to n0
@@ -343,10 +353,10 @@ __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int 
     // stages of one period of both rings and leaves after stage KB - 1.  Loads
     // of stages past the end carry zeros.  Issue order: A0, B0, A1, B1, then per
     // stage s, during its MFMAs: A(s+2) (5 loads), B(s+2) (4).
-    dma_a<MODE, 0>(d, 0, wave);
-    dma_b<MODE, 0>(d, 0, wave);
-    dma_a<MODE, 1>(d, 1, wave);
-    dma_b<MODE, 1>(d, 1, wave);
+    dma_a<MODE, 0, TB>(d, 0, wave);
+    dma_b<MODE, 0, TB>(d, 0, wave);
+    dma_a<MODE, 1, TB>(d, 1, wave);
+    dma_b<MODE, 1, TB>(d, 1, wave);
     i32x8 b[4];
     int s = 0;
     auto stage = [&](auto ab, auto bb) {
@@ -358,7 +368,7 @@ __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int 
         read_b<BB>(q, lane, b);
         wait_lgkm0();
         barrier_lds();  // every wave holds its B fragments of stage s: B buffer s % 2 is free
-        kstep<MODE, AB, (AB + 2) % 3, BB>(d, s + 2, wave, r0, lane, b, p0, p1, acc);
+        kstep<MODE, AB, (AB + 2) % 3, BB, TB>(d, s + 2, wave, r0, lane, b, p0, p1, acc);
     };
     using C0 = std::integral_constant<int, 0>;
     using C1 = std::integral_constant<int, 1>;
@@ -472,7 +482,7 @@ __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int 
     }
 }
 
-template <int MODE>
+template <int MODE, int TB>
 __global__ void __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2, 2)))
 ffn_gemm_fp8(Fp8Args p) {
     const int L = xcd_remap(blockIdx.x, p.n_tiles[0] * p.NT);
@@ -482,7 +492,7 @@ ffn_gemm_fp8(Fp8Args p) {
     const int g = td.x, row0 = td.y, M = td.z - td.y;
     const int n0 = MODE == 0 ? wl.y * (BN / 2) : wl.y * BN;
     if (n0 >= p.N || M <= 0) return;
-    run_tile<MODE>(p, g, row0, M, n0);
+    run_tile<MODE, TB>(p, g, row0, M, n0);
 }
 
 }  // namespace
@@ -490,7 +500,13 @@ ffn_gemm_fp8(Fp8Args p) {
 hipError_t launch_gemm_fp8(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_cap, const void* x_rows,
                            const float* x_scale, const int32_t* offsets, const moe_weights& w, void* y_rows,
                            const FfnWork& wk, void* h, float* h_scale, hipStream_t s) {
-    hipError_t e0 = launch_build_tiles(c, offsets, BM, n_rows_cap, wk, s);
+    // Tile height: groups of about 256 rows or fewer (the DeepSeek-V3 layer's
+    // 256 experts, 8 rows a token) fill 128-row tiles; a 224-row tile would
+    // split them into two 128-row tiles and compute 224 rows of each.
+    const int G = c.E + (c.has_shared ? 1 : 0);
+    const bool small = n_rows_cap <= (int64_t)G * 272;
+    const int tb = small ? kFfnBmFp8Small : BM;
+    hipError_t e0 = launch_build_tiles(c, offsets, tb, n_rows_cap, wk, s);
     if (e0 != hipSuccess) return e0;
     Fp8Args a{};
     a.tiles = reinterpret_cast<const int4*>(wk.tiles);
@@ -509,7 +525,10 @@ hipError_t launch_gemm_fp8(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_c
     a.K = c.H;
     a.N = c.I;
     const int64_t grid1 = max_tiles * wk.nt1;
-    hipLaunchKernelGGL(ffn_gemm_fp8<0>, dim3((unsigned)grid1), dim3(NTH), 0, s, a);
+    if (small)
+        hipLaunchKernelGGL((ffn_gemm_fp8<0, kFfnBmFp8Small>), dim3((unsigned)grid1), dim3(NTH), 0, s, a);
+    else
+        hipLaunchKernelGGL((ffn_gemm_fp8<0, BM>), dim3((unsigned)grid1), dim3(NTH), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // GEMM2: down projection of h
@@ -527,7 +546,10 @@ hipError_t launch_gemm_fp8(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_c
     a.N = c.H;
     a.out_f32 = c.y_dtype == MOE_F32 ? 1 : 0;
     const int64_t grid2 = max_tiles * wk.nt2;
-    hipLaunchKernelGGL(ffn_gemm_fp8<1>, dim3((unsigned)grid2), dim3(NTH), 0, s, a);
+    if (small)
+        hipLaunchKernelGGL((ffn_gemm_fp8<1, kFfnBmFp8Small>), dim3((unsigned)grid2), dim3(NTH), 0, s, a);
+    else
+        hipLaunchKernelGGL((ffn_gemm_fp8<1, BM>), dim3((unsigned)grid2), dim3(NTH), 0, s, a);
     return hipGetLastError();
 }
 
