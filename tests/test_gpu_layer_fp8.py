@@ -100,15 +100,18 @@ def _small_shape():
     ("small", 77, moe.MOE_F32),
     ("small", 77, moe.MOE_BF16),
     ("c3", 24, moe.MOE_BF16),          # DeepSeek-V3 dimensions: 256 fp8 experts and the shared one
+    ("c4", 48, moe.MOE_BF16),          # softmax routing skewed by a Zipf logit bias, 128 experts, no shared
 ])
 def test_layer_fp8_experts_matches_oracle(shape, T, ydt):
-    s = _small_shape() if shape == "small" else synth.config("c3_dsv3_bf16")
+    s = {"small": _small_shape, "c3": lambda: synth.config("c3_dsv3_bf16"),
+         "c4": lambda: synth.config("c4_qwen3_skew_bf16")}[shape]()
     rc = router_case(s, T)
     w8 = _fp8_weights(s)
     ref = _oracle_fp8_layer(s, rc, w8)
     (wg, sg, wu, su, wd, sd), sh = w8
     c = lib_cfg(s, T=T, y_dtype=ydt, out_dtype=moe.MOE_F32)
     c.w_dtype = moe.MOE_FP8_E4M3
+    sh = sh if sh is not None else (None,) * 6
     w = moe.weights(wg, wu, wd, s_gate=sg, s_up=su, s_down=sd,
                     sh_gate=sh[0], sh_up=sh[2], sh_down=sh[4], sh_s_gate=sh[1], sh_s_up=sh[3], sh_s_down=sh[5])
     out = torch.full((T, s.H), float("nan"), device=dev())
