@@ -59,6 +59,10 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--rowmajor-weights", action="store_true",
                    help="time the row-major weight layout instead of the tiled one")
+    p.add_argument("--weight-table", type=int, default=0, metavar="N",
+                   help="read the expert weights through a device pointer table of N layers (the N layers' "
+                        "tables point at the one weight set, each in its own expert order) and run the steps "
+                        "over the layers in turn")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--traffic-run", action="store_true",
                    help="the program to run under rocprofv3 --pmc: CAL_RUNS plain streaming kernels (torch.neg "
@@ -198,19 +202,36 @@ def main():
         torch.cuda.empty_cache()
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     ws = moe.workspace(c, moe.MOE_STAGE_LAYER, dev)
+    ws_layers = [w]
+    table = layer_ids = None
+    if a.weight_table > 0:
+        # layer l's expert e is the weight set's expert (e + 37 l) mod E: each
+        # layer reads all E experts' bytes, as distinct weights would
+        n_l = a.weight_table
+        base = moe.moe_weight_table(c, [w])
+        G = E + (1 if s.shared else 0)
+        entries = []
+        for li in range(n_l):
+            for e in range(G):
+                src = (e + 37 * li) % E if e < E else E
+                entries += base[src * 6:(src + 1) * 6]
+        table = torch.tensor(entries, dtype=torch.int64, device=dev)
+        layer_ids = torch.arange(n_l, dtype=torch.int32, device=dev)
+        ws_layers = [moe.weights(None, None, None, layout=w.layout, table=table,
+                                 layer=layer_ids.data_ptr() + 4 * li, n_layers=n_l) for li in range(n_l)]
     torch.cuda.synchronize()
     print(f"[bench] inputs ready in {time.time() - t_gen:.1f}s; workspace {ws.numel() / 2**30:.2f} GiB",
           file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream()
 
-    def step():
-        moe.moe_layer(c, w_r, bias, w, x, out, ws, stream)
+    def step(i):
+        moe.moe_layer(c, w_r, bias, ws_layers[i % len(ws_layers)], x, out, ws, stream)
 
     ms_step = wall = None
     if not a.traffic_run:
-        for _ in range(a.warmup):
-            step()
+        for i in range(a.warmup):
+            step(i)
         torch.cuda.synchronize()
 
         # ---- timed region: K whole-layer steps
@@ -218,8 +239,8 @@ def main():
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         ev0.record(stream)
-        for _ in range(a.steps):
-            step()
+        for i in range(a.steps):
+            step(i)
         ev1.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
@@ -249,7 +270,8 @@ def main():
     ws_f = moe.workspace(c, moe.MOE_STAGE_FFN, dev)
     names = ["route", "permute", "grouped_ffn", "combine"]
 
-    def stage_step(evs):
+    def stage_step(evs, i):
+        w = ws_layers[i % len(ws_layers)]
         evs[0].record(stream)
         moe.moe_route(c, x, w_r, bias, None, None, ids, tw, ws_r, stream)
         evs[1].record(stream)
@@ -260,13 +282,13 @@ def main():
         moe.moe_combine(c, y_rows, tok_row, tw, y_sh, out, stream)
         evs[4].record(stream)
 
-    for _ in range(a.warmup if a.traffic_run else 2):
-        stage_step([torch.cuda.Event(enable_timing=True) for _ in range(5)])
+    for i in range(a.warmup if a.traffic_run else 2):
+        stage_step([torch.cuda.Event(enable_timing=True) for _ in range(5)], i)
     torch.cuda.synchronize()
     stage_ms = np.zeros(4)
     all_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(a.steps)]
-    for evs in all_evs:
-        stage_step(evs)
+    for i, evs in enumerate(all_evs):
+        stage_step(evs, i)
     torch.cuda.synchronize()
     for evs in all_evs:
         stage_ms += np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(4)])
@@ -348,7 +370,8 @@ def main():
         "config": {"workload": a.workload, "T": T, "H": H, "E": E, "k": k, "I": I, "shared_experts": int(s.shared),
                    "I_shared": I_sh, "router": s.score, "n_groups": s.n_groups, "topk_groups": s.topk_groups,
                    "routed_scale": s.routed_scale, "out_dtype": "bf16", "expert_out_dtype": "bf16",
-                   "weight_layout": "row-major" if a.rowmajor_weights else "tiled"},
+                   "weight_layout": "row-major" if a.rowmajor_weights else "tiled",
+                   **({"weight_table_layers": a.weight_table} if a.weight_table else {})},
         "tokens_per_s": round(T / (ms_step * 1e-3), 1),
         "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
         "layer_flop": layer_flop,
@@ -510,7 +533,8 @@ def bench_fp8_layer(a, s, dev):
     ws_1 = moe.workspace(c1, moe.MOE_STAGE_FFN, dev, n_rows_cap=T) if s.shared else None
     names = ["route", "quantise", "permute", "grouped_ffn", "combine"]
 
-    def stage_step(evs):
+    def stage_step(evs, i):
+        w = ws_layers[i % len(ws_layers)]
         evs[0].record(stream)
         moe.moe_route(c, x, w_r, bias, None, None, ids, tw, ws_r, stream)
         evs[1].record(stream)

@@ -25,7 +25,8 @@ from ._ffi import (MOE_BF16, MOE_ERR_HIP, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORT
 
 __all__ = [
     "MoeError", "make_cfg", "weights", "workspace", "moe_validate", "moe_max_rows", "moe_workspace_bytes", "moe_ffn_workspace_bytes",
-    "moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_quantize_fp8", "moe_layer", "moe_status_string",
+    "moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_quantize_fp8", "moe_layer", "moe_weight_table",
+    "weight_table", "moe_status_string",
     "moe_last_error", "moe_cfg", "moe_weights", "lib_path",
     "MOE_OK", "MOE_ERR_INVALID_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE", "MOE_ERR_HIP",
     "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3", "MOE_SCORE_SOFTMAX", "MOE_SCORE_SIGMOID",
@@ -91,10 +92,29 @@ def _check(status: int):
 
 def weights(w_gate, w_up, w_down, s_gate=None, s_up=None, s_down=None, sh_gate=None, sh_up=None,
             sh_down=None, layout: int = MOE_LAYOUT_ROWMAJOR, sh_s_gate=None, sh_s_up=None,
-            sh_s_down=None) -> moe_weights:
+            sh_s_down=None, table=None, layer=None, n_layers: int = 0) -> moe_weights:
+    """table / layer / n_layers: pointer-table weights (moe_weights.table);
+    the other matrices are then ignored and may be None."""
     return moe_weights(*(_ptr(t) for t in (w_gate, w_up, w_down, s_gate, s_up, s_down, sh_gate,
                                              sh_up, sh_down)), layout,
-                       *(_ptr(t) for t in (sh_s_gate, sh_s_up, sh_s_down)))
+                       *(_ptr(t) for t in (sh_s_gate, sh_s_up, sh_s_down, table, layer)), n_layers)
+
+
+def moe_weight_table(cfg: moe_cfg, layers) -> list:
+    """Host table of moe_weight_table for contiguous per-layer moe_weights:
+    n_layers * (E + has_shared) * 6 device addresses (0 for NULL)."""
+    n = len(layers)
+    arr = (moe_weights * n)(*layers)
+    G = cfg.E + (1 if cfg.has_shared else 0)
+    out = (ctypes.c_void_p * (n * G * 6))()
+    _check(_ffi.lib().moe_weight_table(ctypes.byref(cfg), arr, n, out))
+    return [v or 0 for v in out]
+
+
+def weight_table(cfg: moe_cfg, layers, device) -> torch.Tensor:
+    """The table of moe_weight_table copied to a device int64 tensor (torch
+    allocates it; keep it alive while calls use it)."""
+    return torch.tensor(moe_weight_table(cfg, layers), dtype=torch.int64).to(device)
 
 
 def moe_x_perm_bytes(cfg: moe_cfg) -> int:

@@ -20,7 +20,8 @@ MOE_LAYOUT_ROWMAJOR, MOE_LAYOUT_TILED, MOE_LAYOUT_INDEXED = 0, 1, 2
 
 EXPORTS = ("moe_validate", "moe_max_rows", "moe_workspace_bytes", "moe_ffn_workspace_bytes",
            "moe_x_perm_bytes", "moe_tiled_weights_bytes", "moe_tile_weights", "moe_route", "moe_permute", "moe_grouped_ffn",
-           "moe_combine", "moe_quantize_fp8", "moe_layer", "moe_status_string", "moe_last_error")
+           "moe_combine", "moe_quantize_fp8", "moe_layer", "moe_weight_table", "moe_status_string",
+           "moe_last_error")
 
 
 class moe_cfg(ctypes.Structure):
@@ -34,7 +35,8 @@ class moe_cfg(ctypes.Structure):
 class moe_weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down",
                                                "sh_gate", "sh_up", "sh_down")] + [("layout", ctypes.c_int32)] + \
-               [(n, ctypes.c_void_p) for n in ("sh_s_gate", "sh_s_up", "sh_s_down")]
+               [(n, ctypes.c_void_p) for n in ("sh_s_gate", "sh_s_up", "sh_s_down", "table", "layer")] + \
+               [("n_layers", ctypes.c_int32)]
 
 
 _lib = None
@@ -76,6 +78,8 @@ def lib() -> ctypes.CDLL:
         L.moe_quantize_fp8.restype = i32
         L.moe_layer.argtypes = [C, P, P, W, P, P, P, sz, P]
         L.moe_layer.restype = i32
+        L.moe_weight_table.argtypes = [C, W, i32, P]
+        L.moe_weight_table.restype = i32
         L.moe_status_string.argtypes = [i32]
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_last_error.argtypes = []

@@ -309,6 +309,15 @@ moe_status check_weights(const moe_cfg& c, const moe_weights* w) {
     const bool tiled = w->layout == MOE_LAYOUT_TILED;
     if (tiled && (c.act_dtype != MOE_BF16 || c.w_dtype != MOE_BF16))
         return fail(MOE_ERR_UNSUPPORTED, "tiled weights are bf16 only");
+    if (w->table) {
+        // the matrices are read on the device, through the table
+        if (c.act_dtype == MOE_F32) return fail(MOE_ERR_UNSUPPORTED, "pointer-table weights on the fp32 path");
+        REQUIRE(w->layer, "w->layer");
+        if (w->n_layers < 1) return fail(MOE_ERR_INVALID_ARG, "w->n_layers=%d must be >= 1", w->n_layers);
+        if (reinterpret_cast<uintptr_t>(w->table) % 8) return fail(MOE_ERR_INVALID_ARG, "w->table is not 8-byte aligned");
+        if (reinterpret_cast<uintptr_t>(w->layer) % 4) return fail(MOE_ERR_INVALID_ARG, "w->layer is not 4-byte aligned");
+        return MOE_OK;
+    }
     REQUIRE(w->w_gate, "w->w_gate");
     if (!tiled) REQUIRE(w->w_up, "w->w_up");
     REQUIRE(w->w_down, "w->w_down");
@@ -330,6 +339,13 @@ moe_status check_weights(const moe_cfg& c, const moe_weights* w) {
     return MOE_OK;
 }
 
+// The weight table of a call (tab NULL for contiguous weights); `first` is the
+// table entry of the launch's group 0.
+moe::WTab wtab_of(const moe_cfg& c, const moe_weights& w, int first) {
+    if (!w.table) return moe::WTab{nullptr, nullptr, 0, 0, 0};
+    return moe::WTab{w.table, w.layer, w.n_layers, c.E + (c.has_shared ? 1 : 0), first};
+}
+
 // Enqueue halves of the stage entry points (arguments already checked); the
 // layer calls the same functions, so its kernels are the stage kernels.
 moe_status permute_enqueue(const moe_cfg& c, const void* x, const float* x_scale, const int32_t* ids,
@@ -346,8 +362,8 @@ moe_status permute_enqueue(const moe_cfg& c, const void* x, const float* x_scale
 }
 
 moe_status ffn_enqueue(const moe_cfg& c, int64_t n_rows_cap, const void* x_rows, const float* x_scale,
-                       const int32_t* offsets, const int32_t* row_src, const moe_weights& w, const void* x_tokens,
-                       void* y_rows, void* y_shared, void* ws, hipStream_t s) {
+                       const int32_t* offsets, const int32_t* row_src, const moe_weights& w, const moe::WTab& wt,
+                       const void* x_tokens, void* y_rows, void* y_shared, void* ws, hipStream_t s) {
     moe::FfnOperands op{x_rows, x_tokens, 0, 0, y_rows, y_shared, nullptr};
     const XPermGeom g = x_perm_geom(c);
     if (c.x_layout == MOE_LAYOUT_INDEXED) {
@@ -363,12 +379,12 @@ moe_status ffn_enqueue(const moe_cfg& c, int64_t n_rows_cap, const void* x_rows,
     FfnCarve f = ffn_carve(c, n_rows_cap, ws);
     hipError_t e;
     if (c.act_dtype == MOE_BF16)
-        e = moe::launch_gemm_bf16(c, f.max_tiles, n_rows_cap, op, offsets, w, f.wk, f.h, s);
+        e = moe::launch_gemm_bf16(c, f.max_tiles, n_rows_cap, op, offsets, w, wt, f.wk, f.h, s);
     else if (c.act_dtype == MOE_F32)
         e = moe::launch_gemm_f32(c, f.max_tiles, n_rows_cap, op.x_rows, offsets, w, op.x_tokens, op.y_rows,
                                  op.y_shared, f.wk, f.h, f.h_sh, s);
     else
-        e = moe::launch_gemm_fp8(c, f.max_tiles, n_rows_cap, x_rows, x_scale, offsets, w, y_rows, f.wk, f.h,
+        e = moe::launch_gemm_fp8(c, f.max_tiles, n_rows_cap, x_rows, x_scale, offsets, w, wt, y_rows, f.wk, f.h,
                                  f.h_scale, s);
     if (e != hipSuccess) return hip_fail(e, "moe_grouped_ffn");
     return MOE_OK;
@@ -384,17 +400,19 @@ moe_status layer_fp8_experts(const moe_cfg& c, const moe_weights& w, const void*
     moe_status st = permute_enqueue(cq, l.x_q, l.x_s, l.ids, l.counts, l.offsets, l.row_src, l.tok_row, l.x_perm,
                                     l.x_perm_scale, l.scratch, s);
     if (st != MOE_OK) return st;
-    st = ffn_enqueue(cq, max_rows_of(cq), l.x_perm, l.x_perm_scale, l.offsets, nullptr, w, nullptr, l.y_rows,
-                     nullptr, l.scratch, s);
+    st = ffn_enqueue(cq, max_rows_of(cq), l.x_perm, l.x_perm_scale, l.offsets, nullptr, w, wtab_of(c, w, 0),
+                     nullptr, l.y_rows, nullptr, l.scratch, s);
     if (st != MOE_OK) return st;
     if (c.has_shared) {
         const moe_cfg c1 = fp8_shared_cfg(c);
-        const moe_weights ws1{w.sh_gate, w.sh_up, w.sh_down, w.sh_s_gate, w.sh_s_up, w.sh_s_down,
-                              nullptr, nullptr, nullptr, MOE_LAYOUT_ROWMAJOR, nullptr, nullptr, nullptr};
+        // the shared expert as the one group of its own launch: table entry E
+        const moe_weights ws1{w.sh_gate, w.sh_up,  w.sh_down, w.sh_s_gate, w.sh_s_up, w.sh_s_down,
+                              nullptr,   nullptr,  nullptr,   MOE_LAYOUT_ROWMAJOR, nullptr, nullptr,
+                              nullptr,   nullptr,  nullptr,   0};
         e = moe::launch_offsets_one_group(l.offsets_sh, c.T, s);
         if (e != hipSuccess) return hip_fail(e, "moe_layer (shared offsets)");
-        st = ffn_enqueue(c1, c.T, l.x_q, l.x_s, l.offsets_sh, nullptr, ws1, nullptr, l.y_shared, nullptr,
-                         l.scratch, s);
+        st = ffn_enqueue(c1, c.T, l.x_q, l.x_s, l.offsets_sh, nullptr, ws1, wtab_of(c, w, c.E), nullptr,
+                         l.y_shared, nullptr, l.scratch, s);
         if (st != MOE_OK) return st;
     }
     e = moe::launch_combine(c, l.y_rows, l.tok_row, l.topk_w, l.y_shared, out, s);
@@ -529,8 +547,53 @@ moe_status moe_grouped_ffn(const moe_cfg* cfg, int64_t n_rows_cap, const void* x
     const size_t need = ffn_carve(c, n_rows_cap, nullptr).bytes;
     if ((st = check_ws(ws, ws_bytes, need)) != MOE_OK) return st;
     if (n_rows_cap == 0 && !(c.has_shared && c.T > 0)) return MOE_OK;
-    return ffn_enqueue(c, n_rows_cap, x_rows, x_scale, expert_offsets, row_src, *w, x_tokens, y_rows, y_shared, ws,
-                       static_cast<hipStream_t>(stream));
+    return ffn_enqueue(c, n_rows_cap, x_rows, x_scale, expert_offsets, row_src, *w, wtab_of(c, *w, 0), x_tokens,
+                       y_rows, y_shared, ws, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_weight_table(const moe_cfg* cfg, const moe_weights* layers, int32_t n_layers, const void** table) {
+    moe_status st = check_cfg(cfg);
+    if (st != MOE_OK) return st;
+    const moe_cfg& c = *cfg;
+    if (c.act_dtype == MOE_F32) return fail(MOE_ERR_UNSUPPORTED, "pointer-table weights on the fp32 path");
+    REQUIRE(layers, "layers");
+    REQUIRE(table, "table");
+    if (n_layers < 1) return fail(MOE_ERR_INVALID_ARG, "n_layers=%d must be >= 1", n_layers);
+    const bool f8 = c.w_dtype == MOE_FP8_E4M3;
+    const int G = c.E + (c.has_shared ? 1 : 0);
+    // bytes of one expert's matrices (tiled: the fragment-order gate+up and down)
+    // and floats of its block scales
+    const moe::TiledSizes t = moe::tiled_sizes(c);
+    const size_t el = (size_t)dtype_bytes(c.w_dtype);
+    const size_t mat = (size_t)c.I * c.H * el;
+    const size_t nsc = f8 ? (size_t)(c.I / 128) * (c.H / 128) : 0;
+    for (int32_t L = 0; L < n_layers; ++L) {
+        const moe_weights& w = layers[L];
+        if (w.table) return fail(MOE_ERR_INVALID_ARG, "layers[%d].table must be NULL", L);
+        if ((st = check_weights(c, &w)) != MOE_OK) return st;
+        const bool tiled = w.layout == MOE_LAYOUT_TILED;
+        const size_t m13 = tiled ? t.w13 / c.E : mat, m2 = tiled ? t.w2 / c.E : mat;
+        const void** row = table + (size_t)L * G * 6;
+        for (int e = 0; e < c.E; ++e) {
+            const void** r = row + (size_t)e * 6;
+            r[0] = static_cast<const char*>(w.w_gate) + e * m13;
+            r[1] = tiled ? nullptr : static_cast<const char*>(w.w_up) + e * mat;
+            r[2] = static_cast<const char*>(w.w_down) + e * m2;
+            r[3] = f8 ? w.s_gate + e * nsc : nullptr;
+            r[4] = f8 ? w.s_up + e * nsc : nullptr;
+            r[5] = f8 ? w.s_down + e * nsc : nullptr;
+        }
+        if (c.has_shared) {
+            const void** r = row + (size_t)c.E * 6;
+            r[0] = w.sh_gate;
+            r[1] = tiled ? nullptr : w.sh_up;
+            r[2] = w.sh_down;
+            r[3] = f8 ? w.sh_s_gate : nullptr;
+            r[4] = f8 ? w.sh_s_up : nullptr;
+            r[5] = f8 ? w.sh_s_down : nullptr;
+        }
+    }
+    return MOE_OK;
 }
 
 size_t moe_x_perm_bytes(const moe_cfg* cfg) {
@@ -552,6 +615,7 @@ moe_status moe_tile_weights(const moe_cfg* cfg, const moe_weights* src, void* ds
     if (c.act_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "tiled weights are bf16 only");
     if ((st = check_weights(c, src)) != MOE_OK) return st;
     if (src->layout != MOE_LAYOUT_ROWMAJOR) return fail(MOE_ERR_INVALID_ARG, "src must be row-major");
+    if (src->table) return fail(MOE_ERR_INVALID_ARG, "src must be contiguous (table == NULL)");
     REQUIRE(tiled, "tiled");
     const moe::TiledSizes t = moe::tiled_sizes(c);
     const size_t need = align_up(t.w13) + align_up(t.w2) + align_up(t.sh13) + align_up(t.sh2);
@@ -634,8 +698,8 @@ moe_status moe_layer(const moe_cfg* cfg, const void* w_router, const float* bias
                          l.scratch, s);
     if (st != MOE_OK) return st;
     const void* x_rows = cs.x_layout == MOE_LAYOUT_INDEXED ? x : l.x_perm;
-    st = ffn_enqueue(cs, max_rows_of(cs), x_rows, nullptr, l.offsets, l.row_src, *w, x, l.y_rows, l.y_shared,
-                     l.scratch, s);
+    st = ffn_enqueue(cs, max_rows_of(cs), x_rows, nullptr, l.offsets, l.row_src, *w, wtab_of(c, *w, 0), x, l.y_rows,
+                     l.y_shared, l.scratch, s);
     if (st != MOE_OK) return st;
     e = moe::launch_combine(c, l.y_rows, l.tok_row, l.topk_w, l.y_shared, out, s);
     if (e != hipSuccess) return hip_fail(e, "moe_layer (combine)");

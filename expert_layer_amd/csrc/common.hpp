@@ -166,6 +166,28 @@ struct FfnWork {
 };
 hipError_t launch_build_tiles(const moe_cfg& c, const int32_t* offsets, int bm, int64_t rows_cap,
                               const FfnWork& wk, hipStream_t s);
+// Pointer-table weights (moe_weights.table): entry
+// ((layer * row + first + g) * 6 + slot) holds group g's matrix `slot` (0 gate
+// or tiled gate+up, 1 up, 2 down, 3 .. 5 their fp8 block scales) of the layer
+// *layer, which the kernels read when they run.  tab == NULL: contiguous
+// weights.
+struct WTab {
+    const void* const* tab;
+    const int32_t* layer;
+    int n_layers;
+    int row;    // entries per layer / 6: E + has_shared of the caller's cfg
+    int first;  // entry of the launch's group 0 (the shared expert's own launch: E)
+};
+// The layer a launch reads, or -1 when *layer is outside [0, n_layers) (the
+// launch then does nothing).  Uniform: a scalar load.
+__device__ __forceinline__ int wtab_layer(const WTab& t) {
+    const int L = *t.layer;
+    return (L >= 0 && L < t.n_layers) ? L : -1;
+}
+__device__ __forceinline__ const void* wtab_ptr(const WTab& t, int layer, int g, int slot) {
+    return t.tab[((size_t)layer * (size_t)t.row + (size_t)(t.first + g)) * 6 + (size_t)slot];
+}
+
 // Row operands of the grouped FFN: GEMM1 inputs (routed rows, shared-expert
 // tokens; row-major or tiled) and GEMM2 outputs.
 struct FfnOperands {
@@ -177,8 +199,8 @@ struct FfnOperands {
     const int32_t* row_src;  // non-NULL: x_rows is x [T][H], row r is token row_src[r] / k
 };
 hipError_t launch_gemm_bf16(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_cap, const FfnOperands& op,
-                            const int32_t* offsets, const moe_weights& w, const FfnWork& wk, void* h_tiles,
-                            hipStream_t s);
+                            const int32_t* offsets, const moe_weights& w, const WTab& wt, const FfnWork& wk,
+                            void* h_tiles, hipStream_t s);
 // Bytes of one h tile slot (256 rows) of the bf16 path.
 inline size_t h_slot_bytes(const moe_cfg& c) {
     const int imax = c.has_shared && c.I_shared > c.I ? c.I_shared : c.I;
@@ -193,8 +215,8 @@ hipError_t launch_tile_weights(const moe_cfg& c, const moe_weights& src, void* w
 // fp8 (e4m3) grouped FFN: x_rows [n_rows_cap][H] with x_scale [n_rows_cap][H/128];
 // h [n_rows_cap][I] e4m3 and h_scale [n_rows_cap][I/128] are workspace.
 hipError_t launch_gemm_fp8(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_cap, const void* x_rows,
-                           const float* x_scale, const int32_t* offsets, const moe_weights& w, void* y_rows,
-                           const FfnWork& wk, void* h, float* h_scale, hipStream_t s);
+                           const float* x_scale, const int32_t* offsets, const moe_weights& w, const WTab& wt,
+                           void* y_rows, const FfnWork& wk, void* h, float* h_scale, hipStream_t s);
 hipError_t launch_gemm_f32(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_cap, const void* x_rows,
                            const int32_t* offsets, const moe_weights& w, const void* x_tokens, void* y_rows,
                            void* y_shared, const FfnWork& wk, void* h, void* h_sh, hipStream_t s);

@@ -157,6 +157,8 @@ struct GemmArgs {
     int a_rows;                // rows of x (the indexed A operand)
     int w_tiled;               // weights tiled (fragment order)
     int h_slot_ks;             // k blocks of one h tile slot (ceil(max(I, I_sh) / 32))
+    WTab wt;                   // wt.tab != NULL: w0 / w1 of group g are table entries slot0 / slot1
+    int slot0, slot1;
 };
 
 // Per-tile load state.  A: the buffer descriptor, the byte offsets of this
@@ -367,7 +369,8 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, int mt, int g, int r
         // fragment-order groups of 64 rows: GEMM1 2 * roundup(N, 128) rows, GEMM2 N rows
         const int groups = MODE == 0 ? ((N + 127) / 128) * 4 : (N + 63) / 64;
         const size_t mat = (size_t)groups * KS * 2048;  // elements of one expert's matrix
-        const uint16_t* W = shared ? p.w0_shared : p.w0_routed + (size_t)g * mat;
+        const uint16_t* W = p.wt.tab ? static_cast<const uint16_t*>(wtab_ptr(p.wt, *p.wt.layer, g, p.slot0))
+                            : shared ? p.w0_shared : p.w0_routed + (size_t)g * mat;
         const int q0 = nt * 4;                          // first group of the N tile
         d.rb[0] = make_rsrc(W + (size_t)q0 * KS * 2048, (uint32_t)((groups - q0) * KS * 4096));
         d.rb[1] = d.rb[0];
@@ -379,9 +382,15 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, int mt, int g, int r
     } else {
         const int ncols = MODE == 0 ? min(BN / 2, N - n0) : min(BN, N - n0);
         const size_t wmat = (size_t)K * (size_t)N;
-        const uint16_t* W0 = (shared ? p.w0_shared : p.w0_routed + (size_t)g * wmat) + (size_t)n0 * K;
-        const uint16_t* W1 =
-            MODE == 0 ? (shared ? p.w1_shared : p.w1_routed + (size_t)g * wmat) + (size_t)n0 * K : W0;
+        const uint16_t *W0, *W1;
+        if (p.wt.tab) {
+            const int lay = *p.wt.layer;
+            W0 = static_cast<const uint16_t*>(wtab_ptr(p.wt, lay, g, p.slot0)) + (size_t)n0 * K;
+            W1 = MODE == 0 ? static_cast<const uint16_t*>(wtab_ptr(p.wt, lay, g, p.slot1)) + (size_t)n0 * K : W0;
+        } else {
+            W0 = (shared ? p.w0_shared : p.w0_routed + (size_t)g * wmat) + (size_t)n0 * K;
+            W1 = MODE == 0 ? (shared ? p.w1_shared : p.w1_routed + (size_t)g * wmat) + (size_t)n0 * K : W0;
+        }
         d.rb[0] = make_rsrc(W0, (uint32_t)ncols * (uint32_t)K * 2u);
         d.rb[1] = make_rsrc(W1, (uint32_t)ncols * (uint32_t)K * 2u);
 #pragma unroll
@@ -524,6 +533,7 @@ __global__ void __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1))
 ffn_gemm_bf16(GemmArgs p) {
     const int L = xcd_remap(blockIdx.x, p.n_tiles[0] * p.NT);
     if (L < 0) return;
+    if (p.wt.tab && wtab_layer(p.wt) < 0) return;
     const int2 wl = p.work[L];
     const int mt = wl.x, nt = wl.y;
     const int4 td = p.tiles[mt];
@@ -652,8 +662,8 @@ hipError_t launch_build_tiles(const moe_cfg& c, const int32_t* offsets, int bm, 
 }
 
 hipError_t launch_gemm_bf16(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_cap, const FfnOperands& op,
-                            const int32_t* offsets, const moe_weights& w, const FfnWork& wk, void* h_tiles,
-                            hipStream_t s) {
+                            const int32_t* offsets, const moe_weights& w, const WTab& wt, const FfnWork& wk,
+                            void* h_tiles, hipStream_t s) {
     const int has_sh = c.has_shared ? 1 : 0;
     hipError_t e0 = launch_build_tiles(c, offsets, BM, n_rows_cap, wk, s);
     if (e0 != hipSuccess) return e0;
@@ -665,6 +675,9 @@ hipError_t launch_gemm_bf16(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_
     a.E = c.E;
     a.w_tiled = tiled;
     a.h_slot_ks = (imax + BK - 1) / BK;
+    a.wt = wt;
+    a.slot0 = 0;
+    a.slot1 = 1;
     // GEMM1: gate/up + SwiGLU -> h tile slots
     a.work = reinterpret_cast<const int2*>(wk.work1);
     a.a_routed = static_cast<const uint16_t*>(op.x_rows);
@@ -696,6 +709,7 @@ hipError_t launch_gemm_bf16(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_
     a.a_row_src = nullptr;
     a.w0_routed = static_cast<const uint16_t*>(w.w_down);
     a.w1_routed = nullptr;
+    a.slot0 = 2;
     a.w0_shared = static_cast<const uint16_t*>(w.sh_down);
     a.w1_shared = nullptr;
     a.out_routed = op.y_rows;

@@ -98,6 +98,8 @@ struct Fp8Args {
     int NT;                 // N tiles per M tile
     int K, N;               // GEMM1: K = H, N = I; GEMM2: K = I, N = H
     int out_f32;            // GEMM2 output dtype
+    WTab wt;                // wt.tab != NULL: w0, w1, s0, s1 of group g are table entries
+    int slot0, slot1;       //   slot0, slot1, slot0 + 3, slot1 + 3
 };
 
 // Row scales of a stage in LDS: position P = 128 h + 64 (rb / 4) + 4 l + rb % 4
@@ -298,14 +300,23 @@ __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int 
     // rows 32 j + [0, 32) then the up rows of the same h columns); GEMM2 the
     // weight rows n0 + [0, 256)
     const int nlim = MODE == 0 ? min(N - n0, 128) : min(N - n0, BN);
-    if (MODE == 0) {
-        const size_t mat = (size_t)N * K;
-        d.rb0 = make_rsrc(p.w0 + (size_t)g * mat + (size_t)n0 * K, (uint32_t)nlim * (uint32_t)K);
-        d.rb1 = make_rsrc(p.w1 + (size_t)g * mat + (size_t)n0 * K, (uint32_t)nlim * (uint32_t)K);
-    } else {
-        d.rb0 = make_rsrc(p.w0 + (size_t)g * N * K + (size_t)n0 * K, (uint32_t)nlim * (uint32_t)K);
-        d.rb1 = d.rb0;
+    // this group's matrices and block scales, and its index in them
+    const uint8_t *w0 = p.w0, *w1 = p.w1;
+    const float *s0 = p.s0, *s1 = p.s1;
+    int ge = g;
+    if (p.wt.tab) {
+        const int lay = *p.wt.layer;
+        w0 = static_cast<const uint8_t*>(wtab_ptr(p.wt, lay, g, p.slot0));
+        s0 = static_cast<const float*>(wtab_ptr(p.wt, lay, g, p.slot0 + 3));
+        if (MODE == 0) {
+            w1 = static_cast<const uint8_t*>(wtab_ptr(p.wt, lay, g, p.slot1));
+            s1 = static_cast<const float*>(wtab_ptr(p.wt, lay, g, p.slot1 + 3));
+        }
+        ge = 0;
     }
+    const size_t mat = (size_t)N * K;
+    d.rb0 = make_rsrc(w0 + (size_t)ge * mat + (size_t)n0 * K, (uint32_t)nlim * (uint32_t)K);
+    d.rb1 = MODE == 0 ? make_rsrc(w1 + (size_t)ge * mat + (size_t)n0 * K, (uint32_t)nlim * (uint32_t)K) : d.rb0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int row = wave * 32 + i * 8 + (lane >> 3);  // LDS row this lane fills (B; A modulo TB)
@@ -320,11 +331,11 @@ __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int 
     // with readlane, so no vector-memory load besides the DMA runs in the K loop
     int wbase = -1;
     if (MODE == 0) {
-        wbase = (g * NB + n0 / BK) * KB;
+        wbase = (ge * NB + n0 / BK) * KB;
     } else {
         // a wave whose 64 columns lie past N (N not a multiple of 256) reads no scale
         const int cbk = (n0 + q * 64) / BK;
-        if (cbk < NB) wbase = (g * NB + cbk) * KB;
+        if (cbk < NB) wbase = (ge * NB + cbk) * KB;
     }
     float ws0[2] = {0.f, 0.f}, ws1[2] = {0.f, 0.f};
     if (wbase >= 0) {
@@ -332,8 +343,8 @@ __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int 
         for (int h = 0; h < 2; ++h) {
             const int kb = h * 64 + lane;
             if (kb < KB) {
-                ws0[h] = p.s0[wbase + kb];
-                ws1[h] = MODE == 0 ? p.s1[wbase + kb] : ws0[h];
+                ws0[h] = s0[wbase + kb];
+                ws1[h] = MODE == 0 ? s1[wbase + kb] : ws0[h];
             }
         }
     }
@@ -392,7 +403,7 @@ __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int 
 
     // A lane holds row r0 + 16 rb + l16 of its row blocks and, in column block
     // cb, the four columns 16 cb + g4 + [0, 4) of its 64 weight rows.
-    const int l16 = lane & 15, g4 = 4 * (lane >> 4);
+    const int l16 = lane & 15;
     if (MODE == 0) {
         // h = silu(g) * u for h columns n0 + 32 q + 16 c + g4 + j, c = 0, 1
         float rmax[RB];
@@ -487,6 +498,7 @@ __global__ void __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2, 2))
 ffn_gemm_fp8(Fp8Args p) {
     const int L = xcd_remap(blockIdx.x, p.n_tiles[0] * p.NT);
     if (L < 0) return;
+    if (p.wt.tab && wtab_layer(p.wt) < 0) return;
     const int2 wl = p.work[L];
     const int4 td = p.tiles[wl.x];
     const int g = td.x, row0 = td.y, M = td.z - td.y;
@@ -498,8 +510,8 @@ ffn_gemm_fp8(Fp8Args p) {
 }  // namespace
 
 hipError_t launch_gemm_fp8(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_cap, const void* x_rows,
-                           const float* x_scale, const int32_t* offsets, const moe_weights& w, void* y_rows,
-                           const FfnWork& wk, void* h, float* h_scale, hipStream_t s) {
+                           const float* x_scale, const int32_t* offsets, const moe_weights& w, const WTab& wt,
+                           void* y_rows, const FfnWork& wk, void* h, float* h_scale, hipStream_t s) {
     // Tile height: groups of about 256 rows or fewer (the DeepSeek-V3 layer's
     // 256 experts, 8 rows a token) fill 128-row tiles; a 224-row tile would
     // split them into two 128-row tiles and compute 224 rows of each.
@@ -509,6 +521,9 @@ hipError_t launch_gemm_fp8(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_c
     hipError_t e0 = launch_build_tiles(c, offsets, tb, n_rows_cap, wk, s);
     if (e0 != hipSuccess) return e0;
     Fp8Args a{};
+    a.wt = wt;
+    a.slot0 = 0;
+    a.slot1 = 1;
     a.tiles = reinterpret_cast<const int4*>(wk.tiles);
     a.n_tiles = wk.n_tiles;
     // GEMM1: gate/up + SwiGLU -> h (e4m3) and its row-block scales
@@ -538,6 +553,7 @@ hipError_t launch_gemm_fp8(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_c
     a.a_scale = h_scale;
     a.w0 = static_cast<const uint8_t*>(w.w_down);
     a.w1 = nullptr;
+    a.slot0 = 2;
     a.s0 = w.s_down;
     a.s1 = nullptr;
     a.out = y_rows;

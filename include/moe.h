@@ -157,11 +157,42 @@ typedef struct moe_weights {
     const void *sh_gate, *sh_up, *sh_down;
     int32_t layout;
     const float *sh_s_gate, *sh_s_up, *sh_s_down;
+    /* Pointer-table weights: the layer-oblivious grouped GEMM of ASAP
+     * (section 3.4.2, "Bubble-Free Kernel Dispatching", Figure 9b: pointer
+     * access to the expert weights of every layer, an on-device address array,
+     * the layer id a device-side argument) and the per-buffer weight list of
+     * DWDP (section 4.2: experts held in separate local and prefetched buffers,
+     * read in place).  NULL: the matrices are the contiguous arrays above.
+     * Non-NULL: `table` is a device array [n_layers][E + has_shared][6] of
+     * device pointers {gate, up, down, s_gate, s_up, s_down} to ONE expert's
+     * matrices (the layouts above without the leading [E]; entry E of a layer
+     * is the shared expert; scale entries NULL unless w_dtype is fp8; with
+     * layout MOE_LAYOUT_TILED, gate points to the expert's tiled gate+up
+     * matrix, down to its tiled down matrix, up is unused); `layer` is a device
+     * int32 that the grouped FFN's kernels read when they run, so a call (or a
+     * captured graph) can be enqueued before the layer is known.  A *layer
+     * outside [0, n_layers) makes the FFN kernels skip all work (y_rows,
+     * y_shared and, in moe_layer, out are then undefined).  The other pointer
+     * fields are ignored.  Matrices 16-byte aligned, scales 4-byte.  Supported on
+     * the bf16 and fp8 paths (not fp32).  moe_weight_table fills a table from
+     * contiguous per-layer weights. */
+    const void *const *table;
+    const int32_t *layer;
+    int32_t n_layers;
 } moe_weights;
 
 /* Checks a configuration on the host (no HIP call).  MOE_OK if every entry
  * point accepts it. */
 moe_status moe_validate(const moe_cfg *cfg);
+
+/* Host helper of pointer-table weights (no HIP call, nothing dereferenced):
+ * writes to the HOST array table[n_layers * (E + has_shared) * 6] the
+ * addresses of each expert's matrices in the contiguous weights layers[l]
+ * (table == NULL in each; layout row-major or tiled, as cfg's dtypes allow),
+ * in the order moe_weights.table reads.  The caller copies the array to the
+ * device.  MOE_ERR_UNSUPPORTED for fp32 weights. */
+moe_status moe_weight_table(const moe_cfg *cfg, const moe_weights *layers, int32_t n_layers,
+                            const void **table);
 
 /* Upper bound of the dispatched rows: T*k + E*(m_tile - 1).  Sizes row_src,
  * x_perm and y_rows.  Returns -1 for an invalid cfg. */

@@ -240,3 +240,80 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(ValueError):
         m.moe_combine(c, torch.zeros(8, 64), torch.zeros(4, 2, dtype=torch.int32), torch.zeros(4, 2), None,
                       torch.zeros(4, 64))
+
+
+def test_weight_table_host_addresses():
+    """moe_weight_table writes, per layer and expert, the addresses of that
+    expert's matrices in contiguous weights (fake addresses: nothing is
+    dereferenced), the shared expert as entry E, scales for fp8 only; and the
+    entry points check a table's own fields before any launch."""
+    lib = _ffi.lib()
+    E, H, I, Ish = 4, 256, 384, 128
+    c = m.make_cfg(T=8, H=H, E=E, k=1, I=I, has_shared=True, I_shared=Ish)
+    base = [0x10000000 * (i + 1) for i in range(12)]
+    lay0 = m.moe_weights(w_gate=base[0], w_up=base[1], w_down=base[2], sh_gate=base[3], sh_up=base[4],
+                         sh_down=base[5])
+    lay1 = m.moe_weights(w_gate=base[6], w_up=base[7], w_down=base[8], sh_gate=base[9], sh_up=base[10],
+                         sh_down=base[11])
+    t = m.moe_weight_table(c, [lay0, lay1])
+    G = E + 1
+    assert len(t) == 2 * G * 6
+    mat = I * H * 2
+    for L, b in ((0, base[:6]), (1, base[6:])):
+        for e in range(E):
+            assert t[(L * G + e) * 6:(L * G + e + 1) * 6] == [b[0] + e * mat, b[1] + e * mat, b[2] + e * mat, 0, 0, 0]
+        assert t[(L * G + E) * 6:(L * G + E + 1) * 6] == [b[3], b[4], b[5], 0, 0, 0]
+    # tiled bf16: one expert's gate+up matrix is 2 * roundup(I, 128) rows in
+    # groups of 64, each group ceil(H / 32) stages of 4 KiB; down: ceil(H / 64)
+    # groups of ceil(I / 32) stages
+    tl = m.moe_weights(w_gate=base[0], w_down=base[2], sh_gate=base[3], sh_down=base[5],
+                       layout=m.MOE_LAYOUT_TILED)
+    tt = m.moe_weight_table(c, [tl])
+    m13 = (2 * ((I + 127) // 128 * 128) // 64) * ((H + 31) // 32) * 4096
+    m2 = ((H + 63) // 64) * ((I + 31) // 32) * 4096
+    assert E * (m13 + m2) + ((2 * Ish // 64) * (H // 32) + (H // 64) * (Ish // 32)) * 4096 == \
+        m.moe_tiled_weights_bytes(c)
+    for e in range(E):
+        assert tt[e * 6:(e + 1) * 6] == [base[0] + e * m13, 0, base[2] + e * m2, 0, 0, 0]
+    assert tt[E * 6:(E + 1) * 6] == [base[3], 0, base[5], 0, 0, 0]
+    # fp8 experts: codes are bytes, one fp32 scale per 128 x 128 block
+    f8 = m.make_cfg(T=8, H=H, E=E, k=1, I=I, w_dtype=m.MOE_FP8_E4M3)
+    w8 = m.moe_weights(w_gate=base[0], w_up=base[1], w_down=base[2], s_gate=base[3], s_up=base[4],
+                       s_down=base[5])
+    t8 = m.moe_weight_table(f8, [w8])
+    nsc = (I // 128) * (H // 128) * 4
+    for e in range(E):
+        assert t8[e * 6:(e + 1) * 6] == [base[0] + e * I * H, base[1] + e * I * H, base[2] + e * I * H,
+                                         base[3] + e * nsc, base[4] + e * nsc, base[5] + e * nsc]
+    # refusals
+    f32 = m.make_cfg(T=8, H=H, E=E, k=1, I=I, act_dtype=m.MOE_F32)
+    with pytest.raises(m.MoeError) as ex:
+        m.moe_weight_table(f32, [lay0])
+    assert ex.value.status == m.MOE_ERR_UNSUPPORTED
+    bad = m.moe_weights(w_gate=base[0], w_up=base[1], w_down=base[2], table=0x2000, layer=0x3000, n_layers=1)
+    with pytest.raises(m.MoeError) as ex:
+        m.moe_weight_table(c, [bad])
+    assert ex.value.status == m.MOE_ERR_INVALID_ARG
+    out = (ctypes.c_void_p * 12)()
+    assert lib.moe_weight_table(ctypes.byref(c), (m.moe_weights * 1)(lay0), 0, out) == m.MOE_ERR_INVALID_ARG
+    # a table call is checked on its own fields, the contiguous pointers ignored
+    fake = ctypes.c_void_p(0x100000)
+    cf = m.make_cfg(T=8, H=H, E=E, k=1, I=I)
+    for w, code, msg in ((m.moe_weights(table=0x100000, n_layers=1), m.MOE_ERR_INVALID_ARG, "layer"),
+                         (m.moe_weights(table=0x100000, layer=0x100000, n_layers=0), m.MOE_ERR_INVALID_ARG,
+                          "n_layers"),
+                         (m.moe_weights(table=0x100004, layer=0x100000, n_layers=1), m.MOE_ERR_INVALID_ARG,
+                          "table")):
+        st = lib.moe_grouped_ffn(ctypes.byref(cf), 32, fake, None, fake, None, ctypes.byref(w), None, fake, None,
+                                 fake, 1 << 30, None)
+        assert st == code and msg in m.moe_last_error(), m.moe_last_error()
+    w = m.moe_weights(table=0x100000, layer=0x100000, n_layers=1)
+    cf32 = m.make_cfg(T=8, H=H, E=E, k=1, I=I, act_dtype=m.MOE_F32)
+    st = lib.moe_grouped_ffn(ctypes.byref(cf32), 32, fake, None, fake, None, ctypes.byref(w), None, fake, None,
+                             fake, 1 << 30, None)
+    assert st == m.MOE_ERR_UNSUPPORTED
+    st = lib.moe_tile_weights(ctypes.byref(cf), ctypes.byref(m.moe_weights(w_gate=0x100000, w_up=0x100000,
+                                                                              w_down=0x100000, table=0x100000,
+                                                                              layer=0x100000, n_layers=1)),
+                              fake, 1 << 40, ctypes.byref(m.moe_weights()), None)
+    assert st == m.MOE_ERR_INVALID_ARG
