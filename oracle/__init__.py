@@ -13,7 +13,9 @@ numerical values are fixed by nothing but the oracle itself ("parity unpinned"
 beyond the invariants; the pins cover each step separately).
 
 Array conventions: fp32 arrays are float32; bf16 arrays are uint16 bit
-patterns; e4m3 arrays are uint8 codes.  Matrices are [out][in] row-major.
+patterns; e4m3 arrays are uint8 codes; MXFP4 matrices are packed E2M1 codes
+(uint8, two per byte, the even element in the low nibble) with uint8 E8M0
+scales per 32 elements of a row.  Matrices are [out][in] row-major.
 """
 from __future__ import annotations
 
@@ -73,6 +75,14 @@ def lib():
         L.orc_expert_ffn.restype = None
         L.orc_expert_ffn_fp8.argtypes = [i64, i64, i64, P, P, P, P, P, P, P, P, P, P]
         L.orc_expert_ffn_fp8.restype = None
+        L.orc_e2m1_to_f64.argtypes = [ctypes.c_uint8]
+        L.orc_e2m1_to_f64.restype = dbl
+        L.orc_e8m0_to_f64.argtypes = [ctypes.c_uint8]
+        L.orc_e8m0_to_f64.restype = dbl
+        L.orc_mxfp4_dequant.argtypes = [i64, i64, P, P, P]
+        L.orc_mxfp4_dequant.restype = None
+        L.orc_expert_ffn_mxfp4.argtypes = [i64, i64, i64, P, P, P, P, P, P, P, P, P, P]
+        L.orc_expert_ffn_mxfp4.restype = None
         L.orc_combine.argtypes = [i64, i32, i64, P, P, P, P, P]
         L.orc_combine.restype = None
         L.orc_layer.argtypes = [i64, i64, i32, i32, i64, i32, i32, i32, i32, i32, dbl,
@@ -247,6 +257,47 @@ def expert_ffn_fp8(xq, xs, wg, sg, wu, su, wd, sd, return_h: bool = False):
     a = np.empty((n, I), dtype=np.float64) if return_h else None
     lib().orc_expert_ffn_fp8(n, H, I, _p(xq), _p(xs), _p(wg), _p(sg), _p(wu), _p(su),
                              _p(wd), _p(sd), _p(y), _p(a))
+    return (y, a) if return_h else y
+
+
+def e2m1_to_f64(codes) -> np.ndarray:
+    """OCP MX FP4 E2M1 code (low 4 bits) -> value."""
+    L = lib()
+    c = np.asarray(codes, dtype=np.uint8)
+    return np.array([L.orc_e2m1_to_f64(int(v) & 0xF) for v in c.ravel()]).reshape(c.shape)
+
+
+def e8m0_to_f64(codes) -> np.ndarray:
+    """OCP MX E8M0 scale code -> 2^(code - 127) (255: NaN)."""
+    L = lib()
+    c = np.asarray(codes, dtype=np.uint8)
+    return np.array([L.orc_e8m0_to_f64(int(v)) for v in c.ravel()]).reshape(c.shape)
+
+
+def mxfp4_to_f64(codes, scales) -> np.ndarray:
+    """Dequantised MXFP4 matrix [rows][K] from packed codes [rows][K/2] (the
+    low nibble holds the even element) and E8M0 scales [rows][K/32]."""
+    codes, scales = _c(np.asarray(codes, np.uint8)), _c(np.asarray(scales, np.uint8))
+    rows, K = codes.shape[0], codes.shape[1] * 2
+    assert K % 32 == 0 and scales.shape == (rows, K // 32)
+    out = np.empty((rows, K), dtype=np.float64)
+    lib().orc_mxfp4_dequant(rows, K, _p(codes), _p(scales), _p(out))
+    return out
+
+
+def expert_ffn_mxfp4(xq, xs, wg, sg, wu, su, wd, sd, return_h: bool = False):
+    """y [n][H] (fp64) of one SwiGLU expert on e4m3 rows with MXFP4 weights
+    (packed codes wg, wu [I][H/2], wd [H][I/2]; E8M0 scales sg, su [I][H/32],
+    sd [H][I/32]); see orc_expert_ffn_mxfp4."""
+    xq, xs, wg, sg, wu, su, wd, sd = (_c(a) for a in (xq, xs, wg, sg, wu, su, wd, sd))
+    n, H = xq.shape
+    I = wg.shape[0]
+    assert H % 128 == 0 and I % 128 == 0 and xs.shape == (n, H // 128)
+    assert wg.shape == (I, H // 2) and sg.shape == (I, H // 32) and wd.shape == (H, I // 2) and sd.shape == (H, I // 32)
+    y = np.empty((n, H), dtype=np.float64)
+    a = np.empty((n, I), dtype=np.float64) if return_h else None
+    lib().orc_expert_ffn_mxfp4(n, H, I, _p(xq), _p(xs), _p(wg), _p(sg), _p(wu), _p(su), _p(wd), _p(sd),
+                               _p(y), _p(a))
     return (y, a) if return_h else y
 
 

@@ -516,6 +516,94 @@ void orc_expert_ffn_fp8(int64_t n, int64_t H, int64_t I, const uint8_t *xq, cons
     }
 }
 
+/* ------------------------------------------------------- MXFP4 weights
+ * The low-precision expert weights of the DWDP page (appendix A4: the MoE
+ * weights of its DeepSeek-R1 checkpoint are 4-bit floats with block scales)
+ * in the OCP Microscaling (MX) v1.0 form that gfx950's scaled MFMA reads:
+ * FP4 E2M1 elements, one E8M0 scale per 32 consecutive elements of a row.
+ *   E2M1: sign bit 3, exponent bits 2..1 (bias 1), mantissa bit 0;
+ *         exponent 0: (-1)^s * m / 2;  else (-1)^s * 2^(e - 1) * (1 + m / 2).
+ *   E8M0: 2^(code - 127); code 255 is NaN.
+ * A matrix [rows][K] is stored as packed codes [rows][K / 2] (element k in
+ * byte k / 2, the low nibble for even k) and scales [rows][K / 32]. */
+double orc_e2m1_to_f64(uint8_t c) {
+    double sign = (c & 0x8) ? -1.0 : 1.0;
+    int e = (c >> 1) & 0x3, m = c & 0x1;
+    if (e == 0) return sign * 0.5 * (double)m;
+    return sign * ldexp(1.0 + 0.5 * (double)m, e - 1);
+}
+
+double orc_e8m0_to_f64(uint8_t c) { return c == 255 ? NAN : ldexp(1.0, (int)c - 127); }
+
+/* Dequantised MXFP4 matrix: out[r][k] = e2m1(code of (r, k)) * e8m0(scale[r][k / 32]). */
+void orc_mxfp4_dequant(int64_t rows, int64_t K, const uint8_t *codes, const uint8_t *scales, double *out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t k = 0; k < K; ++k) {
+            uint8_t b = codes[r * (K / 2) + k / 2];
+            uint8_t c = (k & 1) ? (uint8_t)(b >> 4) : (uint8_t)(b & 0xF);
+            out[r * K + k] = orc_e2m1_to_f64(c) * orc_e8m0_to_f64(scales[r * (K / 32) + k / 32]);
+        }
+}
+
+/* One SwiGLU expert on e4m3 rows (1 x 128 fp32 scales, as orc_expert_ffn_fp8)
+ * with MXFP4 weights: the same steps as orc_expert_ffn_fp8 -- fp64 sums, the
+ * intermediate requantised per row and 128 columns to e4m3 -- with each weight
+ * the dequantised MXFP4 value above.  Gate/up [I][H], down [H][I]. */
+void orc_expert_ffn_mxfp4(int64_t n, int64_t H, int64_t I, const uint8_t *xq, const float *xs,
+                          const uint8_t *wg, const uint8_t *sg, const uint8_t *wu, const uint8_t *su,
+                          const uint8_t *wd, const uint8_t *sd, double *y, double *a_out) {
+    int64_t HB = H / 128, IB = I / 128;
+    double *Wg = (double *)malloc(sizeof(double) * (size_t)(I * H));
+    double *Wu = (double *)malloc(sizeof(double) * (size_t)(I * H));
+    double *Wd = (double *)malloc(sizeof(double) * (size_t)(H * I));
+    if (Wg && Wu && Wd) {
+        orc_mxfp4_dequant(I, H, wg, sg, Wg);
+        orc_mxfp4_dequant(I, H, wu, su, Wu);
+        orc_mxfp4_dequant(H, I, wd, sd, Wd);
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int64_t r = 0; r < n; ++r) {
+            double *xr = (double *)malloc(sizeof(double) * (size_t)H);
+            double *a = (double *)malloc(sizeof(double) * (size_t)I);
+            if (xr && a) {
+                for (int64_t h = 0; h < H; ++h)
+                    xr[h] = orc_e4m3_to_f64(xq[r * H + h]) * (double)xs[r * HB + h / 128];
+                for (int64_t i = 0; i < I; ++i) {
+                    double g = 0.0, u = 0.0;
+                    for (int64_t h = 0; h < H; ++h) {
+                        g += xr[h] * Wg[i * H + h];
+                        u += xr[h] * Wu[i * H + h];
+                    }
+                    a[i] = silu(g) * u;
+                    if (a_out) a_out[r * I + i] = a[i];
+                }
+                for (int64_t b = 0; b < IB; ++b) {
+                    float amax = 0.0f;
+                    for (int64_t i = b * 128; i < (b + 1) * 128; ++i) {
+                        float v = fabsf((float)a[i]);
+                        if (v > amax) amax = v;
+                    }
+                    float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+                    for (int64_t i = b * 128; i < (b + 1) * 128; ++i) {
+                        float q = (float)a[i] / s;
+                        a[i] = orc_e4m3_to_f64(orc_e4m3_rne_sat((double)q)) * (double)s;
+                    }
+                }
+                for (int64_t h = 0; h < H; ++h) {
+                    double acc = 0.0;
+                    for (int64_t i = 0; i < I; ++i) acc += a[i] * Wd[h * I + i];
+                    y[r * H + h] = acc;
+                }
+            }
+            free(xr);
+            free(a);
+        }
+    }
+    free(Wg);
+    free(Wu);
+    free(Wd);
+}
+
 /* -------------------------------------------------------------- combine */
 
 /* out[t][h] = sum_{j < k} w[t][j] * y_rows[tok_row[t][j]][h]  (+ y_shared[t][h]) */

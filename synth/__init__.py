@@ -319,6 +319,43 @@ def fp8_expert_weights(cfg: MoeShape, e: int, device="cpu"):
     return tuple(out)
 
 
+def quantize_mxfp4(w: torch.Tensor):
+    """OCP MX v1.0 conversion of an fp32 matrix [R][C] (C a multiple of 32) to
+    MXFP4: per 32 consecutive elements of a row, the shared exponent
+    x = floor(log2(max|w|)) - 2 (2: the largest E2M1 exponent) as an E8M0 code
+    x + 127 (127 for an all-zero block), and each element w / 2^x rounded to
+    the nearest E2M1 value (ties to even, saturating at +-6).  Returns (packed
+    codes uint8 [R][C/2], the even element in the low nibble; scales uint8
+    [R][C/32])."""
+    R, C = w.shape
+    wb = w.view(R, C // 32, 32).to(torch.float32)
+    amax = wb.abs().amax(dim=2)
+    e = torch.where(amax > 0, torch.floor(torch.log2(torch.where(amax > 0, amax, torch.ones_like(amax)))) - 2,
+                    torch.zeros_like(amax))
+    v = wb / torch.exp2(e)[:, :, None]
+    a = v.abs()
+    # E2M1 magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6 (codes 0..7); a tie goes to the even code
+    idx = ((a > 0.25).to(torch.int32) + (a >= 0.75).to(torch.int32) + (a > 1.25).to(torch.int32)
+           + (a >= 1.75).to(torch.int32) + (a > 2.5).to(torch.int32) + (a >= 3.5).to(torch.int32)
+           + (a > 5.0).to(torch.int32))
+    code = (idx | torch.where(v < 0, 8, 0).to(torch.int32)).view(R, C)
+    packed = (code[:, 0::2] | (code[:, 1::2] << 4)).to(torch.uint8)
+    return packed, (e + 127).to(torch.uint8)
+
+
+def mxfp4_expert_weights(cfg: MoeShape, e: int, device="cpu"):
+    """MXFP4 codes and E8M0 scales of expert e, from the same fp32 draws as
+    fp8_expert_weights: (wg, sg, wu, su, wd, sd), wg/wu [I][H/2], wd [H][I/2],
+    scales [out][in/32]."""
+    out = []
+    for name, shape, fan in (("gate", (cfg.I, cfg.H), cfg.H), ("up", (cfg.I, cfg.H), cfg.H),
+                             ("down", (cfg.H, cfg.I), cfg.I)):
+        w = normal(stream_key(cfg.seed, "expert", e, name), shape, 1.0 / math.sqrt(fan),
+                   device, torch.float32)
+        out += list(quantize_mxfp4(w))
+    return tuple(out)
+
+
 def fp8_rows(cfg: MoeShape, n: int, device="cpu", start: int = 0):
     """Dispatched activation rows start .. start+n-1: N(0, 1) quantised with
     1x128 row scales.  Returns (codes uint8 [n][H], scales fp32 [n][H/128])."""

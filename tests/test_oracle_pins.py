@@ -527,3 +527,86 @@ def test_layer_composes_steps():
             e = ids[t, j]
             ref[t] += w[t, j] * _np_ffn(X[t:t + 1], _val(wg[e]), _val(wu[e]), _val(wd[e]))[0]
     np.testing.assert_allclose(r["out"], ref, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------------ MXFP4
+
+def test_e2m1_and_e8m0_decode_closed_forms():
+    """E2M1 (OCP MX v1.0): sign, 2 exponent bits with bias 1, 1 mantissa bit;
+    the eight magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4, 6.  E8M0: 2^(c - 127),
+    255 is NaN."""
+    got = oracle.e2m1_to_f64(np.arange(16))
+    assert list(got[:8]) == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    assert list(got[8:]) == [-0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0]
+    assert math.copysign(1.0, got[8]) == -1.0
+    sc = oracle.e8m0_to_f64(np.arange(256))
+    assert all(sc[c] == math.ldexp(1.0, c - 127) for c in range(255))
+    assert math.isnan(sc[255])
+
+
+def test_mxfp4_dequant_brute_force():
+    """Packed codes: element k of a row in byte k // 2, the low nibble for even
+    k; scale block k // 32.  Checked element by element with Python loops."""
+    rng = np.random.default_rng(3)
+    rows, K = 3, 96
+    codes = rng.integers(0, 256, size=(rows, K // 2), dtype=np.uint8)
+    scales = rng.integers(110, 140, size=(rows, K // 32), dtype=np.uint8)
+    got = oracle.mxfp4_to_f64(codes, scales)
+    mags = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    for r in range(rows):
+        for k in range(K):
+            b = int(codes[r, k // 2])
+            c = (b >> 4) if k % 2 else (b & 0xF)
+            v = (-1.0 if c & 8 else 1.0) * mags[c & 7] * 2.0 ** (int(scales[r, k // 32]) - 127)
+            assert got[r, k] == v, (r, k)
+
+
+def test_quantize_mxfp4_rule():
+    """synth.quantize_mxfp4 follows the OCP conversion: the shared exponent is
+    floor(log2(amax)) - 2, so the block maximum maps into [4, 8) and every
+    element lies within half an E2M1 step of its code;
+    an all-zero block gets scale 127 and zero codes; past 6 units the code
+    saturates."""
+    w = torch.randn(4, 128, generator=torch.Generator().manual_seed(2)) * 0.05
+    w[1, 32:64] = 0.0
+    w[2, :32] = torch.tensor([1.25, 0.75, 2.5, 3.5, 5.0, 0.25, -1.75, -6.5] * 4) * 0.5   # ties at scale 2^-1
+    q, s = synth.quantize_mxfp4(w)
+    deq = oracle.mxfp4_to_f64(q.numpy(), s.numpy())
+    wf = w.double().numpy()
+    assert s[1, 1] == 127 and not q[1, 16:32].any()
+    blk = wf.reshape(4, 4, 32)
+    amax = np.abs(blk).max(2)
+    x = np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2
+    assert np.array_equal(s.numpy().astype(np.int64), np.where(amax > 0, x + 127, 127).astype(np.int64))
+    unit = np.repeat(2.0 ** x, 32, axis=1)
+    v = wf / unit
+    sat = np.abs(v) > 6.0
+    assert np.array_equal(deq[sat], np.sign(v[sat]) * 6.0 * unit[sat])  # saturated at +-6
+    half = np.where(np.abs(v) < 2, 0.25, np.where(np.abs(v) < 4, 0.5, 1.0)) * unit  # half the E2M1 spacing
+    assert np.all(np.abs(deq - wf)[~sat] <= half[~sat])
+    # ties to even: 1.25 -> 1, 0.75 -> 1, 2.5 -> 2, 3.5 -> 4, 5 -> 4, 0.25 -> 0, -1.75 -> -2; -6.5 saturates
+    assert list(deq[2, :8]) == [0.5, 0.5, 1.0, 2.0, 2.0, 0.0, -1.0, -3.0]
+
+
+def test_expert_ffn_mxfp4_reduces_to_fp8_with_block_constant_scales():
+    """MXFP4 weights whose E8M0 scales are constant over every 128 x 128 block
+    are exactly e4m3 weights (each E2M1 value is an e4m3 value) with the fp32
+    block scale 2^(c - 127): the two oracle functions must then agree bit for
+    bit.  Scales varying inside a block are covered by the dequantisation pin."""
+    rng = np.random.default_rng(7)
+    cfg = synth.config("c5_dsv3_ep_fp8", H=256, I=384)
+    H, I = cfg.H, cfg.I
+    xq, xs = (to_np(t) for t in synth.fp8_rows(cfg, 4))
+
+    def mat(R, C):
+        codes = rng.integers(0, 256, size=(R, C // 2), dtype=np.uint8)
+        sb = rng.integers(120, 132, size=(R // 128, C // 128), dtype=np.uint8)
+        scales = np.repeat(np.repeat(sb, 128, 0), 4, 1)
+        vals = oracle.mxfp4_to_f64(codes, np.full_like(scales, 127))
+        e4 = oracle.e4m3_rne_sat(vals.ravel()).reshape(R, C)
+        assert np.array_equal(e4m3_f64(e4), vals)
+        return codes, scales, e4, np.ldexp(1.0, sb.astype(np.int64) - 127).astype(np.float32)
+    g, u, d = mat(I, H), mat(I, H), mat(H, I)
+    y4 = oracle.expert_ffn_mxfp4(xq, xs, g[0], g[1], u[0], u[1], d[0], d[1])
+    y8 = oracle.expert_ffn_fp8(xq, xs, g[2], g[3], u[2], u[3], d[2], d[3])
+    assert np.array_equal(y4, y8)
