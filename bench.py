@@ -59,6 +59,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--rowmajor-weights", action="store_true",
                    help="time the row-major weight layout instead of the tiled one")
+    p.add_argument("--fp4-weights", action="store_true",
+                   help="with the fp8 FFN workload or --fp8-experts: MXFP4 expert weights (E2M1, E8M0 per 32) "
+                        "instead of e4m3 ones")
     p.add_argument("--weight-table", type=int, default=0, metavar="N",
                    help="read the expert weights through a device pointer table of N layers (the N layers' "
                         "tables point at the one weight set, each in its own expert order) and run the steps "
@@ -399,12 +402,15 @@ def bench_fp8_ffn(a, s, dev):
         raise SystemExit("--traffic-run profiles the bf16 layer")
     t_gen = time.time()
     counts = synth.fp8_counts(s)
-    wq = [synth.fp8_expert_weights(s, e, dev) for e in range(s.E)]
+    f4 = a.fp4_weights
+    gen = synth.mxfp4_expert_weights if f4 else synth.fp8_expert_weights
+    wq = [gen(s, e, dev) for e in range(s.E)]
     wg, sg, wu, su, wd, sd = (torch.stack([w[i] for w in wq]) for i in range(6))
     del wq
     xq, xs = synth.fp8_rows(s, s.T, dev)
     offs = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32, device=dev)
-    c = moe.make_cfg(T=s.T, H=s.H, E=s.E, k=1, I=s.I, act_dtype=moe.MOE_FP8_E4M3, y_dtype=moe.MOE_BF16)
+    c = moe.make_cfg(T=s.T, H=s.H, E=s.E, k=1, I=s.I, act_dtype=moe.MOE_FP8_E4M3, y_dtype=moe.MOE_BF16,
+                     w_dtype=moe.MOE_FP4_E2M1 if f4 else moe.MOE_FP8_E4M3)
     y = torch.empty((s.T, s.H), dtype=torch.bfloat16, device=dev)
     ws = moe.workspace(c, moe.MOE_STAGE_FFN, dev, n_rows_cap=s.T)
     w = moe.weights(wg, wu, wd, s_gate=sg, s_up=su, s_down=sd)
@@ -429,10 +435,12 @@ def bench_fp8_ffn(a, s, dev):
     ms = ev0.elapsed_time(ev1) / a.steps
     flop = 6.0 * s.H * s.I * s.T
     tflops = flop / (ms * 1e-3) / 1e12
-    # algorithmic bytes: e4m3 weights and their block scales, the rows and their
-    # scales read once, bf16 y written once
+    # algorithmic bytes: the weights (e4m3 with 128x128 fp32 scales, or MXFP4
+    # at half a byte with one E8M0 byte per 32), the rows and their scales read
+    # once, bf16 y written once
     KB1, KB2 = s.H // 128, s.I // 128
-    nbytes = (3.0 * s.E * s.H * s.I + 3.0 * s.E * KB1 * KB2 * 4 + s.T * s.H + s.T * KB1 * 4 + s.T * s.H * 2)
+    w_bytes = 3.0 * s.E * s.H * s.I * (0.5 + 1.0 / 32) if f4 else 3.0 * s.E * s.H * s.I + 3.0 * s.E * KB1 * KB2 * 4
+    nbytes = w_bytes + s.T * s.H + s.T * KB1 * 4 + s.T * s.H * 2
     t_mfma = flop / (PEAK_FP8_TFLOPS * 1e12)
     t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
     assert t_mfma >= t_hbm, "the fp8 FFN workload is expected to be compute-bound"
@@ -440,9 +448,10 @@ def bench_fp8_ffn(a, s, dev):
         "metric": "grouped FFN TFLOP/s (1 GPU, fp8 expert-parallel share of a DeepSeek-V3 prefill layer)",
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp8_e4m3", "data": "synthetic",
+        "dtype": "fp8_e4m3 x mxfp4" if f4 else "fp8_e4m3", "data": "synthetic",
         "config": {"workload": a.workload, "rows": s.T, "H": s.H, "E_local": s.E, "I": s.I,
-                   "counts": [int(v) for v in counts], "scales": "1x128 rows, 128x128 weights",
+                   "counts": [int(v) for v in counts],
+                   "scales": "1x128 rows, E8M0 per 32 weights (MXFP4)" if f4 else "1x128 rows, 128x128 weights",
                    "out_dtype": "bf16"},
         "tokens_per_s": round(s.T / (ms * 1e-3), 1),
         "wall_s_timed": round(wall, 3),
@@ -474,16 +483,25 @@ def bench_fp8_layer(a, s, dev):
               score_fn=moe.MOE_SCORE_SIGMOID if s.score == "sigmoid" else moe.MOE_SCORE_SOFTMAX,
               renormalize=s.renormalize, routed_scale=s.routed_scale, has_shared=s.shared, I_shared=I_sh,
               y_dtype=moe.MOE_BF16, out_dtype=moe.MOE_BF16)
-    c = moe.make_cfg(**kw, act_dtype=moe.MOE_BF16, w_dtype=moe.MOE_FP8_E4M3)
+    f4 = a.fp4_weights
+    wdt = moe.MOE_FP4_E2M1 if f4 else moe.MOE_FP8_E4M3
+    c = moe.make_cfg(**kw, act_dtype=moe.MOE_BF16, w_dtype=wdt)
     t_gen = time.time()
     x, w_r, bias = synth.router_inputs(s, dev)
-    wg = torch.empty((E, I, H), dtype=torch.uint8, device=dev)
-    wu, wd = torch.empty_like(wg), torch.empty((E, H, I), dtype=torch.uint8, device=dev)
-    sg = torch.empty((E, I // 128, H // 128), device=dev)
-    su, sd = torch.empty_like(sg), torch.empty((E, H // 128, I // 128), device=dev)
+    gen = synth.mxfp4_expert_weights if f4 else synth.fp8_expert_weights
+    if f4:
+        wg = torch.empty((E, I, H // 2), dtype=torch.uint8, device=dev)
+        wu, wd = torch.empty_like(wg), torch.empty((E, H, I // 2), dtype=torch.uint8, device=dev)
+        sg = torch.empty((E, I, H // 32), dtype=torch.uint8, device=dev)
+        su, sd = torch.empty_like(sg), torch.empty((E, H, I // 32), dtype=torch.uint8, device=dev)
+    else:
+        wg = torch.empty((E, I, H), dtype=torch.uint8, device=dev)
+        wu, wd = torch.empty_like(wg), torch.empty((E, H, I), dtype=torch.uint8, device=dev)
+        sg = torch.empty((E, I // 128, H // 128), device=dev)
+        su, sd = torch.empty_like(sg), torch.empty((E, H // 128, I // 128), device=dev)
     for e in range(E):
-        wg[e], sg[e], wu[e], su[e], wd[e], sd[e] = synth.fp8_expert_weights(s, e, dev)
-    sh = synth.fp8_expert_weights(s.with_(I=I_sh), E, dev) if s.shared else (None,) * 6
+        wg[e], sg[e], wu[e], su[e], wd[e], sd[e] = gen(s, e, dev)
+    sh = gen(s.with_(I=I_sh), E, dev) if s.shared else (None,) * 6
     w = moe.weights(wg, wu, wd, s_gate=sg, s_up=su, s_down=sd, sh_gate=sh[0], sh_up=sh[2], sh_down=sh[4],
                     sh_s_gate=sh[1], sh_s_up=sh[3], sh_s_down=sh[5])
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
@@ -511,9 +529,9 @@ def bench_fp8_layer(a, s, dev):
     # ---- the same work as stage calls: route, quantise, permute (e4m3 rows,
     # m_tile 16), the routed grouped FFN, the shared one (one group of T rows),
     # combine
-    cq = moe.make_cfg(**dict(kw, has_shared=False, I_shared=0), act_dtype=moe.MOE_FP8_E4M3, m_tile=16)
+    cq = moe.make_cfg(**dict(kw, has_shared=False, I_shared=0), act_dtype=moe.MOE_FP8_E4M3, w_dtype=wdt, m_tile=16)
     c1 = moe.make_cfg(**dict(kw, E=1, k=1, n_groups=1, topk_groups=1, I=max(I_sh, 128), has_shared=False,
-                             I_shared=0), act_dtype=moe.MOE_FP8_E4M3)
+                             I_shared=0), act_dtype=moe.MOE_FP8_E4M3, w_dtype=wdt)
     rows = moe.moe_max_rows(cq)
     i32 = dict(dtype=torch.int32, device=dev)
     ids, tw = torch.empty((T, k), **i32), torch.empty((T, k), dtype=torch.float32, device=dev)
@@ -533,8 +551,7 @@ def bench_fp8_layer(a, s, dev):
     ws_1 = moe.workspace(c1, moe.MOE_STAGE_FFN, dev, n_rows_cap=T) if s.shared else None
     names = ["route", "quantise", "permute", "grouped_ffn", "combine"]
 
-    def stage_step(evs, i):
-        w = ws_layers[i % len(ws_layers)]
+    def stage_step(evs):
         evs[0].record(stream)
         moe.moe_route(c, x, w_r, bias, None, None, ids, tw, ws_r, stream)
         evs[1].record(stream)
@@ -562,7 +579,10 @@ def bench_fp8_layer(a, s, dev):
     KB1, KB2 = H // 128, I // 128
     ffn_flop = 6.0 * H * I * R + 6.0 * H * I_sh * T
     layer_flop = ffn_flop + 2.0 * T * H * E
-    w_bytes = 3.0 * E * H * I + 3.0 * E * KB1 * KB2 * 4 + 3.0 * H * I_sh + 3.0 * KB1 * (I_sh // 128) * 4
+    if f4:
+        w_bytes = (3.0 * E * H * I + 3.0 * H * I_sh) * (0.5 + 1.0 / 32)
+    else:
+        w_bytes = 3.0 * E * H * I + 3.0 * E * KB1 * KB2 * 4 + 3.0 * H * I_sh + 3.0 * KB1 * (I_sh // 128) * 4
     bytes_ = {
         "route": T * H * 2 + E * H * 2 + T * k * 8,
         "quantise": T * H * 2 + T * H + T * KB1 * 4,
@@ -598,9 +618,11 @@ def bench_fp8_layer(a, s, dev):
     res = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "fp8_e4m3 experts, bf16 activations", "data": "synthetic",
+        "vs_baseline": None, "dtype": ("mxfp4" if f4 else "fp8_e4m3") + " experts, bf16 activations",
+        "data": "synthetic",
         "config": {"workload": a.workload, "T": T, "H": H, "E": E, "k": k, "I": I, "shared_experts": int(s.shared),
-                   "I_shared": I_sh, "experts": "e4m3, 128x128 block scales",
+                   "I_shared": I_sh,
+                   "experts": "MXFP4 (E2M1, E8M0 per 32), e4m3 rows" if f4 else "e4m3, 128x128 block scales",
                    "activations": "bf16, quantised per token (1x128)", "out_dtype": "bf16"},
         "tokens_per_s": round(T / (ms_step * 1e-3), 1),
         "wall_s_timed": round(wall, 3),

@@ -19,7 +19,7 @@ import torch
 
 from . import _ffi
 from ._ffi import (MOE_BF16, MOE_ERR_HIP, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE,
-                   MOE_F32, MOE_FP8_E4M3, MOE_GROUP_MAX, MOE_GROUP_TOP2_SUM, MOE_OK, MOE_SCORE_SIGMOID,
+                   MOE_F32, MOE_FP8_E4M3, MOE_FP4_E2M1, MOE_GROUP_MAX, MOE_GROUP_TOP2_SUM, MOE_OK, MOE_SCORE_SIGMOID,
                    MOE_SCORE_SOFTMAX, MOE_STAGE_FFN, MOE_STAGE_LAYER, MOE_STAGE_PERMUTE, MOE_STAGE_ROUTE,
                    MOE_LAYOUT_ROWMAJOR, MOE_LAYOUT_TILED, MOE_LAYOUT_INDEXED, moe_cfg, moe_weights)
 
@@ -29,7 +29,7 @@ __all__ = [
     "weight_table", "moe_status_string",
     "moe_last_error", "moe_cfg", "moe_weights", "lib_path",
     "MOE_OK", "MOE_ERR_INVALID_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE", "MOE_ERR_HIP",
-    "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3", "MOE_SCORE_SOFTMAX", "MOE_SCORE_SIGMOID",
+    "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3", "MOE_FP4_E2M1", "MOE_SCORE_SOFTMAX", "MOE_SCORE_SIGMOID",
     "MOE_GROUP_TOP2_SUM", "MOE_GROUP_MAX", "MOE_STAGE_ROUTE", "MOE_STAGE_PERMUTE", "MOE_STAGE_FFN",
     "MOE_STAGE_LAYER", "MOE_LAYOUT_ROWMAJOR", "MOE_LAYOUT_TILED", "MOE_LAYOUT_INDEXED", "moe_tiled_weights_bytes",
     "moe_tile_weights", "tile_weights", "moe_x_perm_bytes", "x_perm_buffer",

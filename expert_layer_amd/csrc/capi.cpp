@@ -67,13 +67,18 @@ moe_status check_cfg(const moe_cfg* cp) {
         return fail(MOE_ERR_INVALID_ARG, "I_shared=%d must be a positive multiple of 8", c.I_shared);
     if (c.act_dtype < MOE_F32 || c.act_dtype > MOE_FP8_E4M3)
         return fail(MOE_ERR_INVALID_ARG, "act_dtype=%d", c.act_dtype);
-    const bool fp8x = c.act_dtype == MOE_BF16 && c.w_dtype == MOE_FP8_E4M3;  // fp8 experts, bf16 activations
-    if (c.w_dtype != c.act_dtype && !fp8x)
+    if (c.w_dtype < MOE_F32 || c.w_dtype > MOE_FP4_E2M1) return fail(MOE_ERR_INVALID_ARG, "w_dtype=%d", c.w_dtype);
+    // low-precision experts: e4m3 or MXFP4 weights; with bf16 activations the
+    // layer quantises x per token to e4m3 (fp8x); the grouped FFN takes e4m3 rows
+    const bool lowp = c.w_dtype == MOE_FP8_E4M3 || c.w_dtype == MOE_FP4_E2M1;
+    const bool fp8x = c.act_dtype == MOE_BF16 && lowp;
+    const bool fp4w = c.act_dtype == MOE_FP8_E4M3 && c.w_dtype == MOE_FP4_E2M1;
+    if (c.w_dtype != c.act_dtype && !fp8x && !fp4w)
         return fail(MOE_ERR_UNSUPPORTED, "w_dtype=%d with act_dtype=%d", c.w_dtype, c.act_dtype);
     if (c.y_dtype != MOE_F32 && c.y_dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "y_dtype=%d", c.y_dtype);
     if (c.out_dtype != MOE_F32 && c.out_dtype != MOE_BF16)
         return fail(MOE_ERR_INVALID_ARG, "out_dtype=%d", c.out_dtype);
-    if (c.w_dtype == MOE_FP8_E4M3) {
+    if (lowp) {
         if (c.H % 128 || c.I % 128)
             return fail(MOE_ERR_INVALID_ARG, "fp8 needs H and I multiples of 128 (H=%d, I=%d)", c.H, c.I);
         if (c.H > 16384 || c.I > 16384)
@@ -225,10 +230,11 @@ moe_cfg layer_stage_cfg(const moe_cfg& c) {
 // token, then runs the stages on the fp8 cfg of the quantised rows -- the
 // routed experts as one grouped FFN, the shared expert as a second one over
 // the T quantised tokens (one group).
-bool fp8_experts(const moe_cfg& c) { return c.act_dtype == MOE_BF16 && c.w_dtype == MOE_FP8_E4M3; }
+bool lowp_weights(const moe_cfg& c) { return c.w_dtype == MOE_FP8_E4M3 || c.w_dtype == MOE_FP4_E2M1; }
+bool fp8_experts(const moe_cfg& c) { return c.act_dtype == MOE_BF16 && lowp_weights(c); }
 moe_cfg fp8_routed_cfg(const moe_cfg& c) {
     moe_cfg q = c;
-    q.act_dtype = q.w_dtype = MOE_FP8_E4M3;
+    q.act_dtype = MOE_FP8_E4M3;  // the weights keep their dtype (e4m3 or MXFP4)
     q.has_shared = 0;
     q.I_shared = 0;
     q.m_tile = 16;
@@ -321,7 +327,7 @@ moe_status check_weights(const moe_cfg& c, const moe_weights* w) {
     REQUIRE(w->w_gate, "w->w_gate");
     if (!tiled) REQUIRE(w->w_up, "w->w_up");
     REQUIRE(w->w_down, "w->w_down");
-    if (c.w_dtype == MOE_FP8_E4M3) {
+    if (lowp_weights(c)) {
         REQUIRE(w->s_gate, "w->s_gate");
         REQUIRE(w->s_up, "w->s_up");
         REQUIRE(w->s_down, "w->s_down");
@@ -330,7 +336,7 @@ moe_status check_weights(const moe_cfg& c, const moe_weights* w) {
         REQUIRE(w->sh_gate, "w->sh_gate");
         if (!tiled) REQUIRE(w->sh_up, "w->sh_up");
         REQUIRE(w->sh_down, "w->sh_down");
-        if (c.w_dtype == MOE_FP8_E4M3) {
+        if (lowp_weights(c)) {
             REQUIRE(w->sh_s_gate, "w->sh_s_gate");
             REQUIRE(w->sh_s_up, "w->sh_s_up");
             REQUIRE(w->sh_s_down, "w->sh_s_down");
@@ -559,14 +565,14 @@ moe_status moe_weight_table(const moe_cfg* cfg, const moe_weights* layers, int32
     REQUIRE(layers, "layers");
     REQUIRE(table, "table");
     if (n_layers < 1) return fail(MOE_ERR_INVALID_ARG, "n_layers=%d must be >= 1", n_layers);
-    const bool f8 = c.w_dtype == MOE_FP8_E4M3;
+    const bool f8 = lowp_weights(c), f4 = c.w_dtype == MOE_FP4_E2M1;
     const int G = c.E + (c.has_shared ? 1 : 0);
-    // bytes of one expert's matrices (tiled: the fragment-order gate+up and down)
-    // and floats of its block scales
+    // bytes of one expert's matrices (tiled: the fragment-order gate+up and
+    // down) and of its scales: fp8 one fp32 per 128 x 128 block, MXFP4 one
+    // E8M0 byte per 32 elements of a row
     const moe::TiledSizes t = moe::tiled_sizes(c);
-    const size_t el = (size_t)dtype_bytes(c.w_dtype);
-    const size_t mat = (size_t)c.I * c.H * el;
-    const size_t nsc = f8 ? (size_t)(c.I / 128) * (c.H / 128) : 0;
+    const size_t mat = f4 ? (size_t)c.I * c.H / 2 : (size_t)c.I * c.H * dtype_bytes(c.w_dtype);
+    const size_t nsc = f4 ? (size_t)c.I * (c.H / 32) : f8 ? (size_t)(c.I / 128) * (c.H / 128) * 4 : 0;
     for (int32_t L = 0; L < n_layers; ++L) {
         const moe_weights& w = layers[L];
         if (w.table) return fail(MOE_ERR_INVALID_ARG, "layers[%d].table must be NULL", L);
@@ -579,9 +585,9 @@ moe_status moe_weight_table(const moe_cfg* cfg, const moe_weights* layers, int32
             r[0] = static_cast<const char*>(w.w_gate) + e * m13;
             r[1] = tiled ? nullptr : static_cast<const char*>(w.w_up) + e * mat;
             r[2] = static_cast<const char*>(w.w_down) + e * m2;
-            r[3] = f8 ? w.s_gate + e * nsc : nullptr;
-            r[4] = f8 ? w.s_up + e * nsc : nullptr;
-            r[5] = f8 ? w.s_down + e * nsc : nullptr;
+            r[3] = f8 ? reinterpret_cast<const char*>(w.s_gate) + e * nsc : nullptr;
+            r[4] = f8 ? reinterpret_cast<const char*>(w.s_up) + e * nsc : nullptr;
+            r[5] = f8 ? reinterpret_cast<const char*>(w.s_down) + e * nsc : nullptr;
         }
         if (c.has_shared) {
             const void** r = row + (size_t)c.E * 6;

@@ -45,6 +45,7 @@ constexpr int BM = kFfnBmFp8, BN = 256, BK = 128, NTH = 512;
 constexpr int kChunksA = BM * 8;               // 16-byte chunks of A in one stage (the tallest tile)
 constexpr int kChunksB = BN * 8;               // ... of B
 constexpr int kStageA = kChunksA + 72;         // A, then 288 fp32 row scales (see scale_row)
+constexpr int kScaleB4 = BN * 4;               // MXFP4: chunks of a stage's weight codes; then 8 x 256 B of scales
 static_assert(BM % 32 == 0 && BM <= 224, "three A stages and two B stages must fit in 160 KiB of LDS");
 static_assert(kFfnBmFp8Small == 128, "the load slots below are laid out for 4 and 7 row blocks");
 constexpr uint32_t kOOB = 0x40000000u;         // past every descriptor: the load returns zero
@@ -83,6 +84,16 @@ __device__ __forceinline__ f32x4 mfma16x16x128_fp8(i32x8 a, i32x8 b) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
 }
 
+// FP4 (E2M1) first operand with the lane's E8M0 scale sw, e4m3 second operand
+// at scale 1 (E8M0 127).  The FP4 operand of lane l holds row l % 16, elements
+// 32 (l / 16) + [0, 32) of the K block (low nibble first); the matching e4m3
+// operand of lane l holds column l % 16 at elements 16 (l / 16) + [0, 16) in
+// its first 16 bytes and 64 + 16 (l / 16) + [0, 16) in the last 16 (measured:
+// an in-bounds probe of one MFMA against a host product).
+__device__ __forceinline__ f32x4 mfma16x16x128_fp4_fp8(i32x8 w4, i32x8 a8, int sw) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w4, a8, f32x4{0.f, 0.f, 0.f, 0.f}, 4, 0, 0, sw, 0, 127);
+}
+
 struct Fp8Args {
     const uint8_t* a;       // GEMM1: x rows [rows][H]; GEMM2: h [rows][I]
     const float* a_scale;   // [rows][K / 128]
@@ -117,9 +128,15 @@ __device__ __forceinline__ int scale_row(int pos) {
 
 struct Dma {
     __amdgpu_buffer_rsrc_t ra, rs, rb0, rb1;
-    uint32_t va[4], vb[4], vs;
+    __amdgpu_buffer_rsrc_t rsb0, rsb1;  // MXFP4: the weight rows' E8M0 scales
+    uint32_t va[4], vb[4], vs, vbs;
     int nsteps;  // K blocks
 };
+
+// Loads a wave issues per stage: 4 A chunk loads, the row scales, then 4 B
+// chunk loads (fp8) or 2 B chunk loads and the B scales (MXFP4).
+template <bool W4>
+constexpr int kLoads = W4 ? 8 : 9;
 
 // A loads of stage t into A buffer BUF: 4 chunk loads per lane (8 LDS rows
 // each) and one row-scale load, the same 5 for every wave.  The tile's TB rows
@@ -133,10 +150,31 @@ struct Dma {
 // J = 4 the row-scale load (both into A buffer ABUF), J >= 5 the B chunk loads
 // into B buffer BBUF.  A load that is not real (a stage past the end, rows
 // past the tile) carries an offset past its descriptor and loads zeros.
-template <int MODE, int ABUF, int BBUF, int J, int TB>
+//
+// MXFP4 weights (W4): a weight row of a stage is 64 bytes (four chunks, swizzled
+// by (row >> 2) & 3); J = 5, 6 fill the wave's 32 LDS rows, 16 at a time, and
+// J = 7 loads the rows' E8M0 scales of the stage (one dword a row: the four
+// 32-element blocks) into the wave's 256-byte slot after the codes, lanes
+// 32 .. 63 loading zeros into its unused half.
+template <int MODE, int ABUF, int BBUF, int J, int TB, bool W4>
 __device__ __forceinline__ void dma1(const Dma& d, int t, int wave) {
     const uint32_t k = (uint32_t)t * BK;
     const bool real = t < d.nsteps;
+    if constexpr (W4 && J >= 5) {
+        const __amdgpu_buffer_rsrc_t r = (MODE == 0 && (wave & 1)) ? d.rb1 : d.rb0;
+        if constexpr (J < 7) {
+            constexpr int i = J - 5;
+            const uint32_t off = (!real || d.vb[i] == kOOB) ? kOOB : d.vb[i] + k / 2;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_t)(stgB<BBUF>() + (wave * 2 + i) * 64), 16, off, 0, 0,
+                                                     0);
+        } else {
+            const __amdgpu_buffer_rsrc_t rs = (MODE == 0 && (wave & 1)) ? d.rsb1 : d.rsb0;
+            const uint32_t off = (!real || d.vbs == kOOB) ? kOOB : d.vbs + (uint32_t)t * 4u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_t)(stgB<BBUF>() + kScaleB4 + wave * 16), 4, off, 0, 0,
+                                                     0);
+        }
+        return;
+    }
     if constexpr (J < 4) {
         const uint32_t off = (!real || d.va[J] == kOOB) ? kOOB : d.va[J] + k;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ra, (lds_t)(stgA<ABUF>() + ((wave * 4 + J) % (TB / 8)) * 64), 16,
@@ -155,28 +193,29 @@ __device__ __forceinline__ void dma1(const Dma& d, int t, int wave) {
 }
 
 // The A loads (J = 0..4) of stage t into A buffer BUF.
-template <int MODE, int BUF, int TB>
+template <int MODE, int BUF, int TB, bool W4>
 __device__ __forceinline__ void dma_a(const Dma& d, int t, int wave) {
-    dma1<MODE, BUF, 0, 0, TB>(d, t, wave);
-    dma1<MODE, BUF, 0, 1, TB>(d, t, wave);
-    dma1<MODE, BUF, 0, 2, TB>(d, t, wave);
-    dma1<MODE, BUF, 0, 3, TB>(d, t, wave);
-    dma1<MODE, BUF, 0, 4, TB>(d, t, wave);
+    dma1<MODE, BUF, 0, 0, TB, W4>(d, t, wave);
+    dma1<MODE, BUF, 0, 1, TB, W4>(d, t, wave);
+    dma1<MODE, BUF, 0, 2, TB, W4>(d, t, wave);
+    dma1<MODE, BUF, 0, 3, TB, W4>(d, t, wave);
+    dma1<MODE, BUF, 0, 4, TB, W4>(d, t, wave);
 }
 
-// The B loads (J = 5..8) of stage t into B buffer BUF.
-template <int MODE, int BUF, int TB>
+// The B loads (J = 5 .. kLoads - 1) of stage t into B buffer BUF.
+template <int MODE, int BUF, int TB, bool W4>
 __device__ __forceinline__ void dma_b(const Dma& d, int t, int wave) {
-    dma1<MODE, 0, BUF, 5, TB>(d, t, wave);
-    dma1<MODE, 0, BUF, 6, TB>(d, t, wave);
-    dma1<MODE, 0, BUF, 7, TB>(d, t, wave);
-    dma1<MODE, 0, BUF, 8, TB>(d, t, wave);
+    dma1<MODE, 0, BUF, 5, TB, W4>(d, t, wave);
+    dma1<MODE, 0, BUF, 6, TB, W4>(d, t, wave);
+    dma1<MODE, 0, BUF, 7, TB, W4>(d, t, wave);
+    if constexpr (!W4) dma1<MODE, 0, BUF, 8, TB, W4>(d, t, wave);
 }
 
-// vmcnt(9) with the other counters at zero: a stage's A and B loads and
-// everything before them have landed (the 9 loads of the next stage may be in
+// vmcnt(kLoads) with the other counters at zero: a stage's A and B loads and
+// everything before them have landed (the loads of the next stage may be in
 // flight), and every LDS read of this wave has returned.
-__device__ __forceinline__ void wait_stage() { __builtin_amdgcn_s_waitcnt(9 | 0x0070); }
+template <bool W4>
+__device__ __forceinline__ void wait_stage() { __builtin_amdgcn_s_waitcnt(kLoads<W4> | 0x0070); }
 
 __device__ __forceinline__ i32x8 cat(i32x4 lo, i32x4 hi) {
     return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -210,21 +249,41 @@ __device__ __forceinline__ void read_b(int q, int lane, i32x8 (&b)[4]) {
     for (int cb = 0; cb < 4; ++cb) b[cb] = cat(buf[ib + cb * 128 + plo], buf[ib + cb * 128 + phi]);
 }
 
+// MXFP4: the FP4 fragment of column block cb is the lane's 32 elements of
+// row (16 cb + lane % 16), K block lane / 16 of the stage: logical chunk
+// lane / 16 of the 64-byte LDS row, the low four dwords of the operand; its
+// E8M0 scale is byte lane / 16 of the row's scale dword.
+template <int BUF>
+__device__ __forceinline__ void read_b4(int q, int lane, i32x8 (&b)[4], int (&bs)[4]) {
+    const i32x4* buf = stgB<BUF>();
+    const int l16 = lane & 15, g = lane >> 4;
+    const int ib = ((q & 3) * 64 + l16) * 4 + (g ^ ((l16 >> 2) & 3));  // column block cb: + cb * 64
+    const uint32_t* sc = reinterpret_cast<const uint32_t*>(buf + kScaleB4);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+        const i32x4 v = buf[ib + cb * 64];
+        b[cb] = i32x8{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
+        const int row = (q & 3) * 64 + cb * 16 + l16;  // LDS row; its dword in slot row / 32
+        bs[cb] = (int)((sc[(row >> 5) * 64 + (row & 31)] >> (8 * g)) & 0xFFu);
+    }
+}
+
 // The loads of stage t spread over the row blocks of a K stage, J after the
 // MFMAs of row block rb -- 7 row blocks: two after each of the first three,
 // one after each of the next three; 4 row blocks: three, then two after each
 // of the rest.  A wave that issues all 9 at once stalls until the texture unit
 // has taken them, and the other waves' loads are queued there too.
-template <int RBN>
+template <int RBN, int NJ>
 constexpr int slot_start(int r) {
-    return RBN >= 6 ? (r < 3 ? 2 * r : (r + 3 < 9 ? r + 3 : 9)) : (r == 0 ? 0 : (1 + 2 * r < 9 ? 1 + 2 * r : 9));
+    const int j = RBN >= 6 ? (r < 3 ? 2 * r : r + 3) : (r == 0 ? 0 : 1 + 2 * r);
+    return j < NJ ? j : NJ;
 }
-template <int MODE, int NA, int NB, int RBI, int TB>
+template <int MODE, int NA, int NB, int RBI, int TB, bool W4>
 __device__ __forceinline__ void dma_slot(const Dma& d, int t, int wave) {
-    constexpr int j0 = slot_start<TB / 32>(RBI), j1 = slot_start<TB / 32>(RBI + 1);
-    if constexpr (j0 < j1) dma1<MODE, NA, NB, j0, TB>(d, t, wave);
-    if constexpr (j0 + 1 < j1) dma1<MODE, NA, NB, j0 + 1, TB>(d, t, wave);
-    if constexpr (j0 + 2 < j1) dma1<MODE, NA, NB, j0 + 2, TB>(d, t, wave);
+    constexpr int j0 = slot_start<TB / 32, kLoads<W4>>(RBI), j1 = slot_start<TB / 32, kLoads<W4>>(RBI + 1);
+    if constexpr (j0 < j1) dma1<MODE, NA, NB, j0, TB, W4>(d, t, wave);
+    if constexpr (j0 + 1 < j1) dma1<MODE, NA, NB, j0 + 1, TB, W4>(d, t, wave);
+    if constexpr (j0 + 2 < j1) dma1<MODE, NA, NB, j0 + 2, TB, W4>(d, t, wave);
 }
 
 // One K stage for the RB row blocks of 16 starting at tile row r0: every (row
@@ -233,16 +292,21 @@ __device__ __forceinline__ void dma_slot(const Dma& d, int t, int wave) {
 // columns), with the loads of stage t into A buffer NA and B buffer NB issued
 // between them.  Software-pipelined over row blocks: while the four MFMAs of
 // row block rb run, the fragments of rb + 1 are read and rb - 1 is promoted.
-template <int MODE, int BUF, int NA, int NB, int TB>
+//
+// MXFP4 (W4): the weight operand is FP4 with its E8M0 scales bs applied by the
+// MFMA, and the row fragment takes chunks lane / 16 and lane / 16 + 4 of the
+// row (the K order of the e4m3 operand above); p0 = p1 = 1.
+template <int MODE, int BUF, int NA, int NB, int TB, bool W4>
 __device__ __forceinline__ void kstep(const Dma& d, int t_stage, int wave, int r0, int lane, const i32x8 (&b)[4],
-                                      float p0, float p1, f32x4 (&acc)[TB / 32][4]) {
+                                      const int (&bs)[4], float p0, float p1, f32x4 (&acc)[TB / 32][4]) {
     constexpr int RB = TB / 32;
     // Every access indexes the stage buffer itself (an integer base plus a
     // constant), so the compiler can tell it from the DMA in flight into the
     // other buffers and adds no wait for it.
     const i32x4* buf = stgA<BUF>();
     const int l16 = lane & 15;
-    const int plo = (2 * (lane >> 4)) ^ swz8(l16), phi = plo ^ 1;
+    const int plo = (W4 ? (lane >> 4) : 2 * (lane >> 4)) ^ swz8(l16);
+    const int phi = W4 ? ((lane >> 4) + 4) ^ swz8(l16) : plo ^ 1;
     const int ia = (r0 + l16) * 8;                      // row block rb: + rb * 128
     // this lane's row scales: row blocks 0..3 in chunk 32 h + l16, 4..7 in 32 h + 16 + l16
     const int is = kChunksA + (r0 / (TB / 2)) * 32 + l16;
@@ -256,14 +320,17 @@ __device__ __forceinline__ void kstep(const Dma& d, int t_stage, int wave, int r
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) t[rb & 1][cb] = mfma16x16x128_fp8(b[cb], a[rb & 1]);
+        for (int cb = 0; cb < 4; ++cb) {
+            if constexpr (W4) t[rb & 1][cb] = mfma16x16x128_fp4_fp8(b[cb], a[rb & 1], bs[cb]);
+            else t[rb & 1][cb] = mfma16x16x128_fp8(b[cb], a[rb & 1]);
+        }
         switch (rb) {  // rb is a constant here: the loop is unrolled
-            case 0: dma_slot<MODE, NA, NB, 0, TB>(d, t_stage, wave); break;
-            case 1: dma_slot<MODE, NA, NB, 1, TB>(d, t_stage, wave); break;
-            case 2: dma_slot<MODE, NA, NB, 2, TB>(d, t_stage, wave); break;
-            case 3: dma_slot<MODE, NA, NB, 3, TB>(d, t_stage, wave); break;
-            case 4: dma_slot<MODE, NA, NB, 4, TB>(d, t_stage, wave); break;
-            case 5: dma_slot<MODE, NA, NB, 5, TB>(d, t_stage, wave); break;
+            case 0: dma_slot<MODE, NA, NB, 0, TB, W4>(d, t_stage, wave); break;
+            case 1: dma_slot<MODE, NA, NB, 1, TB, W4>(d, t_stage, wave); break;
+            case 2: dma_slot<MODE, NA, NB, 2, TB, W4>(d, t_stage, wave); break;
+            case 3: dma_slot<MODE, NA, NB, 3, TB, W4>(d, t_stage, wave); break;
+            case 4: dma_slot<MODE, NA, NB, 4, TB, W4>(d, t_stage, wave); break;
+            case 5: dma_slot<MODE, NA, NB, 5, TB, W4>(d, t_stage, wave); break;
             default: break;
         }
         if (rb + 1 < RB) a[(rb + 1) & 1] = cat(buf[ia + (rb + 1) * 128 + plo], buf[ia + (rb + 1) * 128 + phi]);
@@ -277,7 +344,7 @@ __device__ __forceinline__ void kstep(const Dma& d, int t_stage, int wave, int r
 // others (also by a wave whose half of the tile holds no row: its MFMAs carry
 // the stage's loads, and one load schedule for every wave keeps the compiler's
 // count of loads in flight exact).
-template <int MODE, int TB>
+template <int MODE, int TB, bool W4>
 __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int M, int n0) {
     constexpr int RB = TB / 32;
     const int lane = threadIdx.x & 63;
@@ -314,9 +381,10 @@ __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int 
         }
         ge = 0;
     }
-    const size_t mat = (size_t)N * K;
-    d.rb0 = make_rsrc(w0 + (size_t)ge * mat + (size_t)n0 * K, (uint32_t)nlim * (uint32_t)K);
-    d.rb1 = MODE == 0 ? make_rsrc(w1 + (size_t)ge * mat + (size_t)n0 * K, (uint32_t)nlim * (uint32_t)K) : d.rb0;
+    const int KW = W4 ? K / 2 : K;  // bytes of a weight row
+    const size_t mat = (size_t)N * KW;
+    d.rb0 = make_rsrc(w0 + (size_t)ge * mat + (size_t)n0 * KW, (uint32_t)nlim * (uint32_t)KW);
+    d.rb1 = MODE == 0 ? make_rsrc(w1 + (size_t)ge * mat + (size_t)n0 * KW, (uint32_t)nlim * (uint32_t)KW) : d.rb0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int row = wave * 32 + i * 8 + (lane >> 3);  // LDS row this lane fills (B; A modulo TB)
@@ -326,11 +394,34 @@ __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int 
         const int wrow = MODE == 0 ? (wave >> 1) * 32 + i * 8 + (lane >> 3) : row;  // relative to n0
         d.vb[i] = wrow < nlim ? (uint32_t)wrow * (uint32_t)K + logical : kOOB;
     }
+    if constexpr (W4) {
+        // B loads i = 0, 1: LDS rows 32 wave + 16 i + lane / 4, physical chunk
+        // lane % 4 holding logical chunk (lane % 4) ^ ((row >> 2) & 3)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int row = wave * 32 + i * 16 + (lane >> 2);
+            const int wrow = MODE == 0 ? (wave >> 1) * 32 + i * 16 + (lane >> 2) : row;
+            const uint32_t logical = (uint32_t)(((lane & 3) ^ ((row >> 2) & 3)) * 16);
+            d.vb[i] = wrow < nlim ? (uint32_t)wrow * (uint32_t)KW + logical : kOOB;
+        }
+        // E8M0 scales [rows][K / 32]: lane < 32 loads the stage's dword of LDS row 32 wave + lane
+        const uint8_t* sb0 = reinterpret_cast<const uint8_t*>(s0);
+        const uint8_t* sb1 = reinterpret_cast<const uint8_t*>(MODE == 0 ? s1 : s0);
+        const size_t smat = (size_t)N * (K / 32);
+        d.rsb0 = make_rsrc(sb0 + (size_t)ge * smat + (size_t)n0 * (K / 32), (uint32_t)nlim * (uint32_t)(K / 32));
+        d.rsb1 = MODE == 0 ? make_rsrc(sb1 + (size_t)ge * smat + (size_t)n0 * (K / 32),
+                                       (uint32_t)nlim * (uint32_t)(K / 32))
+                           : d.rsb0;
+        const int wrow = MODE == 0 ? (wave >> 1) * 32 + lane : wave * 32 + lane;
+        d.vbs = (lane < 32 && wrow < nlim) ? (uint32_t)wrow * (uint32_t)(K / 32) : kOOB;
+    }
     // weight-block scales of this wave's columns for every K block, lane kb % 64
     // of register kb / 64 holding block kb (K <= 16384): loaded once, then read
     // with readlane, so no vector-memory load besides the DMA runs in the K loop
     int wbase = -1;
-    if (MODE == 0) {
+    if (W4) {
+        // MXFP4: the weight scales are applied by the MFMA
+    } else if (MODE == 0) {
         wbase = (ge * NB + n0 / BK) * KB;
     } else {
         // a wave whose 64 columns lie past N (N not a multiple of 256) reads no scale
@@ -349,6 +440,10 @@ __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int 
         }
     }
     auto wscale = [&](int kb, float& p0, float& p1) {
+        if constexpr (W4) {
+            p0 = p1 = 1.0f;
+            return;
+        }
         const int h = kb >> 6, l = kb & 63;
         p0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(h ? ws0[1] : ws0[0]), l));
         p1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(h ? ws1[1] : ws1[0]), l));
@@ -364,22 +459,24 @@ __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int 
     // stages of one period of both rings and leaves after stage KB - 1.  Loads
     // of stages past the end carry zeros.  Issue order: A0, B0, A1, B1, then per
     // stage s, during its MFMAs: A(s+2) (5 loads), B(s+2) (4).
-    dma_a<MODE, 0, TB>(d, 0, wave);
-    dma_b<MODE, 0, TB>(d, 0, wave);
-    dma_a<MODE, 1, TB>(d, 1, wave);
-    dma_b<MODE, 1, TB>(d, 1, wave);
+    dma_a<MODE, 0, TB, W4>(d, 0, wave);
+    dma_b<MODE, 0, TB, W4>(d, 0, wave);
+    dma_a<MODE, 1, TB, W4>(d, 1, wave);
+    dma_b<MODE, 1, TB, W4>(d, 1, wave);
     i32x8 b[4];
+    int bs[4] = {127, 127, 127, 127};
     int s = 0;
     auto stage = [&](auto ab, auto bb) {
         constexpr int AB = decltype(ab)::value, BB = decltype(bb)::value;
         float p0, p1;
         wscale(s, p0, p1);
-        wait_stage();   // stage s has landed (this wave's loads); this wave's reads of stage s-1 are done
-        barrier_lds();  // ... every wave's: A buffer (s+2) % 3 is free
-        read_b<BB>(q, lane, b);
+        wait_stage<W4>();  // stage s has landed (this wave's loads); this wave's reads of stage s-1 are done
+        barrier_lds();     // ... every wave's: A buffer (s+2) % 3 is free
+        if constexpr (W4) read_b4<BB>(q, lane, b, bs);
+        else read_b<BB>(q, lane, b);
         wait_lgkm0();
         barrier_lds();  // every wave holds its B fragments of stage s: B buffer s % 2 is free
-        kstep<MODE, AB, (AB + 2) % 3, BB, TB>(d, s + 2, wave, r0, lane, b, p0, p1, acc);
+        kstep<MODE, AB, (AB + 2) % 3, BB, TB, W4>(d, s + 2, wave, r0, lane, b, bs, p0, p1, acc);
     };
     using C0 = std::integral_constant<int, 0>;
     using C1 = std::integral_constant<int, 1>;
@@ -493,7 +590,7 @@ __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int 
     }
 }
 
-template <int MODE, int TB>
+template <int MODE, int TB, bool W4>
 __global__ void __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2, 2)))
 ffn_gemm_fp8(Fp8Args p) {
     const int L = xcd_remap(blockIdx.x, p.n_tiles[0] * p.NT);
@@ -504,7 +601,19 @@ ffn_gemm_fp8(Fp8Args p) {
     const int g = td.x, row0 = td.y, M = td.z - td.y;
     const int n0 = MODE == 0 ? wl.y * (BN / 2) : wl.y * BN;
     if (n0 >= p.N || M <= 0) return;
-    run_tile<MODE, TB>(p, g, row0, M, n0);
+    run_tile<MODE, TB, W4>(p, g, row0, M, n0);
+}
+
+template <int MODE>
+void launch_one(bool small, bool w4, int64_t grid, const Fp8Args& a, hipStream_t s) {
+    const dim3 gr((unsigned)grid), bl(NTH);
+    if (w4) {
+        if (small) hipLaunchKernelGGL((ffn_gemm_fp8<MODE, kFfnBmFp8Small, true>), gr, bl, 0, s, a);
+        else hipLaunchKernelGGL((ffn_gemm_fp8<MODE, BM, true>), gr, bl, 0, s, a);
+    } else {
+        if (small) hipLaunchKernelGGL((ffn_gemm_fp8<MODE, kFfnBmFp8Small, false>), gr, bl, 0, s, a);
+        else hipLaunchKernelGGL((ffn_gemm_fp8<MODE, BM, false>), gr, bl, 0, s, a);
+    }
 }
 
 }  // namespace
@@ -518,6 +627,7 @@ hipError_t launch_gemm_fp8(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_c
     const int G = c.E + (c.has_shared ? 1 : 0);
     const bool small = n_rows_cap <= (int64_t)G * 272;
     const int tb = small ? kFfnBmFp8Small : BM;
+    const bool w4 = c.w_dtype == MOE_FP4_E2M1;  // MXFP4 weights, e4m3 rows
     hipError_t e0 = launch_build_tiles(c, offsets, tb, n_rows_cap, wk, s);
     if (e0 != hipSuccess) return e0;
     Fp8Args a{};
@@ -540,10 +650,7 @@ hipError_t launch_gemm_fp8(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_c
     a.K = c.H;
     a.N = c.I;
     const int64_t grid1 = max_tiles * wk.nt1;
-    if (small)
-        hipLaunchKernelGGL((ffn_gemm_fp8<0, kFfnBmFp8Small>), dim3((unsigned)grid1), dim3(NTH), 0, s, a);
-    else
-        hipLaunchKernelGGL((ffn_gemm_fp8<0, BM>), dim3((unsigned)grid1), dim3(NTH), 0, s, a);
+    launch_one<0>(small, w4, grid1, a, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // GEMM2: down projection of h
@@ -562,10 +669,7 @@ hipError_t launch_gemm_fp8(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_c
     a.N = c.H;
     a.out_f32 = c.y_dtype == MOE_F32 ? 1 : 0;
     const int64_t grid2 = max_tiles * wk.nt2;
-    if (small)
-        hipLaunchKernelGGL((ffn_gemm_fp8<1, kFfnBmFp8Small>), dim3((unsigned)grid2), dim3(NTH), 0, s, a);
-    else
-        hipLaunchKernelGGL((ffn_gemm_fp8<1, BM>), dim3((unsigned)grid2), dim3(NTH), 0, s, a);
+    launch_one<1>(small, w4, grid2, a, s);
     return hipGetLastError();
 }
 

@@ -65,7 +65,10 @@ typedef enum moe_status {
 typedef enum moe_dtype {
     MOE_F32 = 0,
     MOE_BF16 = 1,
-    MOE_FP8_E4M3 = 2 /* OCP e4m3: bias 7, max 448, S.1111.111 = NaN, no inf */
+    MOE_FP8_E4M3 = 2, /* OCP e4m3: bias 7, max 448, S.1111.111 = NaN, no inf */
+    MOE_FP4_E2M1 = 3  /* expert weights only: OCP MX FP4 (E2M1) codes, two a byte
+                         (the even element in the low nibble), one E8M0 scale
+                         byte per 32 consecutive elements of a row */
 } moe_dtype;
 
 typedef enum moe_score_fn { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score_fn;

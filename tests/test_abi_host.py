@@ -317,3 +317,36 @@ def test_weight_table_host_addresses():
                                                                               layer=0x100000, n_layers=1)),
                               fake, 1 << 40, ctypes.byref(m.moe_weights()), None)
     assert st == m.MOE_ERR_INVALID_ARG
+
+
+def test_mxfp4_cfg_and_table():
+    """MXFP4 expert weights: accepted with e4m3 rows (grouped FFN) or bf16
+    activations (layer), with H, I multiple of 128; refused with fp32 or bf16
+    rows in the grouped FFN sense (act == w required otherwise); the table
+    helper steps half a byte per element and one scale byte per 32."""
+    kw = dict(T=64, H=7168, E=8, k=2, I=2048)
+    c = m.make_cfg(**kw, act_dtype=m.MOE_FP8_E4M3, w_dtype=m.MOE_FP4_E2M1, y_dtype=m.MOE_BF16)
+    assert m.moe_validate(c) == m.MOE_OK
+    lay = m.make_cfg(**kw, act_dtype=m.MOE_BF16, w_dtype=m.MOE_FP4_E2M1, has_shared=True, I_shared=1024)
+    assert m.moe_validate(lay) == m.MOE_OK
+    assert m.moe_validate(m.make_cfg(**kw, act_dtype=m.MOE_F32, w_dtype=m.MOE_FP4_E2M1)) == m.MOE_ERR_UNSUPPORTED
+    assert m.moe_validate(m.make_cfg(**dict(kw, I=2048 + 64), act_dtype=m.MOE_FP8_E4M3,
+                                     w_dtype=m.MOE_FP4_E2M1)) == m.MOE_ERR_INVALID_ARG
+    assert m.moe_validate(m.make_cfg(**kw, act_dtype=m.MOE_FP4_E2M1)) == m.MOE_ERR_INVALID_ARG
+    assert m.moe_validate(m.make_cfg(**kw, w_dtype=7)) == m.MOE_ERR_INVALID_ARG
+    # the scales are required
+    lib = _ffi.lib()
+    fake = ctypes.c_void_p(0x100000)
+    w = m.moe_weights(w_gate=0x100000, w_up=0x100000, w_down=0x100000)
+    st = lib.moe_grouped_ffn(ctypes.byref(c), 64, fake, fake, fake, None, ctypes.byref(w), None, fake, None, fake,
+                             1 << 40, None)
+    assert st == m.MOE_ERR_INVALID_ARG and "s_gate" in m.moe_last_error()
+    E, H, I = 3, 256, 384
+    f4 = m.make_cfg(T=8, H=H, E=E, k=1, I=I, act_dtype=m.MOE_FP8_E4M3, w_dtype=m.MOE_FP4_E2M1)
+    base = [0x10000000 * (i + 1) for i in range(6)]
+    t = m.moe_weight_table(f4, [m.moe_weights(w_gate=base[0], w_up=base[1], w_down=base[2], s_gate=base[3],
+                                              s_up=base[4], s_down=base[5])])
+    for e in range(E):
+        assert t[e * 6:(e + 1) * 6] == [base[0] + e * I * H // 2, base[1] + e * I * H // 2, base[2] + e * I * H // 2,
+                                        base[3] + e * I * H // 32, base[4] + e * I * H // 32,
+                                        base[5] + e * I * H // 32]
