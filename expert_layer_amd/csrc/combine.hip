@@ -6,7 +6,9 @@
 //
 // One workgroup per token; threads own 8-column chunks and read them from
 // the k expert rows with 16-byte loads.  Pure HBM streaming: the expert rows
-// are read once, the output written once.
+// are read once, the output written once.  The rows are gathered in expert
+// order, so each read is a latency-bound random 16-byte access; the k reads of
+// a chunk are issued together to keep enough of them in flight.
 #include "common.hpp"
 
 namespace moe {
@@ -49,10 +51,48 @@ __device__ __forceinline__ void store8(OT* o, const float (&acc)[8]) {
     }
 }
 
+// Raw 16-byte loads of 8 values (fp32: two), unpacked after every load of a
+// chunk has been issued.
+template <typename YT>
+struct Raw8;
+template <>
+struct Raw8<float> {
+    f32x4 a, b;
+    __device__ __forceinline__ void load(const float* p) {
+        a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+        b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p) + 1);
+    }
+    __device__ __forceinline__ void fma_into(float wj, float (&acc)[8]) const {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[i] = fmaf(wj, a[i], acc[i]);
+            acc[4 + i] = fmaf(wj, b[i], acc[4 + i]);
+        }
+    }
+};
+template <>
+struct Raw8<uint16_t> {
+    i32x4 a;
+    __device__ __forceinline__ void load(const uint16_t* p) {
+        a = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(p));
+    }
+    __device__ __forceinline__ void fma_into(float wj, float (&acc)[8]) const {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t u = (uint32_t)a[i];
+            acc[2 * i] = fmaf(wj, __uint_as_float(u << 16), acc[2 * i]);
+            acc[2 * i + 1] = fmaf(wj, __uint_as_float(u & 0xFFFF0000u), acc[2 * i + 1]);
+        }
+    }
+};
+
 // One workgroup per token; thread i owns the 8-column chunks i and i + 256 of
-// each pass of 512 chunks, so the loads of both chunks' k rows are in flight
-// together.
-template <typename YT, typename OT>
+// each pass of 512 chunks.  With KT = k known at compile time (the layer's
+// common k = 8) the loads of all k rows of both chunks are issued before the
+// first multiply-add, so 2 k loads a thread are in flight; otherwise rows are
+// taken one at a time.  Either way the sum runs in slot order j = 0 .. k-1,
+// then the shared term.
+template <typename YT, typename OT, int KT>
 __global__ void __launch_bounds__(256)
 combine_kernel(const YT* __restrict__ y, const int32_t* __restrict__ tok_row, const float* __restrict__ tw,
                const YT* __restrict__ ysh, OT* __restrict__ out, int k, int H) {
@@ -69,17 +109,28 @@ combine_kernel(const YT* __restrict__ y, const int32_t* __restrict__ tok_row, co
         const int c1 = c0 + 256;
         const bool two = c1 < nchunk;
         float a0[8] = {0, 0, 0, 0, 0, 0, 0, 0}, a1[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        for (int j = 0; j < k; ++j) {
-            const YT* row = y + (size_t)rows[j] * H;
-            const float wj = wts[j];
-            float v0[8], v1[8];
-            load8<YT>(row + c0 * 8, v0);
-            if (two) load8<YT>(row + c1 * 8, v1);
+        if constexpr (KT > 0) {
+            Raw8<YT> r0[KT], r1[KT];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) a0[i] = fmaf(wj, v0[i], a0[i]);
-            if (two)
+            for (int j = 0; j < KT; ++j) {
+                const YT* row = y + (size_t)rows[j] * H;
+                r0[j].load(row + c0 * 8);
+                if (two) r1[j].load(row + c1 * 8);
+            }
 #pragma unroll
-                for (int i = 0; i < 8; ++i) a1[i] = fmaf(wj, v1[i], a1[i]);
+            for (int j = 0; j < KT; ++j) {
+                r0[j].fma_into(wts[j], a0);
+                if (two) r1[j].fma_into(wts[j], a1);
+            }
+        } else {
+            for (int j = 0; j < k; ++j) {
+                const YT* row = y + (size_t)rows[j] * H;
+                Raw8<YT> v0, v1;
+                v0.load(row + c0 * 8);
+                if (two) v1.load(row + c1 * 8);
+                v0.fma_into(wts[j], a0);
+                if (two) v1.fma_into(wts[j], a1);
+            }
         }
         if (ysh) {
             float v0[8], v1[8];
@@ -96,29 +147,30 @@ combine_kernel(const YT* __restrict__ y, const int32_t* __restrict__ tok_row, co
     }
 }
 
+template <typename YT, typename OT>
+void launch_combine_t(const moe_cfg& c, const YT* y, const int32_t* tok_row, const float* topk_w, const YT* ys,
+                      OT* out, hipStream_t s) {
+    const dim3 grid(c.T), block(256);
+    if (c.k == 8)
+        hipLaunchKernelGGL((combine_kernel<YT, OT, 8>), grid, block, 0, s, y, tok_row, topk_w, ys, out, c.k, c.H);
+    else
+        hipLaunchKernelGGL((combine_kernel<YT, OT, 0>), grid, block, 0, s, y, tok_row, topk_w, ys, out, c.k, c.H);
+}
+
 }  // namespace
 
 hipError_t launch_combine(const moe_cfg& c, const void* y_rows, const int32_t* tok_row, const float* topk_w,
                           const void* y_shared, void* out, hipStream_t s) {
-    dim3 grid(c.T), block(256);
     if (c.y_dtype == MOE_F32) {
         auto y = static_cast<const float*>(y_rows);
         auto ys = static_cast<const float*>(y_shared);
-        if (c.out_dtype == MOE_F32)
-            hipLaunchKernelGGL((combine_kernel<float, float>), grid, block, 0, s, y, tok_row, topk_w, ys,
-                               static_cast<float*>(out), c.k, c.H);
-        else
-            hipLaunchKernelGGL((combine_kernel<float, uint16_t>), grid, block, 0, s, y, tok_row, topk_w, ys,
-                               static_cast<uint16_t*>(out), c.k, c.H);
+        if (c.out_dtype == MOE_F32) launch_combine_t(c, y, tok_row, topk_w, ys, static_cast<float*>(out), s);
+        else launch_combine_t(c, y, tok_row, topk_w, ys, static_cast<uint16_t*>(out), s);
     } else {
         auto y = static_cast<const uint16_t*>(y_rows);
         auto ys = static_cast<const uint16_t*>(y_shared);
-        if (c.out_dtype == MOE_F32)
-            hipLaunchKernelGGL((combine_kernel<uint16_t, float>), grid, block, 0, s, y, tok_row, topk_w, ys,
-                               static_cast<float*>(out), c.k, c.H);
-        else
-            hipLaunchKernelGGL((combine_kernel<uint16_t, uint16_t>), grid, block, 0, s, y, tok_row, topk_w, ys,
-                               static_cast<uint16_t*>(out), c.k, c.H);
+        if (c.out_dtype == MOE_F32) launch_combine_t(c, y, tok_row, topk_w, ys, static_cast<float*>(out), s);
+        else launch_combine_t(c, y, tok_row, topk_w, ys, static_cast<uint16_t*>(out), s);
     }
     return hipGetLastError();
 }
