@@ -249,6 +249,39 @@ def main():
         wall = time.perf_counter() - t0
         ms_step = ev0.elapsed_time(ev1) / a.steps
 
+    dispatch = None
+    if table is not None and not a.traffic_run:
+        # Host cost of issuing one layer: an eager moe_layer call (argument
+        # checks and 9 kernel launches) against the replay of a graph captured
+        # once with the layer id read on the device, the id of the next layer
+        # written by a fill kernel ahead of each replay (the ids are already on
+        # the device, so the host need not wait for them).
+        torch.cuda.synchronize()
+        h0 = time.perf_counter()
+        for i in range(a.steps):
+            step(i)
+        h_eager = (time.perf_counter() - h0) / a.steps
+        torch.cuda.synchronize()
+        lay = torch.zeros(1, dtype=torch.int32, device=dev)
+        wg_ = moe.weights(None, None, None, layout=w.layout, table=table, layer=lay, n_layers=a.weight_table)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            moe.moe_layer(c, w_r, bias, wg_, x, out, ws)
+        torch.cuda.synchronize()
+        ev2, ev3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        h0 = time.perf_counter()
+        ev2.record(stream)
+        for i in range(a.steps):
+            lay.fill_(i % a.weight_table)
+            g.replay()
+        ev3.record(stream)
+        h_graph = (time.perf_counter() - h0) / a.steps
+        torch.cuda.synchronize()
+        dispatch = {"eager_host_us_per_layer": round(h_eager * 1e6, 1),
+                    "graph_host_us_per_layer": round(h_graph * 1e6, 1),
+                    "graph_ms_per_step": round(ev2.elapsed_time(ev3) / a.steps, 4)}
+        del g
+
     # ---- per-stage breakdown: moe_layer is these four stage calls with m_tile 16
     # and the indexed x_perm (the permute writes the maps, GEMM1 reads x through
     # row_src; bit-identical results); events between the stages on the launch
@@ -383,6 +416,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "sclk": sclk,
+        **({"dispatch": dispatch} if dispatch else {}),
     }
     print(json.dumps(res), flush=True)
 
