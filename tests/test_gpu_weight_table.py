@@ -122,18 +122,24 @@ def test_table_ffn_equals_contiguous_per_layer(tiled):
         assert bool((y == -12345.0).all()) and bool((y_sh == -12345.0).all())
 
 
-def test_table_fp8_ffn_equals_contiguous_per_layer():
+@pytest.mark.parametrize("mxfp4", [False, True])
+def test_table_fp8_ffn_equals_contiguous_per_layer(mxfp4):
+    """e4m3 rows with e4m3 weights (fp32 128 x 128 block scales) or MXFP4
+    weights (E8M0 scales per 32): the table carries each expert's codes and
+    scales."""
     d = dev()
     H, I, counts = 256, 384, [130, 0, 7, 290]
     E, n = len(counts), int(sum(counts))
     offs = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32, device=d)
-    c = moe.make_cfg(T=n, H=H, E=E, k=1, I=I, act_dtype=moe.MOE_FP8_E4M3, y_dtype=moe.MOE_BF16)
+    c = moe.make_cfg(T=n, H=H, E=E, k=1, I=I, act_dtype=moe.MOE_FP8_E4M3, y_dtype=moe.MOE_BF16,
+                     w_dtype=moe.MOE_FP4_E2M1 if mxfp4 else moe.MOE_FP8_E4M3)
     s = synth.MoeShape("tab8", T=n, H=H, E=E, k=1, I=I, dtype="fp8", seed=5)
     xq, xs = synth.fp8_rows(s, n, d)
+    gen = synth.mxfp4_expert_weights if mxfp4 else synth.fp8_expert_weights
     cont, keep = [], []
     for L in range(N_LAYERS):
         sl = s.with_(seed=300 + L)
-        wq = [synth.fp8_expert_weights(sl, e, d) for e in range(E)]
+        wq = [gen(sl, e, d) for e in range(E)]
         wg, sg, wu, su, wd, sd = (torch.stack([w[i] for w in wq]) for i in range(6))
         keep.append((wg, sg, wu, su, wd, sd))
         cont.append(moe.weights(wg, wu, wd, s_gate=sg, s_up=su, s_down=sd))
