@@ -102,12 +102,14 @@ typedef enum moe_stage {
  *   has_shared   1: a shared expert (weight 1) is added to every token
  *   I_shared     intermediate size of the shared expert
  *   act_dtype    x dtype (MOE_F32, MOE_BF16, or MOE_FP8_E4M3 for the grouped FFN)
- *   w_dtype      expert weight dtype: equal to act_dtype, or MOE_FP8_E4M3
- *                with act_dtype MOE_BF16 ("fp8 experts": moe_layer
- *                quantises x per token with moe_quantize_fp8's rule and runs
- *                the experts in fp8; moe_grouped_ffn refuses this pair -- call
- *                it on the quantised rows with act_dtype = w_dtype =
- *                MOE_FP8_E4M3).  fp8 weights need H, I (and I_shared) to be
+ *   w_dtype      expert weight dtype: equal to act_dtype; or MOE_FP8_E4M3
+ *                or MOE_FP4_E2M1 (MXFP4) with act_dtype MOE_BF16
+ *                ("low-precision experts": moe_layer quantises x per token
+ *                with moe_quantize_fp8's rule and runs the experts on e4m3
+ *                rows; moe_grouped_ffn refuses this pair -- call it on the
+ *                quantised rows with act_dtype = MOE_FP8_E4M3); or
+ *                MOE_FP4_E2M1 with act_dtype MOE_FP8_E4M3 (grouped FFN).
+ *                e4m3 and MXFP4 weights need H, I (and I_shared) to be
  *                multiples of 128 up to 16384.
  *   y_dtype      dtype of the per-row expert outputs (y_rows, y_shared):
  *                MOE_F32 or MOE_BF16
@@ -143,10 +145,17 @@ typedef struct moe_cfg {
 
 /* Expert weights.  For fp8 weights the s_* arrays hold one fp32 scale per
  * 128 x 128 block: s_gate, s_up [E][I/128][H/128]; s_down [E][H/128][I/128]
- * (dequantised weight = e4m3 value * block scale); NULL otherwise.  sh_* are
+ * (dequantised weight = e4m3 value * block scale); NULL otherwise.  For
+ * MXFP4 weights (w_dtype MOE_FP4_E2M1, the OCP Microscaling format that
+ * gfx950's scaled MFMA reads; the 4-bit expert weights of the DWDP page,
+ * appendix A4) the matrices are packed codes w_gate, w_up [E][I][H/2],
+ * w_down [E][H][I/2] and the s_* pointers are uint8_t E8M0 scales, one per
+ * 32 consecutive elements of a row: s_gate, s_up [E][I][H/32], s_down
+ * [E][H][I/32] (dequantised weight = E2M1 value * 2^(scale - 127)).  sh_* are
  * the shared expert's matrices (NULL when has_shared == 0), sh_s_* their
- * block scales (fp8 experts only: [I_shared/128][H/128] for gate and up,
- * [H/128][I_shared/128] for down).
+ * scales (low-precision experts only: fp8 [I_shared/128][H/128] for gate
+ * and up, [H/128][I_shared/128] for down; MXFP4 [I_shared][H/32] and
+ * [H][I_shared/32]).
  * layout MOE_LAYOUT_ROWMAJOR: the matrices as above.  layout MOE_LAYOUT_TILED
  * (bf16 only): w_gate and sh_gate point to the gate+up matrices and w_down and
  * sh_down to the down matrices that moe_tile_weights writes, rearranged into
@@ -169,7 +178,7 @@ typedef struct moe_weights {
      * Non-NULL: `table` is a device array [n_layers][E + has_shared][6] of
      * device pointers {gate, up, down, s_gate, s_up, s_down} to ONE expert's
      * matrices (the layouts above without the leading [E]; entry E of a layer
-     * is the shared expert; scale entries NULL unless w_dtype is fp8; with
+     * is the shared expert; scale entries NULL for bf16 weights; with
      * layout MOE_LAYOUT_TILED, gate points to the expert's tiled gate+up
      * matrix, down to its tiled down matrix, up is unused); `layer` is a device
      * int32 that the grouped FFN's kernels read when they run, so a call (or a
