@@ -58,16 +58,44 @@ __shared__ i32x4 stgA2[kStageA];
 __shared__ i32x4 stgB0[kChunksB];
 __shared__ i32x4 stgB1[kChunksB];
 
-template <int BUF>
+// MXFP4 tiles of kBig rows: with 17 KiB weight stages, three A stages of 256
+// rows fit beside the two weight stages (135 KiB), in buffers of their own.
+constexpr int kBig = 256;
+constexpr int kStageAW = kBig * 8 + 72;
+constexpr int kChunksBW = BN * 4 + 128;  // codes, then 8 x 256 B of scales
+__shared__ i32x4 stgA0w[kStageAW];
+__shared__ i32x4 stgA1w[kStageAW];
+__shared__ i32x4 stgA2w[kStageAW];
+__shared__ i32x4 stgB0w[kChunksBW];
+__shared__ i32x4 stgB1w[kChunksBW];
+
+// The stage buffers of a tile of TB rows (distinct objects per buffer).
+template <int BUF, int TB>
 __device__ __forceinline__ i32x4* stgA() {
-    if constexpr (BUF == 0) return stgA0;
-    else if constexpr (BUF == 1) return stgA1;
-    else return stgA2;
+    if constexpr (TB == kBig) {
+        if constexpr (BUF == 0) return stgA0w;
+        else if constexpr (BUF == 1) return stgA1w;
+        else return stgA2w;
+    } else {
+        if constexpr (BUF == 0) return stgA0;
+        else if constexpr (BUF == 1) return stgA1;
+        else return stgA2;
+    }
 }
-template <int BUF>
+template <int BUF, int TB>
 __device__ __forceinline__ i32x4* stgB() {
-    if constexpr (BUF == 0) return stgB0;
-    else return stgB1;
+    if constexpr (TB == kBig) {
+        if constexpr (BUF == 0) return stgB0w;
+        else return stgB1w;
+    } else {
+        if constexpr (BUF == 0) return stgB0;
+        else return stgB1;
+    }
+}
+// 16-byte chunks of a stage's A rows: the row scales follow them
+template <int TB>
+constexpr int chunks_a() {
+    return (TB == kBig ? kBig : BM) * 8;
 }
 
 __device__ __forceinline__ void barrier_lds() { asm volatile("s_barrier" ::: "memory"); }
@@ -165,30 +193,30 @@ __device__ __forceinline__ void dma1(const Dma& d, int t, int wave) {
         if constexpr (J < 7) {
             constexpr int i = J - 5;
             const uint32_t off = (!real || d.vb[i] == kOOB) ? kOOB : d.vb[i] + k / 2;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_t)(stgB<BBUF>() + (wave * 2 + i) * 64), 16, off, 0, 0,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_t)(stgB<BBUF, TB>() + (wave * 2 + i) * 64), 16, off, 0, 0,
                                                      0);
         } else {
             const __amdgpu_buffer_rsrc_t rs = (MODE == 0 && (wave & 1)) ? d.rsb1 : d.rsb0;
             const uint32_t off = (!real || d.vbs == kOOB) ? kOOB : d.vbs + (uint32_t)t * 4u;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_t)(stgB<BBUF>() + kScaleB4 + wave * 16), 4, off, 0, 0,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_t)(stgB<BBUF, TB>() + kScaleB4 + wave * 16), 4, off, 0, 0,
                                                      0);
         }
         return;
     }
     if constexpr (J < 4) {
         const uint32_t off = (!real || d.va[J] == kOOB) ? kOOB : d.va[J] + k;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ra, (lds_t)(stgA<ABUF>() + ((wave * 4 + J) % (TB / 8)) * 64), 16,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ra, (lds_t)(stgA<ABUF, TB>() + ((wave * 4 + J) % (TB / 8)) * 64), 16,
                                                  off, 0, 0, 0);
     } else if constexpr (J == 4) {
         const uint32_t so = (!real || d.vs == kOOB) ? kOOB : d.vs + (uint32_t)t * 4u;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rs, (lds_t)(stgA<ABUF>() + kChunksA + wave * 8), 4, so, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rs, (lds_t)(stgA<ABUF, TB>() + chunks_a<TB>() + wave * 8), 4, so, 0, 0, 0);
     } else {
         constexpr int i = J - 5;
         const uint32_t off = (!real || d.vb[i] == kOOB) ? kOOB : d.vb[i] + k;
         // GEMM1: wave w fills LDS rows 32 w + [0, 32): gate rows of quarter w / 2
         // on even waves, up rows on odd waves
         const __amdgpu_buffer_rsrc_t r = (MODE == 0 && (wave & 1)) ? d.rb1 : d.rb0;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_t)(stgB<BBUF>() + (wave * 4 + i) * 64), 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_t)(stgB<BBUF, TB>() + (wave * 4 + i) * 64), 16, off, 0, 0, 0);
     }
 }
 
@@ -239,9 +267,9 @@ __device__ __forceinline__ void promote(const f32x4 (&t)[4], float sa, float p0,
 // logical chunks 2 (lane / 16) and 2 (lane / 16) + 1; the swizzle of a row
 // depends on row % 16 only, so every fragment address is one of two per-lane
 // bases plus a constant.
-template <int BUF>
+template <int BUF, int TB>
 __device__ __forceinline__ void read_b(int q, int lane, i32x8 (&b)[4]) {
-    const i32x4* buf = stgB<BUF>();
+    const i32x4* buf = stgB<BUF, TB>();
     const int l16 = lane & 15;
     const int plo = (2 * (lane >> 4)) ^ swz8(l16), phi = plo ^ 1;
     const int ib = ((q & 3) * 64 + l16) * 8;  // column block cb: + cb * 128
@@ -253,9 +281,9 @@ __device__ __forceinline__ void read_b(int q, int lane, i32x8 (&b)[4]) {
 // row (16 cb + lane % 16), K block lane / 16 of the stage: logical chunk
 // lane / 16 of the 64-byte LDS row, the low four dwords of the operand; its
 // E8M0 scale is byte lane / 16 of the row's scale dword.
-template <int BUF>
+template <int BUF, int TB>
 __device__ __forceinline__ void read_b4(int q, int lane, i32x8 (&b)[4], int (&bs)[4]) {
-    const i32x4* buf = stgB<BUF>();
+    const i32x4* buf = stgB<BUF, TB>();
     const int l16 = lane & 15, g = lane >> 4;
     const int ib = ((q & 3) * 64 + l16) * 4 + (g ^ ((l16 >> 2) & 3));  // column block cb: + cb * 64
     const uint32_t* sc = reinterpret_cast<const uint32_t*>(buf + kScaleB4);
@@ -303,20 +331,20 @@ __device__ __forceinline__ void kstep(const Dma& d, int t_stage, int wave, int r
     // Every access indexes the stage buffer itself (an integer base plus a
     // constant), so the compiler can tell it from the DMA in flight into the
     // other buffers and adds no wait for it.
-    const i32x4* buf = stgA<BUF>();
+    const i32x4* buf = stgA<BUF, TB>();
     const int l16 = lane & 15;
     const int plo = (W4 ? (lane >> 4) : 2 * (lane >> 4)) ^ swz8(l16);
     const int phi = W4 ? ((lane >> 4) + 4) ^ swz8(l16) : plo ^ 1;
     const int ia = (r0 + l16) * 8;                      // row block rb: + rb * 128
     // this lane's row scales: row blocks 0..3 in chunk 32 h + l16, 4..7 in 32 h + 16 + l16
-    const int is = kChunksA + (r0 / (TB / 2)) * 32 + l16;
+    const int is = chunks_a<TB>() + (r0 / (TB / 2)) * 32 + l16;
     const f32x4 sa_lo = __builtin_bit_cast(f32x4, buf[is]), sa_hi = __builtin_bit_cast(f32x4, buf[is + 16]);
     auto sa = [&](int rb) { return rb < 4 ? sa_lo[rb & 3] : sa_hi[rb & 3]; };
     i32x8 a[2];
     f32x4 t[2][4];
     a[0] = cat(buf[ia + plo], buf[ia + phi]);
     __builtin_amdgcn_sched_barrier(0);
-    static_assert(RB == 4 || RB == 7, "the load slots are laid out for 4 and 7 row blocks");
+    static_assert(RB == 4 || RB == 7 || RB == 8, "the load slots are laid out for 4, 7 and 8 row blocks");
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
@@ -472,8 +500,8 @@ __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int 
         wscale(s, p0, p1);
         wait_stage<W4>();  // stage s has landed (this wave's loads); this wave's reads of stage s-1 are done
         barrier_lds();     // ... every wave's: A buffer (s+2) % 3 is free
-        if constexpr (W4) read_b4<BB>(q, lane, b, bs);
-        else read_b<BB>(q, lane, b);
+        if constexpr (W4) read_b4<BB, TB>(q, lane, b, bs);
+        else read_b<BB, TB>(q, lane, b);
         wait_lgkm0();
         barrier_lds();  // every wave holds its B fragments of stage s: B buffer s % 2 is free
         kstep<MODE, AB, (AB + 2) % 3, BB, TB, W4>(d, s + 2, wave, r0, lane, b, bs, p0, p1, acc);
@@ -518,7 +546,7 @@ __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int 
             rmax[rb] = m;
         }
         // per-row maxima of the four quarters' 32 columns -> LDS [4][256]
-        float* red = reinterpret_cast<float*>(stgA0);
+        float* red = reinterpret_cast<float*>(stgA<0, TB>());
         if (lane < 16)
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) red[q * 256 + r0 + rb * 16 + l16] = rmax[rb];
@@ -526,7 +554,7 @@ __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int 
         // [BM rows][128 columns] e4m3, 32 words a row, the 16-byte chunk c of row r
         // at chunk c ^ ((r >> 1) & 7): a 4-byte store of 16 rows x 4 words then
         // touches 64 distinct banks
-        uint32_t* qs = reinterpret_cast<uint32_t*>(stgB0);
+        uint32_t* qs = reinterpret_cast<uint32_t*>(TB == kBig ? stgA<1, TB>() : stgB<0, TB>());
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
             const int row = r0 + rb * 16 + l16;
@@ -551,12 +579,13 @@ __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int 
         }
     } else {
         // y through LDS, 16 rows at a time: each wave stages its 16 x 64 block
-        // (fp32, 4 KiB of B buffer 0), row r's 16-byte chunk c at chunk c ^ r,
+        // (fp32, 4 KiB of B buffer 0; of A buffer 1 in 256-row tiles, whose B
+        // buffers are smaller), row r's 16-byte chunk c at chunk c ^ r,
         // so the eight rows of a store group and the eight chunks of a row's
         // read group touch distinct banks; then every lane stores 4 columns
         // (8 B bf16 / 16 B fp32).  LDS operations of one wave are processed in
         // order.
-        float* st = reinterpret_cast<float*>(stgB0 + wave * 256);
+        float* st = reinterpret_cast<float*>((TB == kBig ? stgA<1, TB>() : stgB<0, TB>()) + wave * 256);
         const int cw = n0 + q * 64;  // first output column of this wave
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
@@ -605,13 +634,13 @@ ffn_gemm_fp8(Fp8Args p) {
 }
 
 template <int MODE>
-void launch_one(bool small, bool w4, int64_t grid, const Fp8Args& a, hipStream_t s) {
+void launch_one(int tb, bool w4, int64_t grid, const Fp8Args& a, hipStream_t s) {
     const dim3 gr((unsigned)grid), bl(NTH);
     if (w4) {
-        if (small) hipLaunchKernelGGL((ffn_gemm_fp8<MODE, kFfnBmFp8Small, true>), gr, bl, 0, s, a);
-        else hipLaunchKernelGGL((ffn_gemm_fp8<MODE, BM, true>), gr, bl, 0, s, a);
+        if (tb == kFfnBmFp8Small) hipLaunchKernelGGL((ffn_gemm_fp8<MODE, kFfnBmFp8Small, true>), gr, bl, 0, s, a);
+        else hipLaunchKernelGGL((ffn_gemm_fp8<MODE, kBig, true>), gr, bl, 0, s, a);
     } else {
-        if (small) hipLaunchKernelGGL((ffn_gemm_fp8<MODE, kFfnBmFp8Small, false>), gr, bl, 0, s, a);
+        if (tb == kFfnBmFp8Small) hipLaunchKernelGGL((ffn_gemm_fp8<MODE, kFfnBmFp8Small, false>), gr, bl, 0, s, a);
         else hipLaunchKernelGGL((ffn_gemm_fp8<MODE, BM, false>), gr, bl, 0, s, a);
     }
 }
@@ -624,10 +653,12 @@ hipError_t launch_gemm_fp8(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_c
     // Tile height: groups of about 256 rows or fewer (the DeepSeek-V3 layer's
     // 256 experts, 8 rows a token) fill 128-row tiles; a 224-row tile would
     // split them into two 128-row tiles and compute 224 rows of each.
+    // MXFP4 weights leave LDS for 256-row tiles, so groups of about 256 rows
+    // take one tile instead of two, halving their weight traffic.
     const int G = c.E + (c.has_shared ? 1 : 0);
-    const bool small = n_rows_cap <= (int64_t)G * 272;
-    const int tb = small ? kFfnBmFp8Small : BM;
     const bool w4 = c.w_dtype == MOE_FP4_E2M1;  // MXFP4 weights, e4m3 rows
+    const bool small = n_rows_cap <= (int64_t)G * (w4 ? 136 : 272);
+    const int tb = small ? kFfnBmFp8Small : (w4 ? kBig : BM);
     hipError_t e0 = launch_build_tiles(c, offsets, tb, n_rows_cap, wk, s);
     if (e0 != hipSuccess) return e0;
     Fp8Args a{};
@@ -650,7 +681,7 @@ hipError_t launch_gemm_fp8(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_c
     a.K = c.H;
     a.N = c.I;
     const int64_t grid1 = max_tiles * wk.nt1;
-    launch_one<0>(small, w4, grid1, a, s);
+    launch_one<0>(tb, w4, grid1, a, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // GEMM2: down projection of h
@@ -669,7 +700,7 @@ hipError_t launch_gemm_fp8(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_c
     a.N = c.H;
     a.out_f32 = c.y_dtype == MOE_F32 ? 1 : 0;
     const int64_t grid2 = max_tiles * wk.nt2;
-    launch_one<1>(small, w4, grid2, a, s);
+    launch_one<1>(tb, w4, grid2, a, s);
     return hipGetLastError();
 }
 

@@ -87,7 +87,8 @@ def _run(s, counts, ydt, extra):
 @pytest.mark.parametrize("H,I,counts,ydt,extra", [
     (512, 256, [37, 0, 5, 300, 64, 1, 0, 257], moe.MOE_F32, 0),   # unaligned offsets, empty experts, 128-row tiles
     (384, 384, [129, 3, 260], moe.MOE_BF16, 11),                  # odd K blocks, a partial GEMM2 N tile
-    (1024, 512, [600], moe.MOE_BF16, 0),                          # 224-row tiles
+    (1024, 512, [600], moe.MOE_BF16, 0),                          # 256-row tiles
+    (512, 384, [300, 5, 270, 0, 129], moe.MOE_F32, 3),            # 256-row tiles, ragged groups
     (256, 128, [1, 1, 1, 1], moe.MOE_F32, 5),                     # single rows
 ])
 def test_grouped_ffn_mxfp4_matches_oracle(H, I, counts, ydt, extra):
