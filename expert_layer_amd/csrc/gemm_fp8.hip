@@ -1,6 +1,7 @@
 // gemm_fp8.hip -- the grouped SwiGLU FFN on fp8 (OCP e4m3) MFMA with fp32 block
-// scales ("ASAP", section 3.4.2: the MoE kernel is a grouped matrix
-// multiplication of hidden states by the layer's expert weights).  The operands
+// scales, and on e4m3 rows with MXFP4 weights ("ASAP", section 3.4.2: the MoE
+// kernel is a grouped matrix multiplication of hidden states by the layer's
+// expert weights).  The operands
 // are e4m3 codes with one fp32 scale per 1 x 128 block of a row (activations,
 // h) and per 128 x 128 block (weights); a dequantised value is code * scale.
 //
@@ -17,7 +18,14 @@
 // 112 (w / 4) + [0, 112) and weight rows 64 (w % 4) + [0, 64): 7 x 4 MFMA blocks
 // of 16 x 16 and their fp32 accumulators (112 VGPRs -- the promotion FMAs need
 // them in VALU registers).  224 rather than 256 rows is what lets three A
-// stages and two B stages fit in the 160 KiB of LDS.  GEMM1: the 64 weight
+// stages and two B stages fit in the 160 KiB of LDS.  Launches of small groups
+// take 128-row tiles.
+//
+// MXFP4 weights (W4; OCP MX: E2M1 codes, one E8M0 scale per 32 elements of a
+// row, the 4-bit expert weights of "DWDP", appendix A4).  The weight stage
+// halves to 64-byte rows plus a scale dword per row, the MFMA becomes the
+// scaled FP4 x e4m3 form that applies each lane's E8M0 scale itself, and the
+// smaller weight stages leave LDS for 256-row tiles.  GEMM1: the 64 weight
 // rows of a wave are 32 gate rows then the 32 up rows of the same h columns, so
 // h = silu(g) * u forms in registers; GEMM2: 64 output columns.
 // Pipeline.  K advances in stages of 128 through three A buffers [224 x 128 B |
