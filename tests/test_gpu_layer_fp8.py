@@ -123,3 +123,58 @@ def test_layer_fp8_experts_matches_oracle(shape, T, ydt):
     assert rel_err(got, ref) <= 4e-2
     rms = math.sqrt(float(np.mean(ref ** 2)))
     assert math.sqrt(float(np.mean((got - ref) ** 2))) / rms <= 1e-2
+
+
+def _u8(t):
+    return t.detach().contiguous().cpu().numpy().astype(np.uint8)
+
+
+@pytest.mark.parametrize("wfmt", ["e4m3", "mxfp4"])
+def test_layer_lowp_experts_full_size_sampled(wfmt):
+    """The benchmarked configuration: the c3 layer (T = 8192, 256 routed
+    experts and the shared one) with e4m3 or MXFP4 experts, bf16 expert
+    outputs.  Routing is checked for every token; the output on a seeded sample
+    of tokens (with the first, the last, and tokens of the hottest and coldest
+    experts) against the oracle composed step by step, to the bounds above."""
+    s = synth.config("c3_dsv3_bf16")
+    d = dev()
+    _W8.clear()
+    torch.cuda.empty_cache()
+    rc = router_case(s)
+    T = s.T
+    gen = synth.mxfp4_expert_weights if wfmt == "mxfp4" else synth.fp8_expert_weights
+    wq = [gen(s, e, d) for e in range(s.E)]
+    stack = [torch.stack([w[i] for w in wq]) for i in range(6)]
+    sh = gen(s.with_(I=s.I_shared), s.E, d)
+    c = lib_cfg(s, T=T, y_dtype=moe.MOE_BF16, out_dtype=moe.MOE_F32)
+    c.w_dtype = moe.MOE_FP4_E2M1 if wfmt == "mxfp4" else moe.MOE_FP8_E4M3
+    wg, sg, wu, su, wd, sd = stack
+    w = moe.weights(wg, wu, wd, s_gate=sg, s_up=su, s_down=sd, sh_gate=sh[0], sh_up=sh[2], sh_down=sh[4],
+                    sh_s_gate=sh[1], sh_s_up=sh[3], sh_s_down=sh[5])
+    out = torch.full((T, s.H), float("nan"), device=d)
+    ws = moe.workspace(c, moe.MOE_STAGE_LAYER, d)
+    moe.moe_layer(c, rc["w_r"], rc["bias"], w, rc["x"], out, ws)
+    torch.cuda.synchronize()
+    del ws
+    ids, tw = oracle.route_select(rc["logits"], s.k, renormalize=s.renormalize, routed_scale=s.routed_scale,
+                                  bias=rc["bh"], **route_kw(s))
+    rng = np.random.default_rng(s.seed + 3)
+    cnt = np.bincount(ids.ravel(), minlength=s.E)
+    hot, cold = int(np.argmax(cnt)), int(np.argmin(np.where(cnt > 0, cnt, 1 << 30)))
+    toks = np.unique(np.concatenate([rng.choice(T, 16, replace=False),
+                                     [0, T - 1, int(np.nonzero((ids == hot).any(1))[0][0]),
+                                      int(np.nonzero((ids == cold).any(1))[0][-1])]]))
+    xq, xs = oracle.quantize_rows_e4m3(rc["xh"][toks])
+    ffn = oracle.expert_ffn_mxfp4 if wfmt == "mxfp4" else oracle.expert_ffn_fp8
+    conv = _u8 if wfmt == "mxfp4" else (lambda t: to_np(t))
+    y = np.zeros((len(toks), s.k, s.H))
+    sub = ids[toks]
+    for e in np.unique(sub):
+        r, j = np.nonzero(sub == e)
+        y[r, j] = ffn(xq[r], xs[r], *(conv(t) for t in wq[e]))
+    y_sh = ffn(xq, xs, *(conv(t) for t in sh))
+    ref = np.einsum("tj,tjh->th", tw[toks].astype(np.float64), y) + y_sh
+    got = out[torch.as_tensor(toks, device=d)].cpu().numpy()
+    assert np.isfinite(got).all()
+    assert rel_err(got, ref) <= 4e-2
+    assert math.sqrt(float(np.mean((got - ref) ** 2))) / math.sqrt(float(np.mean(ref ** 2))) <= 1e-2
