@@ -559,7 +559,8 @@ ffn_gemm_bf16(GemmArgs p) {
 
 // ------------------------------------------------------------- tile list
 constexpr int kMBlock = 4;  // M tiles of one expert whose work items are interleaved
-// One workgroup of 1024 threads.  Group g < E covers rows [offsets[g],
+// Workgroups of 1024 threads; each computes the groups' tile prefix and
+// writes its share of the tiles and work items.  Group g < E covers rows [offsets[g],
 // offsets[g+1]); group E (the shared expert, when present) covers tokens
 // [0, T).  A group of n rows gets nmt = ceil(n / bm) tiles of height
 // ceil(ceil(n / nmt) / 32) * 32 (the last one shorter).  The work lists take a
@@ -624,8 +625,11 @@ ffn_build_tiles(const int32_t* __restrict__ offsets, int E, int has_shared, int 
         }
         return lo;
     };
+    // Steps 2 and 3 are split over the launch's workgroups (each recomputed
+    // the prefix above); item i goes to workgroup (i / 1024) % gridDim.x.
+    const int first = blockIdx.x * 1024 + tid, stride = gridDim.x * 1024;
     // 2. tiles: a group of n rows gets nmt equal tiles of height rounded up to 32
-    for (int ti = tid; ti < total; ti += 1024) {
+    for (int ti = first; ti < total; ti += stride) {
         const int g = group_of(ti);
         const int st = g ? gend[g - 1] : 0, nmt = gend[g] - st;
         int b, e;
@@ -639,7 +643,7 @@ ffn_build_tiles(const int32_t* __restrict__ offsets, int E, int has_shared, int 
     //    block's M tiles next to each other (32 consecutive items -- one XCD's
     //    CUs -- share kMBlock row panels and 32 / kMBlock weight panels)
     auto emit = [&](int2* __restrict__ work, int nt) {
-        for (int i = tid; i < total * nt; i += 1024) {
+        for (int i = first; i < total * nt; i += stride) {
             const int g = group_of(i / nt);
             const int st = g ? gend[g - 1] : 0, nmt = gend[g] - st;
             const int j = i - st * nt;
@@ -650,12 +654,17 @@ ffn_build_tiles(const int32_t* __restrict__ offsets, int E, int has_shared, int 
     };
     emit(work1, nt1);
     emit(work2, nt2);
-    if (tid == 0) n_tiles[0] = total;
+    if (blockIdx.x == 0 && tid == 0) n_tiles[0] = total;
 }
 
 hipError_t launch_build_tiles(const moe_cfg& c, const int32_t* offsets, int bm, int64_t rows_cap,
                               const FfnWork& wk, hipStream_t s) {
-    hipLaunchKernelGGL(ffn_build_tiles, dim3(1), dim3(1024), 0, s, offsets, c.E, c.has_shared ? 1 : 0, c.T,
+    // enough workgroups that each thread emits a few items of the longer list
+    const int64_t items = (rows_cap / bm + c.E + 1) * (int64_t)(wk.nt1 > wk.nt2 ? wk.nt1 : wk.nt2);
+    int64_t nbl = (items + 4095) / 4096;
+    nbl = nbl < 1 ? 1 : (nbl > 32 ? 32 : nbl);
+    const unsigned nb = (unsigned)nbl;
+    hipLaunchKernelGGL(ffn_build_tiles, dim3(nb), dim3(1024), 0, s, offsets, c.E, c.has_shared ? 1 : 0, c.T,
                        bm, (int)rows_cap, reinterpret_cast<int4*>(wk.tiles), wk.n_tiles,
                        reinterpret_cast<int2*>(wk.work1), wk.nt1, reinterpret_cast<int2*>(wk.work2), wk.nt2);
     return hipGetLastError();
