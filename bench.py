@@ -560,10 +560,11 @@ def bench_fp8_layer(a, s, dev):
     wall = time.perf_counter() - t0
     ms_step = ev0.elapsed_time(ev1) / a.steps
 
-    # ---- the same work as stage calls: route, quantise, permute (e4m3 rows,
-    # m_tile 16), the routed grouped FFN, the shared one (one group of T rows),
-    # combine
-    cq = moe.make_cfg(**dict(kw, has_shared=False, I_shared=0), act_dtype=moe.MOE_FP8_E4M3, w_dtype=wdt, m_tile=16)
+    # ---- the same work as stage calls: route, quantise, permute (maps only,
+    # m_tile 16), the routed grouped FFN reading the e4m3 token rows through
+    # row_src, the shared one (one group of T rows), combine
+    cq = moe.make_cfg(**dict(kw, has_shared=False, I_shared=0), act_dtype=moe.MOE_FP8_E4M3, w_dtype=wdt, m_tile=16,
+                      x_layout=moe.MOE_LAYOUT_INDEXED)
     c1 = moe.make_cfg(**dict(kw, E=1, k=1, n_groups=1, topk_groups=1, I=max(I_sh, 128), has_shared=False,
                              I_shared=0), act_dtype=moe.MOE_FP8_E4M3, w_dtype=wdt)
     rows = moe.moe_max_rows(cq)
@@ -573,8 +574,7 @@ def bench_fp8_layer(a, s, dev):
                                       torch.empty((T, k), **i32))
     xq = torch.empty((T, H), dtype=torch.uint8, device=dev)
     xs = torch.empty((T, H // 128), device=dev)
-    x_perm = torch.empty((rows, H), dtype=torch.uint8, device=dev)
-    xps = torch.empty((rows, H // 128), device=dev)
+    x_perm = xps = None  # indexed: the permute writes the maps only
     y_rows = torch.empty((rows, H), dtype=torch.bfloat16, device=dev)
     y_sh = torch.empty((T, H), dtype=torch.bfloat16, device=dev) if s.shared else None
     offs1 = torch.tensor([0, T], **i32)
@@ -593,7 +593,7 @@ def bench_fp8_layer(a, s, dev):
         evs[2].record(stream)
         moe.moe_permute(cq, xq, xs, ids, counts, offs, row_src, tok_row, x_perm, xps, ws_p, stream)
         evs[3].record(stream)
-        moe.moe_grouped_ffn(cq, rows, x_perm, xps, offs, w, None, y_rows, None, ws_f, stream)
+        moe.moe_grouped_ffn(cq, rows, xq, xs, offs, w, None, y_rows, None, ws_f, stream, row_src=row_src)
         if s.shared:
             moe.moe_grouped_ffn(c1, T, xq, xs, offs1, w1, None, y_sh, None, ws_1, stream)
         evs[4].record(stream)
@@ -620,7 +620,7 @@ def bench_fp8_layer(a, s, dev):
     bytes_ = {
         "route": T * H * 2 + E * H * 2 + T * k * 8,
         "quantise": T * H * 2 + T * H + T * KB1 * 4,
-        "permute": T * k * 4 + E * 8 + rows * 4 + T * k * 4 + 2 * (R * H + R * KB1 * 4),
+        "permute": T * k * 4 + E * 8 + rows * 4 + T * k * 4,
         "grouped_ffn": w_bytes + (R + T * bool(s.shared)) * (H + KB1 * 4) + (R + T * bool(s.shared)) * H * 2,
         "combine": R * H * 2 + T * H * 2 * bool(s.shared) + T * H * 2 + T * k * 8,
     }

@@ -100,9 +100,10 @@ moe_status check_cfg(const moe_cfg* cp) {
     if (c.x_layout != MOE_LAYOUT_ROWMAJOR && c.x_layout != MOE_LAYOUT_TILED && c.x_layout != MOE_LAYOUT_INDEXED)
         return fail(MOE_ERR_INVALID_ARG, "x_layout=%d", c.x_layout);
     if (c.x_layout == MOE_LAYOUT_INDEXED) {
-        if (c.act_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "indexed x_perm is bf16 only");
-        if ((int64_t)c.T * c.H * 2 >= ((int64_t)1 << 31))
-            return fail(MOE_ERR_UNSUPPORTED, "indexed x_perm needs T*H*2 < 2^31");
+        if (c.act_dtype != MOE_BF16 && c.act_dtype != MOE_FP8_E4M3)
+            return fail(MOE_ERR_UNSUPPORTED, "indexed x_perm is bf16 or e4m3 only");
+        if ((int64_t)c.T * c.H * dtype_bytes(c.act_dtype) >= ((int64_t)1 << 31))
+            return fail(MOE_ERR_UNSUPPORTED, "indexed x_perm needs x under 2 GiB");
     }
     if (c.x_layout == MOE_LAYOUT_TILED) {
         if (c.act_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "tiled x_perm is bf16 only");
@@ -238,7 +239,7 @@ moe_cfg fp8_routed_cfg(const moe_cfg& c) {
     q.has_shared = 0;
     q.I_shared = 0;
     q.m_tile = 16;
-    q.x_layout = MOE_LAYOUT_ROWMAJOR;
+    q.x_layout = MOE_LAYOUT_INDEXED;  // GEMM1 reads the quantised tokens through row_src
     return q;
 }
 moe_cfg fp8_shared_cfg(const moe_cfg& c) {
@@ -246,6 +247,7 @@ moe_cfg fp8_shared_cfg(const moe_cfg& c) {
     q.E = q.k = q.n_groups = q.topk_groups = 1;
     q.I = c.I_shared;
     q.m_tile = 1;
+    q.x_layout = MOE_LAYOUT_ROWMAJOR;  // all T quantised tokens, in order
     return q;
 }
 
@@ -254,7 +256,7 @@ struct LayerCarve {
     float* topk_w;
     void *x_perm, *y_rows, *y_shared, *scratch;
     uint8_t* x_q;                // fp8 experts: x quantised [T][H]
-    float *x_s, *x_perm_scale;   // ... its scales [T][H / 128] and those of x_perm
+    float *x_s, *x_perm_scale;   // ... its scales [T][H / 128]; x_perm_scale NULL (indexed rows)
     int32_t* offsets_sh;         // ... {0, T}
     size_t bytes;
 };
@@ -280,7 +282,7 @@ LayerCarve layer_carve(const moe_cfg& c, void* p) {
     if (f8) {
         l.x_q = cv.take<uint8_t>((size_t)c.T * c.H);
         l.x_s = cv.take<float>((size_t)c.T * (c.H / 128));
-        l.x_perm_scale = cv.take<float>((size_t)rows * (c.H / 128));
+        l.x_perm_scale = nullptr;  // indexed: no dispatched copy of the rows or their scales
         l.offsets_sh = cv.take<int32_t>(2);
         if (c.has_shared) {
             const size_t fs = ffn_carve(fp8_shared_cfg(c), c.T, nullptr).bytes;
@@ -390,14 +392,15 @@ moe_status ffn_enqueue(const moe_cfg& c, int64_t n_rows_cap, const void* x_rows,
         e = moe::launch_gemm_f32(c, f.max_tiles, n_rows_cap, op.x_rows, offsets, w, op.x_tokens, op.y_rows,
                                  op.y_shared, f.wk, f.h, f.h_sh, s);
     else
-        e = moe::launch_gemm_fp8(c, f.max_tiles, n_rows_cap, x_rows, x_scale, offsets, w, wt, y_rows, f.wk, f.h,
-                                 f.h_scale, s);
+        e = moe::launch_gemm_fp8(c, f.max_tiles, n_rows_cap, x_rows, x_scale, op.row_src, offsets, w, wt, y_rows,
+                                 f.wk, f.h, f.h_scale, s);
     if (e != hipSuccess) return hip_fail(e, "moe_grouped_ffn");
     return MOE_OK;
 }
 
-// The rest of moe_layer for fp8 experts (routing done): quantise x, dispatch
-// the fp8 rows, the routed and the shared grouped FFN, combine.
+// The rest of moe_layer for low-precision experts (routing done): quantise x,
+// the dispatch maps (GEMM1 reads the e4m3 token rows through row_src), the
+// routed and the shared grouped FFN, combine.
 moe_status layer_fp8_experts(const moe_cfg& c, const moe_weights& w, const void* x, void* out,
                              const LayerCarve& l, hipStream_t s) {
     const moe_cfg cq = fp8_routed_cfg(c);
@@ -406,8 +409,8 @@ moe_status layer_fp8_experts(const moe_cfg& c, const moe_weights& w, const void*
     moe_status st = permute_enqueue(cq, l.x_q, l.x_s, l.ids, l.counts, l.offsets, l.row_src, l.tok_row, l.x_perm,
                                     l.x_perm_scale, l.scratch, s);
     if (st != MOE_OK) return st;
-    st = ffn_enqueue(cq, max_rows_of(cq), l.x_perm, l.x_perm_scale, l.offsets, nullptr, w, wtab_of(c, w, 0),
-                     nullptr, l.y_rows, nullptr, l.scratch, s);
+    st = ffn_enqueue(cq, max_rows_of(cq), l.x_q, l.x_s, l.offsets, l.row_src, w, wtab_of(c, w, 0), nullptr,
+                     l.y_rows, nullptr, l.scratch, s);
     if (st != MOE_OK) return st;
     if (c.has_shared) {
         const moe_cfg c1 = fp8_shared_cfg(c);
@@ -501,7 +504,7 @@ moe_status moe_permute(const moe_cfg* cfg, const void* x, const float* x_scale, 
     REQUIRE(row_src, "row_src");
     REQUIRE(tok_row, "tok_row");
     if (c.x_layout != MOE_LAYOUT_INDEXED) REQUIRE(x_perm, "x_perm");
-    if (c.act_dtype == MOE_FP8_E4M3) {
+    if (c.act_dtype == MOE_FP8_E4M3 && c.x_layout != MOE_LAYOUT_INDEXED) {
         REQUIRE(x_scale, "x_scale");
         REQUIRE(x_perm_scale, "x_perm_scale");
     }

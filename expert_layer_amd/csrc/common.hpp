@@ -212,11 +212,13 @@ struct TiledSizes {
 TiledSizes tiled_sizes(const moe_cfg& c);
 hipError_t launch_tile_weights(const moe_cfg& c, const moe_weights& src, void* w13, void* w2, void* sh13, void* sh2,
                                hipStream_t s);
-// fp8 (e4m3) grouped FFN: x_rows [n_rows_cap][H] with x_scale [n_rows_cap][H/128];
-// h [n_rows_cap][I] e4m3 and h_scale [n_rows_cap][I/128] are workspace.
+// fp8 (e4m3) grouped FFN: x_rows [n_rows_cap][H] with x_scale [n_rows_cap][H/128]
+// (row_src non-NULL: x_rows is x [T][H] and x_scale [T][H/128], row r being token
+// row_src[r] / k); h [n_rows_cap][I] e4m3 and h_scale [n_rows_cap][I/128] are workspace.
 hipError_t launch_gemm_fp8(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_cap, const void* x_rows,
-                           const float* x_scale, const int32_t* offsets, const moe_weights& w, const WTab& wt,
-                           void* y_rows, const FfnWork& wk, void* h, float* h_scale, hipStream_t s);
+                           const float* x_scale, const int32_t* row_src, const int32_t* offsets,
+                           const moe_weights& w, const WTab& wt, void* y_rows, const FfnWork& wk, void* h,
+                           float* h_scale, hipStream_t s);
 hipError_t launch_gemm_f32(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_cap, const void* x_rows,
                            const int32_t* offsets, const moe_weights& w, const void* x_tokens, void* y_rows,
                            void* y_shared, const FfnWork& wk, void* h, void* h_sh, hipStream_t s);

@@ -147,6 +147,8 @@ struct Fp8Args {
     int out_f32;            // GEMM2 output dtype
     WTab wt;                // wt.tab != NULL: w0, w1, s0, s1 of group g are table entries
     int slot0, slot1;       //   slot0, slot1, slot0 + 3, slot1 + 3
+    const int32_t* a_row_src;  // GEMM1: non-NULL -> a is x [a_rows][K], row r of A is x row a_row_src[r] / a_row_k
+    int a_row_k, a_rows;
 };
 
 // Row scales of a stage in LDS: position P = 128 h + 64 (rb / 4) + 4 l + rb % 4
@@ -391,13 +393,28 @@ __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int 
     const int NB = N / BK;
     Dma d;
     d.nsteps = KB;
-    // ---- A rows row0 .. row0 + M and their row scales
-    d.ra = make_rsrc(p.a + (size_t)row0 * K, (uint32_t)M * (uint32_t)K);
-    d.rs = make_rsrc(p.a_scale + (size_t)row0 * KB, (uint32_t)M * (uint32_t)KB * 4u);
+    // ---- A rows row0 .. row0 + M and their row scales; indexed (GEMM1 of the
+    // layer): the descriptors span all of x and its scales, and row r of the
+    // tile is token row_src[row0 + r] / k (rows with row_src -1, the segment
+    // padding, load as zero)
+    const bool a_idx = MODE == 0 && p.a_row_src != nullptr;
+    auto a_row = [&](int r) {  // the row of the descriptor's array holding tile row r, or -1
+        if (r >= M) return -1;
+        if (!a_idx) return r;
+        const int src = p.a_row_src[row0 + r];
+        return src >= 0 ? src / p.a_row_k : -1;
+    };
+    if (a_idx) {
+        d.ra = make_rsrc(p.a, (uint32_t)p.a_rows * (uint32_t)K);
+        d.rs = make_rsrc(p.a_scale, (uint32_t)p.a_rows * (uint32_t)KB * 4u);
+    } else {
+        d.ra = make_rsrc(p.a + (size_t)row0 * K, (uint32_t)M * (uint32_t)K);
+        d.rs = make_rsrc(p.a_scale + (size_t)row0 * KB, (uint32_t)M * (uint32_t)KB * 4u);
+    }
     {
         const int pos = wave * 32 + lane;  // < 288: the scale area of a stage
-        const int r = pos < 256 ? scale_row<TB>(pos) : TB;
-        d.vs = r < M ? (uint32_t)r * (uint32_t)KB * 4u : kOOB;
+        const int r = a_row(pos < 256 ? scale_row<TB>(pos) : TB);
+        d.vs = r >= 0 ? (uint32_t)r * (uint32_t)KB * 4u : kOOB;
     }
     // ---- B: GEMM1 the gate and up rows n0 + [0, 128) (LDS quarter j holds gate
     // rows 32 j + [0, 32) then the up rows of the same h columns); GEMM2 the
@@ -426,7 +443,8 @@ __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int 
         const int row = wave * 32 + i * 8 + (lane >> 3);  // LDS row this lane fills (B; A modulo TB)
         const int arow = row % TB;
         const uint32_t logical = (uint32_t)(((lane & 7) ^ swz8(row)) * 16);
-        d.va[i] = arow < M ? (uint32_t)arow * (uint32_t)K + (uint32_t)(((lane & 7) ^ swz8(arow)) * 16) : kOOB;
+        const int ar = a_row(arow);
+        d.va[i] = ar >= 0 ? (uint32_t)ar * (uint32_t)K + (uint32_t)(((lane & 7) ^ swz8(arow)) * 16) : kOOB;
         const int wrow = MODE == 0 ? (wave >> 1) * 32 + i * 8 + (lane >> 3) : row;  // relative to n0
         d.vb[i] = wrow < nlim ? (uint32_t)wrow * (uint32_t)K + logical : kOOB;
     }
@@ -656,8 +674,9 @@ void launch_one(int tb, bool w4, int64_t grid, const Fp8Args& a, hipStream_t s) 
 }  // namespace
 
 hipError_t launch_gemm_fp8(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_cap, const void* x_rows,
-                           const float* x_scale, const int32_t* offsets, const moe_weights& w, const WTab& wt,
-                           void* y_rows, const FfnWork& wk, void* h, float* h_scale, hipStream_t s) {
+                           const float* x_scale, const int32_t* row_src, const int32_t* offsets,
+                           const moe_weights& w, const WTab& wt, void* y_rows, const FfnWork& wk, void* h,
+                           float* h_scale, hipStream_t s) {
     // Tile height: groups of about 256 rows or fewer (the DeepSeek-V3 layer's
     // 256 experts, 8 rows a token) fill 128-row tiles; a 224-row tile would
     // split them into two 128-row tiles and compute 224 rows of each.
@@ -680,6 +699,9 @@ hipError_t launch_gemm_fp8(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_c
     a.NT = wk.nt1;
     a.a = static_cast<const uint8_t*>(x_rows);
     a.a_scale = x_scale;
+    a.a_row_src = row_src;  // indexed: x_rows is x [T][H], x_scale its [T][H / 128]
+    a.a_row_k = c.k;
+    a.a_rows = c.T;
     a.w0 = static_cast<const uint8_t*>(w.w_gate);
     a.w1 = static_cast<const uint8_t*>(w.w_up);
     a.s0 = w.s_gate;
@@ -697,6 +719,7 @@ hipError_t launch_gemm_fp8(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_c
     a.NT = wk.nt2;
     a.a = static_cast<const uint8_t*>(h);
     a.a_scale = h_scale;
+    a.a_row_src = nullptr;
     a.w0 = static_cast<const uint8_t*>(w.w_down);
     a.w1 = nullptr;
     a.slot0 = 2;

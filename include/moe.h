@@ -126,10 +126,11 @@ typedef enum moe_stage {
  *                zero padded; R16 = roundup(moe_max_rows, 16) rows, followed,
  *                when has_shared, by the same layout of x's T rows (padded to
  *                16) that the shared expert reads;
- *                MOE_LAYOUT_INDEXED (bf16, T * H * 2 < 2^31): x_perm is not
- *                materialised --
- *                moe_permute writes the maps only and moe_grouped_ffn reads
- *                dispatched row r from x itself, at token row_src[r] / k;
+ *                MOE_LAYOUT_INDEXED (bf16 or e4m3, x under 2 GiB): x_perm is
+ *                not materialised -- moe_permute writes the maps only and
+ *                moe_grouped_ffn reads dispatched row r from x itself (e4m3:
+ *                and its scale from x_scale [T][H/128]), at token
+ *                row_src[r] / k;
  *                moe_x_perm_bytes gives the size (0 when indexed).
  * E <= 1024. */
 typedef struct moe_cfg {

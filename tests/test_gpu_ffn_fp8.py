@@ -158,3 +158,50 @@ def test_grouped_ffn_fp8_full_size_sampled():
         rows[e] = sorted(set(pick.tolist()) | {oc[e], oc[e + 1] - 1})
     err, rms, flipped = _check_rows(wq, xq, xs, y, rows)
     assert err <= TOL and rms <= TOL_RMS_BF16, (err, rms, flipped)
+
+
+@pytest.mark.parametrize("wfmt", ["e4m3", "mxfp4"])
+def test_indexed_e4m3_rows_equal_materialised_rows(wfmt):
+    """The layer's dispatch for low-precision experts: moe_permute writes the
+    maps only (MOE_LAYOUT_INDEXED) and GEMM1 reads each dispatched row and its
+    scale from the quantised tokens through row_src.  Same kernels, same
+    operand values in LDS: y must equal, bit for bit, the call on the
+    materialised e4m3 x_perm (with m_tile padding rows in both)."""
+    d = dev()
+    T, H, E, k, I = 333, 512, 6, 3, 384
+    s = synth.MoeShape("idx8", T=T, H=H, E=E, k=k, I=I, dtype="fp8", seed=17)
+    g = torch.Generator(device="cpu").manual_seed(4)
+    ids = torch.stack([torch.randperm(E, generator=g)[:k] for _ in range(T)]).to(torch.int32).to(d)
+    xb = synth.normal(synth.stream_key(17, "x"), (T, H), 1.0, d, torch.bfloat16)
+    gen = synth.mxfp4_expert_weights if wfmt == "mxfp4" else synth.fp8_expert_weights
+    wq = [gen(s, e, d) for e in range(E)]
+    wg, sg, wu, su, wd, sd = (torch.stack([w[i] for w in wq]) for i in range(6))
+    w = moe.weights(wg, wu, wd, s_gate=sg, s_up=su, s_down=sd)
+    wdt = moe.MOE_FP4_E2M1 if wfmt == "mxfp4" else moe.MOE_FP8_E4M3
+    ys = []
+    for layout in (moe.MOE_LAYOUT_ROWMAJOR, moe.MOE_LAYOUT_INDEXED):
+        c = moe.make_cfg(T=T, H=H, E=E, k=k, I=I, act_dtype=moe.MOE_FP8_E4M3, w_dtype=wdt, y_dtype=moe.MOE_F32,
+                         m_tile=16, x_layout=layout)
+        assert moe.moe_validate(c) == moe.MOE_OK, moe.moe_last_error()
+        xq = torch.empty((T, H), dtype=torch.uint8, device=d)
+        xs = torch.empty((T, H // 128), device=d)
+        moe.moe_quantize_fp8(moe.make_cfg(T=T, H=H, E=E, k=k, I=I), xb, xq, xs)
+        rows = moe.moe_max_rows(c)
+        i32 = dict(dtype=torch.int32, device=d)
+        counts, offs = torch.empty(E, **i32), torch.empty(E + 1, **i32)
+        row_src, tok_row = torch.empty(rows, **i32), torch.empty((T, k), **i32)
+        indexed = layout == moe.MOE_LAYOUT_INDEXED
+        x_perm = None if indexed else torch.empty((rows, H), dtype=torch.uint8, device=d)
+        xps = None if indexed else torch.empty((rows, H // 128), device=d)
+        moe.moe_permute(c, xq, xs, ids, counts, offs, row_src, tok_row, x_perm, xps,
+                        moe.workspace(c, moe.MOE_STAGE_PERMUTE, d))
+        y = torch.full((rows, H), -12345.0, device=d)
+        moe.moe_grouped_ffn(c, rows, xq if indexed else x_perm, xs if indexed else xps, offs, w, None, y, None,
+                            moe.workspace(c, moe.MOE_STAGE_FFN, d, n_rows_cap=rows), row_src=row_src)
+        torch.cuda.synchronize()
+        ys.append((y, offs.cpu().numpy(), row_src.cpu().numpy()))
+    (y0, o0, r0), (y1, o1, r1) = ys
+    assert np.array_equal(o0, o1) and np.array_equal(r0, r1)
+    n = int(o0[-1])
+    assert torch.equal(y0[:n], y1[:n])
+    assert bool(torch.isfinite(y0[:n]).all())
