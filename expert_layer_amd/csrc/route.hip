@@ -270,7 +270,39 @@ route_select(const float* __restrict__ logits, int nsplit, const float* __restri
     bool allowed[PL];
 #pragma unroll
     for (int i = 0; i < PL; ++i) allowed[i] = ok[i];
-    if (n_groups > 1) {
+    if (n_groups > 1 && n_groups == 2 * PL && E == 64 * PL) {
+        // Groups of 32 experts (the DeepSeek-V3 shape): group 2 i + h is
+        // register i of lanes 32 h .. 32 h + 31, so one half-wave butterfly per
+        // register gives two groups' top-2 keys at once.  The kept groups are
+        // those ranked below topk_groups, ties to the lower group: the same
+        // choice as taking the best group topk_groups times.
+        float gsc[2 * PL];
+#pragma unroll
+        for (int i = 0; i < PL; ++i) {
+            float b1 = key[i], b2 = -INFINITY;
+#pragma unroll
+            for (int off = 16; off >= 1; off >>= 1) {
+                const float o1 = __shfl_xor(b1, off), o2 = __shfl_xor(b2, off);
+                const float n1 = fmaxf(b1, o1);
+                const float n2 = fmaxf(fminf(b1, o1), fmaxf(b2, o2));
+                b1 = n1;
+                b2 = n2;
+            }
+            const float g = group_score == MOE_GROUP_MAX ? b1 : b1 + b2;
+            gsc[2 * i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g), 0));
+            gsc[2 * i + 1] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g), 32));
+        }
+        uint32_t kept_mask = 0;
+#pragma unroll
+        for (int g = 0; g < 2 * PL; ++g) {
+            int rank = 0;
+#pragma unroll
+            for (int h = 0; h < 2 * PL; ++h) rank += (gsc[h] > gsc[g] || (gsc[h] == gsc[g] && h < g)) ? 1 : 0;
+            if (rank < topk_groups) kept_mask |= 1u << g;
+        }
+#pragma unroll
+        for (int i = 0; i < PL; ++i) allowed[i] = (kept_mask >> (2 * i + (lane >> 5))) & 1u;
+    } else if (n_groups > 1) {
         const int gs = E / n_groups;
         float gk = -INFINITY;  // lane g holds the score of group g
         for (int g = 0; g < n_groups; ++g) {

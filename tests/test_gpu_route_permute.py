@@ -78,6 +78,32 @@ def test_route_ties_and_group_limit_edge_cases(score):
                 assert np.max(np.abs(w - rw)) <= 1.5e-5
 
 
+@pytest.mark.parametrize("score", [oracle.SOFTMAX, oracle.SIGMOID])
+def test_route_groups_of_32_ties_and_limits(score):
+    """Groups of 32 experts with E = 64, 128, 256 (the kernel's half-wave
+    group path, DeepSeek-V3's 8 groups at E = 256): exact ties between keys
+    and between group scores, every topk_groups, both group scores."""
+    rng = np.random.default_rng(23)
+    T = 41
+    for E in (64, 128, 256):
+        G = E // 32
+        cases = [
+            np.zeros((T, E), np.float32),
+            (rng.integers(-2, 3, (T, E)) * 0.5).astype(np.float32),
+            rng.normal(0, 1, (T, E)).astype(np.float32),
+        ]
+        for KG in sorted({1, max(1, G // 2), G}):
+            k = min(8, 32 * KG)
+            for gsc in (0, 1):
+                for lg in cases:
+                    c = moe.make_cfg(T=T, H=64, E=E, k=k, I=64, n_groups=G, topk_groups=KG, score_fn=score,
+                                     group_score=gsc, renormalize=True, routed_scale=2.5)
+                    ids, w, _ = _route(c, None, None, None, torch.from_numpy(lg).to(dev()))
+                    rid, rw = oracle.route_select(lg, k, score, G, KG, gsc, True, 2.5, None)
+                    assert np.array_equal(ids, rid), (E, KG, gsc)
+                    assert np.max(np.abs(w - rw)) <= 2.5e-5
+
+
 def test_route_k_equals_e_and_single_expert():
     rng = np.random.default_rng(21)
     for E, k in [(1, 1), (8, 8), (32, 32), (64, 32), (65, 3), (1024, 8)]:
