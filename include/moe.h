@@ -352,12 +352,14 @@ moe_status moe_quantize_fp8(const moe_cfg *cfg, const void *x, uint8_t *x_q, flo
  * MOE_LAYOUT_INDEXED, whatever cfg->m_tile and cfg->x_layout say (those shape
  * the standalone stage calls only); the result equals that of the four stage
  * calls made with those two fields.  w may be row-major or tiled.
- * Fp8 experts (act_dtype MOE_BF16, w_dtype MOE_FP8_E4M3, row-major e4m3
- * weights with block scales, x 16-byte aligned): the route on bf16 x, then
- * moe_quantize_fp8 of x, moe_permute of the e4m3 rows and their scales
- * (m_tile 16, row-major), the fp8 grouped FFN over the routed rows and,
- * with a shared expert, a second one over the T quantised tokens, then
- * moe_combine.
+ * Low-precision experts (act_dtype MOE_BF16, w_dtype MOE_FP8_E4M3 or
+ * MOE_FP4_E2M1, row-major weights with their scales, x 16-byte aligned): the
+ * route on bf16 x, then moe_quantize_fp8 of x, moe_permute's maps (m_tile 16,
+ * MOE_LAYOUT_INDEXED: the routed GEMM1 reads the e4m3 token rows and their
+ * scales through row_src), the grouped FFN over the routed rows and, with a
+ * shared expert, a second one over the T quantised tokens, then
+ * moe_combine.  With pointer-table weights (moe_weights.table) the FFN
+ * kernels take the layer from *w->layer when they run.
  * ws: moe_workspace_bytes(cfg, MOE_STAGE_LAYER). */
 moe_status moe_layer(const moe_cfg *cfg, const void *w_router, const float *bias,
                      const moe_weights *w, const void *x, void *out, void *ws,
