@@ -30,7 +30,6 @@ import hashlib
 import json
 import math
 import os
-import subprocess
 import sys
 import time
 
@@ -57,6 +56,9 @@ def parse():
     p.add_argument("--tokens", type=int, default=0,
                    help="override the workload's token count T (the small-T, weight-streaming regime)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extra", action="store_true",
+                   help="the default run also times the c4 (skewed routing) layer and the c5 fp8 grouped FFN as "
+                        "extra keys of its line; this leaves them out")
     p.add_argument("--rowmajor-weights", action="store_true",
                    help="time the row-major weight layout instead of the tiled one")
     p.add_argument("--fp4-weights", action="store_true",
@@ -169,11 +171,104 @@ def main():
         calibrate_copy(dev)
     s = synth.config(a.workload, **({"T": a.tokens} if a.tokens else {}))
     if s.dtype == "fp8":
-        return bench_fp8_ffn(a, s, dev)
-    if a.fp8_experts:
-        return bench_fp8_layer(a, s, dev)
-    if s.dtype != "bf16":
+        res = bench_fp8_ffn(a, s, dev)
+    elif a.fp8_experts:
+        res = bench_fp8_layer(a, s, dev)
+    elif s.dtype != "bf16":
         raise SystemExit("bench.py times the bf16 layers (c2/c3/c4) and the fp8 grouped FFN (c5)")
+    else:
+        res = bench_bf16_layer(a, s, dev)
+    if res is None:  # a traffic run prints no line
+        return
+    default_run = (a.workload == "c3_dsv3_bf16" and not a.tokens and not a.fp8_experts and not a.weight_table
+                   and not a.rowmajor_weights and not a.no_extra)
+    if default_run:
+        # the skewed-routing layer and the fp8 expert-parallel share, timed the
+        # same way in the same run (their own keys; `value` stays the c3 layer)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        extra = {}
+        for name in ("c4_qwen3_skew_bf16", "c5_dsv3_ep_fp8"):
+            se = synth.config(name)
+            r = bench_fp8_ffn(a, se, dev) if se.dtype == "fp8" else bench_bf16_layer(a, se, dev, extra=True)
+            extra[name] = summary(r)
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+        res["extra_workloads"] = extra
+    print(json.dumps(res), flush=True)
+
+
+def summary(r):
+    """The figures of another workload's line that ride along the main one."""
+    keep = ("metric", "value", "unit", "ms_per_step", "dtype", "config", "tokens_per_s", "stages")
+    out = {k: r[k] for k in keep if k in r}
+    rf = r["roofline"]
+    out["roofline"] = {k: rf[k] for k in ("bound", "achieved", "peak", "unit", "frac", "mfma_frac", "hbm_frac",
+                                           "roofline_ms") if k in rf}
+    return out
+
+
+def sclk_under_load(step, ms_step, seconds=1.5):
+    """The GFX clock while the step runs back to back: amdsmi polled every
+    10 ms by a thread while about `seconds` of steps are in flight.  Returns
+    the median, min and max of the samples (MHz), or the reason there are
+    none."""
+    import threading
+
+    import torch
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        hs = amdsmi.amdsmi_get_processor_handles()
+        h = hs[0]
+        bus = getattr(torch.cuda.get_device_properties(0), "pci_bus_id", None)
+        if bus is not None and len(hs) > 1:
+            for c in hs:
+                if int(amdsmi.amdsmi_get_gpu_device_bdf(c).split(":")[1], 16) == int(bus):
+                    h = c
+    except Exception as e:  # no amdsmi or no device access: no figure
+        return {"error": f"amdsmi: {e}"}
+    samples = []
+    stop = threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            try:
+                samples.append(float(amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)["clk"]))
+            except Exception:
+                pass
+            time.sleep(0.01)
+
+    n = max(10, int(seconds * 1e3 / max(ms_step, 0.05)))
+    torch.cuda.synchronize()
+    for i in range(n):
+        step(i)
+    th = threading.Thread(target=poll, daemon=True)
+    th.start()
+    torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    try:
+        amdsmi.amdsmi_shut_down()
+    except Exception:
+        pass
+    if not samples:
+        return {"error": "no samples"}
+    v = sorted(samples)
+    return {"median_mhz": v[len(v) // 2], "min_mhz": v[0], "max_mhz": v[-1], "samples": len(v),
+            "steps": n, "how": "amdsmi GFX clock polled every 10 ms while the steps ran back to back"}
+
+
+def bench_bf16_layer(a, s, dev, extra=False):
+    """A bf16 layer workload (c2/c3/c4): a step is one moe_layer call.  With
+    `extra`, a line that rides along the main one: no CPU baseline, no clock
+    sampling, no host-dispatch figures."""
+    import numpy as np
+    import torch
+
+    import expert_layer_amd as moe
+    import synth
+
     T, H, E, k, I = s.T, s.H, s.E, s.k, s.I
     c = moe.make_cfg(T=T, H=H, E=E, k=k, I=I, n_groups=s.n_groups, topk_groups=s.topk_groups,
                      score_fn=moe.MOE_SCORE_SIGMOID if s.score == "sigmoid" else moe.MOE_SCORE_SOFTMAX,
@@ -197,7 +292,7 @@ def main():
         sh = synth.shared_weights(s, dev) if s.shared else (None, None, None)
     w = moe.weights(wg, wu, wd, sh_gate=sh[0], sh_up=sh[1], sh_down=sh[2])
     tiled_buf = None
-    if not a.rowmajor_weights:
+    if not a.rowmajor_weights or extra:
         # weights are static: tiled once at load time, outside the timed region
         w, tiled_buf = moe.tile_weights(c, w, dev)
         del wg, wu, wd, sh
@@ -207,7 +302,7 @@ def main():
     ws = moe.workspace(c, moe.MOE_STAGE_LAYER, dev)
     ws_layers = [w]
     table = layer_ids = None
-    if a.weight_table > 0:
+    if a.weight_table > 0 and not extra:
         # layer l's expert e is the weight set's expert (e + 37 l) mod E: each
         # layer reads all E experts' bytes, as distinct weights would
         n_l = a.weight_table
@@ -332,7 +427,7 @@ def main():
     if a.traffic_run:
         print(f"[bench] traffic run done: {a.warmup + a.steps} stage passes, grouped FFN "
               f"{stage_ms[2]:.3f} ms", flush=True)
-        return
+        return None
 
     # ---- algorithmic work
     I_sh = s.I_shared if s.shared else 0
@@ -369,7 +464,12 @@ def main():
             traffic = tf.get("hbm_bytes_per_launch")
     # The bound is the larger of the two roofline times, flop / MFMA peak and
     # algorithmic bytes / HBM peak; the other fraction is reported beside it.
-    ffn_bytes = bytes_["grouped_ffn"]
+    # Algorithmic bytes: the minimal bytes of the layer's roofline -- every
+    # weight once, x read once, the output written once (bf16) -- which the
+    # grouped FFN cannot go below; the bytes this design moves per launch
+    # (each dispatched row read, bf16 y written) ride alongside as io_bytes.
+    ffn_io_bytes = bytes_["grouped_ffn"]
+    ffn_bytes = w_bytes + T * H * 2 + T * H * 2
     t_mfma = ffn_flop / (PEAK_BF16_TFLOPS * 1e12)
     t_hbm = ffn_bytes / (PEAK_HBM_GBS * 1e9)
     ffn_gbs = ffn_bytes / (stage_ms[2] * 1e-3) / 1e9
@@ -382,22 +482,14 @@ def main():
     roofline.update({
         "traffic": traffic,
         "kernel": "moe_grouped_ffn (ffn_gemm_bf16<0> gate/up+SwiGLU, ffn_gemm_bf16<1> down, tile list)",
-        "flop_per_launch": ffn_flop, "bytes_per_launch": ffn_bytes,
+        "flop_per_launch": ffn_flop, "bytes_per_launch": ffn_bytes, "io_bytes_per_launch": ffn_io_bytes,
+        "io_frac": round(ffn_io_bytes / (stage_ms[2] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "roofline_ms": round(max(t_mfma, t_hbm) * 1e3, 4),
         "mfma_frac": round(ffn_achieved / PEAK_BF16_TFLOPS, 4),
         "hbm_frac": round(ffn_gbs / PEAK_HBM_GBS, 4)})
 
-    cpu = None if a.no_cpu_baseline else cpu_baseline(s, x, w_r, a.cpu_seconds)
-
-    sclk = None
-    try:
-        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
-        for line in r.stdout.splitlines():
-            if "sclk" in line and "Mhz" in line:
-                sclk = line.split("(")[-1].split(")")[0]
-                break
-    except Exception:
-        pass
+    cpu = None if (a.no_cpu_baseline or extra) else cpu_baseline(s, x, w_r, a.cpu_seconds)
+    sclk = None if extra else sclk_under_load(step, ms_step)
 
     res = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps,
@@ -418,7 +510,7 @@ def main():
         "sclk": sclk,
         **({"dispatch": dispatch} if dispatch else {}),
     }
-    print(json.dumps(res), flush=True)
+    return res
 
 
 def bench_fp8_ffn(a, s, dev):
@@ -497,7 +589,7 @@ def bench_fp8_ffn(a, s, dev):
                      "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
         "cpu_baseline": None,
     }
-    print(json.dumps(res), flush=True)
+    return res
 
 
 def bench_fp8_layer(a, s, dev):
@@ -664,7 +756,7 @@ def bench_fp8_layer(a, s, dev):
         "roofline": roofline,
         "cpu_baseline": None,
     }
-    print(json.dumps(res), flush=True)
+    return res
 
 
 def cpu_baseline(s, x, w_r, target_s):

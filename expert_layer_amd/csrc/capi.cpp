@@ -218,12 +218,20 @@ XPermGeom x_perm_geom(const moe_cfg& c) {
     return g;
 }
 
+// The indexed layout addresses all of x through one buffer descriptor, whose
+// 32-bit offsets reach 2 GiB.
+bool x_indexable(const moe_cfg& c, int elem_bytes) { return (int64_t)c.T * c.H * elem_bytes < ((int64_t)1 << 31); }
+
 // The configuration moe_layer runs its stages with: expert segments padded to
-// 16 rows, and for bf16 no x_perm (GEMM1 reads x through row_src).
+// 16 rows, and for bf16 no x_perm (GEMM1 reads x through row_src) while x is
+// under 2 GiB; a larger x is dispatched into the tiled x_perm.
 moe_cfg layer_stage_cfg(const moe_cfg& c) {
     moe_cfg s = c;
     s.m_tile = 16;
-    s.x_layout = c.act_dtype == MOE_BF16 ? MOE_LAYOUT_INDEXED : MOE_LAYOUT_ROWMAJOR;
+    if (c.act_dtype == MOE_BF16)
+        s.x_layout = x_indexable(c, 2) ? MOE_LAYOUT_INDEXED : MOE_LAYOUT_TILED;
+    else
+        s.x_layout = MOE_LAYOUT_ROWMAJOR;
     return s;
 }
 
@@ -239,7 +247,9 @@ moe_cfg fp8_routed_cfg(const moe_cfg& c) {
     q.has_shared = 0;
     q.I_shared = 0;
     q.m_tile = 16;
-    q.x_layout = MOE_LAYOUT_INDEXED;  // GEMM1 reads the quantised tokens through row_src
+    // GEMM1 reads the quantised tokens through row_src while they are under
+    // 2 GiB; more are dispatched into a row-major x_perm with its scales
+    q.x_layout = x_indexable(c, 1) ? MOE_LAYOUT_INDEXED : MOE_LAYOUT_ROWMAJOR;
     return q;
 }
 moe_cfg fp8_shared_cfg(const moe_cfg& c) {
@@ -282,7 +292,8 @@ LayerCarve layer_carve(const moe_cfg& c, void* p) {
     if (f8) {
         l.x_q = cv.take<uint8_t>((size_t)c.T * c.H);
         l.x_s = cv.take<float>((size_t)c.T * (c.H / 128));
-        l.x_perm_scale = nullptr;  // indexed: no dispatched copy of the rows or their scales
+        // indexed: no dispatched copy of the rows or their scales
+        l.x_perm_scale = cs.x_layout == MOE_LAYOUT_INDEXED ? nullptr : cv.take<float>((size_t)rows * (c.H / 128));
         l.offsets_sh = cv.take<int32_t>(2);
         if (c.has_shared) {
             const size_t fs = ffn_carve(fp8_shared_cfg(c), c.T, nullptr).bytes;
@@ -409,8 +420,9 @@ moe_status layer_fp8_experts(const moe_cfg& c, const moe_weights& w, const void*
     moe_status st = permute_enqueue(cq, l.x_q, l.x_s, l.ids, l.counts, l.offsets, l.row_src, l.tok_row, l.x_perm,
                                     l.x_perm_scale, l.scratch, s);
     if (st != MOE_OK) return st;
-    st = ffn_enqueue(cq, max_rows_of(cq), l.x_q, l.x_s, l.offsets, l.row_src, w, wtab_of(c, w, 0), nullptr,
-                     l.y_rows, nullptr, l.scratch, s);
+    const bool indexed = cq.x_layout == MOE_LAYOUT_INDEXED;
+    st = ffn_enqueue(cq, max_rows_of(cq), indexed ? l.x_q : l.x_perm, indexed ? l.x_s : l.x_perm_scale, l.offsets,
+                     l.row_src, w, wtab_of(c, w, 0), nullptr, l.y_rows, nullptr, l.scratch, s);
     if (st != MOE_OK) return st;
     if (c.has_shared) {
         const moe_cfg c1 = fp8_shared_cfg(c);
@@ -471,6 +483,8 @@ moe_status moe_route(const moe_cfg* cfg, const void* x, const void* w_router, co
     if (!logits_in) {
         REQUIRE(x, "x");
         REQUIRE(w_router, "w_router");
+        REQUIRE_A16(x, "x");
+        REQUIRE_A16(w_router, "w_router");
     }
     REQUIRE(topk_ids, "topk_ids");
     REQUIRE(topk_w, "topk_w");
@@ -504,6 +518,8 @@ moe_status moe_permute(const moe_cfg* cfg, const void* x, const float* x_scale, 
     REQUIRE(row_src, "row_src");
     REQUIRE(tok_row, "tok_row");
     if (c.x_layout != MOE_LAYOUT_INDEXED) REQUIRE(x_perm, "x_perm");
+    REQUIRE_A16(x, "x");
+    REQUIRE_A16(x_perm, "x_perm");
     if (c.act_dtype == MOE_FP8_E4M3 && c.x_layout != MOE_LAYOUT_INDEXED) {
         REQUIRE(x_scale, "x_scale");
         REQUIRE(x_perm_scale, "x_perm_scale");
@@ -655,6 +671,10 @@ moe_status moe_combine(const moe_cfg* cfg, const void* y_rows, const int32_t* to
     REQUIRE(tok_row, "tok_row");
     REQUIRE(topk_w, "topk_w");
     REQUIRE(out, "out");
+    if (c.has_shared) REQUIRE(y_shared, "y_shared");
+    REQUIRE_A16(y_rows, "y_rows");
+    REQUIRE_A16(y_shared, "y_shared");
+    REQUIRE_A16(out, "out");
     if (c.T == 0) return MOE_OK;
     hipError_t e = moe::launch_combine(c, y_rows, tok_row, topk_w, y_shared, out, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "moe_combine");
@@ -688,10 +708,15 @@ moe_status moe_layer(const moe_cfg* cfg, const void* w_router, const float* bias
     if ((st = check_weights(c, w)) != MOE_OK) return st;
     REQUIRE(x, "x");
     REQUIRE(out, "out");
+    REQUIRE_A16(x, "x");
+    REQUIRE_A16(w_router, "w_router");
+    REQUIRE_A16(out, "out");
     if (fp8_experts(c)) {
-        REQUIRE_A16(x, "x");
         if (w->layout != MOE_LAYOUT_ROWMAJOR) return fail(MOE_ERR_UNSUPPORTED, "fp8 experts take row-major weights");
     }
+    // the stage configuration the layer derives must be a valid one
+    const moe_cfg derived = fp8_experts(c) ? fp8_routed_cfg(c) : layer_stage_cfg(c);
+    if ((st = check_cfg(&derived)) != MOE_OK) return st;
     LayerCarve l = layer_carve(c, ws);
     if ((st = check_ws(ws, ws_bytes, l.bytes)) != MOE_OK) return st;
     if (c.T == 0) return MOE_OK;

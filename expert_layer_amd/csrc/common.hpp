@@ -100,7 +100,10 @@ __device__ __forceinline__ int c_row(int i, int lane) { return (i >> 2) * 8 + (l
 // XCD: the dispatcher hands block b to XCD b % 8, so logical tile
 // L = (b % 8) * per_xcd + b / 8 keeps a contiguous run of tiles (sharing an A
 // panel or a weight panel) inside one XCD's L2.  Returns -1 for idle blocks.
-__device__ __forceinline__ int xcd_remap(int b, int n_valid) {
+// Every L < n_valid is reached exactly once when the grid is a multiple of 8
+// of at least n_valid blocks (then each XCD has grid / 8 >= per_xcd blocks):
+// launches size their grids with xcd_grid.
+__host__ __device__ __forceinline__ int xcd_remap(int b, int n_valid) {
     constexpr int kXcd = 8;
     int per = (n_valid + kXcd - 1) / kXcd;
     int x = b % kXcd, i = b / kXcd;
@@ -108,6 +111,9 @@ __device__ __forceinline__ int xcd_remap(int b, int n_valid) {
     int L = x * per + i;
     return L < n_valid ? L : -1;
 }
+// Grid of a launch whose blocks go through xcd_remap for up to `items`
+// logical tiles: `items` rounded up to a multiple of 8.
+__host__ __device__ __forceinline__ int64_t xcd_grid(int64_t items) { return (items + 7) / 8 * 8; }
 
 }  // namespace moe
 

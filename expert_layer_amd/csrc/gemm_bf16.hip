@@ -708,7 +708,7 @@ hipError_t launch_gemm_bf16(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_
     a.N_shared = has_sh ? c.I_shared : c.I;
     a.NT = wk.nt1;
     a.out_f32 = 0;
-    hipLaunchKernelGGL(ffn_gemm_bf16<0>, dim3((unsigned)(max_tiles * a.NT)), dim3(NTH), 0, s, a);
+    hipLaunchKernelGGL(ffn_gemm_bf16<0>, dim3((unsigned)xcd_grid(max_tiles * a.NT)), dim3(NTH), 0, s, a);
     // GEMM2: down -> y
     a.work = reinterpret_cast<const int2*>(wk.work2);
     a.a_routed = static_cast<const uint16_t*>(h_tiles);
@@ -729,7 +729,7 @@ hipError_t launch_gemm_bf16(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_
     a.N_shared = c.H;
     a.NT = wk.nt2;
     a.out_f32 = c.y_dtype == MOE_F32;
-    hipLaunchKernelGGL(ffn_gemm_bf16<1>, dim3((unsigned)(max_tiles * a.NT)), dim3(NTH), 0, s, a);
+    hipLaunchKernelGGL(ffn_gemm_bf16<1>, dim3((unsigned)xcd_grid(max_tiles * a.NT)), dim3(NTH), 0, s, a);
     return hipGetLastError();
 }
 

@@ -56,7 +56,7 @@ constexpr int kStageA = kChunksA + 72;         // A, then 288 fp32 row scales (s
 constexpr int kScaleB4 = BN * 4;               // MXFP4: chunks of a stage's weight codes; then 8 x 256 B of scales
 static_assert(BM % 32 == 0 && BM <= 224, "three A stages and two B stages must fit in 160 KiB of LDS");
 static_assert(kFfnBmFp8Small == 128, "the load slots below are laid out for 4 and 7 row blocks");
-constexpr uint32_t kOOB = 0x40000000u;         // past every descriptor: the load returns zero
+constexpr uint32_t kOOB = 0x80000000u;         // past every descriptor (all are < 2 GiB): the load returns zero
 
 typedef __attribute__((address_space(3))) void* lds_t;
 
@@ -710,7 +710,7 @@ hipError_t launch_gemm_fp8(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_c
     a.out_scale = h_scale;
     a.K = c.H;
     a.N = c.I;
-    const int64_t grid1 = max_tiles * wk.nt1;
+    const int64_t grid1 = xcd_grid(max_tiles * wk.nt1);
     launch_one<0>(tb, w4, grid1, a, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -730,7 +730,7 @@ hipError_t launch_gemm_fp8(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_c
     a.K = c.I;
     a.N = c.H;
     a.out_f32 = c.y_dtype == MOE_F32 ? 1 : 0;
-    const int64_t grid2 = max_tiles * wk.nt2;
+    const int64_t grid2 = xcd_grid(max_tiles * wk.nt2);
     launch_one<1>(tb, w4, grid2, a, s);
     return hipGetLastError();
 }

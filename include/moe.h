@@ -331,14 +331,19 @@ moe_status moe_grouped_ffn(const moe_cfg *cfg, int64_t n_rows_cap, const void *x
  * 3.2.2's expert results per token and choice).
  *   out[t][h] = sum_{j=0..k-1} topk_w[t][j] * y_rows[tok_row[t*k+j]][h]  (+ y_shared[t][h])
  * accumulated in fp32 in slot order, the shared term last.
- * y_rows, y_shared in cfg->y_dtype; y_shared may be NULL; out [T][H] in
- * cfg->out_dtype. */
+ * y_rows, y_shared in cfg->y_dtype; out [T][H] in cfg->out_dtype.  The
+ * shared term is added whenever y_shared != NULL; y_shared must not be NULL
+ * when cfg->has_shared.  y_rows, y_shared and out are 16-byte aligned
+ * (MOE_ERR_INVALID_ARG otherwise). */
 moe_status moe_combine(const moe_cfg *cfg, const void *y_rows, const int32_t *tok_row,
                        const float *topk_w, const void *y_shared, void *out, void *stream);
 
-/* Per-token quantisation of activations for fp8 experts (the DeepSeek-V3
- * page's fp8 MoE GEMMs, "fp8 DeepGEMM"; the per-token 1 x 128 activation
- * scales of its fp8 recipe).  For each row t and 128-column block b of
+/* Per-token quantisation of activations for fp8 experts.  The AFD page runs
+ * its MoE GEMMs in fp8 (section 1, the figure caption on MoE MFU: "fp8
+ * DeepGEMM"; section 7: W8A8) without printing the quantiser; the fp8
+ * expert-parallel workload this library is measured on states per-token
+ * 1 x 128 activation scales.  The rule is the one the grouped FFN applies to
+ * its intermediate.  For each row t and 128-column block b of
  * x [T][H] bf16: s = max|x| / 448 over the block (1 when the block is all
  * zero), q = e4m3_rne_sat(x / s), the divisions in fp32; x_q [T][H] OCP e4m3
  * codes, x_scale [T][H/128] fp32 (x, x_q 16- and 8-byte aligned, device).
@@ -349,14 +354,17 @@ moe_status moe_quantize_fp8(const moe_cfg *cfg, const void *x, uint8_t *x_q, flo
  * enqueued on `stream` with no host synchronisation.  x [T][H] in act_dtype
  * (F32 or BF16); out [T][H] in out_dtype.  All intermediates live in ws.
  * The stages run with m_tile = 16 and, for bf16, x_layout =
- * MOE_LAYOUT_INDEXED, whatever cfg->m_tile and cfg->x_layout say (those shape
- * the standalone stage calls only); the result equals that of the four stage
- * calls made with those two fields.  w may be row-major or tiled.
+ * MOE_LAYOUT_INDEXED while x is under 2 GiB (MOE_LAYOUT_TILED beyond, which
+ * the workspace size accounts for), whatever cfg->m_tile and cfg->x_layout say
+ * (those shape the standalone stage calls only); the result equals that of
+ * the four stage calls made with those two fields.  w may be row-major or
+ * tiled.  x, w_router and out are 16-byte aligned.
  * Low-precision experts (act_dtype MOE_BF16, w_dtype MOE_FP8_E4M3 or
  * MOE_FP4_E2M1, row-major weights with their scales, x 16-byte aligned): the
  * route on bf16 x, then moe_quantize_fp8 of x, moe_permute's maps (m_tile 16,
  * MOE_LAYOUT_INDEXED: the routed GEMM1 reads the e4m3 token rows and their
- * scales through row_src), the grouped FFN over the routed rows and, with a
+ * scales through row_src; for quantised tokens of 2 GiB or more, a row-major
+ * x_perm with its scales), the grouped FFN over the routed rows and, with a
  * shared expert, a second one over the T quantised tokens, then
  * moe_combine.  With pointer-table weights (moe_weights.table) the FFN
  * kernels take the layer from *w->layer when they run.

@@ -85,6 +85,8 @@ def lib():
         L.orc_expert_ffn_mxfp4.restype = None
         L.orc_combine.argtypes = [i64, i32, i64, P, P, P, P, P]
         L.orc_combine.restype = None
+        L.orc_bf16_round_array.argtypes = [i64, P, P]
+        L.orc_bf16_round_array.restype = None
         L.orc_layer.argtypes = [i64, i64, i32, i32, i64, i32, i32, i32, i32, i32, dbl,
                                 i32, P, P, P, i32, P, P, P, i64, P, P, P, i32, P, P, P, P]
         L.orc_layer.restype = i32
@@ -139,9 +141,11 @@ def e4m3_rne_sat(values) -> np.ndarray:
 def quantize_rows_e4m3(x):
     """Per-token 1 x 128 quantisation of activations for fp8 experts.  For each
     row and block of 128 columns: s = fp32(max|x|) / 448 in fp32 (1 for an
-    all-zero block), code = e4m3_rne_sat(fp32(x / s)) -- the rule the fp8
-    recipe of the DeepSeek-V3 page applies to activations (per-token 1 x 128
-    scales) and the one this oracle applies to the SwiGLU intermediate (S9).
+    all-zero block), code = e4m3_rne_sat(fp32(x / s)).  The AFD page runs its
+    MoE GEMMs in fp8 (section 1, the MoE MFU figure's caption: "fp8 DeepGEMM";
+    section 7: W8A8) without printing a quantiser; the fp8 expert-parallel
+    workload states per-token 1 x 128 activation scales.  The rule is read as
+    the one this oracle applies to the SwiGLU intermediate (S9).
     x: bf16 bit patterns (uint16) or fp32, [n][H] with H a multiple of 128.
     Returns (codes uint8 [n][H], scales float32 [n][H/128])."""
     x = np.asarray(x)
@@ -163,6 +167,15 @@ def bf16_rne(values) -> np.ndarray:
     v = np.asarray(values, dtype=np.float64)
     return np.array([L.orc_bf16_rne(float(x)) for x in v.ravel()],
                     dtype=np.uint16).reshape(v.shape)
+
+
+def bf16_round(values) -> np.ndarray:
+    """Each value rounded to bf16 as bf16_rne does (nearest-even, decided on
+    its fp32 value) and widened back to fp64: what a bf16 store keeps."""
+    v = _c(np.asarray(values, dtype=np.float64))
+    out = np.empty_like(v)
+    lib().orc_bf16_round_array(v.size, _p(v), _p(out))
+    return out
 
 
 # ----------------------------------------------------------------- layer

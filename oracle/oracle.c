@@ -429,30 +429,70 @@ static double silu(double z) { return z / (1.0 + exp(-z)); }
 void orc_expert_ffn(int64_t n, int64_t H, int64_t I, int x_dtype, const void *x_rows,
                     int w_dtype, const void *w_gate, const void *w_up, const void *w_down,
                     int h_bf16, double *y) {
-#pragma omp parallel for schedule(dynamic, 1)
-    for (int64_t r = 0; r < n; ++r) {
-        double *xr = (double *)malloc(sizeof(double) * (size_t)H);
-        double *a = (double *)malloc(sizeof(double) * (size_t)I);
-        if (xr && a) {
-            for (int64_t h = 0; h < H; ++h) xr[h] = ld(x_dtype, x_rows, (size_t)(r * H + h));
-            for (int64_t i = 0; i < I; ++i) {
-                double g = 0.0, u = 0.0;
+    /* The loops run over the outputs (a weight row at a time, widened once and
+     * applied to every row); each sum still runs over its index in order. */
+    double *X = (double *)malloc(sizeof(double) * (size_t)(n * H + 1));
+    double *A = (double *)malloc(sizeof(double) * (size_t)(n * I + 1));
+    if (X && A) {
+        for (int64_t e = 0; e < n * H; ++e) X[e] = ld(x_dtype, x_rows, (size_t)e);
+#pragma omp parallel for schedule(dynamic, 4)
+        for (int64_t i = 0; i < I; ++i) {
+            double *wg = (double *)malloc(sizeof(double) * (size_t)H);
+            double *wu = (double *)malloc(sizeof(double) * (size_t)H);
+            if (wg && wu) {
                 for (int64_t h = 0; h < H; ++h) {
-                    g += xr[h] * ld(w_dtype, w_gate, (size_t)(i * H + h));
-                    u += xr[h] * ld(w_dtype, w_up, (size_t)(i * H + h));
+                    wg[h] = ld(w_dtype, w_gate, (size_t)(i * H + h));
+                    wu[h] = ld(w_dtype, w_up, (size_t)(i * H + h));
                 }
-                a[i] = silu(g) * u;
-                if (h_bf16) a[i] = orc_bf16_to_f64(orc_bf16_rne(a[i]));
+                for (int64_t r = 0; r < n; ++r) {
+                    const double *xr = X + r * H;
+                    double g = 0.0, u = 0.0;
+                    for (int64_t h = 0; h < H; ++h) {
+                        g += xr[h] * wg[h];
+                        u += xr[h] * wu[h];
+                    }
+                    double a = silu(g) * u;
+                    if (h_bf16) a = orc_bf16_to_f64(orc_bf16_rne(a));
+                    A[r * I + i] = a;
+                }
             }
-            for (int64_t h = 0; h < H; ++h) {
-                double acc = 0.0;
-                for (int64_t i = 0; i < I; ++i)
-                    acc += a[i] * ld(w_dtype, w_down, (size_t)(h * I + i));
-                y[r * H + h] = acc;
-            }
+            free(wg);
+            free(wu);
         }
-        free(xr);
-        free(a);
+#pragma omp parallel for schedule(dynamic, 4)
+        for (int64_t h = 0; h < H; ++h) {
+            double *wd = (double *)malloc(sizeof(double) * (size_t)I);
+            if (wd) {
+                for (int64_t i = 0; i < I; ++i) wd[i] = ld(w_dtype, w_down, (size_t)(h * I + i));
+                for (int64_t r = 0; r < n; ++r) {
+                    const double *a = A + r * I;
+                    double acc = 0.0;
+                    for (int64_t i = 0; i < I; ++i) acc += a[i] * wd[i];
+                    y[r * H + h] = acc;
+                }
+            }
+            free(wd);
+        }
+    }
+    free(X);
+    free(A);
+}
+
+/* The requantisation of the fp8 intermediate, one row a [I] at a time (see
+ * orc_expert_ffn_fp8): per 128-column block, s = fp32(max |fp32(a_i)|) / 448
+ * (1 for a zero block), a_i <- e4m3(e4m3_rne_sat(fp32(fp32(a_i) / s))) * s. */
+static void requant_row_e4m3(int64_t I, double *a) {
+    for (int64_t b = 0; b < I / 128; ++b) {
+        float amax = 0.0f;
+        for (int64_t i = b * 128; i < (b + 1) * 128; ++i) {
+            float v = fabsf((float)a[i]);
+            if (v > amax) amax = v;
+        }
+        float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+        for (int64_t i = b * 128; i < (b + 1) * 128; ++i) {
+            float q = (float)a[i] / s;
+            a[i] = orc_e4m3_to_f64(orc_e4m3_rne_sat((double)q)) * (double)s;
+        }
     }
 }
 
@@ -474,46 +514,60 @@ void orc_expert_ffn_fp8(int64_t n, int64_t H, int64_t I, const uint8_t *xq, cons
                         const uint8_t *wg, const float *sg, const uint8_t *wu, const float *su,
                         const uint8_t *wd, const float *sd, double *y, double *a_out) {
     int64_t HB = H / 128, IB = I / 128;
-#pragma omp parallel for schedule(dynamic, 1)
-    for (int64_t r = 0; r < n; ++r) {
-        double *xr = (double *)malloc(sizeof(double) * (size_t)H);
-        double *a = (double *)malloc(sizeof(double) * (size_t)I);
-        if (xr && a) {
+    /* loops over the outputs, as in orc_expert_ffn; each sum in index order */
+    double *X = (double *)malloc(sizeof(double) * (size_t)(n * H + 1));
+    double *A = (double *)malloc(sizeof(double) * (size_t)(n * I + 1));
+    if (X && A) {
+        for (int64_t r = 0; r < n; ++r)
             for (int64_t h = 0; h < H; ++h)
-                xr[h] = orc_e4m3_to_f64(xq[r * H + h]) * (double)xs[r * HB + h / 128];
-            for (int64_t i = 0; i < I; ++i) {
-                double g = 0.0, u = 0.0;
+                X[r * H + h] = orc_e4m3_to_f64(xq[r * H + h]) * (double)xs[r * HB + h / 128];
+#pragma omp parallel for schedule(dynamic, 4)
+        for (int64_t i = 0; i < I; ++i) {
+            double *wgr = (double *)malloc(sizeof(double) * (size_t)H);
+            double *wur = (double *)malloc(sizeof(double) * (size_t)H);
+            if (wgr && wur) {
                 for (int64_t h = 0; h < H; ++h) {
-                    double wgv = orc_e4m3_to_f64(wg[i * H + h]) * (double)sg[(i / 128) * HB + h / 128];
-                    double wuv = orc_e4m3_to_f64(wu[i * H + h]) * (double)su[(i / 128) * HB + h / 128];
-                    g += xr[h] * wgv;
-                    u += xr[h] * wuv;
+                    wgr[h] = orc_e4m3_to_f64(wg[i * H + h]) * (double)sg[(i / 128) * HB + h / 128];
+                    wur[h] = orc_e4m3_to_f64(wu[i * H + h]) * (double)su[(i / 128) * HB + h / 128];
                 }
-                a[i] = silu(g) * u;
-                if (a_out) a_out[r * I + i] = a[i];
-            }
-            for (int64_t b = 0; b < IB; ++b) {
-                float amax = 0.0f;
-                for (int64_t i = b * 128; i < (b + 1) * 128; ++i) {
-                    float v = fabsf((float)a[i]);
-                    if (v > amax) amax = v;
-                }
-                float s = amax > 0.0f ? amax / 448.0f : 1.0f;
-                for (int64_t i = b * 128; i < (b + 1) * 128; ++i) {
-                    float q = (float)a[i] / s;
-                    a[i] = orc_e4m3_to_f64(orc_e4m3_rne_sat((double)q)) * (double)s;
+                for (int64_t r = 0; r < n; ++r) {
+                    const double *xr = X + r * H;
+                    double g = 0.0, u = 0.0;
+                    for (int64_t h = 0; h < H; ++h) {
+                        g += xr[h] * wgr[h];
+                        u += xr[h] * wur[h];
+                    }
+                    A[r * I + i] = silu(g) * u;
                 }
             }
-            for (int64_t h = 0; h < H; ++h) {
-                double acc = 0.0;
-                for (int64_t i = 0; i < I; ++i)
-                    acc += a[i] * orc_e4m3_to_f64(wd[h * I + i]) * (double)sd[(h / 128) * IB + i / 128];
-                y[r * H + h] = acc;
-            }
+            free(wgr);
+            free(wur);
         }
-        free(xr);
-        free(a);
+        if (a_out) memcpy(a_out, A, sizeof(double) * (size_t)(n * I));
+#pragma omp parallel for schedule(static)
+        for (int64_t r = 0; r < n; ++r) requant_row_e4m3(I, A + r * I);
+#pragma omp parallel for schedule(dynamic, 4)
+        for (int64_t h = 0; h < H; ++h) {
+            double *wdr = (double *)malloc(sizeof(double) * (size_t)I);
+            double *sdr = (double *)malloc(sizeof(double) * (size_t)I);
+            if (wdr && sdr) {
+                for (int64_t i = 0; i < I; ++i) {
+                    wdr[i] = orc_e4m3_to_f64(wd[h * I + i]);
+                    sdr[i] = (double)sd[(h / 128) * IB + i / 128];
+                }
+                for (int64_t r = 0; r < n; ++r) {
+                    const double *a = A + r * I;
+                    double acc = 0.0;
+                    for (int64_t i = 0; i < I; ++i) acc += a[i] * wdr[i] * sdr[i];
+                    y[r * H + h] = acc;
+                }
+            }
+            free(wdr);
+            free(sdr);
+        }
     }
+    free(X);
+    free(A);
 }
 
 /* ------------------------------------------------------- MXFP4 weights
@@ -553,55 +607,55 @@ void orc_mxfp4_dequant(int64_t rows, int64_t K, const uint8_t *codes, const uint
 void orc_expert_ffn_mxfp4(int64_t n, int64_t H, int64_t I, const uint8_t *xq, const float *xs,
                           const uint8_t *wg, const uint8_t *sg, const uint8_t *wu, const uint8_t *su,
                           const uint8_t *wd, const uint8_t *sd, double *y, double *a_out) {
-    int64_t HB = H / 128, IB = I / 128;
+    int64_t HB = H / 128;
     double *Wg = (double *)malloc(sizeof(double) * (size_t)(I * H));
     double *Wu = (double *)malloc(sizeof(double) * (size_t)(I * H));
     double *Wd = (double *)malloc(sizeof(double) * (size_t)(H * I));
-    if (Wg && Wu && Wd) {
+    double *X = (double *)malloc(sizeof(double) * (size_t)(n * H + 1));
+    double *A = (double *)malloc(sizeof(double) * (size_t)(n * I + 1));
+    if (Wg && Wu && Wd && X && A) {
         orc_mxfp4_dequant(I, H, wg, sg, Wg);
         orc_mxfp4_dequant(I, H, wu, su, Wu);
         orc_mxfp4_dequant(H, I, wd, sd, Wd);
-#pragma omp parallel for schedule(dynamic, 1)
-        for (int64_t r = 0; r < n; ++r) {
-            double *xr = (double *)malloc(sizeof(double) * (size_t)H);
-            double *a = (double *)malloc(sizeof(double) * (size_t)I);
-            if (xr && a) {
-                for (int64_t h = 0; h < H; ++h)
-                    xr[h] = orc_e4m3_to_f64(xq[r * H + h]) * (double)xs[r * HB + h / 128];
-                for (int64_t i = 0; i < I; ++i) {
-                    double g = 0.0, u = 0.0;
-                    for (int64_t h = 0; h < H; ++h) {
-                        g += xr[h] * Wg[i * H + h];
-                        u += xr[h] * Wu[i * H + h];
-                    }
-                    a[i] = silu(g) * u;
-                    if (a_out) a_out[r * I + i] = a[i];
-                }
-                for (int64_t b = 0; b < IB; ++b) {
-                    float amax = 0.0f;
-                    for (int64_t i = b * 128; i < (b + 1) * 128; ++i) {
-                        float v = fabsf((float)a[i]);
-                        if (v > amax) amax = v;
-                    }
-                    float s = amax > 0.0f ? amax / 448.0f : 1.0f;
-                    for (int64_t i = b * 128; i < (b + 1) * 128; ++i) {
-                        float q = (float)a[i] / s;
-                        a[i] = orc_e4m3_to_f64(orc_e4m3_rne_sat((double)q)) * (double)s;
-                    }
-                }
+        for (int64_t r = 0; r < n; ++r)
+            for (int64_t h = 0; h < H; ++h)
+                X[r * H + h] = orc_e4m3_to_f64(xq[r * H + h]) * (double)xs[r * HB + h / 128];
+        /* loops over the outputs, as in orc_expert_ffn; each sum in index order */
+#pragma omp parallel for schedule(dynamic, 4)
+        for (int64_t i = 0; i < I; ++i)
+            for (int64_t r = 0; r < n; ++r) {
+                const double *xr = X + r * H;
+                double g = 0.0, u = 0.0;
                 for (int64_t h = 0; h < H; ++h) {
-                    double acc = 0.0;
-                    for (int64_t i = 0; i < I; ++i) acc += a[i] * Wd[h * I + i];
-                    y[r * H + h] = acc;
+                    g += xr[h] * Wg[i * H + h];
+                    u += xr[h] * Wu[i * H + h];
                 }
+                A[r * I + i] = silu(g) * u;
             }
-            free(xr);
-            free(a);
-        }
+        if (a_out) memcpy(a_out, A, sizeof(double) * (size_t)(n * I));
+#pragma omp parallel for schedule(static)
+        for (int64_t r = 0; r < n; ++r) requant_row_e4m3(I, A + r * I);
+#pragma omp parallel for schedule(dynamic, 4)
+        for (int64_t h = 0; h < H; ++h)
+            for (int64_t r = 0; r < n; ++r) {
+                const double *a = A + r * I;
+                double acc = 0.0;
+                for (int64_t i = 0; i < I; ++i) acc += a[i] * Wd[h * I + i];
+                y[r * H + h] = acc;
+            }
     }
     free(Wg);
     free(Wu);
     free(Wd);
+    free(X);
+    free(A);
+}
+
+/* Rounds n doubles to bf16 (orc_bf16_rne) and widens them back: the stored
+ * value of an activation a bf16 layer keeps in bf16. */
+void orc_bf16_round_array(int64_t n, const double *in, double *out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t e = 0; e < n; ++e) out[e] = orc_bf16_to_f64(orc_bf16_rne(in[e]));
 }
 
 /* -------------------------------------------------------------- combine */

@@ -110,6 +110,29 @@ def rel_err_allow(got: np.ndarray, ref: np.ndarray, allow: np.ndarray) -> float:
     return float(np.max(e)) / max(rms, 1e-300)
 
 
+def cover_tokens(ids, T, E, n, seed):
+    """At least n seeded tokens, then one more for every expert with routed
+    rows that none of them reaches (the survey's token-subset rule), plus the
+    first and last token and tokens of the hottest and the coldest expert."""
+    rng = np.random.default_rng(seed)
+    toks = set(rng.choice(T, min(n, T), replace=False).tolist()) | {0, T - 1}
+    cnt = np.bincount(ids.ravel(), minlength=E)
+    seen = np.zeros(E, bool)
+    seen[np.unique(ids[sorted(toks)])] = True
+    for e in np.nonzero((cnt > 0) & ~seen)[0]:
+        if seen[e]:
+            continue
+        cand = np.nonzero((ids == e).any(1))[0]
+        t = int(cand[rng.integers(len(cand))])
+        toks.add(t)
+        seen[ids[t]] = True
+    hot, cold = int(np.argmax(cnt)), int(np.argmin(np.where(cnt > 0, cnt, 1 << 30)))
+    toks |= {int(np.nonzero((ids == hot).any(1))[0][0]), int(np.nonzero((ids == cold).any(1))[0][-1])}
+    toks = np.array(sorted(toks))
+    assert set(np.unique(ids[toks]).tolist()) == set(np.nonzero(cnt)[0].tolist())
+    return toks
+
+
 def host(t: torch.Tensor) -> np.ndarray:
     return to_np(t)
 

@@ -350,3 +350,53 @@ def test_mxfp4_cfg_and_table():
         assert t[e * 6:(e + 1) * 6] == [base[0] + e * I * H // 2, base[1] + e * I * H // 2, base[2] + e * I * H // 2,
                                         base[3] + e * I * H // 32, base[4] + e * I * H // 32,
                                         base[5] + e * I * H // 32]
+
+
+def test_combine_route_permute_layer_check_pointers():
+    """The shared expert's rows are required when has_shared; the vector
+    loads and stores of combine, route, permute and the layer need 16-byte
+    aligned rows (checked before any launch)."""
+    lib = _ffi.lib()
+    fake = ctypes.c_void_p(0x100000)
+    odd = ctypes.c_void_p(0x100008)
+    cs = m.make_cfg(T=16, H=64, E=8, k=2, I=64, has_shared=True, I_shared=64)
+    st = lib.moe_combine(ctypes.byref(cs), fake, fake, fake, None, fake, None)
+    assert st == m.MOE_ERR_INVALID_ARG and "y_shared" in m.moe_last_error()
+    c = m.make_cfg(T=16, H=64, E=8, k=2, I=64)
+    for args, name in (((odd, fake, fake, None, fake), "y_rows"), ((fake, fake, fake, odd, fake), "y_shared"),
+                       ((fake, fake, fake, None, odd), "out")):
+        st = lib.moe_combine(ctypes.byref(c), *args, None)
+        assert st == m.MOE_ERR_INVALID_ARG and name in m.moe_last_error() and "aligned" in m.moe_last_error()
+    st = lib.moe_route(ctypes.byref(c), odd, fake, None, None, None, fake, fake, fake, 1 << 20, None)
+    assert st == m.MOE_ERR_INVALID_ARG and "x" in m.moe_last_error() and "aligned" in m.moe_last_error()
+    st = lib.moe_route(ctypes.byref(c), fake, odd, None, None, None, fake, fake, fake, 1 << 20, None)
+    assert st == m.MOE_ERR_INVALID_ARG and "w_router" in m.moe_last_error()
+    st = lib.moe_permute(ctypes.byref(c), odd, None, fake, fake, fake, fake, fake, fake, None, fake, 1 << 20, None)
+    assert st == m.MOE_ERR_INVALID_ARG and "aligned" in m.moe_last_error()
+    st = lib.moe_permute(ctypes.byref(c), fake, None, fake, fake, fake, fake, fake, odd, None, fake, 1 << 20, None)
+    assert st == m.MOE_ERR_INVALID_ARG and "x_perm" in m.moe_last_error()
+    w = m.moe_weights(w_gate=0x100000, w_up=0x100000, w_down=0x100000)
+    st = lib.moe_layer(ctypes.byref(c), fake, None, ctypes.byref(w), odd, fake, fake, 1 << 40, None)
+    assert st == m.MOE_ERR_INVALID_ARG and "aligned" in m.moe_last_error()
+    st = lib.moe_layer(ctypes.byref(c), fake, None, ctypes.byref(w), fake, odd, fake, 1 << 40, None)
+    assert st == m.MOE_ERR_INVALID_ARG and "out" in m.moe_last_error()
+
+
+def test_layer_dispatches_a_large_x_into_x_perm():
+    """The layer's GEMM1 reads x through one buffer descriptor (32-bit byte
+    offsets): from 2 GiB of x on, the layer dispatches the rows into a tiled
+    x_perm instead (bf16), or a row-major one with its scales (e4m3 tokens of
+    low-precision experts), and its workspace grows by that much."""
+    def ws(T, **kw):
+        return m.moe_workspace_bytes(_dsv3(T=T, **kw), m.MOE_STAGE_LAYER)
+
+    below, above = (2 ** 31 - 1) // (7168 * 2), (2 ** 31) // (7168 * 2) + 1
+    tiled = m.moe_x_perm_bytes(_dsv3(T=above, m_tile=16, x_layout=m.MOE_LAYOUT_TILED))
+    assert tiled > above * 8 * 7168 * 2
+    per_token = ws(below) / below
+    assert ws(below) < below * per_token * 1.01
+    assert ws(above) >= tiled + above * per_token * 0.99
+    fp8 = dict(w_dtype=m.MOE_FP8_E4M3, y_dtype=m.MOE_BF16)
+    below8, above8 = (2 ** 31 - 1) // 7168, (2 ** 31) // 7168 + 1
+    rows = m.moe_max_rows(_dsv3(T=above8, m_tile=16))
+    assert ws(above8, **fp8) - ws(below8, **fp8) * above8 / below8 >= rows * 7168 * 0.99

@@ -207,3 +207,31 @@ def test_indexed_rows_equal_materialised_rows(H, I, counts, extra):
         torch.cuda.synchronize()
         outs.append(y)
     assert torch.equal(outs[0], outs[1])
+
+
+def test_grouped_ffn_skewed_groups_few_n_tiles():
+    """Few N tiles per M tile (H = 512: two GEMM2 tiles) and skewed groups of
+    256 j + 1 rows: the device tile count (42 work items of GEMM2) sits just
+    below the host-sized grid, which must still reach every item.  y starts as
+    NaN, so an item left out shows."""
+    d = dev()
+    H, I = 512, 256
+    counts = [256 * j + 1 for j in (0, 0, 0, 0, 0, 1, 6, 6)]
+    E = len(counts)
+    s, wg, wu, wd = _weights(E, H, I, "bf16", seed=5, device=d)
+    n = int(sum(counts))
+    x_rows = synth.normal(synth.stream_key(11, "rows"), (n, H), 1.0, d, torch.bfloat16)
+    offs = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32, device=d)
+    c = moe.make_cfg(T=1, H=H, E=E, k=1, I=I, act_dtype=moe.MOE_BF16, y_dtype=moe.MOE_F32)
+    y = torch.full((n, H), float("nan"), dtype=torch.float32, device=d)
+    ws = moe.workspace(c, moe.MOE_STAGE_FFN, d, n_rows_cap=n)
+    moe.moe_grouped_ffn(c, n, x_rows, None, offs, moe.weights(wg, wu, wd), None, y, None, ws)
+    torch.cuda.synchronize()
+    yh = f64(y)
+    assert not np.isnan(yh).any()
+    xh = to_np(x_rows)
+    oc = np.concatenate([[0], np.cumsum(counts)])
+    for e in range(E):
+        sl = slice(oc[e], oc[e + 1])
+        ref = oracle.expert_ffn(xh[sl], to_np(wg[e]), to_np(wu[e]), to_np(wd[e]), h_bf16=True)
+        assert rel_err(yh[sl], ref) <= 1e-2, e

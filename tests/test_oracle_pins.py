@@ -77,6 +77,21 @@ def test_bf16_rounding_golden_and_torch():
     assert np.array_equal(oracle.bf16_to_f64(bits), ref)
 
 
+def test_bf16_round_array_matches_torch_casts():
+    """bf16_round (the stored value of a bf16 activation) against torch's own
+    fp64 -> fp32 -> bf16 casts, on values of every magnitude and on the golden
+    halfway cases."""
+    rng = np.random.default_rng(3)
+    v = rng.normal(0, 1, 20000) * np.exp(rng.normal(0, 8, 20000))
+    g = json.load(open(os.path.join(GOLDEN, "bf16_rne.json")))
+    half = np.array([np.array([int(src, 16)], dtype=np.uint32).view(np.float32)[0] for src, _, _ in g["cases"]],
+                    dtype=np.float64)
+    v = np.concatenate([v, half, -half, [0.0, -0.0]])
+    ref = torch.tensor(v, dtype=torch.float64).to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+    got = oracle.bf16_round(v.reshape(2, -1)).reshape(-1)
+    assert np.array_equal(got, ref)
+
+
 # ------------------------------------------------------------------ router
 
 def _bf16(rng, shape, std=1.0):
