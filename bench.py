@@ -75,6 +75,10 @@ def parse():
                         "passes of the stage calls on the workload's routing, with the expert weights drawn by "
                         "torch.randn (their values do not change which bytes the kernels move; a few hundred "
                         "dispatches in all); prints no JSON line")
+    p.add_argument("--no-clock", action="store_true", help="skip sampling the GPU clock under load")
+    p.add_argument("--pmc-summary", nargs="+", metavar="DB",
+                   help="no GPU: print, per kernel, the per-dispatch average of every counter in these rocprofv3 "
+                        "--pmc result databases (a markdown table), and exit")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                    help="no GPU: read two rocprofv3 --pmc result databases of a --traffic-run (FETCH_SIZE, then "
                         "WRITE_SIZE), write the grouped FFN's HBM bytes per launch to the traffic file, exit")
@@ -144,6 +148,33 @@ def traffic_from(fetch_db, write_db, workload):
     print(json.dumps(res))
 
 
+def pmc_summary(dbs):
+    """Per kernel and counter: the value summed over a dispatch's instances,
+    averaged over the kernel's dispatches, from rocprofv3 --pmc databases."""
+    import sqlite3
+    rows = {}
+    for db in dbs:
+        con = sqlite3.connect(db)
+        per = {}
+        for name, cname, val, disp in con.execute(
+                "select kernel_name, counter_name, value, dispatch_id from counters_collection"):
+            per[(name, cname, disp)] = per.get((name, cname, disp), 0.0) + float(val)
+        con.close()
+        for (name, cname, disp), v in per.items():
+            rows.setdefault((name, cname), []).append(v)
+    counters = sorted({c for _, c in rows})
+    kernels = sorted({k for k, _ in rows})
+    print("| kernel | dispatches | " + " | ".join(counters) + " |")
+    print("|---|---:|" + "---:|" * len(counters))
+    for k in kernels:
+        n = max(len(rows.get((k, c), [])) for c in counters)
+        vals = []
+        for c in counters:
+            v = rows.get((k, c))
+            vals.append(f"{sum(v) / len(v):.6g}" if v else "")
+        print(f"| {k.split('(')[0]} | {n} | " + " | ".join(vals) + " |")
+
+
 def ffn_source_hash() -> str:
     h = hashlib.sha256()
     for f in FFN_SOURCES:
@@ -155,6 +186,9 @@ def main():
     a = parse()
     if a.traffic_from:
         traffic_from(*a.traffic_from, a.workload)
+        return
+    if a.pmc_summary:
+        pmc_summary(a.pmc_summary)
         return
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
@@ -228,13 +262,28 @@ def sclk_under_load(step, ms_step, seconds=1.5):
                     h = c
     except Exception as e:  # no amdsmi or no device access: no figure
         return {"error": f"amdsmi: {e}"}
-    samples = []
+    samples = {"average_gfxclk": [], "current_gfxclk_max": [], "clock_info": []}
     stop = threading.Event()
+
+    def num(v):
+        return float(v) if isinstance(v, (int, float)) and 0 < float(v) < 10000 else None
 
     def poll():
         while not stop.is_set():
             try:
-                samples.append(float(amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)["clk"]))
+                m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+                v = num(m.get("average_gfxclk_frequency"))
+                if v:
+                    samples["average_gfxclk"].append(v)
+                cur = [num(c) for c in (m.get("current_gfxclks") or []) if num(c)]
+                if cur:
+                    samples["current_gfxclk_max"].append(max(cur))
+            except Exception:
+                pass
+            try:
+                v = num(amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)["clk"])
+                if v:
+                    samples["clock_info"].append(v)
             except Exception:
                 pass
             time.sleep(0.01)
@@ -252,11 +301,14 @@ def sclk_under_load(step, ms_step, seconds=1.5):
         amdsmi.amdsmi_shut_down()
     except Exception:
         pass
-    if not samples:
-        return {"error": "no samples"}
-    v = sorted(samples)
-    return {"median_mhz": v[len(v) // 2], "min_mhz": v[0], "max_mhz": v[-1], "samples": len(v),
-            "steps": n, "how": "amdsmi GFX clock polled every 10 ms while the steps ran back to back"}
+    out = {"steps": n, "how": "amdsmi polled every 10 ms while the steps ran back to back: gpu_metrics "
+                              "average_gfxclk_frequency, the largest of its per-XCD current_gfxclks, and "
+                              "clock_info's GFX clock; median (min, max) of the samples in MHz"}
+    for k, v in samples.items():
+        if v:
+            v = sorted(v)
+            out[k] = {"median": v[len(v) // 2], "min": v[0], "max": v[-1], "n": len(v)}
+    return out
 
 
 def bench_bf16_layer(a, s, dev, extra=False):
@@ -489,13 +541,13 @@ def bench_bf16_layer(a, s, dev, extra=False):
         "hbm_frac": round(ffn_gbs / PEAK_HBM_GBS, 4)})
 
     cpu = None if (a.no_cpu_baseline or extra) else cpu_baseline(s, x, w_r, a.cpu_seconds)
-    sclk = None if extra else sclk_under_load(step, ms_step)
+    sclk = None if (extra or a.no_clock) else sclk_under_load(step, ms_step)
 
     res = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": a.workload, "T": T, "H": H, "E": E, "k": k, "I": I, "shared_experts": int(s.shared),
+        "config": {"workload": s.name, "T": T, "H": H, "E": E, "k": k, "I": I, "shared_experts": int(s.shared),
                    "I_shared": I_sh, "router": s.score, "n_groups": s.n_groups, "topk_groups": s.topk_groups,
                    "routed_scale": s.routed_scale, "out_dtype": "bf16", "expert_out_dtype": "bf16",
                    "weight_layout": "row-major" if a.rowmajor_weights else "tiled",
@@ -575,7 +627,7 @@ def bench_fp8_ffn(a, s, dev):
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp8_e4m3 x mxfp4" if f4 else "fp8_e4m3", "data": "synthetic",
-        "config": {"workload": a.workload, "rows": s.T, "H": s.H, "E_local": s.E, "I": s.I,
+        "config": {"workload": s.name, "rows": s.T, "H": s.H, "E_local": s.E, "I": s.I,
                    "counts": [int(v) for v in counts],
                    "scales": "1x128 rows, E8M0 per 32 weights (MXFP4)" if f4 else "1x128 rows, 128x128 weights",
                    "out_dtype": "bf16"},
@@ -746,7 +798,7 @@ def bench_fp8_layer(a, s, dev):
         "warmup": a.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": ("mxfp4" if f4 else "fp8_e4m3") + " experts, bf16 activations",
         "data": "synthetic",
-        "config": {"workload": a.workload, "T": T, "H": H, "E": E, "k": k, "I": I, "shared_experts": int(s.shared),
+        "config": {"workload": s.name, "T": T, "H": H, "E": E, "k": k, "I": I, "shared_experts": int(s.shared),
                    "I_shared": I_sh,
                    "experts": "MXFP4 (E2M1, E8M0 per 32), e4m3 rows" if f4 else "e4m3, 128x128 block scales",
                    "activations": "bf16, quantised per token (1x128)", "out_dtype": "bf16"},
