@@ -158,7 +158,7 @@ hipError_t launch_offsets_one_group(int32_t* offsets, int n, hipStream_t s);
 // Grouped FFN building blocks (gemm_bf16.hip, gemm_fp8.hip, gemm_f32.hip).
 // Tile heights (rows) and the h / output columns one tile covers in GEMM1 /
 // GEMM2; fp8 tiles cover the bf16 tiles' columns.
-constexpr int kFfnBmBf16 = 256, kFfnN1Bf16 = 128, kFfnN2Bf16 = 256;
+constexpr int kFfnBmBf16 = 288, kFfnN1Bf16 = 128, kFfnN2Bf16 = 256;
 constexpr int kFfnBmFp8 = 224, kFfnBmFp8Small = 128;
 constexpr int kFfnBmF32 = 64, kFfnN1F32 = 64, kFfnN2F32 = 64;
 
@@ -207,10 +207,10 @@ struct FfnOperands {
 hipError_t launch_gemm_bf16(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_cap, const FfnOperands& op,
                             const int32_t* offsets, const moe_weights& w, const WTab& wt, const FfnWork& wk,
                             void* h_tiles, hipStream_t s);
-// Bytes of one h tile slot (256 rows) of the bf16 path.
+// Bytes of one h tile slot (kFfnBmBf16 rows) of the bf16 path.
 inline size_t h_slot_bytes(const moe_cfg& c) {
     const int imax = c.has_shared && c.I_shared > c.I ? c.I_shared : c.I;
-    return (size_t)256 * ((imax + 31) / 32) * 32 * 2;
+    return (size_t)kFfnBmBf16 * ((imax + 31) / 32) * 32 * 2;
 }
 struct TiledSizes {
     size_t w13, w2, sh13, sh2;  // bytes of the tiled routed and shared matrices

@@ -4,35 +4,40 @@
 //
 // Work list.  ffn_build_tiles turns the expert offsets into a device-side list
 // of M tiles {group, row_begin, row_end}: an expert with n rows gets
-// ceil(n / 256) tiles of equal height (rounded up to 32 rows), so a skewed
+// ceil(n / 288) tiles of equal height (rounded up to 32 rows), so a skewed
 // expert spreads over many workgroups and a cold one costs one short tile.  The
 // shared expert is one more group over all T tokens.  Nothing returns to the
 // host: the grid is sized from the host-known bound and blocks past the
 // device-side count exit at once.
 //
-// Tile.  256 rows x 256 weight rows, 4 waves.  Each wave owns all rows of the
-// tile and 64 weight rows (two 32-column MFMA blocks, v_mfma_f32_32x32x16_bf16),
-// so a short tile drops whole 32-row blocks and the four SIMDs stay equally
-// loaded; the tile body is specialised on the number of 32-row blocks.
-//   GEMM1: the 64 weight rows of wave w are 32 gate rows and the 32 up rows of
-//          the same h columns: h = silu(g) * u is formed in registers.
+// Tile.  Up to 288 rows x 256 weight rows, 8 waves, two per SIMD.  Each wave
+// owns all rows of the tile and one 32-column MFMA block of weight rows
+// (v_mfma_f32_32x32x16_bf16), so an expert of up to 288 rows -- nearly every
+// expert of a DeepSeek-V3-sized layer at 8 192 tokens -- streams each weight
+// panel in one tile, a short tile drops whole 32-row blocks, and the SIMDs stay
+// equally loaded; the tile body is specialised on the number of 32-row blocks.
+// The second wave on a SIMD issues its MFMAs while the first waits on LDS or
+// the stage barrier.
+//   GEMM1: wave w holds the gate (w < 4) or the up (w >= 4) rows of h columns
+//          32 (w % 4) .. +31 of the tile; the pair meets through LDS at the
+//          end and the gate wave forms h = silu(g) * u.
 //   GEMM2: 256 output columns of y = h . w_down^T, fp32 or bf16.
-// Operand paths.  The rows (A) are shared by the four waves and go through
+// Operand paths.  The rows (A) are shared by the eight waves and go through
 // LDS; the weight rows of a wave are read by that wave alone, so they skip LDS
 // and stream from HBM straight into a ring of register sets, one per stage, in
 // MFMA fragment order (the tiled weight layout below makes each wave's stage
-// one contiguous 4 KiB read).  LDS then carries 80 KiB per stage (16 KiB of DMA
-// writes, 64 KiB of fragment reads) instead of 112 KiB.
+// one contiguous 2 KiB read).
 // Pipeline.  K advances in 32-wide stages; NS stages are in flight: NS LDS
-// buffers of 16 KiB for A, filled by buffer_load ... lds (no staging
-// registers), and NS register sets of 16 VGPRs for B.  A stage's loads are
+// buffers of 19 KiB for A, filled by buffer_load ... lds (no staging
+// registers), and NS register sets of 8 VGPRs for B.  A stage's loads are
 // issued NS - 1 stages ahead; a chunk outside the tile (rows past the expert's
 // end, columns past N, the K tail, stages past the end) carries an offset
 // beyond its buffer descriptor and loads as zero with no memory traffic.  Each
-// stage has two 16-wide k steps with an A register set each: the fragments of
-// the next k step are read while the MFMAs of this one run.  Between a stage's
-// two k steps: wait for the next stage's A, one s_barrier, and reissue the
-// drained A buffer; after a stage's last MFMA its B register set is reloaded.
+// stage has two 16-wide k steps; the A fragments of a row block are re-read
+// for the next k step right after its MFMA has issued, so each read has a
+// whole k step (of both waves on the SIMD) to land.  Between a stage's two k
+// steps: wait for the next stage's A, one s_barrier, and reissue the drained A
+// buffer; after a stage's last MFMA its B register set is reloaded.
 // LDS chunks of 16 B are XOR-swizzled by row, physical chunk = logical ^
 // ((row >> 1) & 3) ^ ((row >> 3) & 1): a fragment read of 16 consecutive rows
 // (one pass of ds_read_b128 through the 64 banks of gfx950's LDS) touches 16
@@ -46,29 +51,37 @@
 namespace moe {
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 32, NTH = 256;
+constexpr int BM = kFfnBmBf16, BN = 256, BK = 32, NWAVES = 8, NTH = NWAVES * 64;
 #ifndef MOE_GEMM1_STAGES
-#define MOE_GEMM1_STAGES 8
+#define MOE_GEMM1_STAGES 6
 #endif
 #ifndef MOE_GEMM2_STAGES
 #define MOE_GEMM2_STAGES 4
 #endif
 // Stages in flight (A: LDS buffers, B: register sets), per GEMM: the longer K
-// of GEMM1 takes a deeper ring, GEMM2's 64 stages per tile a shorter fill
-// (both measured at c3).
+// of GEMM1 takes a deeper ring, GEMM2's 64 stages per tile a shorter fill.
 template <int MODE>
 constexpr int kStages = MODE == 0 ? MOE_GEMM1_STAGES : MOE_GEMM2_STAGES;
-static_assert(kStages<0> >= 3 && kStages<0> <= 8 && kStages<1> >= 3 && kStages<1> <= 8,
-              "the vmcnt arithmetic below holds for 3 to 8 stages");
-constexpr int kSlots = BM * 4;           // 16-byte slots of the A operand in one stage
-constexpr int kLoadsA = 4, kLoadsB = 4;  // vector-memory instructions per wave per stage
+static_assert(kStages<0> >= 3 && kStages<0> <= 7 && kStages<1> >= 3 && kStages<1> <= 7,
+              "ring depth: LDS holds up to seven A stages");
+constexpr int kRowBlocks = BM / 32;      // 32-row MFMA blocks of a full tile
+constexpr int kBlocks16 = BM / 16;       // 16-row DMA blocks of one A stage
+static_assert(BM % 32 == 0 && kRowBlocks <= 9 && kBlocks16 <= 3 * NWAVES, "tile height");
+// A stage buffer: the tile's rows, 64 B each, then one spare 1 KiB block that
+// the surplus DMA instructions of a stage write (with no memory traffic), so
+// that every wave issues the same number of loads and waits on the same counts.
+constexpr int kSlotsA = kBlocks16 * 64;
+constexpr int kSlots = kSlotsA + 64;
+// vector-memory instructions per wave per stage: three A blocks (blocks w,
+// w + 8 and, for w < kBlocks16 - 16, w + 16) and two B fragments
+constexpr int kLoadsA = 3, kLoadsB = 2;
 constexpr uint32_t kOOB = 0x80000000u;   // past every descriptor (all are < 2 GiB): the load returns zero
 
 typedef __attribute__((address_space(3))) void* lds_t;
 
-// The A stage buffers, 256 rows x 64 B each.  They are distinct objects so
-// that the compiler can tell which buffer an in-flight LDS DMA writes and
-// never waits for a load into another buffer.
+// The A stage buffers.  They are distinct objects so that the compiler can
+// tell which buffer an in-flight LDS DMA writes and never waits for a load
+// into another buffer.
 __shared__ i32x4 ring0[kSlots];
 __shared__ i32x4 ring1[kSlots];
 __shared__ i32x4 ring2[kSlots];
@@ -76,19 +89,17 @@ __shared__ i32x4 ring3[kSlots];
 __shared__ i32x4 ring4[kSlots];
 __shared__ i32x4 ring5[kSlots];
 __shared__ i32x4 ring6[kSlots];
-__shared__ i32x4 ring7[kSlots];
 
 template <int BUF>
 __device__ __forceinline__ i32x4* ring() {
-    static_assert(BUF < 8, "ring buffer index");
+    static_assert(BUF < 7, "ring buffer index");
     if constexpr (BUF == 0) return ring0;
     else if constexpr (BUF == 1) return ring1;
     else if constexpr (BUF == 2) return ring2;
     else if constexpr (BUF == 3) return ring3;
     else if constexpr (BUF == 4) return ring4;
     else if constexpr (BUF == 5) return ring5;
-    else if constexpr (BUF == 6) return ring6;
-    else return ring7;
+    else return ring6;
 }
 
 template <int I, int N, typename F>
@@ -133,7 +144,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 //    group q, stage ks at byte (q * KS + ks) * 4096; inside, four 1 KiB MFMA
 //    B fragments j = 2 * c + kk (c: 32-row half, kk: 16-wide k step), lane l's
 //    16 bytes at l * 16 = row 32 c + l % 32, k = 32 ks + 16 kk + 8 (l / 32)
-//    .. + 7.  Zero padded in rows and k.
+//    .. + 7.  Zero padded in rows and k.  A wave reads half c of a group: its
+//    stage is the 2 KiB at byte (q * KS + ks) * 4096 + c * 2048.
 struct GemmArgs {
     const uint16_t* a_routed;  // GEMM1: x rows (row-major or tiled); GEMM2: h tile slots (tiled)
     const uint16_t* a_shared;  // GEMM1: shared-expert tokens (row-major or tiled); GEMM2: h tile slots
@@ -162,20 +174,27 @@ struct GemmArgs {
 };
 
 // Per-tile load state.  A: the buffer descriptor, the byte offsets of this
-// lane's four 16-byte chunks in stage 0 and how far a stage moves them (64 B
-// row-major, 1 KiB tiled).  B: a descriptor per 32-row half of the wave's
-// weight rows, this lane's offset in stage 0, and the per-stage and per-k-step
-// moves (tiled: 4 KiB and 1 KiB; row-major: 64 B and 32 B).
+// lane's three 16-byte chunks in stage 0 and how far a stage moves them (64 B
+// row-major, 1 KiB tiled).  B: the descriptor of the wave's 32 weight rows,
+// this lane's offset in stage 0, and the per-stage and per-k-step moves
+// (tiled: 4 KiB and 1 KiB; row-major: 64 B and 32 B).
 struct Dma {
-    __amdgpu_buffer_rsrc_t ra, rb[2];
-    uint32_t va[4];
-    uint32_t vb[2];
+    __amdgpu_buffer_rsrc_t ra, rb;
+    uint32_t va[kLoadsA];
+    uint32_t vb;
     uint32_t sa, sb, kb;    // bytes per stage (A, B), bytes per k step (B)
     uint32_t kvalid_last;   // valid K columns in the last stage (multiple of 8)
     int nsteps;             // real stages
     int klim;               // B: this lane's loads of k step kk in stage t are real while 32 t + 16 kk < klim
     bool a_rm;              // row-major A: the K tail must be masked
 };
+
+// The 16-row block of an A stage that instruction i of wave w fills: blocks
+// w and w + 8, then w + 16 while it exists; the rest write the spare block.
+__device__ __forceinline__ int a_block(int wave, int i) {
+    const int b = wave + NWAVES * i;
+    return b < kBlocks16 ? b : kBlocks16;
+}
 
 // A load of stage t into buffer BUF, one instruction (i of kLoadsA): row-major
 // chunks of the K tail load zero (tiled operands are zero padded).
@@ -186,9 +205,9 @@ __device__ __forceinline__ void dma_a1(const Dma& d, int t, int lane, int i) {
     const bool real = t < d.nsteps;
     const bool last = t == d.nsteps - 1;
     const uint32_t logical8 = (uint32_t)(((lane & 3) ^ swz_of_row(lane >> 2)) * 8);
-    const bool a_ok = real & (!d.a_rm | !last | (logical8 < d.kvalid_last));  // no short-circuit branch
+    const bool a_ok = real & (!d.a_rm | !last | (logical8 < d.kvalid_last)) & (d.va[i] != kOOB);
     const uint32_t off = a_ok ? d.va[i] + (uint32_t)t * d.sa : kOOB;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ra, (lds_t)(buf + (wave * 4 + i) * 64), 16, off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ra, (lds_t)(buf + a_block(wave, i) * 64), 16, off, 0, 0, 0);
 }
 
 // All A loads of stage t into buffer BUF.
@@ -198,31 +217,28 @@ __device__ __forceinline__ void dma_a(const Dma& d, int t, int lane) {
     for (int i = 0; i < kLoadsA; ++i) dma_a1<BUF>(d, t, lane, i);
 }
 
-// B fragments of stage t: q[2 c + kk] = 32-row half c, k step kk.  A load is
-// real while kk * 16 is below the lane's limit for the stage (no limit for
-// the zero-padded tiled weights, the K tail for row-major ones, none at all
-// past the last stage); the rest carry kOOB.  Selects only: a branch here
+// B fragments of stage t: q[kk] = k step kk of the wave's 32 weight rows.  A
+// load is real while kk * 16 is below the lane's limit for the stage (no limit
+// for the zero-padded tiled weights, the K tail for row-major ones, none at
+// all past the last stage); the rest carry kOOB.  Selects only: a branch here
 // would cost the wait counters their precision.
-__device__ __forceinline__ void load_b(const Dma& d, int t, i32x4 (&q)[4]) {
+__device__ __forceinline__ void load_b(const Dma& d, int t, i32x4 (&q)[2]) {
     const int lim = t < d.nsteps ? d.klim - t * BK : -1;
     const uint32_t base = (uint32_t)t * d.sb;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int c = j >> 1, kk = j & 1;
-        const uint32_t off = kk * 16 < lim ? d.vb[c] + base + (uint32_t)kk * d.kb : kOOB;
-        q[j] = __builtin_amdgcn_raw_buffer_load_b128(d.rb[c], off, 0, 0);
+    for (int kk = 0; kk < 2; ++kk) {
+        const uint32_t off = kk * 16 < lim ? d.vb + base + (uint32_t)kk * d.kb : kOOB;
+        q[kk] = __builtin_amdgcn_raw_buffer_load_b128(d.rb, off, 0, 0);
     }
 }
 
-// A fragments of one 16-wide k step (KK) of a stage: rows r*32 + lane%32 at
-// logical chunk 2*KK + lane/32.
-template <int NRB, int BUF, int KK>
-__device__ __forceinline__ void read_a(int lane, i32x4 (&a)[NRB]) {
+// One fragment read of A: row block r of k step KK in buffer BUF (rows
+// r * 32 + lane % 32 at logical chunk 2 * KK + lane / 32).
+template <int BUF, int KK>
+__device__ __forceinline__ i32x4 read_a1(int lane, int r) {
     const i32x4* buf = ring<BUF>();
     const int l32 = lane & 31, half = lane >> 5;
-    const int phys = (KK * 2 + half) ^ swz_of_row(l32);
-#pragma unroll
-    for (int r = 0; r < NRB; ++r) a[r] = buf[(r * 32 + l32) * 4 + phys];
+    return buf[(r * 32 + l32) * 4 + ((KK * 2 + half) ^ swz_of_row(l32))];
 }
 
 // vmcnt after which this wave's A loads of the next stage have landed: the
@@ -233,12 +249,12 @@ constexpr int kWaitNextA = kLoadsB + (kLoadsA + kLoadsB) * (NS - 2);
 // ... and, in the prologue, stage 0's A loads: every later load of NS stages.
 template <int NS>
 constexpr int kWaitFirstA = kLoadsB + (kLoadsA + kLoadsB) * (NS - 1);
-static_assert(kWaitFirstA<8> < 64, "vmcnt is 6 bits");
+static_assert(kWaitFirstA<kStages<0>> < 64 && kWaitFirstA<kStages<1>> < 64, "vmcnt is 6 bits");
 
 // MFMA row blocks of k step 1 issued before the stage's barrier (they read
-// registers only), so the MFMA pipe stays busy while the waves meet.
+// registers only), so the MFMA pipe has work while the waves meet.
 #ifndef MOE_GEMM1_PRE_ROWS
-#define MOE_GEMM1_PRE_ROWS 1
+#define MOE_GEMM1_PRE_ROWS 2
 #endif
 #ifndef MOE_GEMM2_PRE_ROWS
 #define MOE_GEMM2_PRE_ROWS 2
@@ -246,75 +262,68 @@ static_assert(kWaitFirstA<8> < 64, "vmcnt is 6 bits");
 template <int MODE>
 constexpr int kPreBarrierRows = MODE == 0 ? MOE_GEMM1_PRE_ROWS : MOE_GEMM2_PRE_ROWS;
 
-// One fragment read of A: row block r of k step KK in buffer BUF.
-template <int BUF, int KK>
-__device__ __forceinline__ i32x4 read_a1(int lane, int r) {
-    const i32x4* buf = ring<BUF>();
-    const int l32 = lane & 31, half = lane >> 5;
-    return buf[(r * 32 + l32) * 4 + ((KK * 2 + half) ^ swz_of_row(l32))];
-}
-
-__device__ __forceinline__ void mma1(const i32x4& a, const i32x4& b0i, const i32x4& b1i, f32x16& c0, f32x16& c1) {
-    const bf16x8 av = __builtin_bit_cast(bf16x8, a);
-    c0 = mfma32x32x16(av, __builtin_bit_cast(bf16x8, b0i), c0);
-    c1 = mfma32x32x16(av, __builtin_bit_cast(bf16x8, b1i), c1);
+__device__ __forceinline__ void mma1(const i32x4& a, const i32x4& b, f32x16& c) {
+    c = mfma32x32x16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c);
 }
 
 // One pipeline stage (two 16-wide k steps) on stage s, A in buffer BUF, B in
-// register set BUF.  A set kk holds k step kk; entering, set 0 holds stage s,
-// k step 0.  Memory instructions are spread between the MFMAs (one pair of
-// MFMAs, then a fragment read or an A load), and the first row blocks of k
-// step 1 go ahead of the barrier, so the MFMA pipe is never left without
-// work behind a cluster of issues.
+// register set BUF.  Entering, fa[r] holds row block r of stage s, k step 0.
+// Each MFMA is followed by the read that refills its A register for the next
+// k step (k step 1 of this stage, then k step 0 of stage s + 1 once the
+// barrier has made that buffer safe), so every read has a whole k step to
+// land; the stage's A DMA for stage s + NS is spread over the second k step.
 template <int MODE, int NRB, int BUF>
-__device__ __forceinline__ void stage(const Dma& d, int s, int lane, i32x4 (&fa)[2][NRB],
-                                      i32x4 (&bq)[kStages<MODE>][4], f32x16 (&acc0)[8], f32x16 (&acc1)[8]) {
+__device__ __forceinline__ void stage(const Dma& d, int s, int lane, i32x4 (&fa)[NRB],
+                                      i32x4 (&bq)[kStages<MODE>][2], f32x16 (&acc)[kRowBlocks]) {
     constexpr int NS = kStages<MODE>;
+    constexpr int NB = (BUF + 1) % NS;
     constexpr int PRE = NRB < kPreBarrierRows<MODE> ? NRB : kPreBarrierRows<MODE>;
-    // k step 0 on set 0, reading k step 1 of this stage into set 1
+    // k step 0, refilling each A register with k step 1 of this stage
 #pragma unroll
     for (int r = 0; r < NRB; ++r) {
-        mma1(fa[0][r], bq[BUF][0], bq[BUF][2], acc0[r], acc1[r]);
+        mma1(fa[r], bq[BUF][0], acc[r]);
         __builtin_amdgcn_sched_barrier(0);
-        fa[1][r] = read_a1<BUF, 1>(lane, r);
+        fa[r] = read_a1<BUF, 1>(lane, r);
         __builtin_amdgcn_sched_barrier(0);
     }
     // k step 1, first row blocks: registers only
 #pragma unroll
     for (int r = 0; r < PRE; ++r) {
-        mma1(fa[1][r], bq[BUF][1], bq[BUF][3], acc0[r], acc1[r]);
+        mma1(fa[r], bq[BUF][1], acc[r]);
         __builtin_amdgcn_sched_barrier(0);
     }
     wait_lgkm0();             // every read of buffer BUF by this wave has returned
     wait_vm<kWaitNextA<NS>>();    // this wave's A loads of stage s+1 have landed
     barrier_lds();            // ... everybody's have, and everybody is done with buffer BUF
-    // the rest of k step 1, with the A loads NS ahead into buffer BUF and the
-    // reads of stage s+1's k step 0 in between
-    int issued_dma = 0, issued_rd = 0;
+#pragma unroll
+    for (int r = 0; r < PRE; ++r) fa[r] = read_a1<NB, 0>(lane, r);
+    __builtin_amdgcn_sched_barrier(0);
+    // the rest of k step 1, each MFMA followed by the read of stage s+1's k
+    // step 0 into its register, with the A loads NS ahead into buffer BUF
+    int issued_dma = 0;
 #pragma unroll
     for (int r = PRE; r < NRB; ++r) {
-        mma1(fa[1][r], bq[BUF][1], bq[BUF][3], acc0[r], acc1[r]);
+        mma1(fa[r], bq[BUF][1], acc[r]);
+        __builtin_amdgcn_sched_barrier(0);
+        fa[r] = read_a1<NB, 0>(lane, r);
         __builtin_amdgcn_sched_barrier(0);
         if (issued_dma < kLoadsA) {
             dma_a1<BUF>(d, s + NS, lane, issued_dma);
             ++issued_dma;
             __builtin_amdgcn_sched_barrier(0);
         }
-        if (issued_rd < NRB) {
-            fa[0][issued_rd] = read_a1<(BUF + 1) % NS, 0>(lane, issued_rd);
-            ++issued_rd;
-            __builtin_amdgcn_sched_barrier(0);
-        }
     }
 #pragma unroll
     for (int i = 0; i < kLoadsA; ++i)
         if (i >= issued_dma) dma_a1<BUF>(d, s + NS, lane, i);
-#pragma unroll
-    for (int r = 0; r < NRB; ++r)
-        if (r >= issued_rd) fa[0][r] = read_a1<(BUF + 1) % NS, 0>(lane, r);
     __builtin_amdgcn_sched_barrier(0);
     load_b(d, s + NS, bq[BUF]);  // register set BUF is free once its MFMAs have issued
     __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int NRB, int J>
+__device__ __forceinline__ float* xchg_slot(int g) {
+    return reinterpret_cast<float*>(ring<J>()) + g * 1024;
 }
 
 template <int MODE, int NRB>
@@ -324,6 +333,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, int mt, int g, int r
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l32 = lane & 31;
     const int KS = (K + BK - 1) / BK;
+    const int wg = wave & 3, wc = wave >> 2;  // the wave's 64-row weight group of the tile and its 32-row half
 
     Dma d;
     d.nsteps = KS;
@@ -333,7 +343,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, int mt, int g, int r
     d.a_rm = !a_tiled;
     if (MODE == 1) {
         // GEMM2 reads the h tile slot of this M tile, written tiled by GEMM1
-        const uint16_t* A = (shared ? p.a_shared : p.a_routed) + (size_t)mt * 16 * p.h_slot_ks * 512;
+        const uint16_t* A = (shared ? p.a_shared : p.a_routed) + (size_t)mt * kBlocks16 * p.h_slot_ks * 512;
         d.ra = make_rsrc(A, (uint32_t)((NRB * 2) * KS * 1024));
     } else if (a_tiled) {
         // row0 is a multiple of 16 here (the caller aligns expert segments)
@@ -350,11 +360,13 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, int mt, int g, int r
     d.sa = a_tiled ? 1024u : (uint32_t)(BK * 2);
 #pragma unroll
     for (int i = 0; i < kLoadsA; ++i) {
-        const int blk = wave * 4 + i;           // 16-row block of the tile this instruction fills
+        const int blk = a_block(wave, i);       // 16-row block of the tile this instruction fills
         const int row = blk * 16 + (lane >> 2);
         const uint32_t logical8 = (uint32_t)(((lane & 3) ^ swz_of_row(row)) * 8);
-        if (a_tiled) {
-            d.va[i] = blk * 16 < NRB * 32 ? ((uint32_t)blk * (uint32_t)KS * 1024u + (uint32_t)lane * 16u) : kOOB;
+        if (blk >= kBlocks16 || blk * 16 >= NRB * 32) {
+            d.va[i] = kOOB;                     // the spare block, or rows this tile does not have
+        } else if (a_tiled) {
+            d.va[i] = (uint32_t)blk * (uint32_t)KS * 1024u + (uint32_t)lane * 16u;
         } else if (a_indexed) {
             const int src = row < M ? p.a_row_src[row0 + row] : -1;
             d.va[i] = src >= 0 ? ((uint32_t)(src / p.a_row_k) * (uint32_t)K + logical8) * 2u : kOOB;
@@ -362,8 +374,9 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, int mt, int g, int r
             d.va[i] = row < M ? ((uint32_t)row * (uint32_t)K + logical8) * 2u : kOOB;
         }
     }
-    // ---- B: the 64 weight rows of this wave (GEMM1: 32 gate and 32 up rows of
-    // h columns n0 + 32 w .. +31; GEMM2: rows n0 + 64 w .. +63)
+    // ---- B: the 32 weight rows of this wave (GEMM1: the gate (wc = 0) or up
+    // (wc = 1) rows of h columns n0 + 32 wg .. +31; GEMM2: rows n0 + 64 wg +
+    // 32 wc .. +31)
     if (p.w_tiled) {
         d.klim = 1 << 30;  // zero padded
         // fragment-order groups of 64 rows: GEMM1 2 * roundup(N, 128) rows, GEMM2 N rows
@@ -372,47 +385,38 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, int mt, int g, int r
         const uint16_t* W = p.wt.tab ? static_cast<const uint16_t*>(wtab_ptr(p.wt, *p.wt.layer, g, p.slot0))
                             : shared ? p.w0_shared : p.w0_routed + (size_t)g * mat;
         const int q0 = nt * 4;                          // first group of the N tile
-        d.rb[0] = make_rsrc(W + (size_t)q0 * KS * 2048, (uint32_t)((groups - q0) * KS * 4096));
-        d.rb[1] = d.rb[0];
-        const uint32_t base = (uint32_t)wave * (uint32_t)KS * 4096u + (uint32_t)lane * 16u;
-        d.vb[0] = base;
-        d.vb[1] = base + 2048u;
+        d.rb = make_rsrc(W + (size_t)q0 * KS * 2048, (uint32_t)((groups - q0) * KS * 4096));
+        d.vb = (uint32_t)wg * (uint32_t)KS * 4096u + (uint32_t)wc * 2048u + (uint32_t)lane * 16u;
         d.sb = 4096u;
         d.kb = 1024u;
     } else {
         const int ncols = MODE == 0 ? min(BN / 2, N - n0) : min(BN, N - n0);
         const size_t wmat = (size_t)K * (size_t)N;
-        const uint16_t *W0, *W1;
+        const uint16_t* W;
         if (p.wt.tab) {
             const int lay = *p.wt.layer;
-            W0 = static_cast<const uint16_t*>(wtab_ptr(p.wt, lay, g, p.slot0)) + (size_t)n0 * K;
-            W1 = MODE == 0 ? static_cast<const uint16_t*>(wtab_ptr(p.wt, lay, g, p.slot1)) + (size_t)n0 * K : W0;
+            W = static_cast<const uint16_t*>(wtab_ptr(p.wt, lay, g, MODE == 0 && wc ? p.slot1 : p.slot0));
+        } else if (MODE == 0 && wc) {
+            W = shared ? p.w1_shared : p.w1_routed + (size_t)g * wmat;
         } else {
-            W0 = (shared ? p.w0_shared : p.w0_routed + (size_t)g * wmat) + (size_t)n0 * K;
-            W1 = MODE == 0 ? (shared ? p.w1_shared : p.w1_routed + (size_t)g * wmat) + (size_t)n0 * K : W0;
+            W = shared ? p.w0_shared : p.w0_routed + (size_t)g * wmat;
         }
-        d.rb[0] = make_rsrc(W0, (uint32_t)ncols * (uint32_t)K * 2u);
-        d.rb[1] = make_rsrc(W1, (uint32_t)ncols * (uint32_t)K * 2u);
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            // the B row of half c relative to n0 (GEMM1: gate for c = 0, up for c = 1, same row)
-            const int br = MODE == 0 ? wave * 32 + l32 : wave * 64 + c * 32 + l32;
-            d.vb[c] = br < ncols ? ((uint32_t)br * (uint32_t)K + (uint32_t)(lane >> 5) * 8u) * 2u : kOOB;
-        }
+        W += (size_t)n0 * K;
+        d.rb = make_rsrc(W, (uint32_t)ncols * (uint32_t)K * 2u);
+        // the B row of this lane relative to n0 (GEMM1: same row of gate or up)
+        const int br = MODE == 0 ? wg * 32 + l32 : wg * 64 + wc * 32 + l32;
+        d.vb = br < ncols ? ((uint32_t)br * (uint32_t)K + (uint32_t)(lane >> 5) * 8u) * 2u : kOOB;
         d.sb = (uint32_t)(BK * 2);
         d.kb = 32u;
-        d.klim = K - (lane >> 5) * 8;  // the lane's chunk starts 8 (lane / 32) into the k step
+        d.klim = br < ncols ? K - (lane >> 5) * 8 : -1;  // the lane's chunk starts 8 (lane / 32) into the k step
     }
 
-    f32x16 acc0[8], acc1[8];
+    f32x16 acc[kRowBlocks];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        acc0[i] = f32x16{};
-        acc1[i] = f32x16{};
-    }
-    i32x4 fa[2][NRB];
+    for (int i = 0; i < kRowBlocks; ++i) acc[i] = f32x16{};
+    i32x4 fa[NRB];
     constexpr int NS = kStages<MODE>;
-    i32x4 bq[NS][4];
+    i32x4 bq[NS][2];
 
     static_for<0, NS>([&](auto c) {
         constexpr int t = decltype(c)::value;
@@ -421,96 +425,121 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, int mt, int g, int r
     });
     wait_vm<kWaitFirstA<NS>>();
     barrier_lds();
-    read_a<NRB, 0, 0>(lane, fa[0]);
+#pragma unroll
+    for (int r = 0; r < NRB; ++r) fa[r] = read_a1<0, 0>(lane, r);
     // stages past the end load zeros, so the loop runs in whole turns of the ring
     const int nturns = (d.nsteps + NS - 1) / NS;
     for (int s = 0; s < nturns * NS; s += NS) {
         static_for<0, NS>([&](auto c) {
             constexpr int b = decltype(c)::value;
-            stage<MODE, NRB, b>(d, s + b, lane, fa, bq, acc0, acc1);
+            stage<MODE, NRB, b>(d, s + b, lane, fa, bq, acc);
         });
     }
     wait_vm<0>();  // no LDS DMA may outlive the workgroup
     wait_lgkm0();
     void* out = shared ? p.out_shared : p.out_routed;
+    barrier_lds();  // every wave has left the main loop: the ring is free
     if (MODE == 0) {
         // h = silu(g) * u into this M tile's slot, tiled with the slot's own KS
         // (the K of GEMM2), so GEMM2 streams it with contiguous 1 KiB reads.
         // Columns in [N, roundup(N, 32)) are GEMM2's K padding: they get zeros.
-        // A wave's 32 columns are one k block of the slot.  Each 32-row block
-        // goes through a private 4 KiB LDS slice of the A ring (free once every
-        // wave has left the main loop), fp32, row r at r * 128 B with rows r and
-        // r ^ 1 exchanged when bit 2 of r is set, so the accumulator writes (rows
-        // r and r + 4 in the two half-waves) touch 64 distinct banks.  It is read
+        // The pair's 32 h columns are one k block of the slot.  Round by round,
+        // the up wave stores its accumulators (lane-major, so writes and reads
+        // are contiguous) into one ring buffer per row block, and after a
+        // barrier the gate wave combines them with its own.  Each 32-row block
+        // of h then goes through the gate wave's private 4 KiB slice of the
+        // last ring buffer, fp32, row r at r * 128 B with rows r and r ^ 1
+        // exchanged when bit 2 of r is set, so the accumulator writes (rows r
+        // and r + 4 in the two half-waves) touch 64 distinct banks.  It is read
         // back in the tiled block's own order -- lane q takes slot q, 8 columns
         // of one row, two 16-byte reads on distinct banks -- and every 16-row
         // block is one contiguous 1 KiB store.  Rows of the slot past M hold
         // zeros (their A rows loaded as zeros).  LDS operations of one wave are
         // processed in order.
-        barrier_lds();
+        constexpr int R = kStages<0> - 1;  // row blocks per round
         const int ksh = (N + BK - 1) / BK;
-        const int kb = (n0 >> 5) + wave;  // n0 is a multiple of 32
-        if (kb < ksh) {
-            const bool live = kb * 32 + l32 < N;
-            uint16_t* h = static_cast<uint16_t*>(out) + (size_t)mt * 16 * p.h_slot_ks * 512;
-            float* st = reinterpret_cast<float*>(ring<0>() + wave * 256);
-            const int rr = lane >> 2, c8 = (lane & 3) ^ swz_of_row(rr);  // the slot this lane stores
+        const int kb = (n0 >> 5) + wg;  // n0 is a multiple of 32
+        const bool pair_live = kb < ksh;
+        const bool live = pair_live && kb * 32 + l32 < N;
+        uint16_t* h = static_cast<uint16_t*>(out) + (size_t)mt * kBlocks16 * p.h_slot_ks * 512;
+        float* st = reinterpret_cast<float*>(ring<kStages<0> - 1>()) + wg * 1024;
+        const int rr = lane >> 2, c8 = (lane & 3) ^ swz_of_row(rr);  // the slot this lane stores
+        static_for<0, (NRB + R - 1) / R>([&](auto rc) {
+            constexpr int r0 = decltype(rc)::value * R;
+            if (wc == 1) {
+                static_for<0, R>([&](auto jc) {
+                    constexpr int j = decltype(jc)::value;
+                    if constexpr (r0 + j < NRB) {
+                        float* x = xchg_slot<NRB, j>(wg);
 #pragma unroll
-            for (int r = 0; r < NRB; ++r) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int row = c_row(i, lane);  // bit 2 of row is lane / 32
-                    st[(row ^ ((row >> 2) & 1)) * 32 + l32] = live ? silu_f(acc0[r][i]) * acc1[r][i] : 0.0f;
-                }
-                // the staged values are read by other lanes of this wave: keep the
-                // compiler from moving the reads above the writes (no wait is needed)
-                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-#pragma unroll
-                for (int hb = 0; hb < 2; ++hb) {
-                    const int row = hb * 16 + rr;
-                    const float* src = st + (row ^ ((row >> 2) & 1)) * 32 + c8 * 8;
-                    const f32x4 v0 = *reinterpret_cast<const f32x4*>(src);
-                    const f32x4 v1 = *reinterpret_cast<const f32x4*>(src + 4);
-                    uint4 q;
-                    q.x = (uint32_t)f32_to_bf16(v0[0]) | ((uint32_t)f32_to_bf16(v0[1]) << 16);
-                    q.y = (uint32_t)f32_to_bf16(v0[2]) | ((uint32_t)f32_to_bf16(v0[3]) << 16);
-                    q.z = (uint32_t)f32_to_bf16(v1[0]) | ((uint32_t)f32_to_bf16(v1[1]) << 16);
-                    q.w = (uint32_t)f32_to_bf16(v1[2]) | ((uint32_t)f32_to_bf16(v1[3]) << 16);
-                    if (r * 32 + hb * 16 < M)
-                        *reinterpret_cast<uint4*>(h + ((size_t)(r * 2 + hb) * ksh + kb) * 512 + lane * 8) = q;
-                }
-                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");  // reads before the next block's writes
+                        for (int i = 0; i < 16; ++i) x[i * 64 + lane] = acc[r0 + j][i];
+                    }
+                });
             }
-        }
+            barrier_lds();
+            if (wc == 0 && pair_live) {
+                static_for<0, R>([&](auto jc) {
+                    constexpr int j = decltype(jc)::value;
+                    constexpr int r = r0 + j;
+                    if constexpr (r < NRB) {
+                        const float* x = xchg_slot<NRB, j>(wg);
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) {
+                            const int row = c_row(i, lane);  // bit 2 of row is lane / 32
+                            st[(row ^ ((row >> 2) & 1)) * 32 + l32] =
+                                live ? silu_f(acc[r][i]) * x[i * 64 + lane] : 0.0f;
+                        }
+                        // the staged values are read by other lanes of this wave:
+                        // keep the compiler from moving the reads above the writes
+                        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+                        for (int hb = 0; hb < 2; ++hb) {
+                            const int row = hb * 16 + rr;
+                            const float* src = st + (row ^ ((row >> 2) & 1)) * 32 + c8 * 8;
+                            const f32x4 v0 = *reinterpret_cast<const f32x4*>(src);
+                            const f32x4 v1 = *reinterpret_cast<const f32x4*>(src + 4);
+                            uint4 q;
+                            q.x = (uint32_t)f32_to_bf16(v0[0]) | ((uint32_t)f32_to_bf16(v0[1]) << 16);
+                            q.y = (uint32_t)f32_to_bf16(v0[2]) | ((uint32_t)f32_to_bf16(v0[3]) << 16);
+                            q.z = (uint32_t)f32_to_bf16(v1[0]) | ((uint32_t)f32_to_bf16(v1[1]) << 16);
+                            q.w = (uint32_t)f32_to_bf16(v1[2]) | ((uint32_t)f32_to_bf16(v1[3]) << 16);
+                            if (r * 32 + hb * 16 < M)
+                                *reinterpret_cast<uint4*>(h + ((size_t)(r * 2 + hb) * ksh + kb) * 512 + lane * 8) = q;
+                        }
+                        // reads before the next block's writes
+                        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+                    }
+                });
+            }
+            barrier_lds();  // the round's slots are read before the next round writes them
+        });
     } else {
-        // y through LDS, one 32-row block at a time: each wave stages its 32 x 64
-        // block in a private 8 KiB slice of the A ring (free once every wave has
-        // left the main loop), fp32, row r at r * 256 B with the two 128-byte
-        // halves swapped when bit 2 of r is set -- the accumulator writes (rows
-        // r and r + 4 in the two half-waves) and the 16-byte reads (16 lanes per
-        // row) both touch 64 distinct banks -- then stores 4 columns per lane:
-        // 16 lanes cover a row's 64 columns.  LDS operations of one wave are
+        // y through LDS, one 32-row block at a time: each wave stages its 32 x 32
+        // block in a private 4 KiB slice of the ring (free once every wave has
+        // left the main loop), fp32, row r at r * 128 B with rows r and r ^ 1
+        // exchanged when bit 2 of r is set -- the accumulator writes (rows r and
+        // r + 4 in the two half-waves) and the 16-byte reads (8 lanes per row)
+        // both touch 64 distinct banks -- then stores 4 columns per lane: 8
+        // lanes cover a row's 32 columns.  LDS operations of one wave are
         // processed in order, so a block's reads finish before the next block's
         // writes land.
-        barrier_lds();
-        float* st = reinterpret_cast<float*>((wave < 2 ? ring<0>() : ring<1>()) + (wave & 1) * 512);
-        const int cw = n0 + wave * 64;  // first output column of this wave
+        float* st = reinterpret_cast<float*>(wave < 4 ? ring<0>() : ring<1>()) + (wave & 3) * 1024;
+        const int cw = n0 + wg * 64 + wc * 32;  // first output column of this wave
 #pragma unroll
         for (int r = 0; r < NRB; ++r) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int row = c_row(i, lane);  // bit 2 of row is lane / 32
-                st[row * 64 + lane] = acc0[r][i];
-                st[row * 64 + (lane ^ 32)] = acc1[r][i];
+                st[(row ^ ((row >> 2) & 1)) * 32 + l32] = acc[r][i];
             }
             // the staged values are read by other lanes of this wave: keep the
             // compiler from moving the reads above the writes (no wait is needed)
             __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 #pragma unroll
-            for (int it = 0; it < 8; ++it) {
-                const int q = it * 64 + lane;  // chunk q: row q / 16, columns 4 (q % 16) .. + 3
-                const int row = q >> 4, c4 = (q & 15) * 4;
-                const f32x4 v = *reinterpret_cast<const f32x4*>(st + row * 64 + (c4 ^ (((row >> 2) & 1) << 5)));
+            for (int it = 0; it < 4; ++it) {
+                const int q = it * 64 + lane;  // chunk q: row q / 8, columns 4 (q % 8) .. + 3
+                const int row = q >> 3, c4 = (q & 7) * 4;
+                const f32x4 v = *reinterpret_cast<const f32x4*>(st + (row ^ ((row >> 2) & 1)) * 32 + c4);
                 const int grow = r * 32 + row, col = cw + c4;
                 if (grow < M && col < N) {
                     const size_t o = (size_t)(row0 + grow) * N + col;
@@ -529,7 +558,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, int mt, int g, int r
 }
 
 template <int MODE>
-__global__ void __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2, 2)))
 ffn_gemm_bf16(GemmArgs p) {
     const int L = xcd_remap(blockIdx.x, p.n_tiles[0] * p.NT);
     if (L < 0) return;
@@ -551,7 +580,8 @@ ffn_gemm_bf16(GemmArgs p) {
     case 5: run_tile<MODE, 5>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
     case 6: run_tile<MODE, 6>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
     case 7: run_tile<MODE, 7>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
-    default: run_tile<MODE, 8>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
+    case 8: run_tile<MODE, 8>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
+    default: run_tile<MODE, 9>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
     }
 }
 

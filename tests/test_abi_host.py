@@ -148,10 +148,14 @@ def test_max_rows_and_workspace_sizes():
     # the router's K-split partial logits: whole [T][E] fp32 copies
     assert ws[m.MOE_STAGE_ROUTE] % (8192 * 256 * 4) == 0 and 8192 * 256 * 4 <= ws[m.MOE_STAGE_ROUTE] <= 8 * 8192 * 256 * 4
     assert all(w % 256 == 0 for w in ws)
-    # the layer workspace holds y_rows (fp32) and y_shared at least; a bf16 layer
-    # materialises no x_perm (its GEMM reads x through row_src)
+    # the layer workspace holds y_rows (fp32) and y_shared at least, plus the
+    # h tile slots (one per possible M tile: up to rows / 288 + E + shared tiles);
+    # a bf16 layer materialises no x_perm (its GEMM reads x through row_src)
     rows = 8192 * 8
-    assert rows * 7168 * 4 + 8192 * 7168 * 4 <= ws[m.MOE_STAGE_LAYER] < rows * 7168 * 6
+    rows16 = rows + 256 * 15  # the layer pads expert segments to 16 rows
+    slots = (rows16 + 287) // 288 + 256 + (8192 + 287) // 288 + 1
+    y_bytes = rows16 * 7168 * 4 + 8192 * 7168 * 4
+    assert y_bytes <= ws[m.MOE_STAGE_LAYER] < y_bytes + slots * 288 * 2048 * 2 + (64 << 20)
     assert ws[m.MOE_STAGE_FFN] >= rows * 2048 * 2  # h in bf16
     assert m.moe_workspace_bytes(c, 7) == ctypes.c_size_t(-1).value
     assert m.moe_ffn_workspace_bytes(c, rows) == ws[m.MOE_STAGE_FFN]
