@@ -191,6 +191,14 @@ def moe_permute(cfg, x, x_scale, topk_ids, expert_counts, expert_offsets, row_sr
                                   _ptr(x_perm), _ptr(x_perm_scale), p, n, _stream(stream)))
 
 
+def moe_permute_noalloc(cfg, x, x_scale, topk_ids, expert_counts, expert_offsets, row_src, tok_row, x_perm,
+                        x_perm_scale, stream=None):
+    """moe_permute with the library's static scratch instead of a workspace."""
+    _check(_ffi.lib().moe_permute_noalloc(ctypes.byref(cfg), _ptr(x), _ptr(x_scale), _ptr(topk_ids),
+                                          _ptr(expert_counts), _ptr(expert_offsets), _ptr(row_src), _ptr(tok_row),
+                                          _ptr(x_perm), _ptr(x_perm_scale), _stream(stream)))
+
+
 def moe_grouped_ffn(cfg, n_rows_cap, x_rows, x_scale, expert_offsets, w: moe_weights, x_tokens, y_rows,
                     y_shared, ws, stream=None, row_src=None):
     """row_src: the dispatch map of moe_permute, read with cfg.x_layout ==

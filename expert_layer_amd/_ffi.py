@@ -20,7 +20,8 @@ MOE_LAYOUT_ROWMAJOR, MOE_LAYOUT_TILED, MOE_LAYOUT_INDEXED = 0, 1, 2
 
 EXPORTS = ("moe_validate", "moe_max_rows", "moe_workspace_bytes", "moe_ffn_workspace_bytes",
            "moe_x_perm_bytes", "moe_tiled_weights_bytes", "moe_tile_weights", "moe_route", "moe_permute", "moe_grouped_ffn",
-           "moe_combine", "moe_quantize_fp8", "moe_layer", "moe_weight_table", "moe_status_string",
+           "moe_combine", "moe_quantize_fp8", "moe_layer", "moe_weight_table", "moe_permute_noalloc",
+           "moe_status_string",
            "moe_last_error")
 
 
@@ -70,6 +71,8 @@ def lib() -> ctypes.CDLL:
         L.moe_route.restype = i32
         L.moe_permute.argtypes = [C, P, P, P, P, P, P, P, P, P, P, sz, P]
         L.moe_permute.restype = i32
+        L.moe_permute_noalloc.argtypes = [C, P, P, P, P, P, P, P, P, P, P]
+        L.moe_permute_noalloc.restype = i32
         L.moe_grouped_ffn.argtypes = [C, i64, P, P, P, P, W, P, P, P, P, sz, P]
         L.moe_grouped_ffn.restype = i32
         L.moe_combine.argtypes = [C, P, P, P, P, P, P]

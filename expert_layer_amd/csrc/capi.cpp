@@ -531,6 +531,46 @@ moe_status moe_permute(const moe_cfg* cfg, const void* x, const float* x_scale, 
                            x_perm_scale, ws, static_cast<hipStream_t>(stream));
 }
 
+moe_status moe_permute_noalloc(const moe_cfg* cfg, const void* x, const float* x_scale, const int32_t* topk_ids,
+                               int32_t* expert_counts, int32_t* expert_offsets, int32_t* row_src, int32_t* tok_row,
+                               void* x_perm, float* x_perm_scale, void* stream) {
+    moe_status st = check_cfg(cfg);
+    if (st != MOE_OK) return st;
+    const moe_cfg& c = *cfg;
+    REQUIRE(x, "x");
+    REQUIRE(topk_ids, "topk_ids");
+    REQUIRE(expert_counts, "expert_counts");
+    REQUIRE(expert_offsets, "expert_offsets");
+    REQUIRE(row_src, "row_src");
+    REQUIRE(tok_row, "tok_row");
+    if (c.x_layout != MOE_LAYOUT_INDEXED) REQUIRE(x_perm, "x_perm");
+    if (c.act_dtype == MOE_FP8_E4M3 && c.x_layout != MOE_LAYOUT_INDEXED) {
+        REQUIRE(x_scale, "x_scale");
+        REQUIRE(x_perm_scale, "x_perm_scale");
+    }
+    REQUIRE_A16(x, "x");
+    REQUIRE_A16(x_perm, "x_perm");
+    const int64_t need = 2 * (int64_t)moe::permute_blocks(c.T) * c.E;
+    if (need > moe::kNoAllocPermuteInts)
+        return fail(MOE_ERR_UNSUPPORTED,
+                    "moe_permute_noalloc holds 2 * ceil(T / 256) * E = %lld per-block counts at most %lld "
+                    "(T=%d, E=%d); use moe_permute with a workspace",
+                    (long long)need, (long long)moe::kNoAllocPermuteInts, c.T, c.E);
+    if (c.T == 0) return MOE_OK;
+    int32_t* scratch = nullptr;
+    hipError_t e = moe::noalloc_permute_scratch(&scratch);
+    if (e != hipSuccess) return hip_fail(e, "moe_permute_noalloc (scratch address)");
+    const size_t n = (size_t)moe::permute_blocks(c.T) * c.E;
+    const moe::PermuteWs ws{scratch, scratch + n};
+    const XPermGeom g = x_perm_geom(c);
+    const moe::PermuteLayout lay{g.tiled ? 1 : 0, (g.tiled && c.has_shared) ? g.rows_pad : -1,
+                                 c.x_layout == MOE_LAYOUT_INDEXED ? 0 : 1};
+    e = moe::launch_permute(c, x, x_scale, topk_ids, expert_counts, expert_offsets, row_src, tok_row, x_perm,
+                            x_perm_scale, max_rows_of(c), ws, lay, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "moe_permute_noalloc");
+    return MOE_OK;
+}
+
 moe_status moe_grouped_ffn(const moe_cfg* cfg, int64_t n_rows_cap, const void* x_rows, const float* x_scale,
                            const int32_t* expert_offsets, const int32_t* row_src, const moe_weights* w,
                            const void* x_tokens, void* y_rows, void* y_shared, void* ws, size_t ws_bytes,

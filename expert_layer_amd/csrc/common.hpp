@@ -148,6 +148,12 @@ hipError_t launch_permute(const moe_cfg& c, const void* x, const float* x_scale,
                           void* x_perm, float* x_perm_scale, int64_t max_rows, PermuteWs ws,
                           PermuteLayout lay, hipStream_t s);
 
+// The allocation-free permute's scratch: a static device array of this many
+// int32 (4 MiB), whose address on the current device noalloc_permute_scratch
+// returns (looked up once per device).
+constexpr int64_t kNoAllocPermuteInts = (int64_t)1 << 20;
+hipError_t noalloc_permute_scratch(int32_t** ptr);
+
 // bf16 rows [T][H] -> e4m3 codes [T][H] and fp32 scales [T][H / 128], one
 // scale per 1 x 128 block (H a multiple of 128; x, q 16- and 8-byte aligned).
 hipError_t launch_quant_rows_e4m3(const void* x, int T, int H, uint8_t* q, float* sc, hipStream_t s);

@@ -19,6 +19,8 @@
 // With the indexed layout (moe_layer's) steps 4 and 5 do not run: only the
 // maps are written, and the grouped FFN reads each dispatched row from x
 // through row_src, so the payload crosses HBM once, inside GEMM1.
+#include <mutex>
+
 #include "common.hpp"
 
 namespace moe {
@@ -268,6 +270,37 @@ hipError_t launch_permute(const moe_cfg& c, const void* x, const float* x_scale,
         hipLaunchKernelGGL(perm_zero, dim3((unsigned)((max_rows + 3) / 4)), dim3(256), 0, s, row_src,
                            static_cast<uint8_t*>(x_perm), xps, max_rows, row_bytes, n_scale);
     return hipGetLastError();
+}
+
+// ------------------------------------------------- allocation-free permute
+// The scratch of moe_permute_noalloc: the per-block expert counts and row
+// bases of the counting sort (2 * ceil(T / 256) * E int32), in a file-scope
+// device array of a fixed size that every GPU the library runs on holds until
+// the process ends.  In host code `scratch` only names the symbol: its device
+// address, which differs per GPU, comes from hipGetSymbolAddress with that GPU
+// current, once, and is the only address the kernels are given.
+static __device__ __align__(256) int32_t scratch[kNoAllocPermuteInts];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t* g_scratch[kMaxDevices] = {};
+}  // namespace
+
+hipError_t noalloc_permute_scratch(int32_t** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch[dev] = static_cast<int32_t*>(p);
+    }
+    *ptr = g_scratch[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_offsets_one_group(int32_t* offsets, int n, hipStream_t s) {

@@ -293,6 +293,23 @@ moe_status moe_permute(const moe_cfg *cfg, const void *x, const float *x_scale,
                        void *x_perm, float *x_perm_scale, void *ws, size_t ws_bytes,
                        void *stream);
 
+/* moe_permute without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments, results and layouts as moe_permute,
+ * without ws / ws_bytes: the per-block counts of the counting sort live in a
+ * static device array of the library, 4 MiB on each GPU it runs on, held until
+ * the process ends.  Limit: 2 * ceil(T / 256) * E <= 1048576 (for example
+ * T <= 524288 at E = 256), else MOE_ERR_UNSUPPORTED before anything is
+ * enqueued.  The first call on a device looks up that array's address on the
+ * current device (which must be the stream's device); no call allocates,
+ * frees or synchronises.  Every call on one GPU shares the array, so calls
+ * that overlap on one GPU (work of two of them in flight at once, e.g. on two
+ * streams) race and give undefined results: order them on one stream. */
+moe_status moe_permute_noalloc(const moe_cfg *cfg, const void *x, const float *x_scale,
+                               const int32_t *topk_ids, int32_t *expert_counts,
+                               int32_t *expert_offsets, int32_t *row_src, int32_t *tok_row,
+                               void *x_perm, float *x_perm_scale, void *stream);
+
 /* Grouped SwiGLU FFN over expert-contiguous rows (ASAP section 3.4.2's GMM).
  * For every expert e and every row r in [expert_offsets[e], expert_offsets[e+1]):
  *   g_i = sum_h x_rows[r][h] * w_gate[e][i][h],  u_i = sum_h x_rows[r][h] * w_up[e][i][h]

@@ -404,3 +404,26 @@ def test_layer_dispatches_a_large_x_into_x_perm():
     below8, above8 = (2 ** 31 - 1) // 7168, (2 ** 31) // 7168 + 1
     rows = m.moe_max_rows(_dsv3(T=above8, m_tile=16))
     assert ws(above8, **fp8) - ws(below8, **fp8) * above8 / below8 >= rows * 7168 * 0.99
+
+
+def test_permute_noalloc_checks_before_any_launch():
+    """The allocation-free permute refuses a batch whose per-block counts
+    exceed its static scratch (2 * ceil(T / 256) * E <= 2^20) and bad pointers
+    before it touches the HIP runtime; T = 0 enqueues nothing."""
+    lib = _ffi.lib()
+    fake = ctypes.c_void_p(0x100000)
+    big = m.make_cfg(T=524288 + 256, H=64, E=256, k=8, I=64)
+    st = lib.moe_permute_noalloc(ctypes.byref(big), fake, None, fake, fake, fake, fake, fake, fake, None, None)
+    assert st == m.MOE_ERR_UNSUPPORTED and "moe_permute_noalloc" in m.moe_last_error()
+    c = m.make_cfg(T=16, H=64, E=8, k=2, I=64)
+    st = lib.moe_permute_noalloc(ctypes.byref(c), fake, None, None, fake, fake, fake, fake, fake, None, None)
+    assert st == m.MOE_ERR_INVALID_ARG and "topk_ids" in m.moe_last_error()
+    st = lib.moe_permute_noalloc(ctypes.byref(c), ctypes.c_void_p(0x100008), None, fake, fake, fake, fake, fake,
+                                 fake, None, None)
+    assert st == m.MOE_ERR_INVALID_ARG and "aligned" in m.moe_last_error()
+    z = m.make_cfg(T=0, H=64, E=8, k=2, I=64)
+    assert lib.moe_permute_noalloc(ctypes.byref(z), fake, None, fake, fake, fake, fake, fake, fake, None,
+                                   None) == m.MOE_OK
+    # the largest batch it holds at E = 256
+    ok = m.make_cfg(T=524288, H=64, E=256, k=8, I=64)
+    assert 2 * ((524288 + 255) // 256) * 256 == 1 << 20 and m.moe_validate(ok) == m.MOE_OK
