@@ -75,10 +75,14 @@ def parse():
                         "passes of the stage calls on the workload's routing, with the expert weights drawn by "
                         "torch.randn (their values do not change which bytes the kernels move; a few hundred "
                         "dispatches in all); prints no JSON line")
-    p.add_argument("--no-clock", action="store_true", help="skip sampling the GPU clock under load")
+    p.add_argument("--no-clock", action="store_true", help="accepted for older command lines; does nothing")
     p.add_argument("--pmc-summary", nargs="+", metavar="DB",
                    help="no GPU: print, per kernel, the per-dispatch average of every counter in these rocprofv3 "
                         "--pmc result databases (a markdown table), and exit")
+    p.add_argument("--clock-from", nargs=2, metavar=("SQ_DB", "KT_STATS_CSV"),
+                   help="no GPU: from a --pmc run with GRBM_GUI_ACTIVE and SQ_VALU_MFMA_BUSY_CYCLES of a --traffic-run "
+                        "and the kernel_stats.csv of a --kernel-trace --stats run, write the grouped FFN kernels' "
+                        "clock under load and MFMA utilisation to the clock file, exit")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                    help="no GPU: read two rocprofv3 --pmc result databases of a --traffic-run (FETCH_SIZE, then "
                         "WRITE_SIZE), write the grouped FFN's HBM bytes per launch to the traffic file, exit")
@@ -148,20 +152,34 @@ def traffic_from(fetch_db, write_db, workload):
     print(json.dumps(res))
 
 
-def pmc_summary(dbs):
-    """Per kernel and counter: the value summed over a dispatch's instances,
-    averaged over the kernel's dispatches, from rocprofv3 --pmc databases."""
+def _short(name):
+    """A kernel's name without its return type, namespaces and arguments."""
+    n = name.replace("void ", "").replace("(anonymous namespace)::", "").replace("moe::", "")
+    return n.split("(")[0].strip()
+
+
+def _pmc_dispatches(db):
+    """{dispatch_id: (kernel name, {counter: [value per instance]})} of a
+    rocprofv3 --pmc results database."""
     import sqlite3
+    con = sqlite3.connect(db)
+    out = {}
+    for name, cname, val, disp in con.execute(
+            "select kernel_name, counter_name, value, dispatch_id from counters_collection"):
+        out.setdefault(disp, (name, {}))[1].setdefault(cname, []).append(float(val))
+    con.close()
+    return out
+
+
+def pmc_summary(dbs):
+    """Per kernel and counter: the value of a dispatch (summed over the
+    counter's instances), averaged over the kernel's dispatches, from
+    rocprofv3 --pmc databases."""
     rows = {}
     for db in dbs:
-        con = sqlite3.connect(db)
-        per = {}
-        for name, cname, val, disp in con.execute(
-                "select kernel_name, counter_name, value, dispatch_id from counters_collection"):
-            per[(name, cname, disp)] = per.get((name, cname, disp), 0.0) + float(val)
-        con.close()
-        for (name, cname, disp), v in per.items():
-            rows.setdefault((name, cname), []).append(v)
+        for name, cs in _pmc_dispatches(db).values():
+            for c, v in cs.items():
+                rows.setdefault((_short(name), c), []).append(sum(v))
     counters = sorted({c for _, c in rows})
     kernels = sorted({k for k, _ in rows})
     print("| kernel | dispatches | " + " | ".join(counters) + " |")
@@ -172,7 +190,43 @@ def pmc_summary(dbs):
         for c in counters:
             v = rows.get((k, c))
             vals.append(f"{sum(v) / len(v):.6g}" if v else "")
-        print(f"| {k.split('(')[0]} | {n} | " + " | ".join(vals) + " |")
+        print(f"| {k} | {n} | " + " | ".join(vals) + " |")
+
+
+SIMDS = 1024  # MI355X: 256 CUs x 4 SIMDs
+XCDS = 8      # GRBM_GUI_ACTIVE has one instance per XCD; the database holds their sum
+CLOCK_FILE = os.path.join(ROOT, "profiles", "clock_grouped_ffn_c3_dsv3_bf16.json")
+
+
+def clock_from(sq_db, kt_stats_csv, workload):
+    """The GPU clock under the grouped FFN's load and its MFMA utilisation:
+    per kernel, GRBM_GUI_ACTIVE (busy cycles, summed over the 8 XCDs, so / 8
+    per XCD) over the kernel's average duration from a --kernel-trace --stats run of
+    the same build on the same box, and SQ_VALU_MFMA_BUSY_CYCLES over those
+    cycles times the SIMD count.  Written to the clock file with the FFN
+    sources' hash."""
+    import csv
+    disp = _pmc_dispatches(sq_db)
+    dur = {}
+    for r in csv.DictReader(open(kt_stats_csv)):
+        dur[_short(r["Name"])] = float(r["AverageNs"]) * 1e-9
+    res = {"workload": workload, "source_hash": ffn_source_hash(), "kernels": {}}
+    for k in FFN_KERNELS[1:]:
+        grbm = [sum(cs["GRBM_GUI_ACTIVE"]) / XCDS for n, cs in disp.values()
+                if _short(n) == k and "GRBM_GUI_ACTIVE" in cs]
+        busy = [sum(cs["SQ_VALU_MFMA_BUSY_CYCLES"]) for n, cs in disp.values()
+                if _short(n) == k and "SQ_VALU_MFMA_BUSY_CYCLES" in cs]
+        if not grbm or k not in dur:
+            raise SystemExit(f"no GRBM_GUI_ACTIVE or duration for {k}")
+        cyc = sum(grbm) / len(grbm)
+        e = {"grbm_cycles": cyc, "avg_s": dur[k], "clock_ghz": round(cyc / dur[k] / 1e9, 3)}
+        if busy:
+            e["mfma_busy_frac"] = round(sum(busy) / len(busy) / (cyc * SIMDS), 4)
+        res["kernels"][k] = e
+    os.makedirs(os.path.dirname(CLOCK_FILE), exist_ok=True)
+    with open(CLOCK_FILE, "w") as f:
+        json.dump(res, f, indent=1)
+    print(json.dumps(res))
 
 
 def ffn_source_hash() -> str:
@@ -189,6 +243,9 @@ def main():
         return
     if a.pmc_summary:
         pmc_summary(a.pmc_summary)
+        return
+    if a.clock_from:
+        clock_from(*a.clock_from, a.workload)
         return
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
@@ -239,75 +296,6 @@ def summary(r):
     rf = r["roofline"]
     out["roofline"] = {k: rf[k] for k in ("bound", "achieved", "peak", "unit", "frac", "mfma_frac", "hbm_frac",
                                            "roofline_ms") if k in rf}
-    return out
-
-
-def sclk_under_load(step, ms_step, seconds=1.5):
-    """The GFX clock while the step runs back to back: amdsmi polled every
-    10 ms by a thread while about `seconds` of steps are in flight.  Returns
-    the median, min and max of the samples (MHz), or the reason there are
-    none."""
-    import threading
-
-    import torch
-    try:
-        import amdsmi
-        amdsmi.amdsmi_init()
-        hs = amdsmi.amdsmi_get_processor_handles()
-        h = hs[0]
-        bus = getattr(torch.cuda.get_device_properties(0), "pci_bus_id", None)
-        if bus is not None and len(hs) > 1:
-            for c in hs:
-                if int(amdsmi.amdsmi_get_gpu_device_bdf(c).split(":")[1], 16) == int(bus):
-                    h = c
-    except Exception as e:  # no amdsmi or no device access: no figure
-        return {"error": f"amdsmi: {e}"}
-    samples = {"average_gfxclk": [], "current_gfxclk_max": [], "clock_info": []}
-    stop = threading.Event()
-
-    def num(v):
-        return float(v) if isinstance(v, (int, float)) and 0 < float(v) < 10000 else None
-
-    def poll():
-        while not stop.is_set():
-            try:
-                m = amdsmi.amdsmi_get_gpu_metrics_info(h)
-                v = num(m.get("average_gfxclk_frequency"))
-                if v:
-                    samples["average_gfxclk"].append(v)
-                cur = [num(c) for c in (m.get("current_gfxclks") or []) if num(c)]
-                if cur:
-                    samples["current_gfxclk_max"].append(max(cur))
-            except Exception:
-                pass
-            try:
-                v = num(amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)["clk"])
-                if v:
-                    samples["clock_info"].append(v)
-            except Exception:
-                pass
-            time.sleep(0.01)
-
-    n = max(10, int(seconds * 1e3 / max(ms_step, 0.05)))
-    torch.cuda.synchronize()
-    for i in range(n):
-        step(i)
-    th = threading.Thread(target=poll, daemon=True)
-    th.start()
-    torch.cuda.synchronize()
-    stop.set()
-    th.join()
-    try:
-        amdsmi.amdsmi_shut_down()
-    except Exception:
-        pass
-    out = {"steps": n, "how": "amdsmi polled every 10 ms while the steps ran back to back: gpu_metrics "
-                              "average_gfxclk_frequency, the largest of its per-XCD current_gfxclks, and "
-                              "clock_info's GFX clock; median (min, max) of the samples in MHz"}
-    for k, v in samples.items():
-        if v:
-            v = sorted(v)
-            out[k] = {"median": v[len(v) // 2], "min": v[0], "max": v[-1], "n": len(v)}
     return out
 
 
@@ -541,7 +529,17 @@ def bench_bf16_layer(a, s, dev, extra=False):
         "hbm_frac": round(ffn_gbs / PEAK_HBM_GBS, 4)})
 
     cpu = None if (a.no_cpu_baseline or extra) else cpu_baseline(s, x, w_r, a.cpu_seconds)
-    sclk = None if (extra or a.no_clock) else sclk_under_load(step, ms_step)
+    # the clock under this load: from the committed counter run of the same
+    # FFN sources (GRBM_GUI_ACTIVE per XCD over the kernel's duration), else null
+    sclk = None
+    if not extra and os.path.exists(CLOCK_FILE):
+        cf = json.load(open(CLOCK_FILE))
+        if cf.get("source_hash") == ffn_source_hash() and cf.get("workload") == a.workload and not a.tokens:
+            sclk = {k: {"clock_ghz": v["clock_ghz"], "mfma_busy_frac": v.get("mfma_busy_frac")}
+                    for k, v in cf["kernels"].items()}
+            sclk["source"] = ("rocprofv3 --pmc GRBM_GUI_ACTIVE (one XCD's busy cycles) over the kernel's average "
+                              "duration, SQ_VALU_MFMA_BUSY_CYCLES over those cycles x 1024 SIMDs; "
+                              "profiles/clock_grouped_ffn_c3_dsv3_bf16.json")
 
     res = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps,
