@@ -590,6 +590,10 @@ def bench_fp8_ffn(a, s, dev):
     y = torch.empty((s.T, s.H), dtype=torch.bfloat16, device=dev)
     ws = moe.workspace(c, moe.MOE_STAGE_FFN, dev, n_rows_cap=s.T)
     w = moe.weights(wg, wu, wd, s_gate=sg, s_up=su, s_down=sd)
+    wbuf = None
+    if not f4:  # e4m3 weights in the tiled layout (rewritten once, at load time)
+        w, wbuf = moe.tile_weights(c, w, dev)
+        del wg, wu, wd
     torch.cuda.synchronize()
     print(f"[bench] inputs ready in {time.time() - t_gen:.1f}s", file=sys.stderr, flush=True)
     stream = torch.cuda.current_stream()
@@ -633,7 +637,8 @@ def bench_fp8_ffn(a, s, dev):
         "wall_s_timed": round(wall, 3),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_FP8_TFLOPS, 4), "traffic": None,
-                     "kernel": "moe_grouped_ffn (ffn_gemm_fp8 GEMM1+SwiGLU+requantise, GEMM2, tile list)",
+                     "kernel": "moe_grouped_ffn (%s GEMM1+SwiGLU+requantise, GEMM2, tile list)"
+                               % ("ffn_gemm_fp8" if f4 else "ffn_gemm_e4m3"),
                      "flop_per_launch": flop, "bytes_per_launch": nbytes,
                      "roofline_ms": round(max(t_mfma, t_hbm) * 1e3, 4),
                      "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
@@ -680,6 +685,10 @@ def bench_fp8_layer(a, s, dev):
     sh = gen(s.with_(I=I_sh), E, dev) if s.shared else (None,) * 6
     w = moe.weights(wg, wu, wd, s_gate=sg, s_up=su, s_down=sd, sh_gate=sh[0], sh_up=sh[2], sh_down=sh[4],
                     sh_s_gate=sh[1], sh_s_up=sh[3], sh_s_down=sh[5])
+    wbuf = None
+    if not f4:  # e4m3 weights in the tiled layout (rewritten once, at load time)
+        w, wbuf = moe.tile_weights(c, w, dev)
+        del wg, wu, wd
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     ws = moe.workspace(c, moe.MOE_STAGE_LAYER, dev)
     torch.cuda.synchronize()
@@ -720,7 +729,8 @@ def bench_fp8_layer(a, s, dev):
     y_rows = torch.empty((rows, H), dtype=torch.bfloat16, device=dev)
     y_sh = torch.empty((T, H), dtype=torch.bfloat16, device=dev) if s.shared else None
     offs1 = torch.tensor([0, T], **i32)
-    w1 = moe.weights(sh[0], sh[2], sh[4], s_gate=sh[1], s_up=sh[3], s_down=sh[5]) if s.shared else None
+    w1 = moe.moe_weights(w_gate=w.sh_gate, w_up=w.sh_up, w_down=w.sh_down, s_gate=w.sh_s_gate, s_up=w.sh_s_up,
+                         s_down=w.sh_s_down, layout=w.layout) if s.shared else None
     ws_r = moe.workspace(c, moe.MOE_STAGE_ROUTE, dev)
     ws_p = moe.workspace(cq, moe.MOE_STAGE_PERMUTE, dev)
     ws_f = moe.workspace(cq, moe.MOE_STAGE_FFN, dev, n_rows_cap=rows)
@@ -786,7 +796,8 @@ def bench_fp8_layer(a, s, dev):
     else:
         roofline = {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(tf / PEAK_FP8_TFLOPS, 4)}
-    roofline.update({"traffic": None, "kernel": "grouped FFN (ffn_gemm_fp8 routed + shared, tile lists)",
+    roofline.update({"traffic": None, "kernel": "grouped FFN (%s routed + shared, tile lists)"
+                     % ("ffn_gemm_fp8" if f4 else "ffn_gemm_e4m3"),
                      "flop_per_launch": ffn_flop, "bytes_per_launch": bytes_["grouped_ffn"],
                      "roofline_ms": round(max(t_mfma, t_hbm) * 1e3, 4),
                      "mfma_frac": round(tf / PEAK_FP8_TFLOPS, 4), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)})

@@ -18,8 +18,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libexpert_layer_amd.so")
-SOURCES = ["capi.cpp", "route.hip", "permute.hip", "gemm_bf16.hip", "gemm_fp8.hip", "gemm_f32.hip", "combine.hip"]
-VGPR_FORM = {"gemm_fp8.hip"}
+SOURCES = ["capi.cpp", "route.hip", "permute.hip", "gemm_bf16.hip", "gemm_fp8.hip", "gemm_e4m3.hip", "gemm_f32.hip", "combine.hip"]
+VGPR_FORM = {"gemm_fp8.hip", "gemm_e4m3.hip"}
 ARCH = "gfx950"
 
 

@@ -320,14 +320,19 @@ moe_status check_ws(void* ws, size_t have, size_t need) {
 #define REQUIRE_A16(p, name) \
     if (reinterpret_cast<uintptr_t>(p) % 16) return fail(MOE_ERR_INVALID_ARG, "%s is not 16-byte aligned", name)
 
+// Weights moe_tile_weights can rewrite: bf16 experts on bf16 rows, e4m3 experts
+// (on e4m3 rows, or on bf16 activations that the layer quantises).
+bool tileable(const moe_cfg& c) {
+    return (c.act_dtype == MOE_BF16 && c.w_dtype == MOE_BF16) || c.w_dtype == MOE_FP8_E4M3;
+}
+
 // Checks the weight pointers a call reads (before anything is enqueued).
 moe_status check_weights(const moe_cfg& c, const moe_weights* w) {
     if (!w) return fail(MOE_ERR_INVALID_ARG, "w is NULL");
     if (w->layout != MOE_LAYOUT_ROWMAJOR && w->layout != MOE_LAYOUT_TILED)
         return fail(MOE_ERR_INVALID_ARG, "w->layout=%d", w->layout);
     const bool tiled = w->layout == MOE_LAYOUT_TILED;
-    if (tiled && (c.act_dtype != MOE_BF16 || c.w_dtype != MOE_BF16))
-        return fail(MOE_ERR_UNSUPPORTED, "tiled weights are bf16 only");
+    if (tiled && !tileable(c)) return fail(MOE_ERR_UNSUPPORTED, "tiled weights are bf16 or e4m3 only");
     if (w->table) {
         // the matrices are read on the device, through the table
         if (c.act_dtype == MOE_F32) return fail(MOE_ERR_UNSUPPORTED, "pointer-table weights on the fp32 path");
@@ -428,7 +433,7 @@ moe_status layer_fp8_experts(const moe_cfg& c, const moe_weights& w, const void*
         const moe_cfg c1 = fp8_shared_cfg(c);
         // the shared expert as the one group of its own launch: table entry E
         const moe_weights ws1{w.sh_gate, w.sh_up,  w.sh_down, w.sh_s_gate, w.sh_s_up, w.sh_s_down,
-                              nullptr,   nullptr,  nullptr,   MOE_LAYOUT_ROWMAJOR, nullptr, nullptr,
+                              nullptr,   nullptr,  nullptr,   w.layout, nullptr, nullptr,
                               nullptr,   nullptr,  nullptr,   0};
         e = moe::launch_offsets_one_group(l.offsets_sh, c.T, s);
         if (e != hipSuccess) return hip_fail(e, "moe_layer (shared offsets)");
@@ -668,6 +673,10 @@ size_t moe_x_perm_bytes(const moe_cfg* cfg) {
 
 size_t moe_tiled_weights_bytes(const moe_cfg* cfg) {
     if (check_cfg(cfg) != MOE_OK) return (size_t)-1;
+    if (!tileable(*cfg)) {
+        fail(MOE_ERR_UNSUPPORTED, "tiled weights are bf16 or e4m3 only");
+        return (size_t)-1;
+    }
     const moe::TiledSizes t = moe::tiled_sizes(*cfg);
     return align_up(t.w13) + align_up(t.w2) + align_up(t.sh13) + align_up(t.sh2);
 }
@@ -677,7 +686,7 @@ moe_status moe_tile_weights(const moe_cfg* cfg, const moe_weights* src, void* ds
     moe_status st = check_cfg(cfg);
     if (st != MOE_OK) return st;
     const moe_cfg& c = *cfg;
-    if (c.act_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "tiled weights are bf16 only");
+    if (!tileable(c)) return fail(MOE_ERR_UNSUPPORTED, "tiled weights are bf16 or e4m3 only");
     if ((st = check_weights(c, src)) != MOE_OK) return st;
     if (src->layout != MOE_LAYOUT_ROWMAJOR) return fail(MOE_ERR_INVALID_ARG, "src must be row-major");
     if (src->table) return fail(MOE_ERR_INVALID_ARG, "src must be contiguous (table == NULL)");
@@ -698,6 +707,14 @@ moe_status moe_tile_weights(const moe_cfg* cfg, const moe_weights* src, void* ds
     o.sh_gate = sh13;
     o.sh_down = sh2;
     o.layout = MOE_LAYOUT_TILED;
+    if (c.w_dtype == MOE_FP8_E4M3) {  // the block scales are not rewritten: the caller's arrays
+        o.s_gate = src->s_gate;
+        o.s_up = src->s_up;
+        o.s_down = src->s_down;
+        o.sh_s_gate = src->sh_s_gate;
+        o.sh_s_up = src->sh_s_up;
+        o.sh_s_down = src->sh_s_down;
+    }
     *tiled = o;
     return MOE_OK;
 }
@@ -751,9 +768,6 @@ moe_status moe_layer(const moe_cfg* cfg, const void* w_router, const float* bias
     REQUIRE_A16(x, "x");
     REQUIRE_A16(w_router, "w_router");
     REQUIRE_A16(out, "out");
-    if (fp8_experts(c)) {
-        if (w->layout != MOE_LAYOUT_ROWMAJOR) return fail(MOE_ERR_UNSUPPORTED, "fp8 experts take row-major weights");
-    }
     // the stage configuration the layer derives must be a valid one
     const moe_cfg derived = fp8_experts(c) ? fp8_routed_cfg(c) : layer_stage_cfg(c);
     if ((st = check_cfg(&derived)) != MOE_OK) return st;

@@ -115,6 +115,23 @@ __host__ __device__ __forceinline__ int xcd_remap(int b, int n_valid) {
 // logical tiles: `items` rounded up to a multiple of 8.
 __host__ __device__ __forceinline__ int64_t xcd_grid(int64_t items) { return (items + 7) / 8 * 8; }
 
+// The same with runs: above 256 tiles, XCD x takes runs x, x + 8, x + 16, ...
+// of 32 consecutive logical tiles (up to 256, xcd_remap's even split, so a
+// small launch still spreads over every XCD).  A run fills one XCD's CUs and
+// shares its L2; at any time the eight XCDs work on eight neighbouring runs,
+// whose common panels (the weights of one expert, the row panels of its M
+// tiles) the whole chip then reads from the memory-side cache instead of HBM.
+// Every L < n_valid is reached exactly once for a grid of xcd_grid_runs(items)
+// blocks, n_valid <= items; -1 for idle blocks.
+__host__ __device__ __forceinline__ int xcd_remap_runs(int b, int n_valid) {
+    constexpr int kXcd = 8, kRun = 32;
+    if (n_valid <= kXcd * kRun) return xcd_remap(b, n_valid);
+    const int x = b % kXcd, i = b / kXcd;
+    const int L = ((i / kRun) * kXcd + x) * kRun + i % kRun;
+    return L < n_valid ? L : -1;
+}
+__host__ __device__ __forceinline__ int64_t xcd_grid_runs(int64_t items) { return (items + 255) / 256 * 256; }
+
 }  // namespace moe
 
 // ---------------------------------------------------------------- launchers
@@ -165,7 +182,7 @@ hipError_t launch_offsets_one_group(int32_t* offsets, int n, hipStream_t s);
 // Tile heights (rows) and the h / output columns one tile covers in GEMM1 /
 // GEMM2; fp8 tiles cover the bf16 tiles' columns.
 constexpr int kFfnBmBf16 = 288, kFfnN1Bf16 = 128, kFfnN2Bf16 = 256;
-constexpr int kFfnBmFp8 = 224, kFfnBmFp8Small = 128;
+constexpr int kFfnBmFp8 = 224, kFfnBmFp8Small = 128, kFfnBmE4m3 = 256;
 constexpr int kFfnBmF32 = 64, kFfnN1F32 = 64, kFfnN2F32 = 64;
 
 // Device work lists of the grouped FFN, carved from the workspace.
@@ -231,6 +248,14 @@ hipError_t launch_gemm_fp8(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_c
                            const float* x_scale, const int32_t* row_src, const int32_t* offsets,
                            const moe_weights& w, const WTab& wt, void* y_rows, const FfnWork& wk, void* h,
                            float* h_scale, hipStream_t s);
+// The e4m3-weight path of launch_gemm_fp8 (same arguments): weights row-major
+// or in the tiled e4m3 layout, streamed into registers.
+hipError_t launch_gemm_e4m3(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_cap, const void* x_rows,
+                            const float* x_scale, const int32_t* row_src, const int32_t* offsets,
+                            const moe_weights& w, const WTab& wt, void* y_rows, const FfnWork& wk, void* h,
+                            float* h_scale, hipStream_t s);
+hipError_t launch_tile_weights_e4m3(const moe_cfg& c, const moe_weights& src, void* w13, void* w2, void* sh13,
+                                    void* sh2, hipStream_t s);
 hipError_t launch_gemm_f32(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_cap, const void* x_rows,
                            const int32_t* offsets, const moe_weights& w, const void* x_tokens, void* y_rows,
                            void* y_shared, const FfnWork& wk, void* h, void* h_sh, hipStream_t s);

@@ -800,6 +800,14 @@ static int groups2(int H) { return (H + 63) / 64; }
 
 TiledSizes tiled_sizes(const moe_cfg& c) {
     TiledSizes t{};
+    if (c.w_dtype == MOE_FP8_E4M3) {
+        // tiled e4m3: the row-major sizes (H, I, I_shared are multiples of 128)
+        t.w13 = (size_t)2 * c.I * c.H * c.E;
+        t.w2 = (size_t)c.H * c.I * c.E;
+        t.sh13 = c.has_shared ? (size_t)2 * c.I_shared * c.H : 0;
+        t.sh2 = c.has_shared ? (size_t)c.H * c.I_shared : 0;
+        return t;
+    }
     const size_t ksh = (size_t)((c.H + BK - 1) / BK);
     auto w13 = [&](int I) { return (size_t)groups13(I) * ksh * 4096; };
     auto w2 = [&](int I) { return (size_t)groups2(c.H) * (size_t)((I + BK - 1) / BK) * 4096; };
@@ -812,6 +820,7 @@ TiledSizes tiled_sizes(const moe_cfg& c) {
 
 hipError_t launch_tile_weights(const moe_cfg& c, const moe_weights& src, void* w13, void* w2, void* sh13, void* sh2,
                                hipStream_t s) {
+    if (c.w_dtype == MOE_FP8_E4M3) return launch_tile_weights_e4m3(c, src, w13, w2, sh13, sh2, s);
     auto go = [&](const void* a, const void* b, int E, int rows, int K, int pair, void* dst) {
         const int groups = pair ? groups13(rows) : groups2(rows), KS = (K + BK - 1) / BK;
         const size_t n = (size_t)E * groups * KS * 256;

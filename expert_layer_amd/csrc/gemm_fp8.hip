@@ -1,43 +1,35 @@
-// gemm_fp8.hip -- the grouped SwiGLU FFN on fp8 (OCP e4m3) MFMA with fp32 block
-// scales, and on e4m3 rows with MXFP4 weights ("ASAP", section 3.4.2: the MoE
-// kernel is a grouped matrix multiplication of hidden states by the layer's
-// expert weights).  The operands
-// are e4m3 codes with one fp32 scale per 1 x 128 block of a row (activations,
-// h) and per 128 x 128 block (weights); a dequantised value is code * scale.
+// gemm_fp8.hip -- the grouped SwiGLU FFN on e4m3 rows with MXFP4 expert weights
+// ("ASAP", section 3.4.2: the MoE kernel is a grouped matrix multiplication of
+// hidden states by the layer's expert weights; the 4-bit expert weights of
+// "DWDP", appendix A4).  Rows are e4m3 codes with one fp32 scale per 1 x 128
+// block of a row (x, h); weights are OCP MX: E2M1 codes, one E8M0 scale per 32
+// elements of a row.  (e4m3 weights run in gemm_e4m3.hip.)
 //
-// Scale promotion.  A K block of 128 is exactly one v_mfma_f32_16x16x128_f8f6f4,
-// so every MFMA result t is the unscaled partial sum of one scale block and is
-// folded in as acc += t * (s_row * s_weight) on the VALU.  The MFMAs write VGPRs
-// (this file is compiled in the VGPR form), so the promotion reads t directly.
-// The weight fragment is the MFMA's first operand and the row fragment its
-// second, so a 16 x 16 result comes out transposed: lane l holds row l % 16 and
-// the four columns 4 (l / 16) + [0, 4), and one product s_row * s_weight serves
-// all four.
+// MFMA.  v_mfma_scale_f32_16x16x128_f8f6f4 in its FP4 x e4m3 form applies each
+// lane's E8M0 weight scale itself; a K block of 128 is one MFMA and one row
+// scale block, so every MFMA result t is folded in as acc += t * s_row on the
+// VALU (this file is compiled in the VGPR form).  The weight fragment is the
+// first operand and the row fragment the second, so a 16 x 16 result comes out
+// transposed: lane l holds row l % 16 and the four weight rows 4 (l / 16) +
+// [0, 4).
 //
-// Tile.  224 rows x 256 weight rows, 8 waves (two per SIMD); wave w owns rows
-// 112 (w / 4) + [0, 112) and weight rows 64 (w % 4) + [0, 64): 7 x 4 MFMA blocks
-// of 16 x 16 and their fp32 accumulators (112 VGPRs -- the promotion FMAs need
-// them in VALU registers).  224 rather than 256 rows is what lets three A
-// stages and two B stages fit in the 160 KiB of LDS.  Launches of small groups
-// take 128-row tiles.
-//
-// MXFP4 weights (W4; OCP MX: E2M1 codes, one E8M0 scale per 32 elements of a
-// row, the 4-bit expert weights of "DWDP", appendix A4).  The weight stage
-// halves to 64-byte rows plus a scale dword per row, the MFMA becomes the
-// scaled FP4 x e4m3 form that applies each lane's E8M0 scale itself, and the
-// smaller weight stages leave LDS for 256-row tiles.  GEMM1: the 64 weight
-// rows of a wave are 32 gate rows then the 32 up rows of the same h columns, so
-// h = silu(g) * u forms in registers; GEMM2: 64 output columns.
-// Pipeline.  K advances in stages of 128 through three A buffers [224 x 128 B |
-// 288 row scales] and two B buffers [256 x 128 B]; operands move HBM -> LDS by
-// buffer_load ... lds, both two stages ahead: A of stage s+2 at the start of
-// stage s (its buffer held stage s-1), B of stage s+2 as soon as every wave
-// has read its B fragments of stage s into registers.  Chunks outside the tile (rows past the
-// group's end, weight rows past N) carry an offset beyond their buffer
-// descriptor and load as zero.  LDS chunks of 16 B are XOR-swizzled by
-// (row & 7) ^ ((row >> 3) & 1): a 16-byte read is served eight lanes (128 B)
-// at a time, and the eight rows of such a group, at one logical chunk, land on
-// eight distinct 16-byte bank groups (so do the two row parities of 16 lanes).
+// Tile.  256 rows (128 for launches of small groups) x 256 weight rows, 8 waves
+// (two per SIMD); wave w owns rows TB / 2 (w / 4) + [0, TB / 2) and weight rows
+// 64 (w % 4) + [0, 64): TB / 32 x 4 MFMA blocks of 16 x 16 and their fp32
+// accumulators.  GEMM1: the 64 weight rows of a wave are 32 gate rows then the
+// 32 up rows of the same h columns, so h = silu(g) * u forms in registers;
+// GEMM2: 64 output columns.
+// Pipeline.  K advances in stages of 128 through three A buffers [256 x 128 B |
+// 288 row scales] and two weight buffers [256 x 64 B | 8 x 256 B of E8M0
+// scales]; operands move HBM -> LDS by buffer_load ... lds, both two stages
+// ahead: A of stage s+2 at the start of stage s (its buffer held stage s-1),
+// the weights of stage s+2 as soon as every wave has read its fragments of
+// stage s into registers.  Chunks outside the tile (rows past the group's end,
+// weight rows past N) carry an offset beyond their buffer descriptor and load
+// as zero.  A rows in LDS: 16-byte chunks XOR-swizzled by (row & 7) ^ ((row >>
+// 3) & 1), so a 16-byte read served eight lanes (128 B) at a time lands the
+// eight rows of a group, at one logical chunk, on eight distinct 16-byte bank
+// groups (so do the two row parities of 16 lanes).
 // GEMM1 epilogue: h is requantised per row and 128 columns -- the tile's 128 h
 // columns are one scale block: s = max|h| / 448 (1 for an all-zero block),
 // q = e4m3_rne_sat(h / s) -- staged through LDS and stored as 16-byte chunks.
@@ -46,64 +38,37 @@
 namespace moe {
 namespace {
 
-// BM: the tallest tile (it sizes the LDS); a launch runs tiles of TB = BM or
-// kFfnBmFp8Small rows (the template parameter TB below), a wave owning TB / 32
-// row blocks of 16.
-constexpr int BM = kFfnBmFp8, BN = 256, BK = 128, NTH = 512;
-constexpr int kChunksA = BM * 8;               // 16-byte chunks of A in one stage (the tallest tile)
-constexpr int kChunksB = BN * 8;               // ... of B
+// kBig: the tallest tile (it sizes the LDS); a launch runs tiles of TB = kBig
+// or kFfnBmFp8Small rows (the template parameter TB below), a wave owning
+// TB / 32 row blocks of 16.
+constexpr int kBig = 256, BN = 256, BK = 128, NTH = 512;
+constexpr int kChunksA = kBig * 8;             // 16-byte chunks of A in one stage
 constexpr int kStageA = kChunksA + 72;         // A, then 288 fp32 row scales (see scale_row)
-constexpr int kScaleB4 = BN * 4;               // MXFP4: chunks of a stage's weight codes; then 8 x 256 B of scales
-static_assert(BM % 32 == 0 && BM <= 224, "three A stages and two B stages must fit in 160 KiB of LDS");
-static_assert(kFfnBmFp8Small == 128, "the load slots below are laid out for 4 and 7 row blocks");
+constexpr int kScaleB4 = BN * 4;               // chunks of a stage's weight codes; then 8 x 256 B of scales
+constexpr int kChunksB = kScaleB4 + 128;
+static_assert(kFfnBmFp8Small == 128, "the load slots below are laid out for 4 and 8 row blocks");
 constexpr uint32_t kOOB = 0x80000000u;         // past every descriptor (all are < 2 GiB): the load returns zero
 
 typedef __attribute__((address_space(3))) void* lds_t;
 
+// The stage buffers (distinct objects, so that the compiler can tell which
+// buffer an in-flight LDS DMA writes); both tile heights use them.
 __shared__ i32x4 stgA0[kStageA];
 __shared__ i32x4 stgA1[kStageA];
 __shared__ i32x4 stgA2[kStageA];
 __shared__ i32x4 stgB0[kChunksB];
 __shared__ i32x4 stgB1[kChunksB];
 
-// MXFP4 tiles of kBig rows: with 17 KiB weight stages, three A stages of 256
-// rows fit beside the two weight stages (135 KiB), in buffers of their own.
-constexpr int kBig = 256;
-constexpr int kStageAW = kBig * 8 + 72;
-constexpr int kChunksBW = BN * 4 + 128;  // codes, then 8 x 256 B of scales
-__shared__ i32x4 stgA0w[kStageAW];
-__shared__ i32x4 stgA1w[kStageAW];
-__shared__ i32x4 stgA2w[kStageAW];
-__shared__ i32x4 stgB0w[kChunksBW];
-__shared__ i32x4 stgB1w[kChunksBW];
-
-// The stage buffers of a tile of TB rows (distinct objects per buffer).
-template <int BUF, int TB>
+template <int BUF>
 __device__ __forceinline__ i32x4* stgA() {
-    if constexpr (TB == kBig) {
-        if constexpr (BUF == 0) return stgA0w;
-        else if constexpr (BUF == 1) return stgA1w;
-        else return stgA2w;
-    } else {
-        if constexpr (BUF == 0) return stgA0;
-        else if constexpr (BUF == 1) return stgA1;
-        else return stgA2;
-    }
+    if constexpr (BUF == 0) return stgA0;
+    else if constexpr (BUF == 1) return stgA1;
+    else return stgA2;
 }
-template <int BUF, int TB>
+template <int BUF>
 __device__ __forceinline__ i32x4* stgB() {
-    if constexpr (TB == kBig) {
-        if constexpr (BUF == 0) return stgB0w;
-        else return stgB1w;
-    } else {
-        if constexpr (BUF == 0) return stgB0;
-        else return stgB1;
-    }
-}
-// 16-byte chunks of a stage's A rows: the row scales follow them
-template <int TB>
-constexpr int chunks_a() {
-    return (TB == kBig ? kBig : BM) * 8;
+    if constexpr (BUF == 0) return stgB0;
+    else return stgB1;
 }
 
 __device__ __forceinline__ void barrier_lds() { asm volatile("s_barrier" ::: "memory"); }
@@ -114,10 +79,6 @@ __device__ __forceinline__ int swz8(int row) { return (row & 7) ^ ((row >> 3) & 
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-__device__ __forceinline__ f32x4 mfma16x16x128_fp8(i32x8 a, i32x8 b) {
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
 }
 
 // FP4 (E2M1) first operand with the lane's E8M0 scale sw, e4m3 second operand
@@ -133,10 +94,10 @@ __device__ __forceinline__ f32x4 mfma16x16x128_fp4_fp8(i32x8 w4, i32x8 a8, int s
 struct Fp8Args {
     const uint8_t* a;       // GEMM1: x rows [rows][H]; GEMM2: h [rows][I]
     const float* a_scale;   // [rows][K / 128]
-    const uint8_t* w0;      // GEMM1: w_gate [E][I][H]; GEMM2: w_down [E][H][I]
-    const uint8_t* w1;      // GEMM1: w_up [E][I][H]
-    const float* s0;        // GEMM1: s_gate [E][I/128][H/128]; GEMM2: s_down [E][H/128][I/128]
-    const float* s1;        // GEMM1: s_up
+    const uint8_t* w0;      // GEMM1: w_gate [E][I][H/2]; GEMM2: w_down [E][H][I/2] (E2M1 pairs)
+    const uint8_t* w1;      // GEMM1: w_up [E][I][H/2]
+    const uint8_t* s0;      // E8M0: GEMM1 s_gate [E][I][H/32]; GEMM2 s_down [E][H][I/32]
+    const uint8_t* s1;      // GEMM1: s_up
     void* out;              // GEMM1: h [rows][I] e4m3; GEMM2: y [rows][H]
     float* out_scale;       // GEMM1: h scales [rows][I / 128]
     const int4* tiles;
@@ -171,129 +132,97 @@ struct Dma {
     int nsteps;  // K blocks
 };
 
-// Loads a wave issues per stage: 4 A chunk loads, the row scales, then 4 B
-// chunk loads (fp8) or 2 B chunk loads and the B scales (MXFP4).
-template <bool W4>
-constexpr int kLoads = W4 ? 8 : 9;
+// Loads a wave issues per stage: 4 A chunk loads, the row scales, then 2
+// weight chunk loads and the weight scales.
+constexpr int kLoads = 8;
 
 // A loads of stage t into A buffer BUF: 4 chunk loads per lane (8 LDS rows
 // each) and one row-scale load, the same 5 for every wave.  The tile's TB rows
-// take TB / 8 chunk loads (28 or 16); the remaining waves repeat the first
-// waves' loads, writing the same bytes to the same place.  Wave w loads the scales of rows 32 w + [0, 64): each row's
-// scale is written by two waves, again the same value, and rows past the tile
-// load zeros.  Every destination is an offset into the buffer itself, so the
-// compiler can tell the buffers apart while the loads are in flight.
+// take TB / 8 chunk loads (32 or 16); in 128-row tiles the second four waves
+// repeat the first four's loads, writing the same bytes to the same place.
+// Wave w loads the scales of rows 32 w + [0, 64): each row's scale is written
+// by two waves, again the same value, and rows past the tile load zeros.
+// Every destination is an offset into the buffer itself, so the compiler can
+// tell the buffers apart while the loads are in flight.
 //
-// Load J (0..8) of the 9 a wave issues per stage t: J < 4 the A chunk loads,
-// J = 4 the row-scale load (both into A buffer ABUF), J >= 5 the B chunk loads
-// into B buffer BBUF.  A load that is not real (a stage past the end, rows
+// Load J (0..7) of the 8 a wave issues per stage t: J < 4 the A chunk loads,
+// J = 4 the row-scale load (both into A buffer ABUF); J = 5, 6 fill the wave's
+// 32 weight rows of B buffer BBUF (a weight row of a stage is 64 bytes: four
+// chunks, swizzled by (row >> 2) & 3), 16 rows at a time, and J = 7 loads the
+// rows' E8M0 scales of the stage (one dword a row: the four 32-element blocks)
+// into the wave's 256-byte slot after the codes, lanes 32 .. 63 loading zeros
+// into its unused half.  A load that is not real (a stage past the end, rows
 // past the tile) carries an offset past its descriptor and loads zeros.
-//
-// MXFP4 weights (W4): a weight row of a stage is 64 bytes (four chunks, swizzled
-// by (row >> 2) & 3); J = 5, 6 fill the wave's 32 LDS rows, 16 at a time, and
-// J = 7 loads the rows' E8M0 scales of the stage (one dword a row: the four
-// 32-element blocks) into the wave's 256-byte slot after the codes, lanes
-// 32 .. 63 loading zeros into its unused half.
-template <int MODE, int ABUF, int BBUF, int J, int TB, bool W4>
+template <int MODE, int ABUF, int BBUF, int J, int TB>
 __device__ __forceinline__ void dma1(const Dma& d, int t, int wave) {
     const uint32_t k = (uint32_t)t * BK;
     const bool real = t < d.nsteps;
-    if constexpr (W4 && J >= 5) {
-        const __amdgpu_buffer_rsrc_t r = (MODE == 0 && (wave & 1)) ? d.rb1 : d.rb0;
-        if constexpr (J < 7) {
-            constexpr int i = J - 5;
-            const uint32_t off = (!real || d.vb[i] == kOOB) ? kOOB : d.vb[i] + k / 2;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_t)(stgB<BBUF, TB>() + (wave * 2 + i) * 64), 16, off, 0, 0,
-                                                     0);
-        } else {
-            const __amdgpu_buffer_rsrc_t rs = (MODE == 0 && (wave & 1)) ? d.rsb1 : d.rsb0;
-            const uint32_t off = (!real || d.vbs == kOOB) ? kOOB : d.vbs + (uint32_t)t * 4u;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_t)(stgB<BBUF, TB>() + kScaleB4 + wave * 16), 4, off, 0, 0,
-                                                     0);
-        }
-        return;
-    }
     if constexpr (J < 4) {
         const uint32_t off = (!real || d.va[J] == kOOB) ? kOOB : d.va[J] + k;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ra, (lds_t)(stgA<ABUF, TB>() + ((wave * 4 + J) % (TB / 8)) * 64), 16,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ra, (lds_t)(stgA<ABUF>() + ((wave * 4 + J) % (TB / 8)) * 64), 16,
                                                  off, 0, 0, 0);
     } else if constexpr (J == 4) {
         const uint32_t so = (!real || d.vs == kOOB) ? kOOB : d.vs + (uint32_t)t * 4u;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rs, (lds_t)(stgA<ABUF, TB>() + chunks_a<TB>() + wave * 8), 4, so, 0, 0, 0);
-    } else {
-        constexpr int i = J - 5;
-        const uint32_t off = (!real || d.vb[i] == kOOB) ? kOOB : d.vb[i] + k;
-        // GEMM1: wave w fills LDS rows 32 w + [0, 32): gate rows of quarter w / 2
-        // on even waves, up rows on odd waves
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rs, (lds_t)(stgA<ABUF>() + kChunksA + wave * 8), 4, so, 0, 0, 0);
+    } else if constexpr (J < 7) {
+        // GEMM1: even waves fill gate rows, odd waves the up rows of the same h columns
         const __amdgpu_buffer_rsrc_t r = (MODE == 0 && (wave & 1)) ? d.rb1 : d.rb0;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_t)(stgB<BBUF, TB>() + (wave * 4 + i) * 64), 16, off, 0, 0, 0);
+        constexpr int i = J - 5;
+        const uint32_t off = (!real || d.vb[i] == kOOB) ? kOOB : d.vb[i] + k / 2;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_t)(stgB<BBUF>() + (wave * 2 + i) * 64), 16, off, 0, 0, 0);
+    } else {
+        const __amdgpu_buffer_rsrc_t rs = (MODE == 0 && (wave & 1)) ? d.rsb1 : d.rsb0;
+        const uint32_t off = (!real || d.vbs == kOOB) ? kOOB : d.vbs + (uint32_t)t * 4u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_t)(stgB<BBUF>() + kScaleB4 + wave * 16), 4, off, 0, 0, 0);
     }
 }
 
 // The A loads (J = 0..4) of stage t into A buffer BUF.
-template <int MODE, int BUF, int TB, bool W4>
+template <int MODE, int BUF, int TB>
 __device__ __forceinline__ void dma_a(const Dma& d, int t, int wave) {
-    dma1<MODE, BUF, 0, 0, TB, W4>(d, t, wave);
-    dma1<MODE, BUF, 0, 1, TB, W4>(d, t, wave);
-    dma1<MODE, BUF, 0, 2, TB, W4>(d, t, wave);
-    dma1<MODE, BUF, 0, 3, TB, W4>(d, t, wave);
-    dma1<MODE, BUF, 0, 4, TB, W4>(d, t, wave);
+    dma1<MODE, BUF, 0, 0, TB>(d, t, wave);
+    dma1<MODE, BUF, 0, 1, TB>(d, t, wave);
+    dma1<MODE, BUF, 0, 2, TB>(d, t, wave);
+    dma1<MODE, BUF, 0, 3, TB>(d, t, wave);
+    dma1<MODE, BUF, 0, 4, TB>(d, t, wave);
 }
 
 // The B loads (J = 5 .. kLoads - 1) of stage t into B buffer BUF.
-template <int MODE, int BUF, int TB, bool W4>
+template <int MODE, int BUF, int TB>
 __device__ __forceinline__ void dma_b(const Dma& d, int t, int wave) {
-    dma1<MODE, 0, BUF, 5, TB, W4>(d, t, wave);
-    dma1<MODE, 0, BUF, 6, TB, W4>(d, t, wave);
-    dma1<MODE, 0, BUF, 7, TB, W4>(d, t, wave);
-    if constexpr (!W4) dma1<MODE, 0, BUF, 8, TB, W4>(d, t, wave);
+    dma1<MODE, 0, BUF, 5, TB>(d, t, wave);
+    dma1<MODE, 0, BUF, 6, TB>(d, t, wave);
+    dma1<MODE, 0, BUF, 7, TB>(d, t, wave);
 }
 
 // vmcnt(kLoads) with the other counters at zero: a stage's A and B loads and
 // everything before them have landed (the loads of the next stage may be in
 // flight), and every LDS read of this wave has returned.
-template <bool W4>
-__device__ __forceinline__ void wait_stage() { __builtin_amdgcn_s_waitcnt(kLoads<W4> | 0x0070); }
+__device__ __forceinline__ void wait_stage() { __builtin_amdgcn_s_waitcnt(kLoads | 0x0070); }
 
 __device__ __forceinline__ i32x8 cat(i32x4 lo, i32x4 hi) {
     return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// acc += t * s_row * s_weight for one row block: sa is this lane's row scale,
-// p0 the weight scale of column blocks 0, 1 (gate or down) and p1 of 2, 3 (up).
-__device__ __forceinline__ void promote(const f32x4 (&t)[4], float sa, float p0, float p1, f32x4 (&acc)[4]) {
-    const float q0 = sa * p0, q1 = sa * p1;
+// acc += t * s_row for one row block (the weight scales are applied by the
+// MFMA): sa is this lane's row scale.
+__device__ __forceinline__ void promote(const f32x4 (&t)[4], float sa, f32x4 (&acc)[4]) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        acc[0][j] = __builtin_fmaf(t[0][j], q0, acc[0][j]);
-        acc[1][j] = __builtin_fmaf(t[1][j], q0, acc[1][j]);
-        acc[2][j] = __builtin_fmaf(t[2][j], q1, acc[2][j]);
-        acc[3][j] = __builtin_fmaf(t[3][j], q1, acc[3][j]);
+        acc[0][j] = __builtin_fmaf(t[0][j], sa, acc[0][j]);
+        acc[1][j] = __builtin_fmaf(t[1][j], sa, acc[1][j]);
+        acc[2][j] = __builtin_fmaf(t[2][j], sa, acc[2][j]);
+        acc[3][j] = __builtin_fmaf(t[3][j], sa, acc[3][j]);
     }
 }
 
-// The B fragments of this wave (column blocks of 16 rows of weight rows
-// q * 64 ..) in stage buffer BUF.  A lane reads row (16 i + lane % 16) at
-// logical chunks 2 (lane / 16) and 2 (lane / 16) + 1; the swizzle of a row
-// depends on row % 16 only, so every fragment address is one of two per-lane
-// bases plus a constant.
-template <int BUF, int TB>
-__device__ __forceinline__ void read_b(int q, int lane, i32x8 (&b)[4]) {
-    const i32x4* buf = stgB<BUF, TB>();
-    const int l16 = lane & 15;
-    const int plo = (2 * (lane >> 4)) ^ swz8(l16), phi = plo ^ 1;
-    const int ib = ((q & 3) * 64 + l16) * 8;  // column block cb: + cb * 128
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) b[cb] = cat(buf[ib + cb * 128 + plo], buf[ib + cb * 128 + phi]);
-}
-
-// MXFP4: the FP4 fragment of column block cb is the lane's 32 elements of
+// The FP4 fragment of column block cb is the lane's 32 elements of
 // row (16 cb + lane % 16), K block lane / 16 of the stage: logical chunk
 // lane / 16 of the 64-byte LDS row, the low four dwords of the operand; its
 // E8M0 scale is byte lane / 16 of the row's scale dword.
 template <int BUF, int TB>
 __device__ __forceinline__ void read_b4(int q, int lane, i32x8 (&b)[4], int (&bs)[4]) {
-    const i32x4* buf = stgB<BUF, TB>();
+    const i32x4* buf = stgB<BUF>();
     const int l16 = lane & 15, g = lane >> 4;
     const int ib = ((q & 3) * 64 + l16) * 4 + (g ^ ((l16 >> 2) & 3));  // column block cb: + cb * 64
     const uint32_t* sc = reinterpret_cast<const uint32_t*>(buf + kScaleB4);
@@ -307,82 +236,78 @@ __device__ __forceinline__ void read_b4(int q, int lane, i32x8 (&b)[4], int (&bs
 }
 
 // The loads of stage t spread over the row blocks of a K stage, J after the
-// MFMAs of row block rb -- 7 row blocks: two after each of the first three,
-// one after each of the next three; 4 row blocks: three, then two after each
-// of the rest.  A wave that issues all 9 at once stalls until the texture unit
-// has taken them, and the other waves' loads are queued there too.
+// MFMAs of row block rb -- 8 row blocks: two after each of the first three,
+// one after each of the next two; 4 row blocks: three, two, two, one.  A wave that issues all 8 at once stalls until the texture unit has
+// taken them, and the other waves' loads are queued there too.
 template <int RBN, int NJ>
 constexpr int slot_start(int r) {
     const int j = RBN >= 6 ? (r < 3 ? 2 * r : r + 3) : (r == 0 ? 0 : 1 + 2 * r);
     return j < NJ ? j : NJ;
 }
-template <int MODE, int NA, int NB, int RBI, int TB, bool W4>
+template <int MODE, int NA, int NB, int RBI, int TB>
 __device__ __forceinline__ void dma_slot(const Dma& d, int t, int wave) {
-    constexpr int j0 = slot_start<TB / 32, kLoads<W4>>(RBI), j1 = slot_start<TB / 32, kLoads<W4>>(RBI + 1);
-    if constexpr (j0 < j1) dma1<MODE, NA, NB, j0, TB, W4>(d, t, wave);
-    if constexpr (j0 + 1 < j1) dma1<MODE, NA, NB, j0 + 1, TB, W4>(d, t, wave);
-    if constexpr (j0 + 2 < j1) dma1<MODE, NA, NB, j0 + 2, TB, W4>(d, t, wave);
+    constexpr int j0 = slot_start<TB / 32, kLoads>(RBI), j1 = slot_start<TB / 32, kLoads>(RBI + 1);
+    if constexpr (j0 < j1) dma1<MODE, NA, NB, j0, TB>(d, t, wave);
+    if constexpr (j0 + 1 < j1) dma1<MODE, NA, NB, j0 + 1, TB>(d, t, wave);
+    if constexpr (j0 + 2 < j1) dma1<MODE, NA, NB, j0 + 2, TB>(d, t, wave);
 }
 
 // One K stage for the RB row blocks of 16 starting at tile row r0: every (row
-// block, column block) MFMA of this wave, promoted with the stage's row scales
-// and the wave's weight-block scales p0 (gate or down columns) and p1 (up
-// columns), with the loads of stage t into A buffer NA and B buffer NB issued
+// block, column block) MFMA of this wave, promoted with the stage's row
+// scales, with the loads of stage t into A buffer NA and B buffer NB issued
 // between them.  Software-pipelined over row blocks: while the four MFMAs of
 // row block rb run, the fragments of rb + 1 are read and rb - 1 is promoted.
-//
-// MXFP4 (W4): the weight operand is FP4 with its E8M0 scales bs applied by the
-// MFMA, and the row fragment takes chunks lane / 16 and lane / 16 + 4 of the
-// row (the K order of the e4m3 operand above); p0 = p1 = 1.
-template <int MODE, int BUF, int NA, int NB, int TB, bool W4>
+// The weight operand is FP4 with its E8M0 scales bs applied by the MFMA; the
+// row fragment takes chunks lane / 16 and lane / 16 + 4 of the row (the K
+// order the FP4 x e4m3 form expects).
+template <int MODE, int BUF, int NA, int NB, int TB>
 __device__ __forceinline__ void kstep(const Dma& d, int t_stage, int wave, int r0, int lane, const i32x8 (&b)[4],
-                                      const int (&bs)[4], float p0, float p1, f32x4 (&acc)[TB / 32][4]) {
+                                      const int (&bs)[4], f32x4 (&acc)[TB / 32][4]) {
     constexpr int RB = TB / 32;
     // Every access indexes the stage buffer itself (an integer base plus a
     // constant), so the compiler can tell it from the DMA in flight into the
     // other buffers and adds no wait for it.
-    const i32x4* buf = stgA<BUF, TB>();
+    const i32x4* buf = stgA<BUF>();
     const int l16 = lane & 15;
-    const int plo = (W4 ? (lane >> 4) : 2 * (lane >> 4)) ^ swz8(l16);
-    const int phi = W4 ? ((lane >> 4) + 4) ^ swz8(l16) : plo ^ 1;
+    const int plo = (lane >> 4) ^ swz8(l16);
+    const int phi = ((lane >> 4) + 4) ^ swz8(l16);
     const int ia = (r0 + l16) * 8;                      // row block rb: + rb * 128
     // this lane's row scales: row blocks 0..3 in chunk 32 h + l16, 4..7 in 32 h + 16 + l16
-    const int is = chunks_a<TB>() + (r0 / (TB / 2)) * 32 + l16;
+    const int is = kChunksA + (r0 / (TB / 2)) * 32 + l16;
     const f32x4 sa_lo = __builtin_bit_cast(f32x4, buf[is]), sa_hi = __builtin_bit_cast(f32x4, buf[is + 16]);
     auto sa = [&](int rb) { return rb < 4 ? sa_lo[rb & 3] : sa_hi[rb & 3]; };
     i32x8 a[2];
     f32x4 t[2][4];
     a[0] = cat(buf[ia + plo], buf[ia + phi]);
     __builtin_amdgcn_sched_barrier(0);
-    static_assert(RB == 4 || RB == 7 || RB == 8, "the load slots are laid out for 4, 7 and 8 row blocks");
+    static_assert(RB == 4 || RB == 8, "the load slots are laid out for 4 and 8 row blocks");
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
-            if constexpr (W4) t[rb & 1][cb] = mfma16x16x128_fp4_fp8(b[cb], a[rb & 1], bs[cb]);
-            else t[rb & 1][cb] = mfma16x16x128_fp8(b[cb], a[rb & 1]);
+            t[rb & 1][cb] = mfma16x16x128_fp4_fp8(b[cb], a[rb & 1], bs[cb]);
         }
         switch (rb) {  // rb is a constant here: the loop is unrolled
-            case 0: dma_slot<MODE, NA, NB, 0, TB, W4>(d, t_stage, wave); break;
-            case 1: dma_slot<MODE, NA, NB, 1, TB, W4>(d, t_stage, wave); break;
-            case 2: dma_slot<MODE, NA, NB, 2, TB, W4>(d, t_stage, wave); break;
-            case 3: dma_slot<MODE, NA, NB, 3, TB, W4>(d, t_stage, wave); break;
-            case 4: dma_slot<MODE, NA, NB, 4, TB, W4>(d, t_stage, wave); break;
-            case 5: dma_slot<MODE, NA, NB, 5, TB, W4>(d, t_stage, wave); break;
+            case 0: dma_slot<MODE, NA, NB, 0, TB>(d, t_stage, wave); break;
+            case 1: dma_slot<MODE, NA, NB, 1, TB>(d, t_stage, wave); break;
+            case 2: dma_slot<MODE, NA, NB, 2, TB>(d, t_stage, wave); break;
+            case 3: dma_slot<MODE, NA, NB, 3, TB>(d, t_stage, wave); break;
+            case 4: dma_slot<MODE, NA, NB, 4, TB>(d, t_stage, wave); break;
+            case 5: dma_slot<MODE, NA, NB, 5, TB>(d, t_stage, wave); break;
             default: break;
         }
         if (rb + 1 < RB) a[(rb + 1) & 1] = cat(buf[ia + (rb + 1) * 128 + plo], buf[ia + (rb + 1) * 128 + phi]);
-        if (rb > 0) promote(t[(rb - 1) & 1], sa(rb - 1), p0, p1, acc[rb - 1]);
+        if (rb > 0) promote(t[(rb - 1) & 1], sa(rb - 1), acc[rb - 1]);
         __builtin_amdgcn_sched_barrier(0);
     }
-    promote(t[(RB - 1) & 1], sa(RB - 1), p0, p1, acc[RB - 1]);
+    promote(t[(RB - 1) & 1], sa(RB - 1), acc[RB - 1]);
 }
 
 // Rows of a tile past the group's end load as zero and are computed like the
 // others (also by a wave whose half of the tile holds no row: its MFMAs carry
 // the stage's loads, and one load schedule for every wave keeps the compiler's
 // count of loads in flight exact).
-template <int MODE, int TB, bool W4>
+template <int MODE, int TB>
 __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int M, int n0) {
     constexpr int RB = TB / 32;
     const int lane = threadIdx.x & 63;
@@ -390,7 +315,6 @@ __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int 
     const int mh = wave >> 2, q = wave & 3, r0 = mh * (TB / 2);
     const int K = p.K, N = p.N;
     const int KB = K / BK;  // K and N are multiples of 128
-    const int NB = N / BK;
     Dma d;
     d.nsteps = KB;
     // ---- A rows row0 .. row0 + M and their row scales; indexed (GEMM1 of the
@@ -420,88 +344,53 @@ __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int 
     // rows 32 j + [0, 32) then the up rows of the same h columns); GEMM2 the
     // weight rows n0 + [0, 256)
     const int nlim = MODE == 0 ? min(N - n0, 128) : min(N - n0, BN);
-    // this group's matrices and block scales, and its index in them
+    // this group's codes and E8M0 scales, and its index in them
     const uint8_t *w0 = p.w0, *w1 = p.w1;
-    const float *s0 = p.s0, *s1 = p.s1;
+    const uint8_t *s0 = p.s0, *s1 = p.s1;
     int ge = g;
     if (p.wt.tab) {
         const int lay = *p.wt.layer;
         w0 = static_cast<const uint8_t*>(wtab_ptr(p.wt, lay, g, p.slot0));
-        s0 = static_cast<const float*>(wtab_ptr(p.wt, lay, g, p.slot0 + 3));
+        s0 = static_cast<const uint8_t*>(wtab_ptr(p.wt, lay, g, p.slot0 + 3));
         if (MODE == 0) {
             w1 = static_cast<const uint8_t*>(wtab_ptr(p.wt, lay, g, p.slot1));
-            s1 = static_cast<const float*>(wtab_ptr(p.wt, lay, g, p.slot1 + 3));
+            s1 = static_cast<const uint8_t*>(wtab_ptr(p.wt, lay, g, p.slot1 + 3));
         }
         ge = 0;
     }
-    const int KW = W4 ? K / 2 : K;  // bytes of a weight row
+    const int KW = K / 2;  // bytes of a weight row
     const size_t mat = (size_t)N * KW;
     d.rb0 = make_rsrc(w0 + (size_t)ge * mat + (size_t)n0 * KW, (uint32_t)nlim * (uint32_t)KW);
     d.rb1 = MODE == 0 ? make_rsrc(w1 + (size_t)ge * mat + (size_t)n0 * KW, (uint32_t)nlim * (uint32_t)KW) : d.rb0;
+    // A loads i: LDS row 32 wave + 8 i + lane / 8 (modulo TB), physical chunk
+    // lane % 8 holding logical chunk (lane % 8) ^ swz8(row)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int row = wave * 32 + i * 8 + (lane >> 3);  // LDS row this lane fills (B; A modulo TB)
-        const int arow = row % TB;
-        const uint32_t logical = (uint32_t)(((lane & 7) ^ swz8(row)) * 16);
+        const int arow = (wave * 32 + i * 8 + (lane >> 3)) % TB;
         const int ar = a_row(arow);
         d.va[i] = ar >= 0 ? (uint32_t)ar * (uint32_t)K + (uint32_t)(((lane & 7) ^ swz8(arow)) * 16) : kOOB;
-        const int wrow = MODE == 0 ? (wave >> 1) * 32 + i * 8 + (lane >> 3) : row;  // relative to n0
-        d.vb[i] = wrow < nlim ? (uint32_t)wrow * (uint32_t)K + logical : kOOB;
     }
-    if constexpr (W4) {
-        // B loads i = 0, 1: LDS rows 32 wave + 16 i + lane / 4, physical chunk
-        // lane % 4 holding logical chunk (lane % 4) ^ ((row >> 2) & 3)
+    // B loads i = 0, 1: LDS rows 32 wave + 16 i + lane / 4, physical chunk
+    // lane % 4 holding logical chunk (lane % 4) ^ ((row >> 2) & 3); GEMM1: even
+    // waves the gate rows, odd waves the up rows of h columns 32 (wave / 2) ..
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int row = wave * 32 + i * 16 + (lane >> 2);
-            const int wrow = MODE == 0 ? (wave >> 1) * 32 + i * 16 + (lane >> 2) : row;
-            const uint32_t logical = (uint32_t)(((lane & 3) ^ ((row >> 2) & 3)) * 16);
-            d.vb[i] = wrow < nlim ? (uint32_t)wrow * (uint32_t)KW + logical : kOOB;
-        }
-        // E8M0 scales [rows][K / 32]: lane < 32 loads the stage's dword of LDS row 32 wave + lane
-        const uint8_t* sb0 = reinterpret_cast<const uint8_t*>(s0);
-        const uint8_t* sb1 = reinterpret_cast<const uint8_t*>(MODE == 0 ? s1 : s0);
+    for (int i = 0; i < 2; ++i) {
+        const int row = wave * 32 + i * 16 + (lane >> 2);
+        const int wrow = MODE == 0 ? (wave >> 1) * 32 + i * 16 + (lane >> 2) : row;  // relative to n0
+        const uint32_t logical = (uint32_t)(((lane & 3) ^ ((row >> 2) & 3)) * 16);
+        d.vb[i] = wrow < nlim ? (uint32_t)wrow * (uint32_t)KW + logical : kOOB;
+    }
+    // E8M0 scales [rows][K / 32]: lane < 32 loads the stage's dword of LDS row 32 wave + lane
+    {
+        const uint8_t* sb1 = MODE == 0 ? s1 : s0;
         const size_t smat = (size_t)N * (K / 32);
-        d.rsb0 = make_rsrc(sb0 + (size_t)ge * smat + (size_t)n0 * (K / 32), (uint32_t)nlim * (uint32_t)(K / 32));
+        d.rsb0 = make_rsrc(s0 + (size_t)ge * smat + (size_t)n0 * (K / 32), (uint32_t)nlim * (uint32_t)(K / 32));
         d.rsb1 = MODE == 0 ? make_rsrc(sb1 + (size_t)ge * smat + (size_t)n0 * (K / 32),
                                        (uint32_t)nlim * (uint32_t)(K / 32))
                            : d.rsb0;
         const int wrow = MODE == 0 ? (wave >> 1) * 32 + lane : wave * 32 + lane;
         d.vbs = (lane < 32 && wrow < nlim) ? (uint32_t)wrow * (uint32_t)(K / 32) : kOOB;
     }
-    // weight-block scales of this wave's columns for every K block, lane kb % 64
-    // of register kb / 64 holding block kb (K <= 16384): loaded once, then read
-    // with readlane, so no vector-memory load besides the DMA runs in the K loop
-    int wbase = -1;
-    if (W4) {
-        // MXFP4: the weight scales are applied by the MFMA
-    } else if (MODE == 0) {
-        wbase = (ge * NB + n0 / BK) * KB;
-    } else {
-        // a wave whose 64 columns lie past N (N not a multiple of 256) reads no scale
-        const int cbk = (n0 + q * 64) / BK;
-        if (cbk < NB) wbase = (ge * NB + cbk) * KB;
-    }
-    float ws0[2] = {0.f, 0.f}, ws1[2] = {0.f, 0.f};
-    if (wbase >= 0) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int kb = h * 64 + lane;
-            if (kb < KB) {
-                ws0[h] = s0[wbase + kb];
-                ws1[h] = MODE == 0 ? s1[wbase + kb] : ws0[h];
-            }
-        }
-    }
-    auto wscale = [&](int kb, float& p0, float& p1) {
-        if constexpr (W4) {
-            p0 = p1 = 1.0f;
-            return;
-        }
-        const int h = kb >> 6, l = kb & 63;
-        p0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(h ? ws0[1] : ws0[0]), l));
-        p1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(h ? ws1[1] : ws1[0]), l));
-    };
 
     f32x4 acc[RB][4];
 #pragma unroll
@@ -512,25 +401,22 @@ __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int 
     // Stage s uses A buffer s % 3 and B buffer s % 2; the loop body is the six
     // stages of one period of both rings and leaves after stage KB - 1.  Loads
     // of stages past the end carry zeros.  Issue order: A0, B0, A1, B1, then per
-    // stage s, during its MFMAs: A(s+2) (5 loads), B(s+2) (4).
-    dma_a<MODE, 0, TB, W4>(d, 0, wave);
-    dma_b<MODE, 0, TB, W4>(d, 0, wave);
-    dma_a<MODE, 1, TB, W4>(d, 1, wave);
-    dma_b<MODE, 1, TB, W4>(d, 1, wave);
+    // stage s, during its MFMAs: A(s+2) (5 loads), B(s+2) (3).
+    dma_a<MODE, 0, TB>(d, 0, wave);
+    dma_b<MODE, 0, TB>(d, 0, wave);
+    dma_a<MODE, 1, TB>(d, 1, wave);
+    dma_b<MODE, 1, TB>(d, 1, wave);
     i32x8 b[4];
     int bs[4] = {127, 127, 127, 127};
     int s = 0;
     auto stage = [&](auto ab, auto bb) {
         constexpr int AB = decltype(ab)::value, BB = decltype(bb)::value;
-        float p0, p1;
-        wscale(s, p0, p1);
-        wait_stage<W4>();  // stage s has landed (this wave's loads); this wave's reads of stage s-1 are done
+        wait_stage();  // stage s has landed (this wave's loads); this wave's reads of stage s-1 are done
         barrier_lds();     // ... every wave's: A buffer (s+2) % 3 is free
-        if constexpr (W4) read_b4<BB, TB>(q, lane, b, bs);
-        else read_b<BB, TB>(q, lane, b);
+        read_b4<BB, TB>(q, lane, b, bs);
         wait_lgkm0();
         barrier_lds();  // every wave holds its B fragments of stage s: B buffer s % 2 is free
-        kstep<MODE, AB, (AB + 2) % 3, BB, TB, W4>(d, s + 2, wave, r0, lane, b, bs, p0, p1, acc);
+        kstep<MODE, AB, (AB + 2) % 3, BB, TB>(d, s + 2, wave, r0, lane, b, bs, acc);
     };
     using C0 = std::integral_constant<int, 0>;
     using C1 = std::integral_constant<int, 1>;
@@ -572,15 +458,15 @@ __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int 
             rmax[rb] = m;
         }
         // per-row maxima of the four quarters' 32 columns -> LDS [4][256]
-        float* red = reinterpret_cast<float*>(stgA<0, TB>());
+        float* red = reinterpret_cast<float*>(stgA<0>());
         if (lane < 16)
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) red[q * 256 + r0 + rb * 16 + l16] = rmax[rb];
         __syncthreads();
-        // [BM rows][128 columns] e4m3, 32 words a row, the 16-byte chunk c of row r
+        // [TB rows][128 columns] e4m3, 32 words a row, the 16-byte chunk c of row r
         // at chunk c ^ ((r >> 1) & 7): a 4-byte store of 16 rows x 4 words then
         // touches 64 distinct banks
-        uint32_t* qs = reinterpret_cast<uint32_t*>(TB == kBig ? stgA<1, TB>() : stgB<0, TB>());
+        uint32_t* qs = reinterpret_cast<uint32_t*>(stgA<1>());
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
             const int row = r0 + rb * 16 + l16;
@@ -593,7 +479,7 @@ __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int 
                 for (int j = 0; j < 4; ++j) w |= (uint32_t)f32_to_e4m3(acc[rb][c][j] / sc) << (8 * j);
                 qs[row * 32 + (((q * 2 + c) ^ ((row >> 1) & 7)) << 2) + (lane >> 4)] = w;
             }
-            if (q == 0 && lane < 16 && row < M) p.out_scale[(size_t)(row0 + row) * NB + n0 / BK] = sc;
+            if (q == 0 && lane < 16 && row < M) p.out_scale[(size_t)(row0 + row) * (N / BK) + n0 / BK] = sc;
         }
         __syncthreads();
         // coalesced 16-byte stores of the tile's M rows x 128 h columns
@@ -611,7 +497,7 @@ __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int 
         // read group touch distinct banks; then every lane stores 4 columns
         // (8 B bf16 / 16 B fp32).  LDS operations of one wave are processed in
         // order.
-        float* st = reinterpret_cast<float*>((TB == kBig ? stgA<1, TB>() : stgB<0, TB>()) + wave * 256);
+        float* st = reinterpret_cast<float*>(stgA<1>() + wave * 256);
         const int cw = n0 + q * 64;  // first output column of this wave
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
@@ -645,7 +531,7 @@ __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int 
     }
 }
 
-template <int MODE, int TB, bool W4>
+template <int MODE, int TB>
 __global__ void __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2, 2)))
 ffn_gemm_fp8(Fp8Args p) {
     const int L = xcd_remap(blockIdx.x, p.n_tiles[0] * p.NT);
@@ -656,19 +542,14 @@ ffn_gemm_fp8(Fp8Args p) {
     const int g = td.x, row0 = td.y, M = td.z - td.y;
     const int n0 = MODE == 0 ? wl.y * (BN / 2) : wl.y * BN;
     if (n0 >= p.N || M <= 0) return;
-    run_tile<MODE, TB, W4>(p, g, row0, M, n0);
+    run_tile<MODE, TB>(p, g, row0, M, n0);
 }
 
 template <int MODE>
-void launch_one(int tb, bool w4, int64_t grid, const Fp8Args& a, hipStream_t s) {
+void launch_one(int tb, int64_t grid, const Fp8Args& a, hipStream_t s) {
     const dim3 gr((unsigned)grid), bl(NTH);
-    if (w4) {
-        if (tb == kFfnBmFp8Small) hipLaunchKernelGGL((ffn_gemm_fp8<MODE, kFfnBmFp8Small, true>), gr, bl, 0, s, a);
-        else hipLaunchKernelGGL((ffn_gemm_fp8<MODE, kBig, true>), gr, bl, 0, s, a);
-    } else {
-        if (tb == kFfnBmFp8Small) hipLaunchKernelGGL((ffn_gemm_fp8<MODE, kFfnBmFp8Small, false>), gr, bl, 0, s, a);
-        else hipLaunchKernelGGL((ffn_gemm_fp8<MODE, BM, false>), gr, bl, 0, s, a);
-    }
+    if (tb == kFfnBmFp8Small) hipLaunchKernelGGL((ffn_gemm_fp8<MODE, kFfnBmFp8Small>), gr, bl, 0, s, a);
+    else hipLaunchKernelGGL((ffn_gemm_fp8<MODE, kBig>), gr, bl, 0, s, a);
 }
 
 }  // namespace
@@ -677,15 +558,15 @@ hipError_t launch_gemm_fp8(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_c
                            const float* x_scale, const int32_t* row_src, const int32_t* offsets,
                            const moe_weights& w, const WTab& wt, void* y_rows, const FfnWork& wk, void* h,
                            float* h_scale, hipStream_t s) {
-    // Tile height: groups of about 256 rows or fewer (the DeepSeek-V3 layer's
-    // 256 experts, 8 rows a token) fill 128-row tiles; a 224-row tile would
-    // split them into two 128-row tiles and compute 224 rows of each.
-    // MXFP4 weights leave LDS for 256-row tiles, so groups of about 256 rows
-    // take one tile instead of two, halving their weight traffic.
+    if (c.w_dtype != MOE_FP4_E2M1)  // e4m3 weights
+        return launch_gemm_e4m3(c, max_tiles, n_rows_cap, x_rows, x_scale, row_src, offsets, w, wt, y_rows, wk, h,
+                                h_scale, s);
+    // Tile height: 256 rows, so a group of about 256 rows (the DeepSeek-V3
+    // layer's 256 experts, 8 rows a token) streams its weights once; launches
+    // whose groups average under about 136 rows take 128-row tiles.
     const int G = c.E + (c.has_shared ? 1 : 0);
-    const bool w4 = c.w_dtype == MOE_FP4_E2M1;  // MXFP4 weights, e4m3 rows
-    const bool small = n_rows_cap <= (int64_t)G * (w4 ? 136 : 272);
-    const int tb = small ? kFfnBmFp8Small : (w4 ? kBig : BM);
+    const bool small = n_rows_cap <= (int64_t)G * 136;
+    const int tb = small ? kFfnBmFp8Small : kBig;
     hipError_t e0 = launch_build_tiles(c, offsets, tb, n_rows_cap, wk, s);
     if (e0 != hipSuccess) return e0;
     Fp8Args a{};
@@ -704,14 +585,14 @@ hipError_t launch_gemm_fp8(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_c
     a.a_rows = c.T;
     a.w0 = static_cast<const uint8_t*>(w.w_gate);
     a.w1 = static_cast<const uint8_t*>(w.w_up);
-    a.s0 = w.s_gate;
-    a.s1 = w.s_up;
+    a.s0 = reinterpret_cast<const uint8_t*>(w.s_gate);
+    a.s1 = reinterpret_cast<const uint8_t*>(w.s_up);
     a.out = h;
     a.out_scale = h_scale;
     a.K = c.H;
     a.N = c.I;
     const int64_t grid1 = xcd_grid(max_tiles * wk.nt1);
-    launch_one<0>(tb, w4, grid1, a, s);
+    launch_one<0>(tb, grid1, a, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // GEMM2: down projection of h
@@ -723,7 +604,7 @@ hipError_t launch_gemm_fp8(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_c
     a.w0 = static_cast<const uint8_t*>(w.w_down);
     a.w1 = nullptr;
     a.slot0 = 2;
-    a.s0 = w.s_down;
+    a.s0 = reinterpret_cast<const uint8_t*>(w.s_down);
     a.s1 = nullptr;
     a.out = y_rows;
     a.out_scale = nullptr;
@@ -731,7 +612,7 @@ hipError_t launch_gemm_fp8(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_c
     a.N = c.H;
     a.out_f32 = c.y_dtype == MOE_F32 ? 1 : 0;
     const int64_t grid2 = xcd_grid(max_tiles * wk.nt2);
-    launch_one<1>(tb, w4, grid2, a, s);
+    launch_one<1>(tb, grid2, a, s);
     return hipGetLastError();
 }
 

@@ -289,6 +289,22 @@ def test_weight_table_host_addresses():
     for e in range(E):
         assert t8[e * 6:(e + 1) * 6] == [base[0] + e * I * H, base[1] + e * I * H, base[2] + e * I * H,
                                          base[3] + e * nsc, base[4] + e * nsc, base[5] + e * nsc]
+    # tiled e4m3: the merged gate+up matrix (2 I rows) and the down matrix keep
+    # the row-major byte counts; the scale entries are the caller's arrays
+    assert m.moe_tiled_weights_bytes(f8) == E * 3 * I * H
+    f8s = m.make_cfg(T=8, H=H, E=E, k=1, I=I, w_dtype=m.MOE_FP8_E4M3, has_shared=True, I_shared=Ish)
+    # each of the four matrices starts on a 256-byte boundary
+    al = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    assert m.moe_tiled_weights_bytes(f8s) == al(E * 2 * I * H) + al(E * I * H) + al(2 * Ish * H) + al(Ish * H)
+    t8t = m.moe_weight_table(f8, [m.moe_weights(w_gate=base[0], w_down=base[2], s_gate=base[3], s_up=base[4],
+                                                s_down=base[5], layout=m.MOE_LAYOUT_TILED)])
+    for e in range(E):
+        assert t8t[e * 6:(e + 1) * 6] == [base[0] + e * 2 * I * H, 0, base[2] + e * I * H,
+                                          base[3] + e * nsc, base[4] + e * nsc, base[5] + e * nsc]
+    # MXFP4 weights have no tiled layout
+    f4 = m.make_cfg(T=8, H=H, E=E, k=1, I=I, w_dtype=m.MOE_FP4_E2M1)
+    assert m.moe_tiled_weights_bytes(f4) == ctypes.c_size_t(-1).value
+    assert "bf16 or e4m3" in m.moe_last_error()
     # refusals
     f32 = m.make_cfg(T=8, H=H, E=E, k=1, I=I, act_dtype=m.MOE_F32)
     with pytest.raises(m.MoeError) as ex:

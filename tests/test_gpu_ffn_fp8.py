@@ -53,7 +53,7 @@ def _inputs(E, H, I, n_rows, seed, device):
     return s, wq, stack, xq, xs
 
 
-def _run(E, H, I, counts, ydt, extra_rows, seed):
+def _run(E, H, I, counts, ydt, extra_rows, seed, wlayout=moe.MOE_LAYOUT_ROWMAJOR):
     d = dev()
     n = int(sum(counts))
     cap = n + extra_rows
@@ -66,8 +66,12 @@ def _run(E, H, I, counts, ydt, extra_rows, seed):
     y = torch.full((max(cap, 1), H), sentinel, dtype=ytd, device=d)
     ws = moe.workspace(c, moe.MOE_STAGE_FFN, d, n_rows_cap=cap)
     w = moe.weights(wg, wu, wd, s_gate=sg, s_up=su, s_down=sd)
+    keep = None
+    if wlayout == moe.MOE_LAYOUT_TILED:
+        w, keep = moe.tile_weights(c, w, d)
     moe.moe_grouped_ffn(c, cap, xq, xs, offs, w, None, y, None, ws)
     torch.cuda.synchronize()
+    del keep
     return wq, xq, xs, y, sentinel
 
 
@@ -120,9 +124,10 @@ def _check_rows(wq, xq, xs, y, rows_by_expert):
     (1024, 512, [600], moe.MOE_BF16, 0),                          # one expert over 3 M tiles
     (256, 128, [1, 1, 1, 1], moe.MOE_F32, 5),                     # single rows
 ])
-def test_grouped_ffn_fp8_matches_oracle(H, I, counts, ydt, extra):
+@pytest.mark.parametrize("wlayout", [moe.MOE_LAYOUT_ROWMAJOR, moe.MOE_LAYOUT_TILED])
+def test_grouped_ffn_fp8_matches_oracle(H, I, counts, ydt, extra, wlayout):
     E = len(counts)
-    wq, xq, xs, y, sentinel = _run(E, H, I, counts, ydt, extra, seed=H + 7 * I)
+    wq, xq, xs, y, sentinel = _run(E, H, I, counts, ydt, extra, seed=H + 7 * I, wlayout=wlayout)
     oc = np.concatenate([[0], np.cumsum(counts)]).astype(int)
     rows = {e: list(range(oc[e], oc[e + 1])) for e in range(E)}
     err, rms, flipped = _check_rows(wq, xq, xs, y, rows)
@@ -132,10 +137,12 @@ def test_grouped_ffn_fp8_matches_oracle(H, I, counts, ydt, extra):
         assert torch.all(y[oc[-1]:] == torch.tensor(sentinel, dtype=y.dtype, device=y.device))
 
 
-def test_grouped_ffn_fp8_full_size_sampled():
+@pytest.mark.parametrize("wlayout", [moe.MOE_LAYOUT_TILED, moe.MOE_LAYOUT_ROWMAJOR])
+def test_grouped_ffn_fp8_full_size_sampled(wlayout):
     """The c5 workload: 65536 dispatched rows over 8 experts (Zipf(1.0) counts),
-    H = 7168, I = 2048, bf16 output; the oracle checks at least 512 seeded rows
-    spread over every expert, including each expert's first and last row."""
+    H = 7168, I = 2048, bf16 output, weights tiled (as timed) or row-major; the
+    oracle checks at least 512 seeded rows spread over every expert, including
+    each expert's first and last row."""
     s = synth.config("c5_dsv3_ep_fp8")
     counts = synth.fp8_counts(s)
     assert sum(counts) == s.T
@@ -148,8 +155,12 @@ def test_grouped_ffn_fp8_full_size_sampled():
     y = torch.empty((s.T, s.H), dtype=torch.bfloat16, device=d)
     ws = moe.workspace(c, moe.MOE_STAGE_FFN, d, n_rows_cap=s.T)
     w = moe.weights(wg, wu, wd, s_gate=sg, s_up=su, s_down=sd)
+    keep = None
+    if wlayout == moe.MOE_LAYOUT_TILED:
+        w, keep = moe.tile_weights(c, w, d)
     moe.moe_grouped_ffn(c, s.T, xq, xs, offs, w, None, y, None, ws)
     torch.cuda.synchronize()
+    del keep
     rng = np.random.default_rng(s.seed)
     oc = np.concatenate([[0], np.cumsum(counts)]).astype(int)
     # at least 512 rows: every expert's first and last row, the rest seeded
@@ -163,6 +174,20 @@ def test_grouped_ffn_fp8_full_size_sampled():
     err, rms, flipped = _check_rows(wq, xq, xs, y, rows)
     print(f"c5: {sum(len(r) for r in rows.values())} rows, max {err:.3e}, rms {rms:.3e}, {flipped} resolved")
     assert err <= TOL and rms <= TOL_RMS_BF16, (err, rms, flipped)
+
+
+def test_tiled_e4m3_weights_equal_rowmajor():
+    """moe_tile_weights only moves the e4m3 codes into the order in which a
+    wave loads its MFMA fragments; the kernel sums the same products in the
+    same order either way, so y is bit-identical (fp32 and bf16 outputs, a
+    partial GEMM2 N tile, tiles of 1 .. 8 row units)."""
+    d = dev()
+    for H, I, counts in ((640, 384, [300, 17, 0, 260, 33]), (1152, 256, [512, 1])):
+        for ydt in (moe.MOE_F32, moe.MOE_BF16):
+            ys = [_run(len(counts), H, I, counts, ydt, 0, seed=H + I, wlayout=wl)[3]
+                  for wl in (moe.MOE_LAYOUT_ROWMAJOR, moe.MOE_LAYOUT_TILED)]
+            assert torch.equal(ys[0].view(torch.int16 if ydt == moe.MOE_BF16 else torch.int32),
+                               ys[1].view(torch.int16 if ydt == moe.MOE_BF16 else torch.int32)), (H, I, ydt)
 
 
 @pytest.mark.parametrize("wfmt", ["e4m3", "mxfp4"])

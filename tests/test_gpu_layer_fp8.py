@@ -96,13 +96,15 @@ def _small_shape():
     return synth.config("c3_dsv3_bf16").with_(H=512, I=256, E=16, k=4, n_groups=4, topk_groups=2, I_shared=384)
 
 
-@pytest.mark.parametrize("shape,T,ydt", [
-    ("small", 77, moe.MOE_F32),
-    ("small", 77, moe.MOE_BF16),
-    ("c3", 24, moe.MOE_BF16),          # DeepSeek-V3 dimensions: 256 fp8 experts and the shared one
-    ("c4", 48, moe.MOE_BF16),          # softmax routing skewed by a Zipf logit bias, 128 experts, no shared
+@pytest.mark.parametrize("shape,T,ydt,tiled", [
+    ("small", 77, moe.MOE_F32, False),
+    ("small", 77, moe.MOE_BF16, False),
+    ("small", 77, moe.MOE_BF16, True),   # weights in the tiled e4m3 layout (routed and shared)
+    ("c3", 24, moe.MOE_BF16, False),     # DeepSeek-V3 dimensions: 256 fp8 experts and the shared one
+    ("c3", 24, moe.MOE_BF16, True),
+    ("c4", 48, moe.MOE_BF16, False),     # softmax routing skewed by a Zipf logit bias, 128 experts, no shared
 ])
-def test_layer_fp8_experts_matches_oracle(shape, T, ydt):
+def test_layer_fp8_experts_matches_oracle(shape, T, ydt, tiled):
     s = {"small": _small_shape, "c3": lambda: synth.config("c3_dsv3_bf16"),
          "c4": lambda: synth.config("c4_qwen3_skew_bf16")}[shape]()
     rc = router_case(s, T)
@@ -114,10 +116,14 @@ def test_layer_fp8_experts_matches_oracle(shape, T, ydt):
     sh = sh if sh is not None else (None,) * 6
     w = moe.weights(wg, wu, wd, s_gate=sg, s_up=su, s_down=sd,
                     sh_gate=sh[0], sh_up=sh[2], sh_down=sh[4], sh_s_gate=sh[1], sh_s_up=sh[3], sh_s_down=sh[5])
+    keep = None
+    if tiled:
+        w, keep = moe.tile_weights(c, w, dev())
     out = torch.full((T, s.H), float("nan"), device=dev())
     ws = moe.workspace(c, moe.MOE_STAGE_LAYER, dev())
     moe.moe_layer(c, rc["w_r"], rc["bias"], w, rc["x"], out, ws)
     torch.cuda.synchronize()
+    del keep
     got = out.cpu().numpy()
     assert np.isfinite(got).all()
     assert rel_err(got, ref) <= 4e-2
@@ -129,11 +135,11 @@ def _u8(t):
     return t.detach().contiguous().cpu().numpy().astype(np.uint8)
 
 
-@pytest.mark.parametrize("wfmt", ["e4m3", "mxfp4"])
+@pytest.mark.parametrize("wfmt", ["e4m3-tiled", "e4m3", "mxfp4"])
 def test_layer_lowp_experts_full_size_sampled(wfmt):
     """The benchmarked configuration: the c3 layer (T = 8192, 256 routed
-    experts and the shared one) with e4m3 or MXFP4 experts, bf16 expert
-    outputs.  Routing is checked for every token; the output on at least 512
+    experts and the shared one) with e4m3 experts (tiled, as timed, or
+    row-major) or MXFP4 experts, bf16 expert outputs.  Routing is checked for every token; the output on at least 512
     seeded tokens covering every expert with routed rows (with the first, the
     last, and tokens of the hottest and coldest experts) against the oracle
     composed step by step, to the bounds above."""
@@ -152,11 +158,14 @@ def test_layer_lowp_experts_full_size_sampled(wfmt):
     wg, sg, wu, su, wd, sd = stack
     w = moe.weights(wg, wu, wd, s_gate=sg, s_up=su, s_down=sd, sh_gate=sh[0], sh_up=sh[2], sh_down=sh[4],
                     sh_s_gate=sh[1], sh_s_up=sh[3], sh_s_down=sh[5])
+    keep = None
+    if wfmt == "e4m3-tiled":
+        w, keep = moe.tile_weights(c, w, d)
     out = torch.full((T, s.H), float("nan"), device=d)
     ws = moe.workspace(c, moe.MOE_STAGE_LAYER, d)
     moe.moe_layer(c, rc["w_r"], rc["bias"], w, rc["x"], out, ws)
     torch.cuda.synchronize()
-    del ws
+    del ws, keep
     ids, tw = oracle.route_select(rc["logits"], s.k, renormalize=s.renormalize, routed_scale=s.routed_scale,
                                   bias=rc["bh"], **route_kw(s))
     toks = cover_tokens(ids, T, s.E, 512, s.seed + 3)
