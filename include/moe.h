@@ -76,7 +76,7 @@ typedef enum moe_group_score { MOE_GROUP_TOP2_SUM = 0, MOE_GROUP_MAX = 1 } moe_g
 
 typedef enum moe_layout {
     MOE_LAYOUT_ROWMAJOR = 0, /* [out][in] row-major, the reduction index contiguous */
-    MOE_LAYOUT_TILED = 1,    /* bf16 tiled layout written by moe_tile_weights */
+    MOE_LAYOUT_TILED = 1,    /* weights: the bf16 or e4m3 layout moe_tile_weights writes; x_perm: bf16 tiled rows */
     MOE_LAYOUT_INDEXED = 2   /* x_layout only: no x_perm; the FFN reads x through row_src */
 } moe_layout;
 
@@ -158,10 +158,11 @@ typedef struct moe_cfg {
  * and up, [H/128][I_shared/128] for down; MXFP4 [I_shared][H/32] and
  * [H][I_shared/32]).
  * layout MOE_LAYOUT_ROWMAJOR: the matrices as above.  layout MOE_LAYOUT_TILED
- * (bf16 only): w_gate and sh_gate point to the gate+up matrices and w_down and
- * sh_down to the down matrices that moe_tile_weights writes, rearranged into
- * the order in which the GEMMs load MFMA operands (an internal layout: write
- * it with moe_tile_weights only); w_up and sh_up are unused (NULL).
+ * (bf16 or e4m3 weights): w_gate and sh_gate point to the gate+up matrices and
+ * w_down and sh_down to the down matrices that moe_tile_weights writes,
+ * rearranged into the order in which the GEMMs load MFMA operands (an internal
+ * layout: write it with moe_tile_weights only); w_up and sh_up are unused
+ * (NULL); e4m3 block scales keep their row-major arrays.
  * bf16 needs H, I, I_shared <= 65536 and one expert's gate+up matrices
  * (padded: 2 * roundup(I, 128) x roundup(H, 32) bf16) under 2 GiB. */
 typedef struct moe_weights {
@@ -225,25 +226,34 @@ size_t moe_ffn_workspace_bytes(const moe_cfg *cfg, int64_t n_rows_cap);
 size_t moe_x_perm_bytes(const moe_cfg *cfg);
 
 /* Bytes of the tiled copy of the expert weights (routed and shared) that
- * moe_tile_weights writes; (size_t)-1 for an invalid cfg. */
+ * moe_tile_weights writes; (size_t)-1 for an invalid cfg or weights without a
+ * tiled layout (fp32, MXFP4). */
 size_t moe_tiled_weights_bytes(const moe_cfg *cfg);
 
-/* Rewrites row-major bf16 expert weights into the tiled layout the grouped
- * GEMM streams with contiguous 1 KiB loads (weights are static: done once, at
- * load time).  The tiled layout: a matrix of R rows and K columns becomes 1 KiB
- * blocks of 16 rows x 32 columns, block (r / 16, k / 32) at byte offset
- * ((r / 16) * ceil(K / 32) + k / 32) * 1024; inside a block the 16-byte chunk c
- * (8 columns) of row r sits at chunk index r % 16 * 4 + (c ^ s(r % 16)),
- * s(r) = ((r >> 1) & 3) ^ ((r >> 3) & 1); rows and columns past the matrix are
- * zero.  Gate and up are merged into one matrix of 2 * roundup(I, 128) rows:
- * rows 256 j + 64 w + q hold gate row 128 j + 32 w + q (q < 32) and up row
- * 128 j + 32 w + q - 32 (q >= 32).  Down keeps its H rows.  Per expert the
- * gate+up matrix spans 2 * roundup(I, 128) / 16 * ceil(H / 32) KiB and the down
- * matrix ceil(H / 16) * ceil(I / 32) KiB; the routed experts follow each other,
- * then the shared expert's two matrices.
- * src: row-major bf16 weights (w_gate, w_up, w_down, and sh_* when has_shared);
+/* Rewrites row-major bf16 or e4m3 expert weights into the tiled layout the
+ * grouped GEMMs stream with contiguous loads, each wave's weight fragments of
+ * a K stage one contiguous block (weights are static: done once, at load
+ * time).  Rows and columns past a matrix are zero; the routed experts follow
+ * each other, then the shared expert's two matrices.
+ * bf16: a matrix of R rows and K columns becomes 4 KiB blocks of 64 rows x 32
+ * columns, block (r / 64, k / 32) at byte ((r / 64) * ceil(K / 32) + k / 32) *
+ * 4096; inside, the 16-byte chunk j * 64 + l (j < 4, l < 64) holds row
+ * 32 (j / 2) + l % 32, columns 16 (j % 2) + 8 (l / 32) .. + 7.  Gate and up
+ * merge into one matrix of 2 * roundup(I, 128) rows: rows 64 q + c hold gate
+ * row 32 q + c (c < 32) and up row 32 q + c - 32 (c >= 32).  Down keeps its H
+ * rows.  Per expert the gate+up matrix spans 2 * roundup(I, 128) / 64 *
+ * ceil(H / 32) blocks and the down matrix ceil(H / 64) * ceil(I / 32).
+ * e4m3: 4 KiB blocks of 32 rows x 128 columns, block (r / 32, k / 128) at byte
+ * ((r / 32) * (K / 128) + k / 128) * 4096; inside, byte 1024 i + 16 l + b
+ * (i < 4, l < 64, b < 16) holds row 16 (i / 2) + l % 16, column 32 (l / 16) +
+ * 16 (i % 2) + b.  Gate and up merge into 2 I rows: rows 32 q + c hold gate row
+ * 16 q + c (c < 16) and up row 16 q + c - 16 (c >= 16).  The byte counts are
+ * the row-major ones; the fp32 block scales are not rewritten: `tiled` points
+ * s_* and sh_s_* at src's arrays, which must stay alive.
+ * src: row-major weights (w_gate, w_up, w_down, and sh_* when has_shared);
  * dst: device buffer of moe_tiled_weights_bytes(cfg) bytes, 256-byte aligned;
- * tiled: filled with the pointers into dst and layout MOE_LAYOUT_TILED. */
+ * tiled: filled with the pointers into dst and layout MOE_LAYOUT_TILED.
+ * MOE_ERR_UNSUPPORTED for fp32 or MXFP4 weights. */
 moe_status moe_tile_weights(const moe_cfg *cfg, const moe_weights *src, void *dst, size_t dst_bytes,
                             moe_weights *tiled, void *stream);
 
