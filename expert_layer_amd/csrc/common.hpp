@@ -30,41 +30,20 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return (uint16_t)(u >> 16);
 }
 
-// OCP e4m3 code -> fp32 (exact).
-__device__ __forceinline__ float e4m3_to_f32(uint8_t c) {
-    uint32_t s = (uint32_t)(c & 0x80) << 24;
-    uint32_t e = (c >> 3) & 0xF;
-    uint32_t m = c & 0x7;
-    if (e == 0xF && m == 0x7) return __uint_as_float(0x7FC00000u | s);
-    if (e == 0) return __uint_as_float(s) + (s ? -1.0f : 1.0f) * (float)m * 0.001953125f;  // m * 2^-9
-    return __uint_as_float(s | ((e + 120u) << 23) | (m << 20));
-}
-
-// fp32 -> OCP e4m3, nearest-even, saturating at +-448.  The value v is first
-// clamped; the result is the nearest representable value.  Works on the bit
-// pattern: e4m3 normal numbers keep 3 fraction bits of an fp32 whose exponent
-// lies in [-6, 8]; below 2^-6 the spacing is the fixed 2^-9.
-__device__ __forceinline__ uint8_t f32_to_e4m3(float v) {
-    uint32_t u = __float_as_uint(v);
-    uint8_t sign = (uint8_t)((u >> 24) & 0x80);
-    float a = fabsf(v);
-    if (a != a) return 0x7F;
-    if (a >= 448.0f) return sign | 0x7E;
-    uint8_t code;
-    if (a < 0.015625f) {                   // subnormal range: multiples of 2^-9
-        float q = a * 512.0f;              // exact (power-of-two scaling)
-        float r = rintf(q);                // ties to even
-        code = (uint8_t)r;                 // 0..8 (8 == smallest normal)
-    } else {
-        uint32_t ua = __float_as_uint(a);
-        uint32_t lsb = (ua >> 20) & 1u;
-        ua += 0x7FFFFu + lsb;              // round to 3 fraction bits, ties to even
-        uint32_t e = (ua >> 23) - 120u;    // e4m3 biased exponent
-        uint32_t m = (ua >> 20) & 7u;
-        if (e > 15u || (e == 15u && m == 7u)) return sign | 0x7E;
-        code = (uint8_t)((e << 3) | m);
-    }
-    return code ? (uint8_t)(sign | code) : (uint8_t)0;
+// Four fp32 -> OCP e4m3 codes (nearest-even, saturating at +-448), packed
+// little-endian into a word: gfx950's v_cvt_pk_fp8_f32 rounds to nearest-even
+// in the OCP format; finite values are first clamped to [-448, 448] (the
+// instruction itself does not saturate), a NaN becomes the positive NaN code
+// 0x7F, and a negative value that rounds to zero gets the code 0x00 rather
+// than the instruction's negative zero 0x80.
+__device__ __forceinline__ uint32_t e4m3x4_rne_sat(float a, float b, float c, float d) {
+    auto prep = [](float v) { return v != v ? __builtin_nanf("") : __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f); };
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(prep(a), prep(b), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(prep(c), prep(d), w, true);
+    const uint32_t u = (uint32_t)w;
+    const uint32_t mag = u & 0x7F7F7F7Fu;
+    const uint32_t nonzero = (mag + 0x7F7F7F7Fu) & 0x80808080u;  // bit 7 of a byte: its magnitude is not 0
+    return mag | (u & nonzero);
 }
 
 // The tiled bf16 layout of the grouped FFN's operands: 1 KiB blocks of 16 rows

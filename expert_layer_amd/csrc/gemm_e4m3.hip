@@ -426,9 +426,8 @@ __device__ __forceinline__ void run_tile(const E4m3Args& p, int g, int row0, int
         for (int rb = 0; rb < RB; ++rb) {
             const int row = rb * 16 + l16;
             const float sc = rsc[row];
-            uint32_t w = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) w |= (uint32_t)f32_to_e4m3(acc[rb][0][j] / sc) << (8 * j);
+            const uint32_t w = e4m3x4_rne_sat(acc[rb][0][0] / sc, acc[rb][0][1] / sc, acc[rb][0][2] / sc,
+                                              acc[rb][0][3] / sc);
             qs[row * 32 + ((wave ^ ((row >> 1) & 7)) << 2) + g4] = w;
         }
         __syncthreads();

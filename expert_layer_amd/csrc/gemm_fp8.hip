@@ -474,9 +474,8 @@ __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int 
             const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
-                uint32_t w = 0;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) w |= (uint32_t)f32_to_e4m3(acc[rb][c][j] / sc) << (8 * j);
+                const uint32_t w = e4m3x4_rne_sat(acc[rb][c][0] / sc, acc[rb][c][1] / sc, acc[rb][c][2] / sc,
+                                                  acc[rb][c][3] / sc);
                 qs[row * 32 + (((q * 2 + c) ^ ((row >> 1) & 7)) << 2) + (lane >> 4)] = w;
             }
             if (q == 0 && lane < 16 && row < M) p.out_scale[(size_t)(row0 + row) * (N / BK) + n0 / BK] = sc;

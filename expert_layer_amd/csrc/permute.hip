@@ -220,12 +220,8 @@ quant_rows_e4m3(const uint16_t* __restrict__ x, int64_t n_blocks, int nb, int H,
     m = fmaxf(m, __shfl_xor(m, 4, 16));
     m = fmaxf(m, __shfl_xor(m, 8, 16));
     const float s = m > 0.0f ? m / 448.0f : 1.0f;
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        lo |= (uint32_t)f32_to_e4m3(v[i] / s) << (8 * i);
-        hi |= (uint32_t)f32_to_e4m3(v[4 + i] / s) << (8 * i);
-    }
+    const uint32_t lo = e4m3x4_rne_sat(v[0] / s, v[1] / s, v[2] / s, v[3] / s);
+    const uint32_t hi = e4m3x4_rne_sat(v[4] / s, v[5] / s, v[6] / s, v[7] / s);
     *reinterpret_cast<uint2*>(q + off) = make_uint2(lo, hi);
     if (l == 0) sc[b] = s;
 }
