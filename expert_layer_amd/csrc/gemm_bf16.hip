@@ -42,8 +42,9 @@
 // ((row >> 1) & 3) ^ ((row >> 3) & 1): a fragment read of 16 consecutive rows
 // (one pass of ds_read_b128 through the 64 banks of gfx950's LDS) touches 16
 // distinct 16-byte bank groups, and so does any 8 consecutive rows.
-// Launch order: the work list (see ffn_build_tiles) remapped so that a
-// contiguous run of items lives on one XCD and shares its L2.
+// Launch order: the work list (see ffn_build_tiles) remapped so that runs of
+// 32 consecutive items live on one XCD and share its L2, the eight XCDs
+// working on neighbouring runs at any time (xcd_remap_runs).
 #include <type_traits>
 
 #include "common.hpp"
@@ -560,7 +561,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, int mt, int g, int r
 template <int MODE>
 __global__ void __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2, 2)))
 ffn_gemm_bf16(GemmArgs p) {
-    const int L = xcd_remap(blockIdx.x, p.n_tiles[0] * p.NT);
+    const int L = xcd_remap_runs(blockIdx.x, p.n_tiles[0] * p.NT);
     if (L < 0) return;
     if (p.wt.tab && wtab_layer(p.wt) < 0) return;
     const int2 wl = p.work[L];
@@ -738,7 +739,7 @@ hipError_t launch_gemm_bf16(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_
     a.N_shared = has_sh ? c.I_shared : c.I;
     a.NT = wk.nt1;
     a.out_f32 = 0;
-    hipLaunchKernelGGL(ffn_gemm_bf16<0>, dim3((unsigned)xcd_grid(max_tiles * a.NT)), dim3(NTH), 0, s, a);
+    hipLaunchKernelGGL(ffn_gemm_bf16<0>, dim3((unsigned)xcd_grid_runs(max_tiles * a.NT)), dim3(NTH), 0, s, a);
     // GEMM2: down -> y
     a.work = reinterpret_cast<const int2*>(wk.work2);
     a.a_routed = static_cast<const uint16_t*>(h_tiles);
@@ -759,7 +760,7 @@ hipError_t launch_gemm_bf16(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_
     a.N_shared = c.H;
     a.NT = wk.nt2;
     a.out_f32 = c.y_dtype == MOE_F32;
-    hipLaunchKernelGGL(ffn_gemm_bf16<1>, dim3((unsigned)xcd_grid(max_tiles * a.NT)), dim3(NTH), 0, s, a);
+    hipLaunchKernelGGL(ffn_gemm_bf16<1>, dim3((unsigned)xcd_grid_runs(max_tiles * a.NT)), dim3(NTH), 0, s, a);
     return hipGetLastError();
 }
 

@@ -533,7 +533,7 @@ __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int 
 template <int MODE, int TB>
 __global__ void __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2, 2)))
 ffn_gemm_fp8(Fp8Args p) {
-    const int L = xcd_remap(blockIdx.x, p.n_tiles[0] * p.NT);
+    const int L = xcd_remap_runs(blockIdx.x, p.n_tiles[0] * p.NT);
     if (L < 0) return;
     if (p.wt.tab && wtab_layer(p.wt) < 0) return;
     const int2 wl = p.work[L];
@@ -590,7 +590,7 @@ hipError_t launch_gemm_fp8(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_c
     a.out_scale = h_scale;
     a.K = c.H;
     a.N = c.I;
-    const int64_t grid1 = xcd_grid(max_tiles * wk.nt1);
+    const int64_t grid1 = xcd_grid_runs(max_tiles * wk.nt1);
     launch_one<0>(tb, grid1, a, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -610,7 +610,7 @@ hipError_t launch_gemm_fp8(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_c
     a.K = c.I;
     a.N = c.H;
     a.out_f32 = c.y_dtype == MOE_F32 ? 1 : 0;
-    const int64_t grid2 = xcd_grid(max_tiles * wk.nt2);
+    const int64_t grid2 = xcd_grid_runs(max_tiles * wk.nt2);
     launch_one<1>(tb, grid2, a, s);
     return hipGetLastError();
 }
