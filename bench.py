@@ -74,7 +74,8 @@ def parse():
                         "over CAL_BYTES of fp32, as many bytes written) to scale the counters, then warmup + steps "
                         "passes of the stage calls on the workload's routing, with the expert weights drawn by "
                         "torch.randn (their values do not change which bytes the kernels move; a few hundred "
-                        "dispatches in all); prints no JSON line")
+                        "dispatches in all); with --fp8-experts, warmup + steps moe_quantize_fp8 calls on the "
+                        "workload's bf16 x drawn by torch.randn instead; prints no JSON line")
     p.add_argument("--no-clock", action="store_true", help="accepted for older command lines; does nothing")
     p.add_argument("--pmc-summary", nargs="+", metavar="DB",
                    help="no GPU: print, per kernel, the per-dispatch average of every counter in these rocprofv3 "
@@ -667,6 +668,17 @@ def bench_fp8_layer(a, s, dev):
     f4 = a.fp4_weights
     wdt = moe.MOE_FP4_E2M1 if f4 else moe.MOE_FP8_E4M3
     c = moe.make_cfg(**kw, act_dtype=moe.MOE_BF16, w_dtype=wdt)
+    if a.traffic_run:
+        # the per-token quantiser alone: its bytes do not depend on the values
+        x = torch.randn((T, H), device=dev).to(torch.bfloat16)
+        xq = torch.empty((T, H), dtype=torch.uint8, device=dev)
+        xs = torch.empty((T, H // 128), device=dev)
+        for _ in range(a.warmup + a.steps):
+            moe.moe_quantize_fp8(c, x, xq, xs)
+        torch.cuda.synchronize()
+        print(f"[bench] traffic run done: {a.warmup + a.steps} moe_quantize_fp8 calls on bf16 x [{T}][{H}]",
+              flush=True)
+        return None
     t_gen = time.time()
     x, w_r, bias = synth.router_inputs(s, dev)
     gen = synth.mxfp4_expert_weights if f4 else synth.fp8_expert_weights
