@@ -92,7 +92,8 @@ def parse():
 
 CAL_BYTES = 1 << 30
 CAL_RUNS = 3
-FFN_KERNELS = ("ffn_build_tiles", "ffn_gemm_bf16<0>", "ffn_gemm_bf16<1>")
+# the grouped FFN's kernels, as name prefixes (GEMM1 has a streamed-weights instance)
+FFN_KERNELS = ("ffn_build_tiles", "ffn_gemm_bf16<0", "ffn_gemm_bf16<1")
 
 
 def calibrate_copy(dev):
@@ -212,7 +213,8 @@ def clock_from(sq_db, kt_stats_csv, workload):
     for r in csv.DictReader(open(kt_stats_csv)):
         dur[_short(r["Name"])] = float(r["AverageNs"]) * 1e-9
     res = {"workload": workload, "source_hash": ffn_source_hash(), "kernels": {}}
-    for k in FFN_KERNELS[1:]:
+    names = sorted({_short(n) for n, _ in disp.values() if _short(n).startswith(FFN_KERNELS[1:])})
+    for k in names:
         grbm = [sum(cs["GRBM_GUI_ACTIVE"]) / XCDS for n, cs in disp.values()
                 if _short(n) == k and "GRBM_GUI_ACTIVE" in cs]
         busy = [sum(cs["SQ_VALU_MFMA_BUSY_CYCLES"]) for n, cs in disp.values()
@@ -522,7 +524,7 @@ def bench_bf16_layer(a, s, dev, extra=False):
                     "unit": "TFLOP/s", "frac": round(ffn_achieved / PEAK_BF16_TFLOPS, 4)}
     roofline.update({
         "traffic": traffic,
-        "kernel": "moe_grouped_ffn (ffn_gemm_bf16<0> gate/up+SwiGLU, ffn_gemm_bf16<1> down, tile list)",
+        "kernel": "moe_grouped_ffn (ffn_gemm_bf16<0, ...> gate/up+SwiGLU, ffn_gemm_bf16<1, false> down, tile list)",
         "flop_per_launch": ffn_flop, "bytes_per_launch": ffn_bytes, "io_bytes_per_launch": ffn_io_bytes,
         "io_frac": round(ffn_io_bytes / (stage_ms[2] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "roofline_ms": round(max(t_mfma, t_hbm) * 1e3, 4),

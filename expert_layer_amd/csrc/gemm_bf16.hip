@@ -218,18 +218,23 @@ __device__ __forceinline__ void dma_a(const Dma& d, int t, int lane) {
     for (int i = 0; i < kLoadsA; ++i) dma_a1<BUF>(d, t, lane, i);
 }
 
+// The cache policy of a buffer load with its non-temporal bit set.
+constexpr int kCpolNT = 2;
+
 // B fragments of stage t: q[kk] = k step kk of the wave's 32 weight rows.  A
 // load is real while kk * 16 is below the lane's limit for the stage (no limit
 // for the zero-padded tiled weights, the K tail for row-major ones, none at
 // all past the last stage); the rest carry kOOB.  Selects only: a branch here
-// would cost the wait counters their precision.
+// would cost the wait counters their precision.  STREAM: non-temporal loads,
+// for launches whose weight panels are each read by about one M tile.
+template <bool STREAM>
 __device__ __forceinline__ void load_b(const Dma& d, int t, i32x4 (&q)[2]) {
     const int lim = t < d.nsteps ? d.klim - t * BK : -1;
     const uint32_t base = (uint32_t)t * d.sb;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
         const uint32_t off = kk * 16 < lim ? d.vb + base + (uint32_t)kk * d.kb : kOOB;
-        q[kk] = __builtin_amdgcn_raw_buffer_load_b128(d.rb, off, 0, 0);
+        q[kk] = __builtin_amdgcn_raw_buffer_load_b128(d.rb, off, 0, STREAM ? kCpolNT : 0);
     }
 }
 
@@ -273,7 +278,7 @@ __device__ __forceinline__ void mma1(const i32x4& a, const i32x4& b, f32x16& c) 
 // k step (k step 1 of this stage, then k step 0 of stage s + 1 once the
 // barrier has made that buffer safe), so every read has a whole k step to
 // land; the stage's A DMA for stage s + NS is spread over the second k step.
-template <int MODE, int NRB, int BUF>
+template <int MODE, int NRB, int BUF, bool STREAM>
 __device__ __forceinline__ void stage(const Dma& d, int s, int lane, i32x4 (&fa)[NRB],
                                       i32x4 (&bq)[kStages<MODE>][2], f32x16 (&acc)[kRowBlocks]) {
     constexpr int NS = kStages<MODE>;
@@ -318,7 +323,7 @@ __device__ __forceinline__ void stage(const Dma& d, int s, int lane, i32x4 (&fa)
     for (int i = 0; i < kLoadsA; ++i)
         if (i >= issued_dma) dma_a1<BUF>(d, s + NS, lane, i);
     __builtin_amdgcn_sched_barrier(0);
-    load_b(d, s + NS, bq[BUF]);  // register set BUF is free once its MFMAs have issued
+    load_b<STREAM>(d, s + NS, bq[BUF]);  // register set BUF is free once its MFMAs have issued
     __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -327,7 +332,7 @@ __device__ __forceinline__ float* xchg_slot(int g) {
     return reinterpret_cast<float*>(ring<J>()) + g * 1024;
 }
 
-template <int MODE, int NRB>
+template <int MODE, int NRB, bool STREAM>
 __device__ __forceinline__ void run_tile(const GemmArgs& p, int mt, int g, int row0, int M, int n0, int K, int N,
                                          bool shared, int nt) {
     const int lane = threadIdx.x & 63;
@@ -422,7 +427,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, int mt, int g, int r
     static_for<0, NS>([&](auto c) {
         constexpr int t = decltype(c)::value;
         dma_a<t>(d, t, lane);
-        load_b(d, t, bq[t]);
+        load_b<STREAM>(d, t, bq[t]);
     });
     wait_vm<kWaitFirstA<NS>>();
     barrier_lds();
@@ -433,7 +438,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, int mt, int g, int r
     for (int s = 0; s < nturns * NS; s += NS) {
         static_for<0, NS>([&](auto c) {
             constexpr int b = decltype(c)::value;
-            stage<MODE, NRB, b>(d, s + b, lane, fa, bq, acc);
+            stage<MODE, NRB, b, STREAM>(d, s + b, lane, fa, bq, acc);
         });
     }
     wait_vm<0>();  // no LDS DMA may outlive the workgroup
@@ -558,7 +563,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, int mt, int g, int r
     }
 }
 
-template <int MODE>
+template <int MODE, bool STREAM>
 __global__ void __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2, 2)))
 ffn_gemm_bf16(GemmArgs p) {
     const int L = xcd_remap_runs(blockIdx.x, p.n_tiles[0] * p.NT);
@@ -574,15 +579,15 @@ ffn_gemm_bf16(GemmArgs p) {
     const int n0 = MODE == 0 ? nt * (BN / 2) : nt * BN;
     if (n0 >= N || M <= 0) return;
     switch ((M + 31) >> 5) {
-    case 1: run_tile<MODE, 1>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
-    case 2: run_tile<MODE, 2>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
-    case 3: run_tile<MODE, 3>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
-    case 4: run_tile<MODE, 4>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
-    case 5: run_tile<MODE, 5>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
-    case 6: run_tile<MODE, 6>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
-    case 7: run_tile<MODE, 7>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
-    case 8: run_tile<MODE, 8>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
-    default: run_tile<MODE, 9>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
+    case 1: run_tile<MODE, 1, STREAM>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
+    case 2: run_tile<MODE, 2, STREAM>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
+    case 3: run_tile<MODE, 3, STREAM>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
+    case 4: run_tile<MODE, 4, STREAM>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
+    case 5: run_tile<MODE, 5, STREAM>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
+    case 6: run_tile<MODE, 6, STREAM>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
+    case 7: run_tile<MODE, 7, STREAM>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
+    case 8: run_tile<MODE, 8, STREAM>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
+    default: run_tile<MODE, 9, STREAM>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
     }
 }
 
@@ -739,7 +744,16 @@ hipError_t launch_gemm_bf16(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_
     a.N_shared = has_sh ? c.I_shared : c.I;
     a.NT = wk.nt1;
     a.out_f32 = 0;
-    hipLaunchKernelGGL(ffn_gemm_bf16<0>, dim3((unsigned)xcd_grid_runs(max_tiles * a.NT)), dim3(NTH), 0, s, a);
+    // Streamed (non-temporal) gate/up weights when the routed rows average at
+    // most one M tile per expert: each weight panel is then read about once,
+    // and keeping it out of the caches leaves them to the row panels, which
+    // every N tile of an M tile reads again.  With several M tiles per expert
+    // the tiles of a block share each weight panel through L2, so the default
+    // policy stays; GEMM2 keeps it always.
+    const bool stream_w = n_rows_cap <= (int64_t)c.E * BM;
+    const dim3 g1((unsigned)xcd_grid_runs(max_tiles * a.NT));
+    if (stream_w) hipLaunchKernelGGL((ffn_gemm_bf16<0, true>), g1, dim3(NTH), 0, s, a);
+    else hipLaunchKernelGGL((ffn_gemm_bf16<0, false>), g1, dim3(NTH), 0, s, a);
     // GEMM2: down -> y
     a.work = reinterpret_cast<const int2*>(wk.work2);
     a.a_routed = static_cast<const uint16_t*>(h_tiles);
@@ -760,7 +774,7 @@ hipError_t launch_gemm_bf16(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_
     a.N_shared = c.H;
     a.NT = wk.nt2;
     a.out_f32 = c.y_dtype == MOE_F32;
-    hipLaunchKernelGGL(ffn_gemm_bf16<1>, dim3((unsigned)xcd_grid_runs(max_tiles * a.NT)), dim3(NTH), 0, s, a);
+    hipLaunchKernelGGL((ffn_gemm_bf16<1, false>), dim3((unsigned)xcd_grid_runs(max_tiles * a.NT)), dim3(NTH), 0, s, a);
     return hipGetLastError();
 }
 
