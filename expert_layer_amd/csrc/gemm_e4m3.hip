@@ -44,6 +44,8 @@
 // GEMM1 epilogue: h is requantised per row and 128 columns (the tile's h
 // columns are one scale block): s = max|h| / 448 (1 for an all-zero block),
 // q = e4m3_rne_sat(h / s), staged through LDS and stored as 16-byte chunks.
+// GEMM2 epilogue: bf16 y is staged through LDS one 32-row unit at a time and
+// stored as whole 512-byte rows of the tile (fp32 y straight from registers).
 //
 // Tiled e4m3 weights (written by tile_matrices_e4m3, once): a matrix of R rows
 // and K columns (K a multiple of 128) becomes 4 KiB blocks of 32 rows x 128
@@ -438,8 +440,45 @@ __device__ __forceinline__ void run_tile(const E4m3Args& p, int g, int row0, int
             const int row = c >> 3, ch = c & 7;
             *reinterpret_cast<i32x4*>(h + (size_t)(row0 + row) * N + n0 + ch * 16) = qv[row * 8 + (ch ^ ((row >> 1) & 7))];
         }
+    } else if (!p.out_f32) {
+        // y in bf16, staged through LDS one 32-row unit at a time (two
+        // buffers, one barrier a unit) and stored as whole rows of the tile.
+        // The 16-byte chunk c of a staged row r sits at chunk c ^ (r & 15): a
+        // wave's write (16 rows x 2 chunks) and its read (2 whole rows) both
+        // spread over every bank.
+        uint16_t* y = static_cast<uint16_t*>(p.out);
+        const int tid = threadIdx.x;
+        const int ncols = min(BN, N - n0);  // columns of the tile inside y
+#pragma unroll
+        for (int u = 0; u < NRB; ++u) {
+            uint32_t* st = reinterpret_cast<uint32_t*>(u & 1 ? ring<1>() : ring<0>());
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) {
+                const int r = 16 * hb + l16;
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb) {
+                    const f32x4 v = acc[2 * u + hb][cb];
+                    const uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+                    const uint32_t hi = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+                    const int c = 4 * wave + 2 * cb + (g4 >> 1);
+                    *reinterpret_cast<uint2*>(st + r * 128 + ((c ^ (r & 15)) << 2) + (g4 & 1) * 2) =
+                        make_uint2(lo, hi);
+                }
+            }
+            // the unit is staged; the other buffer's reads (unit u - 1) came
+            // before every thread's writes above, so it is free for unit u + 1
+            __syncthreads();
+            const i32x4* sv = reinterpret_cast<const i32x4*>(st);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int id = i * NTH + tid;
+                const int r = id >> 5, c = id & 31, row = 32 * u + r;
+                if (row < M && c * 8 < ncols)
+                    *reinterpret_cast<i32x4*>(y + (size_t)(row0 + row) * N + n0 + c * 8) = sv[r * 32 + (c ^ (r & 15))];
+            }
+        }
     } else {
-        // y: lane stores 4 consecutive columns of its row per column block
+        // fp32 y: lane stores 4 consecutive columns of its row per column block
         if (!wvalid) return;
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
@@ -448,14 +487,7 @@ __device__ __forceinline__ void run_tile(const E4m3Args& p, int g, int row0, int
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb) {
                 const size_t o = (size_t)(row0 + row) * N + (size_t)(wrow + 16 * cb + 4 * g4);
-                const f32x4 v = acc[rb][cb];
-                if (p.out_f32) {
-                    *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + o) = v;
-                } else {
-                    const uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-                    const uint32_t hi = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-                    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + o) = make_uint2(lo, hi);
-                }
+                *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + o) = acc[rb][cb];
             }
         }
     }
