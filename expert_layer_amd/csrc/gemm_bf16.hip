@@ -519,8 +519,39 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, int mt, int g, int r
             }
             barrier_lds();  // the round's slots are read before the next round writes them
         });
+    } else if (!p.out_f32) {
+        // bf16 y through LDS, one 32-row block at a time, by all eight waves
+        // into one [32 rows][256 columns] image (two buffers, one barrier a
+        // block), then stored as whole rows of the tile.  The 16-byte chunk c
+        // of image row r sits at chunk c ^ (((r >> 2) & 3) << 2): a wave's
+        // element writes (rows r and r + 4, 32 columns each) and its 16-byte
+        // reads (two whole rows) both spread over every bank.
+        const int cl = wg * 64 + wc * 32 + l32;  // this lane's column of the tile
+        const int tid = threadIdx.x;
+        uint16_t* y = static_cast<uint16_t*>(out);
+#pragma unroll
+        for (int r = 0; r < NRB; ++r) {
+            uint16_t* st = reinterpret_cast<uint16_t*>(r & 1 ? ring<1>() : ring<0>());
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int row = c_row(i, lane);
+                st[row * 256 + (((cl >> 3) ^ (((row >> 2) & 3) << 2)) << 3) + (cl & 7)] = f32_to_bf16(acc[r][i]);
+            }
+            // the block is staged; the other buffer's reads (block r - 1) came
+            // before every thread's writes above, so it is free for block r + 1
+            __syncthreads();
+            const i32x4* sv = reinterpret_cast<const i32x4*>(st);
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int id = k * NTH + tid;
+                const int row = id >> 5, c = id & 31, grow = r * 32 + row, col = n0 + c * 8;
+                if (grow < M && col < N)
+                    *reinterpret_cast<i32x4*>(y + (size_t)(row0 + grow) * N + col) =
+                        sv[row * 32 + (c ^ (((row >> 2) & 3) << 2))];
+            }
+        }
     } else {
-        // y through LDS, one 32-row block at a time: each wave stages its 32 x 32
+        // fp32 y through LDS, one 32-row block at a time: each wave stages its 32 x 32
         // block in a private 4 KiB slice of the ring (free once every wave has
         // left the main loop), fp32, row r at r * 128 B with rows r and r ^ 1
         // exchanged when bit 2 of r is set -- the accumulator writes (rows r and
@@ -547,16 +578,8 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, int mt, int g, int r
                 const int row = q >> 3, c4 = (q & 7) * 4;
                 const f32x4 v = *reinterpret_cast<const f32x4*>(st + (row ^ ((row >> 2) & 1)) * 32 + c4);
                 const int grow = r * 32 + row, col = cw + c4;
-                if (grow < M && col < N) {
-                    const size_t o = (size_t)(row0 + grow) * N + col;
-                    if (p.out_f32) {
-                        *reinterpret_cast<f32x4*>(static_cast<float*>(out) + o) = v;
-                    } else {
-                        const uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-                        const uint32_t hi = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-                        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + o) = make_uint2(lo, hi);
-                    }
-                }
+                if (grow < M && col < N)
+                    *reinterpret_cast<f32x4*>(static_cast<float*>(out) + (size_t)(row0 + grow) * N + col) = v;
             }
             __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");  // reads before the next block's writes
         }
