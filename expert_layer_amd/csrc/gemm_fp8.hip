@@ -488,8 +488,46 @@ __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int 
             const int row = c >> 3, ch = c & 7;
             *reinterpret_cast<i32x4*>(h + (size_t)(row0 + row) * N + n0 + ch * 16) = qv[row * 8 + (ch ^ ((row >> 1) & 7))];
         }
+    } else if (!p.out_f32) {
+        // bf16 y through LDS, 32 rows of each half of the tile at a time, by all
+        // eight waves into one [64 rows][256 columns] image (image row 32 h + i
+        // is tile row TB / 2 * h + 32 u + i; two A buffers, one barrier a
+        // round), then stored as whole rows of the tile.  The 16-byte chunk c
+        // of image row r sits at chunk c ^ (r & 15): a wave's writes (16 rows x
+        // 2 chunks) and its reads (two whole rows) both spread over every bank.
+        uint16_t* y = static_cast<uint16_t*>(p.out);
+        const int tid = threadIdx.x, g4 = lane >> 4;
+#pragma unroll
+        for (int u = 0; u < RB / 2; ++u) {
+            uint32_t* st = reinterpret_cast<uint32_t*>(u & 1 ? stgA<1>() : stgA<0>());
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) {
+                const int r = 32 * mh + 16 * hb + l16;
+#pragma unroll
+                for (int cb = 0; cb < 4; ++cb) {
+                    const f32x4 v = acc[2 * u + hb][cb];
+                    const uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+                    const uint32_t hi = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+                    const int c = 8 * q + 2 * cb + (g4 >> 1);
+                    *reinterpret_cast<uint2*>(st + r * 128 + ((c ^ (r & 15)) << 2) + (g4 & 1) * 2) =
+                        make_uint2(lo, hi);
+                }
+            }
+            // the round is staged; the other buffer's reads (round u - 1) came
+            // before every thread's writes above, so it is free for round u + 1
+            __syncthreads();
+            const i32x4* sv = reinterpret_cast<const i32x4*>(st);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int id = k * NTH + tid;
+                const int r = id >> 5, c = id & 31;
+                const int row = (r >> 5) * (TB / 2) + 32 * u + (r & 31), col = n0 + c * 8;
+                if (row < M && col < N)
+                    *reinterpret_cast<i32x4*>(y + (size_t)(row0 + row) * N + col) = sv[r * 32 + (c ^ (r & 15))];
+            }
+        }
     } else {
-        // y through LDS, 16 rows at a time: each wave stages its 16 x 64 block
+        // fp32 y through LDS, 16 rows at a time: each wave stages its 16 x 64 block
         // (fp32, 4 KiB of B buffer 0; of A buffer 1 in 256-row tiles, whose B
         // buffers are smaller), row r's 16-byte chunk c at chunk c ^ r,
         // so the eight rows of a store group and the eight chunks of a row's
@@ -514,16 +552,8 @@ __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int 
                 const int row = qq >> 4, c = qq & 15;
                 const f32x4 v = *reinterpret_cast<const f32x4*>(st + row * 64 + (c ^ row) * 4);
                 const int grow = r0 + rb * 16 + row, col = cw + c * 4;
-                if (grow < M && col < N) {
-                    const size_t o = (size_t)(row0 + grow) * N + col;
-                    if (p.out_f32) {
-                        *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + o) = v;
-                    } else {
-                        const uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-                        const uint32_t hi = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-                        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + o) = make_uint2(lo, hi);
-                    }
-                }
+                if (grow < M && col < N)
+                    *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + (size_t)(row0 + grow) * N + col) = v;
             }
             __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");  // reads before the next block's writes
         }
