@@ -189,10 +189,11 @@ __device__ __forceinline__ void promote(const f32x4 (&t)[2], float sa, float p0,
     }
 }
 
-// One K stage s on A buffer BUF and B register set BUF, RB row blocks.  While
-// the two MFMAs of row block rb run, the fragment of rb + 1 is read and rb - 1
-// is promoted; the stage's five A loads (stage s + 2, into the buffer stage
-// s - 1 used) follow the MFMAs of the first row blocks; the register set is
+// One K stage s on A buffer BUF and B register set BUF, RB row blocks.  The
+// fragment of row block rb + 1 is read just before the two MFMAs of rb issue
+// (a whole row block ahead of its use), and rb - 1 is promoted while they
+// run; the stage's five A loads (stage s + 2, into the buffer stage s - 1
+// used) follow the MFMAs of the first row blocks; the register set is
 // reloaded with stage s + 3 after the last MFMA.
 template <int RB, int BUF>
 __device__ __forceinline__ void stage(const Dma& d, int s, int wave, int lane, i32x8 (&b)[NS][2], float p0,
@@ -215,6 +216,11 @@ __device__ __forceinline__ void stage(const Dma& d, int s, int wave, int lane, i
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
+        // the fragment of rb + 1 goes to the register the MFMAs of rb - 1 read
+        if (rb + 1 < RB) {
+            a[(rb + 1) & 1] = cat(buf[ia + (rb + 1) * 128 + plo], buf[ia + (rb + 1) * 128 + phi]);
+            if ((rb + 1) % 4 == 0) sa[((rb + 1) / 4) & 1] = __builtin_bit_cast(f32x4, buf[is + 16 * ((rb + 1) / 4)]);
+        }
         t[rb & 1][0] = mfma_e4m3(b[BUF][0], a[rb & 1]);
         t[rb & 1][1] = mfma_e4m3(b[BUF][1], a[rb & 1]);
         switch (rb) {  // a constant: the loop is unrolled
@@ -224,10 +230,6 @@ __device__ __forceinline__ void stage(const Dma& d, int s, int wave, int lane, i
             case 3: dma_a1<NA, 3>(d, s + 2, wave); break;
             case 4: dma_a1<NA, 4>(d, s + 2, wave); break;
             default: break;
-        }
-        if (rb + 1 < RB) {
-            a[(rb + 1) & 1] = cat(buf[ia + (rb + 1) * 128 + plo], buf[ia + (rb + 1) * 128 + phi]);
-            if ((rb + 1) % 4 == 0) sa[((rb + 1) / 4) & 1] = __builtin_bit_cast(f32x4, buf[is + 16 * ((rb + 1) / 4)]);
         }
         if (rb > 0) promote(t[(rb - 1) & 1], sa[((rb - 1) / 4) & 1][(rb - 1) & 3], p0, p1, acc[rb - 1]);
         __builtin_amdgcn_sched_barrier(0);
