@@ -255,8 +255,9 @@ __device__ __forceinline__ void dma_slot(const Dma& d, int t, int wave) {
 // One K stage for the RB row blocks of 16 starting at tile row r0: every (row
 // block, column block) MFMA of this wave, promoted with the stage's row
 // scales, with the loads of stage t into A buffer NA and B buffer NB issued
-// between them.  Software-pipelined over row blocks: while the four MFMAs of
-// row block rb run, the fragments of rb + 1 are read and rb - 1 is promoted.
+// between them.  Software-pipelined over row blocks: the fragments of rb + 1
+// are read just before the four MFMAs of rb issue, and rb - 1 is promoted
+// while they run.
 // The weight operand is FP4 with its E8M0 scales bs applied by the MFMA; the
 // row fragment takes chunks lane / 16 and lane / 16 + 4 of the row (the K
 // order the FP4 x e4m3 form expects).
@@ -283,6 +284,8 @@ __device__ __forceinline__ void kstep(const Dma& d, int t_stage, int wave, int r
     static_assert(RB == 4 || RB == 8, "the load slots are laid out for 4 and 8 row blocks");
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
+        // the fragment of rb + 1 goes to the register the MFMAs of rb - 1 read
+        if (rb + 1 < RB) a[(rb + 1) & 1] = cat(buf[ia + (rb + 1) * 128 + plo], buf[ia + (rb + 1) * 128 + phi]);
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
             t[rb & 1][cb] = mfma16x16x128_fp4_fp8(b[cb], a[rb & 1], bs[cb]);
@@ -296,7 +299,6 @@ __device__ __forceinline__ void kstep(const Dma& d, int t_stage, int wave, int r
             case 5: dma_slot<MODE, NA, NB, 5, TB>(d, t_stage, wave); break;
             default: break;
         }
-        if (rb + 1 < RB) a[(rb + 1) & 1] = cat(buf[ia + (rb + 1) * 128 + plo], buf[ia + (rb + 1) * 128 + phi]);
         if (rb > 0) promote(t[(rb - 1) & 1], sa(rb - 1), acc[rb - 1]);
         __builtin_amdgcn_sched_barrier(0);
     }
