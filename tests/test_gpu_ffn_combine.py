@@ -173,6 +173,55 @@ def test_tiled_weights_give_identical_results(H, I, counts, shared_T, I_sh):
         assert rel_err(f64(outs[1][0][o:o + counts[e]]), ref) <= 1e-2
 
 
+@pytest.mark.parametrize("H,I,counts,shared_T", [
+    (1024, 512, [150, 0, 40, 290], 50),   # a group of two M tiles, an empty one, the shared expert
+    (520, 264, [31, 33, 2], 0),
+])
+def test_weight_cache_policy_gives_identical_results(H, I, counts, shared_T):
+    """GEMM1 streams its gate/up weights with non-temporal loads when the row
+    capacity averages at most one 288-row M tile per expert and keeps the default
+    cache policy otherwise; the policy moves no value, so the same call with a
+    capacity on either side of that line must give bit-identical outputs, for
+    row-major and tiled weights."""
+    d = dev()
+    E = len(counts)
+    s, wg, wu, wd = _weights(E, H, I, "bf16", seed=H + 5 * I, device=d)
+    n = int(sum(counts))
+    # streamed, then default: the line (288 rows a tile) lies between them for
+    # any tile height from n / E to 1023 rows
+    caps = (n, E * 1024)
+    x_rows = synth.normal(synth.stream_key(13, "rows"), (caps[1], H), 1.0, d, torch.bfloat16)
+    offs = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32, device=d)
+    has_sh = shared_T > 0
+    T = max(shared_T, 1)
+    sh = (None, None, None)
+    x_tok = None
+    if has_sh:
+        ss = synth.MoeShape("t", T=T, H=H, E=1, k=1, I=I, dtype="bf16", seed=79)
+        sh = synth.expert_weights(ss, 0, d)
+        x_tok = synth.normal(synth.stream_key(13, "tok"), (T, H), 1.0, d, torch.bfloat16)
+    c = moe.make_cfg(T=T, H=H, E=E, k=1, I=I, has_shared=has_sh, I_shared=I if has_sh else 0)
+    rm = moe.weights(wg, wu, wd, sh_gate=sh[0], sh_up=sh[1], sh_down=sh[2])
+    tiled, buf = moe.tile_weights(c, rm, d)
+    for w in (rm, tiled):
+        outs = []
+        for cap in caps:
+            y = torch.full((caps[1], H), -3.0, device=d)
+            ysh = torch.full((T, H), -3.0, device=d) if has_sh else None
+            moe.moe_grouped_ffn(c, cap, x_rows, None, offs, w, x_tok, y, ysh,
+                                moe.workspace(c, moe.MOE_STAGE_FFN, d, n_rows_cap=cap))
+            torch.cuda.synchronize()
+            outs.append((y, ysh))
+        assert torch.equal(outs[0][0][:n], outs[1][0][:n])
+        assert torch.all(outs[0][0][n:] == -3.0) and torch.all(outs[1][0][n:] == -3.0)
+        if has_sh:
+            assert torch.equal(outs[0][1], outs[1][1])
+    e = 3 if E == 4 else 0
+    o = int(np.sum(counts[:e]))
+    ref = oracle.expert_ffn(to_np(x_rows[o:o + counts[e]]), to_np(wg[e]), to_np(wu[e]), to_np(wd[e]), h_bf16=True)
+    assert rel_err(f64(outs[0][0][o:o + counts[e]]), ref) <= 1e-2
+
+
 @pytest.mark.parametrize("H,I,counts,extra", [
     (512, 1024, [37, 0, 5, 300, 64, 1, 0, 257], 9),
     (520, 264, [31, 33, 2], 0),
