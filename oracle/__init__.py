@@ -314,36 +314,81 @@ def expert_ffn_mxfp4(xq, xs, wg, sg, wu, su, wd, sd, return_h: bool = False):
     return (y, a) if return_h else y
 
 
-def fp8_h_alternatives(a: np.ndarray, eta: float):
-    """The requantisation decisions of the fp8 intermediate that a computation
-    in fp32 may take the other way.  For each row and 128-column block of a
-    (fp64, [n][I]) the decision is the one orc_expert_ffn_fp8 takes:
-    s = fp32(max|fp32(a)|) / 448, v = fp32(fp32(a) / s), code = e4m3_rne_sat(v).
-    A decision is ambiguous when v lies within eta * max(|v|, 2^-6) of the
-    midpoint between its two neighbouring e4m3 values: a value of a computed
-    with fp32 rounding (accumulation, exponential, division) can then land on
-    either side.  Returns, per row, a list of (column i, dh): dh is the change
-    of the dequantised intermediate a'_i when the other neighbour is taken."""
+U32 = 2.0 ** -24  # unit roundoff of fp32
+
+
+def ffn_h_error_bound(x: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray, kblock: int = 128) -> np.ndarray:
+    """A bound on |a~ - a| for the SwiGLU intermediate a = silu(g) * u of one
+    block-scaled expert, g = x . w_gate^T and u = x . w_up^T; x [n][K] and the
+    weights [I][K] are the exact dequantised operands (code * scale, fp64).
+    a~ is what any fp32 evaluation of the block-scale promotion may give that
+      (i)   sums each kblock-wide K block of code products in fp32, in any order,
+      (ii)  multiplies each block sum by the fp32 product of its scales and
+            accumulates the K / kblock results in fp32, in any order,
+      (iii) evaluates silu(g) in fp32 with a relative error of at most
+            (8 + |g|) u (an exponential of a rounded fp32 argument: the
+            argument's rounding moves the result by |g| u), and
+      (iv)  rounds silu * u to fp32.
+    Each term of g then passes through at most m = kblock + K / kblock + 2
+    roundings, so |g~ - g| <= gamma_m * sum_k |x_k w_k| with gamma_m =
+    m u / (1 - m u) (the recursive-summation bound for any order, Higham,
+    "Accuracy and Stability of Numerical Algorithms", section 3.1), likewise
+    for u; |silu'| <= 1.1 carries dg into silu."""
+    x = np.asarray(x, dtype=np.float64)
+    wg = np.asarray(w_gate, dtype=np.float64)
+    wu = np.asarray(w_up, dtype=np.float64)
+    K = x.shape[1]
+    assert wg.shape[1] == K and wu.shape == wg.shape and K % kblock == 0
+    m = kblock + K // kblock + 2
+    gam = m * U32 / (1.0 - m * U32)
+    g, u = x @ wg.T, x @ wu.T
+    ax = np.abs(x)
+    dg = gam * (ax @ np.abs(wg).T)
+    du = gam * (ax @ np.abs(wu).T)
+    with np.errstate(over="ignore"):
+        sil = g / (1.0 + np.exp(-g))
+    dsil = 1.1 * dg + (8.0 + np.abs(g)) * U32 * np.abs(sil)
+    return dsil * (np.abs(u) + du) + np.abs(sil) * du + U32 * np.abs(sil * u)
+
+
+def fp8_h_alternatives(a: np.ndarray, da):
+    """The requantisation decisions of the fp8 intermediate that an evaluation
+    within da of a (da: a bound on |a~ - a| per element, as ffn_h_error_bound
+    gives, or one number for all) may take the other way.  For each row and
+    128-column block of a (fp64, [n][I]) the decision is the one
+    orc_expert_ffn_fp8 takes: s = fp32(max|fp32(a)|) / 448, v = fp32(fp32(a) / s),
+    code = e4m3_rne_sat(v).  An evaluation a~ may move v by up to
+      dv = da / s + |v| (max_block(da) / max|a| + 4 u)
+    (its own block maximum moves s; two roundings on each side), so a decision
+    is ambiguous when v lies within dv of the midpoint between its two
+    neighbouring e4m3 values.  Returns, per row, a list of (column i, dh), the
+    decisions nearest their midpoint (relative to dv) first: dh is the change of
+    the dequantised intermediate a'_i when the other neighbour is taken."""
     a32 = np.asarray(a, dtype=np.float64).astype(np.float32)
     n, I = a32.shape
     assert I % 128 == 0
+    da = np.broadcast_to(np.asarray(da, dtype=np.float64), (n, I))
     vals = e4m3_to_f64(np.arange(0, 0x7F, dtype=np.uint8))  # the finite non-negative values, ascending
     blk = a32.reshape(n, I // 128, 128)
+    dab = da.reshape(n, I // 128, 128)
     amax = np.abs(blk).max(axis=2)
     s = np.where(amax > 0, (amax / np.float32(448.0)).astype(np.float32), np.float32(1.0))
     v = (blk / s[:, :, None]).astype(np.float32).astype(np.float64)
     av = np.minimum(np.abs(v), 448.0)
+    rel_s = np.where(amax > 0, dab.max(axis=2) / np.maximum(amax.astype(np.float64), 1e-300), 0.0)
+    dv = dab / s[:, :, None].astype(np.float64) + np.abs(v) * (rel_s[:, :, None] + 4.0 * U32)
     hi_i = np.clip(np.searchsorted(vals, av, side="left"), 1, len(vals) - 1)
     lo, hi = vals[hi_i - 1], vals[hi_i]
     mid = 0.5 * (lo + hi)
-    amb = np.abs(av - mid) <= eta * np.maximum(av, 2.0 ** -6)
+    amb = np.abs(av - mid) <= dv
     chosen = e4m3_to_f64(e4m3_rne_sat(v.reshape(-1))).reshape(v.shape)
     other = np.where(np.abs(chosen) == lo, hi, lo) * np.sign(v)
     dh = (other - chosen) * s[:, :, None].astype(np.float64)
+    closeness = np.abs(av - mid) / np.maximum(dv, 1e-300)
     out = [[] for _ in range(n)]
     for r, b, j in zip(*np.nonzero(amb)):
-        out[r].append((int(b * 128 + j), float(dh[r, b, j])))
-    return out
+        out[r].append((float(closeness[r, b, j]), int(b * 128 + j), float(dh[r, b, j])))
+    return [[(i, d) for _, i, d in sorted(row)] for row in out]
 
 
 def combine(y_rows: np.ndarray, tok_row: np.ndarray, topk_w: np.ndarray,

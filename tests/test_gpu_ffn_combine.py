@@ -38,6 +38,7 @@ def _weights(E, H, I, dt, seed, device):
     (4096, 1536, [513, 1, 33, 0], "bf16", 0, 0, moe.MOE_BF16),
     (256, 384, [0, 0, 0], "bf16", 70, 0, moe.MOE_F32),            # only the shared expert
     (520, 264, [31, 33, 2], "bf16", 9, 3, moe.MOE_F32),           # H, I not multiples of 64
+    (520, 264, [31, 33, 2], "bf16", 9, 3, moe.MOE_BF16),          # bf16 y: a last N tile of 8 columns
     (512, 1024, [37, 0, 5, 130, 64, 1, 0, 67], "f32", 0, 0, moe.MOE_F32),
     (256, 512, [12, 70], "f32", 33, 0, moe.MOE_F32),
 ])
@@ -89,8 +90,8 @@ def test_grouped_ffn_matches_oracle(H, I, counts, dt, shared_T, extra_rows, ydt)
             assert rms_err <= 2e-4, (e, rms_err)
             exact = oracle.expert_ffn(xh[sl], to_np(wg[e]), to_np(wu[e]), to_np(wd[e]))
             assert rel_err(yh[sl], exact) <= 3e-2, (e, rel_err(yh[sl], exact))
-    # rows past the last expert are not written
-    assert np.all(yh[n:cap] == sentinel)
+    # rows past the last expert are not written (the sentinel as y's dtype stores it)
+    assert np.all(yh[n:cap] == float(torch.tensor(sentinel, dtype=ydtype)))
     if has_sh:
         ref = oracle.expert_ffn(to_np(x_tok), to_np(shg), to_np(shu), to_np(shd), h_bf16=dt == "bf16")
         got = f64(y_sh)

@@ -379,19 +379,81 @@ def test_fp8_h_alternatives_flags_midpoints():
     a[0, 5] = 1.5 * 2.0 ** -9            # subnormal tie -> 2^-8 (even); other = 2^-9
     a[0, 6] = 0.0
     a[0, 7] = 1.0625 * (1 + 2.0 ** -8)   # far from the midpoint
-    alt = dict(oracle.fp8_h_alternatives(a, 2.0 ** -12)[0])
+    def rel(x, eta):  # an error bound of eta relative to max(|a|, 2^-6)
+        return eta * np.maximum(np.abs(x), 2.0 ** -6)
+    alt = dict(oracle.fp8_h_alternatives(a, rel(a, 2.0 ** -12))[0])
     assert set(alt) == {1, 2, 3, 4, 5}
     assert alt[1] == 0.125 and alt[2] == -0.125 and alt[3] == -0.125
     assert alt[4] == 32.0 and alt[5] == -(2.0 ** -9)
-    # a tighter eta drops the values that are not exact ties
-    tight = dict(oracle.fp8_h_alternatives(a, 2.0 ** -22)[0])
+    # a tighter bound drops the values that are not exact ties
+    tight = dict(oracle.fp8_h_alternatives(a, rel(a, 2.0 ** -22))[0])
     assert set(tight) == {1, 3, 5}
+    # no error at all leaves only the exact ties
+    assert set(dict(oracle.fp8_h_alternatives(a, 0.0)[0])) == {1, 3, 5}
     # scale != 1: amax 224 gives s = 0.5, v = 2 a, dh in units of a
     b = np.full((1, 128), 1.03, dtype=np.float64)
     b[0, 0] = 224.0
     b[0, 1] = 1.0625 / 2
-    alt_b = dict(oracle.fp8_h_alternatives(b, 2.0 ** -12)[0])
+    alt_b = dict(oracle.fp8_h_alternatives(b, rel(b, 2.0 ** -12))[0])
     assert alt_b[1] == 0.125 * 0.5
+    # a bound on the block maximum moves s, and with it every v of the block:
+    # 1.03 is 0.0325 from the midpoint 1.0625, which a 4% move of s covers
+    # (and 448 itself may land below the midpoint 432 of 416 and 448)
+    c = np.full((1, 128), 1.03, dtype=np.float64)
+    c[0, 0] = 448.0
+    dc = np.zeros((1, 128))
+    dc[0, 0] = 0.04 * 448.0
+    assert set(dict(oracle.fp8_h_alternatives(c, dc)[0])) == set(range(128))
+    dc[0, 0] = 0.01 * 448.0  # 1%: 1.03 stays, 448 stays above 432
+    assert set(dict(oracle.fp8_h_alternatives(c, dc)[0])) == set()
+
+
+def _fp32_block_scaled_swiglu(xc, xs, wc, ws, order, kb=128):
+    """An fp32 evaluation of a = silu(x . wg^T) * (x . wu^T) the way the bound
+    describes: per K block, the fp32 sum of code products (numpy's float32
+    matmul), times the fp32 product of the two scales, accumulated in fp32 in
+    the given block order; silu and the product in fp32."""
+    n, K = xc.shape
+    out = []
+    for w, s in zip(wc, ws):
+        acc = np.zeros((n, w.shape[0]), dtype=np.float32)
+        for b in order:
+            t = xc[:, b * kb:(b + 1) * kb].astype(np.float32) @ w[:, b * kb:(b + 1) * kb].astype(np.float32).T
+            q = xs[:, b][:, None].astype(np.float32) * s[:, b][None, :].astype(np.float32)
+            acc = (acc + (t * q).astype(np.float32)).astype(np.float32)
+        out.append(acc)
+    g, u = out
+    sil = (g / (np.float32(1.0) + np.exp(-g))).astype(np.float32)
+    return (sil * u).astype(np.float32)
+
+
+def test_ffn_h_error_bound_covers_fp32_evaluations():
+    """The bound on |a~ - a| holds for fp32 evaluations of the block-scaled
+    SwiGLU intermediate in two block orders (fp64 is the exact value: products
+    of e4m3 codes and scales are exact there), and it is informative: at
+    K = 1024 its median is below 2^-9 of |a|."""
+    rng = np.random.default_rng(5)
+    n, K, I = 24, 1024, 256
+    codes = np.arange(0, 0x7F, dtype=np.uint8)
+    codes = np.concatenate([codes, codes | 0x80])
+    xq = rng.choice(codes, size=(n, K))
+    wgq, wuq = rng.choice(codes, size=(I, K)), rng.choice(codes, size=(I, K))
+    xs = (2.0 ** rng.uniform(-12, -6, size=(n, K // 128))).astype(np.float32)
+    sg = (2.0 ** rng.uniform(-14, -8, size=(I // 128, K // 128))).astype(np.float32)
+    su = (2.0 ** rng.uniform(-14, -8, size=(I // 128, K // 128))).astype(np.float32)
+    xc, wgc, wuc = (oracle.e4m3_to_f64(q) for q in (xq, wgq, wuq))
+    X = xc * np.repeat(xs.astype(np.float64), 128, axis=1)
+    Wg = wgc * np.repeat(np.repeat(sg.astype(np.float64), 128, 0), 128, 1)
+    Wu = wuc * np.repeat(np.repeat(su.astype(np.float64), 128, 0), 128, 1)
+    g, u = X @ Wg.T, X @ Wu.T
+    a = g / (1 + np.exp(-g)) * u
+    bound = oracle.ffn_h_error_bound(X, Wg, Wu)
+    # the weight scales of a row block, per row
+    sgr, sur = np.repeat(sg, 128, axis=0), np.repeat(su, 128, axis=0)
+    for order in (range(K // 128), reversed(range(K // 128))):
+        a32 = _fp32_block_scaled_swiglu(xc, xs, (wgc, wuc), (sgr, sur), list(order))
+        assert np.all(np.abs(a32.astype(np.float64) - a) <= bound)
+    assert np.median(bound / np.maximum(np.abs(a), 1e-300)) < 2.0 ** -9
 
 
 def test_quantize_rows_e4m3_closed_forms():
