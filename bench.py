@@ -864,7 +864,7 @@ def cpu_baseline(s, x, w_r, target_s):
 
     n = 32
     dt = run(n)
-    n = int(min(4096, max(32, n * target_s / max(dt, 1e-3))))
+    n = int(min(x.shape[0], max(32, n * target_s / max(dt, 1e-3))))  # at most every token row
     dt = run(n)
     threads = min(oracle.threads(), n)
     return {"value": round(n * per_row / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
