@@ -57,7 +57,10 @@ __device__ __forceinline__ size_t tiled_chunk(int64_t row, int chunk, int KS) {
     return ((size_t)(row >> 4) * (size_t)KS + (size_t)(chunk >> 2)) * 64 + (size_t)(r * 4 + ((chunk & 3) ^ tile_swz(r)));
 }
 
-__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+// silu(z) = z / (1 + e^-z) in fp32, the quotient through the hardware reciprocal
+// (about one ulp) rather than the correctly rounded division sequence: every
+// consumer rounds the product silu * u to bf16 or e4m3 or holds fp32 to 1e-4.
+__device__ __forceinline__ float silu_f(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // ---------------------------------------------------------------- MFMA
 // v_mfma_f32_32x32x16_bf16: A fragment = 8 bf16 of one row (lane % 32) at
