@@ -449,69 +449,69 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, int mt, int g, int r
         // h = silu(g) * u into this M tile's slot, tiled with the slot's own KS
         // (the K of GEMM2), so GEMM2 streams it with contiguous 1 KiB reads.
         // Columns in [N, roundup(N, 32)) are GEMM2's K padding: they get zeros.
-        // The pair's 32 h columns are one k block of the slot.  Round by round,
-        // the up wave stores its accumulators (lane-major, so writes and reads
-        // are contiguous) into one ring buffer per row block, and after a
-        // barrier the gate wave combines them with its own.  Each 32-row block
-        // of h then goes through the gate wave's private 4 KiB slice of the
-        // last ring buffer, fp32, row r at r * 128 B with rows r and r ^ 1
-        // exchanged when bit 2 of r is set, so the accumulator writes (rows r
-        // and r + 4 in the two half-waves) touch 64 distinct banks.  It is read
-        // back in the tiled block's own order -- lane q takes slot q, 8 columns
-        // of one row, two 16-byte reads on distinct banks -- and every 16-row
-        // block is one contiguous 1 KiB store.  Rows of the slot past M hold
-        // zeros (their A rows loaded as zeros).  LDS operations of one wave are
-        // processed in order.
+        // The pair's 32 h columns are one k block of the slot.  A lane's 16
+        // accumulators of a row block are rows c_row(i): i < 8 the block's
+        // rows 0..15, i >= 8 rows 16..31.  Round by round, the gate wave hands
+        // the up wave its g of rows 16..31 and the up wave hands the gate wave
+        // its u of rows 0..15 (lane-major through one ring buffer per row
+        // block, so writes and reads are contiguous); after a barrier each
+        // wave forms h of its 16 rows.  They go through the wave's private
+        // 2 KiB slice of the last ring buffer, fp32, row r at r * 128 B with
+        // rows r and r ^ 1 exchanged when bit 2 of r is set, so the writes
+        // (rows r and r + 4 in the two half-waves) touch 64 distinct banks;
+        // read back in the tiled block's own order -- lane q takes slot q, 8
+        // columns of one row, two 16-byte reads on distinct banks -- each
+        // 16-row block is one contiguous 1 KiB store.  Rows of the slot past M
+        // hold zeros (their A rows loaded as zeros).  LDS operations of one
+        // wave are processed in order.
         constexpr int R = kStages<0> - 1;  // row blocks per round
         const int ksh = (N + BK - 1) / BK;
         const int kb = (n0 >> 5) + wg;  // n0 is a multiple of 32
         const bool pair_live = kb < ksh;
         const bool live = pair_live && kb * 32 + l32 < N;
         uint16_t* h = static_cast<uint16_t*>(out) + (size_t)mt * kBlocks16 * p.h_slot_ks * 512;
-        float* st = reinterpret_cast<float*>(ring<kStages<0> - 1>()) + wg * 1024;
+        float* st = reinterpret_cast<float*>(ring<kStages<0> - 1>()) + wg * 1024 + wc * 512;
         const int rr = lane >> 2, c8 = (lane & 3) ^ swz_of_row(rr);  // the slot this lane stores
+        const int mine = wc * 8;  // the accumulators whose rows this wave finishes
         static_for<0, (NRB + R - 1) / R>([&](auto rc) {
             constexpr int r0 = decltype(rc)::value * R;
-            if (wc == 1) {
-                static_for<0, R>([&](auto jc) {
-                    constexpr int j = decltype(jc)::value;
-                    if constexpr (r0 + j < NRB) {
-                        float* x = xchg_slot<NRB, j>(wg);
+            // hand over the other half: the gate wave its g of i >= 8 (slot
+            // half 0), the up wave its u of i < 8 (slot half 1)
+            static_for<0, R>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                if constexpr (r0 + j < NRB) {
+                    float* x = xchg_slot<NRB, j>(wg) + wc * 512;
 #pragma unroll
-                        for (int i = 0; i < 16; ++i) x[i * 64 + lane] = acc[r0 + j][i];
-                    }
-                });
-            }
+                    for (int i = 0; i < 8; ++i) x[i * 64 + lane] = acc[r0 + j][8 - mine + i];
+                }
+            });
             barrier_lds();
-            if (wc == 0 && pair_live) {
+            if (pair_live) {
                 static_for<0, R>([&](auto jc) {
                     constexpr int j = decltype(jc)::value;
                     constexpr int r = r0 + j;
                     if constexpr (r < NRB) {
-                        const float* x = xchg_slot<NRB, j>(wg);
+                        const float* x = xchg_slot<NRB, j>(wg) + (1 - wc) * 512;
 #pragma unroll
-                        for (int i = 0; i < 16; ++i) {
-                            const int row = c_row(i, lane);  // bit 2 of row is lane / 32
-                            st[(row ^ ((row >> 2) & 1)) * 32 + l32] =
-                                live ? silu_f(acc[r][i]) * x[i * 64 + lane] : 0.0f;
+                        for (int i = 0; i < 8; ++i) {
+                            const float mv = acc[r][mine + i], ov = x[i * 64 + lane];
+                            const float g = wc ? ov : mv, u = wc ? mv : ov;
+                            const int row = c_row(mine + i, lane) - wc * 16;  // bit 2 of row is lane / 32
+                            st[(row ^ ((row >> 2) & 1)) * 32 + l32] = live ? silu_f(g) * u : 0.0f;
                         }
                         // the staged values are read by other lanes of this wave:
                         // keep the compiler from moving the reads above the writes
                         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-#pragma unroll
-                        for (int hb = 0; hb < 2; ++hb) {
-                            const int row = hb * 16 + rr;
-                            const float* src = st + (row ^ ((row >> 2) & 1)) * 32 + c8 * 8;
-                            const f32x4 v0 = *reinterpret_cast<const f32x4*>(src);
-                            const f32x4 v1 = *reinterpret_cast<const f32x4*>(src + 4);
-                            uint4 q;
-                            q.x = (uint32_t)f32_to_bf16(v0[0]) | ((uint32_t)f32_to_bf16(v0[1]) << 16);
-                            q.y = (uint32_t)f32_to_bf16(v0[2]) | ((uint32_t)f32_to_bf16(v0[3]) << 16);
-                            q.z = (uint32_t)f32_to_bf16(v1[0]) | ((uint32_t)f32_to_bf16(v1[1]) << 16);
-                            q.w = (uint32_t)f32_to_bf16(v1[2]) | ((uint32_t)f32_to_bf16(v1[3]) << 16);
-                            if (r * 32 + hb * 16 < M)
-                                *reinterpret_cast<uint4*>(h + ((size_t)(r * 2 + hb) * ksh + kb) * 512 + lane * 8) = q;
-                        }
+                        const float* src = st + (rr ^ ((rr >> 2) & 1)) * 32 + c8 * 8;
+                        const f32x4 v0 = *reinterpret_cast<const f32x4*>(src);
+                        const f32x4 v1 = *reinterpret_cast<const f32x4*>(src + 4);
+                        uint4 q;
+                        q.x = (uint32_t)f32_to_bf16(v0[0]) | ((uint32_t)f32_to_bf16(v0[1]) << 16);
+                        q.y = (uint32_t)f32_to_bf16(v0[2]) | ((uint32_t)f32_to_bf16(v0[3]) << 16);
+                        q.z = (uint32_t)f32_to_bf16(v1[0]) | ((uint32_t)f32_to_bf16(v1[1]) << 16);
+                        q.w = (uint32_t)f32_to_bf16(v1[2]) | ((uint32_t)f32_to_bf16(v1[3]) << 16);
+                        if (r * 32 + wc * 16 < M)
+                            *reinterpret_cast<uint4*>(h + ((size_t)(r * 2 + wc) * ksh + kb) * 512 + lane * 8) = q;
                         // reads before the next block's writes
                         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
                     }
