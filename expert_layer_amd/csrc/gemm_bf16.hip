@@ -54,13 +54,16 @@ namespace {
 
 constexpr int BM = kFfnBmBf16, BN = 256, BK = 32, NWAVES = 8, NTH = NWAVES * 64;
 #ifndef MOE_GEMM1_STAGES
-#define MOE_GEMM1_STAGES 6
+#define MOE_GEMM1_STAGES 4
 #endif
 #ifndef MOE_GEMM2_STAGES
 #define MOE_GEMM2_STAGES 4
 #endif
-// Stages in flight (A: LDS buffers, B: register sets), per GEMM: the longer K
-// of GEMM1 takes a deeper ring, GEMM2's 64 stages per tile a shorter fill.
+// Stages in flight (A: LDS buffers, B: register sets), per GEMM.  The loop
+// runs in whole turns of the ring (stages past the end load zeros and still
+// issue their MFMAs), so a depth that divides the stage count of the usual K
+// (7168, 4096, 2048, 1536 are all multiples of 4 stages of 32) runs no zero
+// stage; three stages of loads ahead cover the latency at every T measured.
 template <int MODE>
 constexpr int kStages = MODE == 0 ? MOE_GEMM1_STAGES : MOE_GEMM2_STAGES;
 static_assert(kStages<0> >= 3 && kStages<0> <= 7 && kStages<1> >= 3 && kStages<1> <= 7,
