@@ -52,7 +52,7 @@ def parse():
     p.add_argument("--workload", default="c3_dsv3_bf16")
     p.add_argument("--fp8-experts", action="store_true",
                    help="a bf16 layer workload with e4m3 experts (128x128 block scales): moe_layer quantises the "
-                        "activations per token and runs the experts in fp8")
+                        "activations per token inside the router's pass over x and runs the experts in fp8")
     p.add_argument("--tokens", type=int, default=0,
                    help="override the workload's token count T (the small-T, weight-streaming regime)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -74,8 +74,9 @@ def parse():
                         "over CAL_BYTES of fp32, as many bytes written) to scale the counters, then warmup + steps "
                         "passes of the stage calls on the workload's routing, with the expert weights drawn by "
                         "torch.randn (their values do not change which bytes the kernels move; a few hundred "
-                        "dispatches in all); with --fp8-experts, warmup + steps moe_quantize_fp8 calls on the "
-                        "workload's bf16 x drawn by torch.randn instead; prints no JSON line")
+                        "dispatches in all); with --fp8-experts, warmup + steps moe_route_quantize calls (the route "
+                        "with the per-token quantisation of x) on the workload's router inputs instead; prints no "
+                        "JSON line")
     p.add_argument("--no-clock", action="store_true", help="accepted for older command lines; does nothing")
     p.add_argument("--pmc-summary", nargs="+", metavar="DB",
                    help="no GPU: print, per kernel, the per-dispatch average of every counter in these rocprofv3 "
@@ -671,14 +672,16 @@ def bench_fp8_layer(a, s, dev):
     wdt = moe.MOE_FP4_E2M1 if f4 else moe.MOE_FP8_E4M3
     c = moe.make_cfg(**kw, act_dtype=moe.MOE_BF16, w_dtype=wdt)
     if a.traffic_run:
-        # the per-token quantiser alone: its bytes do not depend on the values
-        x = torch.randn((T, H), device=dev).to(torch.bfloat16)
+        # the route with its fused per-token quantisation alone
+        x, w_r, bias = synth.router_inputs(s, dev)
         xq = torch.empty((T, H), dtype=torch.uint8, device=dev)
         xs = torch.empty((T, H // 128), device=dev)
+        ids, tw = torch.empty((T, k), dtype=torch.int32, device=dev), torch.empty((T, k), device=dev)
+        ws_r = moe.workspace(c, moe.MOE_STAGE_ROUTE, dev)
         for _ in range(a.warmup + a.steps):
-            moe.moe_quantize_fp8(c, x, xq, xs)
+            moe.moe_route_quantize(c, x, w_r, bias, None, ids, tw, xq, xs, ws_r)
         torch.cuda.synchronize()
-        print(f"[bench] traffic run done: {a.warmup + a.steps} moe_quantize_fp8 calls on bf16 x [{T}][{H}]",
+        print(f"[bench] traffic run done: {a.warmup + a.steps} moe_route_quantize calls on bf16 x [{T}][{H}]",
               flush=True)
         return None
     t_gen = time.time()
@@ -725,9 +728,10 @@ def bench_fp8_layer(a, s, dev):
     wall = time.perf_counter() - t0
     ms_step = ev0.elapsed_time(ev1) / a.steps
 
-    # ---- the same work as stage calls: route, quantise, permute (maps only,
-    # m_tile 16), the routed grouped FFN reading the e4m3 token rows through
-    # row_src, the shared one (one group of T rows), combine
+    # ---- the same work as stage calls: route with the per-token quantisation
+    # of x, permute (maps only, m_tile 16), the routed grouped FFN reading the
+    # e4m3 token rows through row_src, the shared one (one group of T rows),
+    # combine
     cq = moe.make_cfg(**dict(kw, has_shared=False, I_shared=0), act_dtype=moe.MOE_FP8_E4M3, w_dtype=wdt, m_tile=16,
                       x_layout=moe.MOE_LAYOUT_INDEXED)
     c1 = moe.make_cfg(**dict(kw, E=1, k=1, n_groups=1, topk_groups=1, I=max(I_sh, 128), has_shared=False,
@@ -749,31 +753,30 @@ def bench_fp8_layer(a, s, dev):
     ws_p = moe.workspace(cq, moe.MOE_STAGE_PERMUTE, dev)
     ws_f = moe.workspace(cq, moe.MOE_STAGE_FFN, dev, n_rows_cap=rows)
     ws_1 = moe.workspace(c1, moe.MOE_STAGE_FFN, dev, n_rows_cap=T) if s.shared else None
-    names = ["route", "quantise", "permute", "grouped_ffn", "combine"]
+    names = ["route_quantise", "permute", "grouped_ffn", "combine"]
 
     def stage_step(evs):
         evs[0].record(stream)
-        moe.moe_route(c, x, w_r, bias, None, None, ids, tw, ws_r, stream)
+        moe.moe_route_quantize(c, x, w_r, bias, None, ids, tw, xq, xs, ws_r, stream)
         evs[1].record(stream)
-        moe.moe_quantize_fp8(c, x, xq, xs, stream)
-        evs[2].record(stream)
         moe.moe_permute(cq, xq, xs, ids, counts, offs, row_src, tok_row, x_perm, xps, ws_p, stream)
-        evs[3].record(stream)
+        evs[2].record(stream)
         moe.moe_grouped_ffn(cq, rows, xq, xs, offs, w, None, y_rows, None, ws_f, stream, row_src=row_src)
         if s.shared:
             moe.moe_grouped_ffn(c1, T, xq, xs, offs1, w1, None, y_sh, None, ws_1, stream)
-        evs[4].record(stream)
+        evs[3].record(stream)
         moe.moe_combine(c, y_rows, tok_row, tw, y_sh, out, stream)
-        evs[5].record(stream)
+        evs[4].record(stream)
 
+    ns = len(names)
     for _ in range(2):
-        stage_step([torch.cuda.Event(enable_timing=True) for _ in range(6)])
+        stage_step([torch.cuda.Event(enable_timing=True) for _ in range(ns + 1)])
     torch.cuda.synchronize()
-    all_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(a.steps)]
+    all_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(ns + 1)] for _ in range(a.steps)]
     for evs in all_evs:
         stage_step(evs)
     torch.cuda.synchronize()
-    stage_ms = np.mean([[evs[i].elapsed_time(evs[i + 1]) for i in range(5)] for evs in all_evs], axis=0)
+    stage_ms = np.mean([[evs[i].elapsed_time(evs[i + 1]) for i in range(ns)] for evs in all_evs], axis=0)
 
     R = T * k
     KB1, KB2 = H // 128, I // 128
@@ -784,8 +787,7 @@ def bench_fp8_layer(a, s, dev):
     else:
         w_bytes = 3.0 * E * H * I + 3.0 * E * KB1 * KB2 * 4 + 3.0 * H * I_sh + 3.0 * KB1 * (I_sh // 128) * 4
     bytes_ = {
-        "route": T * H * 2 + E * H * 2 + T * k * 8,
-        "quantise": T * H * 2 + T * H + T * KB1 * 4,
+        "route_quantise": T * H * 2 + E * H * 2 + T * k * 8 + T * H + T * KB1 * 4,
         "permute": T * k * 4 + E * 8 + rows * 4 + T * k * 4,
         "grouped_ffn": w_bytes + (R + T * bool(s.shared)) * (H + KB1 * 4) + (R + T * bool(s.shared)) * H * 2,
         "combine": R * H * 2 + T * H * 2 * bool(s.shared) + T * H * 2 + T * k * 8,
@@ -799,7 +801,7 @@ def bench_fp8_layer(a, s, dev):
             st["TFLOP/s"] = round(ffn_flop / (ms * 1e-3) / 1e12, 1)
             st["mfma_frac"] = round(ffn_flop / (ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4)
         stages[n] = st
-    ffn_ms = float(stage_ms[3])
+    ffn_ms = float(stage_ms[names.index("grouped_ffn")])
     t_mfma = ffn_flop / (PEAK_FP8_TFLOPS * 1e12)
     t_hbm = bytes_["grouped_ffn"] / (PEAK_HBM_GBS * 1e9)
     tf = ffn_flop / (ffn_ms * 1e-3) / 1e12

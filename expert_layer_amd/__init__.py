@@ -25,7 +25,7 @@ from ._ffi import (MOE_BF16, MOE_ERR_HIP, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORT
 
 __all__ = [
     "MoeError", "make_cfg", "weights", "workspace", "moe_validate", "moe_max_rows", "moe_workspace_bytes", "moe_ffn_workspace_bytes",
-    "moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_quantize_fp8", "moe_layer", "moe_weight_table",
+    "moe_route", "moe_route_quantize", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_quantize_fp8", "moe_layer", "moe_weight_table",
     "weight_table", "moe_status_string",
     "moe_last_error", "moe_cfg", "moe_weights", "lib_path",
     "MOE_OK", "MOE_ERR_INVALID_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE", "MOE_ERR_HIP",
@@ -181,6 +181,14 @@ def moe_route(cfg, x, w_router, bias, logits_in, logits_out, topk_ids, topk_w, w
     p, n = _ws(ws)
     _check(_ffi.lib().moe_route(ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(logits_in),
                                 _ptr(logits_out), _ptr(topk_ids), _ptr(topk_w), p, n, _stream(stream)))
+
+
+def moe_route_quantize(cfg, x, w_router, bias, logits_out, topk_ids, topk_w, x_q, x_scale, ws=None, stream=None):
+    """moe_route on bf16 x that also writes moe_quantize_fp8's x_q and x_scale."""
+    p, n = _ws(ws)
+    _check(_ffi.lib().moe_route_quantize(ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(logits_out),
+                                         _ptr(topk_ids), _ptr(topk_w), _ptr(x_q), _ptr(x_scale), p, n,
+                                         _stream(stream)))
 
 
 def moe_permute(cfg, x, x_scale, topk_ids, expert_counts, expert_offsets, row_src, tok_row, x_perm,

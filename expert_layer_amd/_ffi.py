@@ -21,7 +21,7 @@ MOE_LAYOUT_ROWMAJOR, MOE_LAYOUT_TILED, MOE_LAYOUT_INDEXED = 0, 1, 2
 EXPORTS = ("moe_validate", "moe_max_rows", "moe_workspace_bytes", "moe_ffn_workspace_bytes",
            "moe_x_perm_bytes", "moe_tiled_weights_bytes", "moe_tile_weights", "moe_route", "moe_permute", "moe_grouped_ffn",
            "moe_combine", "moe_quantize_fp8", "moe_layer", "moe_weight_table", "moe_permute_noalloc",
-           "moe_status_string",
+           "moe_route_quantize", "moe_status_string",
            "moe_last_error")
 
 
@@ -69,6 +69,8 @@ def lib() -> ctypes.CDLL:
         L.moe_tile_weights.restype = i32
         L.moe_route.argtypes = [C, P, P, P, P, P, P, P, P, sz, P]
         L.moe_route.restype = i32
+        L.moe_route_quantize.argtypes = [C, P, P, P, P, P, P, P, P, P, sz, P]
+        L.moe_route_quantize.restype = i32
         L.moe_permute.argtypes = [C, P, P, P, P, P, P, P, P, P, P, sz, P]
         L.moe_permute.restype = i32
         L.moe_permute_noalloc.argtypes = [C, P, P, P, P, P, P, P, P, P, P]

@@ -414,14 +414,13 @@ moe_status ffn_enqueue(const moe_cfg& c, int64_t n_rows_cap, const void* x_rows,
     return MOE_OK;
 }
 
-// The rest of moe_layer for low-precision experts (routing done): quantise x,
-// the dispatch maps (GEMM1 reads the e4m3 token rows through row_src), the
-// routed and the shared grouped FFN, combine.
-moe_status layer_fp8_experts(const moe_cfg& c, const moe_weights& w, const void* x, void* out,
-                             const LayerCarve& l, hipStream_t s) {
+// The rest of moe_layer for low-precision experts (routing done, x quantised
+// by the router): the dispatch maps (GEMM1 reads the e4m3 token rows through
+// row_src), the routed and the shared grouped FFN, combine.
+moe_status layer_fp8_experts(const moe_cfg& c, const moe_weights& w, void* out, const LayerCarve& l,
+                             hipStream_t s) {
     const moe_cfg cq = fp8_routed_cfg(c);
-    hipError_t e = moe::launch_quant_rows_e4m3(x, c.T, c.H, l.x_q, l.x_s, s);
-    if (e != hipSuccess) return hip_fail(e, "moe_layer (quantise)");
+    hipError_t e;
     moe_status st = permute_enqueue(cq, l.x_q, l.x_s, l.ids, l.counts, l.offsets, l.row_src, l.tok_row, l.x_perm,
                                     l.x_perm_scale, l.scratch, s);
     if (st != MOE_OK) return st;
@@ -507,6 +506,35 @@ moe_status moe_route(const moe_cfg* cfg, const void* x, const void* w_router, co
     }
     hipError_t e = moe::launch_route_select(c, l, nsplit, bias, logits_out, topk_ids, topk_w, s);
     if (e != hipSuccess) return hip_fail(e, "moe_route (select)");
+    return MOE_OK;
+}
+
+moe_status moe_route_quantize(const moe_cfg* cfg, const void* x, const void* w_router, const float* bias,
+                              float* logits_out, int32_t* topk_ids, float* topk_w, uint8_t* x_q, float* x_scale,
+                              void* ws, size_t ws_bytes, void* stream) {
+    moe_status st = check_cfg(cfg);
+    if (st != MOE_OK) return st;
+    const moe_cfg& c = *cfg;
+    if (c.act_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "moe_route_quantize takes bf16 x");
+    if (c.H % 128) return fail(MOE_ERR_INVALID_ARG, "moe_route_quantize needs H a multiple of 128 (H=%d)", c.H);
+    REQUIRE(x, "x");
+    REQUIRE(w_router, "w_router");
+    REQUIRE(topk_ids, "topk_ids");
+    REQUIRE(topk_w, "topk_w");
+    REQUIRE(x_q, "x_q");
+    REQUIRE(x_scale, "x_scale");
+    REQUIRE_A16(x, "x");
+    REQUIRE_A16(w_router, "w_router");
+    if (reinterpret_cast<uintptr_t>(x_q) % 8) return fail(MOE_ERR_INVALID_ARG, "x_q is not 8-byte aligned");
+    if (reinterpret_cast<uintptr_t>(x_scale) % 4) return fail(MOE_ERR_INVALID_ARG, "x_scale is not 4-byte aligned");
+    if ((st = check_ws(ws, ws_bytes, route_ws(c))) != MOE_OK) return st;
+    if (c.T == 0) return MOE_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = moe::launch_router_logits(c, x, w_router, static_cast<float*>(ws), s, x_q, x_scale);
+    if (e != hipSuccess) return hip_fail(e, "moe_route_quantize (logits)");
+    e = moe::launch_route_select(c, static_cast<const float*>(ws), moe::router_splits(c), bias, logits_out, topk_ids,
+                                 topk_w, s);
+    if (e != hipSuccess) return hip_fail(e, "moe_route_quantize (select)");
     return MOE_OK;
 }
 
@@ -750,6 +778,7 @@ moe_status moe_quantize_fp8(const moe_cfg* cfg, const void* x, uint8_t* x_q, flo
     REQUIRE(x_scale, "x_scale");
     REQUIRE_A16(x, "x");
     if (reinterpret_cast<uintptr_t>(x_q) % 8) return fail(MOE_ERR_INVALID_ARG, "x_q is not 8-byte aligned");
+    if (reinterpret_cast<uintptr_t>(x_scale) % 4) return fail(MOE_ERR_INVALID_ARG, "x_scale is not 4-byte aligned");
     hipError_t e = moe::launch_quant_rows_e4m3(x, c.T, c.H, x_q, x_scale, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "moe_quantize_fp8");
     return MOE_OK;
@@ -775,12 +804,15 @@ moe_status moe_layer(const moe_cfg* cfg, const void* w_router, const float* bias
     if ((st = check_ws(ws, ws_bytes, l.bytes)) != MOE_OK) return st;
     if (c.T == 0) return MOE_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = moe::launch_router_logits(c, x, w_router, static_cast<float*>(l.scratch), s);
+    // low-precision experts: the router also quantises x (moe_route_quantize)
+    const bool f8 = fp8_experts(c);
+    hipError_t e = moe::launch_router_logits(c, x, w_router, static_cast<float*>(l.scratch), s,
+                                             f8 ? l.x_q : nullptr, f8 ? l.x_s : nullptr);
     if (e != hipSuccess) return hip_fail(e, "moe_layer (router)");
     e = moe::launch_route_select(c, static_cast<float*>(l.scratch), moe::router_splits(c), bias, nullptr, l.ids,
                                  l.topk_w, s);
     if (e != hipSuccess) return hip_fail(e, "moe_layer (select)");
-    if (fp8_experts(c)) return layer_fp8_experts(c, *w, x, out, l, s);
+    if (f8) return layer_fp8_experts(c, *w, out, l, s);
     const moe_cfg cs = layer_stage_cfg(c);
     st = permute_enqueue(cs, x, nullptr, l.ids, l.counts, l.offsets, l.row_src, l.tok_row, l.x_perm, nullptr,
                          l.scratch, s);

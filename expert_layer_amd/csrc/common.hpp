@@ -122,10 +122,13 @@ __host__ __device__ __forceinline__ int64_t xcd_grid_runs(int64_t items) { retur
 namespace moe {
 
 // The router writes router_splits(c) K-split partial logits [split][T][E]
-// (one for fp32); route_select sums them in split order.
+// (one for fp32); route_select sums them in split order.  With x_q (bf16 x,
+// H a multiple of 128) it also writes x's per-token e4m3 codes and 1 x 128
+// scales (the rule of launch_quant_rows_e4m3) from the same pass over x.
 int router_splits(const moe_cfg& c);
 hipError_t launch_router_logits(const moe_cfg& c, const void* x, const void* w_router,
-                                float* partial_logits, hipStream_t s);
+                                float* partial_logits, hipStream_t s, uint8_t* x_q = nullptr,
+                                float* x_scale = nullptr);
 hipError_t launch_route_select(const moe_cfg& c, const float* logits, int nsplit, const float* bias,
                                float* logits_copy, int32_t* ids, float* w, hipStream_t s);
 

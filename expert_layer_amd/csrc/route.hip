@@ -13,7 +13,9 @@
 // from HBM once per 256 experts.  K is split so that T / 128 token blocks
 // still fill the chip; the splits write fp32 partial logits that route_select
 // adds in split order (a fixed order, so the result does not depend on
-// scheduling).  The kernel is bound by the HBM read of x.
+// scheduling).  The kernel is bound by the HBM read of x.  Its QUANT form also
+// writes x's per-token e4m3 codes (1 x 128 blocks) from the x tiles it already
+// holds in LDS, so that low-precision experts need no second pass over x.
 // Kernel 2 (route_select_team; route_select for other shapes): a team of 8 or
 // 16 lanes per token -- the partial logits summed, scores, group limit, top-k
 // with ties to the lower index, renormalisation and scaling.
@@ -102,6 +104,40 @@ __device__ __forceinline__ void rstage(int wave, int lane, f32x16 (&acc)[2][2]) 
     }
 }
 
+// The per-token e4m3 quantisation of one 128-column block kb of a token block:
+// thread (row, c) = (tid / 4, tid % 4) holds chunk c of each of the turn's four
+// 32-column stages, i.e. x[t][128 kb + 32 j + 8 c + i], j < 4, i < 8.  The rule
+// is moe_quantize_fp8's: s = max |x| / 448 over the block (1 for an all-zero
+// block), code = e4m3_rne_sat(x / s) with the division in fp32.
+__device__ __forceinline__ void rquant(const i32x4 (&qv)[4], int t, int T, int H, int kb, int c,
+                                       uint8_t* __restrict__ xq, float* __restrict__ xs) {
+    float v[32];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t word = (uint32_t)qv[j][i];
+            v[8 * j + 2 * i] = bf16_to_f32((uint16_t)(word & 0xFFFFu));
+            v[8 * j + 2 * i + 1] = bf16_to_f32((uint16_t)(word >> 16));
+        }
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(v[i]));
+    m = fmaxf(m, __shfl_xor(m, 1));  // the four threads of a row are adjacent lanes
+    m = fmaxf(m, __shfl_xor(m, 2));
+    const float sc = m > 0.0f ? m / 448.0f : 1.0f;
+    if (t >= T) return;
+    uint8_t* q = xq + (size_t)t * H + (size_t)kb * 128 + c * 8;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float* u = v + 8 * j;
+        const uint32_t lo = e4m3x4_rne_sat(u[0] / sc, u[1] / sc, u[2] / sc, u[3] / sc);
+        const uint32_t hi = e4m3x4_rne_sat(u[4] / sc, u[5] / sc, u[6] / sc, u[7] / sc);
+        *reinterpret_cast<uint2*>(q + j * 32) = make_uint2(lo, hi);
+    }
+    if (c == 0) xs[(size_t)t * (H / 128) + kb] = sc;
+}
+
 // partial[split][t][e] = sum over the split's K range of x[t][h] * w[e][h].
 // Workgroup: 128 tokens x 256 experts x one K range, 8 waves (two per SIMD);
 // wave w owns tokens 64 (w / 4) + [0, 64) and experts 64 (w % 4) + [0, 64).  Operands move HBM -> LDS by buffer_load ... lds through a
@@ -109,9 +145,13 @@ __device__ __forceinline__ void rstage(int wave, int lane, f32x16 (&acc)[2][2]) 
 // that fragment reads are free of bank conflicts).  Splitting K lets T / 128
 // token blocks fill the chip; the router weights are then read from L2 about
 // T / 128 times instead of once per 32 tokens.
+// QUANT: ksplit is a multiple of 128, so that each turn of four stages is one
+// 128-column block of x; the workgroups of the first expert block quantise the
+// blocks of their tokens (rquant) into xq [T][H] and xs [T][H / 128].
+template <bool QUANT>
 __global__ void __launch_bounds__(RB_THREADS)
 router_logits_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, float* __restrict__ partial,
-                   int T, int H, int E, int ksplit) {
+                   int T, int H, int E, int ksplit, uint8_t* __restrict__ xq, float* __restrict__ xs) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int t0 = blockIdx.x * RB_M, e0 = blockIdx.y * RB_N, split = blockIdx.z;
@@ -148,6 +188,12 @@ router_logits_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
     // have landed (the 6 loads of stages s+1, s+2 may still fly), one barrier
     // -- everyone's stage s has landed and everyone is done with stage s-1 --
     // refill stage s-1's buffer with stage s+3, then compute on stage s.
+    // QUANT: this thread's chunk of x in each stage of the turn (row qrow, chunk qc)
+    const bool quant = QUANT && blockIdx.y == 0;
+    const int qrow = threadIdx.x >> 2, qc = threadIdx.x & 3;
+    const int qphys = qrow * 4 + (qc ^ tile_swz(qrow));
+    i32x4 qv[4];
+
     rdma<0>(d, 0, wave);
     rdma<1>(d, 1, wave);
     rdma<2>(d, 2, wave);
@@ -160,12 +206,14 @@ router_logits_bf16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
         rdma<(J + 3) % RB_NST>(d, s + J + 3, wave);                  \
         __builtin_amdgcn_sched_barrier(0);                           \
         rstage<J>(wave, lane, acc);                                  \
+        if (quant) qv[J] = rring<J>()[qphys];                        \
         __builtin_amdgcn_sched_barrier(0);
         ROUTER_STAGE(0)
         ROUTER_STAGE(1)
         ROUTER_STAGE(2)
         ROUTER_STAGE(3)
 #undef ROUTER_STAGE
+        if (quant) rquant(qv, t0 + qrow, T, H, (d.k0 + s * RB_K) / 128, qc, xq, xs);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // no LDS DMA may outlive the workgroup
     float* out = partial + (size_t)split * T * E;
@@ -557,14 +605,20 @@ int router_splits(const moe_cfg& c) {
 }
 
 hipError_t launch_router_logits(const moe_cfg& c, const void* x, const void* w_router, float* logits,
-                                hipStream_t s) {
+                                hipStream_t s, uint8_t* x_q, float* x_scale) {
     if (c.act_dtype == MOE_BF16) {
         const int sp = router_splits(c);
-        const int ksplit = ((c.H + sp - 1) / sp + RB_K - 1) / RB_K * RB_K;
+        const int kq = x_q ? 128 : RB_K;  // quantising: whole 128-column blocks per split
+        const int ksplit = ((c.H + sp - 1) / sp + kq - 1) / kq * kq;
         dim3 grid((c.T + RB_M - 1) / RB_M, (c.E + RB_N - 1) / RB_N, sp);
-        hipLaunchKernelGGL(router_logits_bf16, grid, dim3(RB_THREADS), 0, s,
-                           static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_router),
-                           logits, c.T, c.H, c.E, ksplit);
+        if (x_q)
+            hipLaunchKernelGGL(router_logits_bf16<true>, grid, dim3(RB_THREADS), 0, s,
+                               static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_router),
+                               logits, c.T, c.H, c.E, ksplit, x_q, x_scale);
+        else
+            hipLaunchKernelGGL(router_logits_bf16<false>, grid, dim3(RB_THREADS), 0, s,
+                               static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_router),
+                               logits, c.T, c.H, c.E, ksplit, nullptr, nullptr);
     } else {
         int64_t n = (int64_t)c.T * c.E;
         hipLaunchKernelGGL(router_logits_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,

@@ -281,6 +281,21 @@ moe_status moe_route(const moe_cfg *cfg, const void *x, const void *w_router, co
                      const float *logits_in, float *logits_out, int32_t *topk_ids,
                      float *topk_w, void *ws, size_t ws_bytes, void *stream);
 
+/* moe_route on bf16 x that also writes x's per-token e4m3 quantisation, the
+ * rule and outputs of moe_quantize_fp8 (x_q [T][H] OCP e4m3 codes, x_scale
+ * [T][H/128] fp32), from the router's own pass over x: the "fp8 route" of a
+ * layer whose expert GEMMs run in fp8 (the AFD page, section 1, the figure
+ * caption on MoE MFU; section 7, W8A8), with no second read of x for the
+ * quantiser.  topk_ids, topk_w and logits_out (NULL: not written) are those of
+ * moe_route with logits_in == NULL; x_q and x_scale equal moe_quantize_fp8's
+ * bit for bit.  Takes act_dtype MOE_BF16 and H a multiple of 128; x and
+ * w_router 16-byte aligned, x_q 8-byte aligned, x_scale 4-byte aligned
+ * (MOE_ERR_INVALID_ARG otherwise).
+ * ws: moe_workspace_bytes(cfg, MOE_STAGE_ROUTE). */
+moe_status moe_route_quantize(const moe_cfg *cfg, const void *x, const void *w_router, const float *bias,
+                              float *logits_out, int32_t *topk_ids, float *topk_w, uint8_t *x_q,
+                              float *x_scale, void *ws, size_t ws_bytes, void *stream);
+
 /* Dispatch: a deterministic counting sort of the (token, choice) pairs by
  * expert (ASAP section 3.2.1: token counts per expert plus the token payload).
  *   expert_counts[e]  = #{(t, j) : topk_ids[t][j] == e}
@@ -373,8 +388,8 @@ moe_status moe_combine(const moe_cfg *cfg, const void *y_rows, const int32_t *to
  * its intermediate.  For each row t and 128-column block b of
  * x [T][H] bf16: s = max|x| / 448 over the block (1 when the block is all
  * zero), q = e4m3_rne_sat(x / s), the divisions in fp32; x_q [T][H] OCP e4m3
- * codes, x_scale [T][H/128] fp32 (x, x_q 16- and 8-byte aligned, device).
- * Takes act_dtype MOE_BF16 and H a multiple of 128. */
+ * codes, x_scale [T][H/128] fp32 (x, x_q, x_scale 16-, 8- and 4-byte
+ * aligned, device).  Takes act_dtype MOE_BF16 and H a multiple of 128. */
 moe_status moe_quantize_fp8(const moe_cfg *cfg, const void *x, uint8_t *x_q, float *x_scale, void *stream);
 
 /* The whole layer: moe_route -> moe_permute -> moe_grouped_ffn -> moe_combine,
@@ -388,7 +403,7 @@ moe_status moe_quantize_fp8(const moe_cfg *cfg, const void *x, uint8_t *x_q, flo
  * tiled.  x, w_router and out are 16-byte aligned.
  * Low-precision experts (act_dtype MOE_BF16, w_dtype MOE_FP8_E4M3 or
  * MOE_FP4_E2M1, row-major weights with their scales, x 16-byte aligned): the
- * route on bf16 x, then moe_quantize_fp8 of x, moe_permute's maps (m_tile 16,
+ * route and the quantisation of x in one pass (moe_route_quantize), moe_permute's maps (m_tile 16,
  * MOE_LAYOUT_INDEXED: the routed GEMM1 reads the e4m3 token rows and their
  * scales through row_src; for quantised tokens of 2 GiB or more, a row-major
  * x_perm with its scales), the grouped FFN over the routed rows and, with a

@@ -128,8 +128,38 @@ def test_fp8_experts_cfg():
     assert st == m.MOE_ERR_INVALID_ARG and "x_q" in m.moe_last_error()
     f8 = m.make_cfg(T=64, H=128, E=8, k=1, I=128, act_dtype=m.MOE_FP8_E4M3, y_dtype=m.MOE_BF16)
     assert lib.moe_quantize_fp8(ctypes.byref(f8), fake, fake, fake, None) == m.MOE_ERR_UNSUPPORTED
+    st = lib.moe_quantize_fp8(ctypes.byref(c), fake, fake, ctypes.c_void_p(0x100002), None)
+    assert st == m.MOE_ERR_INVALID_ARG and "x_scale" in m.moe_last_error()
     z = m.make_cfg(**dict(kw, T=0))
     assert lib.moe_quantize_fp8(ctypes.byref(z), None, None, None, None) == m.MOE_OK
+
+
+def test_route_quantize_checks_arguments():
+    """moe_route_quantize: bf16 x and H a multiple of 128, every pointer given
+    and aligned, a workspace of the route's size; all refused before a launch."""
+    lib = m._ffi.lib()
+    fake = ctypes.c_void_p(0x100000)
+    c = m.make_cfg(T=64, H=7168, E=256, k=8, I=2048, n_groups=8, topk_groups=4)
+    need = m.moe_workspace_bytes(c, m.MOE_STAGE_ROUTE)
+
+    def call(cfg, x=fake, w_r=fake, ids=fake, w=fake, xq=fake, xs=fake, ws=fake, n=need):
+        return lib.moe_route_quantize(ctypes.byref(cfg), x, w_r, None, None, ids, w, xq, xs, ws, n, None)
+
+    assert call(m.make_cfg(T=64, H=128, E=8, k=1, I=128, act_dtype=m.MOE_FP8_E4M3)) == m.MOE_ERR_UNSUPPORTED
+    assert call(m.make_cfg(T=64, H=128, E=8, k=1, I=128, act_dtype=m.MOE_F32)) == m.MOE_ERR_UNSUPPORTED
+    h = m.make_cfg(T=64, H=192, E=8, k=2, I=128)
+    assert m.moe_validate(h) == m.MOE_OK
+    assert call(h) == m.MOE_ERR_INVALID_ARG and "multiple of 128" in m.moe_last_error()
+    for kw, name in ((dict(x=None), "x"), (dict(w_r=None), "w_router"), (dict(ids=None), "topk_ids"),
+                     (dict(w=None), "topk_w"), (dict(xq=None), "x_q"), (dict(xs=None), "x_scale")):
+        assert call(c, **kw) == m.MOE_ERR_INVALID_ARG and name in m.moe_last_error()
+    for kw, name in ((dict(x=ctypes.c_void_p(0x100008)), "x"), (dict(w_r=ctypes.c_void_p(0x100008)), "w_router"),
+                     (dict(xq=ctypes.c_void_p(0x100004)), "x_q"), (dict(xs=ctypes.c_void_p(0x100002)), "x_scale")):
+        assert call(c, **kw) == m.MOE_ERR_INVALID_ARG and "aligned" in m.moe_last_error()
+        assert name in m.moe_last_error()
+    assert call(c, ws=None) == m.MOE_ERR_WORKSPACE
+    assert call(c, n=need - 1) == m.MOE_ERR_WORKSPACE
+    assert call(m.make_cfg(T=0, H=7168, E=256, k=8, I=2048), ws=None, n=0) == m.MOE_OK
 
 
 def test_status_strings():

@@ -1,5 +1,6 @@
-"""GPU parity of fp8 experts: moe_quantize_fp8 and moe_layer with bf16
-activations and e4m3 expert weights, against the oracle.
+"""GPU parity of fp8 experts: moe_quantize_fp8, the fused route and
+quantisation (moe_route_quantize) and moe_layer with bf16 activations and e4m3
+expert weights, against the oracle.
 
 The per-token quantisation is decided in fp32 on both sides from the same bf16
 values, so its codes and scales are compared bit for bit.  The layer is
@@ -18,7 +19,7 @@ import expert_layer_amd as moe
 import oracle
 import synth
 from tests._cases import cover_tokens, dev, lib_cfg, rel_err, route_kw, router_case
-from tests._np import e4m3_f64, to_np
+from tests._np import e4m3_f64, f64, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -48,6 +49,99 @@ def test_quantize_fp8_is_bit_exact():
     assert np.array_equal(xq.cpu().numpy(), q_ref)
 
 
+def _route_quantize(c, x, w_r, bias):
+    T, H, E, k = c.T, c.H, c.E, c.k
+    ids = torch.full((T, k), -7, dtype=torch.int32, device=dev())
+    w = torch.full((T, k), float("nan"), dtype=torch.float32, device=dev())
+    lg = torch.full((T, E), float("nan"), dtype=torch.float32, device=dev())
+    xq = torch.full((T, H), 0xFF, dtype=torch.uint8, device=dev())
+    xs = torch.full((T, H // 128), float("nan"), device=dev())
+    moe.moe_route_quantize(c, x, w_r, bias, lg, ids, w, xq, xs, moe.workspace(c, moe.MOE_STAGE_ROUTE, dev()))
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), w.cpu().numpy(), lg.cpu().numpy(), xq.cpu().numpy(), xs.cpu().numpy()
+
+
+def _route_on(c, x, w_r, bias, logits_in=None):
+    T, E, k = c.T, c.E, c.k
+    ids = torch.full((T, k), -7, dtype=torch.int32, device=dev())
+    w = torch.full((T, k), float("nan"), dtype=torch.float32, device=dev())
+    lg = torch.full((T, E), float("nan"), dtype=torch.float32, device=dev())
+    ws = None if logits_in is not None else moe.workspace(c, moe.MOE_STAGE_ROUTE, dev())
+    moe.moe_route(c, x, w_r, bias, logits_in, lg, ids, w, ws)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), w.cpu().numpy(), lg.cpu().numpy()
+
+
+@pytest.mark.parametrize("name,T", [
+    ("c3_dsv3_bf16", 1000),
+    ("c4_qwen3_skew_bf16", 777),
+    ("c3_dsv3_bf16", None),          # full size, T = 8192
+])
+def test_route_quantize_matches_oracle(name, T):
+    """The fused route: ids bit-exact and weights as moe_route against the
+    oracle (margin cases), codes and scales bit-exact against the oracle's
+    quantiser, and -- the K splits being whole 128-column blocks here too --
+    the same logits, ids and weights as moe_route bit for bit."""
+    s = synth.config(name)
+    rc = router_case(s, T)
+    T = rc["x"].shape[0]
+    c = lib_cfg(s, T=T)
+    ids, w, lg, xq, xs = _route_quantize(c, rc["x"], rc["w_r"], rc["bias"])
+    ref_ids, ref_w = oracle.route_select(rc["logits"], s.k, renormalize=s.renormalize,
+                                         routed_scale=s.routed_scale, bias=rc["bh"], **route_kw(s))
+    scale = np.sqrt(np.mean(rc["logits"].astype(np.float64) ** 2))
+    assert np.max(np.abs(lg - rc["logits"])) <= 2e-5 * scale
+    assert np.array_equal(ids, ref_ids)
+    assert np.max(np.abs(w - ref_w)) <= 1e-5 * s.routed_scale
+    q_ref, s_ref = oracle.quantize_rows_e4m3(rc["xh"])
+    assert np.array_equal(xs, s_ref)
+    assert np.array_equal(xq, q_ref)
+    ids2, w2, lg2 = _route_on(c, rc["x"], rc["w_r"], rc["bias"])
+    assert np.array_equal(lg2, lg) and np.array_equal(ids2, ids) and np.array_equal(w2, w)
+
+
+@pytest.mark.parametrize("T,H,E,k,groups", [
+    (131, 7168, 64, 4, 1),      # the quantiser's edge blocks; 2 token blocks, 8 K splits
+    (200, 1024, 512, 8, 8),     # two expert blocks: only the first quantises
+    (77, 640, 96, 6, 1),        # 3 K splits of whole blocks (256, 256, 128 columns): other boundaries
+    (1, 128, 8, 2, 1),          # one token, one block
+])
+def test_route_quantize_edge_shapes(T, H, E, k, groups):
+    """Shapes the workloads do not reach: codes and scales bit-exact against the
+    oracle's quantiser (with all-zero, tiny, tie and saturating blocks), logits
+    within fp32 accumulation of the oracle's, and the ids and weights exactly
+    those of moe_route's selection on the fused call's own logits."""
+    g = torch.Generator(device="cpu").manual_seed(1000 + T)
+    x = torch.randn((T, H), generator=g) * torch.exp(2.0 * torch.randn((T, H // 128, 1), generator=g)).repeat(
+        1, 1, 128).view(T, H)
+    if T > 11 and H >= 896:
+        x[3, :128] = 0.0
+        x[5, 128:256] *= 1e-30
+        mids = np.array([(a + b) / 2 for a, b in zip(e4m3_f64(np.arange(0, 0x7E)), e4m3_f64(np.arange(1, 0x7F)))])
+        blk = np.resize(mids, 128) * 8.0
+        blk[0] = 448.0 * 8.0
+        x[9, 512:640] = torch.from_numpy(blk)
+        x[9, 640:768] = -torch.from_numpy(blk)
+        x[11, 768:896] = 1e30
+    xb = x.to(torch.bfloat16)
+    w_r = (torch.randn((E, H), generator=g) * H ** -0.5).to(torch.bfloat16)
+    c = moe.make_cfg(T=T, H=H, E=E, k=k, I=128, n_groups=groups, topk_groups=min(groups, 4))
+    ids, w, lg, xq, xs = _route_quantize(c, xb.to(dev()), w_r.to(dev()), None)
+    xh = to_np(xb)
+    q_ref, s_ref = oracle.quantize_rows_e4m3(xh)
+    assert np.array_equal(xs, s_ref)
+    assert np.array_equal(xq, q_ref)
+    ref = oracle.router_logits(xh, to_np(w_r))
+    fin = np.isfinite(ref)
+    # fp32 sums of exact bf16 products: far inside 1e-4 of sum |x w|, while a
+    # 128-column block lost or counted twice moves a logit by about 128 / H of it
+    mag = np.abs(f64(xb)) @ np.abs(f64(w_r)).T
+    assert np.all((np.abs(lg.astype(np.float64) - ref) <= 1e-4 * mag)[fin])
+    ids2, w2, _ = _route_on(c, None, None, None, torch.from_numpy(lg).to(dev()))
+    assert np.array_equal(ids2, ids) and np.array_equal(w2, w)
+
+
+_W8 = {}
 _W8 = {}
 
 
