@@ -24,15 +24,15 @@ from ._ffi import (MOE_BF16, MOE_ERR_HIP, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORT
                    MOE_LAYOUT_ROWMAJOR, MOE_LAYOUT_TILED, MOE_LAYOUT_INDEXED, moe_cfg, moe_weights)
 
 __all__ = [
-    "MoeError", "make_cfg", "weights", "workspace", "moe_validate", "moe_max_rows", "moe_workspace_bytes", "moe_ffn_workspace_bytes",
-    "moe_route", "moe_route_quantize", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_quantize_fp8", "moe_layer", "moe_weight_table",
-    "weight_table", "moe_status_string",
-    "moe_last_error", "moe_cfg", "moe_weights", "lib_path",
-    "MOE_OK", "MOE_ERR_INVALID_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE", "MOE_ERR_HIP",
-    "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3", "MOE_FP4_E2M1", "MOE_SCORE_SOFTMAX", "MOE_SCORE_SIGMOID",
-    "MOE_GROUP_TOP2_SUM", "MOE_GROUP_MAX", "MOE_STAGE_ROUTE", "MOE_STAGE_PERMUTE", "MOE_STAGE_FFN",
-    "MOE_STAGE_LAYER", "MOE_LAYOUT_ROWMAJOR", "MOE_LAYOUT_TILED", "MOE_LAYOUT_INDEXED", "moe_tiled_weights_bytes",
-    "moe_tile_weights", "tile_weights", "moe_x_perm_bytes", "x_perm_buffer",
+    "MoeError", "make_cfg", "weights", "workspace", "moe_validate", "moe_max_rows", "moe_workspace_bytes",
+    "moe_ffn_workspace_bytes", "moe_route", "moe_route_quantize", "moe_permute", "moe_grouped_ffn",
+    "moe_combine", "moe_quantize_fp8", "moe_layer", "moe_weight_table", "weight_table", "moe_status_string",
+    "moe_last_error", "moe_cfg", "moe_weights", "lib_path", "MOE_OK", "MOE_ERR_INVALID_ARG",
+    "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE", "MOE_ERR_HIP", "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3",
+    "MOE_FP4_E2M1", "MOE_SCORE_SOFTMAX", "MOE_SCORE_SIGMOID", "MOE_GROUP_TOP2_SUM", "MOE_GROUP_MAX",
+    "MOE_STAGE_ROUTE", "MOE_STAGE_PERMUTE", "MOE_STAGE_FFN", "MOE_STAGE_LAYER", "MOE_LAYOUT_ROWMAJOR",
+    "MOE_LAYOUT_TILED", "MOE_LAYOUT_INDEXED", "moe_tiled_weights_bytes", "moe_tile_weights", "tile_weights",
+    "moe_x_perm_bytes", "x_perm_buffer", "moe_permute_noalloc",
 ]
 
 lib_path = _ffi.LIB_PATH

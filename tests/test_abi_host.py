@@ -153,8 +153,9 @@ def test_route_quantize_checks_arguments():
     for kw, name in ((dict(x=None), "x"), (dict(w_r=None), "w_router"), (dict(ids=None), "topk_ids"),
                      (dict(w=None), "topk_w"), (dict(xq=None), "x_q"), (dict(xs=None), "x_scale")):
         assert call(c, **kw) == m.MOE_ERR_INVALID_ARG and name in m.moe_last_error()
-    for kw, name in ((dict(x=ctypes.c_void_p(0x100008)), "x"), (dict(w_r=ctypes.c_void_p(0x100008)), "w_router"),
-                     (dict(xq=ctypes.c_void_p(0x100004)), "x_q"), (dict(xs=ctypes.c_void_p(0x100002)), "x_scale")):
+    odd8, odd4, odd2 = ctypes.c_void_p(0x100008), ctypes.c_void_p(0x100004), ctypes.c_void_p(0x100002)
+    for kw, name in ((dict(x=odd8), "x"), (dict(w_r=odd8), "w_router"), (dict(xq=odd4), "x_q"),
+                     (dict(xs=odd2), "x_scale")):
         assert call(c, **kw) == m.MOE_ERR_INVALID_ARG and "aligned" in m.moe_last_error()
         assert name in m.moe_last_error()
     assert call(c, ws=None) == m.MOE_ERR_WORKSPACE
