@@ -71,13 +71,10 @@ static_assert(kStages<0> >= 3 && kStages<0> <= 7 && kStages<1> >= 3 && kStages<1
 constexpr int kRowBlocks = BM / 32;      // 32-row MFMA blocks of a full tile
 constexpr int kBlocks16 = BM / 16;       // 16-row DMA blocks of one A stage
 static_assert(BM % 32 == 0 && kRowBlocks <= 9 && kBlocks16 <= 3 * NWAVES, "tile height");
-// A stage buffer: the tile's rows, 64 B each, then one spare 1 KiB block that
-// the surplus DMA instructions of a stage write (with no memory traffic), so
-// that every wave issues the same number of loads and waits on the same counts.
-constexpr int kSlotsA = kBlocks16 * 64;
-constexpr int kSlots = kSlotsA + 64;
-// vector-memory instructions per wave per stage: three A blocks (blocks w,
-// w + 8 and, for w < kBlocks16 - 16, w + 16) and two B fragments
+// A stage buffer: the tile's rows, 64 B each.
+constexpr int kSlots = kBlocks16 * 64;
+// vector-memory instructions per wave per stage: up to three A blocks (blocks
+// w, w + 8, w + 16 of the tile's) and two B fragments
 constexpr int kLoadsA = 3, kLoadsB = 2;
 constexpr uint32_t kOOB = 0x80000000u;   // past every descriptor (all are < 2 GiB): the load returns zero
 
@@ -194,14 +191,20 @@ struct Dma {
 };
 
 // The 16-row block of an A stage that instruction i of wave w fills: blocks
-// w and w + 8, then w + 16 while it exists; the rest write the spare block.
-__device__ __forceinline__ int a_block(int wave, int i) {
-    const int b = wave + NWAVES * i;
-    return b < kBlocks16 ? b : kBlocks16;
-}
+// w, w + 8 and w + 16.  A tile of NRB row blocks has L = min(kBlocks16, 2 NRB)
+// 16-row blocks, so wave w issues a_loads(NRB, w) = L / 8 + (w < L % 8) A
+// instructions a stage, the first that many of its three; the tile body is
+// specialised on whether the wave has the extra one, so every load it issues
+// is real and its wait counts are exact.
+__device__ __forceinline__ int a_block(int wave, int i) { return wave + NWAVES * i; }
+template <int NRB>
+constexpr int kTileBlocks16 = 2 * NRB < kBlocks16 ? 2 * NRB : kBlocks16;
+template <int NRB, bool EXTRA>
+constexpr int kLoadsAOf = kTileBlocks16<NRB> / NWAVES + (EXTRA ? 1 : 0);
 
-// A load of stage t into buffer BUF, one instruction (i of kLoadsA): row-major
-// chunks of the K tail load zero (tiled operands are zero padded).
+// A load of stage t into buffer BUF, one instruction (i of the wave's A
+// loads): row-major chunks of the K tail load zero (tiled operands are zero
+// padded).
 template <int BUF>
 __device__ __forceinline__ void dma_a1(const Dma& d, int t, int lane, int i) {
     i32x4* buf = ring<BUF>();
@@ -214,11 +217,11 @@ __device__ __forceinline__ void dma_a1(const Dma& d, int t, int lane, int i) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ra, (lds_t)(buf + a_block(wave, i) * 64), 16, off, 0, 0, 0);
 }
 
-// All A loads of stage t into buffer BUF.
-template <int BUF>
+// All NA A loads of stage t into buffer BUF.
+template <int BUF, int NA>
 __device__ __forceinline__ void dma_a(const Dma& d, int t, int lane) {
 #pragma unroll
-    for (int i = 0; i < kLoadsA; ++i) dma_a1<BUF>(d, t, lane, i);
+    for (int i = 0; i < NA; ++i) dma_a1<BUF>(d, t, lane, i);
 }
 
 // The cache policy of a buffer load with its non-temporal bit set.
@@ -250,15 +253,15 @@ __device__ __forceinline__ i32x4 read_a1(int lane, int r) {
     return buf[(r * 32 + l32) * 4 + ((KK * 2 + half) ^ swz_of_row(l32))];
 }
 
-// vmcnt after which this wave's A loads of the next stage have landed: the
+// vmcnt after which this wave's NA A loads of the next stage have landed: the
 // loads issued after them are that stage's B loads and the A and B loads of
 // the NS - 2 stages after it.
-template <int NS>
-constexpr int kWaitNextA = kLoadsB + (kLoadsA + kLoadsB) * (NS - 2);
+template <int NS, int NA>
+constexpr int kWaitNextA = kLoadsB + (NA + kLoadsB) * (NS - 2);
 // ... and, in the prologue, stage 0's A loads: every later load of NS stages.
-template <int NS>
-constexpr int kWaitFirstA = kLoadsB + (kLoadsA + kLoadsB) * (NS - 1);
-static_assert(kWaitFirstA<kStages<0>> < 64 && kWaitFirstA<kStages<1>> < 64, "vmcnt is 6 bits");
+template <int NS, int NA>
+constexpr int kWaitFirstA = kLoadsB + (NA + kLoadsB) * (NS - 1);
+static_assert(kWaitFirstA<kStages<0>, kLoadsA> < 64 && kWaitFirstA<kStages<1>, kLoadsA> < 64, "vmcnt is 6 bits");
 
 // MFMA row blocks of k step 1 issued before the stage's barrier (they read
 // registers only), so the MFMA pipe has work while the waves meet.
@@ -281,7 +284,7 @@ __device__ __forceinline__ void mma1(const i32x4& a, const i32x4& b, f32x16& c) 
 // k step (k step 1 of this stage, then k step 0 of stage s + 1 once the
 // barrier has made that buffer safe), so every read has a whole k step to
 // land; the stage's A DMA for stage s + NS is spread over the second k step.
-template <int MODE, int NRB, int BUF, bool STREAM>
+template <int MODE, int NRB, int NA, int BUF, bool STREAM>
 __device__ __forceinline__ void stage(const Dma& d, int s, int lane, i32x4 (&fa)[NRB],
                                       i32x4 (&bq)[kStages<MODE>][2], f32x16 (&acc)[kRowBlocks]) {
     constexpr int NS = kStages<MODE>;
@@ -302,7 +305,7 @@ __device__ __forceinline__ void stage(const Dma& d, int s, int lane, i32x4 (&fa)
         __builtin_amdgcn_sched_barrier(0);
     }
     wait_lgkm0();             // every read of buffer BUF by this wave has returned
-    wait_vm<kWaitNextA<NS>>();    // this wave's A loads of stage s+1 have landed
+    wait_vm<kWaitNextA<NS, NA>>();  // this wave's A loads of stage s+1 have landed
     barrier_lds();            // ... everybody's have, and everybody is done with buffer BUF
 #pragma unroll
     for (int r = 0; r < PRE; ++r) fa[r] = read_a1<NB, 0>(lane, r);
@@ -316,14 +319,14 @@ __device__ __forceinline__ void stage(const Dma& d, int s, int lane, i32x4 (&fa)
         __builtin_amdgcn_sched_barrier(0);
         fa[r] = read_a1<NB, 0>(lane, r);
         __builtin_amdgcn_sched_barrier(0);
-        if (issued_dma < kLoadsA) {
+        if (issued_dma < NA) {
             dma_a1<BUF>(d, s + NS, lane, issued_dma);
             ++issued_dma;
             __builtin_amdgcn_sched_barrier(0);
         }
     }
 #pragma unroll
-    for (int i = 0; i < kLoadsA; ++i)
+    for (int i = 0; i < NA; ++i)
         if (i >= issued_dma) dma_a1<BUF>(d, s + NS, lane, i);
     __builtin_amdgcn_sched_barrier(0);
     load_b<STREAM>(d, s + NS, bq[BUF]);  // register set BUF is free once its MFMAs have issued
@@ -335,9 +338,10 @@ __device__ __forceinline__ float* xchg_slot(int g) {
     return reinterpret_cast<float*>(ring<J>()) + g * 1024;
 }
 
-template <int MODE, int NRB, bool STREAM>
+template <int MODE, int NRB, bool EXTRA, bool STREAM>
 __device__ __forceinline__ void run_tile(const GemmArgs& p, int mt, int g, int row0, int M, int n0, int K, int N,
                                          bool shared, int nt) {
+    constexpr int NA = kLoadsAOf<NRB, EXTRA>;  // this wave's A loads a stage
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l32 = lane & 31;
@@ -372,8 +376,8 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, int mt, int g, int r
         const int blk = a_block(wave, i);       // 16-row block of the tile this instruction fills
         const int row = blk * 16 + (lane >> 2);
         const uint32_t logical8 = (uint32_t)(((lane & 3) ^ swz_of_row(row)) * 8);
-        if (blk >= kBlocks16 || blk * 16 >= NRB * 32) {
-            d.va[i] = kOOB;                     // the spare block, or rows this tile does not have
+        if (i >= NA) {
+            d.va[i] = kOOB;                     // not issued
         } else if (a_tiled) {
             d.va[i] = (uint32_t)blk * (uint32_t)KS * 1024u + (uint32_t)lane * 16u;
         } else if (a_indexed) {
@@ -429,10 +433,10 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, int mt, int g, int r
 
     static_for<0, NS>([&](auto c) {
         constexpr int t = decltype(c)::value;
-        dma_a<t>(d, t, lane);
+        dma_a<t, NA>(d, t, lane);
         load_b<STREAM>(d, t, bq[t]);
     });
-    wait_vm<kWaitFirstA<NS>>();
+    wait_vm<kWaitFirstA<NS, NA>>();
     barrier_lds();
 #pragma unroll
     for (int r = 0; r < NRB; ++r) fa[r] = read_a1<0, 0>(lane, r);
@@ -441,7 +445,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, int mt, int g, int r
     for (int s = 0; s < nturns * NS; s += NS) {
         static_for<0, NS>([&](auto c) {
             constexpr int b = decltype(c)::value;
-            stage<MODE, NRB, b, STREAM>(d, s + b, lane, fa, bq, acc);
+            stage<MODE, NRB, NA, b, STREAM>(d, s + b, lane, fa, bq, acc);
         });
     }
     wait_vm<0>();  // no LDS DMA may outlive the workgroup
@@ -589,6 +593,22 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, int mt, int g, int r
     }
 }
 
+// The tile body of this wave: whether it issues the extra A load of the
+// tile's 16-row blocks (waves w < L % 8) is uniform per wave.
+template <int MODE, int NRB, bool STREAM>
+__device__ __forceinline__ void tile_of_wave(const GemmArgs& p, int mt, int g, int row0, int M, int n0, int K,
+                                             int N, bool shared, int nt) {
+    constexpr int extra_waves = kTileBlocks16<NRB> % NWAVES;
+    if constexpr (extra_waves != 0) {
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        if (wave < extra_waves) {
+            run_tile<MODE, NRB, true, STREAM>(p, mt, g, row0, M, n0, K, N, shared, nt);
+            return;
+        }
+    }
+    run_tile<MODE, NRB, false, STREAM>(p, mt, g, row0, M, n0, K, N, shared, nt);
+}
+
 template <int MODE, bool STREAM>
 __global__ void __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2, 2)))
 ffn_gemm_bf16(GemmArgs p) {
@@ -605,15 +625,15 @@ ffn_gemm_bf16(GemmArgs p) {
     const int n0 = MODE == 0 ? nt * (BN / 2) : nt * BN;
     if (n0 >= N || M <= 0) return;
     switch ((M + 31) >> 5) {
-    case 1: run_tile<MODE, 1, STREAM>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
-    case 2: run_tile<MODE, 2, STREAM>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
-    case 3: run_tile<MODE, 3, STREAM>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
-    case 4: run_tile<MODE, 4, STREAM>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
-    case 5: run_tile<MODE, 5, STREAM>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
-    case 6: run_tile<MODE, 6, STREAM>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
-    case 7: run_tile<MODE, 7, STREAM>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
-    case 8: run_tile<MODE, 8, STREAM>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
-    default: run_tile<MODE, 9, STREAM>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
+    case 1: tile_of_wave<MODE, 1, STREAM>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
+    case 2: tile_of_wave<MODE, 2, STREAM>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
+    case 3: tile_of_wave<MODE, 3, STREAM>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
+    case 4: tile_of_wave<MODE, 4, STREAM>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
+    case 5: tile_of_wave<MODE, 5, STREAM>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
+    case 6: tile_of_wave<MODE, 6, STREAM>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
+    case 7: tile_of_wave<MODE, 7, STREAM>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
+    case 8: tile_of_wave<MODE, 8, STREAM>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
+    default: tile_of_wave<MODE, 9, STREAM>(p, mt, g, row0, M, n0, K, N, shared, nt); break;
     }
 }
 
