@@ -67,11 +67,19 @@ constexpr int kRB = TB / 16;             // 16-row MFMA blocks of a full tile
 constexpr int kChunks = TB * 8;          // 16-byte chunks of a stage's rows
 constexpr int kStage = kChunks + TB / 4; // then the stage's TB fp32 row scales
 static_assert(TB == 256, "the load slots below cover 256 rows: 4 chunk loads and 1 scale load per wave");
-constexpr int kLoadsA = 5, kLoadsB = 4;  // vector-memory instructions per wave per stage
-// vmcnt at the top of stage s: this wave's A loads of stage s (issued during
-// stage s - 2) have landed when at most the B loads of stage s + 1, the A
-// loads of stage s + 1 and the B loads of stage s + 2 are outstanding.
-constexpr int kWaitStage = kLoadsB + kLoadsA + kLoadsB;
+constexpr int kLoadsB = 4;  // B vector-memory instructions per wave per stage
+// A instructions per wave per stage: the four row-chunk loads of rows 32 w ..
+// 32 w + 31 while they are rows of the tile (w < NRB 32-row units), and the
+// row-scale load of rows 64 w .. 64 w + 63 for waves w < 4 while those are
+// (2 w < NRB).  The tile body is specialised on both, so a wave issues only
+// real loads and waits on exact counts.
+template <bool CHUNKS, bool SCALES>
+constexpr int kLoadsAOf = (CHUNKS ? 4 : 0) + (SCALES ? 1 : 0);
+// vmcnt at the top of stage s: this wave's NA A loads of stage s (issued
+// during stage s - 2) have landed when at most the B loads of stage s + 1, the
+// A loads of stage s + 1 and the B loads of stage s + 2 are outstanding.
+template <int NA>
+constexpr int kWaitStage = kLoadsB + NA + kLoadsB;
 constexpr uint32_t kOOB = 0x80000000u;   // past every descriptor (all are < 2 GiB): the load returns zero
 
 typedef __attribute__((address_space(3))) void* lds_t;
@@ -144,18 +152,20 @@ struct Dma {
     int nsteps;
 };
 
-// A load J (0..4) of stage t into buffer BUF: J < 4 fills LDS chunks
-// (4 w + J) * 64 + lane (rows (4 w + J) * 8 + lane / 8); J = 4 the row scales,
-// waves w and w + 4 both filling positions 64 (w % 4) + [0, 64) with the same
-// values (position 64 c + 4 l + j holds row 64 c + 16 j + l, so a lane's
-// scales of row blocks 4 c .. 4 c + 3 are one 16-byte chunk).
-template <int BUF, int J>
+// A load J (0..4) of stage t into buffer BUF, issued when this wave has it
+// (CHUNKS for J < 4, SCALES for J = 4): J < 4 fills LDS chunks (4 w + J) * 64
+// + lane (rows (4 w + J) * 8 + lane / 8); J = 4 the row scales of waves w < 4,
+// positions 64 w + [0, 64) (position 64 c + 4 l + j holds row 64 c + 16 j + l,
+// so a lane's scales of row blocks 4 c .. 4 c + 3 are one 16-byte chunk).
+template <int BUF, int J, bool CHUNKS, bool SCALES>
 __device__ __forceinline__ void dma_a1(const Dma& d, int t, int wave) {
     const bool real = t < d.nsteps;
     if constexpr (J < 4) {
+        if constexpr (!CHUNKS) return;
         const uint32_t off = (!real || d.va[J] == kOOB) ? kOOB : d.va[J] + (uint32_t)t * BK;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ra, (lds_t)(ring<BUF>() + (wave * 4 + J) * 64), 16, off, 0, 0, 0);
     } else {
+        if constexpr (!SCALES) return;
         const uint32_t off = (!real || d.vs == kOOB) ? kOOB : d.vs + (uint32_t)t * 4u;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rs, (lds_t)(ring<BUF>() + kChunks + (wave & 3) * 16), 4, off, 0,
                                                  0, 0);
@@ -195,7 +205,7 @@ __device__ __forceinline__ void promote(const f32x4 (&t)[2], float sa, float p0,
 // run; the stage's five A loads (stage s + 2, into the buffer stage s - 1
 // used) follow the MFMAs of the first row blocks; the register set is
 // reloaded with stage s + 3 after the last MFMA.
-template <int RB, int BUF>
+template <int RB, int BUF, bool CH, bool SC>
 __device__ __forceinline__ void stage(const Dma& d, int s, int wave, int lane, i32x8 (&b)[NS][2], float p0,
                                       float p1, f32x4 (&acc)[kRB][2]) {
     constexpr int NA = (BUF + 2) % NS;
@@ -206,7 +216,7 @@ __device__ __forceinline__ void stage(const Dma& d, int s, int wave, int lane, i
     const int plo = (2 * (lane >> 4)) ^ swz8(l16), phi = plo ^ 1;
     const int ia = l16 * 8;  // row block rb: + rb * 128
     const int is = kChunks + l16;  // row scales of row blocks 4 c .. 4 c + 3: + 16 c
-    wait_vm<kWaitStage>();  // this wave's A loads of stage s have landed
+    wait_vm<kWaitStage<kLoadsAOf<CH, SC>>>();  // this wave's A loads of stage s have landed
     barrier_lds();          // ... every wave's, and every wave is done with stage s - 1
     i32x8 a[2];
     f32x4 t[2][2];
@@ -224,20 +234,20 @@ __device__ __forceinline__ void stage(const Dma& d, int s, int wave, int lane, i
         t[rb & 1][0] = mfma_e4m3(b[BUF][0], a[rb & 1]);
         t[rb & 1][1] = mfma_e4m3(b[BUF][1], a[rb & 1]);
         switch (rb) {  // a constant: the loop is unrolled
-            case 0: dma_a1<NA, 0>(d, s + 2, wave); break;
-            case 1: dma_a1<NA, 1>(d, s + 2, wave); break;
-            case 2: dma_a1<NA, 2>(d, s + 2, wave); break;
-            case 3: dma_a1<NA, 3>(d, s + 2, wave); break;
-            case 4: dma_a1<NA, 4>(d, s + 2, wave); break;
+            case 0: dma_a1<NA, 0, CH, SC>(d, s + 2, wave); break;
+            case 1: dma_a1<NA, 1, CH, SC>(d, s + 2, wave); break;
+            case 2: dma_a1<NA, 2, CH, SC>(d, s + 2, wave); break;
+            case 3: dma_a1<NA, 3, CH, SC>(d, s + 2, wave); break;
+            case 4: dma_a1<NA, 4, CH, SC>(d, s + 2, wave); break;
             default: break;
         }
         if (rb > 0) promote(t[(rb - 1) & 1], sa[((rb - 1) / 4) & 1][(rb - 1) & 3], p0, p1, acc[rb - 1]);
         __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (RB < 2) dma_a1<NA, 1>(d, s + 2, wave);
-    if constexpr (RB < 3) dma_a1<NA, 2>(d, s + 2, wave);
-    if constexpr (RB < 4) dma_a1<NA, 3>(d, s + 2, wave);
-    if constexpr (RB < 5) dma_a1<NA, 4>(d, s + 2, wave);
+    if constexpr (RB < 2) dma_a1<NA, 1, CH, SC>(d, s + 2, wave);
+    if constexpr (RB < 3) dma_a1<NA, 2, CH, SC>(d, s + 2, wave);
+    if constexpr (RB < 4) dma_a1<NA, 3, CH, SC>(d, s + 2, wave);
+    if constexpr (RB < 5) dma_a1<NA, 4, CH, SC>(d, s + 2, wave);
     promote(t[(RB - 1) & 1], sa[((RB - 1) / 4) & 1][(RB - 1) & 3], p0, p1, acc[RB - 1]);
     __builtin_amdgcn_sched_barrier(0);
     load_b(d, s + NS, b[BUF]);  // the set is free once its MFMAs have issued
@@ -246,7 +256,7 @@ __device__ __forceinline__ void stage(const Dma& d, int s, int wave, int lane, i
 
 // Rows of a tile past the group's end load as zero and are computed with the
 // rest of their 32-row unit.
-template <int MODE, int NRB>
+template <int MODE, int NRB, bool CH, bool SC>
 __device__ __forceinline__ void run_tile(const E4m3Args& p, int g, int row0, int M, int nt) {
     constexpr int RB = 2 * NRB;
     const int lane = threadIdx.x & 63;
@@ -355,17 +365,17 @@ __device__ __forceinline__ void run_tile(const E4m3Args& p, int g, int row0, int
     // Prologue, in the steady state's issue order: B(0), A(0), B(1), A(1), B(2).
     i32x8 b[NS][2];
     load_b(d, 0, b[0]);
-    dma_a1<0, 0>(d, 0, wave);
-    dma_a1<0, 1>(d, 0, wave);
-    dma_a1<0, 2>(d, 0, wave);
-    dma_a1<0, 3>(d, 0, wave);
-    dma_a1<0, 4>(d, 0, wave);
+    dma_a1<0, 0, CH, SC>(d, 0, wave);
+    dma_a1<0, 1, CH, SC>(d, 0, wave);
+    dma_a1<0, 2, CH, SC>(d, 0, wave);
+    dma_a1<0, 3, CH, SC>(d, 0, wave);
+    dma_a1<0, 4, CH, SC>(d, 0, wave);
     load_b(d, 1, b[1]);
-    dma_a1<1, 0>(d, 1, wave);
-    dma_a1<1, 1>(d, 1, wave);
-    dma_a1<1, 2>(d, 1, wave);
-    dma_a1<1, 3>(d, 1, wave);
-    dma_a1<1, 4>(d, 1, wave);
+    dma_a1<1, 0, CH, SC>(d, 1, wave);
+    dma_a1<1, 1, CH, SC>(d, 1, wave);
+    dma_a1<1, 2, CH, SC>(d, 1, wave);
+    dma_a1<1, 3, CH, SC>(d, 1, wave);
+    dma_a1<1, 4, CH, SC>(d, 1, wave);
     load_b(d, 2, b[2]);
     // Stage s uses A buffer and B register set s % 3.  The loop body is one
     // period of the ring, entered at stage 1: at the loop head the compiler
@@ -376,19 +386,19 @@ __device__ __forceinline__ void run_tile(const E4m3Args& p, int g, int row0, int
     {
         float p0, p1;
         wscale(s, p0, p1);
-        stage<RB, 0>(d, s, wave, lane, b, p0, p1, acc);
+        stage<RB, 0, CH, SC>(d, s, wave, lane, b, p0, p1, acc);
     }
     for (;;) {
         float p0, p1;
         if (++s >= KB) break;
         wscale(s, p0, p1);
-        stage<RB, 1>(d, s, wave, lane, b, p0, p1, acc);
+        stage<RB, 1, CH, SC>(d, s, wave, lane, b, p0, p1, acc);
         if (++s >= KB) break;
         wscale(s, p0, p1);
-        stage<RB, 2>(d, s, wave, lane, b, p0, p1, acc);
+        stage<RB, 2, CH, SC>(d, s, wave, lane, b, p0, p1, acc);
         if (++s >= KB) break;
         wscale(s, p0, p1);
-        stage<RB, 0>(d, s, wave, lane, b, p0, p1, acc);
+        stage<RB, 0, CH, SC>(d, s, wave, lane, b, p0, p1, acc);
     }
     wait_vm<0>();  // the zero loads of the stages past the end land before the buffers are reused
     barrier_lds();
@@ -495,6 +505,21 @@ __device__ __forceinline__ void run_tile(const E4m3Args& p, int g, int row0, int
     }
 }
 
+// The tile body of this wave: whether it loads row chunks (w < NRB) and row
+// scales (w < 4 and 2 w < NRB) is uniform per wave.  A wave that loads scales
+// also loads chunks.
+template <int MODE, int NRB>
+__device__ __forceinline__ void tile_of_wave(const E4m3Args& p, int g, int row0, int M, int nt) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (wave < 4 && 2 * wave < NRB) run_tile<MODE, NRB, true, true>(p, g, row0, M, nt);
+    else if constexpr (NRB < NWAVES) {
+        if (wave < NRB) run_tile<MODE, NRB, true, false>(p, g, row0, M, nt);
+        else run_tile<MODE, NRB, false, false>(p, g, row0, M, nt);
+    } else {
+        run_tile<MODE, NRB, true, false>(p, g, row0, M, nt);
+    }
+}
+
 template <int MODE>
 __global__ void __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2, 2)))
 ffn_gemm_e4m3(E4m3Args p) {
@@ -507,14 +532,14 @@ ffn_gemm_e4m3(E4m3Args p) {
     const int n0 = MODE == 0 ? wl.y * (BN / 2) : wl.y * BN;
     if (n0 >= p.N || M <= 0) return;
     switch ((M + 31) / 32) {  // tile heights are multiples of 32 rows, at most 256
-        case 1: run_tile<MODE, 1>(p, g, row0, M, wl.y); break;
-        case 2: run_tile<MODE, 2>(p, g, row0, M, wl.y); break;
-        case 3: run_tile<MODE, 3>(p, g, row0, M, wl.y); break;
-        case 4: run_tile<MODE, 4>(p, g, row0, M, wl.y); break;
-        case 5: run_tile<MODE, 5>(p, g, row0, M, wl.y); break;
-        case 6: run_tile<MODE, 6>(p, g, row0, M, wl.y); break;
-        case 7: run_tile<MODE, 7>(p, g, row0, M, wl.y); break;
-        default: run_tile<MODE, 8>(p, g, row0, M, wl.y); break;
+        case 1: tile_of_wave<MODE, 1>(p, g, row0, M, wl.y); break;
+        case 2: tile_of_wave<MODE, 2>(p, g, row0, M, wl.y); break;
+        case 3: tile_of_wave<MODE, 3>(p, g, row0, M, wl.y); break;
+        case 4: tile_of_wave<MODE, 4>(p, g, row0, M, wl.y); break;
+        case 5: tile_of_wave<MODE, 5>(p, g, row0, M, wl.y); break;
+        case 6: tile_of_wave<MODE, 6>(p, g, row0, M, wl.y); break;
+        case 7: tile_of_wave<MODE, 7>(p, g, row0, M, wl.y); break;
+        default: tile_of_wave<MODE, 8>(p, g, row0, M, wl.y); break;
     }
 }
 
