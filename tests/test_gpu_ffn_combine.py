@@ -39,6 +39,9 @@ def _weights(E, H, I, dt, seed, device):
     (256, 384, [0, 0, 0], "bf16", 70, 0, moe.MOE_F32),            # only the shared expert
     (520, 264, [31, 33, 2], "bf16", 9, 3, moe.MOE_F32),           # H, I not multiples of 64
     (520, 264, [31, 33, 2], "bf16", 9, 3, moe.MOE_BF16),          # bf16 y: a last N tile of 8 columns
+    # every tile height: 1 .. 9 row blocks of 32 (one tile each), two-tile
+    # groups; the waves that issue a tile's extra A load differ by height
+    (512, 512, [16, 48, 80, 112, 144, 176, 208, 240, 272, 288, 304, 576], "bf16", 40, 0, moe.MOE_BF16),
     (512, 1024, [37, 0, 5, 130, 64, 1, 0, 67], "f32", 0, 0, moe.MOE_F32),
     (256, 512, [12, 70], "f32", 33, 0, moe.MOE_F32),
 ])

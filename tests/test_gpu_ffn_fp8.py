@@ -147,6 +147,7 @@ def _check_rows(wq, xq, xs, y, rows_by_expert):
     (384, 384, [129, 3, 260], moe.MOE_BF16, 11),                  # odd K blocks, a partial GEMM2 N tile
     (1024, 512, [600], moe.MOE_BF16, 0),                          # one expert over 3 M tiles
     (256, 128, [1, 1, 1, 1], moe.MOE_F32, 5),                     # single rows
+    (256, 256, [20, 50, 90, 120, 150, 180, 220, 256, 300], moe.MOE_BF16, 0),  # every tile height, 1 .. 8 units
 ])
 @pytest.mark.parametrize("wlayout", [moe.MOE_LAYOUT_ROWMAJOR, moe.MOE_LAYOUT_TILED])
 def test_grouped_ffn_fp8_matches_oracle(H, I, counts, ydt, extra, wlayout):
