@@ -18,7 +18,9 @@
 // 64 (w % 4) + [0, 64): TB / 32 x 4 MFMA blocks of 16 x 16 and their fp32
 // accumulators.  GEMM1: the 64 weight rows of a wave are 32 gate rows then the
 // 32 up rows of the same h columns, so h = silu(g) * u forms in registers;
-// GEMM2: 64 output columns.
+// GEMM2: 64 output columns.  A wave issues MFMAs only for the 32-row units of
+// its half that hold rows of the group (the tile body is specialised on their
+// count); the rest of its accumulators stay zero.
 // Pipeline.  K advances in stages of 128 through three A buffers [256 x 128 B |
 // 288 row scales] and two weight buffers [256 x 64 B | 8 x 256 B of E8M0
 // scales]; operands move HBM -> LDS by buffer_load ... lds, both two stages
@@ -253,18 +255,20 @@ __device__ __forceinline__ void dma_slot(const Dma& d, int t, int wave) {
 }
 
 // One K stage for the RB row blocks of 16 starting at tile row r0: every (row
-// block, column block) MFMA of this wave, promoted with the stage's row
-// scales, with the loads of stage t into A buffer NA and B buffer NB issued
-// between them.  Software-pipelined over row blocks: the fragments of rb + 1
-// are read just before the four MFMAs of rb issue, and rb - 1 is promoted
-// while they run.
+// block, column block) MFMA of this wave's first LRB row blocks (those that
+// hold rows of the tile), promoted with the stage's row scales, with the
+// loads of stage t into A buffer NA and B buffer NB issued between them (at
+// the slots of all RB row blocks, the MFMAs of the rest left out).
+// Software-pipelined over row blocks: the fragments of rb + 1 are read just
+// before the four MFMAs of rb issue, and rb - 1 is promoted while they run.
 // The weight operand is FP4 with its E8M0 scales bs applied by the MFMA; the
 // row fragment takes chunks lane / 16 and lane / 16 + 4 of the row (the K
 // order the FP4 x e4m3 form expects).
-template <int MODE, int BUF, int NA, int NB, int TB>
+template <int MODE, int BUF, int NA, int NB, int TB, int LRB>
 __device__ __forceinline__ void kstep(const Dma& d, int t_stage, int wave, int r0, int lane, const i32x8 (&b)[4],
                                       const int (&bs)[4], f32x4 (&acc)[TB / 32][4]) {
     constexpr int RB = TB / 32;
+    static_assert(LRB >= 0 && LRB <= RB, "live row blocks");
     // Every access indexes the stage buffer itself (an integer base plus a
     // constant), so the compiler can tell it from the DMA in flight into the
     // other buffers and adds no wait for it.
@@ -279,16 +283,16 @@ __device__ __forceinline__ void kstep(const Dma& d, int t_stage, int wave, int r
     auto sa = [&](int rb) { return rb < 4 ? sa_lo[rb & 3] : sa_hi[rb & 3]; };
     i32x8 a[2];
     f32x4 t[2][4];
-    a[0] = cat(buf[ia + plo], buf[ia + phi]);
+    if constexpr (LRB > 0) a[0] = cat(buf[ia + plo], buf[ia + phi]);
     __builtin_amdgcn_sched_barrier(0);
     static_assert(RB == 4 || RB == 8, "the load slots are laid out for 4 and 8 row blocks");
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         // the fragment of rb + 1 goes to the register the MFMAs of rb - 1 read
-        if (rb + 1 < RB) a[(rb + 1) & 1] = cat(buf[ia + (rb + 1) * 128 + plo], buf[ia + (rb + 1) * 128 + phi]);
+        if (rb + 1 < LRB) a[(rb + 1) & 1] = cat(buf[ia + (rb + 1) * 128 + plo], buf[ia + (rb + 1) * 128 + phi]);
+        if (rb < LRB) {
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-            t[rb & 1][cb] = mfma16x16x128_fp4_fp8(b[cb], a[rb & 1], bs[cb]);
+            for (int cb = 0; cb < 4; ++cb) t[rb & 1][cb] = mfma16x16x128_fp4_fp8(b[cb], a[rb & 1], bs[cb]);
         }
         switch (rb) {  // rb is a constant here: the loop is unrolled
             case 0: dma_slot<MODE, NA, NB, 0, TB>(d, t_stage, wave); break;
@@ -299,17 +303,18 @@ __device__ __forceinline__ void kstep(const Dma& d, int t_stage, int wave, int r
             case 5: dma_slot<MODE, NA, NB, 5, TB>(d, t_stage, wave); break;
             default: break;
         }
-        if (rb > 0) promote(t[(rb - 1) & 1], sa(rb - 1), acc[rb - 1]);
+        if (rb > 0 && rb - 1 < LRB) promote(t[(rb - 1) & 1], sa(rb - 1), acc[rb - 1]);
         __builtin_amdgcn_sched_barrier(0);
     }
-    promote(t[(RB - 1) & 1], sa(RB - 1), acc[RB - 1]);
+    if constexpr (LRB == RB) promote(t[(RB - 1) & 1], sa(RB - 1), acc[RB - 1]);
 }
 
-// Rows of a tile past the group's end load as zero and are computed like the
-// others (also by a wave whose half of the tile holds no row: its MFMAs carry
-// the stage's loads, and one load schedule for every wave keeps the compiler's
-// count of loads in flight exact).
-template <int MODE, int TB>
+// Rows of a tile past the group's end load as zero.  A wave computes the 32-row
+// units of its half of the tile that hold rows (LU of them; a wave whose half
+// holds none issues no MFMA) and accumulates zeros for the rest, while every
+// wave keeps the full load schedule, so the compiler's count of loads in
+// flight stays exact.
+template <int MODE, int TB, int LU>
 __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int M, int n0) {
     constexpr int RB = TB / 32;
     const int lane = threadIdx.x & 63;
@@ -418,7 +423,7 @@ __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int 
         read_b4<BB, TB>(q, lane, b, bs);
         wait_lgkm0();
         barrier_lds();  // every wave holds its B fragments of stage s: B buffer s % 2 is free
-        kstep<MODE, AB, (AB + 2) % 3, BB, TB>(d, s + 2, wave, r0, lane, b, bs, acc);
+        kstep<MODE, AB, (AB + 2) % 3, BB, TB, 2 * LU>(d, s + 2, wave, r0, lane, b, bs, acc);
     };
     using C0 = std::integral_constant<int, 0>;
     using C1 = std::integral_constant<int, 1>;
@@ -573,7 +578,22 @@ ffn_gemm_fp8(Fp8Args p) {
     const int g = td.x, row0 = td.y, M = td.z - td.y;
     const int n0 = MODE == 0 ? wl.y * (BN / 2) : wl.y * BN;
     if (n0 >= p.N || M <= 0) return;
-    run_tile<MODE, TB>(p, g, row0, M, n0);
+    // the 32-row units of this wave's half of the tile (rows TB / 2 * (w / 4) ..)
+    // that hold rows of the group: a uniform branch per wave
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int live = M - (wave >> 2) * (TB / 2);
+    const int lu = live <= 0 ? 0 : min((live + 31) >> 5, TB / 64);
+    switch (lu) {
+    case 0: run_tile<MODE, TB, 0>(p, g, row0, M, n0); break;
+    case 1: run_tile<MODE, TB, 1>(p, g, row0, M, n0); break;
+    case 2: run_tile<MODE, TB, 2>(p, g, row0, M, n0); break;
+    default:
+        if constexpr (TB / 64 >= 4) {
+            if (lu == 3) run_tile<MODE, TB, 3>(p, g, row0, M, n0);
+            else run_tile<MODE, TB, TB / 64>(p, g, row0, M, n0);
+        }
+        break;
+    }
 }
 
 template <int MODE>

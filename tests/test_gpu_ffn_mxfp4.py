@@ -92,6 +92,10 @@ def _run(s, counts, ydt, extra):
     (1024, 512, [600], moe.MOE_BF16, 0),                          # 256-row tiles
     (512, 384, [300, 5, 270, 0, 129], moe.MOE_F32, 3),            # 256-row tiles, ragged groups
     (256, 128, [1, 1, 1, 1], moe.MOE_F32, 5),                     # single rows
+    # every count of 32-row units holding rows in each half of a tile (the waves
+    # of a half issue MFMAs for those only): 256-row tiles, then 128-row tiles
+    (256, 256, [20, 50, 100, 140, 170, 200, 230, 256, 300], moe.MOE_BF16, 0),
+    (256, 256, [10, 40, 70, 100, 128], moe.MOE_F32, 0),
 ])
 def test_grouped_ffn_mxfp4_matches_oracle(H, I, counts, ydt, extra):
     s = synth.MoeShape("mx", T=1, H=H, E=len(counts), k=1, I=I, dtype="fp8", seed=H + 5 * I)
