@@ -6,7 +6,8 @@
 // A deterministic counting sort, no order-dependent atomics:
 //  1. perm_hist    per block of 256 tokens, an LDS histogram of expert ids;
 //  2. perm_scan    one workgroup: per expert, exclusive prefix over blocks, then
-//                  the exclusive prefix of padded counts over experts;
+//                  the exclusive prefix of padded counts over experts, and -1 in
+//                  row_src for the rows no pair fills;
 //  3. perm_scatter per block, an LDS bitmask of the tokens that chose each
 //                  expert; a pair's rank inside its expert is the population
 //                  count of the mask below its token, so rows follow ascending
@@ -41,10 +42,14 @@ perm_hist(const int32_t* __restrict__ ids, int32_t* __restrict__ hist, int T, in
 }
 
 // One workgroup of 1024 threads; thread e owns expert e (E <= 1024).  The
-// block counts are read in groups of 8 independent loads.
+// block counts are read in groups of 8 independent loads.  With row_src, the
+// rows that no pair fills -- each segment's padding up to a multiple of m_tile
+// and the rows from offsets[E] to max_rows -- get -1 here (perm_scatter
+// writes the others).
 __global__ void __launch_bounds__(1024)
 perm_scan(const int32_t* __restrict__ hist, int32_t* __restrict__ base, int32_t* __restrict__ counts,
-          int32_t* __restrict__ offsets, int nblk, int E, int m_tile) {
+          int32_t* __restrict__ offsets, int nblk, int E, int m_tile, int32_t* __restrict__ row_src,
+          int64_t max_rows) {
     __shared__ int32_t wsum[16];
     const int e = threadIdx.x, lane = e & 63, wv = e >> 6;
     int total = 0;
@@ -85,6 +90,13 @@ perm_scan(const int32_t* __restrict__ hist, int32_t* __restrict__ base, int32_t*
         }
     }
     if (e == E - 1) offsets[E] = excl + padded;
+    if (row_src) {
+        if (e < E)
+            for (int r = excl + total; r < excl + padded; ++r) row_src[r] = -1;
+        int all = 0;  // offsets[E]: the padded counts of every wave
+        for (int w = 0; w < 16; ++w) all += wsum[w];
+        for (int64_t r = all + e; r < max_rows; r += 1024) row_src[r] = -1;
+    }
 }
 
 __global__ void __launch_bounds__(256) fill_i32(int32_t* __restrict__ p, int64_t n, int32_t v) {
@@ -240,11 +252,10 @@ hipError_t launch_permute(const moe_cfg& c, const void* x, const float* x_scale,
     const int m_tile = c.m_tile > 0 ? c.m_tile : 1;
     hipLaunchKernelGGL(perm_hist, dim3(nblk), dim3(PB), c.E * sizeof(int32_t), s, ids, ws.hist, c.T, c.k,
                        c.E);
+    // rows no pair fills (m_tile padding, the tail up to max_rows) are -1 in row_src
+    const bool pad_rows = m_tile > 1 || lay.tiled || !lay.payload;
     hipLaunchKernelGGL(perm_scan, dim3(1), dim3(1024), 0, s, ws.hist, ws.base, counts, offsets, nblk, c.E,
-                       m_tile);
-    if (m_tile > 1 || lay.tiled || !lay.payload)
-        hipLaunchKernelGGL(fill_i32, dim3((unsigned)((max_rows + 255) / 256)), dim3(256), 0, s, row_src,
-                           max_rows, -1);
+                       m_tile, pad_rows ? row_src : nullptr, max_rows);
     hipLaunchKernelGGL(perm_scatter, dim3(nblk), dim3(PB), (size_t)c.E * (PB / 32) * sizeof(uint32_t), s,
                        ids, ws.base, row_src, tok_row, c.T, c.k, c.E);
     if (!lay.payload) return hipGetLastError();
