@@ -28,7 +28,7 @@
 // MFMA fragment order (the tiled weight layout below makes each wave's stage
 // one contiguous 2 KiB read).
 // Pipeline.  K advances in 32-wide stages; NS stages are in flight: NS LDS
-// buffers of 19 KiB for A, filled by buffer_load ... lds (no staging
+// buffers of 18 KiB for A, filled by buffer_load ... lds (no staging
 // registers), and NS register sets of 8 VGPRs for B.  A stage's loads are
 // issued NS - 1 stages ahead; a chunk outside the tile (rows past the expert's
 // end, columns past N, the K tail, stages past the end) carries an offset
