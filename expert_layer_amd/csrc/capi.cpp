@@ -12,6 +12,14 @@
 
 #include "common.hpp"
 
+// The layer combines inside the shared expert's GEMM2 from this many tokens
+// on (bf16 y): timed against the separate combine it ties at 4096 and 8192
+// tokens and gains 0.5% at 16384, while at 512 it costs 0.8%.
+#ifndef MOE_FUSED_COMBINE_MIN_T
+#define MOE_FUSED_COMBINE_MIN_T 4096
+#endif
+constexpr int kFusedCombineMinT = MOE_FUSED_COMBINE_MIN_T;
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -176,7 +184,7 @@ FfnCarve ffn_carve(const moe_cfg& c, int64_t n_rows_cap, void* p) {
     f.wk.nt1 = (imax + n1 - 1) / n1;
     f.wk.nt2 = (c.H + n2 - 1) / n2;
     f.wk.tiles = cv.take<int32_t>((size_t)f.max_tiles * 4);
-    f.wk.n_tiles = cv.take<int32_t>(1);
+    f.wk.n_tiles = cv.take<int32_t>(2);
     f.wk.work1 = cv.take<int32_t>((size_t)f.max_tiles * f.wk.nt1 * 2);
     f.wk.work2 = cv.take<int32_t>((size_t)f.max_tiles * f.wk.nt2 * 2);
     if (c.act_dtype == MOE_BF16) {
@@ -385,10 +393,13 @@ moe_status permute_enqueue(const moe_cfg& c, const void* x, const float* x_scale
     return MOE_OK;
 }
 
+// comb_out (with tok_row, topk_w): the bf16 path's shared expert also combines
+// into comb_out (see FfnOperands); the caller then runs no combine.
 moe_status ffn_enqueue(const moe_cfg& c, int64_t n_rows_cap, const void* x_rows, const float* x_scale,
                        const int32_t* offsets, const int32_t* row_src, const moe_weights& w, const moe::WTab& wt,
-                       const void* x_tokens, void* y_rows, void* y_shared, void* ws, hipStream_t s) {
-    moe::FfnOperands op{x_rows, x_tokens, 0, 0, y_rows, y_shared, nullptr};
+                       const void* x_tokens, void* y_rows, void* y_shared, void* ws, hipStream_t s,
+                       void* comb_out = nullptr, const int32_t* tok_row = nullptr, const float* topk_w = nullptr) {
+    moe::FfnOperands op{x_rows, x_tokens, 0, 0, y_rows, y_shared, nullptr, comb_out, tok_row, topk_w};
     const XPermGeom g = x_perm_geom(c);
     if (c.x_layout == MOE_LAYOUT_INDEXED) {
         op.row_src = row_src;
@@ -818,9 +829,14 @@ moe_status moe_layer(const moe_cfg* cfg, const void* w_router, const float* bias
                          l.scratch, s);
     if (st != MOE_OK) return st;
     const void* x_rows = cs.x_layout == MOE_LAYOUT_INDEXED ? x : l.x_perm;
+    // bf16 y with a shared expert: the shared expert's tiles own rows of out,
+    // so its GEMM2 can do the combine in its epilogue (no y_shared, no combine
+    // pass; the same arithmetic as moe_combine)
+    const bool fused = c.act_dtype == MOE_BF16 && c.has_shared && c.y_dtype == MOE_BF16 && c.T >= kFusedCombineMinT;
     st = ffn_enqueue(cs, max_rows_of(cs), x_rows, nullptr, l.offsets, l.row_src, *w, wtab_of(c, *w, 0), x, l.y_rows,
-                     l.y_shared, l.scratch, s);
+                     l.y_shared, l.scratch, s, fused ? out : nullptr, l.tok_row, l.topk_w);
     if (st != MOE_OK) return st;
+    if (fused) return MOE_OK;
     e = moe::launch_combine(c, l.y_rows, l.tok_row, l.topk_w, l.y_shared, out, s);
     if (e != hipSuccess) return hip_fail(e, "moe_layer (combine)");
     return MOE_OK;

@@ -173,7 +173,7 @@ constexpr int kFfnBmF32 = 64, kFfnN1F32 = 64, kFfnN2F32 = 64;
 // Device work lists of the grouped FFN, carved from the workspace.
 struct FfnWork {
     int32_t* tiles;    // [max_tiles] x int4 {group, row_begin, row_end, 0}
-    int32_t* n_tiles;  // [1] M tiles written
+    int32_t* n_tiles;  // [2] M tiles written; of them the routed groups' (first in the list)
     int32_t* work1;    // [max_tiles * nt1] x int2 {M tile, N tile} of GEMM1
     int32_t* work2;    // [max_tiles * nt2] x int2 {M tile, N tile} of GEMM2
     int nt1, nt2;      // N tiles per M tile of GEMM1 / GEMM2
@@ -211,6 +211,13 @@ struct FfnOperands {
     void* y_rows;
     void* y_shared;
     const int32_t* row_src;  // non-NULL: x_rows is x [T][H], row r is token row_src[r] / k
+    // comb_out non-NULL (bf16 y, a shared expert): the shared expert's GEMM2
+    // also combines -- out [T][H] (cfg out_dtype) = sum_j topk_w[t][j] *
+    // y_rows[tok_row[t][j]] + the shared expert's y, rounded to bf16 -- and
+    // y_shared is not written
+    void* comb_out;
+    const int32_t* tok_row;
+    const float* topk_w;
 };
 hipError_t launch_gemm_bf16(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_cap, const FfnOperands& op,
                             const int32_t* offsets, const moe_weights& w, const WTab& wt, const FfnWork& wk,

@@ -22,6 +22,10 @@
 //          32 (w % 4) .. +31 of the tile; the pair meets through LDS at the
 //          end and the gate wave forms h = silu(g) * u.
 //   GEMM2: 256 output columns of y = h . w_down^T, fp32 or bf16.
+//   GEMM2 with the combine (MODE 2, the layer's shared group, launched after
+//          the routed groups' GEMM2): the shared expert's tile rows are token
+//          rows, so the epilogue writes out = sum_j w_j y_j + y_shared itself
+//          (the dispatch's counterpart of the fused row gather in GEMM1).
 // Operand paths.  The rows (A) are shared by the eight waves and go through
 // LDS; the weight rows of a wave are read by that wave alone, so they skip LDS
 // and stream from HBM straight into a ring of register sets, one per stage, in
@@ -172,6 +176,15 @@ struct GemmArgs {
     int h_slot_ks;             // k blocks of one h tile slot (ceil(max(I, I_sh) / 32))
     WTab wt;                   // wt.tab != NULL: w0 / w1 of group g are table entries slot0 / slot1
     int slot0, slot1;
+    int part;                  // work items: 0 all, 1 the routed groups', 2 the shared group's
+    // MODE 2 (the shared group's GEMM2 with the combine): out[t] = sum_j w[t][j] *
+    // y_rows[tok_row[t][j]] + y_shared[t], y_shared the tile's own result
+    // rounded to bf16, and y_rows the routed GEMM2's bf16 output
+    const uint16_t* y_routed;
+    const int32_t* tok_row;
+    const float* topk_w;
+    void* comb_out;
+    int comb_k, comb_out_f32;
 };
 
 // Per-tile load state.  A: the buffer descriptor, the byte offsets of this
@@ -352,9 +365,9 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, int mt, int g, int r
     d.nsteps = KS;
     d.kvalid_last = (uint32_t)(K - (KS - 1) * BK);
     // ---- A: rows row0 .. row0+M of this group
-    const bool a_tiled = MODE == 1 || (shared ? p.a_tiled_shared : p.a_tiled_routed);
+    const bool a_tiled = MODE != 0 || (shared ? p.a_tiled_shared : p.a_tiled_routed);
     d.a_rm = !a_tiled;
-    if (MODE == 1) {
+    if (MODE != 0) {
         // GEMM2 reads the h tile slot of this M tile, written tiled by GEMM1
         const uint16_t* A = (shared ? p.a_shared : p.a_routed) + (size_t)mt * kBlocks16 * p.h_slot_ks * 512;
         d.ra = make_rsrc(A, (uint32_t)((NRB * 2) * KS * 1024));
@@ -526,6 +539,89 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, int mt, int g, int r
             }
             barrier_lds();  // the round's slots are read before the next round writes them
         });
+    } else if (MODE == 2) {
+        // The combine, for the tile's tokens (the shared group's tile row r is
+        // token row0 + r) and columns n0 .. n0 + 255: the shared term is staged
+        // one 32-row block at a time by all eight waves as bf16 -- the value
+        // the GEMM2 store of y_shared would hold -- into a [32 rows][256
+        // columns] image (as the bf16 y store below: chunk c of row r at
+        // c ^ (((r >> 2) & 3) << 2), two buffers, one barrier a block); then
+        // each thread takes two 8-column chunks of the block, issues the loads
+        // of the token's k routed rows, sums w_j * y_j in slot order with fp32
+        // multiply-adds, adds the shared term last and stores the output row
+        // chunk: the arithmetic of combine_kernel, so the result is the same.
+        const int cl = wg * 64 + wc * 32 + l32;
+        const int tid = threadIdx.x;
+        const int K8 = p.comb_k;
+#pragma unroll
+        for (int r = 0; r < NRB; ++r) {
+            uint16_t* st = reinterpret_cast<uint16_t*>(r & 1 ? ring<1>() : ring<0>());
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int row = c_row(i, lane);
+                st[row * 256 + (((cl >> 3) ^ (((row >> 2) & 3) << 2)) << 3) + (cl & 7)] = f32_to_bf16(acc[r][i]);
+            }
+            __syncthreads();
+            const i32x4* sv = reinterpret_cast<const i32x4*>(st);
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const int id = h2 * NTH + tid;
+                const int row = id >> 5, c = id & 31, grow = r * 32 + row, col = n0 + c * 8;
+                if (grow >= M || col >= N) continue;
+                const int t = row0 + grow;
+                float a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                if (K8 == 8) {
+                    i32x4 ys[8];
+                    float wj[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const int yr = p.tok_row[(size_t)t * 8 + j];
+                        wj[j] = p.topk_w[(size_t)t * 8 + j];
+                        ys[j] = __builtin_nontemporal_load(
+                            reinterpret_cast<const i32x4*>(p.y_routed + (size_t)yr * N + col));
+                    }
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const uint32_t u = (uint32_t)ys[j][q];
+                            a[2 * q] = fmaf(wj[j], __uint_as_float(u << 16), a[2 * q]);
+                            a[2 * q + 1] = fmaf(wj[j], __uint_as_float(u & 0xFFFF0000u), a[2 * q + 1]);
+                        }
+                } else {
+                    for (int j = 0; j < K8; ++j) {
+                        const int yr = p.tok_row[(size_t)t * K8 + j];
+                        const float w = p.topk_w[(size_t)t * K8 + j];
+                        const i32x4 y = __builtin_nontemporal_load(
+                            reinterpret_cast<const i32x4*>(p.y_routed + (size_t)yr * N + col));
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const uint32_t u = (uint32_t)y[q];
+                            a[2 * q] = fmaf(w, __uint_as_float(u << 16), a[2 * q]);
+                            a[2 * q + 1] = fmaf(w, __uint_as_float(u & 0xFFFF0000u), a[2 * q + 1]);
+                        }
+                    }
+                }
+                const i32x4 sh = sv[row * 32 + (c ^ (((row >> 2) & 3) << 2))];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t u = (uint32_t)sh[q];
+                    a[2 * q] += __uint_as_float(u << 16);
+                    a[2 * q + 1] += __uint_as_float(u & 0xFFFF0000u);
+                }
+                if (p.comb_out_f32) {
+                    f32x4* o = reinterpret_cast<f32x4*>(static_cast<float*>(p.comb_out) + (size_t)t * N + col);
+                    o[0] = f32x4{a[0], a[1], a[2], a[3]};
+                    o[1] = f32x4{a[4], a[5], a[6], a[7]};
+                } else {
+                    i32x4 o;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        o[q] = (int)((uint32_t)f32_to_bf16(a[2 * q]) | ((uint32_t)f32_to_bf16(a[2 * q + 1]) << 16));
+                    *reinterpret_cast<i32x4*>(static_cast<uint16_t*>(p.comb_out) + (size_t)t * N + col) = o;
+                }
+            }
+        }
     } else if (!p.out_f32) {
         // bf16 y through LDS, one 32-row block at a time, by all eight waves
         // into one [32 rows][256 columns] image (two buffers, one barrier a
@@ -612,8 +708,13 @@ __device__ __forceinline__ void tile_of_wave(const GemmArgs& p, int mt, int g, i
 template <int MODE, bool STREAM>
 __global__ void __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2, 2)))
 ffn_gemm_bf16(GemmArgs p) {
-    const int L = xcd_remap_runs(blockIdx.x, p.n_tiles[0] * p.NT);
-    if (L < 0) return;
+    // the launch's items: all, the routed groups' (the first n_tiles[1] M tiles)
+    // or the shared group's (the rest)
+    const int tot = p.n_tiles[0] * p.NT, nr = p.part == 0 ? tot : p.n_tiles[1] * p.NT;
+    const int base = p.part == 2 ? nr : 0, cnt = p.part == 0 ? tot : (p.part == 1 ? nr : tot - nr);
+    const int L0 = xcd_remap_runs(blockIdx.x, cnt);
+    if (L0 < 0) return;
+    const int L = base + L0;
     if (p.wt.tab && wtab_layer(p.wt) < 0) return;
     const int2 wl = p.work[L];
     const int mt = wl.x, nt = wl.y;
@@ -736,7 +837,10 @@ ffn_build_tiles(const int32_t* __restrict__ offsets, int E, int has_shared, int 
     };
     emit(work1, nt1);
     emit(work2, nt2);
-    if (blockIdx.x == 0 && tid == 0) n_tiles[0] = total;
+    if (blockIdx.x == 0 && tid == 0) {
+        n_tiles[0] = total;
+        n_tiles[1] = E > 0 ? gend[E - 1] : 0;  // the routed groups' M tiles come first
+    }
 }
 
 hipError_t launch_build_tiles(const moe_cfg& c, const int32_t* offsets, int bm, int64_t rows_cap,
@@ -820,7 +924,26 @@ hipError_t launch_gemm_bf16(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_
     a.N_shared = c.H;
     a.NT = wk.nt2;
     a.out_f32 = c.y_dtype == MOE_F32;
-    hipLaunchKernelGGL((ffn_gemm_bf16<1, false>), dim3((unsigned)xcd_grid_runs(max_tiles * a.NT)), dim3(NTH), 0, s, a);
+    const dim3 g2((unsigned)xcd_grid_runs(max_tiles * a.NT));
+    if (!(op.comb_out && has_sh && c.y_dtype == MOE_BF16)) {
+        hipLaunchKernelGGL((ffn_gemm_bf16<1, false>), g2, dim3(NTH), 0, s, a);
+        return hipGetLastError();
+    }
+    // with the combine: the routed groups' GEMM2, then the shared group's with
+    // the combine in its epilogue (its tiles own rows of out: tile row r is
+    // token row0 + r)
+    a.part = 1;
+    hipLaunchKernelGGL((ffn_gemm_bf16<1, false>), g2, dim3(NTH), 0, s, a);
+    a.part = 2;
+    a.out_shared = nullptr;
+    a.y_routed = static_cast<const uint16_t*>(op.y_rows);
+    a.tok_row = op.tok_row;
+    a.topk_w = op.topk_w;
+    a.comb_out = op.comb_out;
+    a.comb_k = c.k;
+    a.comb_out_f32 = c.out_dtype == MOE_F32;
+    const int64_t sh_tiles = (c.T + BM - 1) / BM;  // the shared group's M tiles
+    hipLaunchKernelGGL((ffn_gemm_bf16<2, false>), dim3((unsigned)xcd_grid_runs(sh_tiles * a.NT)), dim3(NTH), 0, s, a);
     return hipGetLastError();
 }
 

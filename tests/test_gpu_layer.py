@@ -217,27 +217,46 @@ def test_layer_full_size_tokens(name):
         assert torch.equal(out_r.view(torch.int16), out_b.view(torch.int16))
 
 
+@pytest.mark.parametrize("ydt", [moe.MOE_F32, moe.MOE_BF16])
 @pytest.mark.parametrize("layout", [moe.MOE_LAYOUT_TILED, moe.MOE_LAYOUT_INDEXED])
 @pytest.mark.parametrize("shape", [
     synth.config("c3_dsv3_bf16").with_(T=300),
     synth.config("c2_mixtral_bf16").with_(T=200),
     # H and I not multiples of 32: the tiled rows carry zero column padding
     synth.MoeShape("ragged_shared", T=77, H=520, E=6, k=2, I=264, shared=True, I_shared=136, seed=9),
+    # from 4096 tokens on, bf16 y with a shared expert: the combine inside the
+    # shared expert's GEMM2 (k = 2)
+    synth.MoeShape("ragged_shared_4k", T=4100, H=520, E=6, k=2, I=264, shared=True, I_shared=136, seed=10),
 ])
-def test_layer_equals_its_stage_calls(shape, layout):
+def test_layer_equals_its_stage_calls(shape, layout, ydt):
     """moe_layer is route -> permute -> grouped_ffn -> combine run with m_tile
     16 and the indexed x_perm: the four stage calls with that cfg give the same
     bits; so do they with the tiled x_perm (the GEMM's arithmetic does not
-    depend on where its operands come from), and they match the oracle."""
-    s = shape
+    depend on where its operands come from), and they match the oracle.  With
+    bf16 y and a shared expert the layer combines inside the shared expert's
+    GEMM2 (its tiles own rows of out), with the arithmetic of moe_combine: the
+    same bits again."""
+    _layer_vs_stages(shape, layout, ydt)
+
+
+def test_layer_equals_its_stage_calls_full_size():
+    """The benchmarked configuration at full c3 size (T = 8192: the combine
+    inside the shared expert's GEMM2, k = 8): the same bits as the stage calls
+    with moe_combine, and a covering token subset against the oracle."""
+    s = synth.config("c3_dsv3_bf16")
+    _layer_vs_stages(s, moe.MOE_LAYOUT_INDEXED, moe.MOE_BF16, n_oracle=64)
+
+
+def _layer_vs_stages(s, layout, ydt, n_oracle=None):
     rc = router_case(s, s.T)
     T = rc["x"].shape[0]
     (wg, wu, wd), sh = _weights(s)
     shg, shu, shd = sh if sh else (None, None, None)
     w = moe.weights(wg, wu, wd, sh_gate=shg, sh_up=shu, sh_down=shd)
     w, _buf = moe.tile_weights(lib_cfg(s, T=T), w, dev())
-    layer = _run_layer(s, rc, T, moe.MOE_F32, moe.MOE_BF16, tiled=True)
-    c = lib_cfg(s, T=T, y_dtype=moe.MOE_F32, out_dtype=moe.MOE_BF16, m_tile=16, x_layout=layout)
+    layer = _run_layer(s, rc, T, ydt, moe.MOE_BF16, tiled=True)
+    c = lib_cfg(s, T=T, y_dtype=ydt, out_dtype=moe.MOE_BF16, m_tile=16, x_layout=layout)
+    ytd = torch.float32 if ydt == moe.MOE_F32 else torch.bfloat16
     rows = moe.moe_max_rows(c)
     i32 = dict(dtype=torch.int32, device=dev())
     ids, tw = torch.empty((T, s.k), **i32), torch.empty((T, s.k), dtype=torch.float32, device=dev())
@@ -246,8 +265,8 @@ def test_layer_equals_its_stage_calls(shape, layout):
     x_perm = moe.x_perm_buffer(c, dev())
     assert x_perm.numel() == max(moe.moe_x_perm_bytes(c), 1)
     x_perm.fill_(0xFF)  # NaN bf16 pattern: everything the FFN reads must be written by permute
-    y_rows = torch.empty((rows, s.H), dtype=torch.float32, device=dev())
-    y_sh = torch.empty((T, s.H), dtype=torch.float32, device=dev()) if s.shared else None
+    y_rows = torch.empty((rows, s.H), dtype=ytd, device=dev())
+    y_sh = torch.empty((T, s.H), dtype=ytd, device=dev()) if s.shared else None
     out = torch.empty((T, s.H), dtype=torch.bfloat16, device=dev())
     moe.moe_route(c, rc["x"], rc["w_r"], rc["bias"], None, None, ids, tw,
                   moe.workspace(c, moe.MOE_STAGE_ROUTE, dev()))
@@ -259,7 +278,11 @@ def test_layer_equals_its_stage_calls(shape, layout):
     moe.moe_combine(c, y_rows, tok_row, tw, y_sh, out)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), layer.view(torch.int16))
-    assert rel_err_bf16_out(out.float().cpu().numpy(), _oracle_tokens(s, rc, np.arange(T))) <= 1e-2
+    toks = np.arange(T) if n_oracle is None else np.unique(
+        np.linspace(0, T - 1, n_oracle).astype(int))
+    got = out[torch.as_tensor(toks, device=dev())].float().cpu().numpy().astype(np.float64)
+    ref, mag = _oracle_tokens(s, rc, toks, absum=True)
+    assert _err(got, ref, mag, ydt, moe.MOE_BF16) <= 1e-2  # beyond the bf16 stores of y and out
 
 
 def test_layer_is_deterministic():
