@@ -184,7 +184,7 @@ FfnCarve ffn_carve(const moe_cfg& c, int64_t n_rows_cap, void* p) {
     f.wk.nt1 = (imax + n1 - 1) / n1;
     f.wk.nt2 = (c.H + n2 - 1) / n2;
     f.wk.tiles = cv.take<int32_t>((size_t)f.max_tiles * 4);
-    f.wk.n_tiles = cv.take<int32_t>(2);
+    f.wk.n_tiles = cv.take<int32_t>(moe::kFfnCtlWords);
     f.wk.work1 = cv.take<int32_t>((size_t)f.max_tiles * f.wk.nt1 * 2);
     f.wk.work2 = cv.take<int32_t>((size_t)f.max_tiles * f.wk.nt2 * 2);
     if (c.act_dtype == MOE_BF16) {

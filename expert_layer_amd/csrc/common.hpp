@@ -103,16 +103,108 @@ __host__ __device__ __forceinline__ int64_t xcd_grid(int64_t items) { return (it
 // shares its L2; at any time the eight XCDs work on eight neighbouring runs,
 // whose common panels (the weights of one expert, the row panels of its M
 // tiles) the whole chip then reads from the memory-side cache instead of HBM.
-// Every L < n_valid is reached exactly once for a grid of xcd_grid_runs(items)
-// blocks, n_valid <= items; -1 for idle blocks.
+// The last, partial round of eight runs is split evenly over the XCDs, so that
+// their shares differ by at most one tile.  Every L < n_valid is reached
+// exactly once for a grid of xcd_grid_runs(items) blocks, n_valid <= items; -1
+// for idle blocks.
 __host__ __device__ __forceinline__ int xcd_remap_runs(int b, int n_valid) {
-    constexpr int kXcd = 8, kRun = 32;
-    if (n_valid <= kXcd * kRun) return xcd_remap(b, n_valid);
-    const int x = b % kXcd, i = b / kXcd;
-    const int L = ((i / kRun) * kXcd + x) * kRun + i % kRun;
-    return L < n_valid ? L : -1;
+    constexpr int kXcd = 8, kRun = 32, kRound = kXcd * kRun;
+    if (n_valid <= kRound) return xcd_remap(b, n_valid);
+    const int x = b % kXcd, i = b / kXcd, r = i / kRun, full = n_valid / kRound;
+    if (r < full) return (r * kXcd + x) * kRun + i % kRun;
+    const int rem = n_valid - full * kRound, per = (rem + kXcd - 1) / kXcd, j = i - r * kRun;
+    const int L = full * kRound + x * per + j;
+    return r == full && j < per && L < n_valid ? L : -1;
 }
 __host__ __device__ __forceinline__ int64_t xcd_grid_runs(int64_t items) { return (items + 255) / 256 * 256; }
+
+// The tiles of XCD x's share in xcd_remap_runs order: its block i = b / 8
+// takes the share's i-th tile for i < xcd_share(x, n_valid).
+__host__ __device__ __forceinline__ int xcd_share(int x, int n_valid) {
+    constexpr int kXcd = 8, kRun = 32, kRound = kXcd * kRun;
+    const bool small = n_valid <= kRound;
+    const int full = small ? 0 : n_valid / kRound, rem = n_valid - full * kRound;
+    const int per = (rem + kXcd - 1) / kXcd, left = rem - x * per;
+    return full * kRun + (left < 0 ? 0 : (left < per ? left : per));
+}
+
+// Work queues.  The XCDs of one chip do not run equally fast (their clocks and
+// their share of the memory traffic differ), so a static split of a grouped
+// GEMM's work items leaves the faster XCDs idle at the end.  The grouped GEMMs
+// therefore hand out the last kQueueTail tiles of each XCD's share at run
+// time: block i = b / 8 of XCD x = b % 8 takes the i-th tile of its share while
+// i < S = xcd_share(7, n) - kQueueTail (the smallest share less the tail; no
+// atomics), and the blocks after that draw tiles S, S + 1, ... of a share from
+// that share's counter -- their own XCD's first, then the other XCDs' -- so an
+// XCD whose workgroups finish sooner takes more of the last tiles.  A queue is
+// 8 counters and a mask of the shares found empty; the tile builder zeroes
+// them.  The grid is xcd_queue_grid(items): xcd_grid_runs plus 8 kQueueTail
+// blocks, which gives every XCD at least S + kQueueTail blocks, so that a fast
+// XCD can take up to twice its own tail.  Each tile is taken exactly once:
+// tiles below S by the one block that owns them, the others by the one counter
+// value that names them.  A block makes at most nine atomic accesses, so every
+// block ends.
+constexpr int kQueueTail = 64;
+constexpr int kQueueWords = 9;
+constexpr int kQueueSets = 3;  // GEMM1, GEMM2 (routed groups or all), GEMM2 of the shared group
+__host__ __device__ __forceinline__ int64_t xcd_queue_grid(int64_t items) {
+    return items > 0 ? xcd_grid_runs(items) + 8 * kQueueTail : 0;
+}
+__host__ __device__ __forceinline__ int xcd_queue_static(int n_valid) {
+    const int s = xcd_share(7, n_valid) - kQueueTail;
+    return s > 0 ? s : 0;
+}
+// The logical tile of block b (-1: none).  Q gives the queue's three atomic
+// accesses: empty() reads the mask, draw(y) takes the next value of counter y,
+// mark(y) sets bit y of the mask.
+template <class Q>
+__host__ __device__ __forceinline__ int xcd_queue_pick(int b, int n_valid, Q& q) {
+    const int x = b & 7, i = b >> 3, S = xcd_queue_static(n_valid);
+    if (i < S) return xcd_remap_runs(b, n_valid);
+    const int empty = q.empty();
+    for (int d = 0; d < 8; ++d) {
+        const int y = (x + d) & 7;
+        if ((empty >> y) & 1) continue;
+        const int j = q.draw(y) + S;
+        if (j < xcd_share(y, n_valid)) return xcd_remap_runs(j * 8 + y, n_valid);
+        q.mark(y);
+    }
+    return -1;
+}
+#if defined(__HIP__)
+// A queue in device memory, used by every lane of one wave: lane 0 makes the
+// accesses (device scope, so the XCDs' L2s see one counter) and the wave
+// shares their results.
+struct XcdQueue {
+    int* c;
+    bool lane0;
+    __device__ int empty() {
+        int e = 0;
+        if (lane0) e = __hip_atomic_load(&c[8], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return __builtin_amdgcn_readfirstlane(e);
+    }
+    __device__ int draw(int y) {
+        int j = 0;
+        if (lane0) j = atomicAdd(&c[y], 1);
+        return __builtin_amdgcn_readfirstlane(j);
+    }
+    __device__ void mark(int y) {
+        if (lane0) atomicOr(&c[8], 1 << y);
+    }
+};
+// The tile of the calling workgroup: wave 0 picks it, and every thread
+// returns it.  Call at the top of the kernel (it uses __syncthreads).
+__device__ __forceinline__ int xcd_queue_tile(int n_valid, int* queue) {
+    __shared__ int s_tile;
+    if (threadIdx.x < 64) {
+        XcdQueue q{queue, threadIdx.x == 0};
+        const int L = xcd_queue_pick((int)blockIdx.x, n_valid, q);
+        if (threadIdx.x == 0) s_tile = L;
+    }
+    __syncthreads();
+    return s_tile;
+}
+#endif
 
 }  // namespace moe
 
@@ -171,9 +263,11 @@ constexpr int kFfnBmFp8 = 224, kFfnBmFp8Small = 128, kFfnBmE4m3 = 256;
 constexpr int kFfnBmF32 = 64, kFfnN1F32 = 64, kFfnN2F32 = 64;
 
 // Device work lists of the grouped FFN, carved from the workspace.
+constexpr int kFfnCtlWords = 2 + kQueueSets * kQueueWords;
 struct FfnWork {
     int32_t* tiles;    // [max_tiles] x int4 {group, row_begin, row_end, 0}
-    int32_t* n_tiles;  // [2] M tiles written; of them the routed groups' (first in the list)
+    int32_t* n_tiles;  // [kFfnCtlWords]: M tiles written; of them the routed groups' (first in the
+                       // list); then the kQueueSets work queues of the launches (kQueueWords each)
     int32_t* work1;    // [max_tiles * nt1] x int2 {M tile, N tile} of GEMM1
     int32_t* work2;    // [max_tiles * nt2] x int2 {M tile, N tile} of GEMM2
     int nt1, nt2;      // N tiles per M tile of GEMM1 / GEMM2

@@ -162,6 +162,7 @@ struct GemmArgs {
     void* out_shared;          // GEMM1: h tile slots; GEMM2: y_shared
     const int4* tiles;
     const int32_t* n_tiles;
+    int32_t* queue;            // the launch's work queue (see xcd_queue_pick)
     const int2* work;          // {M tile, N tile} in launch order
     int E;
     int NT;                    // N tiles per M tile in the launch grid
@@ -712,7 +713,7 @@ ffn_gemm_bf16(GemmArgs p) {
     // or the shared group's (the rest)
     const int tot = p.n_tiles[0] * p.NT, nr = p.part == 0 ? tot : p.n_tiles[1] * p.NT;
     const int base = p.part == 2 ? nr : 0, cnt = p.part == 0 ? tot : (p.part == 1 ? nr : tot - nr);
-    const int L0 = xcd_remap_runs(blockIdx.x, cnt);
+    const int L0 = xcd_queue_tile(cnt, p.queue);
     if (L0 < 0) return;
     const int L = base + L0;
     if (p.wt.tab && wtab_layer(p.wt) < 0) return;
@@ -837,6 +838,8 @@ ffn_build_tiles(const int32_t* __restrict__ offsets, int E, int has_shared, int 
     };
     emit(work1, nt1);
     emit(work2, nt2);
+    // the work queues of the launches that follow start empty
+    if (blockIdx.x == 0 && tid >= 2 && tid < kFfnCtlWords) n_tiles[tid] = 0;
     if (blockIdx.x == 0 && tid == 0) {
         n_tiles[0] = total;
         n_tiles[1] = E > 0 ? gend[E - 1] : 0;  // the routed groups' M tiles come first
@@ -901,7 +904,8 @@ hipError_t launch_gemm_bf16(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_
     // the tiles of a block share each weight panel through L2, so the default
     // policy stays; GEMM2 keeps it always.
     const bool stream_w = n_rows_cap <= (int64_t)c.E * BM;
-    const dim3 g1((unsigned)xcd_grid_runs(max_tiles * a.NT));
+    a.queue = wk.n_tiles + 2;  // queue 0
+    const dim3 g1((unsigned)xcd_queue_grid(max_tiles * a.NT));
     if (stream_w) hipLaunchKernelGGL((ffn_gemm_bf16<0, true>), g1, dim3(NTH), 0, s, a);
     else hipLaunchKernelGGL((ffn_gemm_bf16<0, false>), g1, dim3(NTH), 0, s, a);
     // GEMM2: down -> y
@@ -924,7 +928,8 @@ hipError_t launch_gemm_bf16(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_
     a.N_shared = c.H;
     a.NT = wk.nt2;
     a.out_f32 = c.y_dtype == MOE_F32;
-    const dim3 g2((unsigned)xcd_grid_runs(max_tiles * a.NT));
+    a.queue = wk.n_tiles + 2 + kQueueWords;  // queue 1
+    const dim3 g2((unsigned)xcd_queue_grid(max_tiles * a.NT));
     if (!(op.comb_out && has_sh && c.y_dtype == MOE_BF16)) {
         hipLaunchKernelGGL((ffn_gemm_bf16<1, false>), g2, dim3(NTH), 0, s, a);
         return hipGetLastError();
@@ -935,6 +940,7 @@ hipError_t launch_gemm_bf16(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_
     a.part = 1;
     hipLaunchKernelGGL((ffn_gemm_bf16<1, false>), g2, dim3(NTH), 0, s, a);
     a.part = 2;
+    a.queue = wk.n_tiles + 2 + 2 * kQueueWords;  // queue 2
     a.out_shared = nullptr;
     a.y_routed = static_cast<const uint16_t*>(op.y_rows);
     a.tok_row = op.tok_row;
@@ -943,7 +949,7 @@ hipError_t launch_gemm_bf16(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_
     a.comb_k = c.k;
     a.comb_out_f32 = c.out_dtype == MOE_F32;
     const int64_t sh_tiles = (c.T + BM - 1) / BM;  // the shared group's M tiles
-    hipLaunchKernelGGL((ffn_gemm_bf16<2, false>), dim3((unsigned)xcd_grid_runs(sh_tiles * a.NT)), dim3(NTH), 0, s, a);
+    hipLaunchKernelGGL((ffn_gemm_bf16<2, false>), dim3((unsigned)xcd_queue_grid(sh_tiles * a.NT)), dim3(NTH), 0, s, a);
     return hipGetLastError();
 }
 

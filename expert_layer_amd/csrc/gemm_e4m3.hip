@@ -130,6 +130,7 @@ struct E4m3Args {
     float* out_scale;       // GEMM1: h scales [rows][I / 128]
     const int4* tiles;
     const int32_t* n_tiles;
+    int32_t* queue;  // the launch's work queue (see xcd_queue_pick)
     const int2* work;       // {M tile, N tile} in launch order
     int NT;                 // N tiles per M tile
     int K, N;               // GEMM1: K = H, N = I; GEMM2: K = I, N = H
@@ -523,7 +524,7 @@ __device__ __forceinline__ void tile_of_wave(const E4m3Args& p, int g, int row0,
 template <int MODE>
 __global__ void __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2, 2)))
 ffn_gemm_e4m3(E4m3Args p) {
-    const int L = xcd_remap_runs(blockIdx.x, p.n_tiles[0] * p.NT);
+    const int L = xcd_queue_tile(p.n_tiles[0] * p.NT, p.queue);
     if (L < 0) return;
     if (p.wt.tab && wtab_layer(p.wt) < 0) return;
     const int2 wl = p.work[L];
@@ -600,7 +601,8 @@ hipError_t launch_gemm_e4m3(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_
     a.out_scale = h_scale;
     a.K = c.H;
     a.N = c.I;
-    hipLaunchKernelGGL(ffn_gemm_e4m3<0>, dim3((unsigned)xcd_grid_runs(max_tiles * wk.nt1)), dim3(NTH), 0, s, a);
+    a.queue = wk.n_tiles + 2;  // queue 0
+    hipLaunchKernelGGL(ffn_gemm_e4m3<0>, dim3((unsigned)xcd_queue_grid(max_tiles * wk.nt1)), dim3(NTH), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // GEMM2: down projection of h
@@ -619,7 +621,8 @@ hipError_t launch_gemm_e4m3(const moe_cfg& c, int64_t max_tiles, int64_t n_rows_
     a.K = c.I;
     a.N = c.H;
     a.out_f32 = c.y_dtype == MOE_F32 ? 1 : 0;
-    hipLaunchKernelGGL(ffn_gemm_e4m3<1>, dim3((unsigned)xcd_grid_runs(max_tiles * wk.nt2)), dim3(NTH), 0, s, a);
+    a.queue = wk.n_tiles + 2 + kQueueWords;  // queue 1
+    hipLaunchKernelGGL(ffn_gemm_e4m3<1>, dim3((unsigned)xcd_queue_grid(max_tiles * wk.nt2)), dim3(NTH), 0, s, a);
     return hipGetLastError();
 }
 

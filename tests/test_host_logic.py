@@ -20,7 +20,9 @@ def _hipcc():
 def test_xcd_remap_covers_every_tile(tmp_path):
     """The grouped GEMMs remap block ids so that runs of tiles stay on one XCD;
     with the launch grid rounded up to a multiple of 8 every tile of any
-    device-side count up to the grid is computed exactly once."""
+    device-side count up to the grid is computed exactly once, and so it is
+    when the last tiles of each XCD's share go through the work queues, in any
+    order the blocks run (a fast XCD then takes tiles of the others')."""
     exe = str(tmp_path / "xcd_cover")
     subprocess.check_call([_hipcc(), "-O1", "-std=c++17", "-D__HIP_PLATFORM_AMD__",
                            f"-I{os.path.join(ROOT, 'include')}", os.path.join(HERE, "host", "xcd_cover.cpp"),
@@ -28,3 +30,4 @@ def test_xcd_remap_covers_every_tile(tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "reaches tile 41: 0" in r.stdout
+    assert "a fast XCD took up to" in r.stdout
