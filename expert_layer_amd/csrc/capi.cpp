@@ -8,17 +8,24 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 
 #include "common.hpp"
 
-// The layer combines inside the shared expert's GEMM2 from this many tokens
-// on (bf16 y): timed against the separate combine it ties at 4096 and 8192
-// tokens and gains 0.5% at 16384, while at 512 it costs 0.8%.
+// The layer can combine inside the shared expert's GEMM2 (bf16 y, from this
+// many tokens on) when the environment sets MOE_FUSED_COMBINE=1.  With the
+// grouped GEMMs' work queues the separate combine pass times 0.2-0.7% faster
+// at 8192 tokens and the same at 16384, so it is the default; below 4096
+// tokens the fused form costs 0.8% (512 tokens) and is never used.
 #ifndef MOE_FUSED_COMBINE_MIN_T
 #define MOE_FUSED_COMBINE_MIN_T 4096
 #endif
 constexpr int kFusedCombineMinT = MOE_FUSED_COMBINE_MIN_T;
+bool fused_combine_requested() {
+    const char* v = std::getenv("MOE_FUSED_COMBINE");
+    return v != nullptr && v[0] == '1' && v[1] == '\0';
+}
 
 namespace {
 
@@ -832,7 +839,8 @@ moe_status moe_layer(const moe_cfg* cfg, const void* w_router, const float* bias
     // bf16 y with a shared expert: the shared expert's tiles own rows of out,
     // so its GEMM2 can do the combine in its epilogue (no y_shared, no combine
     // pass; the same arithmetic as moe_combine)
-    const bool fused = c.act_dtype == MOE_BF16 && c.has_shared && c.y_dtype == MOE_BF16 && c.T >= kFusedCombineMinT;
+    const bool fused = c.act_dtype == MOE_BF16 && c.has_shared && c.y_dtype == MOE_BF16 && c.T >= kFusedCombineMinT &&
+                       fused_combine_requested();
     st = ffn_enqueue(cs, max_rows_of(cs), x_rows, nullptr, l.offsets, l.row_src, *w, wtab_of(c, *w, 0), x, l.y_rows,
                      l.y_shared, l.scratch, s, fused ? out : nullptr, l.tok_row, l.topk_w);
     if (st != MOE_OK) return st;

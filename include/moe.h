@@ -400,9 +400,11 @@ moe_status moe_quantize_fp8(const moe_cfg *cfg, const void *x, uint8_t *x_q, flo
  * the workspace size accounts for), whatever cfg->m_tile and cfg->x_layout say
  * (those shape the standalone stage calls only); the result equals that of
  * the four stage calls made with those two fields.  With bf16 y, a shared
- * expert and T >= 4096 the combine runs inside the shared expert's GEMM2 (its
- * tiles own token rows of out; the same arithmetic, so the same bits).  w may
- * be row-major or tiled.  x, w_router and out are 16-byte aligned.
+ * expert, T >= 4096 and the environment variable MOE_FUSED_COMBINE set to 1
+ * (read at each call) the combine runs inside the shared expert's GEMM2 (its
+ * tiles own token rows of out; the same arithmetic, so the same bits); by
+ * default it runs as the separate combine pass, which times as fast or
+ * faster.  w may be row-major or tiled.  x, w_router and out are 16-byte aligned.
  * Low-precision experts (act_dtype MOE_BF16, w_dtype MOE_FP8_E4M3 or
  * MOE_FP4_E2M1, row-major weights with their scales, x 16-byte aligned): the
  * route and the quantisation of x in one pass (moe_route_quantize), moe_permute's maps (m_tile 16,

@@ -10,6 +10,9 @@ bit, and bf16 outputs are also measured beyond their own rounding.  For
 bf16 layers the oracle stores the SwiGLU intermediate in bf16 (an activation of
 a layer whose activations are bf16); the distance to the exact fp64 math
 without that storage is bounded separately (3e-2)."""
+import contextlib
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -224,8 +227,8 @@ def test_layer_full_size_tokens(name):
     synth.config("c2_mixtral_bf16").with_(T=200),
     # H and I not multiples of 32: the tiled rows carry zero column padding
     synth.MoeShape("ragged_shared", T=77, H=520, E=6, k=2, I=264, shared=True, I_shared=136, seed=9),
-    # from 4096 tokens on, bf16 y with a shared expert: the combine inside the
-    # shared expert's GEMM2 (k = 2)
+    # from 4096 tokens on, bf16 y with a shared expert and MOE_FUSED_COMBINE=1:
+    # the combine inside the shared expert's GEMM2 (k = 2)
     synth.MoeShape("ragged_shared_4k", T=4100, H=520, E=6, k=2, I=264, shared=True, I_shared=136, seed=10),
 ])
 def test_layer_equals_its_stage_calls(shape, layout, ydt):
@@ -234,17 +237,36 @@ def test_layer_equals_its_stage_calls(shape, layout, ydt):
     bits; so do they with the tiled x_perm (the GEMM's arithmetic does not
     depend on where its operands come from), and they match the oracle.  With
     bf16 y and a shared expert the layer combines inside the shared expert's
-    GEMM2 (its tiles own rows of out), with the arithmetic of moe_combine: the
-    same bits again."""
-    _layer_vs_stages(shape, layout, ydt)
+    GEMM2 (its tiles own rows of out) when MOE_FUSED_COMBINE=1, with the
+    arithmetic of moe_combine: the same bits again."""
+    with _fused_combine(shape.name == "ragged_shared_4k"):
+        _layer_vs_stages(shape, layout, ydt)
 
 
-def test_layer_equals_its_stage_calls_full_size():
-    """The benchmarked configuration at full c3 size (T = 8192: the combine
-    inside the shared expert's GEMM2, k = 8): the same bits as the stage calls
-    with moe_combine, and a covering token subset against the oracle."""
+@contextlib.contextmanager
+def _fused_combine(on):
+    """MOE_FUSED_COMBINE for the moe_layer calls inside (the library reads it
+    at each call)."""
+    old = os.environ.get("MOE_FUSED_COMBINE")
+    os.environ["MOE_FUSED_COMBINE"] = "1" if on else "0"
+    try:
+        yield
+    finally:
+        if old is None:
+            del os.environ["MOE_FUSED_COMBINE"]
+        else:
+            os.environ["MOE_FUSED_COMBINE"] = old
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["separate_combine", "fused_combine"])
+def test_layer_equals_its_stage_calls_full_size(fused):
+    """The benchmarked configuration at full c3 size (T = 8192, k = 8), with
+    the separate combine pass (the default) and with the combine inside the
+    shared expert's GEMM2: the same bits as the stage calls with moe_combine,
+    and a covering token subset against the oracle."""
     s = synth.config("c3_dsv3_bf16")
-    _layer_vs_stages(s, moe.MOE_LAYOUT_INDEXED, moe.MOE_BF16, n_oracle=64)
+    with _fused_combine(fused):
+        _layer_vs_stages(s, moe.MOE_LAYOUT_INDEXED, moe.MOE_BF16, n_oracle=64)
 
 
 def _layer_vs_stages(s, layout, ydt, n_oracle=None):
