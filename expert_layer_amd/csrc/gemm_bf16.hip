@@ -649,9 +649,11 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, int mt, int g, int r
             for (int k = 0; k < 2; ++k) {
                 const int id = k * NTH + tid;
                 const int row = id >> 5, c = id & 31, grow = r * 32 + row, col = n0 + c * 8;
+                // non-temporal: y is read again only by the combine, after the
+                // launch, so it need not displace the h slots from L2
                 if (grow < M && col < N)
-                    *reinterpret_cast<i32x4*>(y + (size_t)(row0 + grow) * N + col) =
-                        sv[row * 32 + (c ^ (((row >> 2) & 3) << 2))];
+                    __builtin_nontemporal_store(sv[row * 32 + (c ^ (((row >> 2) & 3) << 2))],
+                                                reinterpret_cast<i32x4*>(y + (size_t)(row0 + grow) * N + col));
             }
         }
     } else {
