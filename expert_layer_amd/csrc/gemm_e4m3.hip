@@ -486,8 +486,10 @@ __device__ __forceinline__ void run_tile(const E4m3Args& p, int g, int row0, int
             for (int i = 0; i < 2; ++i) {
                 const int id = i * NTH + tid;
                 const int r = id >> 5, c = id & 31, row = 32 * u + r;
+                // non-temporal: y is read again only by the combine, after the launch
                 if (row < M && c * 8 < ncols)
-                    *reinterpret_cast<i32x4*>(y + (size_t)(row0 + row) * N + n0 + c * 8) = sv[r * 32 + (c ^ (r & 15))];
+                    __builtin_nontemporal_store(sv[r * 32 + (c ^ (r & 15))],
+                                                reinterpret_cast<i32x4*>(y + (size_t)(row0 + row) * N + n0 + c * 8));
             }
         }
     } else {
