@@ -529,8 +529,10 @@ __device__ __forceinline__ void run_tile(const Fp8Args& p, int g, int row0, int 
                 const int id = k * NTH + tid;
                 const int r = id >> 5, c = id & 31;
                 const int row = (r >> 5) * (TB / 2) + 32 * u + (r & 31), col = n0 + c * 8;
+                // non-temporal: y is read again only by the combine, after the launch
                 if (row < M && col < N)
-                    *reinterpret_cast<i32x4*>(y + (size_t)(row0 + row) * N + col) = sv[r * 32 + (c ^ (r & 15))];
+                    __builtin_nontemporal_store(sv[r * 32 + (c ^ (r & 15))],
+                                                reinterpret_cast<i32x4*>(y + (size_t)(row0 + row) * N + col));
             }
         }
     } else {
